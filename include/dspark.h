@@ -1,0 +1,196 @@
+/*
+ * dspark.h -- C ABI of the MI355X (gfx950) DSpark vocabulary-wide
+ * propose / dyadic24 / verify library (libdspark.so).
+ *
+ * Definitions come from three public pages, cited by title and section:
+ *   [Q]  "PP1 q transport and scheduling design", section "Distribution
+ *        contract and precision" (the dyadic24 categorical q, its rejections,
+ *        sparse top-k support, integer sampling) and section "Size and
+ *        critical path" (dense / sparse q layouts and sizes).
+ *   [C]  "Remote DSpark drafter -- wire and state contract (DSV41-OFFLOAD)",
+ *        section 2 (greedy argmax with lowest-index ties; N = 5 block
+ *        positions, anchor-as-first) and section 6.3 (draft_ids int32 and
+ *        confidence float32 per request and position; failed entries carry
+ *        id 0 and confidence 0.0; confidence must be finite in [0, 1]).
+ *   [A]  "DeepSeek-V4.1 DSpark" (ROCm ATOM docs), section "State and
+ *        sampling contracts" (greedy verification matches the target argmax
+ *        over the anchor plus up to five proposals; the accepted prefix is
+ *        committed).
+ *
+ * Conventions shared by every entry point
+ *   Memory.   Every array argument is a DEVICE pointer owned by the caller
+ *             (e.g. a torch tensor); struct arguments themselves are host
+ *             memory.  The library never allocates or frees device memory.
+ *             Logit rows are row-major, `row_stride` elements apart, and the
+ *             first row and the row stride in bytes must be 16-byte aligned.
+ *   Streams.  `stream` is a hipStream_t (NULL = the null stream).  Work is
+ *             enqueued on it and the call returns without synchronising.
+ *   Errors.   The host return value is DSPARK_SUCCESS (0) once the work is
+ *             enqueued, or a negative DSPARK_E* code for a bad argument or a
+ *             failed launch; on an argument error nothing is enqueued.
+ *             dspark_last_error() gives a message (per host thread).
+ *   Data.     Problems with the data itself (NaN rows, bad draws, ...) are
+ *             reported per row / per request in device status arrays using
+ *             the DSPARK_ST_* codes below.  Every output of a row or request
+ *             with a nonzero status is zero (token 0, confidence 0.0,
+ *             counts 0, sparse length 0, accept length 0, bonus 0) [C 6.3].
+ *   Threads.  The library is stateless and reentrant.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSPARK_ABI_VERSION 1
+#define DSPARK_MASS (1u << 24)   /* M, total count of a q row [Q] */
+#define DSPARK_N_DRAFT 5         /* draft rows per request [C 2] */
+#define DSPARK_N_TARGET 6        /* anchor + 5 target rows per request [A] */
+#define DSPARK_K_MAX 1024        /* largest sparse top-k this build supports */
+#define DSPARK_V_MAX (1 << 20)   /* largest vocabulary accepted */
+
+/* host return codes */
+#define DSPARK_SUCCESS 0
+#define DSPARK_EINVAL (-1)       /* bad value, size, NULL pointer or mode */
+#define DSPARK_EALIGN (-2)       /* row pointer or row stride not 16-byte aligned */
+#define DSPARK_EWORKSPACE (-3)   /* workspace smaller than dspark_workspace_bytes() */
+#define DSPARK_EHIP (-4)         /* the HIP runtime refused a launch */
+
+/* device status codes (per row, per request) */
+#define DSPARK_ST_OK 0
+#define DSPARK_ST_ROW_NAN 1            /* a NaN logit or weight [Q] */
+#define DSPARK_ST_ROW_POSINF 2         /* a +inf logit or weight [Q] */
+#define DSPARK_ST_ROW_ZERO_MASS 3      /* every logit -inf / every weight 0 [Q] */
+#define DSPARK_ST_DRAW_RANGE 4         /* a draw >= 2^24 [Q] */
+#define DSPARK_ST_ALLOC_INCONSISTENT 5 /* remaining outside [0, #{r>0}] or sum != M [Q] */
+#define DSPARK_ST_TARGET_INVALID 6     /* a target row of the request is invalid */
+#define DSPARK_ST_DRAFT_INVALID 7      /* a valid draft row carries a token outside [0, V) */
+#define DSPARK_ST_BAD_WEIGHT 8         /* weights-only entry: weight < 0 or > 1 */
+#define DSPARK_ST_BAD_TOPK 9           /* topk[r] outside [0, min(k_max, V)] */
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+typedef enum { DSPARK_GREEDY = 0, DSPARK_SAMPLED = 1 } dspark_mode;
+
+/* A batch of V-wide logit rows (final logits: temperature and any bias are
+ * applied upstream [Q]).  data: device pointer to row 0, float32 or bf16
+ * (dtype); n_rows >= 0; 1 <= vocab <= DSPARK_V_MAX; row_stride >= vocab. */
+typedef struct {
+  const void* data;
+  int32_t dtype;
+  int32_t reserved;
+  int64_t n_rows;
+  int64_t vocab;
+  int64_t row_stride;
+} dspark_rows;
+
+/* Storage for the dyadic24 q of n_rows rows [Q; layouts: "Size and
+ * critical path"].  topk: device int32[n_rows]; topk[r] == 0 makes row r
+ * dense, 1 <= topk[r] <= min(k_max, V) makes it sparse top-k; topk == NULL
+ * makes every row dense.  k_max: 0..DSPARK_K_MAX, the row length of the
+ * sparse arrays.
+ *   dense:  uint32[n_rows][vocab] counts c_v (sum M); written only for dense
+ *           rows; q(v) = c_v / 2^24.  May be NULL if no row is dense.
+ *   sp_ids: int32[n_rows][k_max] support token ids, ascending, positive
+ *           counts only; sp_cnt: uint32[n_rows][k_max] their counts;
+ *   sp_len: int32[n_rows] number of entries written (0 for dense rows and
+ *           failed rows).  May all be NULL if no row is sparse.          */
+typedef struct {
+  const int32_t* topk;
+  int32_t k_max;
+  int32_t reserved;
+  uint32_t* dense;
+  int32_t* sp_ids;
+  uint32_t* sp_cnt;
+  int32_t* sp_len;
+} dspark_q;
+
+/* Greedy proposal of every draft row [C 2]: argmax[r] = lowest index of the
+ * row maximum (IEEE compare, -0 == +0); conf[r] = 1 / sum_v exp(x_v - max)
+ * (softmax probability of the argmax, float32, within 1e-6 relative);
+ * row_status[r] = OK / ROW_NAN / ROW_POSINF / ROW_ZERO_MASS (NaN is checked
+ * first, then +inf, then all -inf).  Outputs are int32/float/int32[n_rows]. */
+int dspark_propose(const dspark_rows* draft, int32_t* argmax, float* conf, int32_t* row_status,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* dyadic24-standard-v1 counts of every draft row [Q] ("allocate integer
+ * counts"; this call does not allocate memory):
+ *   support: all tokens (dense) or the top-k by (logit desc, id asc);
+ *   m = row max; d_v = RN32(x_v - m); w_v = RN32(exp(d_v)) correctly rounded
+ *   (-inf -> 0); S = sum_support w_v exactly; S64 = RN64(S);
+ *   p_v = RN64(w_v / S64); y_v = p_v * 2^24; c_v = floor(y_v), r_v = y_v - c_v;
+ *   remaining = M - sum c_v must satisfy 0 <= remaining <= #{r_v > 0};
+ *   the `remaining` largest r_v (ties to the lowest id) get +1; sum c_v == M.
+ * row_status[r] as in dspark_propose plus ALLOC_INCONSISTENT and BAD_TOPK. */
+int dspark_q_alloc(const dspark_rows* draft, const dspark_q* q, int32_t* row_status, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/* Integer categorical sampling [Q]: for row r and draw j, tokens[r][j] = the
+ * first token (ascending id over the row's support) whose inclusive
+ * cumulative count is strictly greater than draws[r][j].  draws: uint32
+ * [n_rows][draws_per_row]; tokens: int32 same shape.  row_status is in/out:
+ * rows that enter nonzero keep their status and get tokens 0; a draw
+ * >= 2^24 sets DRAW_RANGE; counts that do not sum to M set
+ * ALLOC_INCONSISTENT; either zeroes every token of the row.  Reads q->topk,
+ * q->dense, q->sp_* as written by dspark_q_alloc. */
+int dspark_sample(const dspark_q* q, int64_t n_rows, int64_t vocab, const uint32_t* draws,
+                  int64_t draws_per_row, int32_t* tokens, int32_t* row_status, void* stream);
+
+/* Greedy verification [A; C 2 anchor-as-first] of n_requests requests.
+ * target: 6 rows per request (row i predicts draft position i; row 5 gives
+ * only the bonus).  draft_tokens: int32[n_requests][5]; draft_status:
+ * int32[n_requests][5] or NULL (all valid).  Outputs: target_argmax and
+ * target_status int32[n_requests][6]; accept_len, bonus, req_status
+ * int32[n_requests].  accept_len = number of leading positions whose draft
+ * row is valid and whose token equals the target argmax (0..5); bonus =
+ * target argmax at position accept_len.  Any invalid target row ->
+ * TARGET_INVALID; a valid draft row with a token outside [0, V) ->
+ * DRAFT_INVALID; both give accept_len = bonus = 0. */
+int dspark_verify_greedy(const dspark_rows* target, const int32_t* draft_tokens,
+                         const int32_t* draft_status, int64_t n_requests, int32_t* target_argmax,
+                         int32_t* target_status, int32_t* accept_len, int32_t* bonus,
+                         int32_t* req_status, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole step in one call: propose + (optional) q + (optional) sample on
+ * the 5R draft rows, argmax on the 6R target rows, and greedy verification.
+ * mode GREEDY verifies the argmax tokens, SAMPLED the sampled tokens (then q,
+ * draws and sample are required).  q == NULL skips q; draws/sample == NULL
+ * skip sampling (GREEDY only).  draws: uint32[5R], one per draft row. Output
+ * shapes as in the single-stage calls; row_status covers the draft rows. */
+int dspark_fused(const dspark_rows* draft, const dspark_rows* target, int32_t mode,
+                 const dspark_q* q, const uint32_t* draws, int32_t* argmax, float* conf,
+                 int32_t* sample, int32_t* row_status, int32_t* target_argmax,
+                 int32_t* target_status, int32_t* accept_len, int32_t* bonus, int32_t* req_status,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* Test entry: the dense allocation steps of dspark_q_alloc applied to
+ * caller-given float32 weights (normalised weights in [0, 1]), so that the
+ * consistency assertions can be reached with constructed inputs.
+ * w: float[n_rows] rows of n (stride elements apart); counts: uint32
+ * [n_rows][n] (dense, stride n); row_status: ROW_NAN, ROW_POSINF,
+ * BAD_WEIGHT, ROW_ZERO_MASS or ALLOC_INCONSISTENT on failure. */
+int dspark_q_alloc_weights(const float* w, int64_t n_rows, int64_t n, int64_t stride,
+                           uint32_t* counts, int32_t* row_status, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Test entry: the library's weight function w = RN32(exp(d)) applied to n
+ * float32 values d <= 0 (or -inf).  Used to check it exhaustively. */
+int dspark_cr_expf(const float* d, float* w, int64_t n, void* stream);
+
+/* Workspace bytes an entry point needs (op: 0 propose, 1 q_alloc, 2 sample,
+ * 3 verify, 4 fused, 5 q_alloc_weights).  This build needs none: it returns
+ * 0, and ws may be NULL with ws_bytes 0. */
+size_t dspark_workspace_bytes(int32_t op, int64_t n_rows, int64_t vocab, int32_t k_max);
+
+const char* dspark_q_semantic_id(void); /* "dyadic24-standard-v1" [Q] */
+const char* dspark_status_name(int32_t code);
+const char* dspark_last_error(void);
+int32_t dspark_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSPARK_H */

@@ -1,0 +1,62 @@
+"""CPU checks of the C-ABI library: it loads, exports every function that
+include/dspark.h declares, and answers the pure-host queries.  No compute
+call is made (no GPU here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from vocab_wide_draft_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dspark.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    if not os.path.exists(B.library_path()):
+        pytest.fail("libdspark.so is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(B.library_path())
+    names = _declared()
+    assert "dspark_fused" in names and len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTS) == names
+
+
+def test_host_queries():
+    B.load_library()
+    assert B.abi_version() == 1
+    assert B.q_semantic_id() == "dyadic24-standard-v1"
+    for code, name in B.STATUS_NAMES.items():
+        assert B.status_name(code) == name
+    assert B.status_name(99) == "UNKNOWN"
+    assert B.workspace_bytes(4, 5120, 129280, 1024) == 0
+
+
+def test_argument_errors_enqueue_nothing():
+    """Bad arguments are refused on the host before any launch."""
+    lib = B.load_library()
+    r = B.Rows(None, 7, 0, 5, 100, 100)  # bad dtype
+    assert lib.dspark_propose(ctypes.byref(r), None, None, None, None, 0, None) == -1
+    r = B.Rows(16, 0, 0, 5, 100, 99)  # stride < vocab
+    assert lib.dspark_propose(ctypes.byref(r), None, None, None, None, 0, None) == -1
+    r = B.Rows(8, 0, 0, 5, 100, 100)  # misaligned data pointer
+    assert lib.dspark_propose(ctypes.byref(r), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                              ctypes.c_void_p(16), None, 0, None) == -2
+    r = B.Rows(16, 1, 0, 5, 100, 101)  # bf16 stride * 2 not a multiple of 16
+    assert lib.dspark_propose(ctypes.byref(r), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                              ctypes.c_void_p(16), None, 0, None) == -2
+    assert "aligned" in lib.dspark_last_error().decode()
+    r = B.Rows(16, 0, 0, 5, 100, 100)
+    t = B.Rows(16, 0, 0, 7, 100, 100)  # target rows != 6 per request
+    assert lib.dspark_fused(ctypes.byref(r), ctypes.byref(t), 0, None, None, *([ctypes.c_void_p(16)] * 9),
+                            None, 0, None) == -1
+    q = B.Q(None, 2000, 0, None, None, None, None)  # k_max too large
+    assert lib.dspark_q_alloc(ctypes.byref(r), ctypes.byref(q), ctypes.c_void_p(16), None, 0, None) == -1
+    assert lib.dspark_cr_expf(None, None, -1, None) == -1

@@ -1,0 +1,226 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle,
+element by element.  Argmax, tokens, counts, samples, statuses and accept
+lengths must match bit-exactly; confidences within 1e-6 relative."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dyadic24 as O
+from vocab_wide_draft_amd import binding as B
+from vocab_wide_draft_amd import workloads as W
+
+from gpu_helpers import check_draft_row, check_workload, dev, host, run_fused, to_dev, u32_dev
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = "f32", "bf16"
+
+
+def _bits_bf16(x32):
+    return W.f32_to_bf16_bits(np.asarray(x32, np.float32))
+
+
+# ------------------------------------------------------------ small configs
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("V", [257, 3000, 20011])
+def test_configs_small(cfg, V):
+    R = {1: 2, 2: 4, 3: 3, 4: 4, 5: 8}[cfg]
+    w = W.make(cfg, V=V, R=R, seed=1000 + cfg * 7 + V)
+    h = run_fused(w)
+    check_workload(w, h, label=f"cfg{cfg} V{V}")
+
+
+# ------------------------------------------------------------- edge rows
+def _edge_rows(V, rng):
+    """Constructed draft rows (binary32 values) with a label each."""
+    rows = []
+    base = (rng.standard_normal(V) * 2).astype(np.float32)
+    r = base.copy(); r[V // 2] = np.nan; rows.append(("nan", r))
+    r = base.copy(); r[3 % V] = np.inf; rows.append(("posinf", r))
+    r = base.copy(); r[3 % V] = np.inf; r[7 % V] = np.nan; rows.append(("nan_and_inf", r))
+    rows.append(("all_neginf", np.full(V, -np.inf, np.float32)))
+    r = np.full(V, -np.inf, np.float32); r[V - 1] = -3.5; rows.append(("onehot_last", r))
+    r = np.zeros(V, np.float32); r[::3] = -0.0; rows.append(("signed_zeros", r))
+    r = np.full(V, -np.inf, np.float32); r[0] = -0.0; r[V - 1] = 0.0; rows.append(("zero_pair", r))
+    vals = np.array([1.5, 0.25], np.float32)
+    rows.append(("two_values", vals[rng.integers(0, 2, V)]))
+    rows.append(("constant", np.full(V, 7.0, np.float32)))
+    r = np.full(V, -200.0, np.float32); r[0] = 0.0
+    tail = np.array([-88.0, -90.5, -100.0, -103.9, -104.5, -87.4, -95.25], np.float32)
+    r[1:1 + min(len(tail), V - 1)] = tail[:V - 1]; rows.append(("subnormal_weights", r))
+    r = base.copy(); r[rng.random(V) < 0.9] = -np.inf; r[0] = 1.0; rows.append(("mostly_masked", r))
+    return rows
+
+
+def _midpoint_d():
+    """A binary32 d whose weight RN32(exp(d)) is an odd multiple of 2^-53 below
+    2^-40, so that S = 1 + w is exactly halfway between two binary64 values."""
+    for j in range(0, 4000):
+        target = (2 * j + 1) * 2.0**-53
+        d0 = np.float32(math.log(target))
+        ds = d0 + np.arange(-64, 65, dtype=np.float32) * np.spacing(d0)
+        w = O.cr_exp_f32(ds.astype(np.float32)).astype(np.float64)
+        hit = np.flatnonzero(w == target)
+        if hit.size:
+            return np.float32(ds[hit[0]])
+    raise AssertionError("no binary32 d found")
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("V", [1, 5, 64, 1000, 4099])
+def test_edge_rows(dtype, V):
+    rng = np.random.default_rng(V)
+    rows = [(n, r) for n, r in _edge_rows(V, rng)]
+    if dtype == F32 and V >= 2:
+        r = np.full(V, -np.inf, np.float32); r[0] = 0.0; r[1] = _midpoint_d(); rows.append(("midpoint_sum", r))
+    names = [n for n, _ in rows]
+    x = np.stack([r for _, r in rows]).astype(np.float32)
+    raw = x if dtype == F32 else _bits_bf16(x)
+    ks = [0, min(5, V), min(1024, V), 1]
+    for k in ks:
+        topk = np.full(len(rows), k, np.int32)
+        draws = rng.integers(0, 1 << 24, len(rows), dtype=np.uint32)
+        draws[1] = (1 << 24) + 5  # out of range on a row that is invalid anyway
+        d = to_dev(raw, dtype)
+        q = B.q_alloc(d, topk=topk, k_max=1024)
+        pr = B.propose(d)
+        torch.cuda.synchronize()
+        hq = host(q)
+        hp = host(pr)
+        for j, name in enumerate(names):
+            ref = O.draft_row(raw[j], dtype, k)
+            h = {"status": hq["status"], "argmax": hp["argmax"] * (hq["status"] == 0),
+                 "conf": hp["conf"] * (hq["status"] == 0), "q": hq}
+            check_draft_row(h, j, ref, k, label=f"{dtype} V{V} k{k} {name}")
+            st_p = O.row_status(O.to_f32(raw[j], dtype))
+            assert int(hp["status"][j]) == st_p
+
+
+def test_draw_range_and_bad_topk():
+    V = 300
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((5, V)) * 2).astype(np.float32)
+    t = (rng.standard_normal((6, V)) * 2).astype(np.float32)
+    draws = np.array([1, (1 << 24), 5, 0xFFFFFFFF, 7], np.uint32)
+    topk = np.array([0, 0, V + 1, 3, -1], np.int32)
+    out = B.fused(to_dev(x, F32), to_dev(t, F32), B.SAMPLED, topk=topk, k_max=8, draws=u32_dev(draws))
+    torch.cuda.synchronize()
+    h = host(out)
+    assert h["status"].tolist() == [0, O.ST_DRAW_RANGE, O.ST_BAD_TOPK, O.ST_DRAW_RANGE, O.ST_BAD_TOPK]
+    assert h["sample"][1:].tolist() == [0, 0, 0, 0]
+    assert not h["q"]["dense"][1].any()
+    assert int(h["accept_len"][0]) <= 1
+
+
+def test_large_tie_groups_dense_f32():
+    """More than 2048 equal remainders in one bucket: the refinement passes and
+    the index cut by locate."""
+    V = 20000
+    rng = np.random.default_rng(9)
+    vals = np.array([0.0, -0.6931472, -1.25], np.float32)
+    x = vals[rng.integers(0, 3, (3, V))]
+    x[1, :] = 0.0  # all equal: remainders all equal
+    x[2, rng.random(V) < 0.3] = -np.inf
+    d = to_dev(x, F32)
+    q = host(B.q_alloc(d, topk=None))
+    for j in range(3):
+        ref = O.draft_row(x[j], F32, 0)
+        assert q["status"][j] == 0
+        assert (q["dense"][j] == ref["counts"]).all(), j
+
+
+# --------------------------------------------------- standalone entry points
+def test_sample_entry_many_draws():
+    V = 1000
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((4, V)) * 2).astype(np.float32)
+    x[3, 10:] = -np.inf
+    topk = np.array([0, 16, 0, 4], np.int32)
+    d = to_dev(x, F32)
+    q = B.q_alloc(d, topk=topk, k_max=16)
+    st = q["status"].clone()
+    draws = rng.integers(0, 1 << 24, (4, 64), dtype=np.uint32)
+    draws[:, 0] = 0
+    draws[:, 1] = (1 << 24) - 1
+    tok = B.sample(q, u32_dev(draws), st, V).cpu().numpy()
+    hq = host(q)
+    for r in range(4):
+        ref = O.draft_row(x[r], F32, int(topk[r]))
+        for j in range(64):
+            assert tok[r, j] == O.sample(ref["ids"], ref["counts"], int(draws[r, j]))[1]
+    # an out-of-range draw and a corrupted count row
+    dense = q["dense"]
+    dense[2, 5] += 1
+    st = q["status"].clone()
+    draws[0, 3] = 1 << 24
+    tok = B.sample(q, u32_dev(draws), st, V).cpu().numpy()
+    assert st.cpu().tolist() == [O.ST_DRAW_RANGE, 0, O.ST_ALLOC_INCONSISTENT, 0]
+    assert not tok[0].any() and not tok[2].any()
+
+
+def test_verify_entry():
+    V = 500
+    rng = np.random.default_rng(23)
+    R = 6
+    t = (rng.standard_normal((R * 6, V)) * 2).astype(np.float32)
+    t[6 * 2 + 4, 0] = np.nan  # request 2: invalid target row
+    tam = np.array([O.argmax_first(r)[1] if O.row_status(r) == 0 else 0 for r in t])
+    dt = np.zeros((R, 5), np.int32)
+    ds = np.zeros((R, 5), np.int32)
+    for r in range(R):
+        L = r % 6
+        for i in range(5):
+            dt[r, i] = tam[r * 6 + i] if i < L else (tam[r * 6 + i] + 1) % V
+    ds[4, 1] = O.ST_ROW_NAN  # invalid draft row stops acceptance
+    dt[5, 3] = V + 3  # valid row, token out of range
+    out = host(B.verify_greedy(to_dev(t, F32), torch.from_numpy(dt).to(dev()), torch.from_numpy(ds).to(dev())))
+    for r in range(R):
+        tst = [O.row_status(t[r * 6 + i]) for i in range(6)]
+        tgt = [0 if s else int(tam[r * 6 + i]) for i, s in enumerate(tst)]
+        ref = O.verify_greedy(dt[r].tolist(), ds[r].tolist(), tgt, tst, V)
+        assert (int(out["req_status"][r]), int(out["accept_len"][r]), int(out["bonus"][r])) == ref, r
+        assert out["target_argmax"][r * 6:(r + 1) * 6].tolist() == tgt
+
+
+def test_q_alloc_weights_entry():
+    rng = np.random.default_rng(29)
+    n = 2500
+    rows = [
+        O.cr_exp_f32(-rng.exponential(3.0, n).astype(np.float32)),
+        np.concatenate([[1.0, 2.0**-53], np.zeros(n - 2)]).astype(np.float32),  # binary64 tie in S
+        np.concatenate([[2.0**-149] * 7, np.zeros(n - 7)]).astype(np.float32),  # subnormals only
+        np.concatenate([[1.0, np.nan], np.zeros(n - 2)]).astype(np.float32),
+        np.concatenate([[1.0, np.inf], np.zeros(n - 2)]).astype(np.float32),
+        np.concatenate([[1.0, -0.5], np.zeros(n - 2)]).astype(np.float32),
+        np.concatenate([[1.5], np.zeros(n - 1)]).astype(np.float32),
+        np.zeros(n, np.float32),
+        np.concatenate([[-0.0, 0.25, 0.25, 0.25], np.zeros(n - 4)]).astype(np.float32),
+        np.full(n, 2.0**-30, np.float32),
+    ]
+    w = np.stack(rows)
+    counts, st = B.q_alloc_weights(torch.from_numpy(w).to(dev()))
+    counts, st = counts.cpu().numpy(), st.cpu().numpy()
+    for j, row in enumerate(rows):
+        s, c = O.dyadic24_counts(row)
+        assert int(st[j]) == s, j
+        assert (counts[j] == c).all(), j
+
+
+def test_cr_expf_sampled_and_hard_cases():
+    rng = np.random.default_rng(31)
+    d = np.concatenate([
+        rng.uniform(-104.0, 0.0, 1 << 20).astype(np.float32),
+        -np.abs(rng.standard_normal(1 << 18)).astype(np.float32) * np.float32(1e-3),
+        np.array([0.0, -0.0, -np.inf, -104.0, -103.972, -87.33654, -1e-45], np.float32),
+    ])
+    y = np.exp(d.astype(np.float64))
+    f = y.astype(np.float32).astype(np.float64)
+    ulp = np.spacing(y.astype(np.float32)).astype(np.float64)
+    hard = d[np.argsort(np.abs(np.abs(y - f) / np.where(ulp > 0, ulp, 1) - 0.5))[:4096]]
+    d = np.concatenate([d, hard])
+    got = B.cr_expf(torch.from_numpy(d).to(dev())).cpu().numpy()
+    ref = O.cr_exp_f32(d)
+    bad = np.flatnonzero(got.view(np.uint32) != ref.view(np.uint32))
+    assert bad.size == 0, (d[bad[:5]], got[bad[:5]], ref[bad[:5]])

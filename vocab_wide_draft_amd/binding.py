@@ -1,0 +1,249 @@
+"""ctypes binding of libdspark.so (include/dspark.h).  Argument marshalling
+only: every step runs in the HIP library.  Tensors are torch tensors on the
+GPU; outputs are allocated here with torch and filled by the library on the
+current torch stream."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+GREEDY = 0
+SAMPLED = 1
+MASS = 1 << 24
+K_MAX = 1024
+STATUS_NAMES = {0: "OK", 1: "ROW_NAN", 2: "ROW_POSINF", 3: "ROW_ZERO_MASS", 4: "DRAW_RANGE",
+                5: "ALLOC_INCONSISTENT", 6: "TARGET_INVALID", 7: "DRAFT_INVALID", 8: "BAD_WEIGHT",
+                9: "BAD_TOPK"}
+
+
+class DsparkError(RuntimeError):
+    pass
+
+
+class Rows(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n_rows", ctypes.c_int64), ("vocab", ctypes.c_int64), ("row_stride", ctypes.c_int64)]
+
+
+class Q(ctypes.Structure):
+    _fields_ = [("topk", ctypes.c_void_p), ("k_max", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("dense", ctypes.c_void_p), ("sp_ids", ctypes.c_void_p), ("sp_cnt", ctypes.c_void_p),
+                ("sp_len", ctypes.c_void_p)]
+
+
+EXPORTS = ["dspark_propose", "dspark_q_alloc", "dspark_sample", "dspark_verify_greedy", "dspark_fused",
+           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_workspace_bytes", "dspark_q_semantic_id",
+           "dspark_status_name", "dspark_last_error", "dspark_abi_version"]
+
+
+def library_path() -> str:
+    return os.environ.get("DSPARK_LIB", os.path.join(_HERE, "libdspark.so"))
+
+
+def load_library():
+    """Loads libdspark.so; raises if it is missing (there is no fallback)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise DsparkError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    RP, QP = ctypes.POINTER(Rows), ctypes.POINTER(Q)
+    sig = {
+        "dspark_propose": (ctypes.c_int, [RP, P, P, P, P, SZ, P]),
+        "dspark_q_alloc": (ctypes.c_int, [RP, QP, P, P, SZ, P]),
+        "dspark_sample": (ctypes.c_int, [QP, I64, I64, P, I64, P, P, P]),
+        "dspark_verify_greedy": (ctypes.c_int, [RP, P, P, I64, P, P, P, P, P, P, SZ, P]),
+        "dspark_fused": (ctypes.c_int, [RP, RP, I32, QP, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "dspark_q_alloc_weights": (ctypes.c_int, [P, I64, I64, I64, P, P, P, SZ, P]),
+        "dspark_cr_expf": (ctypes.c_int, [P, P, I64, P]),
+        "dspark_workspace_bytes": (SZ, [I32, I64, I64, I32]),
+        "dspark_q_semantic_id": (ctypes.c_char_p, []),
+        "dspark_status_name": (ctypes.c_char_p, [I32]),
+        "dspark_last_error": (ctypes.c_char_p, []),
+        "dspark_abi_version": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _LIB = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DsparkError(f"libdspark error {rc}: {_LIB.dspark_last_error().decode()}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _rows(x: torch.Tensor) -> Rows:
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("logits must be a 2-D [rows, V] tensor with unit column stride")
+    if x.dtype == torch.float32:
+        dt = DTYPE_F32
+    elif x.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    else:
+        raise ValueError("logits must be float32 or bfloat16")
+    if not x.is_cuda:
+        raise ValueError("logits must be on the GPU")
+    return Rows(x.data_ptr(), dt, 0, x.shape[0], x.shape[1], x.stride(0))
+
+
+def _i32(n, dev):
+    return torch.empty(n, dtype=torch.int32, device=dev)
+
+
+def abi_version() -> int:
+    return int(load_library().dspark_abi_version())
+
+
+def q_semantic_id() -> str:
+    return load_library().dspark_q_semantic_id().decode()
+
+
+def status_name(code: int) -> str:
+    return load_library().dspark_status_name(int(code)).decode()
+
+
+def workspace_bytes(op: int, n_rows: int, vocab: int, k_max: int) -> int:
+    return int(load_library().dspark_workspace_bytes(op, n_rows, vocab, k_max))
+
+
+def _make_q(n_rows, V, dev, topk, k_max, want_dense):
+    qd = {"topk": topk, "k_max": int(k_max)}
+    qd["dense"] = torch.empty((n_rows, V), dtype=torch.int32, device=dev) if want_dense else None
+    if topk is not None and k_max > 0:
+        qd["sp_ids"] = torch.empty((n_rows, k_max), dtype=torch.int32, device=dev)
+        qd["sp_cnt"] = torch.empty((n_rows, k_max), dtype=torch.int32, device=dev)
+        qd["sp_len"] = torch.empty(n_rows, dtype=torch.int32, device=dev)
+    else:
+        qd["sp_ids"] = qd["sp_cnt"] = qd["sp_len"] = None
+    return qd
+
+
+def _qstruct(qd) -> Q:
+    return Q(None if qd["topk"] is None else qd["topk"].data_ptr(), qd["k_max"], 0,
+             None if qd["dense"] is None else qd["dense"].data_ptr(),
+             None if qd["sp_ids"] is None else qd["sp_ids"].data_ptr(),
+             None if qd["sp_cnt"] is None else qd["sp_cnt"].data_ptr(),
+             None if qd["sp_len"] is None else qd["sp_len"].data_ptr())
+
+
+def _topk(topk, dev):
+    if topk is None:
+        return None
+    t = torch.as_tensor(topk, dtype=torch.int32)
+    return t.to(dev).contiguous()
+
+
+def propose(draft: torch.Tensor):
+    lib = load_library()
+    n, dev = draft.shape[0], draft.device
+    am, cf, st = _i32(n, dev), torch.empty(n, dtype=torch.float32, device=dev), _i32(n, dev)
+    r = _rows(draft)
+    _check(lib.dspark_propose(ctypes.byref(r), _p(am), _p(cf), _p(st), None, 0, _stream()))
+    return {"argmax": am, "conf": cf, "status": st}
+
+
+def q_alloc(draft: torch.Tensor, topk=None, k_max: int = 0):
+    """topk: None (all dense) or per-row k (0 = dense)."""
+    lib = load_library()
+    n, V, dev = draft.shape[0], draft.shape[1], draft.device
+    tk = _topk(topk, dev)
+    want_dense = tk is None or bool((tk == 0).any())
+    qd = _make_q(n, V, dev, tk, k_max, want_dense)
+    st = _i32(n, dev)
+    r, q = _rows(draft), _qstruct(qd)
+    _check(lib.dspark_q_alloc(ctypes.byref(r), ctypes.byref(q), _p(st), None, 0, _stream()))
+    qd["status"] = st
+    return qd
+
+
+def sample(qd, draws: torch.Tensor, row_status: torch.Tensor, vocab: int):
+    """draws: uint32-valued int tensor [n_rows, draws_per_row]; row_status is
+    updated in place."""
+    lib = load_library()
+    d = draws.to(torch.int32).contiguous()
+    n, dpr = d.shape
+    tok = torch.empty((n, dpr), dtype=torch.int32, device=d.device)
+    q = _qstruct(qd)
+    _check(lib.dspark_sample(ctypes.byref(q), n, vocab, _p(d), dpr, _p(tok), _p(row_status), _stream()))
+    return tok
+
+
+def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, draft_status=None):
+    lib = load_library()
+    R, dev = draft_tokens.shape[0], target.device
+    t = _rows(target)
+    out = {k: _i32(R * 6, dev) for k in ("target_argmax", "target_status")}
+    out.update({k: _i32(R, dev) for k in ("accept_len", "bonus", "req_status")})
+    dt = draft_tokens.to(torch.int32).contiguous()
+    ds = None if draft_status is None else draft_status.to(torch.int32).contiguous()
+    _check(lib.dspark_verify_greedy(ctypes.byref(t), _p(dt), _p(ds), R, _p(out["target_argmax"]),
+                                    _p(out["target_status"]), _p(out["accept_len"]), _p(out["bonus"]),
+                                    _p(out["req_status"]), None, 0, _stream()))
+    return out
+
+
+def fused(draft: torch.Tensor, target: torch.Tensor, mode: int, topk=None, k_max: int = 0, draws=None,
+          with_q: bool = True, out=None):
+    """The whole step.  draft [5R, V], target [6R, V]; draws [5R] or None.
+    `out` may pass preallocated outputs from an earlier call (same shapes)."""
+    lib = load_library()
+    n, V, dev = draft.shape[0], draft.shape[1], draft.device
+    R = n // 5
+    if out is None:
+        out = {"argmax": _i32(n, dev), "conf": torch.empty(n, dtype=torch.float32, device=dev),
+               "status": _i32(n, dev), "sample": _i32(n, dev) if draws is not None else None,
+               "target_argmax": _i32(R * 6, dev), "target_status": _i32(R * 6, dev),
+               "accept_len": _i32(R, dev), "bonus": _i32(R, dev), "req_status": _i32(R, dev)}
+        if with_q:
+            tk = _topk(topk, dev)
+            want_dense = tk is None or bool((tk == 0).any())
+            out["q"] = _make_q(n, V, dev, tk, k_max, want_dense)
+        else:
+            out["q"] = None
+        out["draws"] = None if draws is None else draws.to(torch.int32).contiguous()
+    d, t = _rows(draft), _rows(target)
+    q = None if out["q"] is None else ctypes.byref(_qstruct(out["q"]))
+    _check(lib.dspark_fused(ctypes.byref(d), ctypes.byref(t), mode, q, _p(out["draws"]), _p(out["argmax"]),
+                            _p(out["conf"]), _p(out["sample"]), _p(out["status"]), _p(out["target_argmax"]),
+                            _p(out["target_status"]), _p(out["accept_len"]), _p(out["bonus"]),
+                            _p(out["req_status"]), None, 0, _stream()))
+    return out
+
+
+def q_alloc_weights(w: torch.Tensor):
+    lib = load_library()
+    if w.dim() != 2 or w.dtype != torch.float32 or w.stride(1) != 1:
+        raise ValueError("w must be a 2-D float32 tensor with unit column stride")
+    n_rows, n = w.shape
+    counts = torch.empty((n_rows, n), dtype=torch.int32, device=w.device)
+    st = _i32(n_rows, w.device)
+    _check(lib.dspark_q_alloc_weights(_p(w), n_rows, n, w.stride(0), _p(counts), _p(st), None, 0, _stream()))
+    return counts, st
+
+
+def cr_expf(d: torch.Tensor):
+    lib = load_library()
+    d = d.contiguous()
+    w = torch.empty_like(d)
+    _check(lib.dspark_cr_expf(_p(d), _p(w), d.numel(), _stream()))
+    return w

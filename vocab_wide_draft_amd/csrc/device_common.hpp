@@ -1,0 +1,300 @@
+// Device building blocks shared by the row kernels: block geometry, wave and
+// block reductions/scans, order-preserving keys, the correctly rounded
+// binary32 exponential and the exact weight-sum accumulator.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dspark.h"
+
+namespace dspark {
+
+constexpr int BS = 1024;            // threads per row workgroup (16 wave64s)
+constexpr int NW = BS / 64;         // waves per workgroup
+constexpr uint32_t kMass = 1u << 24;
+constexpr int kHistBins = 4096;     // histogram bins of one select pass
+constexpr int kCandCap = 2048;      // candidates a select may collect in LDS
+constexpr int kMaxIter = 256;       // (V_MAX / 4) / BS vector iterations per row
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ---------------------------------------------------------------- wave ops
+template <class T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+template <class T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    T u = __shfl_xor(v, o, 64);
+    v = u > v ? u : v;
+  }
+  return v;
+}
+template <class T>
+__device__ __forceinline__ T wave_min(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    T u = __shfl_xor(v, o, 64);
+    v = u < v ? u : v;
+  }
+  return v;
+}
+// inclusive prefix sum over the 64 lanes
+template <class T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    T u = __shfl_up(v, o, 64);
+    if (l >= o) v += u;
+  }
+  return v;
+}
+
+// Scratch for block-wide collectives (must be __shared__).
+struct BlockScratch {
+  uint64_t w[NW + 1];
+};
+
+// Block reductions: every thread calls, every thread gets the result.
+template <class T>
+__device__ T block_sum(T v, BlockScratch& s) {
+  v = wave_sum(v);
+  if (lane_id() == 0) reinterpret_cast<T*>(s.w)[wave_id()] = v;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    T t = threadIdx.x < NW ? reinterpret_cast<T*>(s.w)[threadIdx.x] : T(0);
+    t = wave_sum(t);
+    if (threadIdx.x == 0) reinterpret_cast<T*>(s.w)[NW] = t;
+  }
+  __syncthreads();
+  T r = reinterpret_cast<T*>(s.w)[NW];
+  __syncthreads();
+  return r;
+}
+template <class T>
+__device__ T block_max(T v, BlockScratch& s) {
+  v = wave_max(v);
+  if (lane_id() == 0) reinterpret_cast<T*>(s.w)[wave_id()] = v;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    T t = reinterpret_cast<T*>(s.w)[threadIdx.x < NW ? threadIdx.x : 0];
+    t = wave_max(t);
+    if (threadIdx.x == 0) reinterpret_cast<T*>(s.w)[NW] = t;
+  }
+  __syncthreads();
+  T r = reinterpret_cast<T*>(s.w)[NW];
+  __syncthreads();
+  return r;
+}
+template <class T>
+__device__ T block_min(T v, BlockScratch& s) {
+  v = wave_min(v);
+  if (lane_id() == 0) reinterpret_cast<T*>(s.w)[wave_id()] = v;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    T t = reinterpret_cast<T*>(s.w)[threadIdx.x < NW ? threadIdx.x : 0];
+    t = wave_min(t);
+    if (threadIdx.x == 0) reinterpret_cast<T*>(s.w)[NW] = t;
+  }
+  __syncthreads();
+  T r = reinterpret_cast<T*>(s.w)[NW];
+  __syncthreads();
+  return r;
+}
+// Exclusive prefix sum over threads in threadIdx order; *total gets the sum.
+template <class T>
+__device__ T block_excl_scan(T v, BlockScratch& s, T* total) {
+  T inc = wave_incl_scan(v);
+  if (lane_id() == 63) reinterpret_cast<T*>(s.w)[wave_id()] = inc;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    T t = threadIdx.x < NW ? reinterpret_cast<T*>(s.w)[threadIdx.x] : T(0);
+    T ti = wave_incl_scan(t);
+    if (threadIdx.x < NW) reinterpret_cast<T*>(s.w)[threadIdx.x] = ti - t;
+    if (threadIdx.x == NW - 1) reinterpret_cast<T*>(s.w)[NW] = ti;
+  }
+  __syncthreads();
+  T r = reinterpret_cast<T*>(s.w)[wave_id()] + inc - v;
+  if (total) *total = reinterpret_cast<T*>(s.w)[NW];
+  __syncthreads();
+  return r;
+}
+
+// ------------------------------------------------------------------- keys
+// Order-preserving map of a non-NaN binary32 to uint32; -0 and +0 map to the
+// same key (IEEE equality).  NaN never reaches it.
+__device__ __forceinline__ uint32_t key32(float x) {
+  uint32_t b = __float_as_uint(x);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+// Order-preserving, exact map of a remainder r in [0, 1) to uint64.  For
+// r >= 2^-11 the key is 2^63 + r * 2^63 (an integer: such an r is a multiple
+// of 2^-63), which spreads the usual remainders evenly over the top bits; a
+// smaller r keeps its binary64 bit pattern, which is below 2^63.
+__device__ __forceinline__ uint64_t rem_key(double r) {
+  uint64_t b = (uint64_t)__double_as_longlong(r);
+  uint32_t e = (uint32_t)(b >> 52);
+  if (e >= 1012u) return (1ull << 63) | (((b & ((1ull << 52) - 1)) | (1ull << 52)) << (e - 1012u));
+  return b;
+}
+
+// ------------------------------------------- correctly rounded exp, binary32
+#include "exp_table.inc"
+
+// RN32(exp(d)) for binary32 d <= 0 (or -inf).  Tang's table method in
+// binary64: d = (64 e + j) ln2/64 + r with |r| <= ln2/128, exp(d) =
+// 2^e 2^(j/64) exp(r); 2^(j/64) is a double-double table entry, exp(r) - 1 a
+// degree-7 Taylor polynomial (truncation < 2^-74).  The product is kept as an
+// unevaluated pair H + L (relative error about 2^-70) and rounded to binary32
+// once; when the binary64 sum lands within 2^-48 of a binary32 rounding
+// midpoint, the side is decided from H and L exactly.  The function is checked
+// against an independent evaluation for every binary32 d in [-104, 0].
+__device__ __forceinline__ float cr_expf(float d) {
+  if (!(d > -104.0f)) return 0.0f;  // exp(-104) < 2^-150 rounds to 0; also -inf
+  if (d == 0.0f) return 1.0f;
+  const double dd = (double)d;
+  const double kf = __builtin_rint(dd * kExpInvL);
+  const int k = (int)kf;
+  const int j = k & 63;
+  const int e = k >> 6;  // floor(k / 64)
+  const double rhi = __builtin_fma(-kf, kExpCHi, dd);  // exact: k*C_HI is exact and close to d
+  const double t = kf * kExpCLo;
+  const double r1 = rhi - t;
+  const double r2 = (rhi - r1) - t;  // r1 + r2 = rhi - t to ~2^-100
+  double P = __builtin_fma(r1, kExpP7, kExpP6);
+  P = __builtin_fma(r1, P, kExpP5);
+  P = __builtin_fma(r1, P, kExpP4);
+  P = __builtin_fma(r1, P, kExpP3);
+  P = __builtin_fma(r1, P, kExpP2);
+  const double s = __builtin_fma(r1 * r1, P, r2);  // exp(r) = 1 + r1 + s
+  const double Th = kExpTabHi[j], Tl = kExpTabLo[j];
+  const double ph = Th * r1;
+  const double pl = __builtin_fma(Th, r1, -ph);
+  const double H = Th + ph;
+  const double e1 = ph - (H - Th);
+  const double L = e1 + (pl + __builtin_fma(Th, s, Tl * ((1.0 + r1) + s)));
+  const double tv = __builtin_ldexp(H + L, e);
+  const float f = (float)tv;
+  const double g = (double)f;
+  if (g == tv) return f;
+  // neighbour of f (>= 0) on tv's side: one unit in the last place up or down
+  const uint32_t fb = __float_as_uint(f);
+  const float nb = __uint_as_float(tv > g ? fb + 1u : (fb ? fb - 1u : 0u));
+  const double mid = 0.5 * (g + (double)nb);
+  if (__builtin_fabs(tv - mid) > 0x1p-48 * tv) return f;
+  const double delta = (__builtin_ldexp(H, e) - mid) + __builtin_ldexp(L, e);
+  const float up = f > nb ? f : nb, dn = f > nb ? nb : f;
+  if (delta > 0.0) return up;
+  if (delta < 0.0) return dn;
+  return (__float_as_uint(up) & 1u) ? dn : up;  // exact tie: even significand
+}
+
+// ------------------------------------------------- exact weight accumulator
+// Sum of binary32 weights w in [0, 1], exactly.  Weights >= 2^-47 go to a
+// 128-bit fixed-point word with LSB 2^-70 (each is an integer there; 2^20 of
+// them stay below 2^90), smaller ones to a 128-bit word with LSB 2^-149
+// (each below 2^102, 2^20 of them below 2^122).
+struct Acc {
+  uint64_t mlo, mhi, tlo, thi;
+};
+__device__ __forceinline__ void acc_zero(Acc& a) { a.mlo = a.mhi = a.tlo = a.thi = 0; }
+__device__ __forceinline__ void add128(uint64_t& lo, uint64_t& hi, uint64_t alo, uint64_t ahi) {
+  lo += alo;
+  hi += ahi + (lo < alo ? 1u : 0u);
+}
+// adds n * w (n < 2^21) where wb are the bits of w in [0, 1]
+__device__ __forceinline__ void acc_add(Acc& a, uint32_t wb, uint32_t n = 1) {
+  wb &= 0x7fffffffu;  // -0.0 is 0
+  if (wb == 0u || n == 0u) return;
+  const uint32_t E = wb >> 23;
+  const uint64_t mant = (uint64_t)((wb & 0x7fffffu) | (E ? 0x800000u : 0u)) * n;  // < 2^45
+  if (E >= 80u) {
+    const uint32_t sh = E - 80u;  // 0..47: mant * 2^(E-150) in units of 2^-70
+    const uint64_t lo = mant << sh;
+    const uint64_t hi = sh ? (mant >> (64 - sh)) : 0ull;
+    add128(a.mlo, a.mhi, lo, hi);
+  } else {
+    const uint32_t sh = E ? E - 1u : 0u;  // 0..78: in units of 2^-149
+    const uint64_t lo = sh < 64 ? (mant << sh) : 0ull;
+    const uint64_t hi = sh == 0 ? 0ull : (sh < 64 ? (mant >> (64 - sh)) : (mant << (sh - 64)));
+    add128(a.tlo, a.thi, lo, hi);
+  }
+}
+__device__ __forceinline__ void acc_merge(Acc& a, const Acc& b) {
+  add128(a.mlo, a.mhi, b.mlo, b.mhi);
+  add128(a.tlo, a.thi, b.tlo, b.thi);
+}
+__device__ __forceinline__ Acc acc_shfl_xor(const Acc& a, int o) {
+  Acc b;
+  b.mlo = __shfl_xor(a.mlo, o, 64);
+  b.mhi = __shfl_xor(a.mhi, o, 64);
+  b.tlo = __shfl_xor(a.tlo, o, 64);
+  b.thi = __shfl_xor(a.thi, o, 64);
+  return b;
+}
+struct AccScratch {
+  Acc w[NW];
+  double s64;
+};
+// RN64 of the accumulated sum (round to nearest, ties to even).
+__device__ inline double acc_rn64(const Acc& a) {
+  // S in units of 2^-149 as a 192-bit integer L2:L1:L0 (the main word is in
+  // units of 2^-70 = 2^79 * 2^-149)
+  uint64_t L0 = a.tlo, L1 = a.thi, L2 = 0;
+  const uint64_t add1 = a.mlo << 15;
+  L1 += add1;
+  L2 += (L1 < add1 ? 1u : 0u) + (a.mlo >> 49) + (a.mhi << 15);
+  int p;  // index of the highest set bit
+  if (L2) p = 128 + 63 - __builtin_clzll(L2);
+  else if (L1) p = 64 + 63 - __builtin_clzll(L1);
+  else if (L0) p = 63 - __builtin_clzll(L0);
+  else return 0.0;
+  auto bit_range = [&](int lo) -> uint64_t {  // 64 bits starting at bit lo (lo >= 0)
+    const uint64_t w[3] = {L0, L1, L2};
+    const int q = lo >> 6, r = lo & 63;
+    uint64_t v = q < 3 ? (w[q] >> r) : 0ull;
+    if (r && q + 1 < 3) v |= w[q + 1] << (64 - r);
+    return v;
+  };
+  if (p <= 52) return __builtin_ldexp((double)L0, -149);  // exact
+  const int sh = p - 52;
+  uint64_t mant = bit_range(sh) & ((1ull << 53) - 1);
+  const uint64_t rb = (bit_range(sh - 1) & 1ull);
+  bool sticky = false;
+  if (sh - 1 > 0) {
+    const int nb = sh - 1;  // bits [0, nb) below the round bit
+    const uint64_t w[3] = {L0, L1, L2};
+    for (int q = 0; q < 3 && q * 64 < nb; ++q) {
+      const int take = nb - q * 64;
+      const uint64_t m = take >= 64 ? ~0ull : ((1ull << take) - 1);
+      if (w[q] & m) sticky = true;
+    }
+  }
+  if (rb && (sticky || (mant & 1ull))) mant += 1;
+  return __builtin_ldexp((double)mant, sh - 149);  // mant may be 2^53: still exact
+}
+// Block-wide exact sum; every thread gets RN64(S).
+__device__ inline double block_acc_rn64(Acc a, AccScratch& s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc_merge(a, acc_shfl_xor(a, o));
+  if (lane_id() == 0) s.w[wave_id()] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Acc t = s.w[0];
+    for (int i = 1; i < NW; ++i) acc_merge(t, s.w[i]);
+    s.s64 = acc_rn64(t);
+  }
+  __syncthreads();
+  const double r = s.s64;
+  __syncthreads();
+  return r;
+}
+
+}  // namespace dspark

@@ -1,0 +1,478 @@
+// libdspark: kernels and the C ABI declared in include/dspark.h.
+//
+// One 1024-thread workgroup owns one V-wide logit row (draft or target) and
+// runs every stage of that row on chip: validity and max, argmax and
+// confidence, the dyadic24 counts (dense or sparse top-k) and the sample.  A
+// second, tiny kernel does the per-request greedy verification.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "dspark.h"
+#include "row_alloc.hpp"
+
+namespace dspark {
+
+struct RowsArgs {
+  const void* draft;
+  int64_t d_stride;  // elements
+  int n_draft;
+  const void* target;
+  int64_t t_stride;
+  int n_target;
+  int V;
+  // draft outputs
+  int32_t* argmax;
+  float* conf;
+  int32_t* row_status;
+  int do_q;
+  const int32_t* topk;
+  int k_max;
+  uint32_t* dense;
+  int32_t* sp_ids;
+  uint32_t* sp_cnt;
+  int32_t* sp_len;
+  const uint32_t* draws;
+  int32_t* sample;
+  // target outputs
+  int32_t* t_argmax;
+  int32_t* t_status;
+};
+
+template <int DT>
+__global__ void __launch_bounds__(BS) rows_kernel(RowsArgs a) {
+  __shared__ RowShared sh;
+  constexpr int ES = DT == DSPARK_BF16 ? 2 : 4;
+  const int b = blockIdx.x;
+  const bool is_draft = b < a.n_draft;
+  const int r = is_draft ? b : b - a.n_draft;
+  const char* base = static_cast<const char*>(is_draft ? a.draft : a.target);
+  const Row<DT> row{base + (size_t)r * (size_t)(is_draft ? a.d_stride : a.t_stride) * ES, a.V};
+  const Stats st = row_stats(row, sh);
+
+  if (!is_draft) {
+    int am = 0;
+    float cf = 0.0f;
+    if (st.status == DSPARK_ST_OK) row_argmax_conf(row, st.m, false, sh, &am, &cf);
+    if (threadIdx.x == 0) {
+      a.t_argmax[r] = st.status == DSPARK_ST_OK ? am : 0;
+      a.t_status[r] = st.status;
+    }
+    return;
+  }
+
+  int status = st.status;
+  int k = 0;
+  uint32_t u = 0;
+  const bool want_s = a.draws != nullptr;
+  if (a.do_q) {
+    k = a.topk ? a.topk[r] : 0;
+    const int kcap = a.k_max < a.V ? a.k_max : a.V;
+    if (status == DSPARK_ST_OK && (k < 0 || k > kcap || (k == 0 && a.dense == nullptr)))
+      status = DSPARK_ST_BAD_TOPK;
+  }
+  if (want_s) {
+    u = a.draws[r];
+    if (status == DSPARK_ST_OK && u >= kMass) status = DSPARK_ST_DRAW_RANGE;
+  }
+  int am = 0;
+  float cf = 0.0f;
+  if (status == DSPARK_ST_OK) row_argmax_conf(row, st.m, a.conf != nullptr, sh, &am, &cf);
+  int tok = 0;
+  const bool dense_row = a.do_q && k == 0 && a.dense != nullptr;
+  uint32_t* drow = dense_row ? a.dense + (size_t)r * (size_t)a.V : nullptr;
+  if (a.do_q && status == DSPARK_ST_OK) {
+    QOut qo;
+    if (k == 0) {
+      qo = dense_q(row, st.m, drow, want_s, u, sh);
+    } else {
+      qo = sparse_q(row, st.m, st.tkey, k, a.sp_ids + (size_t)r * a.k_max,
+                    a.sp_cnt + (size_t)r * a.k_max, a.sp_len + r, want_s, u, sh);
+    }
+    status = qo.status;
+    tok = qo.token;
+  }
+  if (a.do_q) {
+    if (status != DSPARK_ST_OK && dense_row) {  // failed dense rows read as all zero
+      for (int i = threadIdx.x; i < a.V; i += BS) drow[i] = 0u;
+    }
+    if (a.sp_len && (status != DSPARK_ST_OK || k == 0) && threadIdx.x == 0) a.sp_len[r] = 0;
+  }
+  if (threadIdx.x == 0) {
+    const bool ok = status == DSPARK_ST_OK;
+    if (a.argmax) a.argmax[r] = ok ? am : 0;
+    if (a.conf) a.conf[r] = ok ? cf : 0.0f;
+    a.row_status[r] = status;
+    if (a.sample) a.sample[r] = ok ? tok : 0;
+  }
+}
+
+// Greedy verification, one thread per request ("DeepSeek-V4.1 DSpark",
+// "State and sampling contracts"): target row i checks draft position i,
+// row 5 supplies only the bonus.
+__global__ void verify_kernel(int R, int V, const int32_t* dtok, const int32_t* dst,
+                              const int32_t* t_am, const int32_t* t_st, int32_t* acc,
+                              int32_t* bonus, int32_t* rst) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  int status = DSPARK_ST_OK;
+  for (int i = 0; i < DSPARK_N_TARGET; ++i)
+    if (t_st[r * DSPARK_N_TARGET + i] != DSPARK_ST_OK) status = DSPARK_ST_TARGET_INVALID;
+  if (status == DSPARK_ST_OK) {
+    for (int i = 0; i < DSPARK_N_DRAFT; ++i) {
+      const bool valid = dst == nullptr || dst[r * DSPARK_N_DRAFT + i] == DSPARK_ST_OK;
+      const int d = dtok[r * DSPARK_N_DRAFT + i];
+      if (valid && (d < 0 || d >= V)) status = DSPARK_ST_DRAFT_INVALID;
+    }
+  }
+  int n = 0;
+  if (status == DSPARK_ST_OK) {
+    while (n < DSPARK_N_DRAFT) {
+      const bool valid = dst == nullptr || dst[r * DSPARK_N_DRAFT + n] == DSPARK_ST_OK;
+      if (!valid || dtok[r * DSPARK_N_DRAFT + n] != t_am[r * DSPARK_N_TARGET + n]) break;
+      ++n;
+    }
+  }
+  acc[r] = status == DSPARK_ST_OK ? n : 0;
+  bonus[r] = status == DSPARK_ST_OK ? t_am[r * DSPARK_N_TARGET + n] : 0;
+  rst[r] = status;
+}
+
+// Standalone sampling from stored q rows.
+__global__ void __launch_bounds__(BS) sample_kernel(const int32_t* topk, int k_max, const uint32_t* dense,
+                                                    const int32_t* sp_ids, const uint32_t* sp_cnt,
+                                                    const int32_t* sp_len, int V, const uint32_t* draws,
+                                                    int dpr, int32_t* tokens, int32_t* row_status) {
+  __shared__ RowShared sh;
+  const int r = blockIdx.x;
+  int status = row_status[r];
+  const uint32_t* dr = draws + (size_t)r * dpr;
+  int32_t* tk = tokens + (size_t)r * dpr;
+  if (status == DSPARK_ST_OK) {
+    for (int j = 0; j < dpr; ++j)
+      if (dr[j] >= kMass) status = DSPARK_ST_DRAW_RANGE;
+  }
+  const int k = topk ? topk[r] : 0;
+  const int kcap = k_max < V ? k_max : V;
+  if (status == DSPARK_ST_OK && (k < 0 || k > kcap || (k == 0 && !dense) || (k > 0 && !sp_cnt)))
+    status = DSPARK_ST_BAD_TOPK;
+  if (status == DSPARK_ST_OK) {
+    if (k == 0) {
+      const URow cr{const_cast<uint32_t*>(dense) + (size_t)r * V, V};
+      uint64_t s = 0;
+      for (int q = threadIdx.x; q < cr.nvec(); q += BS) {
+        uint32_t c[4];
+        cr.load(q, c);
+        s += (uint64_t)c[0] + c[1] + c[2] + c[3];
+      }
+      s = block_sum<uint64_t>(s, sh.bs);
+      if (s != kMass) status = DSPARK_ST_ALLOC_INCONSISTENT;
+      for (int j = 0; j < dpr && status == DSPARK_ST_OK; ++j) {
+        const int t = block_locate<4>(cr.nvec(), [&](int q, uint32_t (&c)[4]) { cr.load(q, c); }, dr[j], sh);
+        if (threadIdx.x == 0) tk[j] = t;
+      }
+    } else {
+      const int len = sp_len[r];
+      const int i = threadIdx.x;
+      const uint32_t c = (i < len && i < k) ? sp_cnt[(size_t)r * k_max + i] : 0u;
+      uint32_t tot;
+      const uint32_t pre = block_excl_scan<uint32_t>(c, sh.bs, &tot);
+      if (tot != kMass || len < 0 || len > k) status = DSPARK_ST_ALLOC_INCONSISTENT;
+      for (int j = 0; j < dpr && status == DSPARK_ST_OK; ++j) {
+        if (c > 0 && pre <= dr[j] && dr[j] < pre + c) tk[j] = sp_ids[(size_t)r * k_max + i];
+      }
+    }
+  }
+  __syncthreads();
+  if (status != DSPARK_ST_OK) {
+    for (int j = threadIdx.x; j < dpr; j += BS) tk[j] = 0;
+    if (threadIdx.x == 0) row_status[r] = status;
+  }
+}
+
+// Weights-only dense allocation (test entry).
+__global__ void __launch_bounds__(BS) weights_kernel(const float* w, int n, int64_t stride, uint32_t* counts,
+                                                     int32_t* row_status) {
+  __shared__ RowShared sh;
+  const int r = blockIdx.x;
+  const float* wr = w + (size_t)r * stride;
+  uint32_t* cr = counts + (size_t)r * n;
+  uint32_t flags = 0;  // bit0 NaN, bit1 +inf, bit2 < 0 or > 1
+  Acc acc;
+  acc_zero(acc);
+  for (int i = threadIdx.x; i < n; i += BS) {
+    const float x = wr[i];
+    flags |= (x != x) ? 1u : 0u;
+    flags |= (x == __builtin_inff()) ? 2u : 0u;
+    flags |= (x < 0.0f || x > 1.0f) ? 4u : 0u;
+    const uint32_t b = (x >= 0.0f && x <= 1.0f) ? __float_as_uint(x) : 0u;
+    cr[i] = b;
+    acc_add(acc, b);
+  }
+  const uint32_t f = block_max<uint32_t>(flags & 1u, sh.bs) | block_max<uint32_t>(flags & 2u, sh.bs) |
+                     block_max<uint32_t>(flags & 4u, sh.bs);
+  const double s64 = block_acc_rn64(acc, sh.acc);
+  int status = (f & 1u) ? DSPARK_ST_ROW_NAN
+               : (f & 2u) ? DSPARK_ST_ROW_POSINF
+               : (f & 4u) ? DSPARK_ST_BAD_WEIGHT
+                          : DSPARK_ST_OK;
+  __threadfence_block();
+  __syncthreads();
+  if (status == DSPARK_ST_OK) status = dense_alloc(URow{cr, n}, s64, false, 0, sh).status;
+  if (status != DSPARK_ST_OK)
+    for (int i = threadIdx.x; i < n; i += BS) cr[i] = 0u;
+  if (threadIdx.x == 0) row_status[r] = status;
+}
+
+__global__ void cr_exp_kernel(const float* d, float* w, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) w[i] = cr_expf(d[i]);
+}
+
+}  // namespace dspark
+
+// ===================================================================== ABI
+using namespace dspark;
+
+namespace {
+thread_local char g_err[512];
+
+int fail(int code, const char* msg) {
+  std::snprintf(g_err, sizeof g_err, "%s", msg);
+  return code;
+}
+
+int check_launch() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    std::snprintf(g_err, sizeof g_err, "HIP launch failed: %s", hipGetErrorString(e));
+    return DSPARK_EHIP;
+  }
+  g_err[0] = 0;
+  return DSPARK_SUCCESS;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_rows(const dspark_rows* r, const char* what) {
+  if (!r) return fail(DSPARK_EINVAL, what);
+  if (r->dtype != DSPARK_F32 && r->dtype != DSPARK_BF16) return fail(DSPARK_EINVAL, "dtype must be F32 or BF16");
+  if (r->n_rows < 0 || r->n_rows > (1 << 24)) return fail(DSPARK_EINVAL, "n_rows out of range");
+  if (r->vocab < 1 || r->vocab > DSPARK_V_MAX) return fail(DSPARK_EINVAL, "vocab must be in [1, DSPARK_V_MAX]");
+  if (r->row_stride < r->vocab) return fail(DSPARK_EINVAL, "row_stride < vocab");
+  if (r->n_rows > 0 && !r->data) return fail(DSPARK_EINVAL, "NULL row data");
+  const int es = r->dtype == DSPARK_BF16 ? 2 : 4;
+  if (!aligned16(r->data) || ((r->row_stride * es) & 15) != 0)
+    return fail(DSPARK_EALIGN, "rows must start 16-byte aligned (data and row_stride * element size)");
+  return DSPARK_SUCCESS;
+}
+
+int check_q(const dspark_q* q, int64_t vocab) {
+  if (!q) return DSPARK_SUCCESS;
+  if (q->k_max < 0 || q->k_max > DSPARK_K_MAX) return fail(DSPARK_EINVAL, "k_max must be in [0, DSPARK_K_MAX]");
+  if (!q->topk && !q->dense) return fail(DSPARK_EINVAL, "all rows dense but q->dense is NULL");
+  if (q->topk && q->k_max > 0 && (!q->sp_ids || !q->sp_cnt || !q->sp_len))
+    return fail(DSPARK_EINVAL, "sparse rows need sp_ids, sp_cnt and sp_len");
+  (void)vocab;
+  return DSPARK_SUCCESS;
+}
+
+int launch_rows(const RowsArgs& a, int dtype, void* stream) {
+  const int nblk = a.n_draft + a.n_target;
+  if (nblk == 0) return DSPARK_SUCCESS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == DSPARK_BF16)
+    hipLaunchKernelGGL(rows_kernel<DSPARK_BF16>, dim3(nblk), dim3(BS), 0, s, a);
+  else
+    hipLaunchKernelGGL(rows_kernel<DSPARK_F32>, dim3(nblk), dim3(BS), 0, s, a);
+  return check_launch();
+}
+
+RowsArgs rows_args_draft(const dspark_rows* d) {
+  RowsArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.draft = d->data;
+  a.d_stride = d->row_stride;
+  a.n_draft = (int)d->n_rows;
+  a.V = (int)d->vocab;
+  return a;
+}
+
+void set_q(RowsArgs& a, const dspark_q* q) {
+  if (!q) return;
+  a.do_q = 1;
+  a.topk = q->topk;
+  a.k_max = q->k_max;
+  a.dense = q->dense;
+  a.sp_ids = q->sp_ids;
+  a.sp_cnt = q->sp_cnt;
+  a.sp_len = q->sp_len;
+}
+}  // namespace
+
+extern "C" {
+
+int32_t dspark_abi_version(void) { return DSPARK_ABI_VERSION; }
+const char* dspark_q_semantic_id(void) { return "dyadic24-standard-v1"; }
+const char* dspark_last_error(void) { return g_err; }
+
+const char* dspark_status_name(int32_t code) {
+  switch (code) {
+    case DSPARK_ST_OK: return "OK";
+    case DSPARK_ST_ROW_NAN: return "ROW_NAN";
+    case DSPARK_ST_ROW_POSINF: return "ROW_POSINF";
+    case DSPARK_ST_ROW_ZERO_MASS: return "ROW_ZERO_MASS";
+    case DSPARK_ST_DRAW_RANGE: return "DRAW_RANGE";
+    case DSPARK_ST_ALLOC_INCONSISTENT: return "ALLOC_INCONSISTENT";
+    case DSPARK_ST_TARGET_INVALID: return "TARGET_INVALID";
+    case DSPARK_ST_DRAFT_INVALID: return "DRAFT_INVALID";
+    case DSPARK_ST_BAD_WEIGHT: return "BAD_WEIGHT";
+    case DSPARK_ST_BAD_TOPK: return "BAD_TOPK";
+    default: return "UNKNOWN";
+  }
+}
+
+size_t dspark_workspace_bytes(int32_t op, int64_t n_rows, int64_t vocab, int32_t k_max) {
+  (void)op; (void)n_rows; (void)vocab; (void)k_max;
+  return 0;
+}
+
+int dspark_propose(const dspark_rows* draft, int32_t* argmax, float* conf, int32_t* row_status,
+                   void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  int rc = check_rows(draft, "draft rows NULL");
+  if (rc) return rc;
+  if (draft->n_rows > 0 && (!argmax || !conf || !row_status)) return fail(DSPARK_EINVAL, "NULL output");
+  RowsArgs a = rows_args_draft(draft);
+  a.argmax = argmax;
+  a.conf = conf;
+  a.row_status = row_status;
+  return launch_rows(a, draft->dtype, stream);
+}
+
+int dspark_q_alloc(const dspark_rows* draft, const dspark_q* q, int32_t* row_status, void* ws,
+                   size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  int rc = check_rows(draft, "draft rows NULL");
+  if (rc) return rc;
+  if (!q) return fail(DSPARK_EINVAL, "q NULL");
+  if ((rc = check_q(q, draft->vocab))) return rc;
+  if (draft->n_rows > 0 && !row_status) return fail(DSPARK_EINVAL, "NULL row_status");
+  RowsArgs a = rows_args_draft(draft);
+  a.row_status = row_status;
+  set_q(a, q);
+  return launch_rows(a, draft->dtype, stream);
+}
+
+int dspark_sample(const dspark_q* q, int64_t n_rows, int64_t vocab, const uint32_t* draws,
+                  int64_t draws_per_row, int32_t* tokens, int32_t* row_status, void* stream) {
+  if (!q) return fail(DSPARK_EINVAL, "q NULL");
+  int rc = check_q(q, vocab);
+  if (rc) return rc;
+  if (n_rows < 0 || vocab < 1 || vocab > DSPARK_V_MAX || draws_per_row < 1 || draws_per_row > (1 << 20))
+    return fail(DSPARK_EINVAL, "bad n_rows, vocab or draws_per_row");
+  if (n_rows == 0) return DSPARK_SUCCESS;
+  if (!draws || !tokens || !row_status) return fail(DSPARK_EINVAL, "NULL draws, tokens or row_status");
+  hipLaunchKernelGGL(sample_kernel, dim3((unsigned)n_rows), dim3(BS), 0, static_cast<hipStream_t>(stream),
+                     q->topk, q->k_max, q->dense, q->sp_ids, q->sp_cnt, q->sp_len, (int)vocab, draws,
+                     (int)draws_per_row, tokens, row_status);
+  return check_launch();
+}
+
+static int launch_verify(int64_t R, int V, const int32_t* dtok, const int32_t* dst, const int32_t* t_am,
+                         const int32_t* t_st, int32_t* acc, int32_t* bonus, int32_t* rst, void* stream) {
+  if (R == 0) return DSPARK_SUCCESS;
+  const int tpb = 256;
+  hipLaunchKernelGGL(verify_kernel, dim3((unsigned)((R + tpb - 1) / tpb)), dim3(tpb), 0,
+                     static_cast<hipStream_t>(stream), (int)R, V, dtok, dst, t_am, t_st, acc, bonus, rst);
+  return check_launch();
+}
+
+int dspark_verify_greedy(const dspark_rows* target, const int32_t* draft_tokens,
+                         const int32_t* draft_status, int64_t n_requests, int32_t* target_argmax,
+                         int32_t* target_status, int32_t* accept_len, int32_t* bonus,
+                         int32_t* req_status, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  int rc = check_rows(target, "target rows NULL");
+  if (rc) return rc;
+  if (n_requests < 0 || target->n_rows != n_requests * DSPARK_N_TARGET)
+    return fail(DSPARK_EINVAL, "target must hold 6 rows per request");
+  if (n_requests > 0 && (!draft_tokens || !target_argmax || !target_status || !accept_len || !bonus || !req_status))
+    return fail(DSPARK_EINVAL, "NULL argument");
+  RowsArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.target = target->data;
+  a.t_stride = target->row_stride;
+  a.n_target = (int)target->n_rows;
+  a.V = (int)target->vocab;
+  a.t_argmax = target_argmax;
+  a.t_status = target_status;
+  if ((rc = launch_rows(a, target->dtype, stream))) return rc;
+  return launch_verify(n_requests, (int)target->vocab, draft_tokens, draft_status, target_argmax, target_status,
+                       accept_len, bonus, req_status, stream);
+}
+
+int dspark_fused(const dspark_rows* draft, const dspark_rows* target, int32_t mode,
+                 const dspark_q* q, const uint32_t* draws, int32_t* argmax, float* conf,
+                 int32_t* sample, int32_t* row_status, int32_t* target_argmax,
+                 int32_t* target_status, int32_t* accept_len, int32_t* bonus, int32_t* req_status,
+                 void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  int rc = check_rows(draft, "draft rows NULL");
+  if (rc) return rc;
+  if ((rc = check_rows(target, "target rows NULL"))) return rc;
+  if (draft->dtype != target->dtype || draft->vocab != target->vocab)
+    return fail(DSPARK_EINVAL, "draft and target rows must share dtype and vocab");
+  if (draft->n_rows % DSPARK_N_DRAFT != 0) return fail(DSPARK_EINVAL, "draft must hold 5 rows per request");
+  const int64_t R = draft->n_rows / DSPARK_N_DRAFT;
+  if (target->n_rows != R * DSPARK_N_TARGET) return fail(DSPARK_EINVAL, "target must hold 6 rows per request");
+  if (mode != DSPARK_GREEDY && mode != DSPARK_SAMPLED) return fail(DSPARK_EINVAL, "bad mode");
+  if (mode == DSPARK_SAMPLED && (!q || !draws || !sample))
+    return fail(DSPARK_EINVAL, "sampled mode needs q, draws and sample");
+  if ((draws == nullptr) != (sample == nullptr)) return fail(DSPARK_EINVAL, "draws and sample go together");
+  if (draws && !q) return fail(DSPARK_EINVAL, "sampling needs q");
+  if ((rc = check_q(q, draft->vocab))) return rc;
+  if (R > 0 && (!argmax || !conf || !row_status || !target_argmax || !target_status || !accept_len || !bonus ||
+                !req_status))
+    return fail(DSPARK_EINVAL, "NULL output");
+  RowsArgs a = rows_args_draft(draft);
+  a.argmax = argmax;
+  a.conf = conf;
+  a.row_status = row_status;
+  set_q(a, q);
+  a.draws = draws;
+  a.sample = sample;
+  a.target = target->data;
+  a.t_stride = target->row_stride;
+  a.n_target = (int)target->n_rows;
+  a.t_argmax = target_argmax;
+  a.t_status = target_status;
+  if ((rc = launch_rows(a, draft->dtype, stream))) return rc;
+  const int32_t* dtok = mode == DSPARK_SAMPLED ? sample : argmax;
+  return launch_verify(R, (int)draft->vocab, dtok, row_status, target_argmax, target_status, accept_len, bonus,
+                       req_status, stream);
+}
+
+int dspark_q_alloc_weights(const float* w, int64_t n_rows, int64_t n, int64_t stride, uint32_t* counts,
+                           int32_t* row_status, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (n_rows < 0 || n < 1 || n > DSPARK_V_MAX || stride < n) return fail(DSPARK_EINVAL, "bad sizes");
+  if (n_rows == 0) return DSPARK_SUCCESS;
+  if (!w || !counts || !row_status) return fail(DSPARK_EINVAL, "NULL argument");
+  hipLaunchKernelGGL(weights_kernel, dim3((unsigned)n_rows), dim3(BS), 0, static_cast<hipStream_t>(stream), w,
+                     (int)n, stride, counts, row_status);
+  return check_launch();
+}
+
+int dspark_cr_expf(const float* d, float* w, int64_t n, void* stream) {
+  if (n < 0) return fail(DSPARK_EINVAL, "n < 0");
+  if (n == 0) return DSPARK_SUCCESS;
+  if (!d || !w) return fail(DSPARK_EINVAL, "NULL argument");
+  const int tpb = 256;
+  hipLaunchKernelGGL(cr_exp_kernel, dim3((unsigned)((n + tpb - 1) / tpb)), dim3(tpb), 0,
+                     static_cast<hipStream_t>(stream), d, w, n);
+  return check_launch();
+}
+
+}  // extern "C"

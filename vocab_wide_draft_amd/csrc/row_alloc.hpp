@@ -1,0 +1,477 @@
+// Row statistics, argmax / confidence, and the dyadic24 allocation of one row
+// ("PP1 q transport and scheduling design", "Distribution contract and
+// precision": FP32-rounded weights, exact normalisation, floor plus largest
+// remainders with lowest-ID ties, FP64 allocation arithmetic, the
+// 0 <= remaining < M and exact-sum assertions, sparse top-k support
+// normalised within the support, sampling by the first cumulative count
+// strictly greater than a 24-bit draw).
+#pragma once
+#include "row_algos.hpp"
+
+namespace dspark {
+
+// --------------------------------------------------------- statistics
+struct Stats {
+  float m;        // row maximum (IEEE, NaN ignored)
+  int status;     // DSPARK_ST_OK / ROW_NAN / ROW_POSINF / ROW_ZERO_MASS
+  uint32_t tkey;  // key of this thread's largest element (0 if it has none)
+};
+
+// Validity per "Distribution contract and precision": NaN first, then +inf,
+// then a row with no finite entry (all -inf) has zero mass.
+template <int DT>
+__device__ Stats row_stats(const Row<DT>& row, RowShared& sh) {
+  constexpr int EPV = Row<DT>::EPV;
+  const int nvec = row.nvec();
+  float mx = -__builtin_inff();
+  uint32_t flags = 0;  // bit0 NaN, bit1 +inf, bit2 any element
+  for (int q = threadIdx.x; q < nvec; q += BS) {
+    float x[EPV];
+    const int nv = row.load(q, x);
+#pragma unroll
+    for (int l = 0; l < EPV; ++l) {
+      if (l < nv) {
+        flags |= (x[l] != x[l]) ? 1u : 0u;
+        flags |= (x[l] == __builtin_inff()) ? 2u : 0u;
+        mx = __builtin_fmaxf(mx, x[l]);
+      }
+    }
+    flags |= 4u;
+  }
+  Stats s;
+  s.tkey = (flags & 4u) ? key32(mx) : 0u;
+  const float m = block_max<float>(mx, sh.bs);
+  const uint32_t f = block_max<uint32_t>(flags & 1u, sh.bs) | block_max<uint32_t>(flags & 2u, sh.bs);
+  s.m = m;
+  s.status = (f & 1u) ? DSPARK_ST_ROW_NAN
+             : (f & 2u) ? DSPARK_ST_ROW_POSINF
+             : (m == -__builtin_inff()) ? DSPARK_ST_ROW_ZERO_MASS
+                                        : DSPARK_ST_OK;
+  return s;
+}
+
+// Lowest index with x == m (greedy argmax, lowest index on ties) and, if
+// want_conf, the softmax probability of the maximum 1 / sum_v exp(x_v - m).
+template <int DT>
+__device__ void row_argmax_conf(const Row<DT>& row, float m, bool want_conf, RowShared& sh, int* am,
+                                float* conf) {
+  constexpr int EPV = Row<DT>::EPV;
+  const int nvec = row.nvec();
+  int first = 0x7fffffff;
+  double sum = 0.0;
+  for (int q = threadIdx.x; q < nvec; q += BS) {
+    float x[EPV];
+    const int nv = row.load(q, x);
+    float part = 0.0f;
+#pragma unroll
+    for (int l = 0; l < EPV; ++l) {
+      if (l < nv) {
+        if (x[l] == m && first == 0x7fffffff) first = q * EPV + l;
+        if (want_conf) part += __builtin_amdgcn_exp2f((x[l] - m) * 1.4426950408889634f);
+      }
+    }
+    sum += (double)part;
+  }
+  *am = block_min<int>(first, sh.bs);
+  if (want_conf) {
+    const double s = block_sum<double>(sum, sh.bs);
+    *conf = (float)(1.0 / s);
+  }
+}
+
+// k-th largest (k >= 1) of one uint32 per thread, radix select by bytes.
+__device__ inline uint32_t block_kth_largest(uint32_t v, int k, RowShared& sh) {
+  uint32_t prefix = 0, pmask = 0;
+  uint64_t need = (uint64_t)k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = threadIdx.x; b < 256; b += BS) sh.hist[b] = 0;
+    __syncthreads();
+    if ((v & pmask) == prefix) atomicAdd(&sh.hist[(v >> shift) & 255u], 1u);
+    __syncthreads();
+    uint64_t before;
+    const int d = block_find_crossing(sh.hist, 256, need, false, sh, &before);
+    need -= before;
+    prefix |= (uint32_t)d << shift;
+    pmask |= 0xffu << shift;
+  }
+  return prefix;
+}
+
+// ------------------------------------------------------ q of one row
+struct QOut {
+  int status;
+  int token;  // sample (valid when status OK and sampling asked)
+};
+
+// y = RN64(w / S64) * 2^24 -> floor count and exact remainder
+__device__ __forceinline__ void floor_rem(float w, double s64, uint32_t& c, double& r) {
+  const double y = ((double)w / s64) * 16777216.0;
+  const double f = __builtin_floor(y);
+  c = (uint32_t)f;
+  r = y - f;
+}
+
+// Finishes a threshold inside one bucket of the remainder keys when the
+// bucket holds at most kCandCap elements: collects them (key, id) in LDS and
+// selects there, ties to the lowest id.  keyfn(q, keys[4], ok[4]) gives the
+// remainder keys of count-row vector q (ok = positive remainder).
+template <class KEYS>
+__device__ Thr finish_in_lds(const URow& out, KEYS keyfn, uint64_t prefix, uint64_t pmask,
+                             uint64_t need, RowShared& sh, int* cut) {
+  if (threadIdx.x == 0) sh.bi[4] = 0;
+  __syncthreads();
+  const int nvec = out.nvec();
+  for (int q = threadIdx.x; q < nvec; q += BS) {
+    uint64_t key[4];
+    bool ok[4];
+    keyfn(q, key, ok);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      if (ok[l] && (key[l] & pmask) == prefix) {
+        const int pos = atomicAdd(&sh.bi[4], 1);
+        if (pos < kCandCap) {
+          sh.ckey[pos] = key[l];
+          sh.cid[pos] = (uint32_t)(q * 4 + l);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int n = sh.bi[4] < kCandCap ? sh.bi[4] : kCandCap;
+  __syncthreads();
+  Thr t = lds_threshold(sh.ckey, n, need, sh);
+  if (t.all_ge) return t;
+  // tie group: keep the need_t lowest ids -> threshold on (2^32-1 - id)
+  uint64_t mine[2];
+  int nm = 0;
+  for (int e = threadIdx.x; e < n; e += BS)
+    if (sh.ckey[e] == t.T) mine[nm++] = 0xffffffffull - sh.cid[e];
+  __syncthreads();
+  if (threadIdx.x == 0) sh.bi[4] = 0;
+  __syncthreads();
+  for (int i = 0; i < nm; ++i) sh.ckey[atomicAdd(&sh.bi[4], 1)] = mine[i];
+  __syncthreads();
+  const int ntie = sh.bi[4];
+  __syncthreads();
+  const Thr ti = lds_threshold(sh.ckey, ntie, t.need_t, sh);  // ids are unique -> all_ge
+  *cut = (int)(0xffffffffull - ti.T);
+  return t;
+}
+
+// Dense allocation on a count row that holds the binary32 weight bits
+// (written by the caller); S64 = RN64(sum of weights).  Overwrites the row
+// with the counts.  Used for logit rows and for the weights-only entry.
+__device__ QOut dense_alloc(const URow& out, double s64, bool want_s, uint32_t u, RowShared& sh) {
+  QOut res{DSPARK_ST_OK, 0};
+  if (!(s64 > 0.0)) {
+    res.status = DSPARK_ST_ROW_ZERO_MASS;
+    return res;
+  }
+  const int nvec = out.nvec();
+  for (int b = threadIdx.x; b < kHistBins; b += BS) sh.hist[b] = 0;
+  __syncthreads();
+  uint64_t csum = 0;
+  uint32_t npos = 0;
+  for (int q = threadIdx.x; q < nvec; q += BS) {
+    uint32_t w[4];
+    const int nv = out.load(q, w);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      if (l < nv) {
+        uint32_t c;
+        double r;
+        floor_rem(__uint_as_float(w[l]), s64, c, r);
+        csum += c;
+        if (r > 0.0) {
+          ++npos;
+          atomicAdd(&sh.hist[rem_key(r) >> 52], 1u);
+        }
+      }
+    }
+  }
+  csum = block_sum<uint64_t>(csum, sh.bs);
+  npos = block_sum<uint32_t>(npos, sh.bs);
+  const int64_t remaining = (int64_t)kMass - (int64_t)csum;
+  if (remaining < 0 || remaining >= (int64_t)kMass || remaining > (int64_t)npos) {
+    res.status = DSPARK_ST_ALLOC_INCONSISTENT;
+    return res;
+  }
+  auto keyfn = [&](int q, uint64_t (&key)[4], bool (&ok)[4]) {
+    uint32_t w[4];
+    const int nv = out.load(q, w);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      uint32_t c;
+      double r;
+      floor_rem(__uint_as_float(w[l]), s64, c, r);
+      ok[l] = l < nv && r > 0.0;
+      key[l] = ok[l] ? rem_key(r) : 0ull;
+    }
+  };
+  Thr thr{~0ull, 0, false};  // selects nothing
+  int cut = -1;
+  if (remaining > 0) {
+    uint64_t before;
+    const int b = block_find_crossing(sh.hist, kHistBins, (uint64_t)remaining, false, sh, &before);
+    uint64_t need = (uint64_t)remaining - before;
+    uint32_t cnt = sh.hist[b];
+    uint64_t prefix = (uint64_t)b << 52, pmask = 0xfffull << 52;
+    __syncthreads();
+    if (cnt == need) {
+      thr = Thr{prefix, need, true};
+    } else {
+      // refine the bucket by 12-bit digits until it is small or exhausted
+      int shift = 52;
+      bool done = false;
+      while (!done) {
+        if (cnt <= (uint32_t)kCandCap) {
+          thr = finish_in_lds(out, keyfn, prefix, pmask, need, sh, &cut);
+          done = true;
+          break;
+        }
+        if (shift == 0) {  // one exact key shared by more than kCandCap elements
+          const uint64_t T = prefix;
+          cut = block_locate<4>(nvec, [&](int q, uint32_t (&wt)[4]) {
+            uint64_t key[4];
+            bool ok[4];
+            keyfn(q, key, ok);
+#pragma unroll
+            for (int l = 0; l < 4; ++l) wt[l] = (ok[l] && key[l] == T) ? 1u : 0u;
+          }, need - 1, sh);
+          thr = Thr{T, need, false};
+          done = true;
+          break;
+        }
+        const int nsh = shift >= 12 ? shift - 12 : 0;
+        const int nbits = shift - nsh;
+        for (int bb = threadIdx.x; bb < kHistBins; bb += BS) sh.hist[bb] = 0;
+        __syncthreads();
+        for (int q = threadIdx.x; q < nvec; q += BS) {
+          uint64_t key[4];
+          bool ok[4];
+          keyfn(q, key, ok);
+#pragma unroll
+          for (int l = 0; l < 4; ++l)
+            if (ok[l] && (key[l] & pmask) == prefix)
+              atomicAdd(&sh.hist[(key[l] >> nsh) & ((1u << nbits) - 1u)], 1u);
+        }
+        __syncthreads();
+        const int d = block_find_crossing(sh.hist, 1 << nbits, need, false, sh, &before);
+        need -= before;
+        cnt = sh.hist[d];
+        __syncthreads();
+        prefix |= (uint64_t)d << nsh;
+        pmask |= (uint64_t)((1u << nbits) - 1u) << nsh;
+        shift = nsh;
+        if (cnt == need) {
+          thr = Thr{prefix, need, true};
+          done = true;
+        }
+      }
+    }
+  }
+  // final pass: counts = floor + selection
+  uint64_t fsum = 0;
+  for (int q = threadIdx.x; q < nvec; q += BS) {
+    uint32_t w[4];
+    const int nv = out.load(q, w);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      uint32_t c;
+      double r;
+      floor_rem(__uint_as_float(w[l]), s64, c, r);
+      if (l < nv && r > 0.0) {
+        const uint64_t key = rem_key(r);
+        const int id = q * 4 + l;
+        const bool sel = key > thr.T || (key == thr.T && (thr.all_ge || id <= cut));
+        c += sel ? 1u : 0u;
+      }
+      w[l] = c;
+      fsum += l < nv ? c : 0u;
+    }
+    out.store(q, w, nv);
+  }
+  fsum = block_sum<uint64_t>(fsum, sh.bs);
+  if (fsum != kMass) {
+    res.status = DSPARK_ST_ALLOC_INCONSISTENT;
+    return res;
+  }
+  __threadfence_block();
+  __syncthreads();
+  if (want_s) {
+    res.token = block_locate<4>(nvec, [&](int q, uint32_t (&c)[4]) { out.load(q, c); }, u, sh);
+    if (res.token < 0) res.status = DSPARK_ST_ALLOC_INCONSISTENT;
+  }
+  return res;
+}
+
+// Dense q of a logit row: weights written into the count row, exact sum,
+// then dense_alloc.
+template <int DT>
+__device__ QOut dense_q(const Row<DT>& row, float m, uint32_t* drow, bool want_s, uint32_t u,
+                        RowShared& sh) {
+  constexpr int EPV = Row<DT>::EPV;
+  const URow out{drow, row.V};
+  const int nvec = row.nvec();
+  Acc acc;
+  acc_zero(acc);
+  for (int q = threadIdx.x; q < nvec; q += BS) {
+    float x[EPV];
+    const int nv = row.load(q, x);
+    uint32_t wb[EPV];
+#pragma unroll
+    for (int l = 0; l < EPV; ++l) {
+      const float w = cr_expf(x[l] - m);  // x = -inf (or past V) gives 0
+      wb[l] = __float_as_uint(w);
+      if (l < nv) acc_add(acc, wb[l]);
+    }
+    if (nv == EPV && out.vec_ok()) {
+      uint4* dst = reinterpret_cast<uint4*>(drow + (size_t)q * EPV);
+#pragma unroll
+      for (int v = 0; v < EPV / 4; ++v) dst[v] = make_uint4(wb[4 * v], wb[4 * v + 1], wb[4 * v + 2], wb[4 * v + 3]);
+    } else {
+      for (int l = 0; l < nv; ++l) drow[(size_t)q * EPV + l] = wb[l];
+    }
+  }
+  const double s64 = block_acc_rn64(acc, sh.acc);
+  __threadfence_block();
+  __syncthreads();
+  return dense_alloc(out, s64, want_s, u, sh);
+}
+
+// Sparse top-k q ("Sparse support ... follow-up": global support first,
+// normalised within it, zero-count entries dropped, ascending ids).
+template <int DT>
+__device__ QOut sparse_q(const Row<DT>& row, float m, uint32_t tkey, int k, int32_t* ids_out,
+                         uint32_t* cnt_out, int32_t* len_out, bool want_s, uint32_t u, RowShared& sh) {
+  constexpr int EPV = Row<DT>::EPV;
+  QOut res{DSPARK_ST_OK, 0};
+  const int nvec = row.nvec();
+  const uint32_t Km = key32(m);
+  // 1. a lower bound for the k-th largest key: the k-th largest per-thread max
+  uint32_t lo = block_kth_largest(tkey, k, sh);
+  uint32_t hi = Km;
+  uint64_t need = (uint64_t)k;
+  uint32_t kthr;
+  bool all_ge = false;
+  int cut = 0x7fffffff;
+  // 2. histograms of (hi - key) over [lo, hi], narrowed until exact
+  for (;;) {
+    const uint32_t range = hi - lo;
+    const int shift = range < (uint32_t)kHistBins ? 0 : (32 - __builtin_clz(range)) - 12;
+    const int nb = (int)(range >> shift) + 1;
+    for (int b = threadIdx.x; b < nb; b += BS) sh.hist[b] = 0;
+    __syncthreads();
+    for (int q = threadIdx.x; q < nvec; q += BS) {
+      float x[EPV];
+      const int nv = row.load(q, x);
+#pragma unroll
+      for (int l = 0; l < EPV; ++l) {
+        const uint32_t K = key32(x[l]);
+        if (l < nv && K >= lo && K <= hi) atomicAdd(&sh.hist[(hi - K) >> shift], 1u);
+      }
+    }
+    __syncthreads();
+    uint64_t before;
+    const int b = block_find_crossing(sh.hist, nb, need, true, sh, &before);
+    need -= before;
+    const uint32_t cnt = sh.hist[b];
+    __syncthreads();
+    const uint32_t bhi = hi - ((uint32_t)b << shift);
+    const uint32_t width = (1u << shift) - 1u;
+    const uint32_t blo = (bhi - lo) > width ? bhi - width : lo;
+    if (cnt == need) {
+      kthr = blo;
+      all_ge = true;
+      break;
+    }
+    if (shift == 0) {
+      kthr = bhi;
+      const uint32_t T = bhi;
+      cut = block_locate<EPV>(nvec, [&](int q, uint32_t (&wt)[EPV]) {
+        float x[EPV];
+        const int nv = row.load(q, x);
+#pragma unroll
+        for (int l = 0; l < EPV; ++l) wt[l] = (l < nv && key32(x[l]) == T) ? 1u : 0u;
+      }, need - 1, sh);
+      break;
+    }
+    hi = bhi;
+    lo = blo;
+  }
+  // 3. support in ascending id order
+  const int n = block_compact(row, [&](int q, const float (&x)[EPV], int nv) -> uint32_t {
+    uint32_t msk = 0;
+#pragma unroll
+    for (int l = 0; l < EPV; ++l) {
+      const uint32_t K = key32(x[l]);
+      const bool s = l < nv && (K > kthr || (K == kthr && (all_ge || q * EPV + l <= cut)));
+      msk |= s ? (1u << l) : 0u;
+    }
+    return msk;
+  }, DSPARK_K_MAX, sh);
+  // 4. weights, exact sum, floors
+  const int j = threadIdx.x;
+  const bool have = j < n;
+  float w = 0.0f;
+  Acc acc;
+  acc_zero(acc);
+  if (have) {
+    w = cr_expf(sh.sx[j] - m);
+    acc_add(acc, __float_as_uint(w));
+  }
+  const double s64 = block_acc_rn64(acc, sh.acc);
+  uint32_t c = 0;
+  double r = 0.0;
+  if (have) floor_rem(w, s64, c, r);
+  const bool pos = have && r > 0.0;
+  const uint64_t key = pos ? rem_key(r) : 0ull;
+  sh.ckey[j] = key;
+  const uint64_t csum = block_sum<uint64_t>(c, sh.bs);
+  const uint32_t npos = block_sum<uint32_t>(pos ? 1u : 0u, sh.bs);
+  const int64_t remaining = (int64_t)kMass - (int64_t)csum;
+  if (!(s64 > 0.0)) {
+    res.status = DSPARK_ST_ROW_ZERO_MASS;
+    return res;
+  }
+  if (remaining < 0 || remaining >= (int64_t)kMass || remaining > (int64_t)npos) {
+    res.status = DSPARK_ST_ALLOC_INCONSISTENT;
+    return res;
+  }
+  // 5. largest remainders, ties to the lowest id (= support order)
+  if (remaining > 0) {
+    const Thr t = lds_threshold(sh.ckey, n, (uint64_t)remaining, sh);
+    const uint32_t tie = (pos && !t.all_ge && key == t.T) ? 1u : 0u;
+    uint32_t ntie;
+    const uint32_t rank = block_excl_scan<uint32_t>(tie, sh.bs, &ntie);
+    const bool sel = pos && (key > t.T || (key == t.T && (t.all_ge || rank < t.need_t)));
+    c += sel ? 1u : 0u;
+  }
+  const uint64_t fsum = block_sum<uint64_t>(c, sh.bs);
+  if (fsum != kMass) {
+    res.status = DSPARK_ST_ALLOC_INCONSISTENT;
+    return res;
+  }
+  // 6. positive entries in id order, and the sample
+  uint32_t len;
+  const uint32_t slot = block_excl_scan<uint32_t>(c > 0 ? 1u : 0u, sh.bs, &len);
+  if (c > 0) {
+    ids_out[slot] = (int32_t)sh.cid[j];
+    cnt_out[slot] = c;
+  }
+  if (threadIdx.x == 0) *len_out = (int32_t)len;
+  if (want_s) {
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan<uint32_t>(c, sh.bs, &tot);
+    if (threadIdx.x == 0) sh.bi[5] = -1;
+    __syncthreads();
+    if (c > 0 && pre <= u && u < pre + c) sh.bi[5] = (int)sh.cid[j];
+    __syncthreads();
+    res.token = sh.bi[5];
+    __syncthreads();
+    if (res.token < 0) res.status = DSPARK_ST_ALLOC_INCONSISTENT;
+  }
+  return res;
+}
+
+}  // namespace dspark
