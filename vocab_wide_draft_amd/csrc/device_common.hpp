@@ -20,11 +20,27 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // ---------------------------------------------------------------- wave ops
+// 32-bit sum over the 64 lanes with DPP moves (quad swaps, half-row and row
+// mirrors, then the row broadcasts of lanes 15 and 31); lane 63 ends with the
+// total, which is read back as a scalar.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xb1, 0xf, 0xf, false);   // quad_perm 1,0,3,2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4e, 0xf, 0xf, false);   // quad_perm 2,3,0,1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xf, 0xf, false);  // row_half_mirror
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xf, 0xf, false);  // row_mirror
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
 template <class T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
+}
+template <>
+__device__ __forceinline__ uint32_t wave_sum<uint32_t>(uint32_t v) {
+  return wave_sum_u32(v);
 }
 template <class T>
 __device__ __forceinline__ T wave_max(T v) {
@@ -63,7 +79,7 @@ struct BlockScratch {
 
 // Block reductions: every thread calls, every thread gets the result.
 template <class T>
-__device__ T block_sum(T v, BlockScratch& s) {
+__device__ __forceinline__ T block_sum(T v, BlockScratch& s) {
   v = wave_sum(v);
   if (lane_id() == 0) reinterpret_cast<T*>(s.w)[wave_id()] = v;
   __syncthreads();
@@ -78,7 +94,7 @@ __device__ T block_sum(T v, BlockScratch& s) {
   return r;
 }
 template <class T>
-__device__ T block_max(T v, BlockScratch& s) {
+__device__ __forceinline__ T block_max(T v, BlockScratch& s) {
   v = wave_max(v);
   if (lane_id() == 0) reinterpret_cast<T*>(s.w)[wave_id()] = v;
   __syncthreads();
@@ -93,7 +109,7 @@ __device__ T block_max(T v, BlockScratch& s) {
   return r;
 }
 template <class T>
-__device__ T block_min(T v, BlockScratch& s) {
+__device__ __forceinline__ T block_min(T v, BlockScratch& s) {
   v = wave_min(v);
   if (lane_id() == 0) reinterpret_cast<T*>(s.w)[wave_id()] = v;
   __syncthreads();
@@ -109,7 +125,7 @@ __device__ T block_min(T v, BlockScratch& s) {
 }
 // Exclusive prefix sum over threads in threadIdx order; *total gets the sum.
 template <class T>
-__device__ T block_excl_scan(T v, BlockScratch& s, T* total) {
+__device__ __forceinline__ T block_excl_scan(T v, BlockScratch& s, T* total) {
   T inc = wave_incl_scan(v);
   if (lane_id() == 63) reinterpret_cast<T*>(s.w)[wave_id()] = inc;
   __syncthreads();
@@ -256,11 +272,11 @@ __device__ inline double acc_rn64(const Acc& a) {
   else if (L1) p = 64 + 63 - __builtin_clzll(L1);
   else if (L0) p = 63 - __builtin_clzll(L0);
   else return 0.0;
+  auto limb = [&](int q) -> uint64_t { return q == 0 ? L0 : q == 1 ? L1 : q == 2 ? L2 : 0ull; };
   auto bit_range = [&](int lo) -> uint64_t {  // 64 bits starting at bit lo (lo >= 0)
-    const uint64_t w[3] = {L0, L1, L2};
     const int q = lo >> 6, r = lo & 63;
-    uint64_t v = q < 3 ? (w[q] >> r) : 0ull;
-    if (r && q + 1 < 3) v |= w[q + 1] << (64 - r);
+    uint64_t v = limb(q) >> r;
+    if (r) v |= limb(q + 1) << (64 - r);
     return v;
   };
   if (p <= 52) return __builtin_ldexp((double)L0, -149);  // exact
@@ -270,11 +286,13 @@ __device__ inline double acc_rn64(const Acc& a) {
   bool sticky = false;
   if (sh - 1 > 0) {
     const int nb = sh - 1;  // bits [0, nb) below the round bit
-    const uint64_t w[3] = {L0, L1, L2};
-    for (int q = 0; q < 3 && q * 64 < nb; ++q) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
       const int take = nb - q * 64;
-      const uint64_t m = take >= 64 ? ~0ull : ((1ull << take) - 1);
-      if (w[q] & m) sticky = true;
+      if (take > 0) {
+        const uint64_t m = take >= 64 ? ~0ull : ((1ull << take) - 1);
+        if (limb(q) & m) sticky = true;
+      }
     }
   }
   if (rb && (sticky || (mant & 1ull))) mant += 1;

@@ -10,7 +10,7 @@
 #include <cstring>
 
 #include "dspark.h"
-#include "row_alloc.hpp"
+#include "dense_vd.hpp"
 
 namespace dspark {
 
@@ -106,6 +106,127 @@ __global__ void __launch_bounds__(BS) rows_kernel(RowsArgs a) {
     a.row_status[r] = status;
     if (a.sample) a.sample[r] = ok ? tok : 0;
   }
+}
+
+
+// bf16 rows of up to NI*BS*8 tokens: the row is loaded into registers once.
+// Each kind of row has its own kernel, so that every path gets its own
+// register allocation (the dense and sparse paths would otherwise force
+// spills onto the simple target path).
+
+__device__ __forceinline__ void res_target_row(const RowsArgs& a, int r, SmemBase& sh) {
+  Res R;
+  res_load(R, static_cast<const uint16_t*>(a.target) + (size_t)r * (size_t)a.t_stride, a.V);
+  const RStats st = res_stats(R, sh);
+  const int am = st.status == DSPARK_ST_OK ? res_argmax(R, st, sh) : 0;
+  if (threadIdx.x == 0) {
+    a.t_argmax[r] = am;
+    a.t_status[r] = st.status;
+  }
+}
+
+struct DraftHead {
+  RStats st;
+  int status, am;
+  float cf;
+};
+
+// validity, argmax, confidence and the draw check of a draft row
+__device__ __forceinline__ DraftHead res_draft_head(const RowsArgs& a, Res& R, int r, int kstatus, uint32_t u,
+                                                    SmemBase& sh) {
+  DraftHead h;
+  h.st = res_stats(R, sh);
+  h.status = h.st.status != DSPARK_ST_OK ? h.st.status : kstatus;
+  if (h.status == DSPARK_ST_OK && a.draws && u >= kMass) h.status = DSPARK_ST_DRAW_RANGE;
+  h.am = 0;
+  h.cf = 0.0f;
+  if (h.status == DSPARK_ST_OK) {
+    h.am = res_argmax(R, h.st, sh);
+    if (a.conf) h.cf = res_conf(R, bf16_to_f32(h.st.m_raw), sh);
+  }
+  return h;
+}
+
+__device__ __forceinline__ void write_draft(const RowsArgs& a, int r, int status, int am, float cf, int tok) {
+  if (threadIdx.x == 0) {
+    const bool ok = status == DSPARK_ST_OK;
+    if (a.argmax) a.argmax[r] = ok ? am : 0;
+    if (a.conf) a.conf[r] = ok ? cf : 0.0f;
+    a.row_status[r] = status;
+    if (a.sample) a.sample[r] = ok ? tok : 0;
+  }
+}
+
+// draft row without q, or with a dense q (kstatus carries BAD_TOPK)
+__device__ __forceinline__ void res_draft_dense(const RowsArgs& a, int r, int kstatus, DenseShared& sh) {
+  Res R;
+  res_load(R, static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V);
+  const uint32_t u = a.draws ? a.draws[r] : 0u;
+  const DraftHead h = res_draft_head(a, R, r, kstatus, u, sh);
+  int status = h.status, tok = 0;
+  const bool dense_row = a.do_q && a.dense != nullptr && kstatus == DSPARK_ST_OK;
+  uint32_t* drow = dense_row ? a.dense + (size_t)r * (size_t)a.V : nullptr;
+  if (dense_row && status == DSPARK_ST_OK) {
+    const QOut qo = res_dense_q(R, h.st, drow, a.V, a.draws != nullptr, u, sh);
+    status = qo.status;
+    tok = qo.token;
+  }
+  if (dense_row && status != DSPARK_ST_OK)
+    for (int i = threadIdx.x; i < a.V; i += BS) drow[i] = 0u;
+  if (a.do_q && a.sp_len && threadIdx.x == 0) a.sp_len[r] = 0;
+  write_draft(a, r, status, h.am, h.cf, tok);
+}
+
+// draft row with a sparse top-k q
+__device__ __forceinline__ void res_draft_sparse(const RowsArgs& a, int r, int k, RowShared& sh) {
+  Res R;
+  res_load(R, static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V);
+  const uint32_t u = a.draws ? a.draws[r] : 0u;
+  const DraftHead h = res_draft_head(a, R, r, DSPARK_ST_OK, u, sh);
+  int status = h.status, tok = 0;
+  if (status == DSPARK_ST_OK) {
+    const int n = res_topk_support(R, h.st, k, sh);
+    const QOut qo = support_alloc(bf16_to_f32(h.st.m_raw), n, a.sp_ids + (size_t)r * a.k_max,
+                                  a.sp_cnt + (size_t)r * a.k_max, a.sp_len + r, a.draws != nullptr, u, sh);
+    status = qo.status;
+    tok = qo.token;
+  }
+  if (status != DSPARK_ST_OK && threadIdx.x == 0) a.sp_len[r] = 0;
+  write_draft(a, r, status, h.am, h.cf, tok);
+}
+
+// the row kind a draft row belongs to: 1 sparse (1 <= k <= kcap), 0 otherwise
+// (no q, dense q, or a bad k reported as BAD_TOPK)
+__device__ __forceinline__ int draft_kind(const RowsArgs& a, int r, int* k, int* kstatus) {
+  *k = 0;
+  *kstatus = DSPARK_ST_OK;
+  if (!a.do_q) return 0;
+  *k = a.topk ? a.topk[r] : 0;
+  const int kcap = a.k_max < a.V ? a.k_max : a.V;
+  if (*k < 0 || *k > kcap || (*k == 0 && a.dense == nullptr)) {
+    *kstatus = DSPARK_ST_BAD_TOPK;
+    return 0;
+  }
+  return *k > 0 ? 1 : 0;
+}
+
+__global__ void __launch_bounds__(BS) rows_bf16_target_kernel(RowsArgs a) {
+  __shared__ SmemBase sh;
+  res_target_row(a, blockIdx.x, sh);
+}
+
+__global__ void __launch_bounds__(BS) rows_bf16_dense_kernel(RowsArgs a) {
+  __shared__ DenseShared sh;
+  int k, kstatus;
+  if (draft_kind(a, blockIdx.x, &k, &kstatus) != 0) return;
+  res_draft_dense(a, blockIdx.x, kstatus, sh);
+}
+
+__global__ void __launch_bounds__(BS) rows_bf16_sparse_kernel(RowsArgs a) {
+  __shared__ RowShared sh;
+  int k, kstatus;
+  if (draft_kind(a, blockIdx.x, &k, &kstatus) != 1) return;
+  res_draft_sparse(a, blockIdx.x, k, sh);
 }
 
 // Greedy verification, one thread per request ("DeepSeek-V4.1 DSpark",
@@ -282,7 +403,13 @@ int launch_rows(const RowsArgs& a, int dtype, void* stream) {
   const int nblk = a.n_draft + a.n_target;
   if (nblk == 0) return DSPARK_SUCCESS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == DSPARK_BF16)
+  if (dtype == DSPARK_BF16 && a.V <= NI * BS * 8) {
+    if (a.n_draft > 0) {
+      hipLaunchKernelGGL(rows_bf16_dense_kernel, dim3(a.n_draft), dim3(BS), 0, s, a);
+      if (a.do_q && a.topk) hipLaunchKernelGGL(rows_bf16_sparse_kernel, dim3(a.n_draft), dim3(BS), 0, s, a);
+    }
+    if (a.n_target > 0) hipLaunchKernelGGL(rows_bf16_target_kernel, dim3(a.n_target), dim3(BS), 0, s, a);
+  } else if (dtype == DSPARK_BF16)
     hipLaunchKernelGGL(rows_kernel<DSPARK_BF16>, dim3(nblk), dim3(BS), 0, s, a);
   else
     hipLaunchKernelGGL(rows_kernel<DSPARK_F32>, dim3(nblk), dim3(BS), 0, s, a);

@@ -81,26 +81,30 @@ struct URow {
 };
 
 // ------------------------------------------------------------ shared state
-struct RowShared {
+// Members every row kernel uses.
+struct SmemBase {
   BlockScratch bs;
   AccScratch acc;
   uint64_t tab[kMaxIter];            // per-iteration totals for locate
-  uint32_t ctab[kMaxIter * NW];      // per (iteration, wave) counts for compaction
   uint32_t hist[kHistBins];
+  int bi[8];
+  uint64_t bu[4];
+};
+// The generic / sparse row kernels add the compaction and support arrays.
+struct RowShared : SmemBase {
+  uint32_t ctab[kMaxIter * NW];      // per (iteration, wave) counts for compaction
   uint64_t ckey[kCandCap];           // candidate / support keys
   uint32_t cid[kCandCap];            // candidate / support ids
   float sx[DSPARK_K_MAX];            // support logits
   uint32_t sc[DSPARK_K_MAX];         // support counts
-  int bi[8];
-  uint64_t bu[4];
 };
 
 // ---------------------------------------------------- crossing search
 // Finds the first bin b, scanning bins in ascending (asc) or descending
 // index order, at which the running count reaches `need` (1 <= need <=
 // total).  Returns b; *before = count of the bins scanned before b.
-__device__ inline int block_find_crossing(const uint32_t* hist, int nbins, uint64_t need, bool asc,
-                                          RowShared& sh, uint64_t* before) {
+__device__ __forceinline__ int block_find_crossing(const uint32_t* hist, int nbins, uint64_t need, bool asc,
+                                          SmemBase& sh, uint64_t* before) {
   const int per = (nbins + BS - 1) / BS;
   const int t = threadIdx.x;
   uint64_t s = 0;
@@ -137,7 +141,7 @@ __device__ inline int block_find_crossing(const uint32_t* hist, int nbins, uint6
 // (0 for lanes past the end).  Phase 1 totals each iteration, phase 2 finds
 // the iteration, phase 3 scans inside it.
 template <int EPV, class WF>
-__device__ int block_locate(int nvec, WF wf, uint64_t u, RowShared& sh) {
+__device__ int block_locate(int nvec, WF wf, uint64_t u, SmemBase& sh) {
   const int n_iter = (nvec + BS - 1) / BS;
   for (int i = threadIdx.x; i < n_iter; i += BS) sh.tab[i] = 0;
   __syncthreads();
@@ -234,16 +238,18 @@ __device__ int block_compact(const Row<DT>& row, SEL sel, int cap, RowShared& sh
     const int per = (n + BS - 1) / BS;
     uint32_t v[4];  // n <= kMaxIter*NW = 4096 -> per <= 4
     uint32_t s = 0;
-    for (int j = 0; j < per; ++j) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
       const int k = threadIdx.x * per + j;
-      v[j] = k < n ? sh.ctab[k] : 0u;
+      v[j] = (j < per && k < n) ? sh.ctab[k] : 0u;
       s += v[j];
     }
     uint32_t tot;
     uint32_t pre = block_excl_scan<uint32_t>(s, sh.bs, &tot);
-    for (int j = 0; j < per; ++j) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
       const int k = threadIdx.x * per + j;
-      if (k < n) sh.ctab[k] = pre;
+      if (j < per && k < n) sh.ctab[k] = pre;
       pre += v[j];
     }
     if (threadIdx.x == 0) sh.bi[3] = (int)tot;
@@ -287,7 +293,7 @@ struct Thr {
 
 // Radix threshold over n keys held in LDS (8-bit digits, top down): the
 // `need` largest (1 <= need <= n).
-__device__ inline Thr lds_threshold(const uint64_t* keys, int n, uint64_t need, RowShared& sh) {
+__device__ inline Thr lds_threshold(const uint64_t* keys, int n, uint64_t need, SmemBase& sh) {
   uint64_t prefix = 0, pmask = 0;
   for (int shift = 56; shift >= 0; shift -= 8) {
     for (int b = threadIdx.x; b < 256; b += BS) sh.hist[b] = 0;

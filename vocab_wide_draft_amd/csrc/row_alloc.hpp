@@ -80,7 +80,7 @@ __device__ void row_argmax_conf(const Row<DT>& row, float m, bool want_conf, Row
 }
 
 // k-th largest (k >= 1) of one uint32 per thread, radix select by bytes.
-__device__ inline uint32_t block_kth_largest(uint32_t v, int k, RowShared& sh) {
+__device__ inline uint32_t block_kth_largest(uint32_t v, int k, SmemBase& sh) {
   uint32_t prefix = 0, pmask = 0;
   uint64_t need = (uint64_t)k;
   for (int shift = 24; shift >= 0; shift -= 8) {
@@ -142,14 +142,15 @@ __device__ Thr finish_in_lds(const URow& out, KEYS keyfn, uint64_t prefix, uint6
   Thr t = lds_threshold(sh.ckey, n, need, sh);
   if (t.all_ge) return t;
   // tie group: keep the need_t lowest ids -> threshold on (2^32-1 - id)
-  uint64_t mine[2];
-  int nm = 0;
-  for (int e = threadIdx.x; e < n; e += BS)
-    if (sh.ckey[e] == t.T) mine[nm++] = 0xffffffffull - sh.cid[e];
+  // each thread holds at most two candidates (n <= kCandCap = 2 * BS)
+  const int e0 = threadIdx.x, e1 = threadIdx.x + BS;
+  const bool t0 = e0 < n && sh.ckey[e0] == t.T, t1 = e1 < n && sh.ckey[e1] == t.T;
+  const uint64_t m0 = t0 ? 0xffffffffull - sh.cid[e0] : 0ull, m1 = t1 ? 0xffffffffull - sh.cid[e1] : 0ull;
   __syncthreads();
   if (threadIdx.x == 0) sh.bi[4] = 0;
   __syncthreads();
-  for (int i = 0; i < nm; ++i) sh.ckey[atomicAdd(&sh.bi[4], 1)] = mine[i];
+  if (t0) sh.ckey[atomicAdd(&sh.bi[4], 1)] = m0;
+  if (t1) sh.ckey[atomicAdd(&sh.bi[4], 1)] = m1;
   __syncthreads();
   const int ntie = sh.bi[4];
   __syncthreads();
@@ -161,7 +162,7 @@ __device__ Thr finish_in_lds(const URow& out, KEYS keyfn, uint64_t prefix, uint6
 // Dense allocation on a count row that holds the binary32 weight bits
 // (written by the caller); S64 = RN64(sum of weights).  Overwrites the row
 // with the counts.  Used for logit rows and for the weights-only entry.
-__device__ QOut dense_alloc(const URow& out, double s64, bool want_s, uint32_t u, RowShared& sh) {
+__device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool want_s, uint32_t u, RowShared& sh) {
   QOut res{DSPARK_ST_OK, 0};
   if (!(s64 > 0.0)) {
     res.status = DSPARK_ST_ROW_ZERO_MASS;
@@ -339,6 +340,76 @@ __device__ QOut dense_q(const Row<DT>& row, float m, uint32_t* drow, bool want_s
   return dense_alloc(out, s64, want_s, u, sh);
 }
 
+// dyadic24 counts on a support held in (sh.cid, sh.sx), ascending ids, n <= 1024
+// entries: weights, exact sum, floors, largest remainders (ties to the lower
+// id = earlier entry), positive entries out in id order, optional sample.
+__device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, uint32_t* cnt_out, int32_t* len_out,
+                              bool want_s, uint32_t u, RowShared& sh) {
+  QOut res{DSPARK_ST_OK, 0};
+  // weights, exact sum, floors
+  const int j = threadIdx.x;
+  const bool have = j < n;
+  float w = 0.0f;
+  Acc acc;
+  acc_zero(acc);
+  if (have) {
+    w = cr_expf(sh.sx[j] - m);
+    acc_add(acc, __float_as_uint(w));
+  }
+  const double s64 = block_acc_rn64(acc, sh.acc);
+  uint32_t c = 0;
+  double r = 0.0;
+  if (have) floor_rem(w, s64, c, r);
+  const bool pos = have && r > 0.0;
+  const uint64_t key = pos ? rem_key(r) : 0ull;
+  sh.ckey[j] = key;
+  const uint64_t csum = block_sum<uint64_t>(c, sh.bs);
+  const uint32_t npos = block_sum<uint32_t>(pos ? 1u : 0u, sh.bs);
+  const int64_t remaining = (int64_t)kMass - (int64_t)csum;
+  if (!(s64 > 0.0)) {
+    res.status = DSPARK_ST_ROW_ZERO_MASS;
+    return res;
+  }
+  if (remaining < 0 || remaining >= (int64_t)kMass || remaining > (int64_t)npos) {
+    res.status = DSPARK_ST_ALLOC_INCONSISTENT;
+    return res;
+  }
+  // 5. largest remainders, ties to the lowest id (= support order)
+  if (remaining > 0) {
+    const Thr t = lds_threshold(sh.ckey, n, (uint64_t)remaining, sh);
+    const uint32_t tie = (pos && !t.all_ge && key == t.T) ? 1u : 0u;
+    uint32_t ntie;
+    const uint32_t rank = block_excl_scan<uint32_t>(tie, sh.bs, &ntie);
+    const bool sel = pos && (key > t.T || (key == t.T && (t.all_ge || rank < t.need_t)));
+    c += sel ? 1u : 0u;
+  }
+  const uint64_t fsum = block_sum<uint64_t>(c, sh.bs);
+  if (fsum != kMass) {
+    res.status = DSPARK_ST_ALLOC_INCONSISTENT;
+    return res;
+  }
+  // 6. positive entries in id order, and the sample
+  uint32_t len;
+  const uint32_t slot = block_excl_scan<uint32_t>(c > 0 ? 1u : 0u, sh.bs, &len);
+  if (c > 0) {
+    ids_out[slot] = (int32_t)sh.cid[j];
+    cnt_out[slot] = c;
+  }
+  if (threadIdx.x == 0) *len_out = (int32_t)len;
+  if (want_s) {
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan<uint32_t>(c, sh.bs, &tot);
+    if (threadIdx.x == 0) sh.bi[5] = -1;
+    __syncthreads();
+    if (c > 0 && pre <= u && u < pre + c) sh.bi[5] = (int)sh.cid[j];
+    __syncthreads();
+    res.token = sh.bi[5];
+    __syncthreads();
+    if (res.token < 0) res.status = DSPARK_ST_ALLOC_INCONSISTENT;
+  }
+  return res;
+}
+
 // Sparse top-k q ("Sparse support ... follow-up": global support first,
 // normalised within it, zero-count entries dropped, ascending ids).
 template <int DT>
@@ -410,68 +481,7 @@ __device__ QOut sparse_q(const Row<DT>& row, float m, uint32_t tkey, int k, int3
     }
     return msk;
   }, DSPARK_K_MAX, sh);
-  // 4. weights, exact sum, floors
-  const int j = threadIdx.x;
-  const bool have = j < n;
-  float w = 0.0f;
-  Acc acc;
-  acc_zero(acc);
-  if (have) {
-    w = cr_expf(sh.sx[j] - m);
-    acc_add(acc, __float_as_uint(w));
-  }
-  const double s64 = block_acc_rn64(acc, sh.acc);
-  uint32_t c = 0;
-  double r = 0.0;
-  if (have) floor_rem(w, s64, c, r);
-  const bool pos = have && r > 0.0;
-  const uint64_t key = pos ? rem_key(r) : 0ull;
-  sh.ckey[j] = key;
-  const uint64_t csum = block_sum<uint64_t>(c, sh.bs);
-  const uint32_t npos = block_sum<uint32_t>(pos ? 1u : 0u, sh.bs);
-  const int64_t remaining = (int64_t)kMass - (int64_t)csum;
-  if (!(s64 > 0.0)) {
-    res.status = DSPARK_ST_ROW_ZERO_MASS;
-    return res;
-  }
-  if (remaining < 0 || remaining >= (int64_t)kMass || remaining > (int64_t)npos) {
-    res.status = DSPARK_ST_ALLOC_INCONSISTENT;
-    return res;
-  }
-  // 5. largest remainders, ties to the lowest id (= support order)
-  if (remaining > 0) {
-    const Thr t = lds_threshold(sh.ckey, n, (uint64_t)remaining, sh);
-    const uint32_t tie = (pos && !t.all_ge && key == t.T) ? 1u : 0u;
-    uint32_t ntie;
-    const uint32_t rank = block_excl_scan<uint32_t>(tie, sh.bs, &ntie);
-    const bool sel = pos && (key > t.T || (key == t.T && (t.all_ge || rank < t.need_t)));
-    c += sel ? 1u : 0u;
-  }
-  const uint64_t fsum = block_sum<uint64_t>(c, sh.bs);
-  if (fsum != kMass) {
-    res.status = DSPARK_ST_ALLOC_INCONSISTENT;
-    return res;
-  }
-  // 6. positive entries in id order, and the sample
-  uint32_t len;
-  const uint32_t slot = block_excl_scan<uint32_t>(c > 0 ? 1u : 0u, sh.bs, &len);
-  if (c > 0) {
-    ids_out[slot] = (int32_t)sh.cid[j];
-    cnt_out[slot] = c;
-  }
-  if (threadIdx.x == 0) *len_out = (int32_t)len;
-  if (want_s) {
-    uint32_t tot;
-    const uint32_t pre = block_excl_scan<uint32_t>(c, sh.bs, &tot);
-    if (threadIdx.x == 0) sh.bi[5] = -1;
-    __syncthreads();
-    if (c > 0 && pre <= u && u < pre + c) sh.bi[5] = (int)sh.cid[j];
-    __syncthreads();
-    res.token = sh.bi[5];
-    __syncthreads();
-    if (res.token < 0) res.status = DSPARK_ST_ALLOC_INCONSISTENT;
-  }
-  return res;
+  return support_alloc(m, n, ids_out, cnt_out, len_out, want_s, u, sh);
 }
 
 }  // namespace dspark
