@@ -81,7 +81,7 @@ __device__ __forceinline__ int vd_find_digit(const uint64_t* rh, int nd, uint64_
 }
 
 __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* drow, int V, bool want_s,
-                                            uint32_t u, DenseShared& sh) {
+                                            uint32_t u, DenseShared& sh DSPARK_PHASE_PARAM) {
   QOut res{DSPARK_ST_OK, 0};
   const int Km = k16(st.m_raw);
   const float m = bf16_to_f32(st.m_raw);
@@ -109,6 +109,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     }
   }
   __syncthreads();
+  DSPARK_PHASE(11);
   // 2. weights and their exact sum, per occupied bin
   Acc acc;
   acc_zero(acc);
@@ -121,6 +122,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     res.status = DSPARK_ST_ROW_ZERO_MASS;
     return res;
   }
+  DSPARK_PHASE(12);
   // 3. floors, remaining, and the first 11-bit digit of the remainder keys
   uint64_t* rh = reinterpret_cast<uint64_t*>(sh.hist);  // 2048 x uint64 in the 16 KB histogram
   for (int d = threadIdx.x; d < 2048; d += BS) rh[d] = 0ull;
@@ -146,6 +148,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     res.status = DSPARK_ST_ALLOC_INCONSISTENT;
     return res;
   }
+  DSPARK_PHASE(13);
   // 4. threshold over bins weighted by their counts: digits of 11 bits
   enum { NONE = 0, ALL = 1, CAND = 2, EXACT = 3 };
   int mode = NONE;
@@ -183,6 +186,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
       __syncthreads();
     }
   }
+  DSPARK_PHASE(14);
   // 5. mark every occupied bin with its final count (candidates wait)
   if (threadIdx.x == 0) sh.bi[4] = 0;
   __syncthreads();
@@ -207,6 +211,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     }
   }
   __syncthreads();
+  DSPARK_PHASE(15);
   // 6. candidates of the threshold bucket: exact weighted threshold in LDS
   uint64_t need_t = need;
   int ntie_bins = mode == EXACT ? 2 : 0;  // EXACT: tie bins found through the table
@@ -252,6 +257,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     if (ntie_bins == 1) tie_bin = sh.bi[6];
     __syncthreads();
   }
+  DSPARK_PHASE(16);
   // 7. a split tie: the need_t lowest ids among the elements of the tie bins
   int cut = -1;
   if (ntie_bins > 0) {
@@ -269,6 +275,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
       return msk;
     }, (uint32_t)(need_t - 1), sh);
   }
+  DSPARK_PHASE(17);
   // 8. counts of every element, written in place of the row
   if (threadIdx.x < NI) sh.tab[threadIdx.x] = 0ull;
   __syncthreads();
@@ -308,6 +315,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     res.status = DSPARK_ST_ALLOC_INCONSISTENT;
     return res;
   }
+  DSPARK_PHASE(18);
   // 9. the sample: first element whose running count exceeds u; the thread
   // owning it re-reads its own eight counts from the row it just wrote
   if (want_s) {

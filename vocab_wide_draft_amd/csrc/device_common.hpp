@@ -16,6 +16,33 @@ constexpr int kHistBins = 4096;     // histogram bins of one select pass
 constexpr int kCandCap = 2048;      // candidates a select may collect in LDS
 constexpr int kMaxIter = 256;       // (V_MAX / 4) / BS vector iterations per row
 
+// Phase hooks: with DSPARK_PHASE_TIMING defined, DSPARK_PHASE(k) adds the
+// cycles since the previous hook of the workgroup to counter k (read with
+// dspark_debug_phases); otherwise they compile to nothing.
+#ifdef DSPARK_PHASE_TIMING
+extern __device__ unsigned long long g_phase[64];
+#define DSPARK_PHASE_BEGIN long long dspark_pt0_ = clock64();
+#define DSPARK_PHASE(k)                                                                   \
+  do {                                                                                    \
+    __syncthreads();                                                                      \
+    if (threadIdx.x == 0) {                                                               \
+      const long long t_ = clock64();                                                     \
+      atomicAdd(&g_phase[k], (unsigned long long)(t_ - dspark_pt0_));                     \
+      atomicAdd(&g_phase[32 + (k)], 1ull);                                                \
+      dspark_pt0_ = t_;                                                                   \
+    }                                                                                     \
+  } while (0)
+#define DSPARK_PHASE_ARG , dspark_pt0_
+#define DSPARK_PHASE_PARAM , long long& dspark_pt0_
+#else
+#define DSPARK_PHASE_ARG
+#define DSPARK_PHASE_PARAM
+#define DSPARK_PHASE_BEGIN
+#define DSPARK_PHASE(k) \
+  do {                  \
+  } while (0)
+#endif
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 

@@ -11,8 +11,13 @@
 
 #include "dspark.h"
 #include "dense_vd.hpp"
+#include "sparse_fast.hpp"
 
 namespace dspark {
+
+#ifdef DSPARK_PHASE_TIMING
+__device__ unsigned long long g_phase[64];
+#endif
 
 struct RowsArgs {
   const void* draft;
@@ -115,10 +120,12 @@ __global__ void __launch_bounds__(BS) rows_kernel(RowsArgs a) {
 // spills onto the simple target path).
 
 __device__ __forceinline__ void res_target_row(const RowsArgs& a, int r, SmemBase& sh) {
+  DSPARK_PHASE_BEGIN
   Res R;
   res_load(R, static_cast<const uint16_t*>(a.target) + (size_t)r * (size_t)a.t_stride, a.V);
   const RStats st = res_stats(R, sh);
   const int am = st.status == DSPARK_ST_OK ? res_argmax(R, st, sh) : 0;
+  DSPARK_PHASE(30);
   if (threadIdx.x == 0) {
     a.t_argmax[r] = am;
     a.t_status[r] = st.status;
@@ -159,17 +166,20 @@ __device__ __forceinline__ void write_draft(const RowsArgs& a, int r, int status
 
 // draft row without q, or with a dense q (kstatus carries BAD_TOPK)
 __device__ __forceinline__ void res_draft_dense(const RowsArgs& a, int r, int kstatus, DenseShared& sh) {
+  DSPARK_PHASE_BEGIN
   Res R;
   res_load(R, static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V);
   const uint32_t u = a.draws ? a.draws[r] : 0u;
   const DraftHead h = res_draft_head(a, R, r, kstatus, u, sh);
+  DSPARK_PHASE(10);
   int status = h.status, tok = 0;
   const bool dense_row = a.do_q && a.dense != nullptr && kstatus == DSPARK_ST_OK;
   uint32_t* drow = dense_row ? a.dense + (size_t)r * (size_t)a.V : nullptr;
   if (dense_row && status == DSPARK_ST_OK) {
-    const QOut qo = res_dense_q(R, h.st, drow, a.V, a.draws != nullptr, u, sh);
+    const QOut qo = res_dense_q(R, h.st, drow, a.V, a.draws != nullptr, u, sh DSPARK_PHASE_ARG);
     status = qo.status;
     tok = qo.token;
+    DSPARK_PHASE(19);
   }
   if (dense_row && status != DSPARK_ST_OK)
     for (int i = threadIdx.x; i < a.V; i += BS) drow[i] = 0u;
@@ -179,17 +189,22 @@ __device__ __forceinline__ void res_draft_dense(const RowsArgs& a, int r, int ks
 
 // draft row with a sparse top-k q
 __device__ __forceinline__ void res_draft_sparse(const RowsArgs& a, int r, int k, RowShared& sh) {
+  DSPARK_PHASE_BEGIN
   Res R;
   res_load(R, static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V);
   const uint32_t u = a.draws ? a.draws[r] : 0u;
   const DraftHead h = res_draft_head(a, R, r, DSPARK_ST_OK, u, sh);
+  DSPARK_PHASE(0);
   int status = h.status, tok = 0;
   if (status == DSPARK_ST_OK) {
-    const int n = res_topk_support(R, h.st, k, sh);
+    int n = res_topk_fast(R, h.st, k, sh DSPARK_PHASE_ARG);
+    if (n < 0) n = res_topk_support(R, h.st, k, sh);  // candidates overflowed: exact multi-pass selection
+    DSPARK_PHASE(4);
     const QOut qo = support_alloc(bf16_to_f32(h.st.m_raw), n, a.sp_ids + (size_t)r * a.k_max,
                                   a.sp_cnt + (size_t)r * a.k_max, a.sp_len + r, a.draws != nullptr, u, sh);
     status = qo.status;
     tok = qo.token;
+    DSPARK_PHASE(8);
   }
   if (status != DSPARK_ST_OK && threadIdx.x == 0) a.sp_len[r] = 0;
   write_draft(a, r, status, h.am, h.cf, tok);
@@ -603,3 +618,14 @@ int dspark_cr_expf(const float* d, float* w, int64_t n, void* stream) {
 }
 
 }  // extern "C"
+
+#ifdef DSPARK_PHASE_TIMING
+extern "C" int dspark_debug_phases(unsigned long long* out, int reset) {
+  if (hipMemcpyFromSymbol(out, HIP_SYMBOL(dspark::g_phase), sizeof(unsigned long long) * 64) != hipSuccess) return -1;
+  if (reset) {
+    unsigned long long z[64] = {0};
+    if (hipMemcpyToSymbol(HIP_SYMBOL(dspark::g_phase), z, sizeof z) != hipSuccess) return -2;
+  }
+  return 0;
+}
+#endif

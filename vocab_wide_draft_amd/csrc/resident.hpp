@@ -106,8 +106,9 @@ __device__ __forceinline__ void res_load(Res& R, const uint16_t* p, int V) {
 // ------------------------------------------------------------- statistics
 struct RStats {
   int status;
-  uint32_t m_raw;  // bf16 bits of the row maximum
-  int smax_t;      // this thread's largest raw int16 (one of its elements)
+  uint32_t m_raw;   // bf16 bits of the row maximum
+  int smax_t;       // this thread's largest raw int16 (one of its elements)
+  uint32_t rep[4];  // packed raw int16 maxima per word position: 8 elements of this thread
 };
 
 // Row maximum and validity from packed int16 maxima of the raw bits: the
@@ -117,7 +118,8 @@ struct RStats {
 // pass (their maximum has the smallest unsigned pattern).
 __device__ __forceinline__ RStats res_stats(Res& R, SmemBase& sh) {
   touch(R);
-  s16x2 smax = {(short)-32768, (short)-32768};
+  s16x2 sm[4] = {{(short)-32768, (short)-32768}, {(short)-32768, (short)-32768},
+                 {(short)-32768, (short)-32768}, {(short)-32768, (short)-32768}};
   u16x2 umax = {0, 0};
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -125,11 +127,15 @@ __device__ __forceinline__ RStats res_stats(Res& R, SmemBase& sh) {
     const uint32_t w[4] = {vi.x, vi.y, vi.z, vi.w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      smax = __builtin_elementwise_max(smax, __builtin_bit_cast(s16x2, w[c]));
+      sm[c] = __builtin_elementwise_max(sm[c], __builtin_bit_cast(s16x2, w[c]));
       umax = __builtin_elementwise_max(umax, __builtin_bit_cast(u16x2, w[c]));
     }
   }
   RStats s;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) s.rep[c] = __builtin_bit_cast(uint32_t, sm[c]);
+  const s16x2 smax = __builtin_elementwise_max(__builtin_elementwise_max(sm[0], sm[1]),
+                                               __builtin_elementwise_max(sm[2], sm[3]));
   s.smax_t = smax.x > smax.y ? smax.x : smax.y;
   const int um_t = umax.x > umax.y ? umax.x : umax.y;
   const int S = block_max<int>(s.smax_t, sh.bs);

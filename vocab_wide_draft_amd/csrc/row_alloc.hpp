@@ -345,6 +345,7 @@ __device__ QOut dense_q(const Row<DT>& row, float m, uint32_t* drow, bool want_s
 // id = earlier entry), positive entries out in id order, optional sample.
 __device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, uint32_t* cnt_out, int32_t* len_out,
                               bool want_s, uint32_t u, RowShared& sh) {
+  DSPARK_PHASE_BEGIN
   QOut res{DSPARK_ST_OK, 0};
   // weights, exact sum, floors
   const int j = threadIdx.x;
@@ -374,13 +375,35 @@ __device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, 
     res.status = DSPARK_ST_ALLOC_INCONSISTENT;
     return res;
   }
-  // 5. largest remainders, ties to the lowest id (= support order)
+  DSPARK_PHASE(5);
+  // 5. largest remainders, ties to the lowest id (= support order j):
+  // bucket the keys by their top 11 bits, then rank inside the threshold
+  // bucket exactly by (key desc, j asc)
   if (remaining > 0) {
-    const Thr t = lds_threshold(sh.ckey, n, (uint64_t)remaining, sh);
-    const uint32_t tie = (pos && !t.all_ge && key == t.T) ? 1u : 0u;
-    uint32_t ntie;
-    const uint32_t rank = block_excl_scan<uint32_t>(tie, sh.bs, &ntie);
-    const bool sel = pos && (key > t.T || (key == t.T && (t.all_ge || rank < t.need_t)));
+    for (int b = threadIdx.x; b < 2048; b += BS) sh.hist[b] = 0u;
+    if (threadIdx.x == 0) sh.bi[4] = 0;
+    __syncthreads();
+    if (pos) atomicAdd(&sh.hist[key >> 53], 1u);
+    __syncthreads();
+    uint64_t before;
+    const int B = block_find_crossing(sh.hist, 2048, (uint64_t)remaining, false, sh, &before);
+    const uint32_t need_b = (uint32_t)((uint64_t)remaining - before);
+    const uint32_t bucket = pos ? (uint32_t)(key >> 53) : 0u;
+    const bool inb = pos && bucket == (uint32_t)B;
+    uint32_t* lj = sh.ctab;  // bucket members: index into ckey
+    if (inb) lj[atomicAdd(&sh.bi[4], 1)] = (uint32_t)j;
+    __syncthreads();
+    const int nb = sh.bi[4];
+    bool sel = pos && bucket > (uint32_t)B;
+    if (inb) {
+      uint32_t rank = 0;
+      for (int f = 0; f < nb; ++f) {
+        const uint32_t o = lj[f];
+        const uint64_t ko = sh.ckey[o];
+        rank += (ko > key || (ko == key && o < (uint32_t)j)) ? 1u : 0u;
+      }
+      sel = rank < need_b;
+    }
     c += sel ? 1u : 0u;
   }
   const uint64_t fsum = block_sum<uint64_t>(c, sh.bs);
@@ -388,6 +411,7 @@ __device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, 
     res.status = DSPARK_ST_ALLOC_INCONSISTENT;
     return res;
   }
+  DSPARK_PHASE(6);
   // 6. positive entries in id order, and the sample
   uint32_t len;
   const uint32_t slot = block_excl_scan<uint32_t>(c > 0 ? 1u : 0u, sh.bs, &len);
