@@ -26,7 +26,7 @@ title and section:
   verification matches the target argmax over the anchor plus up to five
   proposals and commits the accepted prefix).
 
-Readings where the pages leave a step open (all listed in the design doc):
+Readings where the pages leave a step open:
 confidence is the softmax max-probability 1 / sum(exp(x - m)); the weight of
 a token is RN32(exp(RN32(x - m))) correctly rounded; S is summed exactly and
 rounded once to binary64; the remaining assertion also requires
@@ -45,7 +45,7 @@ from fractions import Fraction
 import numpy as np
 
 M = 1 << 24  # total dyadic mass, "PP1 q transport ...", "Distribution contract"
-N_DRAFT = 5  # block positions, CONTRACT section 2 ("block / k")
+N_DRAFT = 5  # block positions, "Remote DSpark drafter -- wire and state contract", section 2
 N_TARGET = N_DRAFT + 1  # anchor + five proposals, "DeepSeek-V4.1 DSpark"
 
 ST_OK = 0
@@ -104,7 +104,8 @@ def row_status(x: np.ndarray) -> int:
 
 
 def argmax_first(x: np.ndarray) -> tuple[float, int]:
-    """Row maximum and the lowest index attaining it (CONTRACT section 2:
+    """Row maximum and the lowest index attaining it ("Remote DSpark drafter -- wire and state
+    contract", section 2:
     greedy argmax resolves ties to the lower vocabulary index).  IEEE
     comparison, so -0.0 and +0.0 are equal."""
     m = float(x.max())
@@ -325,7 +326,8 @@ def sample_many(ids: np.ndarray, counts: np.ndarray, u: np.ndarray) -> np.ndarra
 
 def verify_greedy(draft_tokens, draft_status, target_argmax, target_status, vocab):
     """Greedy verification of one request ("DeepSeek-V4.1 DSpark", "State and
-    sampling contracts"; CONTRACT section 2, anchor-as-first).
+    sampling contracts"; "Remote DSpark drafter -- wire and state contract",
+    section 2, anchor-as-first).
 
     Target row i (i = 0 is the anchor row) predicts the token at draft
     position i; row 5 only supplies the bonus.  accept_len is the number of

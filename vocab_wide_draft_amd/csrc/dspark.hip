@@ -225,23 +225,39 @@ __device__ __forceinline__ int draft_kind(const RowsArgs& a, int r, int* k, int*
   return *k > 0 ? 1 : 0;
 }
 
-__global__ void __launch_bounds__(BS) rows_bf16_target_kernel(RowsArgs a) {
-  __shared__ SmemBase sh;
-  res_target_row(a, blockIdx.x, sh);
+// One launch for every resident row of a call: block b handles row
+// row_of_block(b).  Draft and target blocks are interleaved in proportion to
+// their numbers, so that at any moment some CUs stream target rows while
+// others run the on-chip allocation of draft rows, and the HBM traffic of the
+// first overlaps the computation of the second across the chip.  The row kind
+// is a function of blockIdx alone, so every branch below is uniform.
+union ResShared {
+  SmemBase base;
+  RowShared rs;
+  DenseShared ds;
+};
+
+__device__ __forceinline__ void row_of_block(int b, int nd, int nt, bool* is_draft, int* r) {
+  const int64_t n = (int64_t)nd + nt;
+  const int d0 = (int)((int64_t)b * nd / n), d1 = (int)((int64_t)(b + 1) * nd / n);
+  *is_draft = d1 > d0;
+  *r = *is_draft ? d0 : b - d0;
 }
 
-__global__ void __launch_bounds__(BS) rows_bf16_dense_kernel(RowsArgs a) {
-  __shared__ DenseShared sh;
+__global__ void __launch_bounds__(BS) rows_bf16_kernel(RowsArgs a) {
+  __shared__ ResShared sh;
+  bool is_draft;
+  int r;
+  row_of_block((int)blockIdx.x, a.n_draft, a.n_target, &is_draft, &r);
+  if (!is_draft) {
+    res_target_row(a, r, sh.base);
+    return;
+  }
   int k, kstatus;
-  if (draft_kind(a, blockIdx.x, &k, &kstatus) != 0) return;
-  res_draft_dense(a, blockIdx.x, kstatus, sh);
-}
-
-__global__ void __launch_bounds__(BS) rows_bf16_sparse_kernel(RowsArgs a) {
-  __shared__ RowShared sh;
-  int k, kstatus;
-  if (draft_kind(a, blockIdx.x, &k, &kstatus) != 1) return;
-  res_draft_sparse(a, blockIdx.x, k, sh);
+  if (draft_kind(a, r, &k, &kstatus) == 1)
+    res_draft_sparse(a, r, k, sh.rs);
+  else
+    res_draft_dense(a, r, kstatus, sh.ds);
 }
 
 // Greedy verification, one thread per request ("DeepSeek-V4.1 DSpark",
@@ -419,11 +435,7 @@ int launch_rows(const RowsArgs& a, int dtype, void* stream) {
   if (nblk == 0) return DSPARK_SUCCESS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == DSPARK_BF16 && a.V <= NI * BS * 8) {
-    if (a.n_draft > 0) {
-      hipLaunchKernelGGL(rows_bf16_dense_kernel, dim3(a.n_draft), dim3(BS), 0, s, a);
-      if (a.do_q && a.topk) hipLaunchKernelGGL(rows_bf16_sparse_kernel, dim3(a.n_draft), dim3(BS), 0, s, a);
-    }
-    if (a.n_target > 0) hipLaunchKernelGGL(rows_bf16_target_kernel, dim3(a.n_target), dim3(BS), 0, s, a);
+    hipLaunchKernelGGL(rows_bf16_kernel, dim3(nblk), dim3(BS), 0, s, a);
   } else if (dtype == DSPARK_BF16)
     hipLaunchKernelGGL(rows_kernel<DSPARK_BF16>, dim3(nblk), dim3(BS), 0, s, a);
   else

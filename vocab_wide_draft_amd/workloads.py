@@ -5,7 +5,7 @@ method's arithmetic.  Both the HIP library's tests and the CPU oracle's tests
 take their inputs from here.  bf16 rows are returned as uint16 bit patterns,
 binary32 rows as float32.  Every request has 5 draft rows and 6 target rows
 (anchor + five proposals: "DeepSeek-V4.1 DSpark", "State and sampling
-contracts"; CONTRACT section 2, "block / k").
+contracts"; "Remote DSpark drafter -- wire and state contract", section 2).
 
 Recipe (one numpy PCG64 generator per config, seed 0xD5A10000 + config id;
 draws in the order draft logits, target logits, per-config structure, draws):
