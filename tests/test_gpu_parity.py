@@ -224,3 +224,54 @@ def test_cr_expf_sampled_and_hard_cases():
     ref = O.cr_exp_f32(d)
     bad = np.flatnonzero(got.view(np.uint32) != ref.view(np.uint32))
     assert bad.size == 0, (d[bad[:5]], got[bad[:5]], ref[bad[:5]])
+
+
+# ------------------------------------------- rows aimed at the value table
+def _table_rows(V, rng):
+    """bf16 draft rows (as binary32 values) that exercise the compressed value
+    table of the bf16 path: near-zero logits sharing one entry, top-k
+    thresholds inside that entry, windows that start above zero, maxima on
+    both sides of the table's size limit, negative maxima, bf16 subnormals."""
+    rows = []
+    base = (rng.standard_normal(V) * 2).astype(np.float32)
+    tiny = (rng.choice([-1.0, 1.0], V) * np.exp(rng.uniform(np.log(1e-12), np.log(1e-7), V))).astype(np.float32)
+    r = base.copy(); sel = rng.random(V) < 0.4; r[sel] = tiny[sel]; r[0] = 8.0; rows.append(("tiny_mass", r))
+    r = tiny.copy(); r[V // 3] = 8.0; r[V // 2] = 5.0; rows.append(("tiny_only", r))
+    r = rng.uniform(90.0, 200.0, V).astype(np.float32); r[7 % V] = 200.0; rows.append(("window_above_zero", r))
+    r = (rng.uniform(-1.0, 1.0, V) * 2.0**-20).astype(np.float32)
+    neg = rng.random(V) < 0.5
+    r[neg] = -rng.uniform(0.0, 100.0, int(neg.sum())).astype(np.float32)
+    r[1 % V] = 2.0**-20; rows.append(("max_2^-20", r))
+    r = (-np.abs(rng.standard_normal(V)) * 3).astype(np.float32); r[2 % V] = 1e-30; rows.append(("max_1e-30", r))
+    r = rng.uniform(-50.0, -10.0, V).astype(np.float32); rows.append(("negative_max", r))
+    r = base.copy(); r[rng.random(V) < 0.3] = np.float32(3e-39); r[rng.random(V) < 0.3] = np.float32(-5e-39)
+    rows.append(("subnormals", r))
+    vals = np.array([0.0, 1e-9, -1e-9, 2.0, -1e-12], np.float32)
+    rows.append(("tiny_dups", vals[rng.integers(0, vals.size, V)]))
+    return rows
+
+
+@pytest.mark.parametrize("V", [300, 5000, 129280])
+def test_value_table_rows(V):
+    rng = np.random.default_rng(V + 77)
+    rows = _table_rows(V, rng)
+    names = [n for n, _ in rows]
+    raw = _bits_bf16(np.stack([r for _, r in rows]).astype(np.float32))
+    d = to_dev(raw, BF16)
+    n5 = (len(rows) // 5) * 5
+    t = to_dev(np.tile(raw[:6], ((n5 // 5), 1)), BF16)  # target rows for the fused step (5 per 6)
+    for k in [0, 1, 5, min(300, V), min(1024, V)]:
+        topk = np.full(len(rows), k, np.int32)
+        q = host(B.q_alloc(d, topk=topk, k_max=1024))
+        pr = host(B.propose(d))
+        for j, name in enumerate(names):
+            ref = O.draft_row(raw[j], BF16, k)
+            h = {"status": q["status"], "argmax": pr["argmax"] * (q["status"] == 0),
+                 "conf": pr["conf"] * (q["status"] == 0), "q": q}
+            check_draft_row(h, j, ref, k, label=f"table V{V} k{k} {name}")
+        # the fused step (confidence taken from the value table on q rows)
+        draws = rng.integers(0, 1 << 24, n5, dtype=np.uint32)
+        f = host(B.fused(d[:n5], t, B.SAMPLED, topk=topk[:n5], k_max=1024, draws=u32_dev(draws)))
+        for j in range(n5):
+            ref = O.draft_row(raw[j], BF16, k, int(draws[j]))
+            check_draft_row(f, j, ref, k, label=f"table fused V{V} k{k} {names[j]}")

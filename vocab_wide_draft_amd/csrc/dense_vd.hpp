@@ -283,7 +283,6 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
   const int nvec = (V + 7) >> 3;
   const bool vec_ok = (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
   uint64_t total = 0;
-  uint32_t vsum[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int q = i * BS + (int)threadIdx.x;
@@ -295,15 +294,14 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     if (q < nvec) {
       if (q * 8 + 8 <= V && vec_ok) {
         u32x4* dst = reinterpret_cast<u32x4*>(drow + (size_t)q * 8);
-        dst[0] = u32x4{c[0], c[1], c[2], c[3]};
-        dst[1] = u32x4{c[4], c[5], c[6], c[7]};
+        __builtin_nontemporal_store(u32x4{c[0], c[1], c[2], c[3]}, dst);  // written once, streamed out
+        __builtin_nontemporal_store(u32x4{c[4], c[5], c[6], c[7]}, dst + 1);
       } else {
 #pragma unroll
         for (int l = 0; l < 8; ++l)
           if (q * 8 + l < V) drow[(size_t)q * 8 + l] = c[l];
       }
     }
-    vsum[i] = vs;
     total += vs;
     if (want_s && __ballot(vs != 0u)) {
       const uint32_t w = wave_sum(vs);
@@ -316,8 +314,8 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     return res;
   }
   DSPARK_PHASE(18);
-  // 9. the sample: first element whose running count exceeds u; the thread
-  // owning it re-reads its own eight counts from the row it just wrote
+  // 9. the sample: first element whose running count exceeds u; the counts
+  // of the vector holding it are recomputed from the registers
   if (want_s) {
     if (threadIdx.x == 0) {
       uint64_t run = 0;
@@ -334,18 +332,21 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     __syncthreads();
     const int istar = sh.bi[1];
     const uint64_t u2 = (uint64_t)u - sh.bu[1];
+    const int q = istar * BS + (int)threadIdx.x;
+    uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (istar >= 0) vd_counts(select_vec(R, istar), Km, NB, q * 8, cut, sh, c);
     uint32_t vs = 0;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vs = (i == istar) ? vsum[i] : vs;
+    for (int l = 0; l < 8; ++l) vs += c[l];
     uint64_t tot;
     const uint64_t pre = block_excl_scan<uint64_t>(vs, sh.bs, &tot);
     if (istar >= 0 && vs && pre <= u2 && u2 < pre + vs) {
-      const int q = istar * BS + (int)threadIdx.x;
       uint64_t run = pre;
       int hit = -1;
-      for (int l = 0; l < 8 && hit < 0; ++l) {
-        if (q * 8 + l < V) run += drow[(size_t)q * 8 + l];
-        if (run > u2) hit = l;
+#pragma unroll
+      for (int l = 0; l < 8; ++l) {
+        run += c[l];
+        if (run > u2 && hit < 0) hit = l;
       }
       sh.bi[2] = q * 8 + hit;
     }

@@ -59,43 +59,81 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
+// DPP lane moves (all lanes of the wave active): lanes whose source is out
+// of range, or whose row / bank is masked off, keep `old`.
+template <int CTRL, int RM, int BM>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, RM, BM, false);
+}
+template <int CTRL, int RM, int BM, class T>
+__device__ __forceinline__ T dpp_t(T old, T x) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit lane values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, dpp_u32<CTRL, RM, BM>(__builtin_bit_cast(uint32_t, old), __builtin_bit_cast(uint32_t, x)));
+  } else {
+    const uint64_t o = __builtin_bit_cast(uint64_t, old), v = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = dpp_u32<CTRL, RM, BM>((uint32_t)o, (uint32_t)v);
+    const uint32_t hi = dpp_u32<CTRL, RM, BM>((uint32_t)(o >> 32), (uint32_t)(v >> 32));
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+template <class T>
+__device__ __forceinline__ T readlane63(T v) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, (uint32_t)__builtin_amdgcn_readlane((int)__builtin_bit_cast(uint32_t, v), 63));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+// Reduction over the 64 lanes: quad swaps, half-row and row mirrors give
+// every lane its row's result; the row broadcasts of lanes 15 and 31 then
+// fold the four rows into lane 63, which is read back as a scalar.
+template <class T, class OP>
+__device__ __forceinline__ T wave_reduce(T v, T id, OP op) {
+  v = op(v, dpp_t<0xb1, 0xf, 0xf>(id, v));   // quad_perm 1,0,3,2
+  v = op(v, dpp_t<0x4e, 0xf, 0xf>(id, v));   // quad_perm 2,3,0,1
+  v = op(v, dpp_t<0x141, 0xf, 0xf>(id, v));  // row_half_mirror
+  v = op(v, dpp_t<0x140, 0xf, 0xf>(id, v));  // row_mirror
+  v = op(v, dpp_t<0x142, 0xa, 0xf>(id, v));  // row_bcast:15 into rows 1 and 3
+  v = op(v, dpp_t<0x143, 0xc, 0xf>(id, v));  // row_bcast:31 into rows 2 and 3
+  return readlane63(v);
+}
 template <class T>
 __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce(v, T(0), [](T a, T b) { return a + b; });
 }
 template <>
 __device__ __forceinline__ uint32_t wave_sum<uint32_t>(uint32_t v) {
   return wave_sum_u32(v);
 }
+// identities of max and min for the lane types used
+__device__ __forceinline__ int lowest_of(int) { return -2147483647 - 1; }
+__device__ __forceinline__ uint32_t lowest_of(uint32_t) { return 0u; }
+__device__ __forceinline__ float lowest_of(float) { return -__builtin_inff(); }
+__device__ __forceinline__ int highest_of(int) { return 2147483647; }
+__device__ __forceinline__ uint32_t highest_of(uint32_t) { return 0xffffffffu; }
+__device__ __forceinline__ float highest_of(float) { return __builtin_inff(); }
 template <class T>
 __device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    T u = __shfl_xor(v, o, 64);
-    v = u > v ? u : v;
-  }
-  return v;
+  return wave_reduce(v, lowest_of(T()), [](T a, T b) { return b > a ? b : a; });
 }
 template <class T>
 __device__ __forceinline__ T wave_min(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    T u = __shfl_xor(v, o, 64);
-    v = u < v ? u : v;
-  }
-  return v;
+  return wave_reduce(v, highest_of(T()), [](T a, T b) { return b < a ? b : a; });
 }
-// inclusive prefix sum over the 64 lanes
+// inclusive prefix sum over the 64 lanes: row shifts by 1, 2, 4, 8 (scan
+// inside each row of 16), then the row broadcasts of lanes 15 and 31
 template <class T>
 __device__ __forceinline__ T wave_incl_scan(T v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    T u = __shfl_up(v, o, 64);
-    if (l >= o) v += u;
-  }
+  v += dpp_t<0x111, 0xf, 0xf>(T(0), v);  // row_shr:1
+  v += dpp_t<0x112, 0xf, 0xf>(T(0), v);  // row_shr:2
+  v += dpp_t<0x114, 0xf, 0xf>(T(0), v);  // row_shr:4
+  v += dpp_t<0x118, 0xf, 0xf>(T(0), v);  // row_shr:8
+  v += dpp_t<0x142, 0xa, 0xf>(T(0), v);  // row_bcast:15
+  v += dpp_t<0x143, 0xc, 0xf>(T(0), v);  // row_bcast:31
   return v;
 }
 
@@ -274,12 +312,13 @@ __device__ __forceinline__ void acc_merge(Acc& a, const Acc& b) {
   add128(a.mlo, a.mhi, b.mlo, b.mhi);
   add128(a.tlo, a.thi, b.tlo, b.thi);
 }
-__device__ __forceinline__ Acc acc_shfl_xor(const Acc& a, int o) {
+template <int CTRL, int RM>
+__device__ __forceinline__ Acc acc_dpp(const Acc& a) {
   Acc b;
-  b.mlo = __shfl_xor(a.mlo, o, 64);
-  b.mhi = __shfl_xor(a.mhi, o, 64);
-  b.tlo = __shfl_xor(a.tlo, o, 64);
-  b.thi = __shfl_xor(a.thi, o, 64);
+  b.mlo = dpp_t<CTRL, RM, 0xf, uint64_t>(uint64_t(0), a.mlo);
+  b.mhi = dpp_t<CTRL, RM, 0xf, uint64_t>(uint64_t(0), a.mhi);
+  b.tlo = dpp_t<CTRL, RM, 0xf, uint64_t>(uint64_t(0), a.tlo);
+  b.thi = dpp_t<CTRL, RM, 0xf, uint64_t>(uint64_t(0), a.thi);
   return b;
 }
 struct AccScratch {
@@ -327,9 +366,14 @@ __device__ inline double acc_rn64(const Acc& a) {
 }
 // Block-wide exact sum; every thread gets RN64(S).
 __device__ inline double block_acc_rn64(Acc a, AccScratch& s) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) acc_merge(a, acc_shfl_xor(a, o));
-  if (lane_id() == 0) s.w[wave_id()] = a;
+  // the wave's exact sum lands in lane 63 (same steps as wave_reduce)
+  acc_merge(a, acc_dpp<0xb1, 0xf>(a));
+  acc_merge(a, acc_dpp<0x4e, 0xf>(a));
+  acc_merge(a, acc_dpp<0x141, 0xf>(a));
+  acc_merge(a, acc_dpp<0x140, 0xf>(a));
+  acc_merge(a, acc_dpp<0x142, 0xa>(a));
+  acc_merge(a, acc_dpp<0x143, 0xc>(a));
+  if (lane_id() == 63) s.w[wave_id()] = a;
   __syncthreads();
   if (threadIdx.x == 0) {
     Acc t = s.w[0];

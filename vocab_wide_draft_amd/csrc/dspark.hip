@@ -11,7 +11,7 @@
 
 #include "dspark.h"
 #include "dense_vd.hpp"
-#include "sparse_fast.hpp"
+#include "fast_q.hpp"
 
 namespace dspark {
 
@@ -132,28 +132,6 @@ __device__ __forceinline__ void res_target_row(const RowsArgs& a, int r, SmemBas
   }
 }
 
-struct DraftHead {
-  RStats st;
-  int status, am;
-  float cf;
-};
-
-// validity, argmax, confidence and the draw check of a draft row
-__device__ __forceinline__ DraftHead res_draft_head(const RowsArgs& a, Res& R, int r, int kstatus, uint32_t u,
-                                                    SmemBase& sh) {
-  DraftHead h;
-  h.st = res_stats(R, sh);
-  h.status = h.st.status != DSPARK_ST_OK ? h.st.status : kstatus;
-  if (h.status == DSPARK_ST_OK && a.draws && u >= kMass) h.status = DSPARK_ST_DRAW_RANGE;
-  h.am = 0;
-  h.cf = 0.0f;
-  if (h.status == DSPARK_ST_OK) {
-    h.am = res_argmax(R, h.st, sh);
-    if (a.conf) h.cf = res_conf(R, bf16_to_f32(h.st.m_raw), sh);
-  }
-  return h;
-}
-
 __device__ __forceinline__ void write_draft(const RowsArgs& a, int r, int status, int am, float cf, int tok) {
   if (threadIdx.x == 0) {
     const bool ok = status == DSPARK_ST_OK;
@@ -164,50 +142,141 @@ __device__ __forceinline__ void write_draft(const RowsArgs& a, int r, int status
   }
 }
 
-// draft row without q, or with a dense q (kstatus carries BAD_TOPK)
-__device__ __forceinline__ void res_draft_dense(const RowsArgs& a, int r, int kstatus, DenseShared& sh) {
+union ResShared {
+  SmemBase base;
+  RowShared rs;
+  DenseShared ds;
+  FastDenseShared fd;
+  FastSparseShared fs;
+};
+// The LDS of the resident row kernel, at file scope so that the out-of-line
+// paths below address it directly.
+__shared__ ResShared g_res_sh;
+
+struct QConf {
+  QOut q;
+  float conf;
+};
+
+// Rows whose maximum is at or very near zero (the compressed value table
+// does not apply): the per-value allocation over every bf16 value of the
+// window, on a fresh copy of the row.  Out of line, so that its register
+// needs do not weigh on the common paths; such rows pay one more read.
+__device__ __noinline__ QConf dense_general(const uint16_t* p, int V, uint32_t m_raw, uint32_t* drow, bool want_s,
+                                            uint32_t u, bool want_conf) {
+  Res R;
+  res_load(R, p, V);
+  RStats st;
+  st.status = DSPARK_ST_OK;
+  st.m_raw = m_raw;
+  QConf r;
+  r.conf = want_conf ? res_conf(R, bf16_to_f32(m_raw), g_res_sh.base) : 0.0f;
+  long long dspark_pt0_ = 0;
+  (void)dspark_pt0_;
+  r.q = res_dense_q(R, st, drow, V, want_s, u, g_res_sh.ds DSPARK_PHASE_ARG);
+  return r;
+}
+
+// The exact multi-pass top-k selection (and the confidence sweep when the
+// value table does not apply), on a fresh copy of the row.
+__device__ __noinline__ int sparse_exact(const uint16_t* p, int V, uint32_t m_raw, int k, bool want_conf,
+                                         float* conf) {
+  Res R;
+  res_load(R, p, V);
+  const RStats st = res_stats(R, g_res_sh.base);
+  (void)m_raw;
+  if (want_conf) *conf = res_conf(R, bf16_to_f32(st.m_raw), g_res_sh.base);
+  return res_topk_support(R, st, k, g_res_sh.rs);
+}
+
+// draft row without q, or with a dense q (kstatus carries BAD_TOPK).  With
+// a dense q and a row maximum that admits the compressed value table, the
+// confidence comes from the table; otherwise from a sweep over the row.
+__device__ __forceinline__ void res_draft_dense(const RowsArgs& a, int r, int kstatus, ResShared& sh) {
   DSPARK_PHASE_BEGIN
   Res R;
   res_load(R, static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V);
   const uint32_t u = a.draws ? a.draws[r] : 0u;
-  const DraftHead h = res_draft_head(a, R, r, kstatus, u, sh);
-  DSPARK_PHASE(10);
-  int status = h.status, tok = 0;
   const bool dense_row = a.do_q && a.dense != nullptr && kstatus == DSPARK_ST_OK;
   uint32_t* drow = dense_row ? a.dense + (size_t)r * (size_t)a.V : nullptr;
-  if (dense_row && status == DSPARK_ST_OK) {
-    const QOut qo = res_dense_q(R, h.st, drow, a.V, a.draws != nullptr, u, sh DSPARK_PHASE_ARG);
-    status = qo.status;
-    tok = qo.token;
-    DSPARK_PHASE(19);
+  const RStats st = res_stats(R, sh.base);
+  int status = st.status != DSPARK_ST_OK ? st.status : kstatus;
+  if (status == DSPARK_ST_OK && a.draws && u >= kMass) status = DSPARK_ST_DRAW_RANGE;
+  int am = 0, tok = 0;
+  float cf = 0.0f;
+  if (status == DSPARK_ST_OK) {
+    am = res_argmax(R, st, sh.base);
+    FMap f;
+    bool fast = false;
+    if (dense_row) {
+      f = fmap_make(st.m_raw);
+      fast = f.NB <= kNBF;
+    }
+    if (a.conf && !dense_row) cf = res_conf(R, bf16_to_f32(st.m_raw), sh.base);
+    DSPARK_PHASE(10);
+    if (dense_row) {
+      QOut qo;
+      if (fast) {
+        qo = fast_dense_q(R, st, f, drow, a.V, a.draws != nullptr, u, a.conf != nullptr, &cf, sh.fd DSPARK_PHASE_ARG);
+      } else {
+        const QConf g = dense_general(static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V,
+                                      st.m_raw, drow, a.draws != nullptr, u, a.conf != nullptr);
+        qo = g.q;
+        cf = g.conf;
+      }
+      status = qo.status;
+      tok = qo.token;
+      DSPARK_PHASE(19);
+    }
   }
   if (dense_row && status != DSPARK_ST_OK)
     for (int i = threadIdx.x; i < a.V; i += BS) drow[i] = 0u;
   if (a.do_q && a.sp_len && threadIdx.x == 0) a.sp_len[r] = 0;
-  write_draft(a, r, status, h.am, h.cf, tok);
+  write_draft(a, r, status, am, cf, tok);
 }
 
 // draft row with a sparse top-k q
-__device__ __forceinline__ void res_draft_sparse(const RowsArgs& a, int r, int k, RowShared& sh) {
+__device__ __forceinline__ void res_draft_sparse(const RowsArgs& a, int r, int k, ResShared& sh) {
   DSPARK_PHASE_BEGIN
   Res R;
   res_load(R, static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V);
   const uint32_t u = a.draws ? a.draws[r] : 0u;
-  const DraftHead h = res_draft_head(a, R, r, DSPARK_ST_OK, u, sh);
-  DSPARK_PHASE(0);
-  int status = h.status, tok = 0;
+  const RStats st = res_stats(R, sh.base);
+  int status = st.status;
+  if (status == DSPARK_ST_OK && a.draws && u >= kMass) status = DSPARK_ST_DRAW_RANGE;
+  int am = 0, tok = 0;
+  float cf = 0.0f;
   if (status == DSPARK_ST_OK) {
-    int n = res_topk_fast(R, h.st, k, sh DSPARK_PHASE_ARG);
-    if (n < 0) n = res_topk_support(R, h.st, k, sh);  // candidates overflowed: exact multi-pass selection
+    am = res_argmax(R, st, sh.base);
+    const float m = bf16_to_f32(st.m_raw);
+    const FMap f = fmap_make(st.m_raw);
+    int n = -1;
+    const bool table = f.NB <= kNBF;
+    if (table) {  // value table: confidence and the exact top-k threshold
+      fast_hist(R, f, sh.fs.nb);
+      Acc acc;
+      acc_zero(acc);
+      double cs = 0.0;
+      fast_pass_a<false>(f, m, sh.fs.nb, nullptr, acc, cs);
+      if (a.conf) cf = (float)(1.0 / block_sum<double>(cs, sh.base.bs));
+      DSPARK_PHASE(0);
+      n = fast_topk(R, f, k, sh.fs DSPARK_PHASE_ARG);
+    }
+    if (n < 0) {  // exact multi-pass selection
+      float cfe = 0.0f;
+      n = sparse_exact(static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V, st.m_raw, k,
+                       a.conf != nullptr && !table, &cfe);
+      if (!table) cf = cfe;
+    }
     DSPARK_PHASE(4);
-    const QOut qo = support_alloc(bf16_to_f32(h.st.m_raw), n, a.sp_ids + (size_t)r * a.k_max,
-                                  a.sp_cnt + (size_t)r * a.k_max, a.sp_len + r, a.draws != nullptr, u, sh);
+    const QOut qo = support_alloc(m, n, a.sp_ids + (size_t)r * a.k_max, a.sp_cnt + (size_t)r * a.k_max,
+                                  a.sp_len + r, a.draws != nullptr, u, sh.rs);
     status = qo.status;
     tok = qo.token;
     DSPARK_PHASE(8);
   }
   if (status != DSPARK_ST_OK && threadIdx.x == 0) a.sp_len[r] = 0;
-  write_draft(a, r, status, h.am, h.cf, tok);
+  write_draft(a, r, status, am, cf, tok);
 }
 
 // the row kind a draft row belongs to: 1 sparse (1 <= k <= kcap), 0 otherwise
@@ -231,12 +300,6 @@ __device__ __forceinline__ int draft_kind(const RowsArgs& a, int r, int* k, int*
 // others run the on-chip allocation of draft rows, and the HBM traffic of the
 // first overlaps the computation of the second across the chip.  The row kind
 // is a function of blockIdx alone, so every branch below is uniform.
-union ResShared {
-  SmemBase base;
-  RowShared rs;
-  DenseShared ds;
-};
-
 __device__ __forceinline__ void row_of_block(int b, int nd, int nt, bool* is_draft, int* r) {
   const int64_t n = (int64_t)nd + nt;
   const int d0 = (int)((int64_t)b * nd / n), d1 = (int)((int64_t)(b + 1) * nd / n);
@@ -245,7 +308,7 @@ __device__ __forceinline__ void row_of_block(int b, int nd, int nt, bool* is_dra
 }
 
 __global__ void __launch_bounds__(BS) rows_bf16_kernel(RowsArgs a) {
-  __shared__ ResShared sh;
+  ResShared& sh = g_res_sh;
   bool is_draft;
   int r;
   row_of_block((int)blockIdx.x, a.n_draft, a.n_target, &is_draft, &r);
@@ -255,9 +318,9 @@ __global__ void __launch_bounds__(BS) rows_bf16_kernel(RowsArgs a) {
   }
   int k, kstatus;
   if (draft_kind(a, r, &k, &kstatus) == 1)
-    res_draft_sparse(a, r, k, sh.rs);
+    res_draft_sparse(a, r, k, sh);
   else
-    res_draft_dense(a, r, kstatus, sh.ds);
+    res_draft_dense(a, r, kstatus, sh);
 }
 
 // Greedy verification, one thread per request ("DeepSeek-V4.1 DSpark",

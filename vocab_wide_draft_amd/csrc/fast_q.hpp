@@ -1,0 +1,603 @@
+// dyadic24 q of a register-resident bf16 draft row from a compressed value
+// table ("PP1 q transport and scheduling design", "Distribution contract and
+// precision" for the allocation; "Sparse support and vocabulary-sharded TP2
+// follow-up" for the top-k support).
+//
+// Every quantity of the allocation before the id tie-break is a function of
+// d = RN32(x - m), the binary32 difference of a logit and the row maximum.
+// Logits whose magnitude is below tau = 2^(e_m - 26) (an eighth of a binary32
+// ulp of m, m > 0) all give d = -m exactly, so they share one table entry
+// (the "collapsed" entry); every other bf16 value in the weight window
+// [m - 105, m] has an entry of its own.  Entries are ordered by value, largest
+// first, so the table is both a histogram for the allocation and an order
+// statistic for the top-k threshold.  For a row maximum of ordinary size the
+// table has at most ~9k entries (instead of the ~34k bf16 values of the
+// window), which leaves room in LDS to keep each entry's weight and remainder
+// key between passes.  Rows whose table would exceed kNBF entries (a maximum
+// at or very near zero) take the general per-value path of dense_vd.hpp.
+//
+// The confidence 1 / sum_v exp(x_v - m) is also taken from the table: each
+// entry adds n * exp(x - m), with x - m exact in binary64; the collapsed entry
+// uses exp(-m), which is within a relative 2^(e_m - 26) of each of its terms
+// and holds at most a fraction V e^-m / (1 + V e^-m) of the sum (below 1.2e-7
+// of the confidence for any m).
+#pragma once
+#include "dense_vd.hpp"
+#include "sparse_fast.hpp"
+
+namespace dspark {
+
+constexpr int kNBF = 10240;        // largest compressed table
+constexpr int kNBFD = kNBF + 64;   // plus one overflow slot per lane
+constexpr uint32_t kFT = 1u << 30; // tie flag of a final-count entry
+
+// Table layout of one row.  bin(x) = B0 - c(|x|) for x with the sign bit
+// clear, B0 + c(|x|) with it set, where c(a) = max(a, tb1) - tb1 on the
+// magnitude bits; magnitudes <= tb1 give c = 0, the collapsed entry B0.
+struct FMap {
+  int B0, tb1, NB;
+  uint32_t Cp2, Tp2, Cn2, Tn2;  // the formula's constants, twice per word
+};
+
+__device__ __forceinline__ int fmap_c(uint32_t mag, int tb1) {
+  const int a = (int)mag;
+  return (a > tb1 ? a : tb1) - tb1;
+}
+__device__ __forceinline__ int fmap_bin(uint32_t raw, const FMap& f) {
+  const int c = fmap_c(raw & 0x7fffu, f.tb1);
+  return (raw & 0x8000u) ? f.B0 + c : f.B0 - c;
+}
+// bf16 pattern of the values in entry b (for the collapsed entry: +0, whose d
+// is -m like every member's)
+__device__ __forceinline__ uint32_t fmap_raw(int b, const FMap& f) {
+  if (b <= f.B0) {
+    const int c = f.B0 - b;
+    return c == 0 ? 0u : (uint32_t)(c + f.tb1);
+  }
+  return 0x8000u | (uint32_t)(b - f.B0 + f.tb1);
+}
+
+// Layout for the row maximum m_raw (valid row).  NB > kNBF means "not
+// applicable".
+__device__ __forceinline__ FMap fmap_make(uint32_t m_raw) {
+  FMap f;
+  const uint32_t mag_m = m_raw & 0x7fffu;
+  const bool mneg = (m_raw & 0x8000u) != 0;
+  f.tb1 = 0;
+  if (!mneg && mag_m != 0u) {
+    const int Em = (int)(mag_m >> 7);  // bf16 exponent field of m
+    if (Em - 26 >= 1) f.tb1 = ((Em - 26) << 7) - 1;
+  }
+  const int cm = fmap_c(mag_m, f.tb1);
+  f.B0 = mneg ? -cm : cm;
+  // smallest bf16 >= m - 105 (binary32), never below the most negative finite value
+  const float m = bf16_to_f32(m_raw);
+  const uint32_t b = __float_as_uint(m - 105.0f);
+  uint32_t hb = b >> 16;
+  if ((b & 0xffffu) && !(b & 0x80000000u)) hb += 1u;
+  hb &= 0xffffu;
+  if (hb > 0xff7fu) hb = 0xff7fu;
+  f.NB = fmap_bin(hb, f) + 1;
+  const uint32_t Cp = (uint32_t)(f.B0 + f.tb1) & 0xffffu, Tp = (uint32_t)f.tb1;
+  const uint32_t Cn = (uint32_t)(f.B0 - f.tb1 - 0x8000) & 0xffffu, Tn = 0x8000u + (uint32_t)f.tb1;
+  f.Cp2 = Cp * 0x10001u;
+  f.Tp2 = Tp * 0x10001u;
+  f.Cn2 = Cn * 0x10001u;
+  f.Tn2 = Tn * 0x10001u;
+  return f;
+}
+
+// Byte offsets (bin * 4) of the two bf16 values of word w, in the low and
+// high halves; out-of-window values and -inf land in [NB, kNBFD) (the
+// overflow slots spread by lane).  Packed 16-bit arithmetic: no entry
+// exceeds 0xffff before the clamp, and kNBFD * 4 < 2^16.
+__device__ __forceinline__ uint32_t fmap_off2(uint32_t w, const FMap& f, uint32_t D2) {
+  const u16x2 v = __builtin_bit_cast(u16x2, w);
+  const u16x2 pos = __builtin_bit_cast(u16x2, f.Cp2) - __builtin_elementwise_max(v, __builtin_bit_cast(u16x2, f.Tp2));
+  const u16x2 neg = __builtin_bit_cast(u16x2, f.Cn2) + __builtin_elementwise_max(v, __builtin_bit_cast(u16x2, f.Tn2));
+  const uint32_t s = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, w) >> (short)15);
+  const uint32_t bin = (__builtin_bit_cast(uint32_t, neg) & s) | (__builtin_bit_cast(uint32_t, pos) & ~s);
+  const u16x2 bc = __builtin_elementwise_min(__builtin_bit_cast(u16x2, bin), __builtin_bit_cast(u16x2, D2));
+  return __builtin_bit_cast(uint32_t, bc) << 2 & 0xfffcfffcu;
+}
+__device__ __forceinline__ uint32_t fmap_dummy2() {
+  const uint32_t d = (uint32_t)(kNBF + lane_id());
+  return d * 0x10001u;
+}
+
+// exp(x) for binary64 x in [-106, 0] to about 1e-16 relative (Tang's table
+// reduction with the library's constants, degree-5 Taylor polynomial).
+__device__ __forceinline__ double exp64(double x) {
+  const double kf = __builtin_rint(x * kExpInvL);
+  const int k = (int)kf;
+  const double r = __builtin_fma(-kf, kExpCHi, x) - kf * kExpCLo;
+  double P = __builtin_fma(r, kExpP5, kExpP4);
+  P = __builtin_fma(r, P, kExpP3);
+  P = __builtin_fma(r, P, kExpP2);
+  const double p = __builtin_fma(r * r, P, r);
+  return __builtin_ldexp(__builtin_fma(kExpTabHi[k & 63], p, kExpTabHi[k & 63]), k >> 6);
+}
+
+// --------------------------------------------------------------- shared
+struct FastDenseShared : SmemBase {
+  uint32_t nb[kNBFD];   // counts, then final counts (kFT: tie entry)
+  float wb[kNBF];       // binary32 weight of each occupied entry
+  uint32_t kb[kNBF];    // top 32 bits of each entry's remainder key (0: r = 0)
+  uint64_t ckey[kVdCand];
+  uint32_t cbin[kVdCand];
+};
+struct FastSparseShared : RowShared {
+  uint32_t nb[kNBFD];
+  uint32_t bmB[NI * NW * 16];  // bitmap of the threshold entry's members
+};
+
+// Histogram of the row into nb[0, NB) (overflow slots take the rest).
+__device__ __forceinline__ void fast_hist(Res& R, const FMap& f, uint32_t* nb) {
+  for (int b = (int)threadIdx.x; b < f.NB; b += BS) nb[b] = 0u;
+  __syncthreads();
+  touch(R);
+  const uint32_t D2 = fmap_dummy2();
+  char* base = reinterpret_cast<char*>(nb);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const u32x4 v = fetch(R, i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t o = fmap_off2(w[c], f, D2);
+      atomicAdd(reinterpret_cast<uint32_t*>(base + (o & 0xffffu)), 1u);
+      atomicAdd(reinterpret_cast<uint32_t*>(base + (o >> 16)), 1u);
+    }
+  }
+  __syncthreads();
+}
+
+// Confidence sum (and, with W, the weights, their exact sum) over the table.
+template <bool W>
+__device__ __forceinline__ void fast_pass_a(const FMap& f, float m, const uint32_t* nb, float* wb, Acc& acc,
+                                            double& cs) {
+  const double md = (double)m;
+  for (int b = (int)threadIdx.x; b < f.NB; b += BS) {
+    const uint32_t n = nb[b];
+    if (n) {
+      const float x = bf16_to_f32(fmap_raw(b, f));
+      cs += (double)n * exp64((double)x - md);
+      if (W) {
+        const float w = cr_expf(x - m);
+        wb[b] = w;
+        acc_add(acc, __float_as_uint(w), n);
+      }
+    }
+  }
+}
+
+// binary64 floor and exact remainder key of entry b
+__device__ __forceinline__ void fast_floor_key(float w, double s64, uint32_t& c, uint64_t& key) {
+  double r;
+  floor_rem(w, s64, c, r);
+  key = r > 0.0 ? rem_key(r) : 0ull;
+}
+
+// --------------------------------------------------------------- dense
+__device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMap& f, uint32_t* drow, int V,
+                                             bool want_s, uint32_t u, bool want_conf, float* conf,
+                                             FastDenseShared& sh DSPARK_PHASE_PARAM) {
+  QOut res{DSPARK_ST_OK, 0};
+  const float m = bf16_to_f32(st.m_raw);
+  const int NB = f.NB;
+  fast_hist(R, f, sh.nb);
+  // overflow slots read 0 from here on (the tie mask and the final pass
+  // look up out-of-window elements there)
+  for (int b = NB + (int)threadIdx.x; b < kNBFD; b += BS) sh.nb[b] = 0u;
+  DSPARK_PHASE(11);
+  // A. weights, exact sum, confidence
+  Acc acc;
+  acc_zero(acc);
+  double cs = 0.0;
+  fast_pass_a<true>(f, m, sh.nb, sh.wb, acc, cs);
+  const double s64 = block_acc_rn64(acc, sh.acc);
+  if (want_conf) {
+    const double t = block_sum<double>(cs, sh.bs);
+    *conf = (float)(1.0 / t);
+  }
+  if (!(s64 > 0.0)) {
+    res.status = DSPARK_ST_ROW_ZERO_MASS;
+    return res;
+  }
+  DSPARK_PHASE(12);
+  // B. floors, remaining, keys, first 11-bit digit
+  uint64_t* rh = reinterpret_cast<uint64_t*>(sh.hist);  // 2048 digits
+  for (int d = (int)threadIdx.x; d < 2048; d += BS) rh[d] = 0ull;
+  __syncthreads();
+  uint64_t csum = 0, npos = 0;
+  for (int b = (int)threadIdx.x; b < NB; b += BS) {
+    const uint32_t n = sh.nb[b];
+    if (n) {
+      uint32_t c;
+      uint64_t key;
+      fast_floor_key(sh.wb[b], s64, c, key);
+      csum += (uint64_t)n * c;
+      sh.kb[b] = (uint32_t)(key >> 32);
+      if (key) {
+        npos += n;
+        atomicAdd((unsigned long long*)&rh[key >> 53], (unsigned long long)n | (1ull << 32));
+      }
+    }
+  }
+  csum = block_sum<uint64_t>(csum, sh.bs);
+  npos = block_sum<uint64_t>(npos, sh.bs);
+  const int64_t remaining = (int64_t)kMass - (int64_t)csum;
+  if (remaining < 0 || remaining >= (int64_t)kMass || remaining > (int64_t)npos) {
+    res.status = DSPARK_ST_ALLOC_INCONSISTENT;
+    return res;
+  }
+  DSPARK_PHASE(13);
+  // C. threshold over entries weighted by their counts: 11-bit digits, the
+  // first 32 key bits from kb, lower ones recomputed
+  enum { NONE = 0, ALL = 1, CAND = 2, EXACT = 3 };
+  int mode = NONE;
+  uint64_t prefix = 0, pmask = 0, need = (uint64_t)remaining;
+  if (remaining > 0) {
+    int shift = 53, nd = 2048;
+    for (;;) {
+      uint64_t before;
+      const int d = vd_find_digit(rh, nd, need, sh, &before);
+      need -= before;
+      const uint64_t e = rh[d];
+      __syncthreads();
+      prefix |= (uint64_t)d << shift;
+      pmask |= (uint64_t)(nd - 1) << shift;
+      if ((e & 0xffffffffull) == need) { mode = ALL; break; }
+      if ((e >> 32) <= (uint64_t)kVdCand) { mode = CAND; break; }
+      if (shift == 0) { mode = EXACT; break; }
+      const int nsh = shift > 11 ? shift - 11 : 0;
+      nd = 1 << (shift - nsh);
+      shift = nsh;
+      for (int dd = (int)threadIdx.x; dd < nd; dd += BS) rh[dd] = 0ull;
+      __syncthreads();
+      for (int b = (int)threadIdx.x; b < NB; b += BS) {
+        const uint32_t n = sh.nb[b];
+        if (n && sh.kb[b]) {
+          uint64_t key = (uint64_t)sh.kb[b] << 32;
+          if (shift < 32) {
+            uint32_t c;
+            fast_floor_key(sh.wb[b], s64, c, key);
+          }
+          if ((key & pmask) == prefix)
+            atomicAdd((unsigned long long*)&rh[(key >> shift) & (uint64_t)(nd - 1)],
+                      (unsigned long long)n | (1ull << 32));
+        }
+      }
+      __syncthreads();
+    }
+  }
+  DSPARK_PHASE(14);
+  // D. final count of every entry; the threshold bucket's entries wait (CAND)
+  if ((int)threadIdx.x == 0) sh.bi[4] = 0;
+  __syncthreads();
+  for (int b = (int)threadIdx.x; b < NB; b += BS) {
+    const uint32_t n = sh.nb[b];
+    if (n) {
+      uint32_t c;
+      uint64_t key;
+      fast_floor_key(sh.wb[b], s64, c, key);
+      const bool pos = key != 0ull && mode != NONE;
+      const uint64_t kp = key & pmask;
+      const bool above = pos && kp > prefix, inb = pos && kp == prefix;
+      if (inb && mode == CAND) {
+        const int slot = atomicAdd(&sh.bi[4], 1);
+        sh.ckey[slot] = key;
+        sh.cbin[slot] = (uint32_t)b;
+      } else if (inb && mode == EXACT) {
+        sh.nb[b] = kFT | c;
+      } else {
+        sh.nb[b] = c + ((above || (inb && mode == ALL)) ? 1u : 0u);
+      }
+    }
+  }
+  __syncthreads();
+  DSPARK_PHASE(15);
+  // E. the threshold bucket's entries (CAND): exact weighted threshold
+  uint64_t need_t = need;
+  int ntie = mode == EXACT ? 2 : 0;  // EXACT: tie entries carry kFT
+  int tie_bin = -1;
+  if (mode == CAND) {
+    const int nc = sh.bi[4];
+    const int j = (int)threadIdx.x;
+    uint64_t kj = 0, above = 0, eq = 0;
+    uint32_t bj = 0;
+    if (j < nc) {
+      kj = sh.ckey[j];
+      bj = sh.cbin[j];
+      for (int i = 0; i < nc; ++i) {
+        const uint64_t ki = sh.ckey[i];
+        const uint32_t ni = sh.nb[sh.cbin[i]];
+        if (ki > kj) above += ni;
+        if (ki == kj) eq += ni;
+      }
+    }
+    if ((int)threadIdx.x == 0) sh.bi[5] = 0;
+    __syncthreads();
+    const bool is_t = j < nc && above < need && need <= above + eq;
+    if (is_t) {  // every entry of the threshold key writes the same values
+      sh.bu[2] = kj;
+      sh.bu[3] = need - above;
+      if (need - above < eq) atomicAdd(&sh.bi[5], 1);
+    }
+    __syncthreads();
+    const uint64_t T = sh.bu[2];
+    need_t = sh.bu[3];
+    ntie = sh.bi[5];
+    uint32_t c = 0;
+    uint64_t key;
+    if (j < nc) fast_floor_key(sh.wb[bj], s64, c, key);
+    __syncthreads();
+    if (j < nc) {
+      const bool partial = kj == T && ntie > 0;
+      sh.nb[bj] = partial ? (kFT | c) : c + (kj >= T ? 1u : 0u);
+      if (partial) sh.bi[6] = (int)bj;
+    }
+    __syncthreads();
+    if (ntie == 1) tie_bin = sh.bi[6];
+    __syncthreads();
+  }
+  DSPARK_PHASE(16);
+  // F. a split tie: the need_t lowest ids among the members of the tie entries
+  const uint32_t D2 = fmap_dummy2();
+  const char* nbb = reinterpret_cast<const char*>(sh.nb);
+  int cut = -1;
+  if (ntie > 0) {
+    const uint32_t T2 = (uint32_t)(tie_bin * 4) * 0x10001u;
+    const bool one = tie_bin >= 0;
+    cut = res_locate(R, [&](int, u32x4 v) -> uint32_t {
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      uint32_t msk = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t o = fmap_off2(wv[c], f, D2);
+        bool lo, hi;
+        if (one) {
+          const uint32_t x = o ^ T2;
+          lo = (x & 0xffffu) == 0u;
+          hi = (x >> 16) == 0u;
+        } else {
+          lo = (*reinterpret_cast<const uint32_t*>(nbb + (o & 0xffffu)) & kFT) != 0u;
+          hi = (*reinterpret_cast<const uint32_t*>(nbb + (o >> 16)) & kFT) != 0u;
+        }
+        msk |= (lo ? 1u : 0u) << (2 * c);
+        msk |= (hi ? 1u : 0u) << (2 * c + 1);
+      }
+      return msk;
+    }, (uint32_t)(need_t - 1), sh);
+  }
+  DSPARK_PHASE(17);
+  // G. counts of every element
+  if ((int)threadIdx.x < NI) sh.tab[(int)threadIdx.x] = 0ull;
+  __syncthreads();
+  touch(R);
+  const int nvec = (V + 7) >> 3;
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
+  uint64_t total = 0;
+  auto counts8 = [&](u32x4 v, int q, uint32_t (&c)[8]) {
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    const int lim = cut - q * 8;  // lanes l <= lim are at or below the cut
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t o = fmap_off2(wv[k], f, D2);
+      const uint32_t tl = *reinterpret_cast<const uint32_t*>(nbb + (o & 0xffffu));
+      const uint32_t th = *reinterpret_cast<const uint32_t*>(nbb + (o >> 16));
+      c[2 * k] = (tl & (kFT - 1u)) + (((tl & kFT) && 2 * k <= lim) ? 1u : 0u);
+      c[2 * k + 1] = (th & (kFT - 1u)) + (((th & kFT) && 2 * k + 1 <= lim) ? 1u : 0u);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int q = i * BS + (int)threadIdx.x;
+    uint32_t c[8];
+    counts8(fetch(R, i), q, c);
+    uint32_t vs = 0;
+#pragma unroll
+    for (int l = 0; l < 8; ++l) vs += c[l];
+    if (q < nvec) {
+      if (q * 8 + 8 <= V && vec_ok) {
+        u32x4* dst = reinterpret_cast<u32x4*>(drow + (size_t)q * 8);
+        __builtin_nontemporal_store(u32x4{c[0], c[1], c[2], c[3]}, dst);
+        __builtin_nontemporal_store(u32x4{c[4], c[5], c[6], c[7]}, dst + 1);
+      } else {
+#pragma unroll
+        for (int l = 0; l < 8; ++l)
+          if (q * 8 + l < V) drow[(size_t)q * 8 + l] = c[l];
+      }
+    }
+    total += vs;
+    if (want_s && __ballot(vs != 0u)) {
+      const uint32_t w = wave_sum(vs);
+      if (lane_id() == 0 && w) atomicAdd((unsigned long long*)&sh.tab[i], (unsigned long long)w);
+    }
+  }
+  total = block_sum<uint64_t>(total, sh.bs);
+  if (total != kMass) {
+    res.status = DSPARK_ST_ALLOC_INCONSISTENT;
+    return res;
+  }
+  DSPARK_PHASE(18);
+  // H. the sample: the vector whose running total passes u, then a block scan
+  // of that vector's counts (recomputed from the registers)
+  if (want_s) {
+    if ((int)threadIdx.x == 0) {
+      uint64_t run = 0;
+      sh.bi[1] = -1;
+      for (int i = 0; i < NI; ++i) {
+        if (run + sh.tab[i] > u) {
+          sh.bi[1] = i;
+          sh.bu[1] = run;
+          break;
+        }
+        run += sh.tab[i];
+      }
+    }
+    __syncthreads();
+    const int istar = sh.bi[1];
+    const uint64_t u2 = (uint64_t)u - sh.bu[1];
+    uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int q = istar * BS + (int)threadIdx.x;
+    if (istar >= 0) counts8(select_vec(R, istar < 0 ? 0 : istar), q, c);
+    uint32_t vs = 0;
+#pragma unroll
+    for (int l = 0; l < 8; ++l) vs += c[l];
+    uint64_t tot;
+    const uint64_t pre = block_excl_scan<uint64_t>(vs, sh.bs, &tot);
+    if (istar >= 0 && vs && pre <= u2 && u2 < pre + vs) {
+      uint64_t run = pre;
+      int hit = -1;
+#pragma unroll
+      for (int l = 0; l < 8; ++l) {
+        run += c[l];
+        if (run > u2 && hit < 0) hit = l;
+      }
+      sh.bi[2] = q * 8 + hit;
+    }
+    __syncthreads();
+    res.token = istar >= 0 ? sh.bi[2] : -1;
+    __syncthreads();
+    if (res.token < 0) res.status = DSPARK_ST_ALLOC_INCONSISTENT;
+  }
+  return res;
+}
+
+// --------------------------------------------------------------- sparse
+// Support of the top-k by (logit desc, id asc) into (sh.cid, sh.sx) in
+// ascending id order, from the table (already filled by fast_hist).
+// Returns the support size, or -1 when the exact multi-pass selection must
+// decide (the threshold falls inside the collapsed entry, whose members are
+// distinct values, or the threshold entry is too large for the candidate
+// list).  Entries below the weight window would all get count 0
+// and be dropped, so the support is taken inside the window.
+__device__ __forceinline__ int fast_topk(Res& R, const FMap& f, int k, FastSparseShared& sh DSPARK_PHASE_PARAM) {
+  // total in-window count and the threshold entry
+  uint64_t tot = 0;
+  for (int b = (int)threadIdx.x; b < f.NB; b += BS) tot += sh.nb[b];
+  tot = block_sum<uint64_t>(tot, sh.bs);
+  const uint64_t need = (uint64_t)k < tot ? (uint64_t)k : tot;
+  if (need == 0) return 0;
+  uint64_t before;
+  const int bT = block_find_crossing(sh.nb, f.NB, need, true, sh, &before);
+  const uint32_t nT = sh.nb[bT];
+  const uint32_t need_t = (uint32_t)(need - before);
+  if (bT == f.B0 && f.tb1 > 0 && nT != need_t) return -1;
+  // keys (K16) of the smallest and largest values of the threshold entry
+  const bool coll = bT == f.B0 && f.tb1 > 0;
+  const int Klo = coll ? k16(0x8000u | (uint32_t)f.tb1) : k16(fmap_raw(bT, f));
+  const int Khi = coll ? k16((uint32_t)f.tb1) : Klo;
+  const int ncand = (int)(before + nT);
+  DSPARK_PHASE(1);
+  if (ncand > kCandCap) return -1;  // a large tie entry: the exact multi-pass selection decides
+  // candidates: every element with key >= Klo, as (K16 << 32 | id)
+  if ((int)threadIdx.x == 0) sh.bi[4] = 0;
+  uint32_t* bmA = sh.ctab;
+  for (int w = (int)threadIdx.x; w < NI * NW * 16; w += BS) {
+    bmA[w] = 0u;
+    sh.bmB[w] = 0u;
+  }
+  __syncthreads();
+  touch(R);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const u32x4 v = fetch(R, i);
+    const uint32_t msk = ge_mask(v, Klo);
+    const uint32_t n = (uint32_t)__builtin_popcount(msk);
+    if (__ballot(n != 0u)) {
+      const uint32_t inc = wave_incl_scan(n);
+      const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+      uint32_t wbase = 0;
+      if (lane_id() == 63) wbase = (uint32_t)atomicAdd(&sh.bi[4], (int)wtot);
+      wbase = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 63);
+      int pos = (int)(wbase + inc - n);
+      const uint32_t base = (uint32_t)((i * BS + (int)threadIdx.x) * 8);
+#pragma unroll
+      for (int l = 0; l < 8; ++l) {
+        if (msk & (1u << l)) {
+          if (pos < kCandCap) sh.ckey[pos] = ((uint64_t)k16(elem(v, l)) << 32) | (uint64_t)(base + (uint32_t)l);
+          ++pos;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int nc = sh.bi[4] < kCandCap ? sh.bi[4] : kCandCap;
+  // bitmaps over ids: A = above the threshold entry, B = its members
+  for (int e = (int)threadIdx.x; e < nc; e += BS) {
+    const uint64_t ck = sh.ckey[e];
+    const int K = (int)(ck >> 32);
+    const uint32_t id = (uint32_t)ck;
+    atomicOr(K > Khi ? &bmA[id >> 5] : &sh.bmB[id >> 5], 1u << (id & 31));
+  }
+  __syncthreads();
+  DSPARK_PHASE(2);
+  // the need_t lowest ids of B join A
+  {
+    const int w0 = (int)threadIdx.x * 4;
+    uint32_t bw[4], s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bw[j] = sh.bmB[w0 + j];
+      s += (uint32_t)__builtin_popcount(bw[j]);
+    }
+    uint32_t t;
+    uint32_t pre = block_excl_scan<uint32_t>(s, sh.bs, &t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t keep = bw[j];
+      const uint32_t pc = (uint32_t)__builtin_popcount(bw[j]);
+      if (pre >= need_t) {
+        keep = 0u;
+      } else if (pre + pc > need_t) {  // keep the first need_t - pre members of this word
+        uint32_t rem = need_t - pre, m = bw[j];
+        keep = 0u;
+        while (rem) {
+          const uint32_t low = m & (0u - m);
+          keep |= low;
+          m ^= low;
+          --rem;
+        }
+      }
+      pre += pc;
+      bmA[w0 + j] |= keep;
+    }
+  }
+  __syncthreads();
+  // ascending id order: per-word prefix of A in sh.hist
+  {
+    const int w0 = (int)threadIdx.x * 4;
+    uint32_t pc[4], s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pc[j] = (uint32_t)__builtin_popcount(bmA[w0 + j]);
+      s += pc[j];
+    }
+    uint32_t t;
+    uint32_t pre = block_excl_scan<uint32_t>(s, sh.bs, &t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sh.hist[w0 + j] = pre;
+      pre += pc[j];
+    }
+  }
+  __syncthreads();
+  for (int e = (int)threadIdx.x; e < nc; e += BS) {
+    const uint64_t ck = sh.ckey[e];
+    const uint32_t id = (uint32_t)ck;
+    const uint32_t wd = bmA[id >> 5];
+    if (wd & (1u << (id & 31))) {
+      const uint32_t r = sh.hist[id >> 5] + (uint32_t)__builtin_popcount(wd & ((1u << (id & 31)) - 1u));
+      if (r >= (uint32_t)DSPARK_K_MAX) continue;  // cannot happen: |A| = need <= k
+      sh.cid[r] = id;
+      sh.sx[r] = bf16_to_f32(bf16_of_k16((int)(ck >> 32)));
+    }
+  }
+  __syncthreads();
+  DSPARK_PHASE(3);
+  return (int)need;
+}
+
+}  // namespace dspark

@@ -83,7 +83,7 @@ __device__ __forceinline__ void res_load(Res& R, const uint16_t* p, int V) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int q = i * BS + (int)threadIdx.x;
-      store_vec(R, i, p4[q < nfull ? q : 0]);
+      store_vec(R, i, __builtin_nontemporal_load(p4 + (q < nfull ? q : 0)));  // read once: no cache reuse
     }
   }
 #pragma unroll

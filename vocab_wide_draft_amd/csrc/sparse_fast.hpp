@@ -73,9 +73,16 @@ __device__ __forceinline__ int res_topk_fast(Res& R, const RStats& st, int k, Ro
   for (int i = 0; i < NI; ++i) {
     const u32x4 v = fetch(R, i);
     const uint32_t msk = ge_mask(v, lo);
-    if (msk) {
-      const int n = __builtin_popcount(msk);
-      int pos = atomicAdd(&sh.bi[4], n);
+    // one LDS atomic per wave and vector: a wave-level exclusive scan of the
+    // lanes' hit counts gives each lane its slot after the wave's base
+    const uint32_t n = (uint32_t)__builtin_popcount(msk);
+    if (__ballot(n != 0u)) {
+      const uint32_t inc = wave_incl_scan(n);
+      const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+      uint32_t wbase = 0;
+      if (lane_id() == 63) wbase = (uint32_t)atomicAdd(&sh.bi[4], (int)wtot);
+      wbase = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 63);
+      int pos = (int)(wbase + inc - n);
       const uint32_t base = (uint32_t)((i * BS + (int)threadIdx.x) * 8);
 #pragma unroll
       for (int l = 0; l < 8; ++l) {
