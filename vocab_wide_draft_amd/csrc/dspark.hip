@@ -253,7 +253,7 @@ __device__ __forceinline__ void res_draft_sparse(const RowsArgs& a, int r, int k
     int n = -1;
     const bool table = f.NB <= kNBF;
     if (table) {  // value table: confidence and the exact top-k threshold
-      fast_hist(R, f, sh.fs.nb);
+      fast_hist<false>(R, f, sh.fs.nb);
       Acc acc;
       acc_zero(acc);
       double cs = 0.0;

@@ -29,7 +29,6 @@ namespace dspark {
 
 constexpr int kNBF = 10240;        // largest compressed table
 constexpr int kNBFD = kNBF + 64;   // plus one overflow slot per lane
-constexpr uint32_t kFT = 1u << 30; // tie flag of a final-count entry
 
 // Table layout of one row.  bin(x) = B0 - c(|x|) for x with the sign bit
 // clear, B0 + c(|x|) with it set, where c(a) = max(a, tb1) - tb1 on the
@@ -120,7 +119,8 @@ __device__ __forceinline__ double exp64(double x) {
 
 // --------------------------------------------------------------- shared
 struct FastDenseShared : SmemBase {
-  uint32_t nb[kNBFD];   // counts, then final counts (kFT: tie entry)
+  uint32_t nb[kNBFD];   // counts, then final counts (a tie entry holds its floor)
+  uint32_t tbm[kNBF / 32];  // tie entries (bitmap over entries)
   float wb[kNBF];       // binary32 weight of each occupied entry
   uint32_t kb[kNBF];    // top 32 bits of each entry's remainder key (0: r = 0)
   uint64_t ckey[kVdCand];
@@ -131,7 +131,10 @@ struct FastSparseShared : RowShared {
   uint32_t bmB[NI * NW * 16];  // bitmap of the threshold entry's members
 };
 
-// Histogram of the row into nb[0, NB) (overflow slots take the rest).
+// Histogram of the row into nb[0, NB) (overflow slots take the rest).  With
+// KEEP, every register word is replaced by its two table byte offsets, which
+// is all the later passes of the dense path need.
+template <bool KEEP>
 __device__ __forceinline__ void fast_hist(Res& R, const FMap& f, uint32_t* nb) {
   for (int b = (int)threadIdx.x; b < f.NB; b += BS) nb[b] = 0u;
   __syncthreads();
@@ -147,9 +150,25 @@ __device__ __forceinline__ void fast_hist(Res& R, const FMap& f, uint32_t* nb) {
       const uint32_t o = fmap_off2(w[c], f, D2);
       atomicAdd(reinterpret_cast<uint32_t*>(base + (o & 0xffffu)), 1u);
       atomicAdd(reinterpret_cast<uint32_t*>(base + (o >> 16)), 1u);
+      if (KEEP) R.w[i][c] = o;
     }
   }
   __syncthreads();
+}
+
+// 8-bit mask of the halves of vector v equal to T (T2 = T twice): a half h
+// is zero exactly when bit 15 of ((h & 0x7fff) + 0x7fff) | h is clear.
+__device__ __forceinline__ uint32_t eq16_mask8(u32x4 v, uint32_t T2) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t x = w[c] ^ T2;
+    const uint32_t z = ~(((x & 0x7fff7fffu) + 0x7fff7fffu) | x) & 0x80008000u;
+    m |= ((z >> 15) & 1u) << (2 * c);
+    m |= (z >> 31) << (2 * c + 1);
+  }
+  return m;
 }
 
 // Confidence sum (and, with W, the weights, their exact sum) over the table.
@@ -185,10 +204,11 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   QOut res{DSPARK_ST_OK, 0};
   const float m = bf16_to_f32(st.m_raw);
   const int NB = f.NB;
-  fast_hist(R, f, sh.nb);
-  // overflow slots read 0 from here on (the tie mask and the final pass
-  // look up out-of-window elements there)
+  fast_hist<true>(R, f, sh.nb);  // the registers now hold table offsets
+  // overflow slots read 0 from here on (the final pass looks up
+  // out-of-window elements there); no entry is a tie entry yet
   for (int b = NB + (int)threadIdx.x; b < kNBFD; b += BS) sh.nb[b] = 0u;
+  for (int w = (int)threadIdx.x; w < kNBF / 32; w += BS) sh.tbm[w] = 0u;
   DSPARK_PHASE(11);
   // A. weights, exact sum, confidence
   Acc acc;
@@ -289,7 +309,8 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
         sh.ckey[slot] = key;
         sh.cbin[slot] = (uint32_t)b;
       } else if (inb && mode == EXACT) {
-        sh.nb[b] = kFT | c;
+        sh.nb[b] = c;
+        atomicOr(&sh.tbm[b >> 5], 1u << (b & 31));
       } else {
         sh.nb[b] = c + ((above || (inb && mode == ALL)) ? 1u : 0u);
       }
@@ -299,7 +320,7 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   DSPARK_PHASE(15);
   // E. the threshold bucket's entries (CAND): exact weighted threshold
   uint64_t need_t = need;
-  int ntie = mode == EXACT ? 2 : 0;  // EXACT: tie entries carry kFT
+  int ntie = mode == EXACT ? 2 : 0;  // EXACT: the tie entries are marked in tbm
   int tie_bin = -1;
   if (mode == CAND) {
     const int nc = sh.bi[4];
@@ -334,45 +355,41 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
     __syncthreads();
     if (j < nc) {
       const bool partial = kj == T && ntie > 0;
-      sh.nb[bj] = partial ? (kFT | c) : c + (kj >= T ? 1u : 0u);
-      if (partial) sh.bi[6] = (int)bj;
+      sh.nb[bj] = c + (!partial && kj >= T ? 1u : 0u);
+      if (partial) {
+        sh.bi[6] = (int)bj;
+        atomicOr(&sh.tbm[bj >> 5], 1u << (bj & 31));
+      }
     }
     __syncthreads();
     if (ntie == 1) tie_bin = sh.bi[6];
     __syncthreads();
   }
   DSPARK_PHASE(16);
-  // F. a split tie: the need_t lowest ids among the members of the tie entries
-  const uint32_t D2 = fmap_dummy2();
+  // F. a split tie: the need_t lowest ids among the members of the tie
+  // entries (the registers hold table offsets)
   const char* nbb = reinterpret_cast<const char*>(sh.nb);
-  int cut = -1;
-  if (ntie > 0) {
-    const uint32_t T2 = (uint32_t)(tie_bin * 4) * 0x10001u;
-    const bool one = tie_bin >= 0;
-    cut = res_locate(R, [&](int, u32x4 v) -> uint32_t {
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-      uint32_t msk = 0;
+  const uint32_t T2 = (uint32_t)(tie_bin < 0 ? 0 : tie_bin * 4) * 0x10001u;
+  auto tie_mask = [&](u32x4 v) -> uint32_t {
+    if (tie_bin >= 0) return eq16_mask8(v, T2);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    uint32_t m = 0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t o = fmap_off2(wv[c], f, D2);
-        bool lo, hi;
-        if (one) {
-          const uint32_t x = o ^ T2;
-          lo = (x & 0xffffu) == 0u;
-          hi = (x >> 16) == 0u;
-        } else {
-          lo = (*reinterpret_cast<const uint32_t*>(nbb + (o & 0xffffu)) & kFT) != 0u;
-          hi = (*reinterpret_cast<const uint32_t*>(nbb + (o >> 16)) & kFT) != 0u;
-        }
-        msk |= (lo ? 1u : 0u) << (2 * c);
-        msk |= (hi ? 1u : 0u) << (2 * c + 1);
-      }
-      return msk;
-    }, (uint32_t)(need_t - 1), sh);
-  }
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t bl = (wv[c] & 0xffffu) >> 2, bh = wv[c] >> 18;
+      const uint32_t tl = bl < (uint32_t)kNBF ? (sh.tbm[bl >> 5] >> (bl & 31)) & 1u : 0u;
+      const uint32_t th = bh < (uint32_t)kNBF ? (sh.tbm[bh >> 5] >> (bh & 31)) & 1u : 0u;
+      m |= tl << (2 * c);
+      m |= th << (2 * c + 1);
+    }
+    return m;
+  };
+  int cut = -1;
+  if (ntie > 0) cut = res_locate(R, [&](int, u32x4 v) -> uint32_t { return tie_mask(v); }, (uint32_t)(need_t - 1), sh);
   DSPARK_PHASE(17);
-  // G. counts of every element
-  if ((int)threadIdx.x < NI) sh.tab[(int)threadIdx.x] = 0ull;
+  // G. counts of every element: the entry's count, plus one for the members of
+  // a tie entry at or below the cut (only vectors that start at or below it)
+  if ((int)threadIdx.x < NI) sh.tab[threadIdx.x] = 0ull;
   __syncthreads();
   touch(R);
   const int nvec = (V + 7) >> 3;
@@ -380,14 +397,16 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   uint64_t total = 0;
   auto counts8 = [&](u32x4 v, int q, uint32_t (&c)[8]) {
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-    const int lim = cut - q * 8;  // lanes l <= lim are at or below the cut
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t o = fmap_off2(wv[k], f, D2);
-      const uint32_t tl = *reinterpret_cast<const uint32_t*>(nbb + (o & 0xffffu));
-      const uint32_t th = *reinterpret_cast<const uint32_t*>(nbb + (o >> 16));
-      c[2 * k] = (tl & (kFT - 1u)) + (((tl & kFT) && 2 * k <= lim) ? 1u : 0u);
-      c[2 * k + 1] = (th & (kFT - 1u)) + (((th & kFT) && 2 * k + 1 <= lim) ? 1u : 0u);
+      c[2 * k] = *reinterpret_cast<const uint32_t*>(nbb + (wv[k] & 0xffffu));
+      c[2 * k + 1] = *reinterpret_cast<const uint32_t*>(nbb + (wv[k] >> 16));
+    }
+    const int lim = cut - q * 8;  // lanes l <= lim are at or below the cut
+    if (lim >= 0) {
+      const uint32_t m = tie_mask(v) & (lim >= 7 ? 0xffu : (2u << lim) - 1u);
+#pragma unroll
+      for (int l = 0; l < 8; ++l) c[l] += (m >> l) & 1u;
     }
   };
 #pragma unroll
