@@ -523,22 +523,15 @@ __device__ __forceinline__ int fast_topk(Res& R, const FMap& f, int k, FastSpars
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const u32x4 v = fetch(R, i);
-    const uint32_t msk = ge_mask(v, Klo);
-    const uint32_t n = (uint32_t)__builtin_popcount(msk);
-    if (__ballot(n != 0u)) {
-      const uint32_t inc = wave_incl_scan(n);
-      const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-      uint32_t wbase = 0;
-      if (lane_id() == 63) wbase = (uint32_t)atomicAdd(&sh.bi[4], (int)wtot);
-      wbase = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 63);
-      int pos = (int)(wbase + inc - n);
+    uint32_t msk = ge_mask(v, Klo);
+    if (msk) {  // one LDS atomic per lane holding candidates (few per row)
+      int pos = atomicAdd(&sh.bi[4], __builtin_popcount(msk));
       const uint32_t base = (uint32_t)((i * BS + (int)threadIdx.x) * 8);
-#pragma unroll
-      for (int l = 0; l < 8; ++l) {
-        if (msk & (1u << l)) {
-          if (pos < kCandCap) sh.ckey[pos] = ((uint64_t)k16(elem(v, l)) << 32) | (uint64_t)(base + (uint32_t)l);
-          ++pos;
-        }
+      while (msk) {
+        const int l = __builtin_ctz(msk);
+        msk &= msk - 1u;
+        if (pos < kCandCap) sh.ckey[pos] = ((uint64_t)k16(elem(v, l)) << 32) | (uint64_t)(base + (uint32_t)l);
+        ++pos;
       }
     }
   }

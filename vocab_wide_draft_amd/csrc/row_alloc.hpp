@@ -341,13 +341,13 @@ __device__ QOut dense_q(const Row<DT>& row, float m, uint32_t* drow, bool want_s
 }
 
 // dyadic24 counts on a support held in (sh.cid, sh.sx), ascending ids, n <= 1024
-// entries: weights, exact sum, floors, largest remainders (ties to the lower
-// id = earlier entry), positive entries out in id order, optional sample.
+// entries, one per thread (thread j holds entry j, so thread order is id
+// order): weights, exact sum, floors, largest remainders (ties to the lower
+// id), positive entries out in id order, optional sample.
 __device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, uint32_t* cnt_out, int32_t* len_out,
                               bool want_s, uint32_t u, RowShared& sh) {
   DSPARK_PHASE_BEGIN
   QOut res{DSPARK_ST_OK, 0};
-  // weights, exact sum, floors
   const int j = threadIdx.x;
   const bool have = j < n;
   float w = 0.0f;
@@ -358,74 +358,115 @@ __device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, 
     acc_add(acc, __float_as_uint(w));
   }
   const double s64 = block_acc_rn64(acc, sh.acc);
+  if (!(s64 > 0.0)) {
+    res.status = DSPARK_ST_ROW_ZERO_MASS;
+    return res;
+  }
   uint32_t c = 0;
   double r = 0.0;
   if (have) floor_rem(w, s64, c, r);
   const bool pos = have && r > 0.0;
   const uint64_t key = pos ? rem_key(r) : 0ull;
-  sh.ckey[j] = key;
-  const uint64_t csum = block_sum<uint64_t>(c, sh.bs);
-  const uint32_t npos = block_sum<uint32_t>(pos ? 1u : 0u, sh.bs);
-  const int64_t remaining = (int64_t)kMass - (int64_t)csum;
-  if (!(s64 > 0.0)) {
-    res.status = DSPARK_ST_ROW_ZERO_MASS;
-    return res;
-  }
-  if (remaining < 0 || remaining >= (int64_t)kMass || remaining > (int64_t)npos) {
+  // sum of floors (<= 2^24) and the number of positive remainders, in one reduction
+  const uint64_t fs = block_sum<uint64_t>((uint64_t)c | ((uint64_t)(pos ? 1u : 0u) << 32), sh.bs);
+  const int64_t remaining = (int64_t)kMass - (int64_t)(fs & 0xffffffffull);
+  const int64_t npos = (int64_t)(fs >> 32);
+  if (remaining < 0 || remaining >= (int64_t)kMass || remaining > npos) {
     res.status = DSPARK_ST_ALLOC_INCONSISTENT;
     return res;
   }
   DSPARK_PHASE(5);
-  // 5. largest remainders, ties to the lowest id (= support order j):
-  // bucket the keys by their top 11 bits, then rank inside the threshold
-  // bucket exactly by (key desc, j asc)
+  // the `remaining` largest remainders, ties to the lowest id.  Keys are
+  // bucketed by their top 11 bits; a small threshold bucket is ranked
+  // directly by (key desc, id asc); a large one (many equal weights) is
+  // narrowed by further 11-bit digits, and a tie left when the keys run out
+  // goes to the entries first in thread (= id) order.
   if (remaining > 0) {
+    uint64_t prefix = 0, pmask = 0x7ffull << 53, need = (uint64_t)remaining;
     for (int b = threadIdx.x; b < 2048; b += BS) sh.hist[b] = 0u;
     if (threadIdx.x == 0) sh.bi[4] = 0;
     __syncthreads();
     if (pos) atomicAdd(&sh.hist[key >> 53], 1u);
     __syncthreads();
     uint64_t before;
-    const int B = block_find_crossing(sh.hist, 2048, (uint64_t)remaining, false, sh, &before);
-    const uint32_t need_b = (uint32_t)((uint64_t)remaining - before);
-    const uint32_t bucket = pos ? (uint32_t)(key >> 53) : 0u;
-    const bool inb = pos && bucket == (uint32_t)B;
-    uint32_t* lj = sh.ctab;  // bucket members: index into ckey
-    if (inb) lj[atomicAdd(&sh.bi[4], 1)] = (uint32_t)j;
+    const int B = block_find_crossing(sh.hist, 2048, need, false, sh, &before);
+    need -= before;
+    const uint32_t cntB = sh.hist[B];
+    prefix = (uint64_t)B << 53;
+    uint32_t* lj = sh.ctab;  // bucket members
+    const bool inb = pos && (key >> 53) == (uint64_t)B;
+    if (inb && cntB <= 128u) lj[atomicAdd(&sh.bi[4], 1)] = (uint32_t)j;
+    sh.ckey[j] = key;
     __syncthreads();
-    const int nb = sh.bi[4];
-    bool sel = pos && bucket > (uint32_t)B;
-    if (inb) {
-      uint32_t rank = 0;
-      for (int f = 0; f < nb; ++f) {
-        const uint32_t o = lj[f];
-        const uint64_t ko = sh.ckey[o];
-        rank += (ko > key || (ko == key && o < (uint32_t)j)) ? 1u : 0u;
+    bool sel = pos && (key >> 53) > (uint64_t)B;
+    if (cntB == need) {
+      sel = sel || inb;
+    } else if (cntB <= 128u) {
+      if (inb) {
+        const int nb = (int)cntB;
+        uint32_t rank = 0;
+        for (int f = 0; f < nb; ++f) {
+          const uint32_t o = lj[f];
+          const uint64_t ko = sh.ckey[o];
+          rank += (ko > key || (ko == key && o < (uint32_t)j)) ? 1u : 0u;
+        }
+        sel = rank < need;
       }
-      sel = rank < need_b;
+    } else {
+      bool all_ge = false;
+      int shift = 42, nbits = 11;
+      for (;;) {
+        for (int b = threadIdx.x; b < 2048; b += BS) sh.hist[b] = 0u;
+        __syncthreads();
+        if (pos && (key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & ((1u << nbits) - 1u)], 1u);
+        __syncthreads();
+        const int d = block_find_crossing(sh.hist, 1 << nbits, need, false, sh, &before);
+        need -= before;
+        const uint32_t cnt = sh.hist[d];
+        __syncthreads();
+        prefix |= (uint64_t)d << shift;
+        pmask |= (uint64_t)((1u << nbits) - 1u) << shift;
+        if (cnt == need) {
+          all_ge = true;
+          break;
+        }
+        if (shift == 0) break;
+        const int nsh = shift > 11 ? shift - 11 : 0;
+        nbits = shift - nsh;
+        shift = nsh;
+      }
+      const uint64_t kp = key & pmask;
+      const bool tie = pos && kp == prefix;
+      sel = pos && kp > prefix;
+      if (all_ge) {
+        sel = sel || tie;
+      } else {  // keys equal to the threshold: the first `need` of them in id order
+        uint32_t nt;
+        const uint32_t before_t = block_excl_scan<uint32_t>(tie ? 1u : 0u, sh.bs, &nt);
+        sel = sel || (tie && before_t < need);
+      }
     }
     c += sel ? 1u : 0u;
   }
-  const uint64_t fsum = block_sum<uint64_t>(c, sh.bs);
-  if (fsum != kMass) {
+  DSPARK_PHASE(6);
+  // positive entries in id order and the sample, from one scan of
+  // (count, entry is positive)
+  uint64_t tot;
+  const uint64_t pre = block_excl_scan<uint64_t>((uint64_t)c | ((uint64_t)(c > 0 ? 1u : 0u) << 32), sh.bs, &tot);
+  if ((tot & 0xffffffffull) != kMass) {
     res.status = DSPARK_ST_ALLOC_INCONSISTENT;
     return res;
   }
-  DSPARK_PHASE(6);
-  // 6. positive entries in id order, and the sample
-  uint32_t len;
-  const uint32_t slot = block_excl_scan<uint32_t>(c > 0 ? 1u : 0u, sh.bs, &len);
+  const uint32_t slot = (uint32_t)(pre >> 32), cpre = (uint32_t)pre;
   if (c > 0) {
     ids_out[slot] = (int32_t)sh.cid[j];
     cnt_out[slot] = c;
   }
-  if (threadIdx.x == 0) *len_out = (int32_t)len;
+  if (threadIdx.x == 0) *len_out = (int32_t)(tot >> 32);
   if (want_s) {
-    uint32_t tot;
-    const uint32_t pre = block_excl_scan<uint32_t>(c, sh.bs, &tot);
     if (threadIdx.x == 0) sh.bi[5] = -1;
     __syncthreads();
-    if (c > 0 && pre <= u && u < pre + c) sh.bi[5] = (int)sh.cid[j];
+    if (c > 0 && cpre <= u && u < cpre + c) sh.bi[5] = (int)sh.cid[j];
     __syncthreads();
     res.token = sh.bi[5];
     __syncthreads();
