@@ -375,10 +375,15 @@ __device__ inline double block_acc_rn64(Acc a, AccScratch& s) {
   acc_merge(a, acc_dpp<0x143, 0xc>(a));
   if (lane_id() == 63) s.w[wave_id()] = a;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    Acc t = s.w[0];
-    for (int i = 1; i < NW; ++i) acc_merge(t, s.w[i]);
-    s.s64 = acc_rn64(t);
+  if (threadIdx.x < 64) {  // wave 0 merges the NW wave sums within its first row
+    Acc t;
+    if (threadIdx.x < NW) t = s.w[threadIdx.x];
+    else acc_zero(t);
+    acc_merge(t, acc_dpp<0xb1, 0xf>(t));
+    acc_merge(t, acc_dpp<0x4e, 0xf>(t));
+    acc_merge(t, acc_dpp<0x141, 0xf>(t));
+    acc_merge(t, acc_dpp<0x140, 0xf>(t));
+    if (threadIdx.x == 0) s.s64 = acc_rn64(t);
   }
   __syncthreads();
   const double r = s.s64;

@@ -253,7 +253,9 @@ __device__ __forceinline__ void res_draft_sparse(const RowsArgs& a, int r, int k
     int n = -1;
     const bool table = f.NB <= kNBF;
     if (table) {  // value table: confidence and the exact top-k threshold
+      DSPARK_PHASE(28);
       fast_hist<false>(R, f, sh.fs.nb);
+      DSPARK_PHASE(29);
       Acc acc;
       acc_zero(acc);
       double cs = 0.0;
@@ -262,15 +264,28 @@ __device__ __forceinline__ void res_draft_sparse(const RowsArgs& a, int r, int k
       DSPARK_PHASE(0);
       n = fast_topk(R, f, k, sh.fs DSPARK_PHASE_ARG);
     }
-    if (n < 0) {  // exact multi-pass selection
+    if (n < 0) {  // exact multi-pass selection, then the support moves to the sparse layout
       float cfe = 0.0f;
       n = sparse_exact(static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V, st.m_raw, k,
                        a.conf != nullptr && !table, &cfe);
       if (!table) cf = cfe;
+      const int j = threadIdx.x;
+      uint32_t id = 0;
+      float x = 0.0f;
+      if (j < n) {
+        id = sh.rs.cid[j];
+        x = sh.rs.sx[j];
+      }
+      __syncthreads();
+      if (j < n) {
+        sh.fs.cid[j] = id;
+        sh.fs.sx[j] = x;
+      }
+      __syncthreads();
     }
     DSPARK_PHASE(4);
     const QOut qo = support_alloc(m, n, a.sp_ids + (size_t)r * a.k_max, a.sp_cnt + (size_t)r * a.k_max,
-                                  a.sp_len + r, a.draws != nullptr, u, sh.rs);
+                                  a.sp_len + r, a.draws != nullptr, u, sh.fs);
     status = qo.status;
     tok = qo.token;
     DSPARK_PHASE(8);

@@ -35,6 +35,7 @@ constexpr int kNBFD = kNBF + 64;   // plus one overflow slot per lane
 // magnitude bits; magnitudes <= tb1 give c = 0, the collapsed entry B0.
 struct FMap {
   int B0, tb1, NB;
+  int NBc;  // entries of the values >= m - 28 (the confidence range)
   uint32_t Cp2, Tp2, Cn2, Tn2;  // the formula's constants, twice per word
 };
 
@@ -69,14 +70,17 @@ __device__ __forceinline__ FMap fmap_make(uint32_t m_raw) {
   }
   const int cm = fmap_c(mag_m, f.tb1);
   f.B0 = mneg ? -cm : cm;
-  // smallest bf16 >= m - 105 (binary32), never below the most negative finite value
+  // smallest bf16 >= m - t (binary32), never below the most negative finite value
   const float m = bf16_to_f32(m_raw);
-  const uint32_t b = __float_as_uint(m - 105.0f);
-  uint32_t hb = b >> 16;
-  if ((b & 0xffffu) && !(b & 0x80000000u)) hb += 1u;
-  hb &= 0xffffu;
-  if (hb > 0xff7fu) hb = 0xff7fu;
-  f.NB = fmap_bin(hb, f) + 1;
+  auto lowest_at_or_above = [&](float t) -> uint32_t {
+    const uint32_t b = __float_as_uint(m - t);
+    uint32_t hb = b >> 16;
+    if ((b & 0xffffu) && !(b & 0x80000000u)) hb += 1u;
+    hb &= 0xffffu;
+    return hb > 0xff7fu ? 0xff7fu : hb;
+  };
+  f.NB = fmap_bin(lowest_at_or_above(105.0f), f) + 1;
+  f.NBc = fmap_bin(lowest_at_or_above(28.0f), f) + 1;
   const uint32_t Cp = (uint32_t)(f.B0 + f.tb1) & 0xffffu, Tp = (uint32_t)f.tb1;
   const uint32_t Cn = (uint32_t)(f.B0 - f.tb1 - 0x8000) & 0xffffu, Tn = 0x8000u + (uint32_t)f.tb1;
   f.Cp2 = Cp * 0x10001u;
@@ -97,7 +101,8 @@ __device__ __forceinline__ uint32_t fmap_off2(uint32_t w, const FMap& f, uint32_
   const uint32_t s = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, w) >> (short)15);
   const uint32_t bin = (__builtin_bit_cast(uint32_t, neg) & s) | (__builtin_bit_cast(uint32_t, pos) & ~s);
   const u16x2 bc = __builtin_elementwise_min(__builtin_bit_cast(u16x2, bin), __builtin_bit_cast(u16x2, D2));
-  return __builtin_bit_cast(uint32_t, bc) << 2 & 0xfffcfffcu;
+  const u16x2 two = {2, 2};
+  return __builtin_bit_cast(uint32_t, bc << two);
 }
 __device__ __forceinline__ uint32_t fmap_dummy2() {
   const uint32_t d = (uint32_t)(kNBF + lane_id());
@@ -126,9 +131,16 @@ struct FastDenseShared : SmemBase {
   uint64_t ckey[kVdCand];
   uint32_t cbin[kVdCand];
 };
-struct FastSparseShared : RowShared {
+// The sparse layout keeps the table first (below 64 KB of LDS, so that its
+// base folds into the offset field of the LDS atomics).
+struct FastSparseShared : SmemBase {
   uint32_t nb[kNBFD];
-  uint32_t bmB[NI * NW * 16];  // bitmap of the threshold entry's members
+  uint32_t bmA[NI * NW * 16];  // bitmap over ids: selected elements
+  uint32_t bmB[NI * NW * 16];  // bitmap over ids: members of the threshold entry
+  uint64_t ckey[kCandCap];     // candidates (K16 << 32 | id); later remainder keys
+  uint32_t cid[kCandCap];      // support ids, ascending
+  float sx[DSPARK_K_MAX];      // support logits
+  uint32_t ctab[kMaxIter * NW];  // remainder bucket members
 };
 
 // Histogram of the row into nb[0, NB) (overflow slots take the rest).  With
@@ -172,15 +184,18 @@ __device__ __forceinline__ uint32_t eq16_mask8(u32x4 v, uint32_t T2) {
 }
 
 // Confidence sum (and, with W, the weights, their exact sum) over the table.
+// Entries more than 28 below the maximum are left out of the confidence sum:
+// together they add at most V e^-28 < 9e-8 to a sum that is at least 1.
 template <bool W>
 __device__ __forceinline__ void fast_pass_a(const FMap& f, float m, const uint32_t* nb, float* wb, Acc& acc,
                                             double& cs) {
   const double md = (double)m;
-  for (int b = (int)threadIdx.x; b < f.NB; b += BS) {
+  for (int b = (int)threadIdx.x; b < (W ? f.NB : f.NBc); b += BS) {
     const uint32_t n = nb[b];
     if (n) {
       const float x = bf16_to_f32(fmap_raw(b, f));
-      cs += (double)n * exp64((double)x - md);
+      const double dx = (double)x - md;
+      if (dx >= -28.0) cs += (double)n * exp64(dx);
       if (W) {
         const float w = cr_expf(x - m);
         wb[b] = w;
@@ -485,70 +500,143 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
 }
 
 // --------------------------------------------------------------- sparse
+// Candidates of vector v above a positive threshold: raw bf16 patterns
+// compare like signed 16-bit integers for positive values, and negative
+// values (sign bit set) are below.  Returns the four sign words: bit 15 / 31
+// of word c set for the low / high element of word c when it is a candidate.
+__device__ __forceinline__ void cand_words(u32x4 v, uint32_t rl2, uint32_t (&s)[4]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const s16x2 d = __builtin_elementwise_sub_sat(__builtin_bit_cast(s16x2, w[c]), __builtin_bit_cast(s16x2, rl2));
+    s[c] = ~__builtin_bit_cast(uint32_t, d) & 0x80008000u;
+  }
+}
+
 // Support of the top-k by (logit desc, id asc) into (sh.cid, sh.sx) in
 // ascending id order, from the table (already filled by fast_hist).
 // Returns the support size, or -1 when the exact multi-pass selection must
-// decide (the threshold falls inside the collapsed entry, whose members are
-// distinct values, or the threshold entry is too large for the candidate
-// list).  Entries below the weight window would all get count 0
-// and be dropped, so the support is taken inside the window.
+// decide: the threshold falls inside the collapsed entry (whose members are
+// distinct values), or the threshold entry is too large for the candidate
+// list.  Entries below the weight window would all get count 0 and be
+// dropped, so the support is taken inside the window.
 __device__ __forceinline__ int fast_topk(Res& R, const FMap& f, int k, FastSparseShared& sh DSPARK_PHASE_PARAM) {
-  // total in-window count and the threshold entry
-  uint64_t tot = 0;
-  for (int b = (int)threadIdx.x; b < f.NB; b += BS) tot += sh.nb[b];
-  tot = block_sum<uint64_t>(tot, sh.bs);
-  const uint64_t need = (uint64_t)k < tot ? (uint64_t)k : tot;
+  // in-window total and the threshold entry, from one scan over the table
+  {
+    const int per = (f.NB + BS - 1) / BS;
+    const int b0 = (int)threadIdx.x * per;
+    uint64_t s = 0;
+    for (int i = 0; i < per; ++i)
+      if (b0 + i < f.NB) s += sh.nb[b0 + i];
+    uint64_t tot;
+    const uint64_t pre = block_excl_scan<uint64_t>(s, sh.bs, &tot);
+    const uint64_t need = (uint64_t)k < tot ? (uint64_t)k : tot;
+    if (threadIdx.x == 0) {
+      sh.bu[0] = need;
+      sh.bi[0] = -1;
+    }
+    __syncthreads();
+    if (need > 0 && pre < need && need <= pre + s) {
+      uint64_t run = pre;
+      for (int i = 0; i < per; ++i) {
+        const uint32_t c = sh.nb[b0 + i];
+        if (run + c >= need) {
+          sh.bi[0] = b0 + i;
+          sh.bu[1] = run;
+          break;
+        }
+        run += c;
+      }
+    }
+    __syncthreads();
+  }
+  const uint64_t need = sh.bu[0];
   if (need == 0) return 0;
-  uint64_t before;
-  const int bT = block_find_crossing(sh.nb, f.NB, need, true, sh, &before);
+  const int bT = sh.bi[0];
+  const uint64_t before = sh.bu[1];
   const uint32_t nT = sh.nb[bT];
   const uint32_t need_t = (uint32_t)(need - before);
+  __syncthreads();
   if (bT == f.B0 && f.tb1 > 0 && nT != need_t) return -1;
   // keys (K16) of the smallest and largest values of the threshold entry
   const bool coll = bT == f.B0 && f.tb1 > 0;
   const int Klo = coll ? k16(0x8000u | (uint32_t)f.tb1) : k16(fmap_raw(bT, f));
   const int Khi = coll ? k16((uint32_t)f.tb1) : Klo;
-  const int ncand = (int)(before + nT);
+  if (before + nT > (uint64_t)kCandCap) return -1;  // a large tie entry: the exact multi-pass selection decides
   DSPARK_PHASE(1);
-  if (ncand > kCandCap) return -1;  // a large tie entry: the exact multi-pass selection decides
-  // candidates: every element with key >= Klo, as (K16 << 32 | id)
-  if ((int)threadIdx.x == 0) sh.bi[4] = 0;
-  uint32_t* bmA = sh.ctab;
-  for (int w = (int)threadIdx.x; w < NI * NW * 16; w += BS) {
-    bmA[w] = 0u;
+  // candidates (every element with key >= Klo): per-vector counts, one block
+  // scan for each thread's base, then the writes
+  for (int w = threadIdx.x; w < NI * NW * 16; w += BS) {
+    sh.bmA[w] = 0u;
     sh.bmB[w] = 0u;
   }
-  __syncthreads();
+  const bool posT = Klo > 0x8000;
+  const uint32_t rl2 = posT ? (uint32_t)(Klo - 0x8000) * 0x10001u : 0u;
+  uint32_t nib0 = 0, nib1 = 0, tot = 0;
   touch(R);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const u32x4 v = fetch(R, i);
-    uint32_t msk = ge_mask(v, Klo);
-    if (msk) {  // one LDS atomic per lane holding candidates (few per row)
-      int pos = atomicAdd(&sh.bi[4], __builtin_popcount(msk));
+    uint32_t cnt;
+    if (posT) {
+      uint32_t sw[4];
+      cand_words(v, rl2, sw);
+      cnt = (uint32_t)(__builtin_popcount(sw[0]) + __builtin_popcount(sw[1]) + __builtin_popcount(sw[2]) +
+                       __builtin_popcount(sw[3]));
+    } else {
+      cnt = (uint32_t)__builtin_popcount(ge_mask(v, Klo));
+    }
+    if (i < 8) nib0 |= cnt << (4 * i);
+    else nib1 |= cnt << (4 * (i - 8));
+    tot += cnt;
+  }
+  uint32_t nc;
+  uint32_t pos = block_excl_scan<uint32_t>(tot, sh.bs, &nc);
+  DSPARK_PHASE(27);
+  touch(R);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t cnt = ((i < 8 ? nib0 : nib1) >> (4 * (i & 7))) & 0xfu;
+    if (cnt) {  // candidates stored as (raw bf16 << 32 | id)
+      const u32x4 v = fetch(R, i);
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
       const uint32_t base = (uint32_t)((i * BS + (int)threadIdx.x) * 8);
-      while (msk) {
-        const int l = __builtin_ctz(msk);
-        msk &= msk - 1u;
-        if (pos < kCandCap) sh.ckey[pos] = ((uint64_t)k16(elem(v, l)) << 32) | (uint64_t)(base + (uint32_t)l);
-        ++pos;
+      uint32_t sw[4];
+      if (posT) {
+        cand_words(v, rl2, sw);
+      } else {
+        const uint32_t msk = ge_mask(v, Klo);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sw[c] = ((msk >> (2 * c)) & 1u) << 15 | ((msk >> (2 * c + 1)) & 1u) << 31;
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (sw[c]) {
+          if ((sw[c] & 0x8000u) && pos < (uint32_t)kCandCap)
+            sh.ckey[pos] = ((uint64_t)(wv[c] & 0xffffu) << 32) | (uint64_t)(base + 2 * c);
+          pos += (sw[c] >> 15) & 1u;
+          if ((sw[c] >> 31) && pos < (uint32_t)kCandCap)
+            sh.ckey[pos] = ((uint64_t)(wv[c] >> 16) << 32) | (uint64_t)(base + 2 * c + 1);
+          pos += sw[c] >> 31;
+        }
       }
     }
   }
   __syncthreads();
-  const int nc = sh.bi[4] < kCandCap ? sh.bi[4] : kCandCap;
+  DSPARK_PHASE(26);
+  if (nc > (uint32_t)kCandCap) nc = kCandCap;
   // bitmaps over ids: A = above the threshold entry, B = its members
-  for (int e = (int)threadIdx.x; e < nc; e += BS) {
+  for (int e = threadIdx.x; e < (int)nc; e += BS) {
     const uint64_t ck = sh.ckey[e];
-    const int K = (int)(ck >> 32);
+    const int K = k16((uint32_t)(ck >> 32));
     const uint32_t id = (uint32_t)ck;
-    atomicOr(K > Khi ? &bmA[id >> 5] : &sh.bmB[id >> 5], 1u << (id & 31));
+    atomicOr(K > Khi ? &sh.bmA[id >> 5] : &sh.bmB[id >> 5], 1u << (id & 31));
   }
   __syncthreads();
   DSPARK_PHASE(2);
   // the need_t lowest ids of B join A
   {
-    const int w0 = (int)threadIdx.x * 4;
+    const int w0 = threadIdx.x * 4;
     uint32_t bw[4], s = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -574,17 +662,17 @@ __device__ __forceinline__ int fast_topk(Res& R, const FMap& f, int k, FastSpars
         }
       }
       pre += pc;
-      bmA[w0 + j] |= keep;
+      sh.bmA[w0 + j] |= keep;
     }
   }
   __syncthreads();
   // ascending id order: per-word prefix of A in sh.hist
   {
-    const int w0 = (int)threadIdx.x * 4;
+    const int w0 = threadIdx.x * 4;
     uint32_t pc[4], s = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      pc[j] = (uint32_t)__builtin_popcount(bmA[w0 + j]);
+      pc[j] = (uint32_t)__builtin_popcount(sh.bmA[w0 + j]);
       s += pc[j];
     }
     uint32_t t;
@@ -596,15 +684,15 @@ __device__ __forceinline__ int fast_topk(Res& R, const FMap& f, int k, FastSpars
     }
   }
   __syncthreads();
-  for (int e = (int)threadIdx.x; e < nc; e += BS) {
+  for (int e = threadIdx.x; e < (int)nc; e += BS) {
     const uint64_t ck = sh.ckey[e];
     const uint32_t id = (uint32_t)ck;
-    const uint32_t wd = bmA[id >> 5];
+    const uint32_t wd = sh.bmA[id >> 5];
     if (wd & (1u << (id & 31))) {
       const uint32_t r = sh.hist[id >> 5] + (uint32_t)__builtin_popcount(wd & ((1u << (id & 31)) - 1u));
       if (r >= (uint32_t)DSPARK_K_MAX) continue;  // cannot happen: |A| = need <= k
       sh.cid[r] = id;
-      sh.sx[r] = bf16_to_f32(bf16_of_k16((int)(ck >> 32)));
+      sh.sx[r] = bf16_to_f32((uint32_t)(ck >> 32));
     }
   }
   __syncthreads();

@@ -344,8 +344,9 @@ __device__ QOut dense_q(const Row<DT>& row, float m, uint32_t* drow, bool want_s
 // entries, one per thread (thread j holds entry j, so thread order is id
 // order): weights, exact sum, floors, largest remainders (ties to the lower
 // id), positive entries out in id order, optional sample.
+template <class SH>
 __device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, uint32_t* cnt_out, int32_t* len_out,
-                              bool want_s, uint32_t u, RowShared& sh) {
+                              bool want_s, uint32_t u, SH& sh) {
   DSPARK_PHASE_BEGIN
   QOut res{DSPARK_ST_OK, 0};
   const int j = threadIdx.x;
