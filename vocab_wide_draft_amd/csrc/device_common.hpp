@@ -137,6 +137,22 @@ __device__ __forceinline__ T wave_incl_scan(T v) {
   return v;
 }
 
+// Wave 0 (all 64 lanes): the first i < n (n <= 64) with tab[0] + ... + tab[i] > u.
+// Returns it (-1 if the total is <= u) and *before = tab[0] + ... + tab[i-1];
+// the other waves get nothing.  One scan instead of a serial walk.
+__device__ __forceinline__ int wave_first_above(const uint64_t* tab, int n, uint64_t u, uint64_t* before) {
+  const int l = threadIdx.x & 63;
+  const uint64_t v = l < n ? tab[l] : 0ull;
+  const uint64_t inc = wave_incl_scan(v);
+  const uint64_t hit = __ballot(l < n && inc > u);
+  if (!hit) return -1;
+  const int i = __builtin_ctzll(hit);
+  const uint64_t exc = inc - v;
+  *before = (uint64_t)__builtin_amdgcn_readlane((int)(uint32_t)exc, i) |
+            ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(exc >> 32), i) << 32);
+  return i;
+}
+
 // Scratch for block-wide collectives (must be __shared__).
 struct BlockScratch {
   uint64_t w[NW + 1];

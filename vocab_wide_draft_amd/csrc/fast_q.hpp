@@ -458,31 +458,27 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   // H. the sample: the vector whose running total passes u, then a block scan
   // of that vector's counts (recomputed from the registers)
   if (want_s) {
-    if ((int)threadIdx.x == 0) {
-      uint64_t run = 0;
-      sh.bi[1] = -1;
-      for (int i = 0; i < NI; ++i) {
-        if (run + sh.tab[i] > u) {
-          sh.bi[1] = i;
-          sh.bu[1] = run;
-          break;
-        }
-        run += sh.tab[i];
+    if ((int)threadIdx.x < 64) {
+      uint64_t before = 0;
+      const int i = wave_first_above(sh.tab, NI, u, &before);
+      if (threadIdx.x == 0) {
+        sh.bi[1] = i;
+        sh.bu[1] = before;
       }
     }
     __syncthreads();
     const int istar = sh.bi[1];
-    const uint64_t u2 = (uint64_t)u - sh.bu[1];
+    const uint32_t u2 = (uint32_t)((uint64_t)u - sh.bu[1]);
     uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const int q = istar * BS + (int)threadIdx.x;
     if (istar >= 0) counts8(select_vec(R, istar < 0 ? 0 : istar), q, c);
     uint32_t vs = 0;
 #pragma unroll
     for (int l = 0; l < 8; ++l) vs += c[l];
-    uint64_t tot;
-    const uint64_t pre = block_excl_scan<uint64_t>(vs, sh.bs, &tot);
+    uint32_t tot;  // one vector's counts sum to at most M
+    const uint32_t pre = block_excl_scan<uint32_t>(vs, sh.bs, &tot);
     if (istar >= 0 && vs && pre <= u2 && u2 < pre + vs) {
-      uint64_t run = pre;
+      uint32_t run = pre;
       int hit = -1;
 #pragma unroll
       for (int l = 0; l < 8; ++l) {

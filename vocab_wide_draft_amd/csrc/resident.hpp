@@ -77,15 +77,17 @@ __device__ __forceinline__ void store_vec(Res& R, int i, u32x4 v) {
 // thread patches it from 2-byte loads.
 __device__ __forceinline__ void res_load(Res& R, const uint16_t* p, int V) {
   const int nfull = V >> 3;
-  const u32x4* p4 = reinterpret_cast<const u32x4*>(p);
   const u32x4 pad = {kNegInf2, kNegInf2, kNegInf2, kNegInf2};
-  if (nfull > 0) {
+  // A buffer resource that covers exactly the row: every load is the
+  // thread's offset plus a constant, all sixteen go out back to back, and
+  // lanes past the row end read zeros from the hardware bounds check
+  // (replaced by -inf below) instead of touching memory beyond the row.
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0, V * 2, 0x00020000);
+  const int toff = (int)threadIdx.x * 16;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int q = i * BS + (int)threadIdx.x;
-      store_vec(R, i, __builtin_nontemporal_load(p4 + (q < nfull ? q : 0)));  // read once: no cache reuse
-    }
-  }
+  for (int i = 0; i < NI; ++i)
+    store_vec(R, i, __builtin_amdgcn_raw_buffer_load_b128(rs, toff, i * BS * 16, 2));  // nt: read once
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int q = i * BS + (int)threadIdx.x;
@@ -232,16 +234,12 @@ __device__ __forceinline__ int res_locate(Res& R, MF mf, uint32_t u, SmemBase& s
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t run = 0;
-    sh.bi[1] = -1;
-    for (int i = 0; i < NI; ++i) {
-      if (run + sh.tab[i] > u) {
-        sh.bi[1] = i;
-        sh.bu[1] = run;
-        break;
-      }
-      run += sh.tab[i];
+  if (threadIdx.x < 64) {
+    uint64_t before = 0;
+    const int i = wave_first_above(sh.tab, NI, u, &before);
+    if (threadIdx.x == 0) {
+      sh.bi[1] = i;
+      sh.bu[1] = before;
     }
   }
   __syncthreads();
