@@ -248,6 +248,18 @@ def _table_rows(V, rng):
     rows.append(("subnormals", r))
     vals = np.array([0.0, 1e-9, -1e-9, 2.0, -1e-12], np.float32)
     rows.append(("tiny_dups", vals[rng.integers(0, vals.size, V)]))
+    # a tie entry holding a third of the row below a few hundred distinct
+    # larger values: top-k thresholds inside a tie too large to list
+    r = (rng.standard_normal(V) * 2 - 10).astype(np.float32)
+    r[rng.random(V) < 0.33] = 2.0
+    hi = rng.choice(V, min(200, V), replace=False)
+    r[hi] = rng.uniform(5.0, 10.0, hi.size).astype(np.float32)
+    rows.append(("big_tie_positive", r))
+    r = np.full(V, -3.0, np.float32)
+    hi = rng.choice(V, min(50, V), replace=False)
+    r[hi] = rng.uniform(-1.0, 0.0, hi.size).astype(np.float32)
+    r[rng.random(V) < 0.2] = -np.inf
+    rows.append(("big_tie_negative", r))
     return rows
 
 

@@ -34,7 +34,41 @@ extern __device__ unsigned long long g_phase[64];
   } while (0)
 #define DSPARK_PHASE_ARG , dspark_pt0_
 #define DSPARK_PHASE_PARAM , long long& dspark_pt0_
+// the same, once every outstanding vector memory access has completed
+#define DSPARK_PHASE_LOADED(k)                        \
+  do {                                                \
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); \
+    DSPARK_PHASE(k);                                  \
+  } while (0)
+// per-kind workgroup wall time (100 MHz counter) and shader cycles
+#define DSPARK_WG_BEGIN                                     \
+  const long long dspark_w0_ = wall_clock64(), dspark_c0_ = clock64();
+#define DSPARK_WG_END(kind)                                                                 \
+  do {                                                                                      \
+    __syncthreads();                                                                        \
+    if (threadIdx.x == 0) {                                                                 \
+      const long long w1_ = wall_clock64();                                                 \
+      atomicAdd(&g_phase[20 + (kind)], (unsigned long long)(w1_ - dspark_w0_));            \
+      atomicAdd(&g_phase[23 + (kind)], (unsigned long long)(clock64() - dspark_c0_));      \
+      atomicAdd(&g_phase[52 + (kind)], 1ull);                                               \
+      if (blockIdx.x < kTraceMax) {                                                         \
+        uint32_t hw_, xcc_;                                                                 \
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw_));                  \
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc_));                \
+        g_trace[3 * blockIdx.x] = (unsigned long long)dspark_w0_;                           \
+        g_trace[3 * blockIdx.x + 1] = (unsigned long long)w1_;                              \
+        g_trace[3 * blockIdx.x + 2] = ((unsigned long long)xcc_ << 32) | hw_ | ((unsigned long long)(kind) << 48); \
+      }                                                                                     \
+    }                                                                                       \
+  } while (0)
 #else
+#define DSPARK_PHASE_LOADED(k) \
+  do {                         \
+  } while (0)
+#define DSPARK_WG_BEGIN
+#define DSPARK_WG_END(kind) \
+  do {                      \
+  } while (0)
 #define DSPARK_PHASE_ARG
 #define DSPARK_PHASE_PARAM
 #define DSPARK_PHASE_BEGIN
@@ -159,50 +193,39 @@ struct BlockScratch {
 };
 
 // Block reductions: every thread calls, every thread gets the result.
-template <class T>
-__device__ __forceinline__ T block_sum(T v, BlockScratch& s) {
-  v = wave_sum(v);
+template <class T, class OP>
+__device__ __forceinline__ T block_reduce(T v, T id, OP op, BlockScratch& s) {
+  v = wave_reduce(v, id, op);
   if (lane_id() == 0) reinterpret_cast<T*>(s.w)[wave_id()] = v;
   __syncthreads();
   if (threadIdx.x < 64) {
-    T t = threadIdx.x < NW ? reinterpret_cast<T*>(s.w)[threadIdx.x] : T(0);
-    t = wave_sum(t);
+    T t = threadIdx.x < NW ? reinterpret_cast<T*>(s.w)[threadIdx.x] : id;
+    t = wave_reduce(t, id, op);
     if (threadIdx.x == 0) reinterpret_cast<T*>(s.w)[NW] = t;
   }
   __syncthreads();
   T r = reinterpret_cast<T*>(s.w)[NW];
   __syncthreads();
   return r;
+}
+template <class T>
+__device__ __forceinline__ T block_sum(T v, BlockScratch& s) {
+  return block_reduce(v, T(0), [](T a, T b) { return a + b; }, s);
 }
 template <class T>
 __device__ __forceinline__ T block_max(T v, BlockScratch& s) {
-  v = wave_max(v);
-  if (lane_id() == 0) reinterpret_cast<T*>(s.w)[wave_id()] = v;
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    T t = reinterpret_cast<T*>(s.w)[threadIdx.x < NW ? threadIdx.x : 0];
-    t = wave_max(t);
-    if (threadIdx.x == 0) reinterpret_cast<T*>(s.w)[NW] = t;
-  }
-  __syncthreads();
-  T r = reinterpret_cast<T*>(s.w)[NW];
-  __syncthreads();
-  return r;
+  return block_reduce(v, lowest_of(T()), [](T a, T b) { return b > a ? b : a; }, s);
 }
 template <class T>
 __device__ __forceinline__ T block_min(T v, BlockScratch& s) {
-  v = wave_min(v);
-  if (lane_id() == 0) reinterpret_cast<T*>(s.w)[wave_id()] = v;
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    T t = reinterpret_cast<T*>(s.w)[threadIdx.x < NW ? threadIdx.x : 0];
-    t = wave_min(t);
-    if (threadIdx.x == 0) reinterpret_cast<T*>(s.w)[NW] = t;
-  }
-  __syncthreads();
-  T r = reinterpret_cast<T*>(s.w)[NW];
-  __syncthreads();
-  return r;
+  return block_reduce(v, highest_of(T()), [](T a, T b) { return b < a ? b : a; }, s);
+}
+// maxima of the two unsigned 16-bit halves, independently
+__device__ __forceinline__ uint32_t block_max_u16x2(uint32_t v, BlockScratch& s) {
+  typedef unsigned short h2 __attribute__((ext_vector_type(2)));
+  return block_reduce(v, 0u, [](uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b)));
+  }, s);
 }
 // Exclusive prefix sum over threads in threadIdx order; *total gets the sum.
 template <class T>

@@ -17,6 +17,9 @@ namespace dspark {
 
 #ifdef DSPARK_PHASE_TIMING
 __device__ unsigned long long g_phase[64];
+// per-workgroup start / end (100 MHz wall clock) and hardware placement
+constexpr int kTraceMax = 16384;
+__device__ unsigned long long g_trace[3 * kTraceMax];
 #endif
 
 struct RowsArgs {
@@ -123,6 +126,7 @@ __device__ __forceinline__ void res_target_row(const RowsArgs& a, int r, SmemBas
   DSPARK_PHASE_BEGIN
   Res R;
   res_load(R, static_cast<const uint16_t*>(a.target) + (size_t)r * (size_t)a.t_stride, a.V);
+  DSPARK_PHASE_LOADED(31);
   const RStats st = res_stats(R, sh);
   const int am = st.status == DSPARK_ST_OK ? res_argmax(R, st, sh) : 0;
   DSPARK_PHASE(30);
@@ -196,6 +200,7 @@ __device__ __forceinline__ void res_draft_dense(const RowsArgs& a, int r, int ks
   DSPARK_PHASE_BEGIN
   Res R;
   res_load(R, static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V);
+  DSPARK_PHASE_LOADED(9);
   const uint32_t u = a.draws ? a.draws[r] : 0u;
   const bool dense_row = a.do_q && a.dense != nullptr && kstatus == DSPARK_ST_OK;
   uint32_t* drow = dense_row ? a.dense + (size_t)r * (size_t)a.V : nullptr;
@@ -240,6 +245,7 @@ __device__ __forceinline__ void res_draft_sparse(const RowsArgs& a, int r, int k
   DSPARK_PHASE_BEGIN
   Res R;
   res_load(R, static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V);
+  DSPARK_PHASE_LOADED(7);
   const uint32_t u = a.draws ? a.draws[r] : 0u;
   const RStats st = res_stats(R, sh.base);
   int status = st.status;
@@ -323,19 +329,24 @@ __device__ __forceinline__ void row_of_block(int b, int nd, int nt, bool* is_dra
 }
 
 __global__ void __launch_bounds__(BS) rows_bf16_kernel(RowsArgs a) {
+  DSPARK_WG_BEGIN
   ResShared& sh = g_res_sh;
   bool is_draft;
   int r;
   row_of_block((int)blockIdx.x, a.n_draft, a.n_target, &is_draft, &r);
   if (!is_draft) {
     res_target_row(a, r, sh.base);
+    DSPARK_WG_END(0);
     return;
   }
   int k, kstatus;
-  if (draft_kind(a, r, &k, &kstatus) == 1)
+  if (draft_kind(a, r, &k, &kstatus) == 1) {
     res_draft_sparse(a, r, k, sh);
-  else
+    DSPARK_WG_END(1);
+  } else {
     res_draft_dense(a, r, kstatus, sh);
+    DSPARK_WG_END(2);
+  }
 }
 
 // Greedy verification, one thread per request ("DeepSeek-V4.1 DSpark",
@@ -710,6 +721,12 @@ int dspark_cr_expf(const float* d, float* w, int64_t n, void* stream) {
 }  // extern "C"
 
 #ifdef DSPARK_PHASE_TIMING
+extern "C" int dspark_debug_trace(unsigned long long* out) {
+  if (hipMemcpyFromSymbol(out, HIP_SYMBOL(dspark::g_trace), sizeof(unsigned long long) * 3 * dspark::kTraceMax) !=
+      hipSuccess)
+    return -1;
+  return dspark::kTraceMax;
+}
 extern "C" int dspark_debug_phases(unsigned long long* out, int reset) {
   if (hipMemcpyFromSymbol(out, HIP_SYMBOL(dspark::g_phase), sizeof(unsigned long long) * 64) != hipSuccess) return -1;
   if (reset) {

@@ -23,7 +23,7 @@
 // of the confidence for any m).
 #pragma once
 #include "dense_vd.hpp"
-#include "sparse_fast.hpp"
+#include "resident.hpp"
 
 namespace dspark {
 
@@ -168,24 +168,14 @@ __device__ __forceinline__ void fast_hist(Res& R, const FMap& f, uint32_t* nb) {
   __syncthreads();
 }
 
-// 8-bit mask of the halves of vector v equal to T (T2 = T twice): a half h
-// is zero exactly when bit 15 of ((h & 0x7fff) + 0x7fff) | h is clear.
-__device__ __forceinline__ uint32_t eq16_mask8(u32x4 v, uint32_t T2) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t m = 0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint32_t x = w[c] ^ T2;
-    const uint32_t z = ~(((x & 0x7fff7fffu) + 0x7fff7fffu) | x) & 0x80008000u;
-    m |= ((z >> 15) & 1u) << (2 * c);
-    m |= (z >> 31) << (2 * c + 1);
-  }
-  return m;
-}
-
-// Confidence sum (and, with W, the weights, their exact sum) over the table.
-// Entries more than 28 below the maximum are left out of the confidence sum:
-// together they add at most V e^-28 < 9e-8 to a sum that is at least 1.
+// Over the table: with W, the weights and their exact sum; without, the
+// confidence sum.  Entries more than 28 below the maximum are left out of the
+// confidence sum: together they add at most V e^-28 < 9e-8 to a sum that is
+// at least 1.  (With W the confidence is 1 / RN64 of the exact weight sum:
+// each weight RN32(exp(RN32(x - m))) is within 2^-24 (1 + |x - m|) of
+// exp(x - m) relatively, and the e^(x-m)-weighted mean of |x - m| over at
+// most 2^17 terms, one of them 0, stays below 9, so the sum is within
+// 6e-7 relatively.)
 template <bool W>
 __device__ __forceinline__ void fast_pass_a(const FMap& f, float m, const uint32_t* nb, float* wb, Acc& acc,
                                             double& cs) {
@@ -194,12 +184,13 @@ __device__ __forceinline__ void fast_pass_a(const FMap& f, float m, const uint32
     const uint32_t n = nb[b];
     if (n) {
       const float x = bf16_to_f32(fmap_raw(b, f));
-      const double dx = (double)x - md;
-      if (dx >= -28.0) cs += (double)n * exp64(dx);
       if (W) {
         const float w = cr_expf(x - m);
         wb[b] = w;
         acc_add(acc, __float_as_uint(w), n);
+      } else {
+        const double dx = (double)x - md;
+        if (dx >= -28.0) cs += (double)n * exp64(dx);
       }
     }
   }
@@ -231,10 +222,7 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   double cs = 0.0;
   fast_pass_a<true>(f, m, sh.nb, sh.wb, acc, cs);
   const double s64 = block_acc_rn64(acc, sh.acc);
-  if (want_conf) {
-    const double t = block_sum<double>(cs, sh.bs);
-    *conf = (float)(1.0 / t);
-  }
+  if (want_conf) *conf = (float)(1.0 / s64);
   if (!(s64 > 0.0)) {
     res.status = DSPARK_ST_ROW_ZERO_MASS;
     return res;
@@ -509,13 +497,25 @@ __device__ __forceinline__ void cand_words(u32x4 v, uint32_t rl2, uint32_t (&s)[
   }
 }
 
+// The same test as an 8-bit mask in a fixed permuted order: bits 3..0 are
+// the low halves of words 0..3 (elements 0, 2, 4, 6) and bits 7..4 the high
+// halves of words 0..3 (elements 1, 3, 5, 7); cand_elem maps a bit back.
+__device__ __forceinline__ uint32_t cand_mask8(u32x4 v, uint32_t rl2) {
+  uint32_t s[4];
+  cand_words(v, rl2, s);
+  const uint32_t t = s[0] | (s[1] >> 1) | (s[2] >> 2) | (s[3] >> 3);
+  return ((t >> 12) & 0xfu) | ((t >> 24) & 0xf0u);
+}
+__device__ __forceinline__ int cand_elem(int b) { return b < 4 ? 6 - 2 * b : 15 - 2 * b; }
+
 // Support of the top-k by (logit desc, id asc) into (sh.cid, sh.sx) in
 // ascending id order, from the table (already filled by fast_hist).
 // Returns the support size, or -1 when the exact multi-pass selection must
 // decide: the threshold falls inside the collapsed entry (whose members are
-// distinct values), or the threshold entry is too large for the candidate
-// list.  Entries below the weight window would all get count 0 and be
-// dropped, so the support is taken inside the window.
+// distinct values) and takes only part of it, or takes all of a collapsed
+// entry too large for the candidate list.  Entries below the weight window
+// would all get count 0 and be dropped, so the support is taken inside the
+// window.
 __device__ __forceinline__ int fast_topk(Res& R, const FMap& f, int k, FastSparseShared& sh DSPARK_PHASE_PARAM) {
   // in-window total and the threshold entry, from one scan over the table
   {
@@ -558,64 +558,55 @@ __device__ __forceinline__ int fast_topk(Res& R, const FMap& f, int k, FastSpars
   const bool coll = bT == f.B0 && f.tb1 > 0;
   const int Klo = coll ? k16(0x8000u | (uint32_t)f.tb1) : k16(fmap_raw(bT, f));
   const int Khi = coll ? k16((uint32_t)f.tb1) : Klo;
-  if (before + nT > (uint64_t)kCandCap) return -1;  // a large tie entry: the exact multi-pass selection decides
+  // a threshold entry too large for the candidate list: its members go
+  // straight from the registers into bitmap B, the list takes only the
+  // elements above it (fewer than k).  The collapsed entry holds distinct
+  // values, so there the exact multi-pass selection decides.
+  const bool big = before + nT > (uint64_t)kCandCap;
+  if (big && coll) return -1;
+  const int Kc = big ? Khi + 1 : Klo;  // candidates: every element with key >= Kc
   DSPARK_PHASE(1);
-  // candidates (every element with key >= Klo): per-vector counts, one block
-  // scan for each thread's base, then the writes
+  // candidates: per-thread masks of the sixteen vectors (kept in four
+  // registers), one block scan for each thread's base, then the writes
   for (int w = threadIdx.x; w < NI * NW * 16; w += BS) {
     sh.bmA[w] = 0u;
-    sh.bmB[w] = 0u;
+    if (!big) sh.bmB[w] = 0u;
   }
-  const bool posT = Klo > 0x8000;
-  const uint32_t rl2 = posT ? (uint32_t)(Klo - 0x8000) * 0x10001u : 0u;
-  uint32_t nib0 = 0, nib1 = 0, tot = 0;
+  const bool posT = Kc > 0x8000;
+  const uint32_t rl2 = posT ? (uint32_t)(Kc - 0x8000) * 0x10001u : 0u;
+  const uint32_t T2 = fmap_raw(bT, f) * 0x10001u;
+  const bool tz = Klo == 0x8000;
+  uint8_t* bmb = reinterpret_cast<uint8_t*>(sh.bmB);  // byte q: elements 8q..8q+7
+  uint32_t M[4] = {0u, 0u, 0u, 0u};
   touch(R);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const u32x4 v = fetch(R, i);
-    uint32_t cnt;
-    if (posT) {
-      uint32_t sw[4];
-      cand_words(v, rl2, sw);
-      cnt = (uint32_t)(__builtin_popcount(sw[0]) + __builtin_popcount(sw[1]) + __builtin_popcount(sw[2]) +
-                       __builtin_popcount(sw[3]));
-    } else {
-      cnt = (uint32_t)__builtin_popcount(ge_mask(v, Klo));
-    }
-    if (i < 8) nib0 |= cnt << (4 * i);
-    else nib1 |= cnt << (4 * (i - 8));
-    tot += cnt;
+    const uint32_t m8 = posT ? cand_mask8(v, rl2) : ge_mask(v, Kc);
+    M[i >> 2] |= m8 << (8 * (i & 3));
+    if (big) bmb[i * BS + (int)threadIdx.x] = (uint8_t)eq16_mask8(v, T2, tz ? 0x7fff7fffu : 0xffffffffu);
   }
+  const uint32_t tot = (uint32_t)(__builtin_popcount(M[0]) + __builtin_popcount(M[1]) + __builtin_popcount(M[2]) +
+                                  __builtin_popcount(M[3]));
   uint32_t nc;
   uint32_t pos = block_excl_scan<uint32_t>(tot, sh.bs, &nc);
   DSPARK_PHASE(27);
   touch(R);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const uint32_t cnt = ((i < 8 ? nib0 : nib1) >> (4 * (i & 7))) & 0xfu;
-    if (cnt) {  // candidates stored as (raw bf16 << 32 | id)
+    uint32_t m8 = (M[i >> 2] >> (8 * (i & 3))) & 0xffu;
+    if (m8) {  // candidates stored as (raw bf16 << 32 | id)
       const u32x4 v = fetch(R, i);
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
       const uint32_t base = (uint32_t)((i * BS + (int)threadIdx.x) * 8);
-      uint32_t sw[4];
-      if (posT) {
-        cand_words(v, rl2, sw);
-      } else {
-        const uint32_t msk = ge_mask(v, Klo);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) sw[c] = ((msk >> (2 * c)) & 1u) << 15 | ((msk >> (2 * c + 1)) & 1u) << 31;
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (sw[c]) {
-          if ((sw[c] & 0x8000u) && pos < (uint32_t)kCandCap)
-            sh.ckey[pos] = ((uint64_t)(wv[c] & 0xffffu) << 32) | (uint64_t)(base + 2 * c);
-          pos += (sw[c] >> 15) & 1u;
-          if ((sw[c] >> 31) && pos < (uint32_t)kCandCap)
-            sh.ckey[pos] = ((uint64_t)(wv[c] >> 16) << 32) | (uint64_t)(base + 2 * c + 1);
-          pos += sw[c] >> 31;
-        }
-      }
+      do {
+        const int bt = __builtin_ctz(m8);
+        m8 &= m8 - 1u;
+        const int e = posT ? cand_elem(bt) : bt;
+        const uint32_t wd = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+        const uint32_t raw = (e & 1) ? wd >> 16 : wd & 0xffffu;
+        if (pos < (uint32_t)kCandCap) sh.ckey[pos] = ((uint64_t)raw << 32) | (uint64_t)(base + (uint32_t)e);
+        ++pos;
+      } while (m8);
     }
   }
   __syncthreads();
@@ -689,6 +680,24 @@ __device__ __forceinline__ int fast_topk(Res& R, const FMap& f, int k, FastSpars
       if (r >= (uint32_t)DSPARK_K_MAX) continue;  // cannot happen: |A| = need <= k
       sh.cid[r] = id;
       sh.sx[r] = bf16_to_f32((uint32_t)(ck >> 32));
+    }
+  }
+  if (big) {  // the chosen members of the threshold entry: in A and in B, not in the list
+    const float xT = bf16_to_f32(fmap_raw(bT, f));
+    const int w0 = threadIdx.x * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = sh.bmA[w0 + j], h = sh.hist[w0 + j];
+      uint32_t sel = a & sh.bmB[w0 + j];
+      while (sel) {
+        const int bt = __builtin_ctz(sel);
+        sel &= sel - 1u;
+        const uint32_t r = h + (uint32_t)__builtin_popcount(a & ((1u << bt) - 1u));
+        if (r < (uint32_t)DSPARK_K_MAX) {
+          sh.cid[r] = (uint32_t)((w0 + j) * 32 + bt);
+          sh.sx[r] = xT;
+        }
+      }
     }
   }
   __syncthreads();

@@ -110,7 +110,6 @@ struct RStats {
   int status;
   uint32_t m_raw;   // bf16 bits of the row maximum
   int smax_t;       // this thread's largest raw int16 (one of its elements)
-  uint32_t rep[4];  // packed raw int16 maxima per word position: 8 elements of this thread
 };
 
 // Row maximum and validity from packed int16 maxima of the raw bits: the
@@ -134,14 +133,14 @@ __device__ __forceinline__ RStats res_stats(Res& R, SmemBase& sh) {
     }
   }
   RStats s;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) s.rep[c] = __builtin_bit_cast(uint32_t, sm[c]);
   const s16x2 smax = __builtin_elementwise_max(__builtin_elementwise_max(sm[0], sm[1]),
                                                __builtin_elementwise_max(sm[2], sm[3]));
   s.smax_t = smax.x > smax.y ? smax.x : smax.y;
   const int um_t = umax.x > umax.y ? umax.x : umax.y;
-  const int S = block_max<int>(s.smax_t, sh.bs);
-  const int U = block_max<int>(um_t, sh.bs);
+  // one reduction for both: the signed maximum biased into the high half
+  const uint32_t SU = block_max_u16x2(((uint32_t)(s.smax_t + 0x8000) << 16) | (uint32_t)um_t, sh.bs);
+  const int S = (int)(SU >> 16) - 0x8000;
+  const int U = (int)(SU & 0xffffu);
   if (S > 0x7f80 || U > 0xff80) {
     s.status = DSPARK_ST_ROW_NAN;
     s.m_raw = 0;
@@ -174,18 +173,40 @@ __device__ __forceinline__ RStats res_stats(Res& R, SmemBase& sh) {
 // Lowest index holding the maximum (value compare, so -0 == +0).  For a
 // positive maximum only threads whose own signed maximum equals it can hold
 // it, so the other threads skip the scan.
+// 8-bit mask (bit l = element l) of the halves of vector v equal to T
+// (T2 = T twice) in the bits of M2 (both halves all ones: the whole pattern;
+// 0x7fff7fff: +0 and -0 alike): a half h is zero exactly when bit 15 of
+// ((h & 0x7fff) + 0x7fff) | h is clear.
+__device__ __forceinline__ uint32_t eq16_mask8(u32x4 v, uint32_t T2, uint32_t M2 = 0xffffffffu) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t x = (w[c] ^ T2) & M2;
+    const uint32_t z = ~(((x & 0x7fff7fffu) + 0x7fff7fffu) | x) & 0x80008000u;
+    m |= ((z >> 15) & 1u) << (2 * c);
+    m |= (z >> 31) << (2 * c + 1);
+  }
+  return m;
+}
+
 __device__ __forceinline__ int res_argmax(Res& R, const RStats& st, SmemBase& sh) {
   touch(R);
   const bool pos = st.m_raw > 0u && st.m_raw < 0x8000u;
   int first = 0x7fffffff;
-  if (!pos || (uint32_t)st.smax_t == st.m_raw) {
+  if (!pos || (uint32_t)st.smax_t == st.m_raw) {  // threads that can hold the maximum
     const float m = bf16_to_f32(st.m_raw);
+    const uint32_t T2 = st.m_raw * 0x10001u;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const u32x4 v = fetch(R, i);
       uint32_t msk = 0;
+      if (pos) {  // a positive maximum has one bit pattern
+        msk = eq16_mask8(v, T2);
+      } else {
 #pragma unroll
-      for (int l = 0; l < 8; ++l) msk |= (bf16_to_f32(elem(v, l)) == m ? 1u : 0u) << l;
+        for (int l = 0; l < 8; ++l) msk |= (bf16_to_f32(elem(v, l)) == m ? 1u : 0u) << l;
+      }
       if (msk && first == 0x7fffffff) first = (i * BS + (int)threadIdx.x) * 8 + __builtin_ctz(msk);
     }
   }
