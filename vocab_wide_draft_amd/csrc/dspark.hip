@@ -316,16 +316,50 @@ __device__ __forceinline__ int draft_kind(const RowsArgs& a, int r, int* k, int*
 }
 
 // One launch for every resident row of a call: block b handles row
-// row_of_block(b).  Draft and target blocks are interleaved in proportion to
+// row_of_block(b).  Draft and target rows are interleaved in proportion to
 // their numbers, so that at any moment some CUs stream target rows while
 // others run the on-chip allocation of draft rows, and the HBM traffic of the
-// first overlaps the computation of the second across the chip.  The row kind
-// is a function of blockIdx alone, so every branch below is uniform.
+// first overlaps the computation of the second across the chip.
+//
+// The order follows how the dispatcher places workgroups (as measured with
+// per-workgroup traces on MI355X): block b goes to XCD b mod 8 and, within
+// it, to shader engine (b / 8) mod 4, then to any free CU of that engine;
+// each XCD dispatches its blocks strictly in order and waits while the
+// engine whose turn it is has no free CU.  A row order whose costs differ
+// between engines therefore idles the other engines' CUs.  So the sequence
+// is cut into eight contiguous chunks (one per XCD), each chunk into four
+// contiguous streams (one per engine), and every stream is its own
+// proportional interleave of drafts and targets: every engine sees the same
+// mix at the same pace.  Each stream ends with up to kTailTargets target rows
+// (cheap; at most half of its targets, the rest keep overlapping the drafts),
+// so that the CUs of an engine run out of work together.  Only the speed
+// depends on this placement; any order is correct.  The row kind is a
+// function of blockIdx alone, so every branch below is uniform.
+constexpr int kTailTargets = 32;  // per engine stream
 __device__ __forceinline__ void row_of_block(int b, int nd, int nt, bool* is_draft, int* r) {
-  const int64_t n = (int64_t)nd + nt;
-  const int d0 = (int)((int64_t)b * nd / n), d1 = (int)((int64_t)(b + 1) * nd / n);
-  *is_draft = d1 > d0;
-  *r = *is_draft ? d0 : b - d0;
+  const int n = nd + nt;
+  // this XCD's chunk [L0, L0 + c) of the sequence, its drafts and targets
+  const int x = b & 7, q = n >> 3, rem = n & 7;
+  const int L0 = x * q + (x < rem ? x : rem), c = q + (x < rem ? 1 : 0);
+  const int D0 = (int)((int64_t)L0 * nd / n), ndc = (int)((int64_t)(L0 + c) * nd / n) - D0;
+  const int T0 = L0 - D0;
+  // this engine's stream: chunk positions j = 4 i + s, taken in order i
+  const int j = b >> 3, s = j & 3, i = j >> 2;
+  int off = 0;
+  for (int e = 0; e < s; ++e) off += (c - e + 3) >> 2;
+  const int cs = (c - s + 3) >> 2;
+  const int d0 = (int)((int64_t)off * ndc / c), nds = (int)((int64_t)(off + cs) * ndc / c) - d0;
+  const int nts = cs - nds, t0 = T0 + (off - d0);
+  const int t = nts / 2 < kTailTargets ? nts / 2 : kTailTargets;
+  const int m = cs - t;
+  if (i >= m) {
+    *is_draft = false;
+    *r = t0 + (nts - t) + (i - m);
+    return;
+  }
+  const int e0 = (int)((int64_t)i * nds / m), e1 = (int)((int64_t)(i + 1) * nds / m);
+  *is_draft = e1 > e0;
+  *r = *is_draft ? D0 + d0 + e0 : t0 + (i - e0);
 }
 
 __global__ void __launch_bounds__(BS) rows_bf16_kernel(RowsArgs a) {
