@@ -17,6 +17,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -29,12 +30,21 @@ CSRC = os.path.join(ROOT, "vocab_wide_draft_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def _code_tokens(src: str) -> str:
+    """C++ source without its comments, whitespace runs folded to one space:
+    edits to comments or layout leave the kernels, and so the hash, as they
+    were.  (The sources hold no string literal with // or /* in it.)"""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".hpp", ".inc")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + f.read())
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                h.update(name.encode() + _code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -294,8 +294,12 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     if (q < nvec) {
       if (q * 8 + 8 <= V && vec_ok) {
         u32x4* dst = reinterpret_cast<u32x4*>(drow + (size_t)q * 8);
-        __builtin_nontemporal_store(u32x4{c[0], c[1], c[2], c[3]}, dst);  // written once, streamed out
-        __builtin_nontemporal_store(u32x4{c[4], c[5], c[6], c[7]}, dst + 1);
+        // plain (write-back) stores: each instruction fills half of every
+        // 32-byte piece it touches, and L2 merges the two halves before the
+        // line goes out; streaming stores left part of them as separate
+        // partial writes (about a quarter more HBM write traffic)
+        dst[0] = u32x4{c[0], c[1], c[2], c[3]};
+        dst[1] = u32x4{c[4], c[5], c[6], c[7]};
       } else {
 #pragma unroll
         for (int l = 0; l < 8; ++l)

@@ -16,11 +16,13 @@
 // key between passes.  Rows whose table would exceed kNBF entries (a maximum
 // at or very near zero) take the general per-value path of dense_vd.hpp.
 //
-// The confidence 1 / sum_v exp(x_v - m) is also taken from the table: each
-// entry adds n * exp(x - m), with x - m exact in binary64; the collapsed entry
-// uses exp(-m), which is within a relative 2^(e_m - 26) of each of its terms
-// and holds at most a fraction V e^-m / (1 + V e^-m) of the sum (below 1.2e-7
-// of the confidence for any m).
+// The confidence 1 / sum_v exp(x_v - m) is also taken from the table.  A
+// dense row has the exact sum S of its weights and uses 1 / RN64(S) (error
+// bound at fast_pass_a).  A sparse row sums n * exp(x - m) per entry with
+// x - m exact in binary64; there the collapsed entry uses exp(-m), which is
+// within a relative 2^(e_m - 26) of each of its terms and holds at most a
+// fraction V e^-m / (1 + V e^-m) of the sum (below 1.2e-7 of the confidence
+// for any m).
 #pragma once
 #include "dense_vd.hpp"
 #include "resident.hpp"
@@ -423,8 +425,12 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
     if (q < nvec) {
       if (q * 8 + 8 <= V && vec_ok) {
         u32x4* dst = reinterpret_cast<u32x4*>(drow + (size_t)q * 8);
-        __builtin_nontemporal_store(u32x4{c[0], c[1], c[2], c[3]}, dst);
-        __builtin_nontemporal_store(u32x4{c[4], c[5], c[6], c[7]}, dst + 1);
+        // plain (write-back) stores: each instruction fills half of every
+        // 32-byte piece it touches, and L2 merges the two halves before the
+        // line goes out; streaming stores left part of them as separate
+        // partial writes (about a quarter more HBM write traffic)
+        dst[0] = u32x4{c[0], c[1], c[2], c[3]};
+        dst[1] = u32x4{c[4], c[5], c[6], c[7]};
       } else {
 #pragma unroll
         for (int l = 0; l < 8; ++l)
@@ -516,36 +522,69 @@ __device__ __forceinline__ int cand_elem(int b) { return b < 4 ? 6 - 2 * b : 15 
 // entry too large for the candidate list.  Entries below the weight window
 // would all get count 0 and be dropped, so the support is taken inside the
 // window.
+// Wave 0 (all 64 lanes): walks the table from its largest entry in chunks
+// of 256 (four consecutive entries per lane) until the running count reaches
+// `target`.  Returns the entry where it does (-1 if the whole table holds
+// fewer) with *before = the count of the entries above it; *seen = the count
+// walked (the table total when -1).  The top-k threshold of a row sits in the
+// first few chunks.
+__device__ __forceinline__ int wave0_top_crossing(const uint32_t* nb, int NB, uint32_t target, uint32_t* before,
+                                                  uint32_t* seen) {
+  const int l = threadIdx.x & 63;
+  uint32_t run = 0;
+  for (int base = 0; base < NB; base += 256) {
+    const int e = base + 4 * l;
+    uint32_t c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = e + i < NB ? nb[e + i] : 0u;
+    const uint32_t s = c[0] + c[1] + c[2] + c[3];
+    const uint32_t inc = wave_incl_scan(s);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    if (run + total >= target) {  // the crossing is in this chunk, in the first lane that reaches it
+      const uint64_t hit = __ballot(run + inc >= target);
+      const int lc = __builtin_ctzll(hit);
+      uint32_t r = run + (uint32_t)__builtin_amdgcn_readlane((int)(inc - s), lc);
+      int ent = -1;
+      uint32_t bef = 0;
+      if (l == lc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (ent < 0 && r + c[i] >= target) {
+            ent = e + i;
+            bef = r;
+          }
+          r += c[i];
+        }
+      }
+      *before = (uint32_t)__builtin_amdgcn_readlane((int)bef, lc);
+      *seen = run + total;
+      return __builtin_amdgcn_readlane(ent, lc);
+    }
+    run += total;
+  }
+  *before = run;
+  *seen = run;
+  return -1;
+}
+
 __device__ __forceinline__ int fast_topk(Res& R, const FMap& f, int k, FastSparseShared& sh DSPARK_PHASE_PARAM) {
-  // in-window total and the threshold entry, from one scan over the table
-  {
-    const int per = (f.NB + BS - 1) / BS;
-    const int b0 = (int)threadIdx.x * per;
-    uint64_t s = 0;
-    for (int i = 0; i < per; ++i)
-      if (b0 + i < f.NB) s += sh.nb[b0 + i];
-    uint64_t tot;
-    const uint64_t pre = block_excl_scan<uint64_t>(s, sh.bs, &tot);
-    const uint64_t need = (uint64_t)k < tot ? (uint64_t)k : tot;
+  // the threshold entry: where the count from the top reaches k, or, when the
+  // window holds fewer than k elements, the last occupied entry
+  if (threadIdx.x < 64) {
+    uint32_t before, seen;
+    int ent = wave0_top_crossing(sh.nb, f.NB, (uint32_t)k, &before, &seen);
+    uint32_t need = (uint32_t)k;
+    if (ent < 0) {
+      need = seen;
+      ent = need > 0 ? wave0_top_crossing(sh.nb, f.NB, need, &before, &seen) : -1;
+    }
     if (threadIdx.x == 0) {
       sh.bu[0] = need;
-      sh.bi[0] = -1;
+      sh.bi[0] = ent;
+      sh.bu[1] = before;
     }
-    __syncthreads();
-    if (need > 0 && pre < need && need <= pre + s) {
-      uint64_t run = pre;
-      for (int i = 0; i < per; ++i) {
-        const uint32_t c = sh.nb[b0 + i];
-        if (run + c >= need) {
-          sh.bi[0] = b0 + i;
-          sh.bu[1] = run;
-          break;
-        }
-        run += c;
-      }
-    }
-    __syncthreads();
   }
+  __syncthreads();
   const uint64_t need = sh.bu[0];
   if (need == 0) return 0;
   const int bT = sh.bi[0];

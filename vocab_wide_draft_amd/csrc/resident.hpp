@@ -200,14 +200,18 @@ __device__ __forceinline__ int res_argmax(Res& R, const RStats& st, SmemBase& sh
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const u32x4 v = fetch(R, i);
-      uint32_t msk = 0;
-      if (pos) {  // a positive maximum has one bit pattern
-        msk = eq16_mask8(v, T2);
+      if (pos) {  // a positive maximum has one bit pattern: a zero half of v ^ T2
+        const u16x2 x0 = __builtin_bit_cast(u16x2, v.x ^ T2), x1 = __builtin_bit_cast(u16x2, v.y ^ T2);
+        const u16x2 x2 = __builtin_bit_cast(u16x2, v.z ^ T2), x3 = __builtin_bit_cast(u16x2, v.w ^ T2);
+        const u16x2 p = __builtin_elementwise_min(__builtin_elementwise_min(x0, x1), __builtin_elementwise_min(x2, x3));
+        if ((p.x == 0 || p.y == 0) && first == 0x7fffffff)
+          first = (i * BS + (int)threadIdx.x) * 8 + __builtin_ctz(eq16_mask8(v, T2));
       } else {
+        uint32_t msk = 0;
 #pragma unroll
         for (int l = 0; l < 8; ++l) msk |= (bf16_to_f32(elem(v, l)) == m ? 1u : 0u) << l;
+        if (msk && first == 0x7fffffff) first = (i * BS + (int)threadIdx.x) * 8 + __builtin_ctz(msk);
       }
-      if (msk && first == 0x7fffffff) first = (i * BS + (int)threadIdx.x) * 8 + __builtin_ctz(msk);
     }
   }
   return block_min<int>(first, sh.bs);
