@@ -88,10 +88,14 @@ __device__ __forceinline__ void res_load(Res& R, const uint16_t* p, int V) {
 #pragma unroll
   for (int i = 0; i < NI; ++i)
     store_vec(R, i, __builtin_amdgcn_raw_buffer_load_b128(rs, toff, i * BS * 16, 2));  // nt: read once
+  // only vectors that reach past the last full one can hold padding lanes
+  // (a uniform test), so the others need not wait for their loads here
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int q = i * BS + (int)threadIdx.x;
-    if (q >= nfull) store_vec(R, i, pad);
+    if ((i + 1) * BS > nfull) {
+      const int q = i * BS + (int)threadIdx.x;
+      if (q >= nfull) store_vec(R, i, pad);
+    }
   }
   if ((V & 7) && (int)threadIdx.x == nfull % BS) {
     const int it = nfull / BS;
@@ -118,7 +122,8 @@ struct RStats {
 // unsigned maximum above -inf.  Rows with only negative values take one more
 // pass (their maximum has the smallest unsigned pattern).
 __device__ __forceinline__ RStats res_stats(Res& R, SmemBase& sh) {
-  touch(R);
+  // no touch of the whole row first: each vector is taken as soon as its own
+  // load has returned, so this pass overlaps the tail of the row load
   s16x2 sm[4] = {{(short)-32768, (short)-32768}, {(short)-32768, (short)-32768},
                  {(short)-32768, (short)-32768}, {(short)-32768, (short)-32768}};
   u16x2 umax = {0, 0};
