@@ -34,6 +34,9 @@
  *             the DSPARK_ST_* codes below.  Every output of a row or request
  *             with a nonzero status is zero (token 0, confidence 0.0,
  *             counts 0, sparse length 0, accept length 0, bonus 0) [C 6.3].
+ *   Empty.    A call with no rows (n_rows == 0, or no requests) checks its
+ *             scalar arguments and enqueues nothing; its array pointers may
+ *             then be NULL.
  *   Threads.  The library is stateless and reentrant.
  */
 #ifndef DSPARK_H

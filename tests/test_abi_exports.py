@@ -60,3 +60,24 @@ def test_argument_errors_enqueue_nothing():
     q = B.Q(None, 2000, 0, None, None, None, None)  # k_max too large
     assert lib.dspark_q_alloc(ctypes.byref(r), ctypes.byref(q), ctypes.c_void_p(16), None, 0, None) == -1
     assert lib.dspark_cr_expf(None, None, -1, None) == -1
+
+
+def test_empty_batches_need_no_arrays():
+    """No rows: the scalar arguments are checked and nothing is enqueued, so
+    every array pointer may be NULL (no GPU is touched)."""
+    lib = B.load_library()
+    r = B.Rows(None, 1, 0, 0, 1000, 1000)
+    t = B.Rows(None, 1, 0, 0, 1000, 1000)
+    q = B.Q(None, 8, 0, None, None, None, None)
+    assert lib.dspark_propose(ctypes.byref(r), None, None, None, None, 0, None) == 0
+    assert lib.dspark_q_alloc(ctypes.byref(r), ctypes.byref(q), None, None, 0, None) == 0
+    assert lib.dspark_sample(ctypes.byref(q), 0, 1000, None, 1, None, None, None) == 0
+    assert lib.dspark_fused(ctypes.byref(r), ctypes.byref(t), 1, ctypes.byref(q), *([None] * 10), None, 0,
+                            None) == 0
+    assert lib.dspark_fused(ctypes.byref(r), ctypes.byref(t), 0, None, *([None] * 10), None, 0, None) == 0
+    assert lib.dspark_verify_greedy(ctypes.byref(t), None, None, 0, *([None] * 5), None, 0, None) == 0
+    # the scalar checks still apply
+    assert lib.dspark_fused(ctypes.byref(r), ctypes.byref(t), 7, None, *([None] * 10), None, 0, None) == -1
+    assert lib.dspark_fused(ctypes.byref(r), ctypes.byref(t), 1, None, *([None] * 10), None, 0, None) == -1
+    bad = B.Q(None, 2000, 0, None, None, None, None)
+    assert lib.dspark_q_alloc(ctypes.byref(r), ctypes.byref(bad), None, None, 0, None) == -1

@@ -262,10 +262,7 @@ __device__ __forceinline__ void res_draft_sparse(const RowsArgs& a, int r, int k
       DSPARK_PHASE(28);
       fast_hist<false>(R, f, sh.fs.nb);
       DSPARK_PHASE(29);
-      Acc acc;
-      acc_zero(acc);
-      double cs = 0.0;
-      fast_pass_a<false>(f, m, sh.fs.nb, nullptr, acc, cs);
+      const double cs = fast_conf_sum(f, m, sh.fs.nb);
       if (a.conf) cf = (float)(1.0 / block_sum<double>(cs, sh.base.bs));
       DSPARK_PHASE(0);
       n = fast_topk(R, f, k, sh.fs DSPARK_PHASE_ARG);
@@ -543,13 +540,14 @@ int check_rows(const dspark_rows* r, const char* what) {
   return DSPARK_SUCCESS;
 }
 
-int check_q(const dspark_q* q, int64_t vocab) {
+// q storage checks; the arrays are only required when there are rows
+int check_q(const dspark_q* q, int64_t n_rows) {
   if (!q) return DSPARK_SUCCESS;
   if (q->k_max < 0 || q->k_max > DSPARK_K_MAX) return fail(DSPARK_EINVAL, "k_max must be in [0, DSPARK_K_MAX]");
+  if (n_rows == 0) return DSPARK_SUCCESS;
   if (!q->topk && !q->dense) return fail(DSPARK_EINVAL, "all rows dense but q->dense is NULL");
   if (q->topk && q->k_max > 0 && (!q->sp_ids || !q->sp_cnt || !q->sp_len))
     return fail(DSPARK_EINVAL, "sparse rows need sp_ids, sp_cnt and sp_len");
-  (void)vocab;
   return DSPARK_SUCCESS;
 }
 
@@ -634,7 +632,7 @@ int dspark_q_alloc(const dspark_rows* draft, const dspark_q* q, int32_t* row_sta
   int rc = check_rows(draft, "draft rows NULL");
   if (rc) return rc;
   if (!q) return fail(DSPARK_EINVAL, "q NULL");
-  if ((rc = check_q(q, draft->vocab))) return rc;
+  if ((rc = check_q(q, draft->n_rows))) return rc;
   if (draft->n_rows > 0 && !row_status) return fail(DSPARK_EINVAL, "NULL row_status");
   RowsArgs a = rows_args_draft(draft);
   a.row_status = row_status;
@@ -645,10 +643,10 @@ int dspark_q_alloc(const dspark_rows* draft, const dspark_q* q, int32_t* row_sta
 int dspark_sample(const dspark_q* q, int64_t n_rows, int64_t vocab, const uint32_t* draws,
                   int64_t draws_per_row, int32_t* tokens, int32_t* row_status, void* stream) {
   if (!q) return fail(DSPARK_EINVAL, "q NULL");
-  int rc = check_q(q, vocab);
-  if (rc) return rc;
   if (n_rows < 0 || vocab < 1 || vocab > DSPARK_V_MAX || draws_per_row < 1 || draws_per_row > (1 << 20))
     return fail(DSPARK_EINVAL, "bad n_rows, vocab or draws_per_row");
+  int rc = check_q(q, n_rows);
+  if (rc) return rc;
   if (n_rows == 0) return DSPARK_SUCCESS;
   if (!draws || !tokens || !row_status) return fail(DSPARK_EINVAL, "NULL draws, tokens or row_status");
   hipLaunchKernelGGL(sample_kernel, dim3((unsigned)n_rows), dim3(BS), 0, static_cast<hipStream_t>(stream),
@@ -705,11 +703,12 @@ int dspark_fused(const dspark_rows* draft, const dspark_rows* target, int32_t mo
   const int64_t R = draft->n_rows / DSPARK_N_DRAFT;
   if (target->n_rows != R * DSPARK_N_TARGET) return fail(DSPARK_EINVAL, "target must hold 6 rows per request");
   if (mode != DSPARK_GREEDY && mode != DSPARK_SAMPLED) return fail(DSPARK_EINVAL, "bad mode");
-  if (mode == DSPARK_SAMPLED && (!q || !draws || !sample))
-    return fail(DSPARK_EINVAL, "sampled mode needs q, draws and sample");
+  if (mode == DSPARK_SAMPLED && !q) return fail(DSPARK_EINVAL, "sampled mode needs q");
+  if ((rc = check_q(q, draft->n_rows))) return rc;
+  if (R == 0) return DSPARK_SUCCESS;
+  if (mode == DSPARK_SAMPLED && (!draws || !sample)) return fail(DSPARK_EINVAL, "sampled mode needs draws and sample");
   if ((draws == nullptr) != (sample == nullptr)) return fail(DSPARK_EINVAL, "draws and sample go together");
   if (draws && !q) return fail(DSPARK_EINVAL, "sampling needs q");
-  if ((rc = check_q(q, draft->vocab))) return rc;
   if (R > 0 && (!argmax || !conf || !row_status || !target_argmax || !target_status || !accept_len || !bonus ||
                 !req_status))
     return fail(DSPARK_EINVAL, "NULL output");

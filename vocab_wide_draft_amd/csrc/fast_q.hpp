@@ -18,7 +18,7 @@
 //
 // The confidence 1 / sum_v exp(x_v - m) is also taken from the table.  A
 // dense row has the exact sum S of its weights and uses 1 / RN64(S) (error
-// bound at fast_pass_a).  A sparse row sums n * exp(x - m) per entry with
+// bound at pass A of fast_dense_q).  A sparse row sums n * exp(x - m) per entry with
 // x - m exact in binary64; there the collapsed entry uses exp(-m), which is
 // within a relative 2^(e_m - 26) of each of its terms and holds at most a
 // fraction V e^-m / (1 + V e^-m) of the sum (below 1.2e-7 of the confidence
@@ -170,32 +170,20 @@ __device__ __forceinline__ void fast_hist(Res& R, const FMap& f, uint32_t* nb) {
   __syncthreads();
 }
 
-// Over the table: with W, the weights and their exact sum; without, the
-// confidence sum.  Entries more than 28 below the maximum are left out of the
-// confidence sum: together they add at most V e^-28 < 9e-8 to a sum that is
-// at least 1.  (With W the confidence is 1 / RN64 of the exact weight sum:
-// each weight RN32(exp(RN32(x - m))) is within 2^-24 (1 + |x - m|) of
-// exp(x - m) relatively, and the e^(x-m)-weighted mean of |x - m| over at
-// most 2^17 terms, one of them 0, stays below 9, so the sum is within
-// 6e-7 relatively.)
-template <bool W>
-__device__ __forceinline__ void fast_pass_a(const FMap& f, float m, const uint32_t* nb, float* wb, Acc& acc,
-                                            double& cs) {
+// The confidence sum over the table, n exp(x - m) per entry in binary64.
+// Entries more than 28 below the maximum are left out: together they add at
+// most V e^-28 < 9e-8 to a sum that is at least 1.
+__device__ __forceinline__ double fast_conf_sum(const FMap& f, float m, const uint32_t* nb) {
   const double md = (double)m;
-  for (int b = (int)threadIdx.x; b < (W ? f.NB : f.NBc); b += BS) {
+  double cs = 0.0;
+  for (int b = (int)threadIdx.x; b < f.NBc; b += BS) {
     const uint32_t n = nb[b];
     if (n) {
-      const float x = bf16_to_f32(fmap_raw(b, f));
-      if (W) {
-        const float w = cr_expf(x - m);
-        wb[b] = w;
-        acc_add(acc, __float_as_uint(w), n);
-      } else {
-        const double dx = (double)x - md;
-        if (dx >= -28.0) cs += (double)n * exp64(dx);
-      }
+      const double dx = (double)bf16_to_f32(fmap_raw(b, f)) - md;
+      if (dx >= -28.0) cs += (double)n * exp64(dx);
     }
   }
+  return cs;
 }
 
 // binary64 floor and exact remainder key of entry b
@@ -218,11 +206,21 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   for (int b = NB + (int)threadIdx.x; b < kNBFD; b += BS) sh.nb[b] = 0u;
   for (int w = (int)threadIdx.x; w < kNBF / 32; w += BS) sh.tbm[w] = 0u;
   DSPARK_PHASE(11);
-  // A. weights, exact sum, confidence
+  // A. weights and their exact sum; the confidence is 1 / RN64 of the sum:
+  // each weight RN32(exp(RN32(x - m))) is within 2^-24 (1 + |x - m|) of
+  // exp(x - m) relatively, and the e^(x-m)-weighted mean of |x - m| over at
+  // most 2^17 terms, one of them 0, stays below 9, so the sum is within 6e-7
+  // of sum exp(x - m) relatively
   Acc acc;
   acc_zero(acc);
-  double cs = 0.0;
-  fast_pass_a<true>(f, m, sh.nb, sh.wb, acc, cs);
+  for (int b = (int)threadIdx.x; b < NB; b += BS) {
+    const uint32_t n = sh.nb[b];
+    if (n) {
+      const float w = cr_expf(bf16_to_f32(fmap_raw(b, f)) - m);
+      sh.wb[b] = w;
+      acc_add(acc, __float_as_uint(w), n);
+    }
+  }
   const double s64 = block_acc_rn64(acc, sh.acc);
   if (want_conf) *conf = (float)(1.0 / s64);
   if (!(s64 > 0.0)) {
