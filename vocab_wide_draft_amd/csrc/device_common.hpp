@@ -20,7 +20,7 @@ constexpr int kMaxIter = 256;       // (V_MAX / 4) / BS vector iterations per ro
 // cycles since the previous hook of the workgroup to counter k (read with
 // dspark_debug_phases); otherwise they compile to nothing.
 #ifdef DSPARK_PHASE_TIMING
-extern __device__ unsigned long long g_phase[64];
+extern __device__ unsigned long long g_phase[128];  // [k] cycles, [64 + k] calls; [110 + ...] workgroups
 #define DSPARK_PHASE_BEGIN long long dspark_pt0_ = clock64();
 #define DSPARK_PHASE(k)                                                                   \
   do {                                                                                    \
@@ -28,7 +28,7 @@ extern __device__ unsigned long long g_phase[64];
     if (threadIdx.x == 0) {                                                               \
       const long long t_ = clock64();                                                     \
       atomicAdd(&g_phase[k], (unsigned long long)(t_ - dspark_pt0_));                     \
-      atomicAdd(&g_phase[32 + (k)], 1ull);                                                \
+      atomicAdd(&g_phase[64 + (k)], 1ull);                                                \
       dspark_pt0_ = t_;                                                                   \
     }                                                                                     \
   } while (0)
@@ -48,9 +48,9 @@ extern __device__ unsigned long long g_phase[64];
     __syncthreads();                                                                        \
     if (threadIdx.x == 0) {                                                                 \
       const long long w1_ = wall_clock64();                                                 \
-      atomicAdd(&g_phase[20 + (kind)], (unsigned long long)(w1_ - dspark_w0_));            \
-      atomicAdd(&g_phase[23 + (kind)], (unsigned long long)(clock64() - dspark_c0_));      \
-      atomicAdd(&g_phase[52 + (kind)], 1ull);                                               \
+      atomicAdd(&g_phase[110 + (kind)], (unsigned long long)(w1_ - dspark_w0_));           \
+      atomicAdd(&g_phase[113 + (kind)], (unsigned long long)(clock64() - dspark_c0_));     \
+      atomicAdd(&g_phase[116 + (kind)], 1ull);                                              \
       if (blockIdx.x < kTraceMax) {                                                         \
         uint32_t hw_, xcc_;                                                                 \
         asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw_));                  \

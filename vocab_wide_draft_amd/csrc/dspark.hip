@@ -16,7 +16,7 @@
 namespace dspark {
 
 #ifdef DSPARK_PHASE_TIMING
-__device__ unsigned long long g_phase[64];
+__device__ unsigned long long g_phase[128];
 // per-workgroup start / end (100 MHz wall clock) and hardware placement
 constexpr int kTraceMax = 16384;
 __device__ unsigned long long g_trace[3 * kTraceMax];
@@ -128,6 +128,7 @@ __device__ __forceinline__ void res_target_row(const RowsArgs& a, int r, SmemBas
   res_load(R, static_cast<const uint16_t*>(a.target) + (size_t)r * (size_t)a.t_stride, a.V);
   DSPARK_PHASE_LOADED(31);
   const RStats st = res_stats(R, sh);
+  DSPARK_PHASE(32);
   const int am = st.status == DSPARK_ST_OK ? res_argmax(R, st, sh) : 0;
   DSPARK_PHASE(30);
   if (threadIdx.x == 0) {
@@ -205,6 +206,7 @@ __device__ __forceinline__ void res_draft_dense(const RowsArgs& a, int r, int ks
   const bool dense_row = a.do_q && a.dense != nullptr && kstatus == DSPARK_ST_OK;
   uint32_t* drow = dense_row ? a.dense + (size_t)r * (size_t)a.V : nullptr;
   const RStats st = res_stats(R, sh.base);
+  DSPARK_PHASE(35);
   int status = st.status != DSPARK_ST_OK ? st.status : kstatus;
   if (status == DSPARK_ST_OK && a.draws && u >= kMass) status = DSPARK_ST_DRAW_RANGE;
   int am = 0, tok = 0;
@@ -248,6 +250,7 @@ __device__ __forceinline__ void res_draft_sparse(const RowsArgs& a, int r, int k
   DSPARK_PHASE_LOADED(7);
   const uint32_t u = a.draws ? a.draws[r] : 0u;
   const RStats st = res_stats(R, sh.base);
+  DSPARK_PHASE(34);
   int status = st.status;
   if (status == DSPARK_ST_OK && a.draws && u >= kMass) status = DSPARK_ST_DRAW_RANGE;
   int am = 0, tok = 0;
@@ -761,9 +764,9 @@ extern "C" int dspark_debug_trace(unsigned long long* out) {
   return dspark::kTraceMax;
 }
 extern "C" int dspark_debug_phases(unsigned long long* out, int reset) {
-  if (hipMemcpyFromSymbol(out, HIP_SYMBOL(dspark::g_phase), sizeof(unsigned long long) * 64) != hipSuccess) return -1;
+  if (hipMemcpyFromSymbol(out, HIP_SYMBOL(dspark::g_phase), sizeof(unsigned long long) * 128) != hipSuccess) return -1;
   if (reset) {
-    unsigned long long z[64] = {0};
+    unsigned long long z[128] = {0};
     if (hipMemcpyToSymbol(HIP_SYMBOL(dspark::g_phase), z, sizeof z) != hipSuccess) return -2;
   }
   return 0;
