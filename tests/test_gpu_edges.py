@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import dyadic24 as O
 from vocab_wide_draft_amd import binding as B
 from vocab_wide_draft_amd import workloads as W
 
@@ -66,3 +67,50 @@ def test_vocabulary_limits(dtype, V):
     out = B.fused(dd, td, B.SAMPLED, topk=w.topk, k_max=1024, draws=u32_dev(w.draws))
     torch.cuda.synchronize()
     check_workload(w, host(out), label=f"{dtype} V{V}")
+
+
+def _special_target_rows(V, rng):
+    """Target rows (binary32 values) for every status and every kind of
+    maximum: NaN, +inf, all -inf, -0 before +0, all negative, constant,
+    one-hot at the last id, ordinary."""
+    base = (rng.standard_normal(V) * 2).astype(np.float32)
+    rows = []
+    r = base.copy(); r[V // 3] = np.nan; rows.append(r)
+    r = base.copy(); r[V - 1] = np.inf; rows.append(r)
+    rows.append(np.full(V, -np.inf, np.float32))
+    r = np.full(V, -1.0, np.float32); r[1 % V] = -0.0; r[V // 2] = 0.0; rows.append(r)
+    rows.append(-np.abs(base) - 0.5)
+    rows.append(np.full(V, 3.0, np.float32))
+    r = np.full(V, -np.inf, np.float32); r[V - 1] = -7.25; rows.append(r)
+    rows.append(base)
+    r = base.copy(); r[::7] = -np.inf; rows.append(r)
+    r = np.zeros(V, np.float32); r[::2] = -0.0; rows.append(r)
+    r = base.copy(); r[5 % V] = r.max(); r[V - 2] = r.max(); rows.append(r)
+    rows.append((base - 200.0).astype(np.float32))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("V", [129280, 129283, 5001, 64])
+def test_target_rows_every_maximum(V):
+    """Target argmax and status for rows of every kind of maximum, through
+    the verify entry point and the fused step (bf16 and fp32)."""
+    rng = np.random.default_rng(V + 11)
+    x = _special_target_rows(V, rng)
+    R = x.shape[0] // 6
+    for dtype in ("bf16", "f32"):
+        raw = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+        t = to_dev(raw, dtype)
+        dtok = torch.from_numpy(rng.integers(0, V, size=(R, 5), dtype=np.int32)).to(dev())
+        out = host(B.verify_greedy(t, dtok))
+        for j in range(x.shape[0]):
+            f = O.to_f32(raw[j], dtype)
+            st = O.row_status(f)
+            assert int(out["target_status"][j]) == st, (dtype, V, j)
+            want = O.argmax_first(f)[1] if st == O.ST_OK else 0
+            assert int(out["target_argmax"][j]) == want, (dtype, V, j)
+        # the fused step with ordinary draft rows
+        d = (rng.standard_normal((5 * R, V)) * 2).astype(np.float32)
+        draw = W.f32_to_bf16_bits(d) if dtype == "bf16" else d
+        w = SimpleNamespace(R=R, V=V, dtype=dtype, mode="greedy", draft=draw, target=raw, topk=None, draws=None)
+        f = host(B.fused(to_dev(draw, dtype), t, B.GREEDY, with_q=False))
+        check_workload(w, f, label=f"targets {dtype} V{V}")
