@@ -150,14 +150,6 @@ __device__ __forceinline__ float lowest_of(float) { return -__builtin_inff(); }
 __device__ __forceinline__ int highest_of(int) { return 2147483647; }
 __device__ __forceinline__ uint32_t highest_of(uint32_t) { return 0xffffffffu; }
 __device__ __forceinline__ float highest_of(float) { return __builtin_inff(); }
-template <class T>
-__device__ __forceinline__ T wave_max(T v) {
-  return wave_reduce(v, lowest_of(T()), [](T a, T b) { return b > a ? b : a; });
-}
-template <class T>
-__device__ __forceinline__ T wave_min(T v) {
-  return wave_reduce(v, highest_of(T()), [](T a, T b) { return b < a ? b : a; });
-}
 // inclusive prefix sum over the 64 lanes: row shifts by 1, 2, 4, 8 (scan
 // inside each row of 16), then the row broadcasts of lanes 15 and 31
 template <class T>
@@ -347,19 +339,6 @@ __device__ __forceinline__ void acc_add(Acc& a, uint32_t wb, uint32_t n = 1) {
     add128(a.tlo, a.thi, lo, hi);
   }
 }
-__device__ __forceinline__ void acc_merge(Acc& a, const Acc& b) {
-  add128(a.mlo, a.mhi, b.mlo, b.mhi);
-  add128(a.tlo, a.thi, b.tlo, b.thi);
-}
-template <int CTRL, int RM>
-__device__ __forceinline__ Acc acc_dpp(const Acc& a) {
-  Acc b;
-  b.mlo = dpp_t<CTRL, RM, 0xf, uint64_t>(uint64_t(0), a.mlo);
-  b.mhi = dpp_t<CTRL, RM, 0xf, uint64_t>(uint64_t(0), a.mhi);
-  b.tlo = dpp_t<CTRL, RM, 0xf, uint64_t>(uint64_t(0), a.tlo);
-  b.thi = dpp_t<CTRL, RM, 0xf, uint64_t>(uint64_t(0), a.thi);
-  return b;
-}
 struct AccScratch {
   Acc w[NW];
   double s64;
@@ -403,26 +382,87 @@ __device__ inline double acc_rn64(const Acc& a) {
   if (rb && (sticky || (mant & 1ull))) mant += 1;
   return __builtin_ldexp((double)mant, sh - 149);  // mant may be 2^53: still exact
 }
-// Block-wide exact sum; every thread gets RN64(S).
+// One step of a wave-wide sum of 128-bit integers held as four 32-bit limbs
+// (lowest first): every enabled lane adds the limbs of the lane that the DPP
+// control names, the carry running through VCC; rows outside the row mask
+// keep their value.  The leading s_nop covers the two wait states a DPP read
+// needs after a VALU write of the same register.
+#define DSPARK_ADD128_DPP(L0, L1, L2, L3, DPP)                              \
+  asm volatile("s_nop 1\n\t"                                               \
+               "v_add_co_u32_dpp %0, vcc, %0, %0 " DPP "\n\t"              \
+               "v_addc_co_u32_dpp %1, vcc, %1, %1, vcc " DPP "\n\t"        \
+               "v_addc_co_u32_dpp %2, vcc, %2, %2, vcc " DPP "\n\t"        \
+               "v_addc_co_u32_dpp %3, vcc, %3, %3, vcc " DPP                \
+               : "+v"(L0), "+v"(L1), "+v"(L2), "+v"(L3)                     \
+               :                                                            \
+               : "vcc")
+struct Limbs4 {
+  uint32_t l0, l1, l2, l3;
+};
+__device__ __forceinline__ Limbs4 limbs_of(uint64_t lo, uint64_t hi) {
+  return Limbs4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+}
+__device__ __forceinline__ uint64_t limbs_lo(const Limbs4& x) { return ((uint64_t)x.l1 << 32) | x.l0; }
+__device__ __forceinline__ uint64_t limbs_hi(const Limbs4& x) { return ((uint64_t)x.l3 << 32) | x.l2; }
+// the sum of the word over the 16 lanes of each row, in every lane of the row
+__device__ __forceinline__ void add128_rows(Limbs4& x) {
+  DSPARK_ADD128_DPP(x.l0, x.l1, x.l2, x.l3, "quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf");
+  DSPARK_ADD128_DPP(x.l0, x.l1, x.l2, x.l3, "quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf");
+  DSPARK_ADD128_DPP(x.l0, x.l1, x.l2, x.l3, "row_half_mirror row_mask:0xf bank_mask:0xf");
+  DSPARK_ADD128_DPP(x.l0, x.l1, x.l2, x.l3, "row_mirror row_mask:0xf bank_mask:0xf");
+}
+// the sum of the word over the wave, in lane 63
+__device__ __forceinline__ void add128_wave(Limbs4& x) {
+  add128_rows(x);
+  DSPARK_ADD128_DPP(x.l0, x.l1, x.l2, x.l3, "row_bcast:15 row_mask:0xa bank_mask:0xf");
+  DSPARK_ADD128_DPP(x.l0, x.l1, x.l2, x.l3, "row_bcast:31 row_mask:0xc bank_mask:0xf");
+}
+#undef DSPARK_ADD128_DPP
+
+// Block-wide exact sum; every thread gets RN64(S).  The small-weight word is
+// summed only where some lane holds a part of it.
 __device__ inline double block_acc_rn64(Acc a, AccScratch& s) {
-  // the wave's exact sum lands in lane 63 (same steps as wave_reduce)
-  acc_merge(a, acc_dpp<0xb1, 0xf>(a));
-  acc_merge(a, acc_dpp<0x4e, 0xf>(a));
-  acc_merge(a, acc_dpp<0x141, 0xf>(a));
-  acc_merge(a, acc_dpp<0x140, 0xf>(a));
-  acc_merge(a, acc_dpp<0x142, 0xa>(a));
-  acc_merge(a, acc_dpp<0x143, 0xc>(a));
-  if (lane_id() == 63) s.w[wave_id()] = a;
+  Limbs4 mw = limbs_of(a.mlo, a.mhi);
+  add128_wave(mw);
+  Limbs4 tw = limbs_of(a.tlo, a.thi);
+  const bool tiny = __ballot((a.tlo | a.thi) != 0ull) != 0ull;  // uniform over the wave
+  if (tiny) add128_wave(tw);
+  if (lane_id() == 63) {
+    Acc w;
+    w.mlo = limbs_lo(mw);
+    w.mhi = limbs_hi(mw);
+    w.tlo = tiny ? limbs_lo(tw) : 0ull;
+    w.thi = tiny ? limbs_hi(tw) : 0ull;
+    s.w[wave_id()] = w;
+  }
   __syncthreads();
   if (threadIdx.x < 64) {  // wave 0 merges the NW wave sums within its first row
     Acc t;
     if (threadIdx.x < NW) t = s.w[threadIdx.x];
     else acc_zero(t);
-    acc_merge(t, acc_dpp<0xb1, 0xf>(t));
-    acc_merge(t, acc_dpp<0x4e, 0xf>(t));
-    acc_merge(t, acc_dpp<0x141, 0xf>(t));
-    acc_merge(t, acc_dpp<0x140, 0xf>(t));
-    if (threadIdx.x == 0) s.s64 = acc_rn64(t);
+    Limbs4 m = limbs_of(t.mlo, t.mhi);
+    add128_rows(m);
+    const bool ttiny = __ballot((t.tlo | t.thi) != 0ull) != 0ull;
+    Limbs4 tt = limbs_of(t.tlo, t.thi);
+    if (ttiny) add128_rows(tt);
+    if (threadIdx.x == 0) {
+      const uint64_t mlo = limbs_lo(m), mhi = limbs_hi(m);
+      double r;
+      if (!ttiny && mhi < (1ull << 26)) {
+        // S = M 2^-70 with M < 2^90: M = H 2^38 + L with H < 2^52 and
+        // L < 2^38, both exact in binary64, so one addition rounds S once
+        const uint64_t H = (mhi << 26) | (mlo >> 38), L = mlo & ((1ull << 38) - 1);
+        r = __builtin_ldexp((double)H, -32) + __builtin_ldexp((double)L, -70);
+      } else {
+        Acc u;
+        u.mlo = mlo;
+        u.mhi = mhi;
+        u.tlo = ttiny ? limbs_lo(tt) : 0ull;
+        u.thi = ttiny ? limbs_hi(tt) : 0ull;
+        r = acc_rn64(u);
+      }
+      s.s64 = r;
+    }
   }
   __syncthreads();
   const double r = s.s64;

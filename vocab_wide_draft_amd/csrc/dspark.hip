@@ -118,9 +118,9 @@ __global__ void __launch_bounds__(BS) rows_kernel(RowsArgs a) {
 
 
 // bf16 rows of up to NI*BS*8 tokens: the row is loaded into registers once.
-// Each kind of row has its own kernel, so that every path gets its own
-// register allocation (the dense and sparse paths would otherwise force
-// spills onto the simple target path).
+// One kernel (rows_bf16_kernel, below) takes every kind of row; the paths of
+// rare rows are out of line, so that their register needs do not weigh on
+// the common paths, and reload the row.
 
 __device__ __forceinline__ void res_target_row(const RowsArgs& a, int r, SmemBase& sh) {
   DSPARK_PHASE_BEGIN

@@ -358,7 +358,9 @@ __device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, 
     w = cr_expf(sh.sx[j] - m);
     acc_add(acc, __float_as_uint(w));
   }
+  DSPARK_PHASE(37);
   const double s64 = block_acc_rn64(acc, sh.acc);
+  DSPARK_PHASE(38);
   if (!(s64 > 0.0)) {
     res.status = DSPARK_ST_ROW_ZERO_MASS;
     return res;
