@@ -225,7 +225,9 @@ __device__ __forceinline__ void res_draft_dense(const RowsArgs& a, int r, int ks
       QOut qo;
       if (fast) {
         qo = fast_dense_q(R, st, f, drow, a.V, a.draws != nullptr, u, a.conf != nullptr, &cf, sh.fd DSPARK_PHASE_ARG);
-      } else {
+        fast = qo.status != kStGeneral;
+      }
+      if (!fast) {
         const QConf g = dense_general(static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V,
                                       st.m_raw, drow, a.draws != nullptr, u, a.conf != nullptr);
         qo = g.q;

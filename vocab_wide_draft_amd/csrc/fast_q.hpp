@@ -30,6 +30,9 @@
 namespace dspark {
 
 constexpr int kNBF = 10240;        // largest compressed table
+// internal row status: several table entries share the threshold remainder
+// key exactly, and the general per-value path decides the row
+constexpr int kStGeneral = -1;
 constexpr int kNBFD = kNBF + 64;   // plus one overflow slot per lane
 
 // Table layout of one row.  bin(x) = B0 - c(|x|) for x with the sign bit
@@ -127,7 +130,6 @@ __device__ __forceinline__ double exp64(double x) {
 // --------------------------------------------------------------- shared
 struct FastDenseShared : SmemBase {
   uint32_t nb[kNBFD];   // counts, then final counts (a tie entry holds its floor)
-  uint32_t tbm[kNBF / 32];  // tie entries (bitmap over entries)
   float wb[kNBF];       // binary32 weight of each occupied entry
   uint32_t kb[kNBF];    // top 32 bits of each entry's remainder key (0: r = 0)
   uint64_t ckey[kVdCand];
@@ -202,9 +204,8 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   const int NB = f.NB;
   fast_hist<true>(R, f, sh.nb);  // the registers now hold table offsets
   // overflow slots read 0 from here on (the final pass looks up
-  // out-of-window elements there); no entry is a tie entry yet
+  // out-of-window elements there)
   for (int b = NB + (int)threadIdx.x; b < kNBFD; b += BS) sh.nb[b] = 0u;
-  for (int w = (int)threadIdx.x; w < kNBF / 32; w += BS) sh.tbm[w] = 0u;
   DSPARK_PHASE(11);
   // A. weights and their exact sum; the confidence is 1 / RN64 of the sum:
   // each weight RN32(exp(RN32(x - m))) is within 2^-24 (1 + |x - m|) of
@@ -221,6 +222,7 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
       acc_add(acc, __float_as_uint(w), n);
     }
   }
+  DSPARK_PHASE(36);
   const double s64 = block_acc_rn64(acc, sh.acc);
   if (want_conf) *conf = (float)(1.0 / s64);
   if (!(s64 > 0.0)) {
@@ -272,7 +274,7 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
       pmask |= (uint64_t)(nd - 1) << shift;
       if ((e & 0xffffffffull) == need) { mode = ALL; break; }
       if ((e >> 32) <= (uint64_t)kVdCand) { mode = CAND; break; }
-      if (shift == 0) { mode = EXACT; break; }
+      if (shift == 0) { mode = EXACT; break; }  // entries with equal keys: the general path decides
       const int nsh = shift > 11 ? shift - 11 : 0;
       nd = 1 << (shift - nsh);
       shift = nsh;
@@ -294,6 +296,10 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
       __syncthreads();
     }
   }
+  if (mode == EXACT) {
+    res.status = kStGeneral;
+    return res;
+  }
   DSPARK_PHASE(14);
   // D. final count of every entry; the threshold bucket's entries wait (CAND)
   if ((int)threadIdx.x == 0) sh.bi[4] = 0;
@@ -311,9 +317,6 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
         const int slot = atomicAdd(&sh.bi[4], 1);
         sh.ckey[slot] = key;
         sh.cbin[slot] = (uint32_t)b;
-      } else if (inb && mode == EXACT) {
-        sh.nb[b] = c;
-        atomicOr(&sh.tbm[b >> 5], 1u << (b & 31));
       } else {
         sh.nb[b] = c + ((above || (inb && mode == ALL)) ? 1u : 0u);
       }
@@ -323,7 +326,7 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   DSPARK_PHASE(15);
   // E. the threshold bucket's entries (CAND): exact weighted threshold
   uint64_t need_t = need;
-  int ntie = mode == EXACT ? 2 : 0;  // EXACT: the tie entries are marked in tbm
+  int ntie = 0;
   int tie_bin = -1;
   if (mode == CAND) {
     const int nc = sh.bi[4];
@@ -359,36 +362,23 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
     if (j < nc) {
       const bool partial = kj == T && ntie > 0;
       sh.nb[bj] = c + (!partial && kj >= T ? 1u : 0u);
-      if (partial) {
-        sh.bi[6] = (int)bj;
-        atomicOr(&sh.tbm[bj >> 5], 1u << (bj & 31));
-      }
+      if (partial) sh.bi[6] = (int)bj;
     }
     __syncthreads();
     if (ntie == 1) tie_bin = sh.bi[6];
     __syncthreads();
   }
+  if (ntie > 1) {  // several entries with the threshold key: the general path decides
+    res.status = kStGeneral;
+    return res;
+  }
   DSPARK_PHASE(16);
   // F. a split tie: the need_t lowest ids among the members of the tie
-  // entries (the registers hold table offsets)
+  // entry (the registers hold table offsets)
   const char* nbb = reinterpret_cast<const char*>(sh.nb);
-  const uint32_t T2 = (uint32_t)(tie_bin < 0 ? 0 : tie_bin * 4) * 0x10001u;
-  auto tie_mask = [&](u32x4 v) -> uint32_t {
-    if (tie_bin >= 0) return eq16_mask8(v, T2);
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-    uint32_t m = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t bl = (wv[c] & 0xffffu) >> 2, bh = wv[c] >> 18;
-      const uint32_t tl = bl < (uint32_t)kNBF ? (sh.tbm[bl >> 5] >> (bl & 31)) & 1u : 0u;
-      const uint32_t th = bh < (uint32_t)kNBF ? (sh.tbm[bh >> 5] >> (bh & 31)) & 1u : 0u;
-      m |= tl << (2 * c);
-      m |= th << (2 * c + 1);
-    }
-    return m;
-  };
+  const uint32_t T4 = (uint32_t)(tie_bin < 0 ? 0 : tie_bin * 4);
   int cut = -1;
-  if (ntie > 0) cut = res_locate(R, [&](int, u32x4 v) -> uint32_t { return tie_mask(v); }, (uint32_t)(need_t - 1), sh);
+  if (tie_bin >= 0) cut = tie_locate(R, T4, (uint32_t)(need_t - 1), sh);
   DSPARK_PHASE(17);
   // G. counts of every element: the entry's count, plus one for the members of
   // a tie entry at or below the cut (only vectors that start at or below it)
@@ -406,8 +396,14 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
       c[2 * k + 1] = *reinterpret_cast<const uint32_t*>(nbb + (wv[k] >> 16));
     }
     const int lim = cut - q * 8;  // lanes l <= lim are at or below the cut
-    if (lim >= 0) {
-      const uint32_t m = tie_mask(v) & (lim >= 7 ? 0xffu : (2u << lim) - 1u);
+    if (lim >= 7) {  // the whole vector: every member of the tie entry
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        c[2 * k] += (uint16_t)wv[k] == (uint16_t)T4 ? 1u : 0u;
+        c[2 * k + 1] += (uint16_t)(wv[k] >> 16) == (uint16_t)T4 ? 1u : 0u;
+      }
+    } else if (lim >= 0) {  // the vector of the cut
+      const uint32_t m = eq16_mask8(v, T4 * 0x10001u) & ((2u << lim) - 1u);
 #pragma unroll
       for (int l = 0; l < 8; ++l) c[l] += (m >> l) & 1u;
     }

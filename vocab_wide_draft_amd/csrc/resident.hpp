@@ -302,6 +302,77 @@ __device__ __forceinline__ int res_locate(Res& R, MF mf, uint32_t u, SmemBase& s
   return result;
 }
 
+// res_locate for the members of one table entry, from registers that hold
+// two 16-bit table offsets per word (T: the entry's offset): the id of the
+// (u+1)-th member in id order, or -1 when there are at most u members.  The
+// count of each (vector, wave) cell comes from wave ballots of the 16-bit
+// compares (scalar population counts); wave 0 finds the cell, and that
+// cell's wave alone finds the lane.
+__device__ __forceinline__ int tie_locate(Res& R, uint32_t T, uint32_t u, SmemBase& sh) {
+  touch(R);
+  const uint16_t T16 = (uint16_t)T;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const u32x4 v = fetch(R, i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      cnt += (uint32_t)__builtin_popcountll(__ballot((uint16_t)w[c] == T16));
+      cnt += (uint32_t)__builtin_popcountll(__ballot((uint16_t)(w[c] >> 16) == T16));
+    }
+    if (lane_id() == 0) sh.tab[i * NW + wave_id()] = cnt;  // cells in id order: vector, then wave
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {  // lane l takes cells 4l .. 4l + 3
+    const int l = lane_id();
+    uint64_t c4[4], s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c4[j] = sh.tab[4 * l + j];
+      s += c4[j];
+    }
+    const uint64_t inc = wave_incl_scan(s);
+    const uint64_t hit = __ballot(inc > (uint64_t)u);
+    if (l == 0) sh.bi[2] = -1;
+    if (hit == 0ull) {
+      if (l == 0) sh.bi[1] = -1;
+    } else if (l == __builtin_ctzll(hit)) {
+      uint64_t run = inc - s;
+      int cell = -1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (cell < 0 && run + c4[j] > (uint64_t)u) cell = 4 * l + j;
+        if (cell < 0) run += c4[j];
+      }
+      sh.bi[1] = cell;
+      sh.bu[1] = run;  // members before the cell
+    }
+  }
+  __syncthreads();
+  const int cell = sh.bi[1];
+  int result = -1;
+  if (cell >= 0) {
+    if (wave_id() == (cell % NW)) {
+      const int i = cell / NW;
+      const u32x4 v = select_vec(R, i);
+      const uint32_t m = eq16_mask8(v, T * 0x10001u);
+      const uint64_t pc = (uint64_t)__builtin_popcount(m);
+      const uint64_t exc = wave_incl_scan(pc) - pc;
+      const uint64_t u2 = (uint64_t)u - sh.bu[1];
+      if (exc <= u2 && u2 < exc + pc) {
+        uint32_t mm = m;
+        for (uint64_t k = exc; k < u2; ++k) mm &= mm - 1u;  // drop the members before
+        sh.bi[2] = (i * BS + (int)threadIdx.x) * 8 + __builtin_ctz(mm);
+      }
+    }
+    __syncthreads();
+    result = sh.bi[2];
+  }
+  __syncthreads();
+  return result;
+}
+
 // Writes the selected elements (mf mask) to (sh.cid, sh.sx) in ascending ID
 // order.  Returns the count (at most cap are stored).
 template <class MF>
