@@ -184,7 +184,10 @@ struct BlockScratch {
   uint64_t w[NW + 1];
 };
 
-// Block reductions: every thread calls, every thread gets the result.
+// Block reductions: every thread calls, every thread gets the result.  The
+// per-wave slots of the scratch are written only before a collective's first
+// barrier and the result slot only after it, so one collective may follow
+// another without a barrier in between (nothing else writes the scratch).
 template <class T, class OP>
 __device__ __forceinline__ T block_reduce(T v, T id, OP op, BlockScratch& s) {
   v = wave_reduce(v, id, op);
@@ -196,9 +199,7 @@ __device__ __forceinline__ T block_reduce(T v, T id, OP op, BlockScratch& s) {
     if (threadIdx.x == 0) reinterpret_cast<T*>(s.w)[NW] = t;
   }
   __syncthreads();
-  T r = reinterpret_cast<T*>(s.w)[NW];
-  __syncthreads();
-  return r;
+  return reinterpret_cast<T*>(s.w)[NW];
 }
 template <class T>
 __device__ __forceinline__ T block_sum(T v, BlockScratch& s) {
@@ -234,7 +235,6 @@ __device__ __forceinline__ T block_excl_scan(T v, BlockScratch& s, T* total) {
   __syncthreads();
   T r = reinterpret_cast<T*>(s.w)[wave_id()] + inc - v;
   if (total) *total = reinterpret_cast<T*>(s.w)[NW];
-  __syncthreads();
   return r;
 }
 
@@ -465,9 +465,7 @@ __device__ inline double block_acc_rn64(Acc a, AccScratch& s) {
     }
   }
   __syncthreads();
-  const double r = s.s64;
-  __syncthreads();
-  return r;
+  return s.s64;  // (written again only after the next call's first barrier)
 }
 
 }  // namespace dspark

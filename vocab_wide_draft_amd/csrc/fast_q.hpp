@@ -381,13 +381,15 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   if (tie_bin >= 0) cut = tie_locate(R, T4, (uint32_t)(need_t - 1), sh);
   DSPARK_PHASE(17);
   // G. counts of every element: the entry's count, plus one for the members of
-  // a tie entry at or below the cut (only vectors that start at or below it)
-  if ((int)threadIdx.x < NI) sh.tab[threadIdx.x] = 0ull;
-  __syncthreads();
+  // a tie entry at or below the cut.  Each 16-lane row of a wave sums its
+  // counts of every vector into a cell; the cells, in id order (vector, wave,
+  // row), give the total and locate the draw.
+  uint32_t* cells = sh.hist;  // NI * NW * 4 cells
   touch(R);
   const int nvec = (V + 7) >> 3;
   const bool vec_ok = (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
-  uint64_t total = 0;
+  const bool row_lead = (lane_id() & 15) == 0;
+  const int cell0 = wave_id() * 4 + (lane_id() >> 4);
   auto counts8 = [&](u32x4 v, int q, uint32_t (&c)[8]) {
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -413,9 +415,6 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
     const int q = i * BS + (int)threadIdx.x;
     uint32_t c[8];
     counts8(fetch(R, i), q, c);
-    uint32_t vs = 0;
-#pragma unroll
-    for (int l = 0; l < 8; ++l) vs += c[l];
     if (q < nvec) {
       if (q * 8 + 8 <= V && vec_ok) {
         u32x4* dst = reinterpret_cast<u32x4*>(drow + (size_t)q * 8);
@@ -431,53 +430,82 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
           if (q * 8 + l < V) drow[(size_t)q * 8 + l] = c[l];
       }
     }
-    total += vs;
-    if (want_s && __ballot(vs != 0u)) {
-      const uint32_t w = wave_sum(vs);
-      if (lane_id() == 0 && w) atomicAdd((unsigned long long*)&sh.tab[i], (unsigned long long)w);
+    uint32_t vs = 0;  // at most 2^31 in a row of 16 lanes (every count <= M)
+#pragma unroll
+    for (int l = 0; l < 8; ++l) vs += c[l];
+    vs += dpp_t<0xb1, 0xf, 0xf>(0u, vs);   // quad_perm 1,0,3,2
+    vs += dpp_t<0x4e, 0xf, 0xf>(0u, vs);   // quad_perm 2,3,0,1
+    vs += dpp_t<0x141, 0xf, 0xf>(0u, vs);  // row_half_mirror
+    vs += dpp_t<0x140, 0xf, 0xf>(0u, vs);  // row_mirror: the row's sum in every lane
+    if (row_lead) cells[i * (NW * 4) + cell0] = vs;
+  }
+  __syncthreads();
+  // H. wave 0: the total, and the cell whose running count passes u (lane l
+  // takes cells 16 l .. 16 l + 15)
+  if (threadIdx.x < 64) {
+    const int l = lane_id();
+    uint64_t s = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += cells[16 * l + j];
+    const uint64_t inc = wave_incl_scan(s);
+    if (l == 63) sh.bu[0] = inc;
+    if (want_s) {
+      const uint64_t hit = __ballot(inc > (uint64_t)u);
+      if (l == 0) sh.bi[1] = -1;
+      if (hit != 0ull && l == __builtin_ctzll(hit)) {
+        uint64_t run = inc - s;
+        int cell = -1;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t cj = cells[16 * l + j];
+          if (cell < 0 && run + cj > (uint64_t)u) cell = 16 * l + j;
+          if (cell < 0) run += cj;
+        }
+        sh.bi[1] = cell;
+        sh.bu[1] = run;  // counts before the cell
+      }
     }
   }
-  total = block_sum<uint64_t>(total, sh.bs);
-  if (total != kMass) {
+  __syncthreads();
+  if (sh.bu[0] != kMass) {
     res.status = DSPARK_ST_ALLOC_INCONSISTENT;
     return res;
   }
   DSPARK_PHASE(18);
-  // H. the sample: the vector whose running total passes u, then a block scan
-  // of that vector's counts (recomputed from the registers)
+  // the sample: the 16 lanes of the draw's cell recompute their counts of its
+  // vector and scan them
   if (want_s) {
-    if ((int)threadIdx.x < 64) {
-      uint64_t before = 0;
-      const int i = wave_first_above(sh.tab, NI, u, &before);
-      if (threadIdx.x == 0) {
-        sh.bi[1] = i;
-        sh.bu[1] = before;
+    const int cell = sh.bi[1];
+    if (threadIdx.x == 0) sh.bi[2] = -1;
+    __syncthreads();
+    if (cell >= 0 && wave_id() == ((cell >> 2) & (NW - 1)) && (lane_id() >> 4) == (cell & 3)) {
+      const int i = cell / (NW * 4);
+      const int q = i * BS + (int)threadIdx.x;
+      uint32_t c[8];
+      counts8(select_vec(R, i), q, c);
+      uint32_t vs = 0;
+#pragma unroll
+      for (int l = 0; l < 8; ++l) vs += c[l];
+      uint32_t inc = vs;  // inclusive scan over the 16 lanes of the row
+      inc += dpp_t<0x111, 0xf, 0xf>(0u, inc);  // row_shr:1
+      inc += dpp_t<0x112, 0xf, 0xf>(0u, inc);  // row_shr:2
+      inc += dpp_t<0x114, 0xf, 0xf>(0u, inc);  // row_shr:4
+      inc += dpp_t<0x118, 0xf, 0xf>(0u, inc);  // row_shr:8
+      const uint32_t u2 = (uint32_t)((uint64_t)u - sh.bu[1]);
+      const uint32_t pre = inc - vs;
+      if (pre <= u2 && u2 < inc) {
+        uint32_t run = pre;
+        int hit = -1;
+#pragma unroll
+        for (int l = 0; l < 8; ++l) {
+          run += c[l];
+          if (run > u2 && hit < 0) hit = l;
+        }
+        sh.bi[2] = q * 8 + hit;
       }
     }
     __syncthreads();
-    const int istar = sh.bi[1];
-    const uint32_t u2 = (uint32_t)((uint64_t)u - sh.bu[1]);
-    uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int q = istar * BS + (int)threadIdx.x;
-    if (istar >= 0) counts8(select_vec(R, istar < 0 ? 0 : istar), q, c);
-    uint32_t vs = 0;
-#pragma unroll
-    for (int l = 0; l < 8; ++l) vs += c[l];
-    uint32_t tot;  // one vector's counts sum to at most M
-    const uint32_t pre = block_excl_scan<uint32_t>(vs, sh.bs, &tot);
-    if (istar >= 0 && vs && pre <= u2 && u2 < pre + vs) {
-      uint32_t run = pre;
-      int hit = -1;
-#pragma unroll
-      for (int l = 0; l < 8; ++l) {
-        run += c[l];
-        if (run > u2 && hit < 0) hit = l;
-      }
-      sh.bi[2] = q * 8 + hit;
-    }
-    __syncthreads();
-    res.token = istar >= 0 ? sh.bi[2] : -1;
-    __syncthreads();
+    res.token = sh.bi[2];
     if (res.token < 0) res.status = DSPARK_ST_ALLOC_INCONSISTENT;
   }
   return res;

@@ -142,6 +142,7 @@ __device__ __forceinline__ RStats res_stats(Res& R, SmemBase& sh) {
                                                __builtin_elementwise_max(sm[2], sm[3]));
   s.smax_t = smax.x > smax.y ? smax.x : smax.y;
   const int um_t = umax.x > umax.y ? umax.x : umax.y;
+  if (threadIdx.x == 0) sh.amin = 0x7fffffff;  // for res_argmax (ordered by the barriers below)
   // one reduction for both: the signed maximum biased into the high half
   const uint32_t SU = block_max_u16x2(((uint32_t)(s.smax_t + 0x8000) << 16) | (uint32_t)um_t, sh.bs);
   const int S = (int)(SU >> 16) - 0x8000;
@@ -219,7 +220,10 @@ __device__ __forceinline__ int res_argmax(Res& R, const RStats& st, SmemBase& sh
       }
     }
   }
-  return block_min<int>(first, sh.bs);
+  // the threads that hold the maximum (usually one) meet in one LDS minimum
+  if (first != 0x7fffffff) atomicMin(&sh.amin, first);
+  __syncthreads();
+  return sh.amin;
 }
 
 // 1 / sum_v exp(x_v - m); x_v - m is exact in binary32 for bf16 operands of
@@ -311,17 +315,23 @@ __device__ __forceinline__ int res_locate(Res& R, MF mf, uint32_t u, SmemBase& s
 __device__ __forceinline__ int tie_locate(Res& R, uint32_t T, uint32_t u, SmemBase& sh) {
   touch(R);
   const uint16_t T16 = (uint16_t)T;
+  uint32_t* cells = sh.hist;  // [NI][NW] member counts, in id order: vector, then wave
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const u32x4 v = fetch(R, i);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t cnt = 0;
+    uint64_t b[8];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      cnt += (uint32_t)__builtin_popcountll(__ballot((uint16_t)w[c] == T16));
-      cnt += (uint32_t)__builtin_popcountll(__ballot((uint16_t)(w[c] >> 16) == T16));
+      b[2 * c] = __ballot((uint16_t)w[c] == T16);
+      b[2 * c + 1] = __ballot((uint16_t)(w[c] >> 16) == T16);
     }
-    if (lane_id() == 0) sh.tab[i * NW + wave_id()] = cnt;  // cells in id order: vector, then wave
+    uint32_t cnt = 0;
+    if ((b[0] | b[1] | b[2] | b[3] | b[4] | b[5] | b[6] | b[7]) != 0ull) {  // most cells hold no member
+#pragma unroll
+      for (int l = 0; l < 8; ++l) cnt += (uint32_t)__builtin_popcountll(b[l]);
+    }
+    if (lane_id() == 0) cells[i * NW + wave_id()] = cnt;
   }
   __syncthreads();
   if (threadIdx.x < 64) {  // lane l takes cells 4l .. 4l + 3
@@ -329,7 +339,7 @@ __device__ __forceinline__ int tie_locate(Res& R, uint32_t T, uint32_t u, SmemBa
     uint64_t c4[4], s = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      c4[j] = sh.tab[4 * l + j];
+      c4[j] = cells[4 * l + j];
       s += c4[j];
     }
     const uint64_t inc = wave_incl_scan(s);

@@ -89,6 +89,7 @@ struct SmemBase {
   uint32_t hist[kHistBins];
   int bi[8];
   uint64_t bu[4];
+  int amin;                          // argmax: lowest index of the maximum
 };
 // The generic / sparse row kernels add the compaction and support arrays.
 struct RowShared : SmemBase {
