@@ -118,6 +118,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     if (n) acc_add(acc, __float_as_uint(vd_weight(Km, b, m)), n);
   }
   const double s64 = block_acc_rn64(acc, sh.acc);
+  const SumR S = sum_r(s64);
   if (!(s64 > 0.0)) {
     res.status = DSPARK_ST_ROW_ZERO_MASS;
     return res;
@@ -133,7 +134,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     if (n) {
       uint32_t c;
       double r;
-      floor_rem(vd_weight(Km, b, m), s64, c, r);
+      floor_rem(vd_weight(Km, b, m), S, c, r);
       csum += (uint64_t)n * c;
       if (r > 0.0) {
         npos += n;
@@ -176,7 +177,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
         if (n) {
           uint32_t c;
           double r;
-          floor_rem(vd_weight(Km, b, m), s64, c, r);
+          floor_rem(vd_weight(Km, b, m), S, c, r);
           const uint64_t key = rem_key(r);
           if (r > 0.0 && (key & pmask) == prefix)
             atomicAdd((unsigned long long*)&rh[(key >> shift) & (uint64_t)(nd - 1)],
@@ -195,7 +196,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     if (n) {
       uint32_t c;
       double r;
-      floor_rem(vd_weight(Km, b, m), s64, c, r);
+      floor_rem(vd_weight(Km, b, m), S, c, r);
       const uint64_t kp = r > 0.0 ? (rem_key(r) & pmask) : 0ull;
       const bool pos = r > 0.0 && mode != NONE;
       const bool above = pos && kp > prefix, inb = pos && kp == prefix;
@@ -246,7 +247,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     ntie_bins = sh.bi[5];
     uint32_t c = 0;
     double r = 0.0;
-    if (j < nc) floor_rem(vd_weight(Km, (int)bj, m), s64, c, r);
+    if (j < nc) floor_rem(vd_weight(Km, (int)bj, m), S, c, r);
     __syncthreads();
     if (j < nc) {
       const bool partial = kj == T && ntie_bins > 0;

@@ -189,9 +189,9 @@ __device__ __forceinline__ double fast_conf_sum(const FMap& f, float m, const ui
 }
 
 // binary64 floor and exact remainder key of entry b
-__device__ __forceinline__ void fast_floor_key(float w, double s64, uint32_t& c, uint64_t& key) {
+__device__ __forceinline__ void fast_floor_key(float w, const SumR& S, uint32_t& c, uint64_t& key) {
   double r;
-  floor_rem(w, s64, c, r);
+  floor_rem(w, S, c, r);
   key = r > 0.0 ? rem_key(r) : 0ull;
 }
 
@@ -223,9 +223,9 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
     }
   }
   DSPARK_PHASE(36);
-  const double s64 = block_acc_rn64(acc, sh.acc);
-  if (want_conf) *conf = (float)(1.0 / s64);
-  if (!(s64 > 0.0)) {
+  const SumR S = sum_r(block_acc_rn64(acc, sh.acc));
+  if (want_conf) *conf = (float)S.y;
+  if (!(S.s > 0.0)) {
     res.status = DSPARK_ST_ROW_ZERO_MASS;
     return res;
   }
@@ -240,7 +240,7 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
     if (n) {
       uint32_t c;
       uint64_t key;
-      fast_floor_key(sh.wb[b], s64, c, key);
+      fast_floor_key(sh.wb[b], S, c, key);
       csum += (uint64_t)n * c;
       sh.kb[b] = (uint32_t)(key >> 32);
       if (key) {
@@ -286,7 +286,7 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
           uint64_t key = (uint64_t)sh.kb[b] << 32;
           if (shift < 32) {
             uint32_t c;
-            fast_floor_key(sh.wb[b], s64, c, key);
+            fast_floor_key(sh.wb[b], S, c, key);
           }
           if ((key & pmask) == prefix)
             atomicAdd((unsigned long long*)&rh[(key >> shift) & (uint64_t)(nd - 1)],
@@ -309,7 +309,7 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
     if (n) {
       uint32_t c;
       uint64_t key;
-      fast_floor_key(sh.wb[b], s64, c, key);
+      fast_floor_key(sh.wb[b], S, c, key);
       const bool pos = key != 0ull && mode != NONE;
       const uint64_t kp = key & pmask;
       const bool above = pos && kp > prefix, inb = pos && kp == prefix;
@@ -357,7 +357,7 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
     ntie = sh.bi[5];
     uint32_t c = 0;
     uint64_t key;
-    if (j < nc) fast_floor_key(sh.wb[bj], s64, c, key);
+    if (j < nc) fast_floor_key(sh.wb[bj], S, c, key);
     __syncthreads();
     if (j < nc) {
       const bool partial = kj == T && ntie > 0;

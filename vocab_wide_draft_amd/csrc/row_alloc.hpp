@@ -110,6 +110,24 @@ __device__ __forceinline__ void floor_rem(float w, double s64, uint32_t& c, doub
   c = (uint32_t)f;
   r = y - f;
 }
+// The same for many weights over one sum: S64 and y = RN64(1 / S64).  The
+// quotient comes from the reciprocal: q0 = RN64(w y) is within one ulp of
+// w / S64, e = w - S64 q0 is exact (one FMA), and RN64(q0 + e y) is the
+// correctly rounded quotient RN64(w / S64) (Markstein's theorem for a
+// correctly rounded reciprocal; no underflow here: w >= 2^-149, S64 < 2^21).
+struct SumR {
+  double s, y;
+};
+__device__ __forceinline__ SumR sum_r(double s64) { return SumR{s64, 1.0 / s64}; }
+__device__ __forceinline__ void floor_rem(float w, const SumR& S, uint32_t& c, double& r) {
+  const double wd = (double)w;
+  const double q0 = wd * S.y;
+  const double e = __builtin_fma(-q0, S.s, wd);
+  const double y = __builtin_fma(e, S.y, q0) * 16777216.0;
+  const double f = __builtin_floor(y);
+  c = (uint32_t)f;
+  r = y - f;
+}
 
 // Finishes a threshold inside one bucket of the remainder keys when the
 // bucket holds at most kCandCap elements: collects them (key, id) in LDS and
@@ -168,6 +186,7 @@ __device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool wa
     res.status = DSPARK_ST_ROW_ZERO_MASS;
     return res;
   }
+  const SumR S = sum_r(s64);
   const int nvec = out.nvec();
   for (int b = threadIdx.x; b < kHistBins; b += BS) sh.hist[b] = 0;
   __syncthreads();
@@ -181,7 +200,7 @@ __device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool wa
       if (l < nv) {
         uint32_t c;
         double r;
-        floor_rem(__uint_as_float(w[l]), s64, c, r);
+        floor_rem(__uint_as_float(w[l]), S, c, r);
         csum += c;
         if (r > 0.0) {
           ++npos;
@@ -204,7 +223,7 @@ __device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool wa
     for (int l = 0; l < 4; ++l) {
       uint32_t c;
       double r;
-      floor_rem(__uint_as_float(w[l]), s64, c, r);
+      floor_rem(__uint_as_float(w[l]), S, c, r);
       ok[l] = l < nv && r > 0.0;
       key[l] = ok[l] ? rem_key(r) : 0ull;
     }
@@ -280,7 +299,7 @@ __device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool wa
     for (int l = 0; l < 4; ++l) {
       uint32_t c;
       double r;
-      floor_rem(__uint_as_float(w[l]), s64, c, r);
+      floor_rem(__uint_as_float(w[l]), S, c, r);
       if (l < nv && r > 0.0) {
         const uint64_t key = rem_key(r);
         const int id = q * 4 + l;
