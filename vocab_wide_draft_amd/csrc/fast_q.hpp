@@ -415,16 +415,30 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
     const int q = i * BS + (int)threadIdx.x;
     uint32_t c[8];
     counts8(fetch(R, i), q, c);
-    if (q < nvec) {
-      if (q * 8 + 8 <= V && vec_ok) {
-        u32x4* dst = reinterpret_cast<u32x4*>(drow + (size_t)q * 8);
-        // plain (write-back) stores: each instruction fills half of every
-        // 32-byte piece it touches, and L2 merges the two halves before the
-        // line goes out; streaming stores left part of them as separate
-        // partial writes (about a quarter more HBM write traffic)
-        dst[0] = u32x4{c[0], c[1], c[2], c[3]};
-        dst[1] = u32x4{c[4], c[5], c[6], c[7]};
-      } else {
+    {
+      // The four lanes of a quad hold four consecutive vectors (128 bytes of
+      // counts).  They trade halves with DPP so that each store instruction
+      // writes whole 64-byte pieces: the first one vectors 4j and 4j + 1, the
+      // second 4j + 2 and 4j + 3; lane l of the quad takes half (l & 1) of
+      // lane (l & 3) >> 1 (then of 2 + ((l & 3) >> 1)).  Whole pieces go out
+      // as streaming stores with no partial writes (storing each lane's own
+      // 32 bytes instead fills half of every piece per instruction).
+      const uint32_t l4 = threadIdx.x & 3u;
+      const bool hi = (l4 & 1u) != 0u;
+      uint32_t f[4], g[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t a0 = dpp_t<0x50, 0xf, 0xf>(0u, c[k]), a1 = dpp_t<0x50, 0xf, 0xf>(0u, c[k + 4]);  // quad_perm 0,0,1,1
+        const uint32_t b0 = dpp_t<0xfa, 0xf, 0xf>(0u, c[k]), b1 = dpp_t<0xfa, 0xf, 0xf>(0u, c[k + 4]);  // quad_perm 2,2,3,3
+        f[k] = hi ? a1 : a0;
+        g[k] = hi ? b1 : b0;
+      }
+      const int q4 = q & ~3;
+      if (q4 * 8 + 32 <= V && vec_ok) {  // the quad's four vectors are whole
+        char* dst = reinterpret_cast<char*>(drow + (size_t)q4 * 8) + l4 * 16;
+        __builtin_nontemporal_store(u32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<u32x4*>(dst));
+        __builtin_nontemporal_store(u32x4{g[0], g[1], g[2], g[3]}, reinterpret_cast<u32x4*>(dst + 64));
+      } else if (q < nvec) {  // the ragged end of the row: element by element
 #pragma unroll
         for (int l = 0; l < 8; ++l)
           if (q * 8 + l < V) drow[(size_t)q * 8 + l] = c[l];
