@@ -11,10 +11,11 @@
 // [m - 105, m] has an entry of its own.  Entries are ordered by value, largest
 // first, so the table is both a histogram for the allocation and an order
 // statistic for the top-k threshold.  For a row maximum of ordinary size the
-// table has at most ~9k entries (instead of the ~34k bf16 values of the
-// window), which leaves room in LDS to keep each entry's weight and remainder
-// key between passes.  Rows whose table would exceed kNBF entries (a maximum
-// at or very near zero) take the general per-value path of dense_vd.hpp.
+// table has about 7k entries (instead of the ~34k bf16 values of the window),
+// which leaves room in LDS to keep each entry's weight and remainder key
+// between passes.  Rows whose table would exceed kNBF entries (a maximum
+// below about 0.04, or not positive) take the general per-value path of
+// dense_vd.hpp.
 //
 // The confidence 1 / sum_v exp(x_v - m) is also taken from the table.  A
 // dense row has the exact sum S of its weights and uses 1 / RN64(S) (error
@@ -29,7 +30,7 @@
 
 namespace dspark {
 
-constexpr int kNBF = 10240;        // largest compressed table
+constexpr int kNBF = 8192;         // largest compressed table
 // internal row status: several table entries share the threshold remainder
 // key exactly, and the general per-value path decides the row
 constexpr int kStGeneral = -1;
@@ -132,6 +133,7 @@ struct FastDenseShared : SmemBase {
   uint32_t nb[kNBFD];   // counts, then final counts (a tie entry holds its floor)
   float wb[kNBF];       // binary32 weight of each occupied entry
   uint32_t kb[kNBF];    // top 32 bits of each entry's remainder key (0: r = 0)
+  uint16_t occ[kNBF];   // the occupied entries, in no particular order
   uint64_t ckey[kVdCand];
   uint32_t cbin[kVdCand];
 };
@@ -202,10 +204,18 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   QOut res{DSPARK_ST_OK, 0};
   const float m = bf16_to_f32(st.m_raw);
   const int NB = f.NB;
+  if (threadIdx.x == 0) sh.bi[3] = 0;  // (ordered by the histogram's barriers)
   fast_hist<true>(R, f, sh.nb);  // the registers now hold table offsets
   // overflow slots read 0 from here on (the final pass looks up
   // out-of-window elements there)
   for (int b = NB + (int)threadIdx.x; b < kNBFD; b += BS) sh.nb[b] = 0u;
+  // The per-entry passes below run over the occupied entries only (about 40 %
+  // of the table, in runs): listed once, every pass then keeps all lanes
+  // busy and every wave equally loaded.  No pass depends on the order.
+  for (int b = (int)threadIdx.x; b < NB; b += BS)
+    if (sh.nb[b]) sh.occ[atomicAdd(&sh.bi[3], 1)] = (uint16_t)b;
+  __syncthreads();
+  const int nocc = sh.bi[3];
   DSPARK_PHASE(11);
   // A. weights and their exact sum; the confidence is 1 / RN64 of the sum:
   // each weight RN32(exp(RN32(x - m))) is within 2^-24 (1 + |x - m|) of
@@ -214,13 +224,12 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   // of sum exp(x - m) relatively
   Acc acc;
   acc_zero(acc);
-  for (int b = (int)threadIdx.x; b < NB; b += BS) {
+  for (int j = (int)threadIdx.x; j < nocc; j += BS) {
+    const int b = sh.occ[j];
     const uint32_t n = sh.nb[b];
-    if (n) {
-      const float w = cr_expf(bf16_to_f32(fmap_raw(b, f)) - m);
-      sh.wb[b] = w;
-      acc_add(acc, __float_as_uint(w), n);
-    }
+    const float w = cr_expf(bf16_to_f32(fmap_raw(b, f)) - m);
+    sh.wb[b] = w;
+    acc_add(acc, __float_as_uint(w), n);
   }
   DSPARK_PHASE(36);
   const SumR S = sum_r(block_acc_rn64(acc, sh.acc));
@@ -235,18 +244,17 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   for (int d = (int)threadIdx.x; d < 2048; d += BS) rh[d] = 0ull;
   __syncthreads();
   uint64_t csum = 0, npos = 0;
-  for (int b = (int)threadIdx.x; b < NB; b += BS) {
+  for (int j = (int)threadIdx.x; j < nocc; j += BS) {
+    const int b = sh.occ[j];
     const uint32_t n = sh.nb[b];
-    if (n) {
-      uint32_t c;
-      uint64_t key;
-      fast_floor_key(sh.wb[b], S, c, key);
-      csum += (uint64_t)n * c;
-      sh.kb[b] = (uint32_t)(key >> 32);
-      if (key) {
-        npos += n;
-        atomicAdd((unsigned long long*)&rh[key >> 53], (unsigned long long)n | (1ull << 32));
-      }
+    uint32_t c;
+    uint64_t key;
+    fast_floor_key(sh.wb[b], S, c, key);
+    csum += (uint64_t)n * c;
+    sh.kb[b] = (uint32_t)(key >> 32);
+    if (key) {
+      npos += n;
+      atomicAdd((unsigned long long*)&rh[key >> 53], (unsigned long long)n | (1ull << 32));
     }
   }
   csum = block_sum<uint64_t>(csum, sh.bs);
@@ -280,9 +288,10 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
       shift = nsh;
       for (int dd = (int)threadIdx.x; dd < nd; dd += BS) rh[dd] = 0ull;
       __syncthreads();
-      for (int b = (int)threadIdx.x; b < NB; b += BS) {
+      for (int j = (int)threadIdx.x; j < nocc; j += BS) {
+        const int b = sh.occ[j];
         const uint32_t n = sh.nb[b];
-        if (n && sh.kb[b]) {
+        if (sh.kb[b]) {
           uint64_t key = (uint64_t)sh.kb[b] << 32;
           if (shift < 32) {
             uint32_t c;
@@ -304,22 +313,20 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   // D. final count of every entry; the threshold bucket's entries wait (CAND)
   if ((int)threadIdx.x == 0) sh.bi[4] = 0;
   __syncthreads();
-  for (int b = (int)threadIdx.x; b < NB; b += BS) {
-    const uint32_t n = sh.nb[b];
-    if (n) {
-      uint32_t c;
-      uint64_t key;
-      fast_floor_key(sh.wb[b], S, c, key);
-      const bool pos = key != 0ull && mode != NONE;
-      const uint64_t kp = key & pmask;
-      const bool above = pos && kp > prefix, inb = pos && kp == prefix;
-      if (inb && mode == CAND) {
-        const int slot = atomicAdd(&sh.bi[4], 1);
-        sh.ckey[slot] = key;
-        sh.cbin[slot] = (uint32_t)b;
-      } else {
-        sh.nb[b] = c + ((above || (inb && mode == ALL)) ? 1u : 0u);
-      }
+  for (int j = (int)threadIdx.x; j < nocc; j += BS) {
+    const int b = sh.occ[j];
+    uint32_t c;
+    uint64_t key;
+    fast_floor_key(sh.wb[b], S, c, key);
+    const bool pos = key != 0ull && mode != NONE;
+    const uint64_t kp = key & pmask;
+    const bool above = pos && kp > prefix, inb = pos && kp == prefix;
+    if (inb && mode == CAND) {
+      const int slot = atomicAdd(&sh.bi[4], 1);
+      sh.ckey[slot] = key;
+      sh.cbin[slot] = (uint32_t)b;
+    } else {
+      sh.nb[b] = c + ((above || (inb && mode == ALL)) ? 1u : 0u);
     }
   }
   __syncthreads();
