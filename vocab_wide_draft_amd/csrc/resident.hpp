@@ -320,16 +320,19 @@ __device__ __forceinline__ int tie_locate(Res& R, uint32_t T, uint32_t u, SmemBa
   for (int i = 0; i < NI; ++i) {
     const u32x4 v = fetch(R, i);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint64_t b[8];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      b[2 * c] = __ballot((uint16_t)w[c] == T16);
-      b[2 * c + 1] = __ballot((uint16_t)(w[c] >> 16) == T16);
-    }
+    // a zero half of w ^ T2 marks a member: a packed minimum tells whether
+    // this lane has one, and most cells hold none
+    const uint32_t T2 = T * 0x10001u;
+    const u16x2 p = __builtin_elementwise_min(
+        __builtin_elementwise_min(__builtin_bit_cast(u16x2, w[0] ^ T2), __builtin_bit_cast(u16x2, w[1] ^ T2)),
+        __builtin_elementwise_min(__builtin_bit_cast(u16x2, w[2] ^ T2), __builtin_bit_cast(u16x2, w[3] ^ T2)));
     uint32_t cnt = 0;
-    if ((b[0] | b[1] | b[2] | b[3] | b[4] | b[5] | b[6] | b[7]) != 0ull) {  // most cells hold no member
+    if (__ballot(p.x == 0 || p.y == 0) != 0ull) {
 #pragma unroll
-      for (int l = 0; l < 8; ++l) cnt += (uint32_t)__builtin_popcountll(b[l]);
+      for (int c = 0; c < 4; ++c) {
+        cnt += (uint32_t)__builtin_popcountll(__ballot((uint16_t)w[c] == T16));
+        cnt += (uint32_t)__builtin_popcountll(__ballot((uint16_t)(w[c] >> 16) == T16));
+      }
     }
     if (lane_id() == 0) cells[i * NW + wave_id()] = cnt;
   }
