@@ -703,25 +703,30 @@ __device__ __forceinline__ int fast_topk(Res& R, const FMap& f, int k, FastSpars
   }
   __syncthreads();
   DSPARK_PHASE(2);
-  // the need_t lowest ids of B join A
+  // the need_t lowest ids of B join A, and the per-word prefix of the joined
+  // A in sh.hist, from one scan of both counts: A and B are disjoint, so
+  // before word j the joined A holds preA + min(preB, need_t) ids
   {
     const int w0 = threadIdx.x * 4;
-    uint32_t bw[4], s = 0;
+    uint32_t aw[4], bw[4];
+    uint64_t s = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      aw[j] = sh.bmA[w0 + j];
       bw[j] = sh.bmB[w0 + j];
-      s += (uint32_t)__builtin_popcount(bw[j]);
+      s += (uint64_t)__builtin_popcount(aw[j]) | ((uint64_t)__builtin_popcount(bw[j]) << 32);
     }
-    uint32_t t;
-    uint32_t pre = block_excl_scan<uint32_t>(s, sh.bs, &t);
+    uint64_t t;
+    const uint64_t pre = block_excl_scan<uint64_t>(s, sh.bs, &t);
+    uint32_t preA = (uint32_t)pre, preB = (uint32_t)(pre >> 32);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t keep = bw[j];
-      const uint32_t pc = (uint32_t)__builtin_popcount(bw[j]);
-      if (pre >= need_t) {
+      const uint32_t pb = (uint32_t)__builtin_popcount(bw[j]);
+      if (preB >= need_t) {
         keep = 0u;
-      } else if (pre + pc > need_t) {  // keep the first need_t - pre members of this word
-        uint32_t rem = need_t - pre, m = bw[j];
+      } else if (preB + pb > need_t) {  // keep the first need_t - preB members of this word
+        uint32_t rem = need_t - preB, m = bw[j];
         keep = 0u;
         while (rem) {
           const uint32_t low = m & (0u - m);
@@ -730,26 +735,10 @@ __device__ __forceinline__ int fast_topk(Res& R, const FMap& f, int k, FastSpars
           --rem;
         }
       }
-      pre += pc;
-      sh.bmA[w0 + j] |= keep;
-    }
-  }
-  __syncthreads();
-  // ascending id order: per-word prefix of A in sh.hist
-  {
-    const int w0 = threadIdx.x * 4;
-    uint32_t pc[4], s = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pc[j] = (uint32_t)__builtin_popcount(sh.bmA[w0 + j]);
-      s += pc[j];
-    }
-    uint32_t t;
-    uint32_t pre = block_excl_scan<uint32_t>(s, sh.bs, &t);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sh.hist[w0 + j] = pre;
-      pre += pc[j];
+      sh.hist[w0 + j] = preA + (preB < need_t ? preB : need_t);
+      sh.bmA[w0 + j] = aw[j] | keep;
+      preA += (uint32_t)__builtin_popcount(aw[j]);
+      preB += pb;
     }
   }
   __syncthreads();
