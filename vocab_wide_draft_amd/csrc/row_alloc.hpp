@@ -377,6 +377,13 @@ __device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, 
     w = cr_expf(sh.sx[j] - m);
     acc_add(acc, __float_as_uint(w));
   }
+  // the remainder histogram, its bucket list and the sample slot start empty
+  // (the barriers of the reductions below order this before their use)
+  for (int b = threadIdx.x; b < 2048; b += BS) sh.hist[b] = 0u;
+  if (threadIdx.x == 0) {
+    sh.bi[4] = 0;
+    sh.bi[5] = -1;
+  }
   DSPARK_PHASE(37);
   const double s64 = block_acc_rn64(acc, sh.acc);
   DSPARK_PHASE(38);
@@ -405,9 +412,6 @@ __device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, 
   // goes to the entries first in thread (= id) order.
   if (remaining > 0) {
     uint64_t prefix = 0, pmask = 0x7ffull << 53, need = (uint64_t)remaining;
-    for (int b = threadIdx.x; b < 2048; b += BS) sh.hist[b] = 0u;
-    if (threadIdx.x == 0) sh.bi[4] = 0;
-    __syncthreads();
     if (pos) atomicAdd(&sh.hist[key >> 53], 1u);
     __syncthreads();
     uint64_t before;
@@ -486,12 +490,9 @@ __device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, 
   }
   if (threadIdx.x == 0) *len_out = (int32_t)(tot >> 32);
   if (want_s) {
-    if (threadIdx.x == 0) sh.bi[5] = -1;
-    __syncthreads();
     if (c > 0 && cpre <= u && u < cpre + c) sh.bi[5] = (int)sh.cid[j];
     __syncthreads();
     res.token = sh.bi[5];
-    __syncthreads();
     if (res.token < 0) res.status = DSPARK_ST_ALLOC_INCONSISTENT;
   }
   return res;
