@@ -222,6 +222,11 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   // exp(x - m) relatively, and the e^(x-m)-weighted mean of |x - m| over at
   // most 2^17 terms, one of them 0, stays below 9, so the sum is within 6e-7
   // of sum exp(x - m) relatively
+  // the first digit histogram and the candidate counter start empty (the
+  // barriers of the reductions below order this first)
+  uint64_t* rh = reinterpret_cast<uint64_t*>(sh.hist);  // 2048 digits
+  for (int d = (int)threadIdx.x; d < 2048; d += BS) rh[d] = 0ull;
+  if ((int)threadIdx.x == 0) sh.bi[4] = 0;
   Acc acc;
   acc_zero(acc);
   for (int j = (int)threadIdx.x; j < nocc; j += BS) {
@@ -240,9 +245,6 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   }
   DSPARK_PHASE(12);
   // B. floors, remaining, keys, first 11-bit digit
-  uint64_t* rh = reinterpret_cast<uint64_t*>(sh.hist);  // 2048 digits
-  for (int d = (int)threadIdx.x; d < 2048; d += BS) rh[d] = 0ull;
-  __syncthreads();
   uint64_t csum = 0, npos = 0;
   for (int j = (int)threadIdx.x; j < nocc; j += BS) {
     const int b = sh.occ[j];
@@ -257,8 +259,11 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
       atomicAdd((unsigned long long*)&rh[key >> 53], (unsigned long long)n | (1ull << 32));
     }
   }
-  csum = block_sum<uint64_t>(csum, sh.bs);
-  npos = block_sum<uint64_t>(npos, sh.bs);
+  {  // one reduction for both: the floor sum is at most M, npos at most 2^20
+    const uint64_t both = block_sum<uint64_t>(csum | (npos << 32), sh.bs);
+    csum = both & 0xffffffffull;
+    npos = both >> 32;
+  }
   const int64_t remaining = (int64_t)kMass - (int64_t)csum;
   if (remaining < 0 || remaining >= (int64_t)kMass || remaining > (int64_t)npos) {
     res.status = DSPARK_ST_ALLOC_INCONSISTENT;
@@ -311,8 +316,6 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   }
   DSPARK_PHASE(14);
   // D. final count of every entry; the threshold bucket's entries wait (CAND)
-  if ((int)threadIdx.x == 0) sh.bi[4] = 0;
-  __syncthreads();
   for (int j = (int)threadIdx.x; j < nocc; j += BS) {
     const int b = sh.occ[j];
     uint32_t c;
@@ -470,6 +473,7 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
     for (int j = 0; j < 16; ++j) s += cells[16 * l + j];
     const uint64_t inc = wave_incl_scan(s);
     if (l == 63) sh.bu[0] = inc;
+    if (l == 0) sh.bi[2] = -1;  // the sample's element (written by one lane below)
     if (want_s) {
       const uint64_t hit = __ballot(inc > (uint64_t)u);
       if (l == 0) sh.bi[1] = -1;
@@ -497,8 +501,6 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
   // vector and scan them
   if (want_s) {
     const int cell = sh.bi[1];
-    if (threadIdx.x == 0) sh.bi[2] = -1;
-    __syncthreads();
     if (cell >= 0 && wave_id() == ((cell >> 2) & (NW - 1)) && (lane_id() >> 4) == (cell & 3)) {
       const int i = cell / (NW * 4);
       const int q = i * BS + (int)threadIdx.x;
@@ -634,7 +636,6 @@ __device__ __forceinline__ int fast_topk(Res& R, const FMap& f, int k, FastSpars
   const uint64_t before = sh.bu[1];
   const uint32_t nT = sh.nb[bT];
   const uint32_t need_t = (uint32_t)(need - before);
-  __syncthreads();
   if (bT == f.B0 && f.tb1 > 0 && nT != need_t) return -1;
   // keys (K16) of the smallest and largest values of the threshold entry
   const bool coll = bT == f.B0 && f.tb1 > 0;
