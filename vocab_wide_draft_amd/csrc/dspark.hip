@@ -201,6 +201,7 @@ __device__ __forceinline__ void res_draft_dense(const RowsArgs& a, int r, int ks
   DSPARK_PHASE_BEGIN
   Res R;
   res_load(R, static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V);
+  fast_clear(sh.fd.nb);  // while the row loads (ordered before the histogram by the head's barriers)
   DSPARK_PHASE_LOADED(9);
   const uint32_t u = a.draws ? a.draws[r] : 0u;
   const bool dense_row = a.do_q && a.dense != nullptr && kstatus == DSPARK_ST_OK;
@@ -249,6 +250,7 @@ __device__ __forceinline__ void res_draft_sparse(const RowsArgs& a, int r, int k
   DSPARK_PHASE_BEGIN
   Res R;
   res_load(R, static_cast<const uint16_t*>(a.draft) + (size_t)r * (size_t)a.d_stride, a.V);
+  fast_clear(sh.fs.nb);  // while the row loads (ordered before the histogram by the head's barriers)
   DSPARK_PHASE_LOADED(7);
   const uint32_t u = a.draws ? a.draws[r] : 0u;
   const RStats st = res_stats(R, sh.base);

@@ -149,13 +149,17 @@ struct FastSparseShared : SmemBase {
   uint32_t ctab[kMaxIter * NW];  // remainder bucket members
 };
 
-// Histogram of the row into nb[0, NB) (overflow slots take the rest).  With
-// KEEP, every register word is replaced by its two table byte offsets, which
-// is all the later passes of the dense path need.
+// Clears the whole table (entries and overflow slots); the callers do this
+// while the row is still loading.
+__device__ __forceinline__ void fast_clear(uint32_t* nb) {
+  for (int b = (int)threadIdx.x; b < kNBFD; b += BS) nb[b] = 0u;
+}
+// Histogram of the row into nb[0, NB) (overflow slots take the rest), on a
+// table cleared by fast_clear before some earlier barrier.  With KEEP, every
+// register word is replaced by its two table byte offsets, which is all the
+// later passes of the dense path need.
 template <bool KEEP>
 __device__ __forceinline__ void fast_hist(Res& R, const FMap& f, uint32_t* nb) {
-  for (int b = (int)threadIdx.x; b < f.NB; b += BS) nb[b] = 0u;
-  __syncthreads();
   touch(R);
   const uint32_t D2 = fmap_dummy2();
   char* base = reinterpret_cast<char*>(nb);

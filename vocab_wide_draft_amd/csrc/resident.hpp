@@ -382,8 +382,7 @@ __device__ __forceinline__ int tie_locate(Res& R, uint32_t T, uint32_t u, SmemBa
     __syncthreads();
     result = sh.bi[2];
   }
-  __syncthreads();
-  return result;
+  return result;  // (bi[1], bi[2], bu[1] are written again only after later barriers)
 }
 
 // Writes the selected elements (mf mask) to (sh.cid, sh.sx) in ascending ID
