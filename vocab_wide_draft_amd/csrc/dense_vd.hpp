@@ -76,8 +76,7 @@ __device__ __forceinline__ int vd_find_digit(const uint64_t* rh, int nd, uint64_
   __syncthreads();
   const int d = sh.bi[0];
   *before = sh.bu[0];
-  __syncthreads();
-  return d;
+  return d;  // (bi[0] and bu[0] are written again only after later barriers)
 }
 
 __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* drow, int V, bool want_s,

@@ -286,12 +286,12 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
       const int d = vd_find_digit(rh, nd, need, sh, &before);
       need -= before;
       const uint64_t e = rh[d];
-      __syncthreads();
       prefix |= (uint64_t)d << shift;
       pmask |= (uint64_t)(nd - 1) << shift;
       if ((e & 0xffffffffull) == need) { mode = ALL; break; }
       if ((e >> 32) <= (uint64_t)kVdCand) { mode = CAND; break; }
       if (shift == 0) { mode = EXACT; break; }  // entries with equal keys: the general path decides
+      __syncthreads();  // every thread has read rh[d] before it is cleared for the next digit
       const int nsh = shift > 11 ? shift - 11 : 0;
       nd = 1 << (shift - nsh);
       shift = nsh;
