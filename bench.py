@@ -92,6 +92,101 @@ def copy_probe(nbytes: int, reps: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
+def _timed(fn, steps, warmup):
+    """Mean HIP-event duration (ms) of fn on the current stream, and the wall
+    time per call (ms) between two synchronisations."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return sum(s.elapsed_time(e) for s, e in evs) / steps, wall * 1e3 / steps
+
+
+def wire_bench(args):
+    """Receiver-side check of the q rows of the R = 1024 mixed workload in
+    the wire form: dense rows of V binary32 values, sparse rows of (id,
+    value) pairs, each with its sampled token.  The q, tokens and wire values
+    are made once by the library; the timed step is the check alone."""
+    import numpy as np
+    import torch
+
+    from vocab_wide_draft_amd import binding as B
+    from vocab_wide_draft_amd import workloads as W
+
+    w = W.make(5)
+    dev = torch.device("cuda:0")
+    d = torch.from_numpy(w.draft.view(np.int16)).view(torch.bfloat16).to(dev)
+    t = torch.from_numpy(w.target.view(np.int16)).view(torch.bfloat16).to(dev)
+    draws = torch.from_numpy(w.draws.view(np.int32)).to(dev)
+    out = B.fused(d, t, B.SAMPLED, topk=w.topk, k_max=1024, draws=draws)
+    q = out["q"]
+    dense_w = B.q_encode(q["dense"])
+    sp_w = B.q_encode(q["sp_cnt"])
+    tok = out["sample"]
+    del d, t
+    torch.cuda.synchronize()
+    n = w.draft.shape[0]
+    topk = np.asarray(w.topk)
+    lens = q["sp_len"].cpu().numpy()
+    n_dense = int((topk == 0).sum())
+    alg = n_dense * w.V * 4 + int(lens[topk != 0].sum()) * 8 + n * 16
+
+    topk_dev = torch.from_numpy(topk.astype(np.int32)).to(dev)
+
+    def check():
+        return B.q_validate(w.V, topk=topk_dev, k_max=1024, dense=dense_w, sp_ids=q["sp_ids"], sp_val=sp_w,
+                            sp_len=q["sp_len"], tokens=tok)
+
+    kernel_ms, ms_per_step = _timed(check, args.steps, args.warmup)
+    st = check()["status"].cpu().numpy()
+    dense_rows = q["dense"][torch.from_numpy(topk == 0).to(dev)].contiguous()
+    enc_out = torch.empty(dense_rows.shape, dtype=torch.float32, device=dev)
+    enc_ms, _ = _timed(lambda: B.q_encode(dense_rows, out=enc_out), args.steps, args.warmup)
+    enc_bytes = dense_rows.numel() * 8
+    achieved = alg / (kernel_ms * 1e-3) / 1e9
+    res = {
+        "metric": "q rows checked per second (wire form, receiver side)",
+        "value": round(n / (ms_per_step * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u32", "data": "synthetic",
+        "config": {"workload": "wire check of the R=1024 mixed workload's q", "rows": n, "dense_rows": n_dense,
+                   "V": w.V, "rows_refused": int((st != 0).sum())},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": alg, "kernel_ms": round(kernel_ms, 4)},
+        "encode": {"rows": n_dense, "kernel_ms": round(enc_ms, 4), "bytes": enc_bytes,
+                   "achieved_GBs": round(enc_bytes / (enc_ms * 1e-3) / 1e9, 1)},
+    }
+    if not args.no_cpu:
+        from oracle import q_wire as Q
+        hw, ht = dense_w.cpu().numpy(), tok.cpu().numpy()
+        t0 = time.perf_counter()
+        done = 0
+        for r in range(n):
+            if topk[r] != 0:
+                continue
+            Q.check_dense(hw[r], w.V, token=int(ht[r]))
+            done += 1
+            if time.perf_counter() - t0 > args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(done / el, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{done} dense rows of the same q, oracle.q_wire.check_dense"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +196,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
+    ap.add_argument("--op", choices=["step", "wire"], default="step",
+                    help="step: the fused propose/q/sample/verify step; wire: the receiver's check of the "
+                         "workload's q in the FP32 wire form (and the sender's encoding, reported beside it)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this step shards by request with no "
@@ -108,6 +206,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe, 10)
+        return
+    if args.op == "wire":
+        wire_bench(args)
         return
 
     import numpy as np

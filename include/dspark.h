@@ -74,6 +74,17 @@ extern "C" {
 #define DSPARK_ST_DRAFT_INVALID 7      /* a valid draft row carries a token outside [0, V) */
 #define DSPARK_ST_BAD_WEIGHT 8         /* weights-only entry: weight < 0 or > 1 */
 #define DSPARK_ST_BAD_TOPK 9           /* topk[r] outside [0, min(k_max, V)] */
+/* receiver-side refusals of a q row in the wire form [Q, "Versioned v2
+ * message design"]; a row breaking several rules gets the smallest code */
+#define DSPARK_ST_Q_BAD_LEN 10         /* sparse length outside [0, topk[r]] */
+#define DSPARK_ST_Q_BAD_ID 11          /* sparse id outside [0, V) */
+#define DSPARK_ST_Q_UNSORTED 12        /* sparse ids not strictly ascending (duplicates included) */
+#define DSPARK_ST_Q_NONFINITE 13       /* a NaN or infinite value */
+#define DSPARK_ST_Q_NEGATIVE 14        /* a value with the sign bit set (-0.0 included) */
+#define DSPARK_ST_Q_NOT_DYADIC 15      /* value * 2^24 is not an integer */
+#define DSPARK_ST_Q_PADDING 16         /* dense padding past V that is not +0.0 */
+#define DSPARK_ST_Q_MASS 17            /* a value above 1, or counts not summing to M */
+#define DSPARK_ST_Q_TOKEN 18           /* proposed token outside [0, V) or with q = 0 */
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 typedef enum { DSPARK_GREEDY = 0, DSPARK_SAMPLED = 1 } dspark_mode;
@@ -168,6 +179,48 @@ int dspark_fused(const dspark_rows* draft, const dspark_rows* target, int32_t mo
                  int32_t* sample, int32_t* row_status, int32_t* target_argmax,
                  int32_t* target_status, int32_t* accept_len, int32_t* bonus, int32_t* req_status,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* q rows in the wire form [Q, "Distribution contract and precision"]: each
+ * value is c_v / 2^24 as a little-endian binary32, exact for c_v <= 2^24.
+ *   topk:   as in dspark_q (device int32[n_rows]; 0 = dense row, else a
+ *           sparse row of at most topk[r] entries; NULL = every row dense).
+ *   dense:  float[n_rows][dense_stride]; a dense row sends `padded` values
+ *           (vocab <= padded <= dense_stride): the vocabulary, then padding
+ *           that must be +0.0.  16-byte aligned, dense_stride a multiple of
+ *           4.  May be NULL if no row is dense.
+ *   sp_ids: int32[n_rows][k_max], sp_val: float[n_rows][k_max] and
+ *   sp_len: int32[n_rows], the first sp_len[r] entries of row r.  May be
+ *           NULL if no row is sparse.                                     */
+typedef struct {
+  const int32_t* topk;
+  int32_t k_max;
+  int32_t reserved;
+  const float* dense;
+  int64_t padded;
+  int64_t dense_stride;
+  const int32_t* sp_ids;
+  const float* sp_val;
+  const int32_t* sp_len;
+} dspark_q_wire;
+
+/* Wire encoding of counts [Q]: values[i] = counts[i] / 2^24 as binary32
+ * (the conversion rounds to nearest even, so counts above 2^24, which no
+ * valid q holds, are not exact).  counts: uint32[n], values: float[n]
+ * (device; may be the same memory).  Covers dense rows (n = rows * V) and
+ * sparse count arrays alike; sparse ids travel unchanged. */
+int dspark_q_encode(const uint32_t* counts, int64_t n, float* values, void* stream);
+
+/* Receiver-side check of n_rows wire q rows [Q, "Versioned v2 message
+ * design"; totals with 64-bit integers, no renormalisation, "Distribution
+ * contract and precision"].  row_status[r] (int32[n_rows], required) gets
+ * OK or the smallest DSPARK_ST_Q_* code (or BAD_TOPK for a bad topk[r] or a
+ * dense row without dense storage) among the rules the row breaks.
+ * tokens: int32[n_rows] proposed tokens, or NULL to skip that rule.
+ * Recovered counts (optional): dense_counts uint32[n_rows][vocab] for dense
+ * rows, sp_counts uint32[n_rows][k_max] for sparse rows (count of entry i at
+ * i, zeros past sp_len[r]); a refused row's counts are all zero. */
+int dspark_q_validate(const dspark_q_wire* q, int64_t n_rows, int64_t vocab, const int32_t* tokens,
+                      uint32_t* dense_counts, uint32_t* sp_counts, int32_t* row_status, void* stream);
 
 /* Test entry: the dense allocation steps of dspark_q_alloc applied to
  * caller-given float32 weights (normalised weights in [0, 1]), so that the

@@ -81,3 +81,37 @@ def test_empty_batches_need_no_arrays():
     assert lib.dspark_fused(ctypes.byref(r), ctypes.byref(t), 1, None, *([None] * 10), None, 0, None) == -1
     bad = B.Q(None, 2000, 0, None, None, None, None)
     assert lib.dspark_q_alloc(ctypes.byref(r), ctypes.byref(bad), None, None, 0, None) == -1
+
+
+def test_wire_entry_argument_errors():
+    """Host-side argument checks of the wire entry points return before any
+    device work, so they run without a GPU."""
+    lib = B.load_library()
+    assert lib.dspark_q_encode(None, 0, None, None) == 0
+    assert lib.dspark_q_encode(None, -1, None, None) == -1
+    assert lib.dspark_q_encode(None, 8, None, None) == -1
+    q = B.QWire(None, 0, 0, None, 0, 0, None, None, None)
+    assert lib.dspark_q_validate(None, 1, 10, None, None, None, None, None) == -1
+    assert lib.dspark_q_validate(ctypes.byref(q), 0, 10, None, None, None, None, None) == 0
+    assert lib.dspark_q_validate(ctypes.byref(q), 1, 0, None, None, None, None, None) == -1
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.dspark_q_validate(ctypes.byref(q), 1, 10, None, None, None, fake, None) == -1   # no dense storage
+    q = B.QWire(None, 0, 0, fake, 8, 16, None, None, None)                                      # padded < vocab
+    assert lib.dspark_q_validate(ctypes.byref(q), 1, 10, None, None, None, fake, None) == -1
+    q = B.QWire(None, 0, 0, ctypes.c_void_p(0x1004), 12, 16, None, None, None)                 # misaligned rows
+    assert lib.dspark_q_validate(ctypes.byref(q), 1, 10, None, None, None, fake, None) == -2
+    q = B.QWire(None, 0, 0, fake, 12, 14, None, None, None)                                     # stride not % 4
+    assert lib.dspark_q_validate(ctypes.byref(q), 1, 10, None, None, None, fake, None) == -2
+    q = B.QWire(fake, 2048, 0, None, 0, 0, None, None, None)                                    # k_max too big
+    assert lib.dspark_q_validate(ctypes.byref(q), 1, 10, None, None, None, fake, None) == -1
+    q = B.QWire(fake, 64, 0, None, 0, 0, None, None, None)                                      # sparse arrays missing
+    assert lib.dspark_q_validate(ctypes.byref(q), 1, 10, None, None, None, fake, None) == -1
+
+
+def test_wire_status_codes_agree_with_the_oracle():
+    from oracle import q_wire as Q
+    src = open(os.path.join(ROOT, "include", "dspark.h")).read()
+    for name in ("BAD_LEN", "BAD_ID", "UNSORTED", "NONFINITE", "NEGATIVE", "NOT_DYADIC", "PADDING", "MASS", "TOKEN"):
+        code = int(re.search(r"#define DSPARK_ST_Q_%s (\d+)" % name, src).group(1))
+        assert getattr(Q, "ST_Q_" + name) == code
+        assert B.STATUS_NAMES[code] == "Q_" + name

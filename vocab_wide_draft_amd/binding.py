@@ -20,7 +20,8 @@ MASS = 1 << 24
 K_MAX = 1024
 STATUS_NAMES = {0: "OK", 1: "ROW_NAN", 2: "ROW_POSINF", 3: "ROW_ZERO_MASS", 4: "DRAW_RANGE",
                 5: "ALLOC_INCONSISTENT", 6: "TARGET_INVALID", 7: "DRAFT_INVALID", 8: "BAD_WEIGHT",
-                9: "BAD_TOPK"}
+                9: "BAD_TOPK", 10: "Q_BAD_LEN", 11: "Q_BAD_ID", 12: "Q_UNSORTED", 13: "Q_NONFINITE",
+                14: "Q_NEGATIVE", 15: "Q_NOT_DYADIC", 16: "Q_PADDING", 17: "Q_MASS", 18: "Q_TOKEN"}
 
 
 class DsparkError(RuntimeError):
@@ -38,8 +39,14 @@ class Q(ctypes.Structure):
                 ("sp_len", ctypes.c_void_p)]
 
 
+class QWire(ctypes.Structure):
+    _fields_ = [("topk", ctypes.c_void_p), ("k_max", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("dense", ctypes.c_void_p), ("padded", ctypes.c_int64), ("dense_stride", ctypes.c_int64),
+                ("sp_ids", ctypes.c_void_p), ("sp_val", ctypes.c_void_p), ("sp_len", ctypes.c_void_p)]
+
+
 EXPORTS = ["dspark_propose", "dspark_q_alloc", "dspark_sample", "dspark_verify_greedy", "dspark_fused",
-           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_workspace_bytes", "dspark_q_semantic_id",
+           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_workspace_bytes", "dspark_q_semantic_id",
            "dspark_status_name", "dspark_last_error", "dspark_abi_version"]
 
 
@@ -66,6 +73,8 @@ def load_library():
         "dspark_fused": (ctypes.c_int, [RP, RP, I32, QP, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "dspark_q_alloc_weights": (ctypes.c_int, [P, I64, I64, I64, P, P, P, SZ, P]),
         "dspark_cr_expf": (ctypes.c_int, [P, P, I64, P]),
+        "dspark_q_encode": (ctypes.c_int, [P, I64, P, P]),
+        "dspark_q_validate": (ctypes.c_int, [ctypes.POINTER(QWire), I64, I64, P, P, P, P, P]),
         "dspark_workspace_bytes": (SZ, [I32, I64, I64, I32]),
         "dspark_q_semantic_id": (ctypes.c_char_p, []),
         "dspark_status_name": (ctypes.c_char_p, [I32]),
@@ -247,3 +256,37 @@ def cr_expf(d: torch.Tensor):
     w = torch.empty_like(d)
     _check(lib.dspark_cr_expf(_p(d), _p(w), d.numel(), _stream()))
     return w
+
+
+def q_encode(counts: torch.Tensor, out: torch.Tensor | None = None):
+    """Wire values counts / 2**24 (float32, same shape).  `out` may be the
+    counts tensor itself viewed as float32 (in-place encoding)."""
+    lib = load_library()
+    c = counts.contiguous()
+    if out is None:
+        out = torch.empty(c.shape, dtype=torch.float32, device=c.device)
+    _check(lib.dspark_q_encode(_p(c), c.numel(), _p(out), _stream()))
+    return out
+
+
+def q_validate(vocab: int, topk=None, k_max: int = 0, dense=None, sp_ids=None, sp_val=None, sp_len=None,
+               tokens=None, padded=None, want_counts: bool = False):
+    """Receiver check of wire q rows.  dense: float32 [n_rows, stride] with
+    `padded` (default vocab) values sent per row; sp_*: [n_rows, k_max] and
+    [n_rows].  Returns {"status", "dense_counts", "sp_counts"}."""
+    lib = load_library()
+    ref = dense if dense is not None else sp_len
+    n_rows, dev = ref.shape[0], ref.device
+    tk = _topk(topk, dev)
+    padded = vocab if padded is None else int(padded)
+    if dense is not None and (dense.dim() != 2 or dense.stride(1) != 1 or dense.dtype != torch.float32):
+        raise ValueError("dense must be a 2-D float32 tensor with unit column stride")
+    q = QWire(_p(tk), int(k_max), 0, _p(dense), padded, 0 if dense is None else dense.stride(0),
+              _p(sp_ids), _p(sp_val), _p(sp_len))
+    st = _i32(n_rows, dev)
+    dc = torch.empty((n_rows, vocab), dtype=torch.int32, device=dev) if want_counts and dense is not None else None
+    sc = (torch.empty((n_rows, k_max), dtype=torch.int32, device=dev)
+          if want_counts and tk is not None and k_max > 0 else None)
+    tok = None if tokens is None else tokens.to(torch.int32).contiguous()
+    _check(lib.dspark_q_validate(ctypes.byref(q), n_rows, vocab, _p(tok), _p(dc), _p(sc), _p(st), _stream()))
+    return {"status": st, "dense_counts": dc, "sp_counts": sc}

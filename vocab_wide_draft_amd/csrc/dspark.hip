@@ -6,12 +6,14 @@
 // second, tiny kernel does the per-request greedy verification.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 
 #include "dspark.h"
 #include "dense_vd.hpp"
 #include "fast_q.hpp"
+#include "q_wire.hpp"
 
 namespace dspark {
 
@@ -611,6 +613,15 @@ const char* dspark_status_name(int32_t code) {
     case DSPARK_ST_DRAFT_INVALID: return "DRAFT_INVALID";
     case DSPARK_ST_BAD_WEIGHT: return "BAD_WEIGHT";
     case DSPARK_ST_BAD_TOPK: return "BAD_TOPK";
+    case DSPARK_ST_Q_BAD_LEN: return "Q_BAD_LEN";
+    case DSPARK_ST_Q_BAD_ID: return "Q_BAD_ID";
+    case DSPARK_ST_Q_UNSORTED: return "Q_UNSORTED";
+    case DSPARK_ST_Q_NONFINITE: return "Q_NONFINITE";
+    case DSPARK_ST_Q_NEGATIVE: return "Q_NEGATIVE";
+    case DSPARK_ST_Q_NOT_DYADIC: return "Q_NOT_DYADIC";
+    case DSPARK_ST_Q_PADDING: return "Q_PADDING";
+    case DSPARK_ST_Q_MASS: return "Q_MASS";
+    case DSPARK_ST_Q_TOKEN: return "Q_TOKEN";
     default: return "UNKNOWN";
   }
 }
@@ -755,6 +766,61 @@ int dspark_cr_expf(const float* d, float* w, int64_t n, void* stream) {
   const int tpb = 256;
   hipLaunchKernelGGL(cr_exp_kernel, dim3((unsigned)((n + tpb - 1) / tpb)), dim3(tpb), 0,
                      static_cast<hipStream_t>(stream), d, w, n);
+  return check_launch();
+}
+
+int dspark_q_encode(const uint32_t* counts, int64_t n, float* values, void* stream) {
+  if (n < 0) return fail(DSPARK_EINVAL, "n < 0");
+  if (n == 0) return DSPARK_SUCCESS;
+  if (!counts || !values) return fail(DSPARK_EINVAL, "NULL argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int tpb = 256;
+  if (aligned16(counts) && aligned16(values) && (n & 3) == 0) {
+    const int64_t n4 = n >> 2;
+    const int64_t blocks = std::min<int64_t>((n4 + tpb - 1) / tpb, 8192);
+    hipLaunchKernelGGL(wire_encode_vec_kernel, dim3((unsigned)blocks), dim3(tpb), 0, s,
+                       reinterpret_cast<const wire_u32x4*>(counts), reinterpret_cast<wire_f32x4*>(values), n4);
+  } else {
+    const int64_t blocks = std::min<int64_t>((n + tpb - 1) / tpb, 8192);
+    hipLaunchKernelGGL(wire_encode_kernel, dim3((unsigned)blocks), dim3(tpb), 0, s, counts, values, n);
+  }
+  return check_launch();
+}
+
+int dspark_q_validate(const dspark_q_wire* q, int64_t n_rows, int64_t vocab, const int32_t* tokens,
+                      uint32_t* dense_counts, uint32_t* sp_counts, int32_t* row_status, void* stream) {
+  if (!q) return fail(DSPARK_EINVAL, "q NULL");
+  if (n_rows < 0 || n_rows > (1 << 24) || vocab < 1 || vocab > DSPARK_V_MAX)
+    return fail(DSPARK_EINVAL, "bad n_rows or vocab");
+  if (q->k_max < 0 || q->k_max > DSPARK_K_MAX) return fail(DSPARK_EINVAL, "k_max must be in [0, DSPARK_K_MAX]");
+  if (n_rows == 0) return DSPARK_SUCCESS;
+  if (!row_status) return fail(DSPARK_EINVAL, "NULL row_status");
+  if (!q->topk && !q->dense) return fail(DSPARK_EINVAL, "all rows dense but q->dense is NULL");
+  if (q->dense) {
+    if (q->padded < vocab || q->padded > (int64_t)DSPARK_V_MAX + 64 || q->dense_stride < q->padded)
+      return fail(DSPARK_EINVAL, "need vocab <= padded <= dense_stride");
+    if (!aligned16(q->dense) || (q->dense_stride & 3) != 0)
+      return fail(DSPARK_EALIGN, "dense wire rows must start 16-byte aligned (dense_stride a multiple of 4)");
+  }
+  if (q->topk && q->k_max > 0 && (!q->sp_ids || !q->sp_val || !q->sp_len))
+    return fail(DSPARK_EINVAL, "sparse rows need sp_ids, sp_val and sp_len");
+  WireArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.topk = q->topk;
+  a.k_max = q->k_max;
+  a.V = (int)vocab;
+  a.padded = q->dense ? (int)q->padded : (int)vocab;
+  a.d_stride = q->dense_stride;
+  a.dense = q->dense;
+  a.sp_ids = q->sp_ids;
+  a.sp_val = q->sp_val;
+  a.sp_len = q->sp_len;
+  a.tokens = tokens;
+  a.dense_cnt = dense_counts;
+  a.sp_cnt = q->topk ? sp_counts : nullptr;
+  a.row_status = row_status;
+  hipLaunchKernelGGL(wire_check_kernel, dim3((unsigned)n_rows), dim3(kWireBS), 0, static_cast<hipStream_t>(stream),
+                     a);
   return check_launch();
 }
 
