@@ -27,7 +27,7 @@ namespace dspark {
 typedef unsigned int wire_u32x4 __attribute__((ext_vector_type(4)));
 typedef float wire_f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWireBS = 256;  // threads per check workgroup (4 waves)
+constexpr int kWireBS = 1024;  // threads per check workgroup (16 waves)
 constexpr int kWireNW = kWireBS / 64;
 
 // One bit per refusal status: bit (code - DSPARK_ST_BAD_TOPK), so the lowest
@@ -118,14 +118,27 @@ __device__ __forceinline__ void wire_reduce(uint64_t& sum, uint32_t& bits, WireS
 // whole 16-byte groups up to round_up(padded, 4), which the row stride
 // (a multiple of 4 elements, at least `padded`) covers; elements at or past
 // `padded` are not looked at.
+//
+// The streaming pass spends a few operations per value: the largest bit
+// pattern (every negative, non-finite or above-one value has a pattern above
+// that of 1.0), the OR of the fractional parts of v * 2^24 (nonzero exactly
+// when some value is off the 2^-24 grid, once all patterns are at most
+// 1.0), the truncated counts' sum, and the OR of the padding patterns.  A
+// row with a pattern above 1.0 is refused whatever else holds; it is read a
+// second time with the full per-value classification, so that it gets the
+// smallest code it breaks.  The token rule needs only the token's own value:
+// a nonzero pattern there is a positive count once the rest of the row
+// passes.
 __device__ void wire_check_dense(const WireArgs& a, int r, int token, WireScratch& sh) {
   const float* row = a.dense + (int64_t)r * a.d_stride;
   const wire_u32x4* row4 = reinterpret_cast<const wire_u32x4*>(row);
   uint32_t* out = a.dense_cnt ? a.dense_cnt + (int64_t)r * a.V : nullptr;
   const int V = a.V, P = a.padded;
   const int n4 = (P + 3) >> 2;
+  uint32_t tok_bits = 1u;
+  if (threadIdx.x == 0 && token >= 0) tok_bits = __float_as_uint(row[token]);
   uint64_t sum = 0;
-  uint32_t bits = 0, hit = 0;
+  uint32_t hi = 0, frac = 0, pad = 0;
   constexpr int U = 4;
   for (int g0 = threadIdx.x; g0 < n4; g0 += U * kWireBS) {
     wire_u32x4 x[U];
@@ -134,31 +147,69 @@ __device__ void wire_check_dense(const WireArgs& a, int r, int token, WireScratc
       const int g = g0 + k * kWireBS;
       x[k] = g < n4 ? __builtin_nontemporal_load(&row4[g]) : wire_u32x4{0u, 0u, 0u, 0u};
     }
+    uint32_t part = 0;  // at most 16 counts of at most 2^24 while every pattern is <= 1.0
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int g = g0 + k * kWireBS;
       const uint32_t e[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+      if (4 * g + 3 < V) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * g + j;
-        if (i < V) {
-          uint32_t c;
-          bits |= wire_entry(e[j], &c);
-          sum += c;
-          hit |= (uint32_t)(i == token && c != 0);
-          if (out) out[i] = c;
-        } else if (i < P && e[j] != 0u) {
-          bits |= wire_bit(DSPARK_ST_Q_PADDING);
+        for (int j = 0; j < 4; ++j) {
+          hi = e[j] > hi ? e[j] : hi;
+          const float t = __uint_as_float(e[j]) * 16777216.0f;
+          frac |= __float_as_uint(__builtin_amdgcn_fractf(t));
+          const uint32_t c = __float2uint_rz(t);
+          part += c;
+          if (out) out[4 * g + j] = c;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * g + j;
+          if (i < V) {
+            hi = e[j] > hi ? e[j] : hi;
+            const float t = __uint_as_float(e[j]) * 16777216.0f;
+            frac |= __float_as_uint(__builtin_amdgcn_fractf(t));
+            const uint32_t c = __float2uint_rz(t);
+            part += c;
+            if (out) out[i] = c;
+          } else if (i < P) {
+            pad |= e[j];
+          }
         }
       }
     }
+    sum += part;
   }
-  bits |= hit ? (1u << 31) : 0u;
+  uint32_t bits = (hi > 0x3f800000u ? 1u : 0u) | (frac ? 2u : 0u) | (pad ? 4u : 0u);
   wire_reduce(sum, bits, sh);
+  if (bits & 1u) {
+    // refused row: classify every value to find the smallest code
+    uint32_t f = 0;
+    for (int g = threadIdx.x; g < n4; g += kWireBS) {
+      const wire_u32x4 x = row4[g];
+      const uint32_t e[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+        uint32_t c;
+        if (i < V)
+          f |= wire_entry(e[j], &c);
+        else if (i < P && e[j] != 0u)
+          f |= wire_bit(DSPARK_ST_Q_PADDING);
+      }
+    }
+    __syncthreads();  // every thread has read the first reduction's result
+    uint64_t unused = 0;
+    wire_reduce(unused, f, sh);
+    bits = f;
+  } else {
+    bits = ((bits & 2u) ? wire_bit(DSPARK_ST_Q_NOT_DYADIC) : 0u) | ((bits & 4u) ? wire_bit(DSPARK_ST_Q_PADDING) : 0u);
+  }
   if (threadIdx.x == 0) {
-    uint32_t f = bits & 0x7fffffffu;
+    uint32_t f = bits;
     if (f == 0 && sum != (uint64_t)kMass) f |= wire_bit(DSPARK_ST_Q_MASS);
-    if (token != -2 && !(bits >> 31)) f |= wire_bit(DSPARK_ST_Q_TOKEN);
+    if (token != -2 && (token < 0 || tok_bits == 0u)) f |= wire_bit(DSPARK_ST_Q_TOKEN);
     const int st = f ? DSPARK_ST_BAD_TOPK + __builtin_ctz(f) : DSPARK_ST_OK;
     sh.status = st;
     a.row_status[r] = st;
