@@ -777,7 +777,7 @@ int dspark_q_encode(const uint32_t* counts, int64_t n, float* values, void* stre
   const int tpb = 256;
   if (aligned16(counts) && aligned16(values) && (n & 3) == 0) {
     const int64_t n4 = n >> 2;
-    const int64_t blocks = std::min<int64_t>((n4 + tpb - 1) / tpb, 8192);
+    const int64_t blocks = std::min<int64_t>((n4 + 4 * tpb - 1) / (4 * tpb), 8192);
     hipLaunchKernelGGL(wire_encode_vec_kernel, dim3((unsigned)blocks), dim3(tpb), 0, s,
                        reinterpret_cast<const wire_u32x4*>(counts), reinterpret_cast<wire_f32x4*>(values), n4);
   } else {

@@ -73,15 +73,27 @@ struct WireArgs {
 // conversion of c to binary32 (round to nearest even, exact up to 2^24) and
 // an exact scaling by 2^-24.  The arrays may be the same memory.
 __global__ void __launch_bounds__(256) wire_encode_vec_kernel(const wire_u32x4* c, wire_f32x4* v, int64_t n4) {
-  const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += step) {
-    const wire_u32x4 x = __builtin_nontemporal_load(&c[i]);
-    wire_f32x4 y;
-    y.x = (float)x.x * 0x1p-24f;
-    y.y = (float)x.y * 0x1p-24f;
-    y.z = (float)x.z * 0x1p-24f;
-    y.w = (float)x.w * 0x1p-24f;
-    v[i] = y;
+  // four groups per thread per step, all loaded before any is stored (the
+  // arrays may alias, so the compiler cannot hoist later loads over stores)
+  constexpr int U = 4;
+  const int64_t T = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < n4; i0 += U * T) {
+    wire_u32x4 x[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int64_t i = i0 + k * T;
+      x[k] = i < n4 ? __builtin_nontemporal_load(&c[i]) : wire_u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int64_t i = i0 + k * T;
+      wire_f32x4 y;
+      y.x = (float)x[k].x * 0x1p-24f;
+      y.y = (float)x[k].y * 0x1p-24f;
+      y.z = (float)x[k].z * 0x1p-24f;
+      y.w = (float)x[k].w * 0x1p-24f;
+      if (i < n4) __builtin_nontemporal_store(y, &v[i]);
+    }
   }
 }
 __global__ void __launch_bounds__(256) wire_encode_kernel(const uint32_t* c, float* v, int64_t n) {
