@@ -28,6 +28,7 @@ METRIC = "rows/sec at V=129280 (propose+dyadic24+verify); achieved HBM GB/s vs p
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "vocab_wide_draft_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+WIRE_WORKLOAD = "wire_check_r1024_mixed_q"
 
 
 def _code_tokens(src: str) -> str:
@@ -164,7 +165,7 @@ def wire_bench(args):
         "config": {"workload": "wire check of the R=1024 mixed workload's q", "rows": n, "dense_rows": n_dense,
                    "V": w.V, "rows_refused": int((st != 0).sum())},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(WIRE_WORKLOAD),
                      "algorithmic_bytes": alg, "kernel_ms": round(kernel_ms, 4)},
         "encode": {"rows": n_dense, "kernel_ms": round(enc_ms, 4), "bytes": enc_bytes,
                    "achieved_GBs": round(enc_bytes / (enc_ms * 1e-3) / 1e9, 1)},
