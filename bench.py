@@ -153,6 +153,10 @@ def wire_bench(args):
     enc_out = torch.empty(dense_rows.shape, dtype=torch.float32, device=dev)
     enc_ms, _ = _timed(lambda: B.q_encode(dense_rows, out=enc_out), args.steps, args.warmup)
     enc_bytes = dense_rows.numel() * 8
+    del dense_rows, enc_out
+    d = torch.from_numpy(w.draft.view(np.int16)).view(torch.bfloat16).to(dev)
+    mrg_ms, _ = _timed(lambda: B.margin(d), args.steps, args.warmup)
+    mrg_bytes = n * w.V * 2 + n * 4
     achieved = alg / (kernel_ms * 1e-3) / 1e9
     res = {
         "metric": "q rows checked per second (wire form, receiver side)",
@@ -169,6 +173,8 @@ def wire_bench(args):
                      "algorithmic_bytes": alg, "kernel_ms": round(kernel_ms, 4)},
         "encode": {"rows": n_dense, "kernel_ms": round(enc_ms, 4), "bytes": enc_bytes,
                    "achieved_GBs": round(enc_bytes / (enc_ms * 1e-3) / 1e9, 1)},
+        "margin": {"rows": n, "kernel_ms": round(mrg_ms, 4), "bytes": mrg_bytes,
+                   "achieved_GBs": round(mrg_bytes / (mrg_ms * 1e-3) / 1e9, 1)},
     }
     if not args.no_cpu:
         from oracle import q_wire as Q

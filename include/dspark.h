@@ -222,6 +222,15 @@ int dspark_q_encode(const uint32_t* counts, int64_t n, float* values, void* stre
 int dspark_q_validate(const dspark_q_wire* q, int64_t n_rows, int64_t vocab, const int32_t* tokens,
                       uint32_t* dense_counts, uint32_t* sp_counts, int32_t* row_status, void* stream);
 
+/* Margin of every row [C 6.3, the HAS_MARGIN reply field: top1 - top2 of
+ * the logits, finite and >= 0; failed entries carry 0].  margin: float
+ * [n_rows].  top2 is the second value in sorted order (a repeated maximum
+ * gives 0); the binary32 difference m1 - m2, with a zero as +0.0; the
+ * largest finite binary32 when no second finite logit exists or the
+ * difference overflows; 0 for a row with a NaN, a +inf or only -inf.  One
+ * extra read of the rows (the fused step does not compute it). */
+int dspark_margin(const dspark_rows* rows, float* margin, void* stream);
+
 /* Test entry: the dense allocation steps of dspark_q_alloc applied to
  * caller-given float32 weights (normalised weights in [0, 1]), so that the
  * consistency assertions can be reached with constructed inputs.

@@ -1,5 +1,5 @@
-"""Plain CPU oracle for q on the wire: the FP32 form of a dyadic24 q row and
-the receiver's check of it.
+"""Plain CPU oracle for q on the wire: the FP32 form of a dyadic24 q row, the
+receiver's check of it, and the margin a reply entry may carry.
 
 TEST INFRASTRUCTURE ONLY, like ``oracle.dyadic24`` (which it uses for the
 constants and for binary32 rounding): only ``tests/``,
@@ -13,7 +13,11 @@ Sources, cited by page title and section:
   value; every such value is exact; the receiver multiplies by M, requires an
   integer, and checks the total with 64-bit integers; there is no
   renormalisation on the receiving side.
-* the same page, section "Versioned v2 message design": the receiver refuses
+* "Remote DSpark drafter -- wire and state contract (DSV41-OFFLOAD)",
+  section 6.3: the optional margin, top1 - top2 of the logits, finite and
+  >= 0 in a reply (readings in ``margin``).
+* "PP1 q transport and scheduling design", section "Versioned v2 message
+  design": the receiver refuses
   duplicate sparse ids (zeros included), an unsorted or non-canonical
   support, ids outside the vocabulary, non-finite, negative or non-dyadic
   values, a total other than M and a zero q at the proposed token; dense
@@ -42,7 +46,7 @@ from fractions import Fraction
 
 import numpy as np
 
-from oracle.dyadic24 import M, ST_BAD_TOPK, ST_OK, round_to_f32
+from oracle.dyadic24 import M, ST_BAD_TOPK, ST_OK, round_to_f32, row_status
 
 ST_Q_BAD_LEN = 10     # sparse length outside [0, topk]
 ST_Q_BAD_ID = 11      # sparse id outside [0, V)
@@ -149,3 +153,36 @@ def check_sparse(ids, vals, length: int, topk: int, k_max: int, vocab: int,
     out = zero.copy()
     out[:length] = counts
     return ST_OK, out
+
+
+# --------------------------------------------------------------------------
+# the margin of a reply entry
+# --------------------------------------------------------------------------
+FLT_MAX = np.float32(np.finfo(np.float32).max)
+
+
+def margin(x) -> np.float32:
+    """Margin of one logit row ("Remote DSpark drafter -- wire and state
+    contract", section 6.3, HAS_MARGIN: top1 - top2 of the logits; the reply
+    must carry a finite value >= 0, and a failed entry carries 0).
+
+    Readings: top2 is the second entry of the row sorted by value, so a
+    repeated maximum gives 0; the difference is rounded to binary32 and a
+    zero is +0.0; when no second finite logit exists (V = 1, or every other
+    logit is -inf) or the difference overflows, the margin is the largest
+    finite binary32.  A row the validity rule refuses (NaN, +inf, all -inf)
+    has margin 0.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if row_status(x) != ST_OK:
+        return np.float32(0.0)
+    v = sorted((float(t) for t in x), reverse=True)
+    m1 = v[0]
+    m2 = v[1] if len(v) > 1 else float("-inf")
+    if m2 == float("-inf"):
+        return FLT_MAX
+    with np.errstate(over="ignore"):
+        d = np.float32(m1) - np.float32(m2)
+    if np.isinf(d):
+        return FLT_MAX
+    return np.float32(0.0) if d == 0 else d

@@ -336,3 +336,37 @@ def test_full_chain_at_full_vocabulary():
     s = out["status"].cpu().numpy()
     assert all(s[r] == Q.ST_Q_MASS for r in range(n) if topk[r] == 0)
     assert all(s[r] == O.ST_OK for r in range(n) if topk[r] != 0)
+
+
+def _margin_rows(V, rng):
+    """Logit rows (binary32 values) for every margin case: ordinary, a
+    repeated maximum, one finite logit, +0/-0 maxima, extreme values, the
+    maximum in the ragged tail, and the refused kinds."""
+    base = (rng.standard_normal(V) * 2).astype(np.float32)
+    rows = [base.copy()]
+    r = base.copy(); r[V // 2] = r.max(); rows.append(r)
+    r = np.full(V, -np.inf, np.float32); r[V - 1] = 2.5; rows.append(r)
+    r = np.full(V, -1.0, np.float32); r[0] = -0.0; r[V - 1] = 0.0; rows.append(r)
+    r = base.copy(); r[1 % V] = 3e38; r[0] = -3e38; rows.append(r)
+    r = base.copy(); r[V - 1] = 50.0; rows.append(r)
+    r = np.round(base).astype(np.float32); rows.append(r)                   # many ties
+    r = base.copy(); r[V // 3] = np.nan; rows.append(r)
+    r = base.copy(); r[V - 1] = np.inf; rows.append(r)
+    rows.append(np.full(V, -np.inf, np.float32))
+    r = base.copy(); r[::3] = -np.inf; rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("V", [1, 2, 7, 257, 3001, 129280, 129283])
+def test_margin(V):
+    from vocab_wide_draft_amd import workloads as W
+    from gpu_helpers import to_dev
+    rng = np.random.default_rng(V + 99)
+    x = _margin_rows(V, rng)
+    for dtype in ("f32", "bf16"):
+        raw = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+        got = B.margin(to_dev(raw, dtype)).cpu().numpy()
+        for j in range(x.shape[0]):
+            f = O.to_f32(raw[j], dtype)
+            want = Q.margin(f)
+            assert got[j].view(np.uint32) == want.view(np.uint32), (dtype, V, j, got[j], want)

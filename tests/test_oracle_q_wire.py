@@ -184,3 +184,39 @@ def test_sparse_refusals():
     i = ids.copy(); i[1] = i[0]; v = vals.copy(); v[4] = np.inf
     st, got = Q.check_sparse(i, v, n, k, kmax, V, token=t)
     assert st == Q.ST_Q_UNSORTED and not got.any()
+
+
+def test_margin_closed_forms():
+    big = np.finfo(np.float32).max
+    assert Q.margin(np.array([1.0, 2.0], np.float32)) == np.float32(1.0)
+    assert Q.margin(np.array([3.0, 1.0, 3.0], np.float32)) == 0.0                  # repeated maximum
+    assert Q.margin(np.array([-np.inf, 5.0, -np.inf], np.float32)) == big          # one finite logit
+    assert Q.margin(np.array([7.0], np.float32)) == big                            # V = 1
+    z = Q.margin(np.array([-0.0, 0.0, -1.0], np.float32))
+    assert z == 0 and not np.signbit(z)                                             # +0.0
+    z = Q.margin(np.array([0.0, -0.0], np.float32))
+    assert z == 0 and not np.signbit(z)
+    assert Q.margin(np.array([3e38, -3e38], np.float32)) == big                    # overflow
+    assert Q.margin(np.array([1.0, np.nan], np.float32)) == 0.0                    # refused rows
+    assert Q.margin(np.array([1.0, np.inf], np.float32)) == 0.0
+    assert Q.margin(np.full(4, -np.inf, np.float32)) == 0.0
+    # binary32 rounding of the difference: 1 - 2**-30 rounds to 1
+    assert Q.margin(np.array([1.0, 2.0 ** -30], np.float32)) == np.float32(1.0)
+
+
+def test_margin_against_partition():
+    """Random rows (bf16-like values with repeats, masks): the top two by
+    numpy.partition, subtracted in binary32."""
+    rng = np.random.default_rng(3)
+    for n in (2, 3, 17, 1000):
+        for _ in range(40):
+            x = np.round(rng.standard_normal(n) * 4, int(rng.integers(0, 3))).astype(np.float32)
+            if rng.integers(0, 3) == 0:
+                x[rng.random(n) < 0.5] = -np.inf
+            if not np.isfinite(x).any():
+                x[0] = 1.0
+            top = np.partition(x, n - 2)[n - 2:]
+            m1, m2 = np.float32(top.max()), np.float32(top.min())
+            want = np.finfo(np.float32).max if m2 == -np.inf else np.float32(m1 - m2)
+            got = Q.margin(x)
+            assert got == want and got >= 0

@@ -46,7 +46,7 @@ class QWire(ctypes.Structure):
 
 
 EXPORTS = ["dspark_propose", "dspark_q_alloc", "dspark_sample", "dspark_verify_greedy", "dspark_fused",
-           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_workspace_bytes", "dspark_q_semantic_id",
+           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_margin", "dspark_workspace_bytes", "dspark_q_semantic_id",
            "dspark_status_name", "dspark_last_error", "dspark_abi_version"]
 
 
@@ -74,6 +74,7 @@ def load_library():
         "dspark_q_alloc_weights": (ctypes.c_int, [P, I64, I64, I64, P, P, P, SZ, P]),
         "dspark_cr_expf": (ctypes.c_int, [P, P, I64, P]),
         "dspark_q_encode": (ctypes.c_int, [P, I64, P, P]),
+        "dspark_margin": (ctypes.c_int, [RP, P, P]),
         "dspark_q_validate": (ctypes.c_int, [ctypes.POINTER(QWire), I64, I64, P, P, P, P, P]),
         "dspark_workspace_bytes": (SZ, [I32, I64, I64, I32]),
         "dspark_q_semantic_id": (ctypes.c_char_p, []),
@@ -290,3 +291,12 @@ def q_validate(vocab: int, topk=None, k_max: int = 0, dense=None, sp_ids=None, s
     tok = None if tokens is None else tokens.to(torch.int32).contiguous()
     _check(lib.dspark_q_validate(ctypes.byref(q), n_rows, vocab, _p(tok), _p(dc), _p(sc), _p(st), _stream()))
     return {"status": st, "dense_counts": dc, "sp_counts": sc}
+
+
+def margin(rows: torch.Tensor):
+    """top1 - top2 of every row (float32 [n_rows])."""
+    lib = load_library()
+    r = _rows(rows)
+    out = torch.empty(rows.shape[0], dtype=torch.float32, device=rows.device)
+    _check(lib.dspark_margin(ctypes.byref(r), _p(out), _stream()))
+    return out

@@ -13,6 +13,7 @@
 #include "dspark.h"
 #include "dense_vd.hpp"
 #include "fast_q.hpp"
+#include "margin.hpp"
 #include "q_wire.hpp"
 
 namespace dspark {
@@ -766,6 +767,21 @@ int dspark_cr_expf(const float* d, float* w, int64_t n, void* stream) {
   const int tpb = 256;
   hipLaunchKernelGGL(cr_exp_kernel, dim3((unsigned)((n + tpb - 1) / tpb)), dim3(tpb), 0,
                      static_cast<hipStream_t>(stream), d, w, n);
+  return check_launch();
+}
+
+int dspark_margin(const dspark_rows* rows, float* margin, void* stream) {
+  int rc = check_rows(rows, "rows NULL");
+  if (rc) return rc;
+  if (rows->n_rows == 0) return DSPARK_SUCCESS;
+  if (!margin) return fail(DSPARK_EINVAL, "NULL margin");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (rows->dtype == DSPARK_BF16)
+    hipLaunchKernelGGL(margin_kernel<DSPARK_BF16>, dim3((unsigned)rows->n_rows), dim3(kMarginBS), 0, s, rows->data,
+                       rows->row_stride, (int)rows->vocab, margin);
+  else
+    hipLaunchKernelGGL(margin_kernel<DSPARK_F32>, dim3((unsigned)rows->n_rows), dim3(kMarginBS), 0, s, rows->data,
+                       rows->row_stride, (int)rows->vocab, margin);
   return check_launch();
 }
 
