@@ -777,7 +777,7 @@ int dspark_margin(const dspark_rows* rows, float* margin, void* stream) {
   if (!margin) return fail(DSPARK_EINVAL, "NULL margin");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (rows->dtype == DSPARK_BF16)
-    hipLaunchKernelGGL(margin_kernel<DSPARK_BF16>, dim3((unsigned)rows->n_rows), dim3(kMarginBS), 0, s, rows->data,
+    hipLaunchKernelGGL(margin_bf16_kernel, dim3((unsigned)rows->n_rows), dim3(kMarginBS), 0, s, rows->data,
                        rows->row_stride, (int)rows->vocab, margin);
   else
     hipLaunchKernelGGL(margin_kernel<DSPARK_F32>, dim3((unsigned)rows->n_rows), dim3(kMarginBS), 0, s, rows->data,
