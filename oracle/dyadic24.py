@@ -405,3 +405,37 @@ def request(draft_rows, target_rows, dtype, mode, topk=None, draws=None):
     return {"draft": drafts, "target_status": [t[0] for t in tg],
             "target_argmax": [t[1] for t in tg], "req_status": rst,
             "accept_len": acc, "bonus": bonus}
+
+
+# --------------------------------------------------------------------------
+# stochastic verification
+# --------------------------------------------------------------------------
+def target_sample_row(raw, dtype, draw):
+    """The target's own draw for one target row: its dense dyadic24 q (the
+    whole vocabulary, as for a dense draft row) sampled with the 24-bit draw.
+    Returns (status, token); a refused row or a draw >= 2**24 gives token 0."""
+    x = to_f32(raw, dtype)
+    st = row_status(x)
+    if st != ST_OK:
+        return st, 0
+    st, ids, c = q_row(x, 0)
+    if st != ST_OK:
+        return st, 0
+    return sample(ids, c, draw)
+
+
+def verify_stochastic(draft_tokens, draft_status, target_rows, dtype, target_draws):
+    """Stochastic verification of one request ("DeepSeek-V4.1 DSpark",
+    "State and sampling contracts"): each of the 6 target rows draws its own
+    token from the target distribution with its own noise; the proposals are
+    accepted while they equal those draws, up to the first mismatch, and the
+    bonus is the target's draw at that position.  Reading: the target
+    distribution of a row is its dyadic24 q, sampled by the integer rule.
+    The acceptance rule itself is the greedy one applied to the drawn target
+    tokens.  Returns (req_status, accept_len, bonus, target tokens, target
+    statuses)."""
+    vocab = len(target_rows[0])
+    tg = [target_sample_row(target_rows[i], dtype, target_draws[i]) for i in range(N_TARGET)]
+    toks, sts = [t[1] for t in tg], [t[0] for t in tg]
+    rst, acc, bonus = verify_greedy(draft_tokens, draft_status, toks, sts, vocab)
+    return rst, acc, bonus, toks, sts

@@ -309,3 +309,42 @@ def test_verify_bruteforce():
         assert acc <= 5
     assert O.verify_greedy([0] * 5, [0] * 5, [0] * 6, [0, 0, 1, 0, 0, 0], 3) == (O.ST_TARGET_INVALID, 0, 0)
     assert O.verify_greedy([0, 7, 0, 0, 0], [0] * 5, [0] * 6, [0] * 6, 3) == (O.ST_DRAFT_INVALID, 0, 0)
+
+
+def test_verify_stochastic_pins():
+    """Stochastic verification: with one-hot target rows every draw gives the
+    argmax, so it equals greedy verification; the emitted tokens (accepted
+    proposals, then the bonus) are always the target's own draws t_0 .. t_L,
+    so the first emitted token follows the target q exactly; a draw out of
+    range or a refused target row refuses the request."""
+    rng = np.random.default_rng(41)
+    V = 9
+    for _ in range(50):
+        tg = np.full((6, V), -np.inf, np.float32)
+        am = rng.integers(0, V, 6)
+        tg[np.arange(6), am] = 1.0
+        d = [int(am[i]) if rng.random() < 0.7 else int((am[i] + 1) % V) for i in range(5)]
+        ds = [O.ST_OK] * 5
+        draws = rng.integers(0, 1 << 24, 6)
+        st, acc, bonus, toks, sts = O.verify_stochastic(d, ds, tg, "f32", draws)
+        g = O.verify_greedy(d, ds, list(am), [O.ST_OK] * 6, V)
+        assert (st, acc, bonus) == g and toks == list(am)
+    for _ in range(50):
+        tg = (rng.standard_normal((6, V)) * 1.5).astype(np.float32)
+        draws = rng.integers(0, 1 << 24, 6)
+        toks = [O.target_sample_row(tg[i], "f32", draws[i])[1] for i in range(6)]
+        d = [toks[i] if rng.random() < 0.6 else int(rng.integers(0, V)) for i in range(5)]
+        st, acc, bonus, t2, _ = O.verify_stochastic(d, [O.ST_OK] * 5, tg, "f32", draws)
+        assert st == O.ST_OK and t2 == toks
+        assert d[:acc] == toks[:acc] and bonus == toks[acc] and (acc == 5 or d[acc] != toks[acc])
+    # the first emitted token over every draw of row 0 is distributed as that row's counts
+    x = np.array([0.5, -1.0, 2.0, 0.0], np.float32)
+    _, ids, c = O.q_row(x, 0)
+    u = np.arange(1 << 24, dtype=np.int64)
+    hist = np.bincount(O.sample_many(ids, c, u), minlength=4)
+    assert np.array_equal(hist, c)
+    tg = np.stack([x] * 6)
+    st, _, _, _, sts = O.verify_stochastic([0] * 5, [O.ST_OK] * 5, tg, "f32", [1 << 24] + [0] * 5)
+    assert st == O.ST_TARGET_INVALID and sts[0] == O.ST_DRAW_RANGE
+    tg2 = tg.copy(); tg2[3, 1] = np.nan
+    assert O.verify_stochastic([0] * 5, [O.ST_OK] * 5, tg2, "f32", [0] * 6)[0] == O.ST_TARGET_INVALID
