@@ -194,6 +194,50 @@ def wire_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def stochastic_bench(args):
+    """Stochastic verification of the R = 1024 mixed workload: the 6,144
+    target rows each get their dense dyadic24 q and their own draw, and the
+    workload's sampled drafts are checked against those draws.  The drafts
+    come from one fused step made before the timed region."""
+    import numpy as np
+    import torch
+
+    from vocab_wide_draft_amd import binding as B
+    from vocab_wide_draft_amd import workloads as W
+
+    w = W.make(5)
+    dev = torch.device("cuda:0")
+    d = torch.from_numpy(w.draft.view(np.int16)).view(torch.bfloat16).to(dev)
+    t = torch.from_numpy(w.target.view(np.int16)).view(torch.bfloat16).to(dev)
+    draws = torch.from_numpy(w.draws.view(np.int32)).to(dev)
+    f = B.fused(d, t, B.SAMPLED, topk=w.topk, k_max=1024, draws=draws)
+    dtok = f["sample"].view(w.R, 5).clone()
+    dst = f["status"].view(w.R, 5).clone()
+    del f, d
+    rng = np.random.default_rng(0xD5A1F00D)
+    tdraws = torch.from_numpy(rng.integers(0, 1 << 24, (w.R, 6), dtype=np.int64).astype(np.int32)).to(dev)
+    out = B.verify_stochastic(t, dtok, tdraws, draft_status=dst)
+    kernel_ms, ms_per_step = _timed(lambda: B.verify_stochastic(t, dtok, tdraws, draft_status=dst, out=out),
+                                    args.steps, args.warmup)
+    n = 6 * w.R
+    alg = n * (w.V * 2 + w.V * 4) + n * 12 + w.R * 32
+    achieved = alg / (kernel_ms * 1e-3) / 1e9
+    acc = out["accept_len"].cpu().numpy()
+    res = {
+        "metric": "target rows verified per second (stochastic verification)",
+        "value": round(n / (ms_per_step * 1e-3), 1), "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "stochastic verification of the R=1024 mixed workload", "R": w.R, "V": w.V,
+                   "target_rows": n, "mean_accept_len": round(float(acc.mean()), 3),
+                   "requests_refused": int((out["req_status"].cpu().numpy() != 0).sum())},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": alg, "kernel_ms": round(kernel_ms, 4)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,9 +247,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
-    ap.add_argument("--op", choices=["step", "wire"], default="step",
+    ap.add_argument("--op", choices=["step", "wire", "stochastic"], default="step",
                     help="step: the fused propose/q/sample/verify step; wire: the receiver's check of the "
-                         "workload's q in the FP32 wire form (and the sender's encoding, reported beside it)")
+                         "workload's q in the FP32 wire form (and the sender's encoding, reported beside it); "
+                         "stochastic: stochastic verification of the workload's sampled drafts")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this step shards by request with no "
@@ -216,6 +261,9 @@ def main():
         return
     if args.op == "wire":
         wire_bench(args)
+        return
+    if args.op == "stochastic":
+        stochastic_bench(args)
         return
 
     import numpy as np

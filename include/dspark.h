@@ -168,6 +168,24 @@ int dspark_verify_greedy(const dspark_rows* target, const int32_t* draft_tokens,
                          int32_t* target_status, int32_t* accept_len, int32_t* bonus,
                          int32_t* req_status, void* ws, size_t ws_bytes, void* stream);
 
+/* Stochastic verification [A, "State and sampling contracts": every target
+ * row draws its own token from the target distribution with independent
+ * noise; proposals are accepted while they match those draws, up to the
+ * first mismatch].  The target distribution of a row is its dense dyadic24
+ * q (as dspark_q_alloc builds it for a dense draft row), sampled by the
+ * integer rule of dspark_sample with target_draws (uint32[n_requests][6],
+ * one per target row).  target_q: uint32[6 * n_requests][vocab], written
+ * with those counts (caller-owned storage; the library allocates nothing).
+ * target_sample, target_status: int32[n_requests][6].  accept_len, bonus,
+ * req_status: int32[n_requests], with the rules of dspark_verify_greedy
+ * applied to the drawn target tokens (bonus = the target's draw at position
+ * accept_len); a target draw >= 2^24 sets that row's DRAW_RANGE and makes
+ * the request TARGET_INVALID. */
+int dspark_verify_stochastic(const dspark_rows* target, const int32_t* draft_tokens,
+                             const int32_t* draft_status, int64_t n_requests, const uint32_t* target_draws,
+                             uint32_t* target_q, int32_t* target_sample, int32_t* target_status,
+                             int32_t* accept_len, int32_t* bonus, int32_t* req_status, void* stream);
+
 /* The whole step in one call: propose + (optional) q + (optional) sample on
  * the 5R draft rows, argmax on the 6R target rows, and greedy verification.
  * mode GREEDY verifies the argmax tokens, SAMPLED the sampled tokens (then q,

@@ -115,3 +115,16 @@ def test_wire_status_codes_agree_with_the_oracle():
         code = int(re.search(r"#define DSPARK_ST_Q_%s (\d+)" % name, src).group(1))
         assert getattr(Q, "ST_Q_" + name) == code
         assert B.STATUS_NAMES[code] == "Q_" + name
+
+
+def test_stochastic_argument_errors():
+    lib = B.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    r = B.Rows(0x1000, 1, 0, 12, 64, 64)
+    assert lib.dspark_verify_stochastic(ctypes.byref(r), fake, None, 3, fake, fake, fake, fake, fake, fake, fake,
+                                        None) == -1                                      # 12 rows != 6 * 3
+    assert lib.dspark_verify_stochastic(ctypes.byref(r), fake, None, 2, None, fake, fake, fake, fake, fake, fake,
+                                        None) == -1                                      # no draws
+    r0 = B.Rows(0x1000, 1, 0, 0, 64, 64)
+    assert lib.dspark_verify_stochastic(ctypes.byref(r0), None, None, 0, None, None, None, None, None, None, None,
+                                        None) == 0

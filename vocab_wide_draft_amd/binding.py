@@ -46,7 +46,7 @@ class QWire(ctypes.Structure):
 
 
 EXPORTS = ["dspark_propose", "dspark_q_alloc", "dspark_sample", "dspark_verify_greedy", "dspark_fused",
-           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_margin", "dspark_workspace_bytes", "dspark_q_semantic_id",
+           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_margin", "dspark_verify_stochastic", "dspark_workspace_bytes", "dspark_q_semantic_id",
            "dspark_status_name", "dspark_last_error", "dspark_abi_version"]
 
 
@@ -75,6 +75,7 @@ def load_library():
         "dspark_cr_expf": (ctypes.c_int, [P, P, I64, P]),
         "dspark_q_encode": (ctypes.c_int, [P, I64, P, P]),
         "dspark_margin": (ctypes.c_int, [RP, P, P]),
+        "dspark_verify_stochastic": (ctypes.c_int, [RP, P, P, I64, P, P, P, P, P, P, P, P]),
         "dspark_q_validate": (ctypes.c_int, [ctypes.POINTER(QWire), I64, I64, P, P, P, P, P]),
         "dspark_workspace_bytes": (SZ, [I32, I64, I64, I32]),
         "dspark_q_semantic_id": (ctypes.c_char_p, []),
@@ -299,4 +300,25 @@ def margin(rows: torch.Tensor):
     r = _rows(rows)
     out = torch.empty(rows.shape[0], dtype=torch.float32, device=rows.device)
     _check(lib.dspark_margin(ctypes.byref(r), _p(out), _stream()))
+    return out
+
+
+def verify_stochastic(target: torch.Tensor, draft_tokens: torch.Tensor, target_draws: torch.Tensor,
+                      draft_status=None, out=None):
+    """target [6R, V]; draft_tokens [R, 5]; target_draws uint32-valued [R, 6].
+    `out` may pass the outputs of an earlier call (same shapes)."""
+    lib = load_library()
+    R, dev = draft_tokens.shape[0], target.device
+    V = target.shape[1]
+    if out is None:
+        out = {"target_q": torch.empty((6 * R, V), dtype=torch.int32, device=dev),
+               "target_sample": _i32(6 * R, dev), "target_status": _i32(6 * R, dev),
+               "accept_len": _i32(R, dev), "bonus": _i32(R, dev), "req_status": _i32(R, dev)}
+    t = _rows(target)
+    dt = draft_tokens.to(torch.int32).contiguous()
+    ds = None if draft_status is None else draft_status.to(torch.int32).contiguous()
+    dr = target_draws.to(torch.int32).contiguous()
+    _check(lib.dspark_verify_stochastic(ctypes.byref(t), _p(dt), _p(ds), R, _p(dr), _p(out["target_q"]),
+                                        _p(out["target_sample"]), _p(out["target_status"]), _p(out["accept_len"]),
+                                        _p(out["bonus"]), _p(out["req_status"]), _stream()))
     return out

@@ -707,6 +707,30 @@ int dspark_verify_greedy(const dspark_rows* target, const int32_t* draft_tokens,
                        accept_len, bonus, req_status, stream);
 }
 
+int dspark_verify_stochastic(const dspark_rows* target, const int32_t* draft_tokens,
+                             const int32_t* draft_status, int64_t n_requests, const uint32_t* target_draws,
+                             uint32_t* target_q, int32_t* target_sample, int32_t* target_status,
+                             int32_t* accept_len, int32_t* bonus, int32_t* req_status, void* stream) {
+  int rc = check_rows(target, "target rows NULL");
+  if (rc) return rc;
+  if (n_requests < 0 || target->n_rows != n_requests * DSPARK_N_TARGET)
+    return fail(DSPARK_EINVAL, "target must hold 6 rows per request");
+  if (n_requests == 0) return DSPARK_SUCCESS;
+  if (!draft_tokens || !target_draws || !target_q || !target_sample || !target_status || !accept_len || !bonus ||
+      !req_status)
+    return fail(DSPARK_EINVAL, "NULL argument");
+  // the target rows take the draft rows' path: dense q, then the in-kernel draw
+  RowsArgs a = rows_args_draft(target);
+  a.row_status = target_status;
+  a.do_q = 1;
+  a.dense = target_q;
+  a.draws = target_draws;
+  a.sample = target_sample;
+  if ((rc = launch_rows(a, target->dtype, stream))) return rc;
+  return launch_verify(n_requests, (int)target->vocab, draft_tokens, draft_status, target_sample, target_status,
+                       accept_len, bonus, req_status, stream);
+}
+
 int dspark_fused(const dspark_rows* draft, const dspark_rows* target, int32_t mode,
                  const dspark_q* q, const uint32_t* draws, int32_t* argmax, float* conf,
                  int32_t* sample, int32_t* row_status, int32_t* target_argmax,
