@@ -29,6 +29,7 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "vocab_wide_draft_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 WIRE_WORKLOAD = "wire_check_r1024_mixed_q"
+STOCHASTIC_WORKLOAD = "stochastic_verify_r1024_targets"
 
 
 def _code_tokens(src: str) -> str:
@@ -232,7 +233,7 @@ def stochastic_bench(args):
                    "target_rows": n, "mean_accept_len": round(float(acc.mean()), 3),
                    "requests_refused": int((out["req_status"].cpu().numpy() != 0).sum())},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(STOCHASTIC_WORKLOAD),
                      "algorithmic_bytes": alg, "kernel_ms": round(kernel_ms, 4)},
     }
     print(json.dumps(res), flush=True)
