@@ -203,9 +203,10 @@ int dspark_fused(const dspark_rows* draft, const dspark_rows* target, int32_t mo
  *   topk:   as in dspark_q (device int32[n_rows]; 0 = dense row, else a
  *           sparse row of at most topk[r] entries; NULL = every row dense).
  *   dense:  float[n_rows][dense_stride]; a dense row sends `padded` values
- *           (vocab <= padded <= dense_stride): the vocabulary, then padding
- *           that must be +0.0.  16-byte aligned, dense_stride a multiple of
- *           4.  May be NULL if no row is dense.
+ *           (vocab <= padded <= dense_stride, padded <= DSPARK_V_MAX + 64):
+ *           the vocabulary, then padding that must be +0.0.  16-byte
+ *           aligned, dense_stride a multiple of 4.  May be NULL if no row is
+ *           dense.
  *   sp_ids: int32[n_rows][k_max], sp_val: float[n_rows][k_max] and
  *   sp_len: int32[n_rows], the first sp_len[r] entries of row r.  May be
  *           NULL if no row is sparse.                                     */
