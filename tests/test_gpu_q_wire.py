@@ -370,3 +370,56 @@ def test_margin(V):
             f = O.to_f32(raw[j], dtype)
             want = Q.margin(f)
             assert got[j].view(np.uint32) == want.view(np.uint32), (dtype, V, j, got[j], want)
+
+
+def test_empty_batches():
+    """No rows: every new entry point succeeds and launches nothing."""
+    V = 1000
+    e = torch.empty((0, V), dtype=torch.float32, device=dev())
+    assert B.q_encode(torch.empty(0, dtype=torch.int32, device=dev())).numel() == 0
+    out = B.q_validate(V, dense=e, want_counts=True)
+    assert out["status"].numel() == 0 and out["dense_counts"].numel() == 0
+    assert B.margin(torch.empty((0, V), dtype=torch.bfloat16, device=dev())).numel() == 0
+    s = B.verify_stochastic(torch.empty((0, V), dtype=torch.bfloat16, device=dev()),
+                            torch.empty((0, 5), dtype=torch.int32, device=dev()),
+                            torch.empty((0, 6), dtype=torch.int32, device=dev()))
+    torch.cuda.synchronize()
+    assert s["accept_len"].numel() == 0
+
+
+def test_largest_vocabulary():
+    """Wire rows and margins at V = 2^20 (the largest vocabulary accepted),
+    with the most padding accepted, against the oracle."""
+    V = 1 << 20
+    P = V + 64
+    rng = np.random.default_rng(2024)
+    pos = rng.choice(V, 3, replace=False)
+    c = np.zeros(V, np.int64)
+    c[pos] = [M // 2, M // 4, M // 4]
+    base = Q.wire_f32(c[pos])
+    rows = np.zeros((3, P), np.float32)
+    rows[:, pos] = base
+    rows[1, V - 1] = np.nan                                  # the last vocabulary entry
+    rows[2, P - 1] = np.float32(2 ** -24)                    # the last padding entry
+    toks = np.array([pos[0], pos[0], pos[1]], np.int32)
+    out = B.q_validate(V, dense=_f32(rows), tokens=_i32(toks), padded=P, want_counts=True)
+    st = out["status"].cpu().numpy()
+    cnt = out["dense_counts"].cpu().numpy().view(np.uint32)
+    for j in range(3):
+        ws, wc = Q.check_dense(rows[j], V, token=int(toks[j]))
+        assert int(st[j]) == ws and np.array_equal(cnt[j], wc), j
+    assert list(st) == [0, Q.ST_Q_NONFINITE, Q.ST_Q_PADDING]
+    # margins of full-size rows, the maximum and the runner-up at the far end
+    from vocab_wide_draft_amd import workloads as W
+    from gpu_helpers import to_dev
+    x = (rng.standard_normal((2, V)) * 2).astype(np.float32)
+    x[0, V - 1] = 40.0
+    x[0, V - 2] = 39.0
+    x[1, :] = -np.inf
+    x[1, V - 1] = 1.0
+    for dtype in ("bf16", "f32"):
+        raw = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+        got = B.margin(to_dev(raw, dtype)).cpu().numpy()
+        for j in range(2):
+            want = Q.margin(O.to_f32(raw[j], dtype))
+            assert got[j].view(np.uint32) == want.view(np.uint32), (dtype, j)
