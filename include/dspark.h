@@ -175,7 +175,10 @@ int dspark_verify_greedy(const dspark_rows* target, const int32_t* draft_tokens,
  * q (as dspark_q_alloc builds it for a dense draft row), sampled by the
  * integer rule of dspark_sample with target_draws (uint32[n_requests][6],
  * one per target row).  target_q: uint32[6 * n_requests][vocab], written
- * with those counts (caller-owned storage; the library allocates nothing).
+ * with those counts (caller-owned storage; the library allocates nothing),
+ * or NULL to keep the counts off memory (the draw needs only their running
+ * sums on chip); NULL is accepted for bf16 rows with vocab <= 131072, whose
+ * rows stay on chip, and is DSPARK_EINVAL otherwise.
  * target_sample, target_status: int32[n_requests][6].  accept_len, bonus,
  * req_status: int32[n_requests], with the rules of dspark_verify_greedy
  * applied to the drawn target tokens (bonus = the target's draw at position

@@ -78,3 +78,27 @@ def test_stochastic_full_vocabulary():
                               draft_status=torch.from_numpy(dst).to(dev()))
     torch.cuda.synchronize()
     _check(raw, draws, dtok, dst, "bf16", out, V, R, q_rows={0, 5, 13})
+
+
+@pytest.mark.parametrize("V", [3001, 129280])
+def test_stochastic_without_counts(V):
+    """With no count storage the draws, accept lengths and bonuses are the
+    same as with it (and as the oracle's)."""
+    R = 6
+    raw, draws, dtok, dst = _case(V, R, "bf16", V + 7)
+    args = (to_dev(raw, "bf16"), torch.from_numpy(dtok).to(dev()), torch.from_numpy(draws.view(np.int32)).to(dev()))
+    a = B.verify_stochastic(*args, draft_status=torch.from_numpy(dst).to(dev()))
+    b = B.verify_stochastic(*args, draft_status=torch.from_numpy(dst).to(dev()), store_q=False)
+    torch.cuda.synchronize()
+    assert b["target_q"] is None
+    for k in ("target_sample", "target_status", "accept_len", "bonus", "req_status"):
+        assert torch.equal(a[k], b[k]), k
+    if V < 10000:
+        _check(raw, draws, dtok, dst, "bf16", {**b, "target_q": a["target_q"]}, V, R, q_rows=set())
+
+
+def test_stochastic_without_counts_needs_resident_rows():
+    x = np.zeros((6, 64), np.float32)
+    with pytest.raises(B.DsparkError):
+        B.verify_stochastic(to_dev(x, "f32"), torch.zeros((1, 5), dtype=torch.int32, device=dev()),
+                            torch.zeros((1, 6), dtype=torch.int32, device=dev()), store_q=False)

@@ -304,14 +304,15 @@ def margin(rows: torch.Tensor):
 
 
 def verify_stochastic(target: torch.Tensor, draft_tokens: torch.Tensor, target_draws: torch.Tensor,
-                      draft_status=None, out=None):
+                      draft_status=None, out=None, store_q: bool = True):
     """target [6R, V]; draft_tokens [R, 5]; target_draws uint32-valued [R, 6].
-    `out` may pass the outputs of an earlier call (same shapes)."""
+    store_q=False keeps the target counts off memory (bf16 rows with
+    V <= 131072 only).  `out` may pass the outputs of an earlier call."""
     lib = load_library()
     R, dev = draft_tokens.shape[0], target.device
     V = target.shape[1]
     if out is None:
-        out = {"target_q": torch.empty((6 * R, V), dtype=torch.int32, device=dev),
+        out = {"target_q": torch.empty((6 * R, V), dtype=torch.int32, device=dev) if store_q else None,
                "target_sample": _i32(6 * R, dev), "target_status": _i32(6 * R, dev),
                "accept_len": _i32(R, dev), "bonus": _i32(R, dev), "req_status": _i32(R, dev)}
     t = _rows(target)

@@ -291,7 +291,7 @@ __device__ __forceinline__ QOut res_dense_q(Res& R, const RStats& st, uint32_t* 
     uint32_t vs = 0;
 #pragma unroll
     for (int l = 0; l < 8; ++l) vs += c[l];
-    if (q < nvec) {
+    if (drow && q < nvec) {  // no count row wanted: the counts only feed the draw
       if (q * 8 + 8 <= V && vec_ok) {
         u32x4* dst = reinterpret_cast<u32x4*>(drow + (size_t)q * 8);
         // plain (write-back) stores: each instruction fills half of every

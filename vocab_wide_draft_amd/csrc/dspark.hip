@@ -46,6 +46,7 @@ struct RowsArgs {
   int32_t* sp_len;
   const uint32_t* draws;
   int32_t* sample;
+  int no_counts;  // dense rows without a count row: the counts only feed the draw (resident bf16 rows)
   // target outputs
   int32_t* t_argmax;
   int32_t* t_status;
@@ -207,8 +208,8 @@ __device__ __forceinline__ void res_draft_dense(const RowsArgs& a, int r, int ks
   fast_clear(sh.fd.nb);  // while the row loads (ordered before the histogram by the head's barriers)
   DSPARK_PHASE_LOADED(9);
   const uint32_t u = a.draws ? a.draws[r] : 0u;
-  const bool dense_row = a.do_q && a.dense != nullptr && kstatus == DSPARK_ST_OK;
-  uint32_t* drow = dense_row ? a.dense + (size_t)r * (size_t)a.V : nullptr;
+  const bool dense_row = a.do_q && (a.dense != nullptr || a.no_counts) && kstatus == DSPARK_ST_OK;
+  uint32_t* drow = dense_row && a.dense ? a.dense + (size_t)r * (size_t)a.V : nullptr;
   const RStats st = res_stats(R, sh.base);
   DSPARK_PHASE(35);
   int status = st.status != DSPARK_ST_OK ? st.status : kstatus;
@@ -242,7 +243,7 @@ __device__ __forceinline__ void res_draft_dense(const RowsArgs& a, int r, int ks
       DSPARK_PHASE(19);
     }
   }
-  if (dense_row && status != DSPARK_ST_OK)
+  if (drow && status != DSPARK_ST_OK)
     for (int i = threadIdx.x; i < a.V; i += BS) drow[i] = 0u;
   if (a.do_q && a.sp_len && threadIdx.x == 0) a.sp_len[r] = 0;
   write_draft(a, r, status, am, cf, tok);
@@ -315,7 +316,7 @@ __device__ __forceinline__ int draft_kind(const RowsArgs& a, int r, int* k, int*
   if (!a.do_q) return 0;
   *k = a.topk ? a.topk[r] : 0;
   const int kcap = a.k_max < a.V ? a.k_max : a.V;
-  if (*k < 0 || *k > kcap || (*k == 0 && a.dense == nullptr)) {
+  if (*k < 0 || *k > kcap || (*k == 0 && a.dense == nullptr && !a.no_counts)) {
     *kstatus = DSPARK_ST_BAD_TOPK;
     return 0;
   }
@@ -716,14 +717,18 @@ int dspark_verify_stochastic(const dspark_rows* target, const int32_t* draft_tok
   if (n_requests < 0 || target->n_rows != n_requests * DSPARK_N_TARGET)
     return fail(DSPARK_EINVAL, "target must hold 6 rows per request");
   if (n_requests == 0) return DSPARK_SUCCESS;
-  if (!draft_tokens || !target_draws || !target_q || !target_sample || !target_status || !accept_len || !bonus ||
-      !req_status)
+  if (!draft_tokens || !target_draws || !target_sample || !target_status || !accept_len || !bonus || !req_status)
     return fail(DSPARK_EINVAL, "NULL argument");
+  // without target_q the counts are not stored; only register-resident bf16
+  // rows work without that row (the streaming path uses it as scratch)
+  if (!target_q && !(target->dtype == DSPARK_BF16 && target->vocab <= NI * BS * 8))
+    return fail(DSPARK_EINVAL, "target_q is required for float32 rows and for vocab > 131072");
   // the target rows take the draft rows' path: dense q, then the in-kernel draw
   RowsArgs a = rows_args_draft(target);
   a.row_status = target_status;
   a.do_q = 1;
   a.dense = target_q;
+  a.no_counts = target_q == nullptr;
   a.draws = target_draws;
   a.sample = target_sample;
   if ((rc = launch_rows(a, target->dtype, stream))) return rc;

@@ -448,7 +448,9 @@ __device__ __forceinline__ QOut fast_dense_q(Res& R, const RStats& st, const FMa
         g[k] = hi ? b1 : b0;
       }
       const int q4 = q & ~3;
-      if (q4 * 8 + 32 <= V && vec_ok) {  // the quad's four vectors are whole
+      if (!drow) {
+        // no count row wanted: the counts only feed the cells of the draw
+      } else if (q4 * 8 + 32 <= V && vec_ok) {  // the quad's four vectors are whole
         char* dst = reinterpret_cast<char*>(drow + (size_t)q4 * 8) + l4 * 16;
         __builtin_nontemporal_store(u32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<u32x4*>(dst));
         __builtin_nontemporal_store(u32x4{g[0], g[1], g[2], g[3]}, reinterpret_cast<u32x4*>(dst + 64));
