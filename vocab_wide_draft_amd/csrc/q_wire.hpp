@@ -12,9 +12,10 @@
 //
 // Both kernels stream: each element is read once and (for the encoder, or
 // when recovered counts are asked for) written once, so HBM bandwidth bounds
-// them.  The check takes one 256-thread workgroup per row; a thread keeps
-// four 16-byte loads in flight and several workgroups share a CU, so the
-// loads of one row overlap the checks of another.
+// them.  The check takes one 1,024-thread workgroup per row (two share a
+// CU, so the dense rows of a batch fill whole rounds of the chip with little
+// tail); a thread keeps four 16-byte loads in flight, and the loads of one
+// row overlap the checks of the other.
 #pragma once
 
 #include <hip/hip_runtime.h>
