@@ -250,6 +250,20 @@ def stochastic_bench(args):
         "with_counts": {"kernel_ms": round(q_ms, 4), "bytes": q_bytes,
                         "achieved_GBs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1)},
     }
+    if not args.no_cpu:
+        from oracle import dyadic24 as O
+        ht, hs, hd = dtok.cpu().numpy(), dst.cpu().numpy(), tdraws.cpu().numpy().view(np.uint32)
+        t0 = time.perf_counter()
+        done = 0
+        for r in range(w.R):
+            O.verify_stochastic(list(ht[r]), list(hs[r]), w.target[6 * r:6 * r + 6], "bf16",
+                                [int(u) for u in hd[r]])
+            done += 1
+            if time.perf_counter() - t0 > args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(6 * done / el, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {done} requests ({6 * done} target rows), oracle.verify_stochastic"}
     print(json.dumps(res), flush=True)
 
 
