@@ -253,6 +253,21 @@ int dspark_q_validate(const dspark_q_wire* q, int64_t n_rows, int64_t vocab, con
  * extra read of the rows (the fused step does not compute it). */
 int dspark_margin(const dspark_rows* rows, float* margin, void* stream);
 
+/* Vocabulary-sharded propose, emulated on one GPU [Q, "Sparse support and
+ * vocabulary-sharded TP2 follow-up"]: each row is cut into n_shards
+ * contiguous shards (ids [g V / n_shards, (g + 1) V / n_shards)), each
+ * handled by its own workgroup as a rank would; shard maxima are merged by
+ * (value desc, id asc), the shards' exact integer weight sums are added and
+ * rounded once.  Outputs (n_rows each; s64 and conf may be NULL): argmax,
+ * s64 = RN64 of the exact sum of RN32(exp(RN32(x - max))), conf =
+ * RN32(1 / s64), row_status (OK, ROW_NAN, ROW_POSINF, ROW_ZERO_MASS; a
+ * refused row has argmax 0, s64 0, conf 0).  Every output is the same for
+ * every n_shards in [1, min(64, vocab)].  ws: device scratch of at least
+ * 48 * n_rows * n_shards bytes, 16-byte aligned (the shard results that
+ * ranks would exchange). */
+int dspark_sharded_propose(const dspark_rows* rows, int32_t n_shards, int32_t* argmax, double* s64, float* conf,
+                           int32_t* row_status, void* ws, size_t ws_bytes, void* stream);
+
 /* Test entry: the dense allocation steps of dspark_q_alloc applied to
  * caller-given float32 weights (normalised weights in [0, 1]), so that the
  * consistency assertions can be reached with constructed inputs.

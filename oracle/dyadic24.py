@@ -439,3 +439,21 @@ def verify_stochastic(draft_tokens, draft_status, target_rows, dtype, target_dra
     toks, sts = [t[1] for t in tg], [t[0] for t in tg]
     rst, acc, bonus = verify_greedy(draft_tokens, draft_status, toks, sts, vocab)
     return rst, acc, bonus, toks, sts
+
+
+# --------------------------------------------------------------------------
+# vocabulary-sharded propose
+# --------------------------------------------------------------------------
+def propose_sum(raw, dtype):
+    """What a vocabulary-sharded propose must reproduce for one row, whatever
+    the shards ("PP1 q transport and scheduling design", "Sparse support and
+    vocabulary-sharded TP2 follow-up": shard maxima merged, exact shard sums
+    merged as integers): (status, argmax, S64) with S64 = RN64 of the exact
+    sum of the weights RN32(exp(RN32(x - m))); a refused row gives (st, 0, 0.0)."""
+    x = to_f32(raw, dtype)
+    st = row_status(x)
+    if st != ST_OK:
+        return st, 0, 0.0
+    m, a = argmax_first(x)
+    A = exact_sum_scaled(weights(x, m))
+    return ST_OK, a, math.ldexp(float(A), -149)

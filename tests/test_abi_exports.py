@@ -128,3 +128,14 @@ def test_stochastic_argument_errors():
     r0 = B.Rows(0x1000, 1, 0, 0, 64, 64)
     assert lib.dspark_verify_stochastic(ctypes.byref(r0), None, None, 0, None, None, None, None, None, None, None,
                                         None) == 0
+
+
+def test_sharded_argument_errors():
+    lib = B.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    r = B.Rows(0x1000, 1, 0, 4, 64, 64)
+    assert lib.dspark_sharded_propose(ctypes.byref(r), 0, fake, None, None, fake, fake, 1 << 20, None) == -1
+    assert lib.dspark_sharded_propose(ctypes.byref(r), 65, fake, None, None, fake, fake, 1 << 20, None) == -1
+    assert lib.dspark_sharded_propose(ctypes.byref(r), 2, fake, None, None, fake, fake, 48 * 8 - 1, None) == -3
+    assert lib.dspark_sharded_propose(ctypes.byref(r), 2, fake, None, None, fake, ctypes.c_void_p(0x1008), 1 << 20,
+                                      None) == -2

@@ -348,3 +348,22 @@ def test_verify_stochastic_pins():
     assert st == O.ST_TARGET_INVALID and sts[0] == O.ST_DRAW_RANGE
     tg2 = tg.copy(); tg2[3, 1] = np.nan
     assert O.verify_stochastic([0] * 5, [O.ST_OK] * 5, tg2, "f32", [0] * 6)[0] == O.ST_TARGET_INVALID
+
+
+def test_propose_sum_closed_forms():
+    """S64 of constant, one-hot and n-equal-maxima rows, and a row whose
+    exact sum needs rounding to binary64."""
+    V = 1000
+    st, a, s = O.propose_sum(np.full(V, 2.5, np.float32), "f32")
+    assert (st, a, s) == (O.ST_OK, 0, float(V))
+    x = np.full(V, -np.inf, np.float32); x[17] = 3.0
+    assert O.propose_sum(x, "f32") == (O.ST_OK, 17, 1.0)
+    x[[5, 900]] = 3.0
+    assert O.propose_sum(x, "f32") == (O.ST_OK, 5, 3.0)
+    # 1 + 2^-60 (twice) + 2^-149 ... : the exact sum rounds once
+    x = np.array([0.0] + [-np.inf] * 3, np.float32)
+    x[1] = np.float32(-41.58883083359672)          # exp gives a weight far below 2^-53
+    st, a, s = O.propose_sum(x, "f32")
+    w = O.weights(x, 0.0)
+    assert s == 1.0 + float(w[1]) and w[1] > 0      # binary64 sum of two terms, rounded once
+    assert O.propose_sum(np.array([1.0, np.nan], np.float32), "f32") == (O.ST_ROW_NAN, 0, 0.0)

@@ -46,7 +46,7 @@ class QWire(ctypes.Structure):
 
 
 EXPORTS = ["dspark_propose", "dspark_q_alloc", "dspark_sample", "dspark_verify_greedy", "dspark_fused",
-           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_margin", "dspark_verify_stochastic", "dspark_workspace_bytes", "dspark_q_semantic_id",
+           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_margin", "dspark_verify_stochastic", "dspark_sharded_propose", "dspark_workspace_bytes", "dspark_q_semantic_id",
            "dspark_status_name", "dspark_last_error", "dspark_abi_version"]
 
 
@@ -75,6 +75,7 @@ def load_library():
         "dspark_cr_expf": (ctypes.c_int, [P, P, I64, P]),
         "dspark_q_encode": (ctypes.c_int, [P, I64, P, P]),
         "dspark_margin": (ctypes.c_int, [RP, P, P]),
+        "dspark_sharded_propose": (ctypes.c_int, [RP, I32, P, P, P, P, P, SZ, P]),
         "dspark_verify_stochastic": (ctypes.c_int, [RP, P, P, I64, P, P, P, P, P, P, P, P]),
         "dspark_q_validate": (ctypes.c_int, [ctypes.POINTER(QWire), I64, I64, P, P, P, P, P]),
         "dspark_workspace_bytes": (SZ, [I32, I64, I64, I32]),
@@ -322,4 +323,18 @@ def verify_stochastic(target: torch.Tensor, draft_tokens: torch.Tensor, target_d
     _check(lib.dspark_verify_stochastic(ctypes.byref(t), _p(dt), _p(ds), R, _p(dr), _p(out["target_q"]),
                                         _p(out["target_sample"]), _p(out["target_status"]), _p(out["accept_len"]),
                                         _p(out["bonus"]), _p(out["req_status"]), _stream()))
+    return out
+
+
+def sharded_propose(rows: torch.Tensor, n_shards: int):
+    """Vocabulary-sharded propose emulated on one GPU: argmax, exact-sum S64,
+    confidence and status of every row, from n_shards shard workgroups."""
+    lib = load_library()
+    n, dev = rows.shape[0], rows.device
+    out = {"argmax": _i32(n, dev), "s64": torch.empty(n, dtype=torch.float64, device=dev),
+           "conf": torch.empty(n, dtype=torch.float32, device=dev), "status": _i32(n, dev)}
+    ws = torch.empty(max(1, 48 * n * n_shards), dtype=torch.uint8, device=dev)
+    r = _rows(rows)
+    _check(lib.dspark_sharded_propose(ctypes.byref(r), int(n_shards), _p(out["argmax"]), _p(out["s64"]),
+                                      _p(out["conf"]), _p(out["status"]), _p(ws), ws.numel(), _stream()))
     return out

@@ -15,6 +15,7 @@
 #include "fast_q.hpp"
 #include "margin.hpp"
 #include "q_wire.hpp"
+#include "sharded.hpp"
 
 namespace dspark {
 
@@ -811,6 +812,38 @@ int dspark_margin(const dspark_rows* rows, float* margin, void* stream) {
   else
     hipLaunchKernelGGL(margin_kernel<DSPARK_F32>, dim3((unsigned)rows->n_rows), dim3(kMarginBS), 0, s, rows->data,
                        rows->row_stride, (int)rows->vocab, margin);
+  return check_launch();
+}
+
+int dspark_sharded_propose(const dspark_rows* rows, int32_t n_shards, int32_t* argmax, double* s64, float* conf,
+                           int32_t* row_status, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_rows(rows, "rows NULL");
+  if (rc) return rc;
+  if (n_shards < 1 || n_shards > 64 || n_shards > rows->vocab) return fail(DSPARK_EINVAL, "n_shards must be in [1, min(64, vocab)]");
+  if (rows->n_rows * n_shards > 0x7fffffff) return fail(DSPARK_EINVAL, "too many shards in one call");
+  if (rows->n_rows == 0) return DSPARK_SUCCESS;
+  if (!argmax || !row_status) return fail(DSPARK_EINVAL, "NULL argmax or row_status");
+  const size_t nb = (size_t)rows->n_rows * (size_t)n_shards;
+  if (!ws || ws_bytes < nb * (sizeof(ShardHead) + sizeof(Acc))) return fail(DSPARK_EWORKSPACE, "workspace too small");
+  if (!aligned16(ws)) return fail(DSPARK_EALIGN, "workspace must be 16-byte aligned");
+  ShardHead* heads = static_cast<ShardHead*>(ws);
+  Acc* sums = reinterpret_cast<Acc*>(static_cast<char*>(ws) + nb * sizeof(ShardHead));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int V = (int)rows->vocab;
+  if (rows->dtype == DSPARK_BF16) {
+    hipLaunchKernelGGL(shard_max_kernel<DSPARK_BF16>, dim3((unsigned)nb), dim3(kShardBS), 0, s, rows->data,
+                       rows->row_stride, V, (int)n_shards, heads);
+    hipLaunchKernelGGL(shard_sum_kernel<DSPARK_BF16>, dim3((unsigned)nb), dim3(kShardBS), 0, s, rows->data,
+                       rows->row_stride, V, (int)n_shards, heads, sums);
+  } else {
+    hipLaunchKernelGGL(shard_max_kernel<DSPARK_F32>, dim3((unsigned)nb), dim3(kShardBS), 0, s, rows->data,
+                       rows->row_stride, V, (int)n_shards, heads);
+    hipLaunchKernelGGL(shard_sum_kernel<DSPARK_F32>, dim3((unsigned)nb), dim3(kShardBS), 0, s, rows->data,
+                       rows->row_stride, V, (int)n_shards, heads, sums);
+  }
+  const int n = (int)rows->n_rows;
+  hipLaunchKernelGGL(shard_merge_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, (int)n_shards, heads,
+                     sums, argmax, s64, conf, row_status);
   return check_launch();
 }
 
