@@ -267,6 +267,41 @@ def stochastic_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def sharded_bench(args):
+    """The vocabulary-sharded propose emulated on one GPU over the 5,120
+    draft rows of the R = 1024 mixed workload, two shards per row (64,640
+    ids each).  Algorithmic bytes are one read of the rows; the emulator
+    reads each shard twice (maximum, then exact sum), as a rank would not
+    have to if its shard stayed on chip."""
+    import numpy as np
+    import torch
+
+    from vocab_wide_draft_amd import binding as B
+    from vocab_wide_draft_amd import workloads as W
+
+    w = W.make(5)
+    dev = torch.device("cuda:0")
+    d = torch.from_numpy(w.draft.view(np.int16)).view(torch.bfloat16).to(dev)
+    G = 2
+    kernel_ms, ms_per_step = _timed(lambda: B.sharded_propose(d, G), args.steps, args.warmup)
+    n = d.shape[0]
+    alg = n * w.V * 2 + n * 20
+    achieved = alg / (kernel_ms * 1e-3) / 1e9
+    st = B.sharded_propose(d, G)["status"].cpu().numpy()
+    res = {
+        "metric": "draft rows proposed per second (vocabulary-sharded, emulated on one GPU)",
+        "value": round(n / (ms_per_step * 1e-3), 1), "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "sharded propose of the R=1024 mixed workload's draft rows", "rows": n, "V": w.V,
+                   "shards": G, "rows_refused": int((st != 0).sum())},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": alg, "kernel_ms": round(kernel_ms, 4)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,10 +311,11 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
-    ap.add_argument("--op", choices=["step", "wire", "stochastic"], default="step",
+    ap.add_argument("--op", choices=["step", "wire", "stochastic", "sharded"], default="step",
                     help="step: the fused propose/q/sample/verify step; wire: the receiver's check of the "
                          "workload's q in the FP32 wire form (and the sender's encoding, reported beside it); "
-                         "stochastic: stochastic verification of the workload's sampled drafts")
+                         "stochastic: stochastic verification of the workload's sampled drafts; "
+                         "sharded: the vocabulary-sharded propose (two shards per row) of its draft rows")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this step shards by request with no "
@@ -293,6 +329,9 @@ def main():
         return
     if args.op == "stochastic":
         stochastic_bench(args)
+        return
+    if args.op == "sharded":
+        sharded_bench(args)
         return
 
     import numpy as np
