@@ -408,34 +408,76 @@ def request(draft_rows, target_rows, dtype, mode, topk=None, draws=None):
 
 
 # --------------------------------------------------------------------------
-# stochastic verification
+# the target distribution p and exact draws from it
 # --------------------------------------------------------------------------
-def target_sample_row(raw, dtype, draw):
-    """The target's own draw for one target row: its dense dyadic24 q (the
-    whole vocabulary, as for a dense draft row) sampled with the 24-bit draw.
-    Returns (status, token); a refused row or a draw >= 2**24 gives token 0."""
+def weight_ints(raw, dtype):
+    """The target distribution of one row at T = 1 as exact integers.
+
+    "PP1 q transport and scheduling design", "Distribution contract and
+    precision": the full target p is the distribution after the unchanged
+    target processors at T = 1, and the CPU oracle's FP32 helper first rounds
+    weights, then normalises them as exact rationals.  Reading: p_v = A_v / A
+    with A_v = w_v * 2**149 (w_v = RN32(exp(RN32(x_v - m))), the same weights
+    as the draft's q) and A = sum A_v.  Returns (status, [A_v], A); a refused
+    row gives (status, None, 0)."""
     x = to_f32(raw, dtype)
     st = row_status(x)
     if st != ST_OK:
-        return st, 0
-    st, ids, c = q_row(x, 0)
+        return st, None, 0
+    m, _ = argmax_first(x)
+    w = weights(x, m)
+    a = [int(v * 2.0**149) for v in w.astype(np.float64).tolist()]
+    return ST_OK, a, sum(a)
+
+
+def inverse_cdf(a, u) -> int:
+    """Exact inverse-CDF draw from non-negative integer weights a (total > 0)
+    with a uniform 64-bit draw u: the first index v (ascending) whose
+    inclusive cumulative weight C_v satisfies C_v * 2**64 > u * total, i.e.
+    C_v > floor(u * total / 2**64).  Index v is returned for
+    ceil(C_v 2**64 / total) - ceil(C_(v-1) 2**64 / total) of the 2**64 draws,
+    within one draw of the exact share a_v / total."""
+    u = int(u)
+    if not 0 <= u < 1 << 64:
+        raise ValueError("draw out of range")
+    total = sum(int(t) for t in a)
+    if total <= 0:
+        raise ValueError("zero total")
+    t = (u * total) >> 64
+    run = 0
+    for v, av in enumerate(a):
+        run += int(av)
+        if run > t:
+            return v
+    raise AssertionError("unreachable: t < total")
+
+
+def target_draw_row(raw, dtype, draw):
+    """The target's own token for one row: an exact inverse-CDF draw from p
+    (weight_ints) with a 64-bit draw.  Returns (status, token); a refused row
+    gives token 0."""
+    st, a, _ = weight_ints(raw, dtype)
     if st != ST_OK:
         return st, 0
-    return sample(ids, c, draw)
+    return ST_OK, inverse_cdf(a, draw)
 
 
+# --------------------------------------------------------------------------
+# stochastic verification
+# --------------------------------------------------------------------------
 def verify_stochastic(draft_tokens, draft_status, target_rows, dtype, target_draws):
     """Stochastic verification of one request ("DeepSeek-V4.1 DSpark",
     "State and sampling contracts"): each of the 6 target rows draws its own
     token from the target distribution with its own noise; the proposals are
     accepted while they equal those draws, up to the first mismatch, and the
-    bonus is the target's draw at that position.  Reading: the target
-    distribution of a row is its dyadic24 q, sampled by the integer rule.
-    The acceptance rule itself is the greedy one applied to the drawn target
-    tokens.  Returns (req_status, accept_len, bonus, target tokens, target
-    statuses)."""
+    bonus is the target's draw at that position.  The target distribution is
+    the full p of weight_ints (the rounding to dyadic counts belongs to the
+    proposal only, "Distribution contract and precision"), drawn exactly
+    with one 64-bit draw per row.  The acceptance rule is the greedy one
+    applied to the drawn target tokens.  Returns (req_status, accept_len,
+    bonus, target tokens, target statuses)."""
     vocab = len(target_rows[0])
-    tg = [target_sample_row(target_rows[i], dtype, target_draws[i]) for i in range(N_TARGET)]
+    tg = [target_draw_row(target_rows[i], dtype, target_draws[i]) for i in range(N_TARGET)]
     toks, sts = [t[1] for t in tg], [t[0] for t in tg]
     rst, acc, bonus = verify_greedy(draft_tokens, draft_status, toks, sts, vocab)
     return rst, acc, bonus, toks, sts

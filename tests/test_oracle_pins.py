@@ -311,12 +311,64 @@ def test_verify_bruteforce():
     assert O.verify_greedy([0, 7, 0, 0, 0], [0] * 5, [0] * 6, [0] * 6, 3) == (O.ST_DRAFT_INVALID, 0, 0)
 
 
+def _draw_hist_closed_form(a, k):
+    """Histogram of inverse-CDF tokens over the 2**k draws u = U * 2**(64 - k):
+    token v takes the U with C_(v-1) 2**k / total <= U < C_v 2**k / total,
+    i.e. ceil(C_v 2**k / total) - ceil(C_(v-1) 2**k / total) of them."""
+    total = sum(a)
+    out, prev, run = [], 0, 0
+    for av in a:
+        run += av
+        cur = -((-run << k) // total)  # ceil(run * 2**k / total)
+        out.append(cur - prev)
+        prev = cur
+    return out
+
+
+def test_inverse_cdf_exhaustive_small_draws():
+    """Every 2**k draw of a k-bit grid: the histogram of the exact inverse-CDF
+    draw equals the closed-form floor shares, on weights with zeros, ties and
+    a wide dynamic range; a one-hot row always gives its token."""
+    rng = np.random.default_rng(59)
+    for k in (1, 4, 10, 13):
+        for trial in range(6):
+            n = int(rng.integers(1, 9))
+            bits = int(rng.integers(1, 150))
+            a = [int.from_bytes(rng.bytes(19), "little") >> (152 - bits) for _ in range(n)]
+            a = [v if rng.random() > 0.3 else 0 for v in a]
+            if sum(a) == 0:
+                a[-1] = 1
+            got = np.bincount([O.inverse_cdf(a, U << (64 - k)) for U in range(1 << k)], minlength=n)
+            assert got.tolist() == _draw_hist_closed_form(a, k), (a, k)
+    a = [0, 0, 5, 0]
+    assert {O.inverse_cdf(a, int(u)) for u in [0, 1, 2**63, 2**64 - 1]} == {2}
+    a = [3, 1]  # boundaries: u * 4 / 2**64 crosses 3 at u = 3 * 2**62
+    assert O.inverse_cdf(a, 3 * 2**62 - 1) == 0 and O.inverse_cdf(a, 3 * 2**62) == 1
+    assert O.inverse_cdf(a, 2**64 - 1) == 1
+    with pytest.raises(ValueError):
+        O.inverse_cdf(a, 2**64)
+
+
+def test_weight_ints_pins():
+    """p's integer weights are the binary32 weights times 2**149 (exact), the
+    argmax token gets 2**149, masked tokens 0, and the constant row gives the
+    uniform distribution."""
+    x = np.array([-np.inf, 0.5, 2.0, 2.0, -3.0], np.float32)
+    st, a, A = O.weight_ints(x, "f32")
+    assert st == O.ST_OK and a[0] == 0 and a[2] == a[3] == 1 << 149 and A == sum(a)
+    assert Fraction(a[1], 1 << 149) == Fraction(float(O.cr_exp_f32(np.array([-1.5], np.float32))[0]))
+    st, a, A = O.weight_ints(np.full(7, -1.25, np.float32), "f32")
+    assert a == [1 << 149] * 7 and A == 7 << 149
+    assert O.weight_ints(np.array([0.0, np.nan], np.float32), "f32")[0] == O.ST_ROW_NAN
+
+
 def test_verify_stochastic_pins():
-    """Stochastic verification: with one-hot target rows every draw gives the
-    argmax, so it equals greedy verification; the emitted tokens (accepted
-    proposals, then the bonus) are always the target's own draws t_0 .. t_L,
-    so the first emitted token follows the target q exactly; a draw out of
-    range or a refused target row refuses the request."""
+    """Stochastic verification draws each target token exactly from p at
+    T = 1: with one-hot target rows every draw gives the argmax, so it equals
+    greedy verification; the emitted tokens are the target's own draws
+    t_0 .. t_L; the first emitted token over a k-bit grid of draws has the
+    closed-form histogram of p's integer weights, including tokens whose
+    dyadic24 count would be 0; a refused target row refuses the request."""
     rng = np.random.default_rng(41)
     V = 9
     for _ in range(50):
@@ -325,29 +377,59 @@ def test_verify_stochastic_pins():
         tg[np.arange(6), am] = 1.0
         d = [int(am[i]) if rng.random() < 0.7 else int((am[i] + 1) % V) for i in range(5)]
         ds = [O.ST_OK] * 5
-        draws = rng.integers(0, 1 << 24, 6)
+        draws = [int(v) for v in rng.integers(0, 2**63, 6, dtype=np.uint64) * 2 + 1]
         st, acc, bonus, toks, sts = O.verify_stochastic(d, ds, tg, "f32", draws)
         g = O.verify_greedy(d, ds, list(am), [O.ST_OK] * 6, V)
         assert (st, acc, bonus) == g and toks == list(am)
     for _ in range(50):
         tg = (rng.standard_normal((6, V)) * 1.5).astype(np.float32)
-        draws = rng.integers(0, 1 << 24, 6)
-        toks = [O.target_sample_row(tg[i], "f32", draws[i])[1] for i in range(6)]
+        draws = [int(v) for v in rng.integers(0, 2**63, 6, dtype=np.uint64) * 2]
+        toks = [O.target_draw_row(tg[i], "f32", draws[i])[1] for i in range(6)]
         d = [toks[i] if rng.random() < 0.6 else int(rng.integers(0, V)) for i in range(5)]
         st, acc, bonus, t2, _ = O.verify_stochastic(d, [O.ST_OK] * 5, tg, "f32", draws)
         assert st == O.ST_OK and t2 == toks
         assert d[:acc] == toks[:acc] and bonus == toks[acc] and (acc == 5 or d[acc] != toks[acc])
-    # the first emitted token over every draw of row 0 is distributed as that row's counts
-    x = np.array([0.5, -1.0, 2.0, 0.0], np.float32)
-    _, ids, c = O.q_row(x, 0)
-    u = np.arange(1 << 24, dtype=np.int64)
-    hist = np.bincount(O.sample_many(ids, c, u), minlength=4)
-    assert np.array_equal(hist, c)
+    # a token far in the tail (dyadic24 count 0) is still drawn with its share of p
+    x = np.array([0.0, -20.0, -30.0, -2.0], np.float32)
+    assert O.q_row(x, 0)[2][2] == 0
+    w = O.weights(x, 0.0)
+    a = [int(Fraction(float(v)) * (1 << 149)) for v in w]
+    k = 16
+    hist = np.bincount([O.target_draw_row(x, "f32", U << (64 - k))[1] for U in range(1 << k)], minlength=4)
+    assert hist.tolist() == _draw_hist_closed_form(a, k)
+    u_tail = -((-(a[0] + a[1]) << 64) // sum(a))  # first draw that reaches token 2
+    assert O.target_draw_row(x, "f32", u_tail)[1] == 2 and O.target_draw_row(x, "f32", u_tail - 1)[1] == 1
     tg = np.stack([x] * 6)
-    st, _, _, _, sts = O.verify_stochastic([0] * 5, [O.ST_OK] * 5, tg, "f32", [1 << 24] + [0] * 5)
-    assert st == O.ST_TARGET_INVALID and sts[0] == O.ST_DRAW_RANGE
     tg2 = tg.copy(); tg2[3, 1] = np.nan
-    assert O.verify_stochastic([0] * 5, [O.ST_OK] * 5, tg2, "f32", [0] * 6)[0] == O.ST_TARGET_INVALID
+    st, _, _, _, sts = O.verify_stochastic([0] * 5, [O.ST_OK] * 5, tg2, "f32", [0] * 6)
+    assert st == O.ST_TARGET_INVALID and sts[3] == O.ST_ROW_NAN
+
+
+def test_weights_rounds_the_difference_to_binary32():
+    """d = RN32(x - m) is a binary32 subtraction: on pairs whose difference is
+    not a binary32 value, the weight equals an independent RN32(exp(d)) of
+    the difference rounded with fractions, and on many of them it differs
+    from the weight of the unrounded binary64 difference (so a subtraction
+    in binary64 would fail this pin)."""
+    rng = np.random.default_rng(61)
+    n_inexact = n_teeth = 0
+    for _ in range(600):
+        m = np.float32(rng.uniform(1.0, 64.0))
+        x = np.float32(m - np.float32(rng.uniform(0.5, 40.0)) + np.float32(rng.uniform(-1e-3, 1e-3)))
+        if rng.random() < 0.3:
+            x = np.float32(rng.uniform(-1e-4, 1e-4))  # far smaller magnitude than m
+        exact = Fraction(float(x)) - Fraction(float(m))
+        if exact > 0:
+            continue
+        d = -O.round_to_f32(-exact)  # RN32 is symmetric
+        if Fraction(float(d)) == exact:
+            continue
+        n_inexact += 1
+        w = O.weights(np.array([x], np.float32), float(m))[0]
+        assert w == _mp_rn32_exp(float(d)), (x, m)
+        if w != _mp_rn32_exp(float(exact)):
+            n_teeth += 1
+    assert n_inexact > 300 and n_teeth > 20, (n_inexact, n_teeth)
 
 
 def test_propose_sum_closed_forms():
