@@ -37,7 +37,8 @@
  *   Empty.    A call with no rows (n_rows == 0, or no requests) checks its
  *             scalar arguments and enqueues nothing; its array pointers may
  *             then be NULL.
- *   Threads.  The library is stateless and reentrant.
+ *   Threads.  The library is stateless and reentrant, except for the one
+ *             allocation-free entry point, whose device scratch is shared.
  */
 #ifndef DSPARK_H
 #define DSPARK_H
@@ -267,6 +268,22 @@ int dspark_margin(const dspark_rows* rows, float* margin, void* stream);
  * ranks would exchange). */
 int dspark_sharded_propose(const dspark_rows* rows, int32_t n_shards, int32_t* argmax, double* s64, float* conf,
                            int32_t* row_status, void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as dspark_sharded_propose, with the shard results kept in a fixed
+ * device array inside the library (DSPARK_NOALLOC_SCRATCH_BYTES per GPU,
+ * held until the process ends) instead of a caller workspace.  Nothing is
+ * allocated.  Limit: n_rows * n_shards <= DSPARK_NOALLOC_ROW_SHARDS; a larger
+ * call returns DSPARK_EWORKSPACE and enqueues nothing.  The array of the
+ * current device is used (the stream must belong to that device); its
+ * address is looked up on the first call on each device.  Every call on one
+ * device shares that array: calls that overlap in time on one device race,
+ * so the caller serialises them (one stream, or events). */
+#define DSPARK_NOALLOC_SCRATCH_BYTES (1u << 22)
+#define DSPARK_NOALLOC_ROW_SHARDS 87381 /* DSPARK_NOALLOC_SCRATCH_BYTES / 48 */
+int dspark_sharded_propose_noalloc(const dspark_rows* rows, int32_t n_shards, int32_t* argmax, double* s64,
+                                   float* conf, int32_t* row_status, void* stream);
 
 /* Test entry: the dense allocation steps of dspark_q_alloc applied to
  * caller-given float32 weights (normalised weights in [0, 1]), so that the

@@ -139,3 +139,14 @@ def test_sharded_argument_errors():
     assert lib.dspark_sharded_propose(ctypes.byref(r), 2, fake, None, None, fake, fake, 48 * 8 - 1, None) == -3
     assert lib.dspark_sharded_propose(ctypes.byref(r), 2, fake, None, None, fake, ctypes.c_void_p(0x1008), 1 << 20,
                                       None) == -2
+
+
+def test_noalloc_limit_refused_on_the_host():
+    """The allocation-free sharded propose refuses a call beyond its device
+    scratch before touching the GPU."""
+    lib = B.load_library()
+    r = B.Rows(16, 1, 0, 1366, 64, 64)
+    fake = ctypes.c_void_p(16)
+    assert lib.dspark_sharded_propose_noalloc(ctypes.byref(r), 64, fake, None, None, fake, None) == -3
+    assert "exceeds" in lib.dspark_last_error().decode()
+    assert lib.dspark_sharded_propose_noalloc(ctypes.byref(r), 65, fake, None, None, fake, None) == -1

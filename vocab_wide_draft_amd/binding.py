@@ -46,7 +46,7 @@ class QWire(ctypes.Structure):
 
 
 EXPORTS = ["dspark_propose", "dspark_q_alloc", "dspark_sample", "dspark_verify_greedy", "dspark_fused",
-           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_margin", "dspark_verify_stochastic", "dspark_sharded_propose", "dspark_workspace_bytes", "dspark_q_semantic_id",
+           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_margin", "dspark_verify_stochastic", "dspark_sharded_propose", "dspark_sharded_propose_noalloc", "dspark_workspace_bytes", "dspark_q_semantic_id",
            "dspark_status_name", "dspark_last_error", "dspark_abi_version"]
 
 
@@ -76,6 +76,7 @@ def load_library():
         "dspark_q_encode": (ctypes.c_int, [P, I64, P, P]),
         "dspark_margin": (ctypes.c_int, [RP, P, P]),
         "dspark_sharded_propose": (ctypes.c_int, [RP, I32, P, P, P, P, P, SZ, P]),
+        "dspark_sharded_propose_noalloc": (ctypes.c_int, [RP, I32, P, P, P, P, P]),
         "dspark_verify_stochastic": (ctypes.c_int, [RP, P, P, I64, P, P, P, P, P, P, P, P]),
         "dspark_q_validate": (ctypes.c_int, [ctypes.POINTER(QWire), I64, I64, P, P, P, P, P]),
         "dspark_workspace_bytes": (SZ, [I32, I64, I64, I32]),
@@ -337,4 +338,19 @@ def sharded_propose(rows: torch.Tensor, n_shards: int):
     r = _rows(rows)
     _check(lib.dspark_sharded_propose(ctypes.byref(r), int(n_shards), _p(out["argmax"]), _p(out["s64"]),
                                       _p(out["conf"]), _p(out["status"]), _p(ws), ws.numel(), _stream()))
+    return out
+
+
+def sharded_propose_noalloc(rows: torch.Tensor, n_shards: int, out=None):
+    """sharded_propose through the allocation-free entry point (the shard
+    results stay in the library's device scratch).  `out` may pass the
+    outputs of an earlier call."""
+    lib = load_library()
+    n, dev = rows.shape[0], rows.device
+    if out is None:
+        out = {"argmax": _i32(n, dev), "s64": torch.empty(n, dtype=torch.float64, device=dev),
+               "conf": torch.empty(n, dtype=torch.float32, device=dev), "status": _i32(n, dev)}
+    r = _rows(rows)
+    _check(lib.dspark_sharded_propose_noalloc(ctypes.byref(r), int(n_shards), _p(out["argmax"]), _p(out["s64"]),
+                                              _p(out["conf"]), _p(out["status"]), _stream()))
     return out

@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "dspark.h"
 #include "dense_vd.hpp"
@@ -516,6 +517,15 @@ __global__ void cr_exp_kernel(const float* d, float* w, int64_t n) {
 
 }  // namespace dspark
 
+// Device scratch of the allocation-free entry point
+// dspark_sharded_propose_noalloc: the per-shard results of a sharded propose
+// (a 16-byte shard head and a 32-byte exact sum per row and shard).  Every
+// GPU the library runs on holds its own copy until the process ends.  In
+// host code the name stands for a host-side shadow, never for the device
+// memory: host code uses only the address that hipGetSymbolAddress returns.
+constexpr size_t kScratchBytes = (size_t)1 << 22;  // 87,381 row-shards
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 // ===================================================================== ABI
 using namespace dspark;
 
@@ -538,6 +548,30 @@ int check_launch() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(DSPARK_EHIP, "no current HIP device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      std::snprintf(g_err, sizeof g_err, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+      return DSPARK_EHIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSPARK_SUCCESS;
+}
 
 int check_rows(const dspark_rows* r, const char* what) {
   if (!r) return fail(DSPARK_EINVAL, what);
@@ -815,17 +849,26 @@ int dspark_margin(const dspark_rows* rows, float* margin, void* stream) {
   return check_launch();
 }
 
-int dspark_sharded_propose(const dspark_rows* rows, int32_t n_shards, int32_t* argmax, double* s64, float* conf,
-                           int32_t* row_status, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Argument checks shared by the two sharded propose entry points.
+int check_sharded(const dspark_rows* rows, int32_t n_shards, const int32_t* argmax, const int32_t* row_status) {
   int rc = check_rows(rows, "rows NULL");
   if (rc) return rc;
   if (n_shards < 1 || n_shards > 64 || n_shards > rows->vocab) return fail(DSPARK_EINVAL, "n_shards must be in [1, min(64, vocab)]");
   if (rows->n_rows * n_shards > 0x7fffffff) return fail(DSPARK_EINVAL, "too many shards in one call");
-  if (rows->n_rows == 0) return DSPARK_SUCCESS;
-  if (!argmax || !row_status) return fail(DSPARK_EINVAL, "NULL argmax or row_status");
+  if (rows->n_rows > 0 && (!argmax || !row_status)) return fail(DSPARK_EINVAL, "NULL argmax or row_status");
+  return DSPARK_SUCCESS;
+}
+
+constexpr size_t kShardBytes = sizeof(ShardHead) + sizeof(Acc);  // workspace per row and shard
+
+// The three launches of a sharded propose, with the shard results in ws
+// (at least kShardBytes per row and shard, 16-byte aligned).
+int launch_sharded(const dspark_rows* rows, int32_t n_shards, int32_t* argmax, double* s64, float* conf,
+                   int32_t* row_status, void* ws, void* stream) {
   const size_t nb = (size_t)rows->n_rows * (size_t)n_shards;
-  if (!ws || ws_bytes < nb * (sizeof(ShardHead) + sizeof(Acc))) return fail(DSPARK_EWORKSPACE, "workspace too small");
-  if (!aligned16(ws)) return fail(DSPARK_EALIGN, "workspace must be 16-byte aligned");
   ShardHead* heads = static_cast<ShardHead*>(ws);
   Acc* sums = reinterpret_cast<Acc*>(static_cast<char*>(ws) + nb * sizeof(ShardHead));
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -845,6 +888,39 @@ int dspark_sharded_propose(const dspark_rows* rows, int32_t n_shards, int32_t* a
   hipLaunchKernelGGL(shard_merge_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, (int)n_shards, heads,
                      sums, argmax, s64, conf, row_status);
   return check_launch();
+}
+}  // namespace
+
+extern "C" {
+
+int dspark_sharded_propose(const dspark_rows* rows, int32_t n_shards, int32_t* argmax, double* s64, float* conf,
+                           int32_t* row_status, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_sharded(rows, n_shards, argmax, row_status);
+  if (rc) return rc;
+  if (rows->n_rows == 0) return DSPARK_SUCCESS;
+  const size_t nb = (size_t)rows->n_rows * (size_t)n_shards;
+  if (!ws || ws_bytes < nb * kShardBytes) return fail(DSPARK_EWORKSPACE, "workspace too small");
+  if (!aligned16(ws)) return fail(DSPARK_EALIGN, "workspace must be 16-byte aligned");
+  return launch_sharded(rows, n_shards, argmax, s64, conf, row_status, ws, stream);
+}
+
+int dspark_sharded_propose_noalloc(const dspark_rows* rows, int32_t n_shards, int32_t* argmax, double* s64,
+                                   float* conf, int32_t* row_status, void* stream) {
+  int rc = check_sharded(rows, n_shards, argmax, row_status);
+  if (rc) return rc;
+  if (rows->n_rows == 0) return DSPARK_SUCCESS;
+  const size_t nb = (size_t)rows->n_rows * (size_t)n_shards;
+  if (nb > kScratchBytes / kShardBytes) {
+    std::snprintf(g_err, sizeof g_err,
+                  "n_rows * n_shards = %zu exceeds the %zu row-shards of the library's device scratch", nb,
+                  kScratchBytes / kShardBytes);
+    return DSPARK_EWORKSPACE;
+  }
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  // every shard result is written before it is read within the call, so the
+  // scratch needs no clearing
+  return launch_sharded(rows, n_shards, argmax, s64, conf, row_status, ws, stream);
 }
 
 int dspark_q_encode(const uint32_t* counts, int64_t n, float* values, void* stream) {
