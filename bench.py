@@ -200,12 +200,10 @@ def wire_bench(args):
     print(json.dumps(res), flush=True)
 
 
-def stochastic_bench(args):
-    """Stochastic verification of the R = 1024 mixed workload: the 6,144
-    target rows each get their dense dyadic24 q (kept on chip) and their own
-    draw, and the workload's sampled drafts are checked against those draws.
-    The drafts come from one fused step made before the timed region; the
-    same call with the count rows written out is timed beside it."""
+def _mixed_step_outputs():
+    """The R = 1024 mixed workload on the device and one fused step of it
+    (made before any timed region): target rows, the sampled drafts, their
+    statuses and q."""
     import numpy as np
     import torch
 
@@ -220,50 +218,127 @@ def stochastic_bench(args):
     f = B.fused(d, t, B.SAMPLED, topk=w.topk, k_max=1024, draws=draws)
     dtok = f["sample"].view(w.R, 5).clone()
     dst = f["status"].view(w.R, 5).clone()
-    del f, d
+    return w, t, dtok, dst, f["q"]
+
+
+def stochastic_bench(args):
+    """Stochastic verification of the R = 1024 mixed workload: each of the
+    6,144 target rows gets an exact inverse-CDF draw from its p with its own
+    64-bit draw, and the workload's sampled drafts are checked against those
+    draws."""
+    import numpy as np
+
+    from vocab_wide_draft_amd import binding as B
+
+    w, t, dtok, dst, _ = _mixed_step_outputs()
     rng = np.random.default_rng(0xD5A1F00D)
-    tdraws = torch.from_numpy(rng.integers(0, 1 << 24, (w.R, 6), dtype=np.int64).astype(np.int32)).to(dev)
-    # the verification needs only the draws, so the target counts stay on chip
-    out = B.verify_stochastic(t, dtok, tdraws, draft_status=dst, store_q=False)
+    tdr = rng.integers(0, 2**63, (w.R, 6), dtype=np.uint64) * np.uint64(2)
+    tdraws = B.u64_draws(tdr, t.device)
+    out = B.verify_stochastic(t, dtok, tdraws, draft_status=dst)
     kernel_ms, ms_per_step = _timed(lambda: B.verify_stochastic(t, dtok, tdraws, draft_status=dst, out=out),
                                     args.steps, args.warmup)
     n = 6 * w.R
-    alg = n * w.V * 2 + n * 12 + w.R * 32
-    # beside it: the same call with the target count rows written out
-    out_q = B.verify_stochastic(t, dtok, tdraws, draft_status=dst)
-    q_ms, _ = _timed(lambda: B.verify_stochastic(t, dtok, tdraws, draft_status=dst, out=out_q),
-                     args.steps, args.warmup)
-    q_bytes = alg + n * w.V * 4
+    alg = n * w.V * 2 + n * 16 + w.R * 32
     achieved = alg / (kernel_ms * 1e-3) / 1e9
     acc = out["accept_len"].cpu().numpy()
     res = {
         "metric": "target rows verified per second (stochastic verification)",
         "value": round(n / (ms_per_step * 1e-3), 1), "unit": "rows/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int256", "data": "synthetic",
         "config": {"workload": "stochastic verification of the R=1024 mixed workload", "R": w.R, "V": w.V,
                    "target_rows": n, "mean_accept_len": round(float(acc.mean()), 3),
                    "requests_refused": int((out["req_status"].cpu().numpy() != 0).sum())},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(STOCHASTIC_WORKLOAD),
                      "algorithmic_bytes": alg, "kernel_ms": round(kernel_ms, 4)},
-        "with_counts": {"kernel_ms": round(q_ms, 4), "bytes": q_bytes,
-                        "achieved_GBs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1)},
     }
     if not args.no_cpu:
         from oracle import dyadic24 as O
-        ht, hs, hd = dtok.cpu().numpy(), dst.cpu().numpy(), tdraws.cpu().numpy().view(np.uint32)
+        ht, hs = dtok.cpu().numpy(), dst.cpu().numpy()
         t0 = time.perf_counter()
         done = 0
         for r in range(w.R):
             O.verify_stochastic(list(ht[r]), list(hs[r]), w.target[6 * r:6 * r + 6], "bf16",
-                                [int(u) for u in hd[r]])
+                                [int(u) for u in tdr[r]])
             done += 1
             if time.perf_counter() - t0 > args.cpu_seconds:
                 break
         el = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": round(6 * done / el, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
                                "sample": f"first {done} requests ({6 * done} target rows), oracle.verify_stochastic"}
+    print(json.dumps(res), flush=True)
+
+
+def ratio_bench(args):
+    """Probability-ratio verification of the R = 1024 mixed workload's
+    sampled drafts against its target rows, with the drafts' dyadic q (dense,
+    k = 32 and k = 1024 rows).  Algorithmic bytes per request: the target
+    rows it reads (up to the position that ends it), and the q row of a
+    rejected position (4 B per dense count, 8 B per sparse entry)."""
+    import numpy as np
+
+    from oracle import dyadic24 as O  # noqa: F401  (cpu_baseline leg below)
+    from vocab_wide_draft_amd import binding as B
+
+    w, t, dtok, dst, qd = _mixed_step_outputs()
+    rng = np.random.default_rng(0xD5A1F00E)
+    ad = rng.integers(0, 2**63, (w.R, 5), dtype=np.uint64) * np.uint64(2)
+    fd = rng.integers(0, 2**63, w.R, dtype=np.uint64) * np.uint64(2) + np.uint64(1)
+    adv, fdv = B.u64_draws(ad, t.device), B.u64_draws(fd, t.device)
+    out = B.verify_ratio(t, dtok, qd, adv, fdv, draft_status=dst)
+    kernel_ms, ms_per_step = _timed(lambda: B.verify_ratio(t, dtok, qd, adv, fdv, draft_status=dst, out=out),
+                                    args.steps, args.warmup)
+    acc = out["accept_len"].cpu().numpy()
+    rst = out["req_status"].cpu().numpy()
+    hs = dst.cpu().numpy()
+    lens = qd["sp_len"].cpu().numpy()
+    topk = np.asarray(w.topk)
+    alg = 0
+    for r in range(w.R):
+        if rst[r] != 0:
+            continue
+        i = int(acc[r])
+        alg += (i + 1) * w.V * 2 + 5 * 8 + 8 + 12
+        j = 5 * r + i
+        if i < 5 and hs[r, i] == 0:  # ended by a rejection: the residual reads q
+            alg += w.V * 4 if topk[j] == 0 else int(lens[j]) * 8
+    achieved = alg / (kernel_ms * 1e-3) / 1e9
+    res = {
+        "metric": "requests verified per second (probability-ratio verification)",
+        "value": round(w.R / (ms_per_step * 1e-3), 1), "unit": "requests/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int256", "data": "synthetic",
+        "config": {"workload": "ratio verification of the R=1024 mixed workload", "R": w.R, "V": w.V,
+                   "mean_accept_len": round(float(acc[rst == 0].mean()), 3),
+                   "requests_refused": int((rst != 0).sum())},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": alg, "kernel_ms": round(kernel_ms, 4)},
+    }
+    if not args.no_cpu:
+        from oracle import ratio as RT
+        hq = {k: (v.cpu().numpy() if v is not None and hasattr(v, "cpu") else v) for k, v in qd.items()}
+        ht = dtok.cpu().numpy()
+        t0 = time.perf_counter()
+        done = 0
+        for r in range(w.R):
+            qs = []
+            for i in range(5):
+                j = 5 * r + i
+                if topk[j] == 0:
+                    qs.append((np.arange(w.V), hq["dense"][j].view(np.uint32)))
+                else:
+                    n = int(hq["sp_len"][j])
+                    qs.append((hq["sp_ids"][j, :n], hq["sp_cnt"][j, :n].view(np.uint32)))
+            RT.verify_ratio(list(ht[r]), list(hs[r]), qs, w.target[6 * r:6 * r + 6], "bf16",
+                            [int(u) for u in ad[r]], int(fd[r]))
+            done += 1
+            if time.perf_counter() - t0 > args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(done / el, 3), "unit": "requests/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {done} requests, oracle.ratio.verify_ratio"}
     print(json.dumps(res), flush=True)
 
 
@@ -311,10 +386,11 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
-    ap.add_argument("--op", choices=["step", "wire", "stochastic", "sharded"], default="step",
+    ap.add_argument("--op", choices=["step", "wire", "stochastic", "ratio", "sharded"], default="step",
                     help="step: the fused propose/q/sample/verify step; wire: the receiver's check of the "
                          "workload's q in the FP32 wire form (and the sender's encoding, reported beside it); "
                          "stochastic: stochastic verification of the workload's sampled drafts; "
+                         "ratio: probability-ratio verification of them with their q; "
                          "sharded: the vocabulary-sharded propose (two shards per row) of its draft rows")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -329,6 +405,9 @@ def main():
         return
     if args.op == "stochastic":
         stochastic_bench(args)
+        return
+    if args.op == "ratio":
+        ratio_bench(args)
         return
     if args.op == "sharded":
         sharded_bench(args)

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 1
+#define DSPARK_ABI_VERSION 2
 #define DSPARK_MASS (1u << 24)   /* M, total count of a q row [Q] */
 #define DSPARK_N_DRAFT 5         /* draft rows per request [C 2] */
 #define DSPARK_N_TARGET 6        /* anchor + 5 target rows per request [A] */
@@ -172,23 +172,56 @@ int dspark_verify_greedy(const dspark_rows* target, const int32_t* draft_tokens,
 /* Stochastic verification [A, "State and sampling contracts": every target
  * row draws its own token from the target distribution with independent
  * noise; proposals are accepted while they match those draws, up to the
- * first mismatch].  The target distribution of a row is its dense dyadic24
- * q (as dspark_q_alloc builds it for a dense draft row), sampled by the
- * integer rule of dspark_sample with target_draws (uint32[n_requests][6],
- * one per target row).  target_q: uint32[6 * n_requests][vocab], written
- * with those counts (caller-owned storage; the library allocates nothing),
- * or NULL to keep the counts off memory (the draw needs only their running
- * sums on chip); NULL is accepted for bf16 rows with vocab <= 131072, whose
- * rows stay on chip, and is DSPARK_EINVAL otherwise.
- * target_sample, target_status: int32[n_requests][6].  accept_len, bonus,
- * req_status: int32[n_requests], with the rules of dspark_verify_greedy
- * applied to the drawn target tokens (bonus = the target's draw at position
- * accept_len); a target draw >= 2^24 sets that row's DRAW_RANGE and makes
- * the request TARGET_INVALID. */
+ * first mismatch].  The target distribution of a row is the full p at T = 1
+ * [Q, "Distribution contract and precision": rounding to dyadic counts
+ * changes the proposal only, not the legal target]: p_v = A_v / A with the
+ * exact integers A_v = w_v 2^149 of the weights w_v = RN32(exp(RN32(x_v - m)))
+ * and A = sum_v A_v.  Row i of request r takes the first token v (ascending
+ * id) whose cumulative weight C_v satisfies C_v > floor(u A / 2^64), u =
+ * target_draws[r][i] (uniform 64-bit; every value is valid).
+ * target_draws: uint64[n_requests][6].  target_sample, target_status:
+ * int32[n_requests][6] (a refused row: its status and token 0).
+ * accept_len, bonus, req_status: int32[n_requests], with the rules of
+ * dspark_verify_greedy applied to the drawn target tokens (bonus = the
+ * target's draw at position accept_len).  Every target row is read once
+ * (bf16 rows up to 131072 ids) or three times (float32 rows, longer rows). */
 int dspark_verify_stochastic(const dspark_rows* target, const int32_t* draft_tokens,
-                             const int32_t* draft_status, int64_t n_requests, const uint32_t* target_draws,
-                             uint32_t* target_q, int32_t* target_sample, int32_t* target_status,
-                             int32_t* accept_len, int32_t* bonus, int32_t* req_status, void* stream);
+                             const int32_t* draft_status, int64_t n_requests, const uint64_t* target_draws,
+                             int32_t* target_sample, int32_t* target_status, int32_t* accept_len, int32_t* bonus,
+                             int32_t* req_status, void* stream);
+
+/* Probability-ratio verification with the dyadic q and full-vocabulary
+ * residual sampling [Q, "Distribution contract and precision", last
+ * paragraph: ratio tests and residual sampling use the full target p at
+ * T = 1 and the defined q; "Sparse support and vocabulary-sharded TP2
+ * follow-up": max(p - q, 0) for every token, including tokens outside a
+ * sparse q's support; "Versioned v2 message design": zero q at the proposed
+ * token is refused, acceptance and correction draws are separate].  p is the
+ * distribution of dspark_verify_stochastic; q(v) = c_v / 2^24 from draft_q
+ * (the draft rows' counts as dspark_q_alloc / dspark_fused write them, 5
+ * rows per request).  Per request, at fixed depth five:
+ *   - every draft row with status OK (draft_status int32[n][5], or NULL =
+ *     all OK) must carry a token in [0, V) with q(token) > 0, else
+ *     DRAFT_INVALID;
+ *   - positions i = 0..4 in order read target row i (refused ->
+ *     TARGET_INVALID); a draft row that failed ends the request with a draw
+ *     from p_i; otherwise the proposal x is accepted when
+ *     u_i c_x A < A_x 2^88 (U = u_i / 2^64 < p_i(x) / q_i(x), u_i =
+ *     accept_draws[r][i]); on rejection the request ends with a draw from the
+ *     residual, weights max(2^24 A_v - c_v A, 0), by the rule of
+ *     dspark_verify_stochastic with u = final_draws[r];
+ *   - after five acceptances, the bonus is drawn from p_5 with final_draws[r].
+ * Target rows after the one that ends a request are not read.  Outputs
+ * (int32[n_requests]): accept_len (0..5 committed proposals), token (the
+ * correction or bonus token), req_status (OK, DRAFT_INVALID, TARGET_INVALID,
+ * or ALLOC_INCONSISTENT for a zero residual, which needs counts that do not
+ * sum to 2^24).  accept_draws: uint64[n_requests][5]; final_draws:
+ * uint64[n_requests].  Six launches of n_requests workgroups; the outputs
+ * carry the state between them, so they must not alias the inputs. */
+int dspark_verify_ratio(const dspark_rows* target, const int32_t* draft_tokens, const int32_t* draft_status,
+                        const dspark_q* draft_q, int64_t n_requests, const uint64_t* accept_draws,
+                        const uint64_t* final_draws, int32_t* accept_len, int32_t* token, int32_t* req_status,
+                        void* stream);
 
 /* The whole step in one call: propose + (optional) q + (optional) sample on
  * the 5R draft rows, argmax on the 6R target rows, and greedy verification.

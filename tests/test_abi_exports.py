@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_host_queries():
     B.load_library()
-    assert B.abi_version() == 1
+    assert B.abi_version() == 2
     assert B.q_semantic_id() == "dyadic24-standard-v1"
     for code, name in B.STATUS_NAMES.items():
         assert B.status_name(code) == name
@@ -117,17 +117,29 @@ def test_wire_status_codes_agree_with_the_oracle():
         assert B.STATUS_NAMES[code] == "Q_" + name
 
 
-def test_stochastic_argument_errors():
+def test_stochastic_and_ratio_argument_errors():
     lib = B.load_library()
     fake = ctypes.c_void_p(0x1000)
     r = B.Rows(0x1000, 1, 0, 12, 64, 64)
-    assert lib.dspark_verify_stochastic(ctypes.byref(r), fake, None, 3, fake, fake, fake, fake, fake, fake, fake,
+    assert lib.dspark_verify_stochastic(ctypes.byref(r), fake, None, 3, fake, fake, fake, fake, fake, fake,
                                         None) == -1                                      # 12 rows != 6 * 3
-    assert lib.dspark_verify_stochastic(ctypes.byref(r), fake, None, 2, None, fake, fake, fake, fake, fake, fake,
+    assert lib.dspark_verify_stochastic(ctypes.byref(r), fake, None, 2, None, fake, fake, fake, fake, fake,
                                         None) == -1                                      # no draws
     r0 = B.Rows(0x1000, 1, 0, 0, 64, 64)
-    assert lib.dspark_verify_stochastic(ctypes.byref(r0), None, None, 0, None, None, None, None, None, None, None,
+    assert lib.dspark_verify_stochastic(ctypes.byref(r0), None, None, 0, None, None, None, None, None, None,
                                         None) == 0
+    q = B.Q(None, 0, 0, fake, None, None, None)
+    assert lib.dspark_verify_ratio(ctypes.byref(r), fake, None, None, 2, fake, fake, fake, fake, fake,
+                                   None) == -1                                           # no q
+    assert lib.dspark_verify_ratio(ctypes.byref(r), fake, None, ctypes.byref(q), 3, fake, fake, fake, fake, fake,
+                                   None) == -1                                           # 12 rows != 6 * 3
+    assert lib.dspark_verify_ratio(ctypes.byref(r), fake, None, ctypes.byref(q), 2, None, fake, fake, fake, fake,
+                                   None) == -1                                           # no acceptance draws
+    qs = B.Q(fake, 64, 0, None, None, None, None)
+    assert lib.dspark_verify_ratio(ctypes.byref(r), fake, None, ctypes.byref(qs), 2, fake, fake, fake, fake, fake,
+                                   None) == -1                                           # sparse arrays missing
+    assert lib.dspark_verify_ratio(ctypes.byref(r0), None, None, ctypes.byref(q), 0, None, None, None, None, None,
+                                   None) == 0
 
 
 def test_sharded_argument_errors():

@@ -68,17 +68,49 @@ def test_stochastic_bench_launch(step):
     dtok = out["sample"].view(w.R, 5)
     dst = out["status"].view(w.R, 5)
     rng = np.random.default_rng(0xD5A1F00D)
-    tdr = rng.integers(0, 1 << 24, (w.R, 6), dtype=np.int64).astype(np.uint32)
-    tdraws = torch.from_numpy(tdr.view(np.int32)).to(DEV)
-    res = B.verify_stochastic(t, dtok, tdraws, draft_status=dst, store_q=False)
+    tdr = rng.integers(0, 2**63, (w.R, 6), dtype=np.uint64) * np.uint64(2)
+    res = B.verify_stochastic(t, dtok, tdr, draft_status=dst)
     acc = res["accept_len"].cpu().numpy()
     assert ((acc >= 0) & (acc <= 5)).all()
     ht, hs = dtok.cpu().numpy(), dst.cpu().numpy()
-    for r in rng.choice(w.R, 2, replace=False):
+    for r in rng.choice(w.R, 3, replace=False):
         st, a, b, toks, sts = O.verify_stochastic(list(ht[r]), list(hs[r]), w.target[6 * r:6 * r + 6], "bf16",
                                                   [int(u) for u in tdr[r]])
         assert (int(res["req_status"][r]), int(res["accept_len"][r]), int(res["bonus"][r])) == (st, a, b)
         assert res["target_sample"][6 * r:6 * r + 6].cpu().tolist() == toks
+
+
+def test_ratio_bench_launch(step):
+    """Probability-ratio verification in the bench's launch configuration
+    (the R = 1024 mixed workload's sampled drafts and q): valid ranges for
+    every request, sampled requests against the oracle."""
+    from oracle import ratio as RT
+    w, d, t, out = step
+    dtok = out["sample"].view(w.R, 5)
+    dst = out["status"].view(w.R, 5)
+    qd = out["q"]
+    rng = np.random.default_rng(0xD5A1F00E)
+    ad = rng.integers(0, 2**63, (w.R, 5), dtype=np.uint64) * np.uint64(2)
+    fd = rng.integers(0, 2**63, w.R, dtype=np.uint64) * np.uint64(2) + np.uint64(1)
+    res = B.verify_ratio(t, dtok, qd, ad, fd, draft_status=dst)
+    acc, tok, rst = (res[k].cpu().numpy() for k in ("accept_len", "token", "req_status"))
+    assert ((acc >= 0) & (acc <= 5)).all() and ((tok >= 0) & (tok < w.V)).all()
+    assert (rst == 0).all()
+    ht, hs = dtok.cpu().numpy(), dst.cpu().numpy()
+    topk = np.asarray(w.topk)
+    hq = {k: (v.cpu().numpy() if hasattr(v, "cpu") else v) for k, v in qd.items()}
+    for r in rng.choice(w.R, 3, replace=False):
+        qs = []
+        for i in range(5):
+            j = 5 * r + i
+            if topk[j] == 0:
+                qs.append((np.arange(w.V), hq["dense"][j].view(np.uint32)))
+            else:
+                n = int(hq["sp_len"][j])
+                qs.append((hq["sp_ids"][j, :n], hq["sp_cnt"][j, :n].view(np.uint32)))
+        want = RT.verify_ratio(list(ht[r]), list(hs[r]), qs, w.target[6 * r:6 * r + 6], "bf16",
+                               [int(u) for u in ad[r]], int(fd[r]))
+        assert (int(rst[r]), int(acc[r]), int(tok[r])) == want[:3], (r, want)
 
 
 def test_sharded_bench_launch(step):

@@ -382,7 +382,7 @@ def test_empty_batches():
     assert B.margin(torch.empty((0, V), dtype=torch.bfloat16, device=dev())).numel() == 0
     s = B.verify_stochastic(torch.empty((0, V), dtype=torch.bfloat16, device=dev()),
                             torch.empty((0, 5), dtype=torch.int32, device=dev()),
-                            torch.empty((0, 6), dtype=torch.int32, device=dev()))
+                            torch.empty((0, 6), dtype=torch.int64, device=dev()))
     torch.cuda.synchronize()
     assert s["accept_len"].numel() == 0
 

@@ -46,7 +46,7 @@ class QWire(ctypes.Structure):
 
 
 EXPORTS = ["dspark_propose", "dspark_q_alloc", "dspark_sample", "dspark_verify_greedy", "dspark_fused",
-           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_margin", "dspark_verify_stochastic", "dspark_sharded_propose", "dspark_sharded_propose_noalloc", "dspark_workspace_bytes", "dspark_q_semantic_id",
+           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_margin", "dspark_verify_stochastic", "dspark_verify_ratio", "dspark_sharded_propose", "dspark_sharded_propose_noalloc", "dspark_workspace_bytes", "dspark_q_semantic_id",
            "dspark_status_name", "dspark_last_error", "dspark_abi_version"]
 
 
@@ -77,7 +77,8 @@ def load_library():
         "dspark_margin": (ctypes.c_int, [RP, P, P]),
         "dspark_sharded_propose": (ctypes.c_int, [RP, I32, P, P, P, P, P, SZ, P]),
         "dspark_sharded_propose_noalloc": (ctypes.c_int, [RP, I32, P, P, P, P, P]),
-        "dspark_verify_stochastic": (ctypes.c_int, [RP, P, P, I64, P, P, P, P, P, P, P, P]),
+        "dspark_verify_stochastic": (ctypes.c_int, [RP, P, P, I64, P, P, P, P, P, P, P]),
+        "dspark_verify_ratio": (ctypes.c_int, [RP, P, P, QP, I64, P, P, P, P, P, P]),
         "dspark_q_validate": (ctypes.c_int, [ctypes.POINTER(QWire), I64, I64, P, P, P, P, P]),
         "dspark_workspace_bytes": (SZ, [I32, I64, I64, I32]),
         "dspark_q_semantic_id": (ctypes.c_char_p, []),
@@ -305,25 +306,54 @@ def margin(rows: torch.Tensor):
     return out
 
 
-def verify_stochastic(target: torch.Tensor, draft_tokens: torch.Tensor, target_draws: torch.Tensor,
-                      draft_status=None, out=None, store_q: bool = True):
-    """target [6R, V]; draft_tokens [R, 5]; target_draws uint32-valued [R, 6].
-    store_q=False keeps the target counts off memory (bf16 rows with
-    V <= 131072 only).  `out` may pass the outputs of an earlier call."""
+def u64_draws(a, dev) -> torch.Tensor:
+    """64-bit draws (numpy uint64 or int64 array, or a tensor) as an int64
+    device tensor holding the same bits."""
+    if isinstance(a, torch.Tensor):
+        return a.to(dev, torch.int64).contiguous()
+    import numpy as np
+    arr = np.ascontiguousarray(a)
+    if arr.dtype == np.uint64:
+        arr = arr.view(np.int64)
+    return torch.from_numpy(arr.astype(np.int64, copy=False)).to(dev)
+
+
+def verify_stochastic(target: torch.Tensor, draft_tokens: torch.Tensor, target_draws, draft_status=None,
+                      out=None):
+    """target [6R, V]; draft_tokens [R, 5]; target_draws: 64-bit draws [R, 6]
+    (see u64_draws).  `out` may pass the outputs of an earlier call."""
     lib = load_library()
     R, dev = draft_tokens.shape[0], target.device
-    V = target.shape[1]
     if out is None:
-        out = {"target_q": torch.empty((6 * R, V), dtype=torch.int32, device=dev) if store_q else None,
-               "target_sample": _i32(6 * R, dev), "target_status": _i32(6 * R, dev),
+        out = {"target_sample": _i32(6 * R, dev), "target_status": _i32(6 * R, dev),
                "accept_len": _i32(R, dev), "bonus": _i32(R, dev), "req_status": _i32(R, dev)}
     t = _rows(target)
     dt = draft_tokens.to(torch.int32).contiguous()
     ds = None if draft_status is None else draft_status.to(torch.int32).contiguous()
-    dr = target_draws.to(torch.int32).contiguous()
-    _check(lib.dspark_verify_stochastic(ctypes.byref(t), _p(dt), _p(ds), R, _p(dr), _p(out["target_q"]),
-                                        _p(out["target_sample"]), _p(out["target_status"]), _p(out["accept_len"]),
-                                        _p(out["bonus"]), _p(out["req_status"]), _stream()))
+    dr = u64_draws(target_draws, dev)
+    _check(lib.dspark_verify_stochastic(ctypes.byref(t), _p(dt), _p(ds), R, _p(dr), _p(out["target_sample"]),
+                                        _p(out["target_status"]), _p(out["accept_len"]), _p(out["bonus"]),
+                                        _p(out["req_status"]), _stream()))
+    return out
+
+
+def verify_ratio(target: torch.Tensor, draft_tokens: torch.Tensor, qd, accept_draws, final_draws,
+                 draft_status=None, out=None):
+    """Probability-ratio verification.  target [6R, V]; draft_tokens [R, 5];
+    qd: the draft rows' q (a dict as q_alloc / fused return it); accept_draws
+    64-bit [R, 5]; final_draws 64-bit [R].  Returns accept_len, token,
+    req_status (int32 [R])."""
+    lib = load_library()
+    R, dev = draft_tokens.shape[0], target.device
+    if out is None:
+        out = {"accept_len": _i32(R, dev), "token": _i32(R, dev), "req_status": _i32(R, dev)}
+    t = _rows(target)
+    dt = draft_tokens.to(torch.int32).contiguous()
+    ds = None if draft_status is None else draft_status.to(torch.int32).contiguous()
+    ad, fd = u64_draws(accept_draws, dev), u64_draws(final_draws, dev)
+    q = _qstruct(qd)
+    _check(lib.dspark_verify_ratio(ctypes.byref(t), _p(dt), _p(ds), ctypes.byref(q), R, _p(ad), _p(fd),
+                                   _p(out["accept_len"]), _p(out["token"]), _p(out["req_status"]), _stream()))
     return out
 
 

@@ -13,6 +13,7 @@
 
 #include "dspark.h"
 #include "dense_vd.hpp"
+#include "draw.hpp"
 #include "fast_q.hpp"
 #include "margin.hpp"
 #include "q_wire.hpp"
@@ -63,7 +64,7 @@ __global__ void __launch_bounds__(BS) rows_kernel(RowsArgs a) {
   const int r = is_draft ? b : b - a.n_draft;
   const char* base = static_cast<const char*>(is_draft ? a.draft : a.target);
   const Row<DT> row{base + (size_t)r * (size_t)(is_draft ? a.d_stride : a.t_stride) * ES, a.V};
-  const Stats st = row_stats(row, sh);
+  const Stats st = row_stats(row, sh.bs);
 
   if (!is_draft) {
     int am = 0;
@@ -424,6 +425,253 @@ __global__ void verify_kernel(int R, int V, const int32_t* dtok, const int32_t* 
   rst[r] = status;
 }
 
+// ---------------------------------------------------------------------------
+// Exact draws from the target distribution (stochastic and probability-ratio
+// verification).  SRC: 0 = bf16 row held in registers (V <= 131072),
+// 1 = streamed bf16 row, 2 = streamed float32 row.
+constexpr int kSrcRes = 0, kSrcBf16 = 1, kSrcF32 = 2;
+
+// Head of a target row for the draws: status, row maximum and the weight
+// context (value table built when it applies).  All threads; ends with a
+// barrier.  The resident source loads the row into R.
+template <int SRC>
+__device__ __forceinline__ int draw_head(Res& R, const void* p, int V, DrawCtx& c, DrawShared& sh) {
+  int status;
+  uint32_t m_raw = 0;
+  if constexpr (SRC == kSrcRes) {
+    wres_load(R, static_cast<const uint16_t*>(p), V);
+    const RStats st = res_stats(R, sh);
+    status = st.status;
+    m_raw = st.m_raw;
+    c.m = bf16_to_f32(m_raw);
+  } else {
+    constexpr int DT = SRC == kSrcF32 ? DSPARK_F32 : DSPARK_BF16;
+    const Stats st = row_stats(Row<DT>{p, V}, sh.bs);
+    status = st.status;
+    c.m = st.m;
+    m_raw = __float_as_uint(st.m) >> 16;
+  }
+  c.V = V;
+  c.dense = nullptr;
+  c.sp_len = 0;
+  c.A = u256_zero();
+  c.s64 = 0.0;
+  c.table = false;
+  if (status == DSPARK_ST_OK && SRC != kSrcF32) {
+    c.f = fmap_make(m_raw);
+    c.table = c.f.NB <= kNBF;
+  }
+  if (c.table) draw_table(c, sh);  // (uniform: every thread sees the same status and maximum)
+  return status;
+}
+
+template <int SRC, int mode>
+__device__ __forceinline__ int draw_run(Res& R, const void* p, int V, const DrawCtx& c, bool u_valid, uint64_t u,
+                                        DrawShared& sh) {
+  if constexpr (SRC == kSrcRes) {
+    return wres_draw<mode>(R, p, V, c, u_valid, u, sh);
+  } else {
+    constexpr int DT = SRC == kSrcF32 ? DSPARK_F32 : DSPARK_BF16;
+    StreamSrc<DT> s;
+    s.row = Row<DT>{p, V};
+    const int nvec = (V + StreamSrc<DT>::E - 1) / StreamSrc<DT>::E;
+    s.cpw = (nvec + 64 * NW - 1) / (64 * NW);
+    return stream_draw<mode, DT>(s, c, u_valid, u, sh);
+  }
+}
+
+// weight bits of the element at id x (thread-level; same value as the passes)
+template <int SRC>
+__device__ __forceinline__ uint32_t draw_weight_at(const void* p, int x, const DrawCtx& c, const DrawShared& sh) {
+  if constexpr (SRC == kSrcF32) {
+    return __float_as_uint(cr_expf(static_cast<const float*>(p)[x] - c.m));
+  } else {
+    return bf16_weight_bits((uint32_t)static_cast<const uint16_t*>(p)[x], c, sh);
+  }
+}
+
+struct DrawArgs {
+  const void* rows;
+  int64_t stride;  // elements
+  int V;
+  const uint64_t* draws;  // one per row
+  int32_t* token;
+  int32_t* status;
+};
+
+// Stochastic verification's target draws ("DeepSeek-V4.1 DSpark", "State
+// and sampling contracts"): one workgroup per target row, an exact draw from
+// the row's p with its own 64-bit draw.
+template <int SRC>
+__global__ void __launch_bounds__(BS) target_draw_kernel(DrawArgs a) {
+  __shared__ DrawShared sh;
+  const int r = blockIdx.x;
+  const int es = SRC == kSrcF32 ? 4 : 2;
+  const void* p = static_cast<const char*>(a.rows) + (size_t)r * (size_t)a.stride * es;
+  Res R;
+  DrawCtx c;
+  const int status = draw_head<SRC>(R, p, a.V, c, sh);
+  int tok = 0;
+  if (status == DSPARK_ST_OK) tok = draw_run<SRC, kDrawPlain>(R, p, a.V, c, true, a.draws[r], sh);
+  if (threadIdx.x == 0) {
+    a.status[r] = status;
+    a.token[r] = status == DSPARK_ST_OK ? tok : 0;
+  }
+}
+
+struct RatioArgs {
+  const void* target;
+  int64_t t_stride;  // elements
+  int V;
+  const int32_t* dtok;
+  const int32_t* dst;
+  const int32_t* topk;
+  int k_max;
+  const uint32_t* dense;
+  const int32_t* sp_ids;
+  const uint32_t* sp_cnt;
+  const int32_t* sp_len;
+  const uint64_t* acc_draws;  // [R][5]
+  const uint64_t* fin_draws;  // [R]
+  int32_t* accept_len;
+  int32_t* token;
+  int32_t* req_status;
+  int pos;
+};
+
+// q's count of token x in draft row j (0 for a bad support or a token
+// outside it); thread-level
+__device__ __forceinline__ uint32_t ratio_q_count(const RatioArgs& a, int j, int x) {
+  const int k = a.topk ? a.topk[j] : 0;
+  const int kcap = a.k_max < a.V ? a.k_max : a.V;
+  if (k < 0 || k > kcap) return 0u;
+  if (k == 0) return a.dense ? a.dense[(size_t)j * a.V + x] : 0u;
+  if (!a.sp_ids || !a.sp_cnt || !a.sp_len) return 0u;
+  const int len = a.sp_len[j];
+  if (len <= 0 || len > k) return 0u;
+  const int32_t* ids = a.sp_ids + (size_t)j * a.k_max;
+  int lo = 0, hi = len;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (ids[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo < len && ids[lo] == x ? a.sp_cnt[(size_t)j * a.k_max + lo] : 0u;
+}
+
+// U = u / 2^64 < p(x) / q(x): u c_x A < A_x 2^88, in integers
+__device__ __forceinline__ bool ratio_accepts(uint64_t u, uint32_t cx, const U256& ax, const U256& A) {
+  uint64_t p[5];
+  u256_mul64_full(A, u, p);
+  uint64_t q[6], carry = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint64_t lo = p[i] * cx, hi = __umul64hi(p[i], (uint64_t)cx);
+    const uint64_t s = lo + carry;
+    q[i] = s;
+    carry = hi + (s < lo ? 1ull : 0ull);
+  }
+  q[5] = carry;
+  if (q[4] | q[5]) return false;  // ax 2^88 < 2^238
+  const U256 rhs = u256_shl(U256{{0ull, ax.w[0], ax.w[1], ax.w[2]}}, 24);
+  return u256_lt(U256{{q[0], q[1], q[2], q[3]}}, rhs);
+}
+
+// Probability-ratio verification, position a.pos of every request ("PP1 q
+// transport and scheduling design", "Distribution contract and precision":
+// ratio tests and full-vocabulary residual sampling with p at T = 1 and the
+// dyadic q).  One workgroup per request; a request still open at this
+// position reads its target row pos: a failed draft row (or pos 5) ends it
+// with a draw from p; otherwise the proposal is accepted when
+// U < p(x) / q(x), else the residual max(p - q, 0) is drawn and the request
+// ends.  State between the six launches: req_status OK with token -1 and
+// accept_len == pos marks a request still open.
+template <int SRC>
+__global__ void __launch_bounds__(BS) ratio_step_kernel(RatioArgs a) {
+  __shared__ DrawShared sh;
+  const int r = blockIdx.x;
+  if (a.pos == 0) {
+    // every valid draft row carries a token in [0, V) with q(token) > 0
+    if (threadIdx.x == 0) {
+      int st = DSPARK_ST_OK;
+      for (int i = 0; i < DSPARK_N_DRAFT; ++i) {
+        const int j = r * DSPARK_N_DRAFT + i;
+        if (a.dst && a.dst[j] != DSPARK_ST_OK) continue;
+        const int x = a.dtok[j];
+        if (x < 0 || x >= a.V || ratio_q_count(a, j, x) == 0u) st = DSPARK_ST_DRAFT_INVALID;
+      }
+      sh.bi[0] = st;
+    }
+    __syncthreads();
+    if (sh.bi[0] != DSPARK_ST_OK) {
+      if (threadIdx.x == 0) {
+        a.req_status[r] = sh.bi[0];
+        a.accept_len[r] = 0;
+        a.token[r] = 0;
+      }
+      return;
+    }
+  } else if (!(a.req_status[r] == DSPARK_ST_OK && a.token[r] < 0 && a.accept_len[r] == a.pos)) {
+    return;  // (the same values for every thread)
+  }
+  const int es = SRC == kSrcF32 ? 4 : 2;
+  const int trow = r * DSPARK_N_TARGET + a.pos;
+  const void* p = static_cast<const char*>(a.target) + (size_t)trow * (size_t)a.t_stride * es;
+  Res R;
+  DrawCtx c;
+  const int status = draw_head<SRC>(R, p, a.V, c, sh);
+  if (status != DSPARK_ST_OK) {
+    if (threadIdx.x == 0) {
+      a.req_status[r] = DSPARK_ST_TARGET_INVALID;
+      a.accept_len[r] = 0;
+      a.token[r] = 0;
+    }
+    return;
+  }
+  const int j = r * DSPARK_N_DRAFT + a.pos;
+  const bool final_p = a.pos == DSPARK_N_DRAFT || (a.dst && a.dst[j] != DSPARK_ST_OK);
+  const uint64_t uf = a.fin_draws[r];
+  int st = DSPARK_ST_OK;
+  int acc_len = a.pos;
+  // one plain pass: the draw from p at the end of the request, or the total A
+  // (sh.total) for the ratio test
+  int tok = draw_run<SRC, kDrawPlain>(R, p, a.V, c, final_p, uf, sh);
+  if (!final_p) {
+    if (threadIdx.x == 0) {
+      const int x = a.dtok[j];
+      const uint32_t cx = ratio_q_count(a, j, x);
+      const U256 ax = u256_of_weight(draw_weight_at<SRC>(p, x, c, sh));
+      sh.bi[1] = ratio_accepts(a.acc_draws[(size_t)r * DSPARK_N_DRAFT + a.pos], cx, ax, sh.total) ? 1 : 0;
+    }
+    __syncthreads();
+    if (sh.bi[1]) {
+      if (threadIdx.x == 0) {
+        a.req_status[r] = DSPARK_ST_OK;
+        a.accept_len[r] = a.pos + 1;
+        a.token[r] = -1;
+      }
+      return;
+    }
+    c.A = sh.total;
+    c.s64 = u256_approx_scaled(c.A);
+    const int k = a.topk ? a.topk[j] : 0;
+    if (k == 0) {
+      c.dense = a.dense + (size_t)j * a.V;
+    } else {
+      c.sp_len = a.sp_len[j];
+      draw_sparse_q(a.sp_ids + (size_t)j * a.k_max, a.sp_cnt + (size_t)j * a.k_max, c.sp_len, sh);
+    }
+    tok = draw_run<SRC, kDrawResidual>(R, p, a.V, c, true, uf, sh);
+    if (tok < 0) st = DSPARK_ST_ALLOC_INCONSISTENT;  // zero residual: q's counts do not sum to 2^24
+  }
+  if (threadIdx.x == 0) {
+    const bool ok = st == DSPARK_ST_OK;
+    a.req_status[r] = st;
+    a.accept_len[r] = ok ? acc_len : 0;
+    a.token[r] = ok ? tok : 0;
+  }
+}
+
 // Standalone sampling from stored q rows.
 __global__ void __launch_bounds__(BS) sample_kernel(const int32_t* topk, int k_max, const uint32_t* dense,
                                                     const int32_t* sp_ids, const uint32_t* sp_cnt,
@@ -743,32 +991,90 @@ int dspark_verify_greedy(const dspark_rows* target, const int32_t* draft_tokens,
                        accept_len, bonus, req_status, stream);
 }
 
-int dspark_verify_stochastic(const dspark_rows* target, const int32_t* draft_tokens,
-                             const int32_t* draft_status, int64_t n_requests, const uint32_t* target_draws,
-                             uint32_t* target_q, int32_t* target_sample, int32_t* target_status,
-                             int32_t* accept_len, int32_t* bonus, int32_t* req_status, void* stream) {
+}  // extern "C"
+
+namespace {
+int draw_source(const dspark_rows* r) {
+  if (r->dtype == DSPARK_F32) return kSrcF32;
+  return r->vocab <= NI * BS * 8 ? kSrcRes : kSrcBf16;
+}
+
+int check_draw_rows(const dspark_rows* target, int64_t n_requests) {
   int rc = check_rows(target, "target rows NULL");
   if (rc) return rc;
   if (n_requests < 0 || target->n_rows != n_requests * DSPARK_N_TARGET)
     return fail(DSPARK_EINVAL, "target must hold 6 rows per request");
+  if (n_requests > (1 << 22)) return fail(DSPARK_EINVAL, "too many requests");
+  return DSPARK_SUCCESS;
+}
+}  // namespace
+
+extern "C" {
+
+int dspark_verify_stochastic(const dspark_rows* target, const int32_t* draft_tokens,
+                             const int32_t* draft_status, int64_t n_requests, const uint64_t* target_draws,
+                             int32_t* target_sample, int32_t* target_status, int32_t* accept_len, int32_t* bonus,
+                             int32_t* req_status, void* stream) {
+  int rc = check_draw_rows(target, n_requests);
+  if (rc) return rc;
   if (n_requests == 0) return DSPARK_SUCCESS;
   if (!draft_tokens || !target_draws || !target_sample || !target_status || !accept_len || !bonus || !req_status)
     return fail(DSPARK_EINVAL, "NULL argument");
-  // without target_q the counts are not stored; only register-resident bf16
-  // rows work without that row (the streaming path uses it as scratch)
-  if (!target_q && !(target->dtype == DSPARK_BF16 && target->vocab <= NI * BS * 8))
-    return fail(DSPARK_EINVAL, "target_q is required for float32 rows and for vocab > 131072");
-  // the target rows take the draft rows' path: dense q, then the in-kernel draw
-  RowsArgs a = rows_args_draft(target);
-  a.row_status = target_status;
-  a.do_q = 1;
-  a.dense = target_q;
-  a.no_counts = target_q == nullptr;
-  a.draws = target_draws;
-  a.sample = target_sample;
-  if ((rc = launch_rows(a, target->dtype, stream))) return rc;
+  DrawArgs d{target->data, target->row_stride, (int)target->vocab, target_draws, target_sample, target_status};
+  const dim3 grid((unsigned)target->n_rows);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (draw_source(target)) {
+    case kSrcRes: hipLaunchKernelGGL(target_draw_kernel<kSrcRes>, grid, dim3(BS), 0, s, d); break;
+    case kSrcBf16: hipLaunchKernelGGL(target_draw_kernel<kSrcBf16>, grid, dim3(BS), 0, s, d); break;
+    default: hipLaunchKernelGGL(target_draw_kernel<kSrcF32>, grid, dim3(BS), 0, s, d); break;
+  }
+  if ((rc = check_launch())) return rc;
   return launch_verify(n_requests, (int)target->vocab, draft_tokens, draft_status, target_sample, target_status,
                        accept_len, bonus, req_status, stream);
+}
+
+int dspark_verify_ratio(const dspark_rows* target, const int32_t* draft_tokens, const int32_t* draft_status,
+                        const dspark_q* draft_q, int64_t n_requests, const uint64_t* accept_draws,
+                        const uint64_t* final_draws, int32_t* accept_len, int32_t* token, int32_t* req_status,
+                        void* stream) {
+  int rc = check_draw_rows(target, n_requests);
+  if (rc) return rc;
+  if (!draft_q) return fail(DSPARK_EINVAL, "draft_q NULL");
+  if ((rc = check_q(draft_q, n_requests * DSPARK_N_DRAFT))) return rc;
+  if (n_requests == 0) return DSPARK_SUCCESS;
+  if (!draft_tokens || !accept_draws || !final_draws || !accept_len || !token || !req_status)
+    return fail(DSPARK_EINVAL, "NULL argument");
+  RatioArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.target = target->data;
+  a.t_stride = target->row_stride;
+  a.V = (int)target->vocab;
+  a.dtok = draft_tokens;
+  a.dst = draft_status;
+  a.topk = draft_q->topk;
+  a.k_max = draft_q->k_max;
+  a.dense = draft_q->dense;
+  a.sp_ids = draft_q->sp_ids;
+  a.sp_cnt = draft_q->sp_cnt;
+  a.sp_len = draft_q->sp_len;
+  a.acc_draws = accept_draws;
+  a.fin_draws = final_draws;
+  a.accept_len = accept_len;
+  a.token = token;
+  a.req_status = req_status;
+  const dim3 grid((unsigned)n_requests);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int src = draw_source(target);
+  for (int pos = 0; pos <= DSPARK_N_DRAFT; ++pos) {
+    a.pos = pos;
+    switch (src) {
+      case kSrcRes: hipLaunchKernelGGL(ratio_step_kernel<kSrcRes>, grid, dim3(BS), 0, s, a); break;
+      case kSrcBf16: hipLaunchKernelGGL(ratio_step_kernel<kSrcBf16>, grid, dim3(BS), 0, s, a); break;
+      default: hipLaunchKernelGGL(ratio_step_kernel<kSrcF32>, grid, dim3(BS), 0, s, a); break;
+    }
+    if ((rc = check_launch())) return rc;
+  }
+  return DSPARK_SUCCESS;
 }
 
 int dspark_fused(const dspark_rows* draft, const dspark_rows* target, int32_t mode,

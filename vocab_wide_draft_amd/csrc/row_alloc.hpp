@@ -20,7 +20,7 @@ struct Stats {
 // Validity per "Distribution contract and precision": NaN first, then +inf,
 // then a row with no finite entry (all -inf) has zero mass.
 template <int DT>
-__device__ Stats row_stats(const Row<DT>& row, RowShared& sh) {
+__device__ Stats row_stats(const Row<DT>& row, BlockScratch& bs) {
   constexpr int EPV = Row<DT>::EPV;
   const int nvec = row.nvec();
   float mx = -__builtin_inff();
@@ -40,8 +40,8 @@ __device__ Stats row_stats(const Row<DT>& row, RowShared& sh) {
   }
   Stats s;
   s.tkey = (flags & 4u) ? key32(mx) : 0u;
-  const float m = block_max<float>(mx, sh.bs);
-  const uint32_t f = block_max<uint32_t>(flags & 1u, sh.bs) | block_max<uint32_t>(flags & 2u, sh.bs);
+  const float m = block_max<float>(mx, bs);
+  const uint32_t f = block_max<uint32_t>(flags & 1u, bs) | block_max<uint32_t>(flags & 2u, bs);
   s.m = m;
   s.status = (f & 1u) ? DSPARK_ST_ROW_NAN
              : (f & 2u) ? DSPARK_ST_ROW_POSINF
