@@ -345,18 +345,63 @@ struct StreamSrc {
   static constexpr int E = Row<DT>::EPV;
   __device__ int vec(int ch) const { return (wave_id() * cpw + ch) * 64 + lane_id(); }
 };
+// One chunk of a lane: its E logits and, for residual sums over a dense q,
+// their E counts, all loaded before any is used (counts past V read 0).
+template <int DT>
+struct ChunkData {
+  float x[StreamSrc<DT>::E];
+  uint32_t cnt[StreamSrc<DT>::E];
+};
 template <int mode, int DT>
-__device__ __forceinline__ void stream_chunk(const StreamSrc<DT>& s, int ch, const DrawCtx& c,
-                                             const DrawShared& sh, Acc& s1, uint64_t& s2) {
+__device__ __forceinline__ void stream_load(const StreamSrc<DT>& s, int ch, const DrawCtx& c,
+                                            __amdgpu_buffer_rsrc_t crs, ChunkData<DT>& d) {
   constexpr int E = StreamSrc<DT>::E;
   const int q = s.vec(ch);
-  float x[E];
-  s.row.load(q, x);
+  s.row.load(q, d.x);
+  if (mode != kDrawPlain && c.dense) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) d.cnt[e] = __builtin_amdgcn_raw_buffer_load_b32(crs, (q * E + e) * 4, 0, 0);
+  }
+}
+// buffer over a dense q row (reads past V give 0)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t count_rsrc(const DrawCtx& c) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(c.dense), (short)0, c.dense ? c.V * 4 : 0,
+                                           0x00020000);
+}
+template <int DT>
+__device__ __forceinline__ uint32_t chunk_weight_bits(float x, const DrawCtx& c, const DrawShared& sh) {
+  return DT == DSPARK_BF16 ? bf16_weight_bits(__float_as_uint(x) >> 16, c, sh) : __float_as_uint(cr_expf(x - c.m));
+}
+template <int mode, int DT>
+__device__ __forceinline__ void stream_add(const ChunkData<DT>& d, int q, const DrawCtx& c, const DrawShared& sh,
+                                           Acc& s1, uint64_t& s2) {
+  constexpr int E = StreamSrc<DT>::E;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const uint32_t wb = DT == DSPARK_BF16 ? bf16_weight_bits(__float_as_uint(x[e]) >> 16, c, sh)
-                                          : __float_as_uint(cr_expf(x[e] - c.m));
-    draw_add<mode>(wb, q * E + e, c, sh, s1, s2);
+    const uint32_t wb = chunk_weight_bits<DT>(d.x[e], c, sh);
+    if (mode == kDrawPlain) {
+      acc_add(s1, wb);
+    } else if ((wb & 0x7fffffffu) != 0u) {
+      const uint32_t cnt = c.dense ? d.cnt[e] : draw_count(c, sh, q * E + e);
+      if (resid_positive(wb, cnt, c)) {
+        acc_add(s1, wb);
+        s2 += cnt;
+      }
+    }
+  }
+}
+// this lane's sums over every chunk of its wave, the next chunk's loads in
+// flight while one is added
+template <int mode, int DT>
+__device__ __forceinline__ void stream_sums(const StreamSrc<DT>& s, const DrawCtx& c, const DrawShared& sh, Acc& s1,
+                                            uint64_t& s2) {
+  const __amdgpu_buffer_rsrc_t crs = count_rsrc(c);
+  ChunkData<DT> cur, nxt;
+  stream_load<mode, DT>(s, 0, c, crs, cur);
+  for (int ch = 0; ch < s.cpw; ++ch) {
+    if (ch + 1 < s.cpw) stream_load<mode, DT>(s, ch + 1, c, crs, nxt);
+    stream_add<mode, DT>(cur, s.vec(ch), c, sh, s1, s2);
+    cur = nxt;
   }
 }
 
@@ -424,25 +469,29 @@ __device__ __forceinline__ int draw_find_lane(const Acc& s1, uint64_t s2, const 
 }
 
 // The draw itself, from the totals of draw_totals: the crossing wave walks
-// its chunks in order (reloading them from memory: a resident row's chunk i
-// of wave w is the streamed chunk i with cpw = 16) to the crossing chunk,
-// scans its lanes, and the crossing lane walks its elements.  Returns the
-// token (-1 for a zero total).
+// its chunks in order (reloading them from memory, the next chunk's loads in
+// flight) to the crossing chunk, scans its lanes, and the crossing lane
+// walks its elements.  Returns the token (-1 for a zero total).
 template <int mode, int DT>
 __device__ __forceinline__ int stream_walk(const StreamSrc<DT>& s, const DrawCtx& c, uint64_t u, DrawShared& sh) {
   draw_find_wave(u, sh);
   if (sh.wstar < 0) return -1;
   if (wave_id() == sh.wstar) {
+    constexpr int E = StreamSrc<DT>::E;
+    const __amdgpu_buffer_rsrc_t crs = count_rsrc(c);
     U256 t = sh.rest;
     int ich = -1;
     Acc cs1;
     uint64_t cs2 = 0;
     acc_zero(cs1);
+    ChunkData<DT> cur, nxt, hit;
+    stream_load<mode, DT>(s, 0, c, crs, cur);
     for (int ch = 0; ch < s.cpw && ich < 0; ++ch) {
+      if (ch + 1 < s.cpw) stream_load<mode, DT>(s, ch + 1, c, crs, nxt);
       Acc a;
       acc_zero(a);
       uint64_t b = 0;
-      stream_chunk<mode, DT>(s, ch, c, sh, a, b);
+      stream_add<mode, DT>(cur, s.vec(ch), c, sh, a, b);
       Acc ta;
       uint64_t tb;
       wave_total(a, b, &ta, &tb);
@@ -451,26 +500,84 @@ __device__ __forceinline__ int stream_walk(const StreamSrc<DT>& s, const DrawCtx
         ich = ch;
         cs1 = a;
         cs2 = b;
+        hit = cur;
       } else {
         t = u256_sub(t, wc);
       }
+      cur = nxt;
     }
     U256 lr;
     const int l = draw_find_lane<mode>(cs1, cs2, c, t, &lr);
     if (lane_id() == l && ich >= 0) {
-      constexpr int E = StreamSrc<DT>::E;
       const int q = s.vec(ich);
-      float x[E];
-      s.row.load(q, x);
       int tok = -1;
       U256 run = u256_zero();
-      for (int e = 0; e < E && tok < 0; ++e) {
-        const uint32_t wb = DT == DSPARK_BF16 ? bf16_weight_bits(__float_as_uint(x[e]) >> 16, c, sh)
-                                              : __float_as_uint(cr_expf(x[e] - c.m));
-        // ids past V carry weight 0 and have no count
-        const uint32_t cnt = mode == kDrawPlain || (wb & 0x7fffffffu) == 0u ? 0u : draw_count(c, sh, q * E + e);
-        run = u256_add(run, elem_weight<mode>(wb, cnt, c));
-        if (u256_lt(lr, run)) tok = q * E + e;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (tok < 0) {
+          const uint32_t wb = chunk_weight_bits<DT>(hit.x[e], c, sh);
+          // ids past V carry weight 0 and have no count
+          uint32_t cnt = 0u;
+          if (mode != kDrawPlain && (wb & 0x7fffffffu) != 0u)
+            cnt = c.dense ? hit.cnt[e] : draw_count(c, sh, q * E + e);
+          run = u256_add(run, elem_weight<mode>(wb, cnt, c));
+          if (u256_lt(lr, run)) tok = q * E + e;
+        }
+      }
+      sh.token = tok;
+    }
+  }
+  __syncthreads();
+  return sh.token;
+}
+
+// wave-uniform copy of a value every lane holds (scalar registers)
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v) |
+         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)) << 32);
+}
+__device__ __forceinline__ U256 uniform_u256(const U256& v) {
+  return U256{{uniform_u64(v.w[0]), uniform_u64(v.w[1]), uniform_u64(v.w[2]), uniform_u64(v.w[3])}};
+}
+
+// The same draw for a resident bf16 row whose weights come from the value
+// table: the crossing wave's chunks are taken from its registers (a select
+// chain picks each one); the running threshold stays in scalar registers.
+__device__ __forceinline__ int wres_walk(Res& R, const DrawCtx& c, uint64_t u, DrawShared& sh) {
+  draw_find_wave(u, sh);
+  if (sh.wstar < 0) return -1;
+  if (wave_id() == sh.wstar) {
+    U256 t = uniform_u256(sh.rest);
+    int ich = -1;
+    touch(R);
+    for (int i = 0; i < NI && ich < 0; ++i) {
+      Acc a;
+      acc_zero(a);
+      wres_chunk(select_vec(R, i), c, sh, a);
+      Acc ta;
+      uint64_t tb;
+      wave_total(a, 0ull, &ta, &tb);
+      const U256 wc = u256_of_acc(ta);
+      if (u256_lt(t, wc)) ich = i;
+      else t = u256_sub(t, wc);
+    }
+    ich = ich < 0 ? 0 : ich;
+    const u32x4 v = select_vec(R, ich);
+    Acc a;
+    acc_zero(a);
+    wres_chunk(v, c, sh, a);
+    U256 lr;
+    const int l = draw_find_lane<kDrawPlain>(a, 0ull, c, t, &lr);
+    if (lane_id() == l) {
+      const int base = wres_base(ich);
+      int tok = -1;
+      U256 run = u256_zero();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (tok < 0) {
+          run = u256_add(run, u256_of_weight(bf16_weight_table(elem(v, e), c, sh)));
+          if (u256_lt(lr, run)) tok = base + e;
+        }
       }
       sh.token = tok;
     }
@@ -488,7 +595,7 @@ __device__ __forceinline__ int stream_draw(const StreamSrc<DT>& s, const DrawCtx
   Acc s1;
   acc_zero(s1);
   uint64_t s2 = 0;
-  for (int ch = 0; ch < s.cpw; ++ch) stream_chunk<mode, DT>(s, ch, c, sh, s1, s2);
+  stream_sums<mode, DT>(s, c, sh, s1, s2);
   draw_totals<mode>(s1, s2, c, sh);
   if (!u_valid) return -1;
   return stream_walk<mode, DT>(s, c, u, sh);
@@ -498,29 +605,17 @@ __device__ __forceinline__ int stream_draw(const StreamSrc<DT>& s, const DrawCtx
 // the registers when the value table applies; otherwise, for residual sums
 // (one row per request, whose per-element count lookups would not fit beside
 // the row's registers) and for the walk, the row is reloaded.
-template <int mode>
-__device__ __forceinline__ int wres_draw(Res& R, const void* p, int V, const DrawCtx& c, bool u_valid, uint64_t u,
-                                         DrawShared& sh) {
-  StreamSrc<DSPARK_BF16> s;
-  s.row = Row<DSPARK_BF16>{p, V};
-  s.cpw = NI;
+// Resident bf16 row (loaded by wres_load) whose weights come from the value
+// table (c.table): plain sums and the draw from its registers.
+__device__ __forceinline__ int wres_draw(Res& R, const DrawCtx& c, bool u_valid, uint64_t u, DrawShared& sh) {
   Acc s1;
   acc_zero(s1);
-  uint64_t s2 = 0;
-  bool slow = mode != kDrawPlain || !c.table;
-  if (mode == kDrawPlain && c.table) {
-    touch(R);
+  touch(R);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) wres_chunk(fetch(R, i), c, sh, s1);
-  }
-  if (slow) {
-    acc_zero(s1);
-    s2 = 0;
-    for (int ch = 0; ch < s.cpw; ++ch) stream_chunk<mode, DSPARK_BF16>(s, ch, c, sh, s1, s2);
-  }
-  draw_totals<mode>(s1, s2, c, sh);
+  for (int i = 0; i < NI; ++i) wres_chunk(fetch(R, i), c, sh, s1);
+  draw_totals<kDrawPlain>(s1, 0ull, c, sh);
   if (!u_valid) return -1;
-  return stream_walk<mode, DSPARK_BF16>(s, c, u, sh);
+  return wres_walk(R, c, u, sh);
 }
 
 }  // namespace dspark

@@ -427,13 +427,15 @@ __global__ void verify_kernel(int R, int V, const int32_t* dtok, const int32_t* 
 
 // ---------------------------------------------------------------------------
 // Exact draws from the target distribution (stochastic and probability-ratio
-// verification).  SRC: 0 = bf16 row held in registers (V <= 131072),
-// 1 = streamed bf16 row, 2 = streamed float32 row.
+// verification).  SRC: 0 = bf16 row held in registers (V <= 131072; rows
+// whose maximum admits the value table), 1 = streamed bf16 row, 2 = streamed
+// float32 row.
 constexpr int kSrcRes = 0, kSrcBf16 = 1, kSrcF32 = 2;
+constexpr int kTokDeferred = -2;  // a resident row without a value table: streamed by a second launch
 
-// Head of a target row for the draws: status, row maximum and the weight
-// context (value table built when it applies).  All threads; ends with a
-// barrier.  The resident source loads the row into R.
+// Head of a row for the draws: status, row maximum and the weight context
+// (value table built when it applies).  All threads; ends with a barrier.
+// The resident source loads the row into R.
 template <int SRC>
 __device__ __forceinline__ int draw_head(Res& R, const void* p, int V, DrawCtx& c, DrawShared& sh) {
   int status;
@@ -465,19 +467,16 @@ __device__ __forceinline__ int draw_head(Res& R, const void* p, int V, DrawCtx& 
   return status;
 }
 
+// A streamed row's sums in the mode's weights and (with u_valid) the draw.
 template <int SRC, int mode>
-__device__ __forceinline__ int draw_run(Res& R, const void* p, int V, const DrawCtx& c, bool u_valid, uint64_t u,
-                                        DrawShared& sh) {
-  if constexpr (SRC == kSrcRes) {
-    return wres_draw<mode>(R, p, V, c, u_valid, u, sh);
-  } else {
-    constexpr int DT = SRC == kSrcF32 ? DSPARK_F32 : DSPARK_BF16;
-    StreamSrc<DT> s;
-    s.row = Row<DT>{p, V};
-    const int nvec = (V + StreamSrc<DT>::E - 1) / StreamSrc<DT>::E;
-    s.cpw = (nvec + 64 * NW - 1) / (64 * NW);
-    return stream_draw<mode, DT>(s, c, u_valid, u, sh);
-  }
+__device__ __forceinline__ int draw_streamed(const void* p, int V, const DrawCtx& c, bool u_valid, uint64_t u,
+                                             DrawShared& sh) {
+  constexpr int DT = SRC == kSrcF32 ? DSPARK_F32 : DSPARK_BF16;
+  StreamSrc<DT> s;
+  s.row = Row<DT>{p, V};
+  const int nvec = (V + StreamSrc<DT>::E - 1) / StreamSrc<DT>::E;
+  s.cpw = (nvec + 64 * NW - 1) / (64 * NW);
+  return stream_draw<mode, DT>(s, c, u_valid, u, sh);
 }
 
 // weight bits of the element at id x (thread-level; same value as the passes)
@@ -497,22 +496,31 @@ struct DrawArgs {
   const uint64_t* draws;  // one per row
   int32_t* token;
   int32_t* status;
+  int deferred_only;  // streamed launch after a resident one: only rows it deferred
 };
 
 // Stochastic verification's target draws ("DeepSeek-V4.1 DSpark", "State
 // and sampling contracts"): one workgroup per target row, an exact draw from
-// the row's p with its own 64-bit draw.
+// the row's p with its own 64-bit draw.  The resident launch defers rows
+// without a value table (token kTokDeferred) to a streamed launch.
 template <int SRC>
 __global__ void __launch_bounds__(BS) target_draw_kernel(DrawArgs a) {
   __shared__ DrawShared sh;
   const int r = blockIdx.x;
+  if (a.deferred_only && a.token[r] != kTokDeferred) return;  // (the same value for every thread)
   const int es = SRC == kSrcF32 ? 4 : 2;
   const void* p = static_cast<const char*>(a.rows) + (size_t)r * (size_t)a.stride * es;
   Res R;
   DrawCtx c;
   const int status = draw_head<SRC>(R, p, a.V, c, sh);
   int tok = 0;
-  if (status == DSPARK_ST_OK) tok = draw_run<SRC, kDrawPlain>(R, p, a.V, c, true, a.draws[r], sh);
+  if (status == DSPARK_ST_OK) {
+    if constexpr (SRC == kSrcRes) {
+      tok = c.table ? wres_draw(R, c, true, a.draws[r], sh) : kTokDeferred;
+    } else {
+      tok = draw_streamed<SRC, kDrawPlain>(p, a.V, c, true, a.draws[r], sh);
+    }
+  }
   if (threadIdx.x == 0) {
     a.status[r] = status;
     a.token[r] = status == DSPARK_ST_OK ? tok : 0;
@@ -635,7 +643,7 @@ __global__ void __launch_bounds__(BS) ratio_step_kernel(RatioArgs a) {
   int acc_len = a.pos;
   // one plain pass: the draw from p at the end of the request, or the total A
   // (sh.total) for the ratio test
-  int tok = draw_run<SRC, kDrawPlain>(R, p, a.V, c, final_p, uf, sh);
+  int tok = draw_streamed<SRC, kDrawPlain>(p, a.V, c, final_p, uf, sh);
   if (!final_p) {
     if (threadIdx.x == 0) {
       const int x = a.dtok[j];
@@ -661,7 +669,7 @@ __global__ void __launch_bounds__(BS) ratio_step_kernel(RatioArgs a) {
       c.sp_len = a.sp_len[j];
       draw_sparse_q(a.sp_ids + (size_t)j * a.k_max, a.sp_cnt + (size_t)j * a.k_max, c.sp_len, sh);
     }
-    tok = draw_run<SRC, kDrawResidual>(R, p, a.V, c, true, uf, sh);
+    tok = draw_streamed<SRC, kDrawResidual>(p, a.V, c, true, uf, sh);
     if (tok < 0) st = DSPARK_ST_ALLOC_INCONSISTENT;  // zero residual: q's counts do not sum to 2^24
   }
   if (threadIdx.x == 0) {
@@ -1020,11 +1028,18 @@ int dspark_verify_stochastic(const dspark_rows* target, const int32_t* draft_tok
   if (n_requests == 0) return DSPARK_SUCCESS;
   if (!draft_tokens || !target_draws || !target_sample || !target_status || !accept_len || !bonus || !req_status)
     return fail(DSPARK_EINVAL, "NULL argument");
-  DrawArgs d{target->data, target->row_stride, (int)target->vocab, target_draws, target_sample, target_status};
+  DrawArgs d{target->data, target->row_stride, (int)target->vocab, target_draws, target_sample, target_status, 0};
   const dim3 grid((unsigned)target->n_rows);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (draw_source(target)) {
-    case kSrcRes: hipLaunchKernelGGL(target_draw_kernel<kSrcRes>, grid, dim3(BS), 0, s, d); break;
+    case kSrcRes:
+      // register-resident rows first; rows without a value table (maxima
+      // near zero) are deferred to the streamed kernel
+      hipLaunchKernelGGL(target_draw_kernel<kSrcRes>, grid, dim3(BS), 0, s, d);
+      if ((rc = check_launch())) return rc;
+      d.deferred_only = 1;
+      hipLaunchKernelGGL(target_draw_kernel<kSrcBf16>, grid, dim3(BS), 0, s, d);
+      break;
     case kSrcBf16: hipLaunchKernelGGL(target_draw_kernel<kSrcBf16>, grid, dim3(BS), 0, s, d); break;
     default: hipLaunchKernelGGL(target_draw_kernel<kSrcF32>, grid, dim3(BS), 0, s, d); break;
   }
@@ -1064,14 +1079,13 @@ int dspark_verify_ratio(const dspark_rows* target, const int32_t* draft_tokens, 
   a.req_status = req_status;
   const dim3 grid((unsigned)n_requests);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int src = draw_source(target);
+  // the rows are streamed: a request reads at most one row whose residual
+  // is drawn, and its q row beside it
+  const bool f32 = target->dtype == DSPARK_F32;
   for (int pos = 0; pos <= DSPARK_N_DRAFT; ++pos) {
     a.pos = pos;
-    switch (src) {
-      case kSrcRes: hipLaunchKernelGGL(ratio_step_kernel<kSrcRes>, grid, dim3(BS), 0, s, a); break;
-      case kSrcBf16: hipLaunchKernelGGL(ratio_step_kernel<kSrcBf16>, grid, dim3(BS), 0, s, a); break;
-      default: hipLaunchKernelGGL(ratio_step_kernel<kSrcF32>, grid, dim3(BS), 0, s, a); break;
-    }
+    if (f32) hipLaunchKernelGGL(ratio_step_kernel<kSrcF32>, grid, dim3(BS), 0, s, a);
+    else hipLaunchKernelGGL(ratio_step_kernel<kSrcBf16>, grid, dim3(BS), 0, s, a);
     if ((rc = check_launch())) return rc;
   }
   return DSPARK_SUCCESS;
