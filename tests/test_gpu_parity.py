@@ -160,6 +160,79 @@ def test_sample_entry_many_draws():
     assert not tok[0].any() and not tok[2].any()
 
 
+@pytest.mark.parametrize("k", [0, 1024])
+def test_sample_entry_all_2_24_draws(k):
+    """Every one of the 2^24 draws, on a full-vocabulary q row (16 copies of
+    the row, 2^20 draws each): the token histogram equals the counts
+    exactly, for a dense and a sparse row."""
+    V = 129280
+    rng = np.random.default_rng(27 + k)
+    x = (rng.standard_normal((1, V)) * 2).astype(np.float32)
+    x[0, 7:40] = -np.inf
+    d = to_dev(np.repeat(x, 16, axis=0), F32)
+    q = B.q_alloc(d, topk=np.full(16, k, np.int32), k_max=max(k, 1))
+    st = q["status"].clone()
+    assert (st == 0).all()
+    draws = torch.arange(1 << 24, dtype=torch.int64, device=dev()).to(torch.int32).view(16, 1 << 20)
+    tok = B.sample(q, draws, st, V)
+    torch.cuda.synchronize()
+    assert (st == 0).all()
+    hist = torch.bincount(tok.view(-1).to(torch.int64), minlength=V).cpu().numpy()
+    ref = O.draft_row(x[0], F32, k)
+    want = np.zeros(V, np.int64)
+    want[ref["ids"]] = ref["counts"]
+    assert np.array_equal(hist, want)
+
+
+def _shared_key_rows(V=3000):
+    """Rows whose threshold remainder is shared by distinct table entries:
+    the maximum 10.0 (binary32 ulp 2^-20) and values x with
+    2^-23 <= |x| <= 2^-21, which are distinct bf16 values above the
+    collapse bound 2^-23 but all give RN32(x - 10) = -10, so every one of
+    their entries has the weight, the floor and the remainder of the
+    collapsed entry.  The largest-remainder cut falls inside that shared key
+    and splits it across entries: 2 and 3 entries (the candidate path's tie
+    of several entries) and 515 entries (more than a threshold bucket holds:
+    the exact path), both handed to the general per-value path."""
+    rng = np.random.default_rng(31)
+    above = [b | sg for b in range(0x3400, 0x3501) for sg in (0, 0x8000)]
+    rows = []
+    for distinct, copies in (([0, 0x3480], 60), ([0x3480, 0x3481, 0x3482], 50), ([0] + above, 3)):
+        row = np.full(V, 0xFF80, np.uint16)
+        pos = rng.permutation(V)
+        row[pos[0]] = 0x4120  # 10.0
+        k = 1
+        for v in distinct:
+            for _ in range(copies):
+                row[pos[k]] = v
+                k += 1
+        rows.append(row)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("k", [0, 100])
+def test_shared_remainder_key_rows(k):
+    raw = _shared_key_rows()
+    for i in range(raw.shape[0]):  # the oracle splits the shared key across distinct values
+        x = O.to_f32(raw[i], BF16)
+        st, ids, c = O.q_row(x, 0)
+        grp = (raw[i] != 0xFF80) & (x != 10.0)
+        up, lo = raw[i][grp & (c == c[grp].max())], raw[i][grp & (c == c[grp].min())]
+        assert c[grp].max() == c[grp].min() + 1 and len(set(up.tolist())) >= 2 and len(set(lo.tolist())) >= 2
+    draft = np.concatenate([raw, raw[:2]])  # one request of 5 draft rows
+    target = np.repeat(raw[:1], 6, axis=0)
+    rng = np.random.default_rng(37)
+    draws = rng.integers(0, 1 << 24, 5, dtype=np.uint32)
+    topk = np.full(5, k, np.int32)
+    out = B.fused(to_dev(draft, BF16), to_dev(target, BF16), B.SAMPLED, topk=topk, k_max=max(k, 1),
+                  draws=u32_dev(draws))
+    torch.cuda.synchronize()
+    h = host(out)
+    for j in range(5):
+        ref = O.draft_row(draft[j], BF16, k, int(draws[j]))
+        check_draft_row(h, j, ref, k, f"shared key k={k}")
+
+
 def test_verify_entry():
     V = 500
     rng = np.random.default_rng(23)

@@ -202,6 +202,40 @@ def test_rejections():
     assert st == O.ST_OK and c.tolist() == [M, 0]
 
 
+def test_remaining_assertion_cannot_fail():
+    """The binary64 quotients sum to within 2^-27 of M (two roundings of
+    relative size 2^-53 each: S64 = RN64(S), p_v = RN64(w_v / S64)), so
+    remaining = (M - sum y) + sum r lies in (-1, #{r > 0} + 1): the
+    "0 <= remaining <= #{r > 0}" refusal is never taken for weights in
+    [0, 1] with a positive sum.  Checked exactly with fractions on weight
+    vectors built to push the roundings one way: many equal weights,
+    powers of two, one large weight beside many tiny or subnormal ones,
+    sums that land on binary64 midpoints."""
+    rng = np.random.default_rng(67)
+    f32 = np.float32
+    cases = [
+        np.full(3, 1.0, f32), np.full(7, 0.6, f32), np.full(131072, 1.0, f32), np.full(131071, 0.75, f32),
+        np.array([1.0] + [2.0**-149] * 5000, f32), np.array([1.0, 2.0**-53, 2.0**-53], f32),
+        np.array([1.0] * 3 + [2.0**-60] * 9, f32), (2.0 ** -rng.integers(0, 149, 4000)).astype(f32),
+    ]
+    for _ in range(12):
+        n = int(rng.integers(2, 20000))
+        w = O.cr_exp_f32(-rng.exponential(rng.uniform(0.5, 40), n).astype(f32))
+        w[rng.random(n) < 0.1] = rng.choice(w, 1)[0]
+        cases.append(w)
+    for w in cases:
+        S = sum(Fraction(float(v)) for v in w)
+        s64 = float(S)
+        ys = [Fraction(float(v) / s64) * M for v in w.astype(np.float64)]
+        total = sum(ys)
+        assert abs(total - M) < Fraction(1, 1 << 27), len(w)
+        fl = [y.numerator // y.denominator for y in ys]
+        remaining = M - sum(fl)
+        assert 0 <= remaining <= sum(1 for y, c in zip(ys, fl) if y != c) < M
+        st, c = O.dyadic24_counts(w)
+        assert st == O.ST_OK and int(c.sum()) == M
+
+
 def test_sum_midpoint_rounds_to_even():
     """S = 1 + 2**-53 lies exactly between two binary64 values: RN64 keeps 1,
     so the small token gets p = 2**-53 and y = 2**-29 (count 0)."""

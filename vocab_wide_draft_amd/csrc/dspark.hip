@@ -680,48 +680,95 @@ __global__ void __launch_bounds__(BS) ratio_step_kernel(RatioArgs a) {
   }
 }
 
-// Standalone sampling from stored q rows.
+// Standalone sampling from stored q rows ("PP1 q transport and scheduling
+// design", "Distribution contract and precision": the first token whose
+// cumulative count is strictly greater than the draw).  The row is read
+// once into an LDS table of inclusive prefix sums (dense rows: one entry per
+// block of kSampleBlk counts; sparse rows: one per support entry), every
+// prefix of a row whose counts sum to 2^24 fits in 32 bits; then each thread
+// takes draws j = t, t + BS, ...: a binary search of the table, and for a
+// dense row a scan of one block.  A call costs one read of the row plus
+// O(log V + kSampleBlk) per draw.
+constexpr int kSampleBlk = 64;
+constexpr int kSampleTab = DSPARK_V_MAX / kSampleBlk;  // 16384 entries (64 KB)
+
 __global__ void __launch_bounds__(BS) sample_kernel(const int32_t* topk, int k_max, const uint32_t* dense,
                                                     const int32_t* sp_ids, const uint32_t* sp_cnt,
                                                     const int32_t* sp_len, int V, const uint32_t* draws,
                                                     int dpr, int32_t* tokens, int32_t* row_status) {
-  __shared__ RowShared sh;
+  __shared__ uint32_t pre[kSampleTab];
+  __shared__ BlockScratch bs;
   const int r = blockIdx.x;
-  int status = row_status[r];
   const uint32_t* dr = draws + (size_t)r * dpr;
   int32_t* tk = tokens + (size_t)r * dpr;
-  if (status == DSPARK_ST_OK) {
-    for (int j = 0; j < dpr; ++j)
-      if (dr[j] >= kMass) status = DSPARK_ST_DRAW_RANGE;
-  }
+  int status = row_status[r];  // (the same value for every thread)
+  uint32_t bad = 0;
+  for (int j = (int)threadIdx.x; j < dpr; j += BS) bad |= dr[j] >= kMass ? 1u : 0u;
+  bad = block_max<uint32_t>(bad, bs);
+  if (status == DSPARK_ST_OK && bad) status = DSPARK_ST_DRAW_RANGE;
   const int k = topk ? topk[r] : 0;
   const int kcap = k_max < V ? k_max : V;
   if (status == DSPARK_ST_OK && (k < 0 || k > kcap || (k == 0 && !dense) || (k > 0 && !sp_cnt)))
     status = DSPARK_ST_BAD_TOPK;
-  if (status == DSPARK_ST_OK) {
-    if (k == 0) {
-      const URow cr{const_cast<uint32_t*>(dense) + (size_t)r * V, V};
-      uint64_t s = 0;
-      for (int q = threadIdx.x; q < cr.nvec(); q += BS) {
-        uint32_t c[4];
-        cr.load(q, c);
-        s += (uint64_t)c[0] + c[1] + c[2] + c[3];
+  if (status == DSPARK_ST_OK && k == 0) {
+    const URow cr{const_cast<uint32_t*>(dense) + (size_t)r * V, V};
+    const int nb = (V + kSampleBlk - 1) / kSampleBlk;
+    uint64_t carry = 0;
+    for (int b0 = 0; b0 < nb; b0 += BS) {  // blocks b0 .. b0 + BS - 1, one per thread
+      const int b = b0 + (int)threadIdx.x;
+      uint64_t sb = 0;
+      if (b < nb) {
+        for (int q = b * (kSampleBlk / 4); q < (b + 1) * (kSampleBlk / 4) && q < cr.nvec(); ++q) {
+          uint32_t c[4];
+          cr.load(q, c);
+          sb += (uint64_t)c[0] + c[1] + c[2] + c[3];
+        }
       }
-      s = block_sum<uint64_t>(s, sh.bs);
-      if (s != kMass) status = DSPARK_ST_ALLOC_INCONSISTENT;
-      for (int j = 0; j < dpr && status == DSPARK_ST_OK; ++j) {
-        const int t = block_locate<4>(cr.nvec(), [&](int q, uint32_t (&c)[4]) { cr.load(q, c); }, dr[j], sh);
-        if (threadIdx.x == 0) tk[j] = t;
+      uint64_t tot;
+      const uint64_t ex = block_excl_scan<uint64_t>(sb, bs, &tot);
+      if (b < nb) pre[b] = (uint32_t)min(carry + ex + sb, (uint64_t)0xffffffffu);
+      carry += tot;
+    }
+    if (carry != kMass) status = DSPARK_ST_ALLOC_INCONSISTENT;
+    __syncthreads();
+    if (status == DSPARK_ST_OK) {
+      for (int j = (int)threadIdx.x; j < dpr; j += BS) {
+        const uint32_t u = dr[j];
+        int lo = 0, hi = nb - 1;  // first block whose inclusive prefix exceeds u (the last one does)
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (pre[mid] > u) hi = mid;
+          else lo = mid + 1;
+        }
+        uint32_t run = lo ? pre[lo - 1] : 0u;
+        int t = -1;
+        for (int v = lo * kSampleBlk; v < (lo + 1) * kSampleBlk && v < V && t < 0; ++v) {
+          run += cr.p[v];
+          if (run > u) t = v;
+        }
+        tk[j] = t;
       }
-    } else {
-      const int len = sp_len[r];
-      const int i = threadIdx.x;
-      const uint32_t c = (i < len && i < k) ? sp_cnt[(size_t)r * k_max + i] : 0u;
-      uint32_t tot;
-      const uint32_t pre = block_excl_scan<uint32_t>(c, sh.bs, &tot);
-      if (tot != kMass || len < 0 || len > k) status = DSPARK_ST_ALLOC_INCONSISTENT;
-      for (int j = 0; j < dpr && status == DSPARK_ST_OK; ++j) {
-        if (c > 0 && pre <= dr[j] && dr[j] < pre + c) tk[j] = sp_ids[(size_t)r * k_max + i];
+    }
+  } else if (status == DSPARK_ST_OK) {
+    const int len = sp_len[r];
+    const int i = threadIdx.x;
+    const bool lenok = len >= 0 && len <= k;
+    const uint32_t c = (lenok && i < len) ? sp_cnt[(size_t)r * k_max + i] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<uint32_t>(c, bs, &tot);
+    if (i < DSPARK_K_MAX) pre[i] = ex + c;
+    if (tot != kMass || !lenok) status = DSPARK_ST_ALLOC_INCONSISTENT;
+    __syncthreads();
+    if (status == DSPARK_ST_OK) {
+      for (int j = i; j < dpr; j += BS) {
+        const uint32_t u = dr[j];
+        int lo = 0, hi = len - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (pre[mid] > u) hi = mid;
+          else lo = mid + 1;
+        }
+        tk[j] = sp_ids[(size_t)r * k_max + lo];
       }
     }
   }
