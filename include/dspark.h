@@ -318,6 +318,35 @@ int dspark_sharded_propose(const dspark_rows* rows, int32_t n_shards, int32_t* a
 int dspark_sharded_propose_noalloc(const dspark_rows* rows, int32_t n_shards, int32_t* argmax, double* s64,
                                    float* conf, int32_t* row_status, void* stream);
 
+/* Vocabulary-sharded q, emulated on one GPU [Q, "Sparse support and
+ * vocabulary-sharded TP2 follow-up"]: the q of every row, and its sample, as
+ * n_shards ranks holding contiguous shards (ids [g V / n_shards,
+ * (g + 1) V / n_shards)) would compute them, with the values they would
+ * exchange passed through ws:
+ *   dense rows  - shard maxima and exact shard sums merged (every shard then
+ *                 holds m and S64); each shard's floors and remainder keys;
+ *                 remaining = M - the all-reduced floor sum; the threshold
+ *                 key found digit by digit from all-reduced histograms of
+ *                 the shards' keys; the tie at the threshold cut by lowest
+ *                 global id across shards ("coordinate remaining tickets
+ *                 globally");
+ *   sparse rows - each shard's local top-k (at most k candidates) merged by
+ *                 (logit desc, global id asc) into the exact global top-k,
+ *                 the counts allocated on that support;
+ *   sample      - the draw (uint32, < 2^24) picks the shard whose
+ *                 cumulative count mass first exceeds it, then the token in
+ *                 that shard.
+ * q (storage, topk, k_max), draws, argmax, sample and row_status as in
+ * dspark_q_alloc / dspark_fused (draws and sample: both NULL or both
+ * given).  Every output equals dspark_q_alloc's and the unsharded sample
+ * for every n_shards in [1, min(64, V)].  Sparse rows need
+ * n_shards * k_max <= 4096.  ws: at least dspark_sharded_q_workspace()
+ * bytes, 256-byte aligned. */
+size_t dspark_sharded_q_workspace(int64_t n_rows, int32_t n_shards, int32_t k_max);
+int dspark_sharded_q(const dspark_rows* rows, int32_t n_shards, const dspark_q* q, const uint32_t* draws,
+                     int32_t* argmax, int32_t* sample, int32_t* row_status, void* ws, size_t ws_bytes,
+                     void* stream);
+
 /* Test entry: the dense allocation steps of dspark_q_alloc applied to
  * caller-given float32 weights (normalised weights in [0, 1]), so that the
  * consistency assertions can be reached with constructed inputs.

@@ -10,7 +10,7 @@ from oracle import dyadic24 as O
 from vocab_wide_draft_amd import binding as B
 from vocab_wide_draft_amd import workloads as W
 
-from gpu_helpers import to_dev
+from gpu_helpers import to_dev, u32_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -48,3 +48,53 @@ def test_sharded_propose(dtype, V):
             assert (int(st[j]), int(am[j])) == (ws, wa), (dtype, V, G, j)
             assert s64[j] == wsum, (dtype, V, G, j, s64[j], wsum)
             assert cf[j] == (np.float32(1.0 / wsum) if ws == O.ST_OK else 0.0), (dtype, V, G, j)
+
+
+def _q_rows(V, rng):
+    base = (rng.standard_normal(V) * 2).astype(np.float32)
+    rows = [base.copy()]
+    vals = (rng.standard_normal(3) * 2).astype(np.float32)
+    rows.append(vals[rng.integers(0, 3, V)])                                # remainder and top-k ties across shards
+    rows.append(np.full(V, 0.75, np.float32))                                # one tie over every shard
+    r = np.full(V, -np.inf, np.float32); r[rng.integers(0, V, 9)] = 1.5; rows.append(r)  # few finite logits
+    r = base.copy(); r[rng.random(V) < 0.4] = -np.inf; rows.append(r)
+    r = (base - 70.0).astype(np.float32); r[V // 2] = 0.0; rows.append(r)    # tiny weights
+    r = base.copy(); r[V - 1] = np.nan; rows.append(r)                      # refused
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 3001), ("bf16", 3001), ("bf16", 129280), ("f32", 129280)])
+def test_sharded_q(dtype, V):
+    """The vocabulary-sharded q and its shard-then-token sample equal the
+    unsharded oracle (and the unsharded library call) bit for bit, dense
+    rows with globally coordinated tickets and sparse rows from merged
+    shard top-k, for G in {1, 2, 3, 8, 64}."""
+    rng = np.random.default_rng(V + 11)
+    x = _q_rows(V, rng)
+    raw = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    n = raw.shape[0]
+    d = to_dev(raw, dtype)
+    draws = rng.integers(0, 1 << 24, n, dtype=np.uint32)
+    for ks in ((0,) * n, (7, 0, 64, 0, 33, 1, 5)[:n]):
+        topk = np.array(ks, np.int32)
+        refs = [O.draft_row(raw[j], dtype, int(topk[j]), int(draws[j])) for j in range(n)]
+        for G in (1, 2, 3, 8, 64):
+            k_max = 64 if topk.any() else 0
+            out = B.sharded_q(d, G, topk=topk, k_max=k_max, draws=u32_dev(draws))
+            unsh = B.q_alloc(d, topk=topk, k_max=k_max)
+            torch.cuda.synchronize()
+            st, am, smp = (out[k].cpu().numpy() for k in ("status", "argmax", "sample"))
+            for j in range(n):
+                ref, k = refs[j], int(topk[j])
+                assert (int(st[j]), int(am[j]), int(smp[j])) == (ref["status"], ref["argmax"], ref["sample"]), (G, j)
+                if k == 0:
+                    got = out["dense"][j].cpu().numpy().view(np.uint32).astype(np.int64)
+                    want = ref["counts"] if ref["status"] == O.ST_OK else np.zeros(V, np.int64)
+                    assert np.array_equal(got, want), (G, j)
+                    if ref["status"] == O.ST_OK:
+                        assert torch.equal(out["dense"][j], unsh["dense"][j]), (G, j)
+                else:
+                    m = int(out["sp_len"][j])
+                    assert m == len(ref["ids"]), (G, j)
+                    assert out["sp_ids"][j, :m].cpu().tolist() == ref["ids"].tolist(), (G, j)
+                    assert out["sp_cnt"][j, :m].cpu().numpy().view(np.uint32).tolist() == ref["counts"].tolist(), (G, j)

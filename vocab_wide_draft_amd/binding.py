@@ -46,7 +46,7 @@ class QWire(ctypes.Structure):
 
 
 EXPORTS = ["dspark_propose", "dspark_q_alloc", "dspark_sample", "dspark_verify_greedy", "dspark_fused",
-           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_margin", "dspark_verify_stochastic", "dspark_verify_ratio", "dspark_sharded_propose", "dspark_sharded_propose_noalloc", "dspark_workspace_bytes", "dspark_q_semantic_id",
+           "dspark_q_alloc_weights", "dspark_cr_expf", "dspark_q_encode", "dspark_q_validate", "dspark_margin", "dspark_verify_stochastic", "dspark_verify_ratio", "dspark_sharded_propose", "dspark_sharded_propose_noalloc", "dspark_sharded_q", "dspark_sharded_q_workspace", "dspark_workspace_bytes", "dspark_q_semantic_id",
            "dspark_status_name", "dspark_last_error", "dspark_abi_version"]
 
 
@@ -77,6 +77,8 @@ def load_library():
         "dspark_margin": (ctypes.c_int, [RP, P, P]),
         "dspark_sharded_propose": (ctypes.c_int, [RP, I32, P, P, P, P, P, SZ, P]),
         "dspark_sharded_propose_noalloc": (ctypes.c_int, [RP, I32, P, P, P, P, P]),
+        "dspark_sharded_q": (ctypes.c_int, [RP, I32, QP, P, P, P, P, P, SZ, P]),
+        "dspark_sharded_q_workspace": (SZ, [I64, I32, I32]),
         "dspark_verify_stochastic": (ctypes.c_int, [RP, P, P, I64, P, P, P, P, P, P, P]),
         "dspark_verify_ratio": (ctypes.c_int, [RP, P, P, QP, I64, P, P, P, P, P, P]),
         "dspark_q_validate": (ctypes.c_int, [ctypes.POINTER(QWire), I64, I64, P, P, P, P, P]),
@@ -384,3 +386,25 @@ def sharded_propose_noalloc(rows: torch.Tensor, n_shards: int, out=None):
     _check(lib.dspark_sharded_propose_noalloc(ctypes.byref(r), int(n_shards), _p(out["argmax"]), _p(out["s64"]),
                                               _p(out["conf"]), _p(out["status"]), _stream()))
     return out
+
+
+def sharded_q(rows: torch.Tensor, n_shards: int, topk=None, k_max: int = 0, draws=None):
+    """The vocabulary-sharded q (dense rows with globally coordinated
+    tickets, sparse rows from merged shard top-k) and, with draws, the
+    shard-then-token sample; the same outputs as q_alloc plus argmax."""
+    lib = load_library()
+    n, V, dev = rows.shape[0], rows.shape[1], rows.device
+    tk = _topk(topk, dev)
+    want_dense = tk is None or bool((tk == 0).any())
+    qd = _make_q(n, V, dev, tk, k_max, want_dense)
+    am, st = _i32(n, dev), _i32(n, dev)
+    d = None if draws is None else draws.to(torch.int32).contiguous()
+    smp = None if draws is None else _i32(n, dev)
+    nbytes = int(lib.dspark_sharded_q_workspace(n, int(n_shards), int(k_max)))
+    ws = torch.empty(max(nbytes, 1) + 256, dtype=torch.uint8, device=dev)
+    off = (-ws.data_ptr()) % 256
+    r, q = _rows(rows), _qstruct(qd)
+    _check(lib.dspark_sharded_q(ctypes.byref(r), int(n_shards), ctypes.byref(q), _p(d), _p(am), _p(smp), _p(st),
+                                ctypes.c_void_p(ws.data_ptr() + off), nbytes, _stream()))
+    qd.update({"status": st, "argmax": am, "sample": smp, "_ws": ws})
+    return qd

@@ -18,6 +18,7 @@
 #include "margin.hpp"
 #include "q_wire.hpp"
 #include "sharded.hpp"
+#include "sharded_q.hpp"
 
 namespace dspark {
 
@@ -1288,6 +1289,110 @@ int dspark_sharded_propose_noalloc(const dspark_rows* rows, int32_t n_shards, in
   // every shard result is written before it is read within the call, so the
   // scratch needs no clearing
   return launch_sharded(rows, n_shards, argmax, s64, conf, row_status, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+// Workspace of the sharded q: the per-shard results the ranks would exchange
+// and the per-row merged state, each section 256-byte aligned.
+struct SqLayout {
+  size_t heads, sums, tks, tkr, hist, cand, total;
+};
+SqLayout sq_layout(int64_t n_rows, int32_t G, int32_t k_max) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t nb = (size_t)n_rows * (size_t)G;
+  SqLayout L;
+  L.heads = 0;
+  L.sums = up(L.heads + nb * sizeof(ShardHead));
+  L.tks = up(L.sums + nb * sizeof(Acc));
+  L.tkr = up(L.tks + nb * sizeof(TkShard));
+  L.hist = up(L.tkr + (size_t)n_rows * sizeof(TkRow));
+  L.cand = up(L.hist + nb * kTkBins * sizeof(uint32_t));
+  L.total = up(L.cand + nb * (size_t)(k_max > 0 ? k_max : 0) * sizeof(SqCand));
+  return L;
+}
+
+template <int DT>
+void launch_sharded_q(ShardQArgs a, bool sparse, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned nb = (unsigned)((int64_t)a.n_rows * a.G);
+  const unsigned nr = (unsigned)a.n_rows;
+  const unsigned tr = (nr + 255) / 256;
+  hipLaunchKernelGGL(shard_max_kernel<DT>, dim3(nb), dim3(kShardBS), 0, s, a.data, a.stride, a.V, a.G, a.heads);
+  hipLaunchKernelGGL(sq_rows_kernel, dim3(tr), dim3(256), 0, s, a);
+  if (a.dense) {
+    hipLaunchKernelGGL(shard_sum_kernel<DT>, dim3(nb), dim3(kShardBS), 0, s, a.data, a.stride, a.V, a.G,
+                       a.heads, a.sums);
+    hipLaunchKernelGGL(sq_floor_kernel<DT>, dim3(nb), dim3(BS), 0, s, a);
+    for (int L = 0; L < kTkLevels; ++L) {
+      a.level = L;
+      hipLaunchKernelGGL(sq_level_kernel, dim3(nr), dim3(BS), 0, s, a);
+      if (L + 1 < kTkLevels) {
+        a.level = L + 1;
+        hipLaunchKernelGGL(sq_hist_kernel, dim3(nb), dim3(BS), 0, s, a);
+      }
+    }
+    hipLaunchKernelGGL(sq_final_kernel<DT>, dim3(nb), dim3(BS), 0, s, a);
+  }
+  if (sparse) {
+    hipLaunchKernelGGL(sq_local_topk_kernel<DT>, dim3(nb), dim3(BS), 0, s, a);
+    hipLaunchKernelGGL(sq_merge_topk_kernel, dim3(nr), dim3(BS), 0, s, a);
+  }
+  if (a.draws) hipLaunchKernelGGL(sq_sample_kernel, dim3(nr), dim3(BS), 0, s, a);
+  hipLaunchKernelGGL(sq_out_kernel, dim3(tr), dim3(256), 0, s, a);
+}
+}  // namespace
+
+extern "C" {
+
+size_t dspark_sharded_q_workspace(int64_t n_rows, int32_t n_shards, int32_t k_max) {
+  if (n_rows < 0 || n_shards < 1 || n_shards > 64 || k_max < 0 || k_max > DSPARK_K_MAX) return 0;
+  return sq_layout(n_rows, n_shards, k_max).total;
+}
+
+int dspark_sharded_q(const dspark_rows* rows, int32_t n_shards, const dspark_q* q, const uint32_t* draws,
+                     int32_t* argmax, int32_t* sample, int32_t* row_status, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int rc = check_sharded(rows, n_shards, argmax, row_status);
+  if (rc) return rc;
+  if (!q) return fail(DSPARK_EINVAL, "q NULL");
+  if ((rc = check_q(q, rows->n_rows))) return rc;
+  const bool sparse = q->topk && q->k_max > 0;
+  if (sparse && (int64_t)n_shards * q->k_max > kSqMergeCap)
+    return fail(DSPARK_EINVAL, "n_shards * k_max must be at most 4096 (the candidates a row's merge holds)");
+  if (rows->n_rows == 0) return DSPARK_SUCCESS;
+  if ((draws == nullptr) != (sample == nullptr)) return fail(DSPARK_EINVAL, "draws and sample go together");
+  const SqLayout L = sq_layout(rows->n_rows, n_shards, q->k_max);
+  if (!ws || ws_bytes < L.total) return fail(DSPARK_EWORKSPACE, "workspace smaller than dspark_sharded_q_workspace()");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(DSPARK_EALIGN, "workspace must be 256-byte aligned");
+  char* w = static_cast<char*>(ws);
+  ShardQArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.data = rows->data;
+  a.stride = rows->row_stride;
+  a.V = (int)rows->vocab;
+  a.G = n_shards;
+  a.n_rows = (int)rows->n_rows;
+  a.topk = q->topk;
+  a.k_max = q->k_max;
+  a.dense = q->dense;
+  a.sp_ids = q->sp_ids;
+  a.sp_cnt = q->sp_cnt;
+  a.sp_len = q->sp_len;
+  a.draws = draws;
+  a.sample = sample;
+  a.argmax = argmax;
+  a.row_status = row_status;
+  a.heads = reinterpret_cast<ShardHead*>(w + L.heads);
+  a.sums = reinterpret_cast<Acc*>(w + L.sums);
+  a.tks = reinterpret_cast<TkShard*>(w + L.tks);
+  a.tkr = reinterpret_cast<TkRow*>(w + L.tkr);
+  a.hist = reinterpret_cast<uint32_t*>(w + L.hist);
+  a.cand = reinterpret_cast<SqCand*>(w + L.cand);
+  if (rows->dtype == DSPARK_BF16) launch_sharded_q<DSPARK_BF16>(a, sparse, stream);
+  else launch_sharded_q<DSPARK_F32>(a, sparse, stream);
+  return check_launch();
 }
 
 int dspark_q_encode(const uint32_t* counts, int64_t n, float* values, void* stream) {

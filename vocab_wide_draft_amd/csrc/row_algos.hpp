@@ -50,6 +50,32 @@ struct Row {
   }
 };
 
+// A row, or a vocabulary shard of one, that starts at any element offset:
+// element-wise loads, so no alignment is assumed.  Same interface as Row.
+template <int DT>
+struct ScalarRow {
+  static constexpr int EPV = 4;
+  const void* p;
+  int V;
+  __device__ int nvec() const { return (V + EPV - 1) / EPV; }
+  __device__ __forceinline__ int load(int q, float (&x)[EPV]) const {
+    const int base = q * EPV;
+    const int nv = V - base < EPV ? V - base : EPV;
+#pragma unroll
+    for (int l = 0; l < EPV; ++l) {
+      if (l < nv) {
+        if (DT == DSPARK_BF16)
+          x[l] = __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[base + l] << 16);
+        else
+          x[l] = static_cast<const float*>(p)[base + l];
+      } else {
+        x[l] = -__builtin_inff();
+      }
+    }
+    return nv;
+  }
+};
+
 // 4 x uint32 per vector view of a dense count / weight scratch row.  Rows
 // of a [n][V] buffer are 16-byte aligned only when V % 4 == 0; other rows
 // take the scalar path.
@@ -217,9 +243,9 @@ __device__ int block_locate(int nvec, WF wf, uint64_t u, SmemBase& sh) {
 // ------------------------------------------------- ordered compaction
 // Writes the selected elements of a row to (sh.cid, sh.sx) in ascending ID
 // order; sel(q, x, nv, mask) marks lanes.  Returns the count (<= cap).
-template <int DT, class SEL>
-__device__ int block_compact(const Row<DT>& row, SEL sel, int cap, RowShared& sh) {
-  constexpr int EPV = Row<DT>::EPV;
+template <class ROW, class SEL>
+__device__ int block_compact(const ROW& row, SEL sel, int cap, RowShared& sh) {
+  constexpr int EPV = ROW::EPV;
   const int nvec = row.nvec();
   const int n_iter = (nvec + BS - 1) / BS;
   for (int i = 0; i < n_iter; ++i) {

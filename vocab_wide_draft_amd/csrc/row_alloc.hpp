@@ -19,9 +19,9 @@ struct Stats {
 
 // Validity per "Distribution contract and precision": NaN first, then +inf,
 // then a row with no finite entry (all -inf) has zero mass.
-template <int DT>
-__device__ Stats row_stats(const Row<DT>& row, BlockScratch& bs) {
-  constexpr int EPV = Row<DT>::EPV;
+template <class ROW>
+__device__ Stats row_stats(const ROW& row, BlockScratch& bs) {
+  constexpr int EPV = ROW::EPV;
   const int nvec = row.nvec();
   float mx = -__builtin_inff();
   uint32_t flags = 0;  // bit0 NaN, bit1 +inf, bit2 any element
@@ -498,13 +498,13 @@ __device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, 
   return res;
 }
 
-// Sparse top-k q ("Sparse support ... follow-up": global support first,
-// normalised within it, zero-count entries dropped, ascending ids).
-template <int DT>
-__device__ QOut sparse_q(const Row<DT>& row, float m, uint32_t tkey, int k, int32_t* ids_out,
-                         uint32_t* cnt_out, int32_t* len_out, bool want_s, uint32_t u, RowShared& sh) {
-  constexpr int EPV = Row<DT>::EPV;
-  QOut res{DSPARK_ST_OK, 0};
+// The top-k support of a streamed row by (logit desc, id asc), 1 <= k <=
+// the row's length, into (sh.cid, sh.sx) in ascending id order (ids
+// relative to the row's start); m = the row maximum, tkey = key32 of this
+// thread's largest element (0 if none).  Returns the support size.
+template <class ROW>
+__device__ int stream_topk_support(const ROW& row, float m, uint32_t tkey, int k, RowShared& sh) {
+  constexpr int EPV = ROW::EPV;
   const int nvec = row.nvec();
   const uint32_t Km = key32(m);
   // 1. a lower bound for the k-th largest key: the k-th largest per-thread max
@@ -559,7 +559,7 @@ __device__ QOut sparse_q(const Row<DT>& row, float m, uint32_t tkey, int k, int3
     lo = blo;
   }
   // 3. support in ascending id order
-  const int n = block_compact(row, [&](int q, const float (&x)[EPV], int nv) -> uint32_t {
+  return block_compact(row, [&](int q, const float (&x)[EPV], int nv) -> uint32_t {
     uint32_t msk = 0;
 #pragma unroll
     for (int l = 0; l < EPV; ++l) {
@@ -569,6 +569,14 @@ __device__ QOut sparse_q(const Row<DT>& row, float m, uint32_t tkey, int k, int3
     }
     return msk;
   }, DSPARK_K_MAX, sh);
+}
+
+// Sparse top-k q ("Sparse support ... follow-up": global support first,
+// normalised within it, zero-count entries dropped, ascending ids).
+template <int DT>
+__device__ QOut sparse_q(const Row<DT>& row, float m, uint32_t tkey, int k, int32_t* ids_out,
+                         uint32_t* cnt_out, int32_t* len_out, bool want_s, uint32_t u, RowShared& sh) {
+  const int n = stream_topk_support(row, m, tkey, k, sh);
   return support_alloc(m, n, ids_out, cnt_out, len_out, want_s, u, sh);
 }
 
