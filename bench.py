@@ -363,6 +363,15 @@ def sharded_bench(args):
     alg = n * w.V * 2 + n * 20
     achieved = alg / (kernel_ms * 1e-3) / 1e9
     st = B.sharded_propose(d, G)["status"].cpu().numpy()
+    # beside it: the sharded q (dense rows with global tickets, sparse rows
+    # from merged shard top-k) and the shard-then-token sample of every row
+    draws = torch.from_numpy(w.draws.view(np.int32)).to(dev)
+    qo = B.sharded_q(d, G, topk=w.topk, k_max=1024, draws=draws)
+    q_ms, _ = _timed(lambda: B.sharded_q(d, G, draws=draws, out=qo), args.steps, args.warmup)
+    topk = np.asarray(w.topk)
+    lens = qo["sp_len"].cpu().numpy()
+    q_bytes = alg + int((topk == 0).sum()) * w.V * 4 + int(lens[topk != 0].sum()) * 8 + n * 4
+    q_rows_refused = int((qo["status"].cpu().numpy() != 0).sum())
     res = {
         "metric": "draft rows proposed per second (vocabulary-sharded, emulated on one GPU)",
         "value": round(n / (ms_per_step * 1e-3), 1), "unit": "rows/s",
@@ -373,6 +382,8 @@ def sharded_bench(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "algorithmic_bytes": alg, "kernel_ms": round(kernel_ms, 4)},
+        "sharded_q": {"rows": n, "shards": G, "kernel_ms": round(q_ms, 4), "algorithmic_bytes": q_bytes,
+                      "achieved_GBs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "rows_refused": q_rows_refused},
     }
     print(json.dumps(res), flush=True)
 

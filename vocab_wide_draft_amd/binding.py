@@ -388,23 +388,25 @@ def sharded_propose_noalloc(rows: torch.Tensor, n_shards: int, out=None):
     return out
 
 
-def sharded_q(rows: torch.Tensor, n_shards: int, topk=None, k_max: int = 0, draws=None):
+def sharded_q(rows: torch.Tensor, n_shards: int, topk=None, k_max: int = 0, draws=None, out=None):
     """The vocabulary-sharded q (dense rows with globally coordinated
     tickets, sparse rows from merged shard top-k) and, with draws, the
-    shard-then-token sample; the same outputs as q_alloc plus argmax."""
+    shard-then-token sample; the same outputs as q_alloc plus argmax.  `out`
+    may pass the outputs (and workspace) of an earlier call."""
     lib = load_library()
     n, V, dev = rows.shape[0], rows.shape[1], rows.device
-    tk = _topk(topk, dev)
-    want_dense = tk is None or bool((tk == 0).any())
-    qd = _make_q(n, V, dev, tk, k_max, want_dense)
-    am, st = _i32(n, dev), _i32(n, dev)
+    if out is None:
+        tk = _topk(topk, dev)
+        want_dense = tk is None or bool((tk == 0).any())
+        out = _make_q(n, V, dev, tk, k_max, want_dense)
+        nbytes = int(lib.dspark_sharded_q_workspace(n, int(n_shards), int(k_max)))
+        ws = torch.empty(max(nbytes, 1) + 256, dtype=torch.uint8, device=dev)
+        out.update({"status": _i32(n, dev), "argmax": _i32(n, dev),
+                    "sample": None if draws is None else _i32(n, dev),
+                    "_ws": ws, "_ws_ptr": ws.data_ptr() + (-ws.data_ptr()) % 256, "_ws_bytes": nbytes})
     d = None if draws is None else draws.to(torch.int32).contiguous()
-    smp = None if draws is None else _i32(n, dev)
-    nbytes = int(lib.dspark_sharded_q_workspace(n, int(n_shards), int(k_max)))
-    ws = torch.empty(max(nbytes, 1) + 256, dtype=torch.uint8, device=dev)
-    off = (-ws.data_ptr()) % 256
-    r, q = _rows(rows), _qstruct(qd)
-    _check(lib.dspark_sharded_q(ctypes.byref(r), int(n_shards), ctypes.byref(q), _p(d), _p(am), _p(smp), _p(st),
-                                ctypes.c_void_p(ws.data_ptr() + off), nbytes, _stream()))
-    qd.update({"status": st, "argmax": am, "sample": smp, "_ws": ws})
-    return qd
+    r, q = _rows(rows), _qstruct(out)
+    _check(lib.dspark_sharded_q(ctypes.byref(r), int(n_shards), ctypes.byref(q), _p(d), _p(out["argmax"]),
+                                _p(out["sample"]), _p(out["status"]), ctypes.c_void_p(out["_ws_ptr"]),
+                                out["_ws_bytes"], _stream()))
+    return out
