@@ -64,6 +64,19 @@ def measured_traffic(workload: str):
     return e.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (Linux), else what
+    platform reports."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, max_seconds: float):
     """The oracle (single-threaded numpy + Python integers) on the first
     requests of the same workload until about max_seconds have passed."""
@@ -78,7 +91,7 @@ def cpu_baseline(w, max_seconds: float):
     el = time.perf_counter() - t0
     return {"value": round(11 * n / el, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} requests ({11 * n} rows) of {w.name}, {el:.1f} s single-threaded on "
-                      f"{platform.processor() or platform.machine()} ({os.cpu_count()} host cores present)"}
+                      f"{cpu_model()} ({os.cpu_count()} host cores present)"}
 
 
 def copy_probe(nbytes: int, reps: int):
@@ -92,6 +105,16 @@ def copy_probe(nbytes: int, reps: int):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
+
+
+def _tensors(o, pre=""):
+    """(name, tensor) pairs of an output dict, nested dicts included."""
+    import torch
+    for k, v in o.items():
+        if isinstance(v, torch.Tensor):
+            yield pre + k, v
+        elif isinstance(v, dict):
+            yield from _tensors(v, pre + k + ".")
 
 
 def _timed(fn, steps, warmup):
@@ -395,6 +418,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=5, help="workload 1..5 (default: the R=1024 mixed batch)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
+                    help="replay the step as one captured HIP graph (default) or launch it eagerly")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
     ap.add_argument("--op", choices=["step", "wire", "stochastic", "ratio", "sharded"], default="step",
@@ -443,23 +468,30 @@ def main():
     mode = B.SAMPLED if w.mode == "sampled" else B.GREEDY
     with_q = w.topk is not None
     out = B.fused(d, t, mode, topk=w.topk, k_max=1024 if with_q else 0, draws=draws, with_q=with_q)
-    for _ in range(max(args.warmup - 1, 0)):
-        B.fused(d, t, mode, draws=draws, out=out)
-    torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s, e in evs:
-        s.record(stream)
+    def eager():
         B.fused(d, t, mode, draws=draws, out=out)
-        e.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in evs]
-    mean_launch = sum(launch_ms) / len(launch_ms)
-    ms_per_step = wall * 1e3 / args.steps
+
+    run, launch = eager, "eager"
+    if args.graph:
+        # the whole step captured once into a HIP graph and replayed: one
+        # submission per step instead of one per kernel
+        torch.cuda.synchronize()
+        ref = {k: v.clone() for k, v in _tensors(out)}
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager()
+        graph.replay()
+        torch.cuda.synchronize()
+        now = dict(_tensors(out))
+        for k, v in ref.items():
+            if not torch.equal(now[k], v):
+                raise RuntimeError(f"graph replay differs from the eager step in {k}")
+        run, launch = graph.replay, "hip graph"
+    eager_ms = None
+    if args.graph:
+        _, eager_ms = _timed(eager, max(args.steps // 2, 1), 1)
+    mean_launch, ms_per_step = _timed(run, args.steps, max(args.warmup - 1, 0))
     st = out["status"].cpu().numpy()
     rows = w.rows
     alg = w.algorithmic_bytes()
@@ -479,7 +511,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "R": w.R, "V": w.V, "rows": rows, "logits": w.dtype, "mode": w.mode,
                    "requests_per_s": round(w.R / (ms_per_step * 1e-3), 1),
-                   "rows_failed": int((st != 0).sum()), "parallelism": "single GPU, one workgroup per row"},
+                   "rows_failed": int((st != 0).sum()), "launch": launch,
+                   "eager_ms_per_step": None if eager_ms is None else round(eager_ms, 4),
+                   "parallelism": "single GPU, one workgroup per row (fewer than 128 streamed dense rows: "
+                                  "vocabulary shards per row)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name),
                      "algorithmic_bytes": alg, "kernel_ms": round(mean_launch, 4)},

@@ -361,9 +361,16 @@ int dspark_q_alloc_weights(const float* w, int64_t n_rows, int64_t n, int64_t st
  * float32 values d <= 0 (or -inf).  Used to check it exhaustively. */
 int dspark_cr_expf(const float* d, float* w, int64_t n, void* stream);
 
-/* Workspace bytes an entry point needs (op: 0 propose, 1 q_alloc, 2 sample,
- * 3 verify, 4 fused, 5 q_alloc_weights).  This build needs none: it returns
- * 0, and ws may be NULL with ws_bytes 0. */
+/* Workspace bytes an entry point can use (op: 0 propose, 1 q_alloc, 2
+ * sample, 3 verify, 4 fused, 5 q_alloc_weights; n_rows = draft rows).  No
+ * entry point needs one (ws may be NULL with ws_bytes 0).  dspark_q_alloc
+ * and dspark_fused use a workspace of at least this size, 256-byte aligned,
+ * to split each dense-q draft row that is streamed from memory (float32
+ * rows, bf16 rows above 131072 ids) over several workgroups -- the rows'
+ * vocabulary shards, merged as dspark_sharded_q merges them -- which fills
+ * the chip when there are few rows; the results are the same either way.
+ * It returns 0 where splitting does not apply (other ops, or 512 or more
+ * draft rows). */
 size_t dspark_workspace_bytes(int32_t op, int64_t n_rows, int64_t vocab, int32_t k_max);
 
 const char* dspark_q_semantic_id(void); /* "dyadic24-standard-v1" [Q] */

@@ -233,6 +233,48 @@ def test_shared_remainder_key_rows(k):
         check_draft_row(h, j, ref, k, f"shared key k={k}")
 
 
+@pytest.mark.parametrize("dtype,V", [(F32, 129280), (F32, 3001), (BF16, 140001)])
+def test_split_streamed_rows_equal_one_workgroup_rows(dtype, V):
+    """Streamed dense rows split over several workgroups (a workspace given)
+    equal the one-workgroup path and the oracle: q, argmax, confidence,
+    sample, verification, with a refused row, a constant row (every id in
+    the crossing bin) and sparse rows beside them; target rows (whose
+    argmax comes from shard heads then) with NaN, +inf, no finite entry and
+    a maximum tied across the first and last shard."""
+    R = 2
+    rng = np.random.default_rng(V + 3)
+    dr = (rng.standard_normal((5 * R, V)) * 2).astype(np.float32)
+    dr[3, V // 2] = np.nan
+    dr[6, :V // 3] = -np.inf
+    dr[7] = 1.25
+    tg = (rng.standard_normal((6 * R, V)) * 2).astype(np.float32)
+    tg[1, V // 2] = np.nan
+    tg[4] = -np.inf
+    tg[7, V - 1] = np.inf
+    tg[9, [0, V - 1]] = tg[9].max() + 1
+    raw_d = W.f32_to_bf16_bits(dr) if dtype == BF16 else dr
+    raw_t = W.f32_to_bf16_bits(tg) if dtype == BF16 else tg
+    topk = np.array([0, 0, 16, 0, 0, 0, 0, 0, 64, 0], np.int32)
+    draws = rng.integers(0, 1 << 24, 5 * R, dtype=np.uint32)
+    d, t = to_dev(raw_d, dtype), to_dev(raw_t, dtype)
+    a = host(B.fused(d, t, B.SAMPLED, topk=topk, k_max=64, draws=u32_dev(draws), split=True))
+    b = host(B.fused(d, t, B.SAMPLED, topk=topk, k_max=64, draws=u32_dev(draws), split=False))
+    torch.cuda.synchronize()
+    for k in ("argmax", "status", "sample", "target_argmax", "target_status", "accept_len", "bonus", "req_status"):
+        assert np.array_equal(a[k], b[k]), k
+    for i in range(6 * R):
+        x = O.to_f32(raw_t[i], dtype)
+        st = O.row_status(x)
+        assert a["target_status"][i] == st, i
+        assert a["target_argmax"][i] == (O.argmax_first(x)[1] if st == O.ST_OK else 0), i
+    assert a["target_argmax"][9] == 0 and a["target_status"][1] != 0 and a["target_status"][4] != 0
+    for j in range(5 * R):
+        ref = O.draft_row(raw_d[j], dtype, int(topk[j]), int(draws[j]))
+        check_draft_row(a, j, ref, int(topk[j]), "split")
+    dense = topk == 0
+    assert np.array_equal(a["q"]["dense"][dense], b["q"]["dense"][dense])
+
+
 def test_verify_entry():
     V = 500
     rng = np.random.default_rng(23)

@@ -162,6 +162,20 @@ def _qstruct(qd) -> Q:
              None if qd["sp_len"] is None else qd["sp_len"].data_ptr())
 
 
+def _split_ws(x: torch.Tensor, op: int, split: bool = True):
+    """Workspace that lets dense q rows streamed from memory (float32 rows,
+    bf16 rows above 131072 ids) be split over several workgroups: (tensor,
+    aligned pointer, bytes), or (None, None, 0) when it does not apply."""
+    n, V = x.shape
+    if not split or (x.dtype == torch.bfloat16 and V <= 131072):
+        return None, None, 0
+    nbytes = int(load_library().dspark_workspace_bytes(op, n, V, 0))
+    if nbytes == 0:
+        return None, None, 0
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=x.device)
+    return ws, ctypes.c_void_p(ws.data_ptr() + (-ws.data_ptr()) % 256), nbytes
+
+
 def _topk(topk, dev):
     if topk is None:
         return None
@@ -178,8 +192,9 @@ def propose(draft: torch.Tensor):
     return {"argmax": am, "conf": cf, "status": st}
 
 
-def q_alloc(draft: torch.Tensor, topk=None, k_max: int = 0):
-    """topk: None (all dense) or per-row k (0 = dense)."""
+def q_alloc(draft: torch.Tensor, topk=None, k_max: int = 0, split: bool = True):
+    """topk: None (all dense) or per-row k (0 = dense).  split=False keeps
+    every streamed dense row on one workgroup (no workspace)."""
     lib = load_library()
     n, V, dev = draft.shape[0], draft.shape[1], draft.device
     tk = _topk(topk, dev)
@@ -187,7 +202,8 @@ def q_alloc(draft: torch.Tensor, topk=None, k_max: int = 0):
     qd = _make_q(n, V, dev, tk, k_max, want_dense)
     st = _i32(n, dev)
     r, q = _rows(draft), _qstruct(qd)
-    _check(lib.dspark_q_alloc(ctypes.byref(r), ctypes.byref(q), _p(st), None, 0, _stream()))
+    ws, wp, wb = _split_ws(draft, 1, split)
+    _check(lib.dspark_q_alloc(ctypes.byref(r), ctypes.byref(q), _p(st), wp, wb, _stream()))
     qd["status"] = st
     return qd
 
@@ -219,7 +235,7 @@ def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, draft_status
 
 
 def fused(draft: torch.Tensor, target: torch.Tensor, mode: int, topk=None, k_max: int = 0, draws=None,
-          with_q: bool = True, out=None):
+          with_q: bool = True, out=None, split: bool = True):
     """The whole step.  draft [5R, V], target [6R, V]; draws [5R] or None.
     `out` may pass preallocated outputs from an earlier call (same shapes)."""
     lib = load_library()
@@ -237,12 +253,14 @@ def fused(draft: torch.Tensor, target: torch.Tensor, mode: int, topk=None, k_max
         else:
             out["q"] = None
         out["draws"] = None if draws is None else draws.to(torch.int32).contiguous()
+        out["_ws"] = _split_ws(draft, 4, split and with_q)
     d, t = _rows(draft), _rows(target)
     q = None if out["q"] is None else ctypes.byref(_qstruct(out["q"]))
+    _, wp, wb = out["_ws"]
     _check(lib.dspark_fused(ctypes.byref(d), ctypes.byref(t), mode, q, _p(out["draws"]), _p(out["argmax"]),
                             _p(out["conf"]), _p(out["sample"]), _p(out["status"]), _p(out["target_argmax"]),
                             _p(out["target_status"]), _p(out["accept_len"]), _p(out["bonus"]),
-                            _p(out["req_status"]), None, 0, _stream()))
+                            _p(out["req_status"]), wp, wb, _stream()))
     return out
 
 

@@ -51,6 +51,7 @@ struct RowsArgs {
   const uint32_t* draws;
   int32_t* sample;
   int no_counts;  // dense rows without a count row: the counts only feed the draw (resident bf16 rows)
+  int skip_dense;  // streamed rows: dense-q draft rows are split across workgroups by the sharded pipeline
   // target outputs
   int32_t* t_argmax;
   int32_t* t_status;
@@ -63,6 +64,7 @@ __global__ void __launch_bounds__(BS) rows_kernel(RowsArgs a) {
   const int b = blockIdx.x;
   const bool is_draft = b < a.n_draft;
   const int r = is_draft ? b : b - a.n_draft;
+  if (is_draft && a.skip_dense && a.do_q && (a.topk ? a.topk[r] : 0) == 0) return;  // (uniform)
   const char* base = static_cast<const char*>(is_draft ? a.draft : a.target);
   const Row<DT> row{base + (size_t)r * (size_t)(is_draft ? a.d_stride : a.t_stride) * ES, a.V};
   const Stats st = row_stats(row, sh.bs);
@@ -834,6 +836,54 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 using namespace dspark;
 
 namespace {
+// Workspace of the sharded q: the per-shard results the ranks would exchange
+// and the per-row merged state, each section 256-byte aligned.
+struct SqLayout {
+  size_t heads, sums, tks, tkr, cut, s64, hist, cids, cand, total;
+};
+SqLayout sq_layout(int64_t n_rows, int32_t G, int32_t k_max) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t nb = (size_t)n_rows * (size_t)G;
+  SqLayout L;
+  L.heads = 0;
+  L.sums = up(L.heads + 2 * nb * sizeof(ShardHead));  // the draft rows' heads, then room for target rows'
+
+  L.tks = up(L.sums + nb * sizeof(Acc));
+  L.tkr = up(L.tks + nb * sizeof(TkShard));
+  L.cut = up(L.tkr + (size_t)n_rows * sizeof(TkRow));
+  L.s64 = up(L.cut + (size_t)n_rows * sizeof(TkCut));
+  L.hist = up(L.s64 + (size_t)n_rows * sizeof(double));
+  L.cids = up(L.hist + (size_t)n_rows * kTkBins * sizeof(uint32_t));
+  L.cand = up(L.cids + nb * kSqCandCap * sizeof(uint32_t));
+  L.total = up(L.cand + nb * (size_t)(k_max > 0 ? k_max : 0) * sizeof(SqCand));
+  return L;
+}
+
+template <int DT>
+void launch_sharded_q(ShardQArgs a, bool sparse, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned nb = (unsigned)((int64_t)a.n_rows * a.G);
+  const unsigned nr = (unsigned)a.n_rows;
+  const unsigned tr = (nr + 255) / 256;
+  const unsigned nt = (unsigned)a.n_target;
+  hipLaunchKernelGGL(sq_max_kernel<DT>, dim3(nb + nt * (unsigned)a.Gt), dim3(kShardBS), 0, s, a);
+  hipLaunchKernelGGL(sq_rows_kernel, dim3(nr + nt), dim3(64), 0, s, a);
+  if (a.dense) {
+    hipLaunchKernelGGL(sq_sum_kernel<DT>, dim3(nb), dim3(kShardBS), 0, s, a);
+    hipLaunchKernelGGL(sq_floor_kernel, dim3(nb), dim3(BS), 0, s, a);
+    hipLaunchKernelGGL(sq_cand_kernel, dim3(nb), dim3(BS), 0, s, a);
+    hipLaunchKernelGGL(sq_resolve_kernel<DT>, dim3(nr), dim3(BS), 0, s, a);
+  }
+  if (sparse) {
+    hipLaunchKernelGGL(sq_local_topk_kernel<DT>, dim3(nb), dim3(BS), 0, s, a);
+    hipLaunchKernelGGL(sq_merge_topk_kernel, dim3(nr), dim3(BS), 0, s, a);
+  }
+  if (a.draws) hipLaunchKernelGGL(sq_sample_kernel, dim3(nr), dim3(BS), 0, s, a);
+  hipLaunchKernelGGL(sq_out_kernel, dim3(tr), dim3(256), 0, s, a);
+}
+}  // namespace
+
+namespace {
 thread_local char g_err[512];
 
 int fail(int code, const char* msg) {
@@ -901,13 +951,87 @@ int check_q(const dspark_q* q, int64_t n_rows) {
   return DSPARK_SUCCESS;
 }
 
-int launch_rows(const RowsArgs& a, int dtype, void* stream) {
-  const int nblk = a.n_draft + a.n_target;
+}  // namespace
+
+// Shards per dense row when streamed rows are split across workgroups:
+// enough for about four waves of workgroups over the chip.
+int split_shards(int64_t n_draft, int64_t vocab) {
+  if (n_draft <= 0 || n_draft >= 128) return 1;  // 128 or more rows (and their target rows) fill the chip
+  int64_t g = (1024 + n_draft - 1) / n_draft;
+  if (g > 64) g = 64;
+  if (g > vocab) g = vocab;
+  return g < 1 ? 1 : (int)g;
+}
+// Workspace that lets dspark_q_alloc / dspark_fused split dense streamed
+// rows (0 when splitting would not help: 128 rows or more already fill the
+// chip).
+size_t split_workspace_bytes(int64_t n_draft, int64_t vocab) {
+  const int G = split_shards(n_draft, vocab);
+  return G >= 2 ? sq_layout(n_draft, G, 0).total : 0;
+}
+
+namespace {
+int launch_rows(RowsArgs a, int dtype, void* stream, void* ws = nullptr, size_t ws_bytes = 0) {
+  int nblk = a.n_draft + a.n_target;
   if (nblk == 0) return DSPARK_SUCCESS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == DSPARK_BF16 && a.V <= NI * BS * 8) {
     hipLaunchKernelGGL(rows_bf16_kernel, dim3(nblk), dim3(BS), 0, s, a);
-  } else if (dtype == DSPARK_BF16)
+    return check_launch();
+  }
+  // streamed rows: with a large enough workspace, every dense-q draft row is
+  // split over several workgroups (the sharded pipeline, dense rows only) and
+  // the row kernel takes the other rows
+  const size_t need = split_workspace_bytes(a.n_draft, a.V);
+  const bool split = a.do_q && a.dense && need > 0 && ws && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0 &&
+                     ws_bytes >= need;
+  if (split) {
+    const int G = split_shards(a.n_draft, a.V);
+    const SqLayout L = sq_layout(a.n_draft, G, 0);
+    char* w = static_cast<char*>(ws);
+    ShardQArgs q;
+    std::memset(&q, 0, sizeof q);
+    q.data = a.draft;
+    q.stride = a.d_stride;
+    q.V = a.V;
+    q.G = G;
+    q.n_rows = a.n_draft;
+    q.topk = a.topk;
+    q.k_max = a.k_max;
+    q.dense = a.dense;
+    q.draws = a.sample ? a.draws : nullptr;
+    q.sample = a.sample;
+    q.argmax = a.argmax;
+    q.row_status = a.row_status;
+    q.conf = a.conf;
+    q.dense_only = 1;
+    // target rows come along (their heads fill the second half of the heads
+    // area) when the area holds a shard per row
+    const int64_t gt = a.n_target > 0 ? (int64_t)a.n_draft * G / a.n_target : 0;
+    if (gt >= 1) {
+      q.target = a.target;
+      q.t_stride = a.t_stride;
+      q.n_target = a.n_target;
+      q.Gt = (int)std::min<int64_t>(std::min<int64_t>(gt, 64), a.V);
+      q.t_argmax = a.t_argmax;
+      q.t_status = a.t_status;
+    }
+    q.heads = reinterpret_cast<ShardHead*>(w + L.heads);
+    q.sums = reinterpret_cast<Acc*>(w + L.sums);
+    q.tks = reinterpret_cast<TkShard*>(w + L.tks);
+    q.tkr = reinterpret_cast<TkRow*>(w + L.tkr);
+    q.cut = reinterpret_cast<TkCut*>(w + L.cut);
+    q.s64 = reinterpret_cast<double*>(w + L.s64);
+    q.hist = reinterpret_cast<uint32_t*>(w + L.hist);
+    q.cids = reinterpret_cast<uint32_t*>(w + L.cids);
+    if (dtype == DSPARK_BF16) launch_sharded_q<DSPARK_BF16>(q, false, stream);
+    else launch_sharded_q<DSPARK_F32>(q, false, stream);
+    int rc = check_launch();
+    if (rc) return rc;
+    a.skip_dense = 1;
+    if (gt >= 1) nblk = a.n_draft;  // the row kernel's blocks: draft rows only
+  }
+  if (dtype == DSPARK_BF16)
     hipLaunchKernelGGL(rows_kernel<DSPARK_BF16>, dim3(nblk), dim3(BS), 0, s, a);
   else
     hipLaunchKernelGGL(rows_kernel<DSPARK_F32>, dim3(nblk), dim3(BS), 0, s, a);
@@ -968,8 +1092,9 @@ const char* dspark_status_name(int32_t code) {
 }
 
 size_t dspark_workspace_bytes(int32_t op, int64_t n_rows, int64_t vocab, int32_t k_max) {
-  (void)op; (void)n_rows; (void)vocab; (void)k_max;
-  return 0;
+  (void)k_max;
+  if ((op != 1 && op != 4) || n_rows <= 0 || vocab < 1) return 0;
+  return split_workspace_bytes(n_rows, vocab);
 }
 
 int dspark_propose(const dspark_rows* draft, int32_t* argmax, float* conf, int32_t* row_status,
@@ -987,7 +1112,6 @@ int dspark_propose(const dspark_rows* draft, int32_t* argmax, float* conf, int32
 
 int dspark_q_alloc(const dspark_rows* draft, const dspark_q* q, int32_t* row_status, void* ws,
                    size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   int rc = check_rows(draft, "draft rows NULL");
   if (rc) return rc;
   if (!q) return fail(DSPARK_EINVAL, "q NULL");
@@ -996,7 +1120,7 @@ int dspark_q_alloc(const dspark_rows* draft, const dspark_q* q, int32_t* row_sta
   RowsArgs a = rows_args_draft(draft);
   a.row_status = row_status;
   set_q(a, q);
-  return launch_rows(a, draft->dtype, stream);
+  return launch_rows(a, draft->dtype, stream, ws, ws_bytes);
 }
 
 int dspark_sample(const dspark_q* q, int64_t n_rows, int64_t vocab, const uint32_t* draws,
@@ -1144,7 +1268,6 @@ int dspark_fused(const dspark_rows* draft, const dspark_rows* target, int32_t mo
                  int32_t* sample, int32_t* row_status, int32_t* target_argmax,
                  int32_t* target_status, int32_t* accept_len, int32_t* bonus, int32_t* req_status,
                  void* ws, size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   int rc = check_rows(draft, "draft rows NULL");
   if (rc) return rc;
   if ((rc = check_rows(target, "target rows NULL"))) return rc;
@@ -1175,7 +1298,7 @@ int dspark_fused(const dspark_rows* draft, const dspark_rows* target, int32_t mo
   a.n_target = (int)target->n_rows;
   a.t_argmax = target_argmax;
   a.t_status = target_status;
-  if ((rc = launch_rows(a, draft->dtype, stream))) return rc;
+  if ((rc = launch_rows(a, draft->dtype, stream, ws, ws_bytes))) return rc;
   const int32_t* dtok = mode == DSPARK_SAMPLED ? sample : argmax;
   return launch_verify(R, (int)draft->vocab, dtok, row_status, target_argmax, target_status, accept_len, bonus,
                        req_status, stream);
@@ -1293,56 +1416,6 @@ int dspark_sharded_propose_noalloc(const dspark_rows* rows, int32_t n_shards, in
 
 }  // extern "C"
 
-namespace {
-// Workspace of the sharded q: the per-shard results the ranks would exchange
-// and the per-row merged state, each section 256-byte aligned.
-struct SqLayout {
-  size_t heads, sums, tks, tkr, hist, cand, total;
-};
-SqLayout sq_layout(int64_t n_rows, int32_t G, int32_t k_max) {
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t nb = (size_t)n_rows * (size_t)G;
-  SqLayout L;
-  L.heads = 0;
-  L.sums = up(L.heads + nb * sizeof(ShardHead));
-  L.tks = up(L.sums + nb * sizeof(Acc));
-  L.tkr = up(L.tks + nb * sizeof(TkShard));
-  L.hist = up(L.tkr + (size_t)n_rows * sizeof(TkRow));
-  L.cand = up(L.hist + nb * kTkBins * sizeof(uint32_t));
-  L.total = up(L.cand + nb * (size_t)(k_max > 0 ? k_max : 0) * sizeof(SqCand));
-  return L;
-}
-
-template <int DT>
-void launch_sharded_q(ShardQArgs a, bool sparse, void* stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const unsigned nb = (unsigned)((int64_t)a.n_rows * a.G);
-  const unsigned nr = (unsigned)a.n_rows;
-  const unsigned tr = (nr + 255) / 256;
-  hipLaunchKernelGGL(shard_max_kernel<DT>, dim3(nb), dim3(kShardBS), 0, s, a.data, a.stride, a.V, a.G, a.heads);
-  hipLaunchKernelGGL(sq_rows_kernel, dim3(tr), dim3(256), 0, s, a);
-  if (a.dense) {
-    hipLaunchKernelGGL(shard_sum_kernel<DT>, dim3(nb), dim3(kShardBS), 0, s, a.data, a.stride, a.V, a.G,
-                       a.heads, a.sums);
-    hipLaunchKernelGGL(sq_floor_kernel<DT>, dim3(nb), dim3(BS), 0, s, a);
-    for (int L = 0; L < kTkLevels; ++L) {
-      a.level = L;
-      hipLaunchKernelGGL(sq_level_kernel, dim3(nr), dim3(BS), 0, s, a);
-      if (L + 1 < kTkLevels) {
-        a.level = L + 1;
-        hipLaunchKernelGGL(sq_hist_kernel, dim3(nb), dim3(BS), 0, s, a);
-      }
-    }
-    hipLaunchKernelGGL(sq_final_kernel<DT>, dim3(nb), dim3(BS), 0, s, a);
-  }
-  if (sparse) {
-    hipLaunchKernelGGL(sq_local_topk_kernel<DT>, dim3(nb), dim3(BS), 0, s, a);
-    hipLaunchKernelGGL(sq_merge_topk_kernel, dim3(nr), dim3(BS), 0, s, a);
-  }
-  if (a.draws) hipLaunchKernelGGL(sq_sample_kernel, dim3(nr), dim3(BS), 0, s, a);
-  hipLaunchKernelGGL(sq_out_kernel, dim3(tr), dim3(256), 0, s, a);
-}
-}  // namespace
 
 extern "C" {
 
@@ -1388,7 +1461,10 @@ int dspark_sharded_q(const dspark_rows* rows, int32_t n_shards, const dspark_q* 
   a.sums = reinterpret_cast<Acc*>(w + L.sums);
   a.tks = reinterpret_cast<TkShard*>(w + L.tks);
   a.tkr = reinterpret_cast<TkRow*>(w + L.tkr);
+  a.cut = reinterpret_cast<TkCut*>(w + L.cut);
+  a.s64 = reinterpret_cast<double*>(w + L.s64);
   a.hist = reinterpret_cast<uint32_t*>(w + L.hist);
+  a.cids = reinterpret_cast<uint32_t*>(w + L.cids);
   a.cand = reinterpret_cast<SqCand*>(w + L.cand);
   if (rows->dtype == DSPARK_BF16) launch_sharded_q<DSPARK_BF16>(a, sparse, stream);
   else launch_sharded_q<DSPARK_F32>(a, sparse, stream);

@@ -106,6 +106,30 @@ struct URow {
   }
 };
 
+// ------------------------------------------------------- streamed passes
+// Visits this thread's vectors q = threadIdx.x, threadIdx.x + BS, ... below
+// nvec: the loads of PF consecutive ones are issued together, before any of
+// them is used, so that a pass waits for one load latency per PF vectors.
+// ld(q, buf) fills buf and returns the valid count; body(q, buf, nv).
+template <int PF, class T, int EPV, class LD, class BODY>
+__device__ __forceinline__ void for_vecs(int nvec, LD ld, BODY body) {
+  for (int q0 = threadIdx.x; q0 < nvec; q0 += PF * BS) {
+    T buf[PF][EPV];
+    int nv[PF];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      const int q = q0 + k * BS;
+      nv[k] = q < nvec ? ld(q, buf[k]) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      const int q = q0 + k * BS;
+      if (q < nvec) body(q, buf[k], nv[k]);
+    }
+  }
+}
+constexpr int kPF = 4;  // vectors in flight per thread in streamed passes
+
 // ------------------------------------------------------------ shared state
 // Members every row kernel uses.
 struct SmemBase {
@@ -172,17 +196,28 @@ __device__ int block_locate(int nvec, WF wf, uint64_t u, SmemBase& sh) {
   const int n_iter = (nvec + BS - 1) / BS;
   for (int i = threadIdx.x; i < n_iter; i += BS) sh.tab[i] = 0;
   __syncthreads();
-  for (int i = 0; i < n_iter; ++i) {
-    const int q = i * BS + threadIdx.x;
-    uint64_t s = 0;
-    if (q < nvec) {
-      uint32_t w[EPV];
-      wf(q, w);
+  for (int i0 = 0; i0 < n_iter; i0 += kPF) {  // kPF iterations' loads in flight together
+    uint32_t w[kPF][EPV];
 #pragma unroll
-      for (int l = 0; l < EPV; ++l) s += w[l];
+    for (int k = 0; k < kPF; ++k) {
+      const int q = (i0 + k) * BS + threadIdx.x;
+      if (i0 + k < n_iter && q < nvec) {
+        wf(q, w[k]);
+      } else {
+#pragma unroll
+        for (int l = 0; l < EPV; ++l) w[k][l] = 0u;
+      }
     }
-    s = wave_sum(s);
-    if (lane_id() == 0 && s) atomicAdd((unsigned long long*)&sh.tab[i], (unsigned long long)s);
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      if (i0 + k < n_iter) {  // (uniform)
+        uint64_t s = 0;
+#pragma unroll
+        for (int l = 0; l < EPV; ++l) s += w[k][l];
+        s = wave_sum(s);
+        if (lane_id() == 0 && s) atomicAdd((unsigned long long*)&sh.tab[i0 + k], (unsigned long long)s);
+      }
+    }
   }
   __syncthreads();
   if (threadIdx.x < 64) {

@@ -25,9 +25,8 @@ __device__ Stats row_stats(const ROW& row, BlockScratch& bs) {
   const int nvec = row.nvec();
   float mx = -__builtin_inff();
   uint32_t flags = 0;  // bit0 NaN, bit1 +inf, bit2 any element
-  for (int q = threadIdx.x; q < nvec; q += BS) {
-    float x[EPV];
-    const int nv = row.load(q, x);
+  for_vecs<kPF, float, EPV>(nvec, [&](int q, float (&x)[EPV]) { return row.load(q, x); },
+                            [&](int q, const float (&x)[EPV], int nv) {
 #pragma unroll
     for (int l = 0; l < EPV; ++l) {
       if (l < nv) {
@@ -37,7 +36,7 @@ __device__ Stats row_stats(const ROW& row, BlockScratch& bs) {
       }
     }
     flags |= 4u;
-  }
+  });
   Stats s;
   s.tkey = (flags & 4u) ? key32(mx) : 0u;
   const float m = block_max<float>(mx, bs);
@@ -59,9 +58,8 @@ __device__ void row_argmax_conf(const Row<DT>& row, float m, bool want_conf, Row
   const int nvec = row.nvec();
   int first = 0x7fffffff;
   double sum = 0.0;
-  for (int q = threadIdx.x; q < nvec; q += BS) {
-    float x[EPV];
-    const int nv = row.load(q, x);
+  for_vecs<kPF, float, EPV>(nvec, [&](int q, float (&x)[EPV]) { return row.load(q, x); },
+                            [&](int q, const float (&x)[EPV], int nv) {
     float part = 0.0f;
 #pragma unroll
     for (int l = 0; l < EPV; ++l) {
@@ -71,7 +69,7 @@ __device__ void row_argmax_conf(const Row<DT>& row, float m, bool want_conf, Row
       }
     }
     sum += (double)part;
-  }
+  });
   *am = block_min<int>(first, sh.bs);
   if (want_conf) {
     const double s = block_sum<double>(sum, sh.bs);
@@ -134,15 +132,16 @@ __device__ __forceinline__ void floor_rem(float w, const SumR& S, uint32_t& c, d
 // selects there, ties to the lowest id.  keyfn(q, keys[4], ok[4]) gives the
 // remainder keys of count-row vector q (ok = positive remainder).
 template <class KEYS>
-__device__ Thr finish_in_lds(const URow& out, KEYS keyfn, uint64_t prefix, uint64_t pmask,
+__device__ Thr finish_in_lds(const URow& out, KEYS keys_of, uint64_t prefix, uint64_t pmask,
                              uint64_t need, RowShared& sh, int* cut) {
   if (threadIdx.x == 0) sh.bi[4] = 0;
   __syncthreads();
   const int nvec = out.nvec();
-  for (int q = threadIdx.x; q < nvec; q += BS) {
+  for_vecs<kPF, uint32_t, 4>(nvec, [&](int q, uint32_t (&w)[4]) { return out.load(q, w); },
+                             [&](int q, const uint32_t (&w)[4], int nv) {
     uint64_t key[4];
     bool ok[4];
-    keyfn(q, key, ok);
+    keys_of(w, nv, key, ok);
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
       if (ok[l] && (key[l] & pmask) == prefix) {
@@ -153,7 +152,7 @@ __device__ Thr finish_in_lds(const URow& out, KEYS keyfn, uint64_t prefix, uint6
         }
       }
     }
-  }
+  });
   __syncthreads();
   const int n = sh.bi[4] < kCandCap ? sh.bi[4] : kCandCap;
   __syncthreads();
@@ -192,9 +191,8 @@ __device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool wa
   __syncthreads();
   uint64_t csum = 0;
   uint32_t npos = 0;
-  for (int q = threadIdx.x; q < nvec; q += BS) {
-    uint32_t w[4];
-    const int nv = out.load(q, w);
+  for_vecs<kPF, uint32_t, 4>(nvec, [&](int q, uint32_t (&w)[4]) { return out.load(q, w); },
+                             [&](int q, const uint32_t (&w)[4], int nv) {
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
       if (l < nv) {
@@ -208,7 +206,7 @@ __device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool wa
         }
       }
     }
-  }
+  });
   csum = block_sum<uint64_t>(csum, sh.bs);
   npos = block_sum<uint32_t>(npos, sh.bs);
   const int64_t remaining = (int64_t)kMass - (int64_t)csum;
@@ -216,9 +214,7 @@ __device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool wa
     res.status = DSPARK_ST_ALLOC_INCONSISTENT;
     return res;
   }
-  auto keyfn = [&](int q, uint64_t (&key)[4], bool (&ok)[4]) {
-    uint32_t w[4];
-    const int nv = out.load(q, w);
+  auto keys_of = [&](const uint32_t (&w)[4], int nv, uint64_t (&key)[4], bool (&ok)[4]) {
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
       uint32_t c;
@@ -227,6 +223,11 @@ __device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool wa
       ok[l] = l < nv && r > 0.0;
       key[l] = ok[l] ? rem_key(r) : 0ull;
     }
+  };
+  auto keyfn = [&](int q, uint64_t (&key)[4], bool (&ok)[4]) {
+    uint32_t w[4];
+    const int nv = out.load(q, w);
+    keys_of(w, nv, key, ok);
   };
   Thr thr{~0ull, 0, false};  // selects nothing
   int cut = -1;
@@ -245,7 +246,7 @@ __device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool wa
       bool done = false;
       while (!done) {
         if (cnt <= (uint32_t)kCandCap) {
-          thr = finish_in_lds(out, keyfn, prefix, pmask, need, sh, &cut);
+          thr = finish_in_lds(out, keys_of, prefix, pmask, need, sh, &cut);
           done = true;
           break;
         }
@@ -266,15 +267,16 @@ __device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool wa
         const int nbits = shift - nsh;
         for (int bb = threadIdx.x; bb < kHistBins; bb += BS) sh.hist[bb] = 0;
         __syncthreads();
-        for (int q = threadIdx.x; q < nvec; q += BS) {
+        for_vecs<kPF, uint32_t, 4>(nvec, [&](int q, uint32_t (&w)[4]) { return out.load(q, w); },
+                                   [&](int q, const uint32_t (&w)[4], int nv) {
           uint64_t key[4];
           bool ok[4];
-          keyfn(q, key, ok);
+          keys_of(w, nv, key, ok);
 #pragma unroll
           for (int l = 0; l < 4; ++l)
             if (ok[l] && (key[l] & pmask) == prefix)
               atomicAdd(&sh.hist[(key[l] >> nsh) & ((1u << nbits) - 1u)], 1u);
-        }
+        });
         __syncthreads();
         const int d = block_find_crossing(sh.hist, 1 << nbits, need, false, sh, &before);
         need -= before;
@@ -292,14 +294,14 @@ __device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool wa
   }
   // final pass: counts = floor + selection
   uint64_t fsum = 0;
-  for (int q = threadIdx.x; q < nvec; q += BS) {
+  for_vecs<kPF, uint32_t, 4>(nvec, [&](int q, uint32_t (&w)[4]) { return out.load(q, w); },
+                             [&](int q, const uint32_t (&wi)[4], int nv) {
     uint32_t w[4];
-    const int nv = out.load(q, w);
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
       uint32_t c;
       double r;
-      floor_rem(__uint_as_float(w[l]), S, c, r);
+      floor_rem(__uint_as_float(wi[l]), S, c, r);
       if (l < nv && r > 0.0) {
         const uint64_t key = rem_key(r);
         const int id = q * 4 + l;
@@ -310,7 +312,7 @@ __device__ __forceinline__ QOut dense_alloc(const URow& out, double s64, bool wa
       fsum += l < nv ? c : 0u;
     }
     out.store(q, w, nv);
-  }
+  });
   fsum = block_sum<uint64_t>(fsum, sh.bs);
   if (fsum != kMass) {
     res.status = DSPARK_ST_ALLOC_INCONSISTENT;
@@ -335,9 +337,8 @@ __device__ QOut dense_q(const Row<DT>& row, float m, uint32_t* drow, bool want_s
   const int nvec = row.nvec();
   Acc acc;
   acc_zero(acc);
-  for (int q = threadIdx.x; q < nvec; q += BS) {
-    float x[EPV];
-    const int nv = row.load(q, x);
+  for_vecs<kPF, float, EPV>(nvec, [&](int q, float (&x)[EPV]) { return row.load(q, x); },
+                            [&](int q, const float (&x)[EPV], int nv) {
     uint32_t wb[EPV];
 #pragma unroll
     for (int l = 0; l < EPV; ++l) {
@@ -352,7 +353,7 @@ __device__ QOut dense_q(const Row<DT>& row, float m, uint32_t* drow, bool want_s
     } else {
       for (int l = 0; l < nv; ++l) drow[(size_t)q * EPV + l] = wb[l];
     }
-  }
+  });
   const double s64 = block_acc_rn64(acc, sh.acc);
   __threadfence_block();
   __syncthreads();

@@ -51,13 +51,13 @@ __device__ __forceinline__ bool head_better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// one workgroup of kShardBS threads: the head of shard g of row r
 template <int DT>
-__global__ void __launch_bounds__(kShardBS) shard_max_kernel(const void* data, int64_t stride, int V, int G,
-                                                             ShardHead* heads) {
+__device__ __forceinline__ void shard_max_block(const void* data, int64_t stride, int r, int V, int G, int g,
+                                                ShardHead* out) {
   __shared__ float s_v[kShardNW];
   __shared__ int s_i[kShardNW];
   __shared__ uint32_t s_f[kShardNW];
-  const int r = blockIdx.x / G, g = blockIdx.x % G;
   int lo, hi;
   shard_range(V, G, g, &lo, &hi);
   float bv = -__builtin_inff();
@@ -96,8 +96,14 @@ __global__ void __launch_bounds__(kShardBS) shard_max_kernel(const void* data, i
       }
       fl |= s_f[w];
     }
-    heads[blockIdx.x] = ShardHead{__float_as_uint(bv), bv == -__builtin_inff() ? 0x7fffffff : bi, fl, 0u};
+    *out = ShardHead{__float_as_uint(bv), bv == -__builtin_inff() ? 0x7fffffff : bi, fl, 0u};
   }
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kShardBS) shard_max_kernel(const void* data, int64_t stride, int V, int G,
+                                                             ShardHead* heads) {
+  shard_max_block<DT>(data, stride, (int)blockIdx.x / G, V, G, (int)blockIdx.x % G, heads + blockIdx.x);
 }
 
 // the merged head of row r from its G shard heads
@@ -117,6 +123,32 @@ __device__ __forceinline__ ShardHead merge_heads(const ShardHead* heads, int r, 
   return ShardHead{__float_as_uint(bv), bi, fl, 0u};
 }
 
+// the exact sum of the lanes' accumulators, in every lane: 128-bit adds
+// with carries over a butterfly
+__device__ __forceinline__ Acc wave_acc_total(Acc a) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t mlo = __shfl_xor(a.mlo, off), mhi = __shfl_xor(a.mhi, off);
+    const uint64_t tlo = __shfl_xor(a.tlo, off), thi = __shfl_xor(a.thi, off);
+    add128(a.mlo, a.mhi, mlo, mhi);
+    add128(a.tlo, a.thi, tlo, thi);
+  }
+  return a;
+}
+// the exact sum over a kShardBS workgroup (in thread 0)
+__device__ __forceinline__ Acc block_acc_total(Acc a, Acc* s_a) {
+  a = wave_acc_total(a);
+  if (lane_id() == 0) s_a[wave_id()] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kShardNW; ++w) {
+      add128(a.mlo, a.mhi, s_a[w].mlo, s_a[w].mhi);
+      add128(a.tlo, a.thi, s_a[w].tlo, s_a[w].thi);
+    }
+  }
+  return a;
+}
+
 template <int DT>
 __global__ void __launch_bounds__(kShardBS) shard_sum_kernel(const void* data, int64_t stride, int V, int G,
                                                              const ShardHead* heads, Acc* sums) {
@@ -134,23 +166,8 @@ __global__ void __launch_bounds__(kShardBS) shard_sum_kernel(const void* data, i
       acc_add(a, __float_as_uint(cr_expf(x - m)));
     }
   }
-  // exact sum over the workgroup: 128-bit adds with carries
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t mlo = __shfl_xor(a.mlo, off), mhi = __shfl_xor(a.mhi, off);
-    const uint64_t tlo = __shfl_xor(a.tlo, off), thi = __shfl_xor(a.thi, off);
-    add128(a.mlo, a.mhi, mlo, mhi);
-    add128(a.tlo, a.thi, tlo, thi);
-  }
-  if (lane_id() == 0) s_a[wave_id()] = a;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < kShardNW; ++w) {
-      add128(a.mlo, a.mhi, s_a[w].mlo, s_a[w].mhi);
-      add128(a.tlo, a.thi, s_a[w].tlo, s_a[w].thi);
-    }
-    sums[blockIdx.x] = a;
-  }
+  a = block_acc_total(a, s_a);
+  if (threadIdx.x == 0) sums[blockIdx.x] = a;
 }
 
 // one thread per row: merge the heads and the integer sums, round once

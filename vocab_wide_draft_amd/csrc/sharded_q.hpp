@@ -7,15 +7,19 @@
 // workgroup (or thread) per row as the collectives would merge them.
 //
 // Dense rows, with the remaining tickets coordinated globally:
-//   shard max / exact shard sum (sharded.hpp) -> every shard holds m and
-//   S64 = RN64(sum of the shard sums); each shard writes its weights into its
-//   part of the count row, computes floors and exact remainder keys, and
-//   sends its floor sum and a histogram of the keys' top 11 bits;
-//   remaining = M - sum of floor sums; the threshold key is found digit by
-//   digit (11, 11, 11, 11, 11, 9 bits) from the all-reduced histograms; the
-//   shards' counts of the final key give each shard's share of the tie cut,
-//   lowest global ids first (shards are in id order); each shard then writes
-//   its counts and sends its count mass.
+//   shard max (sharded.hpp) -> m; each shard sums its weights exactly and
+//   keeps them in its part of the count row; every shard then holds
+//   S64 = RN64(sum of the shard sums), computes floors and exact remainder
+//   keys, and sends its floor sum and a histogram of the keys' top 11 bits
+//   (all-reduced: added into the row's histogram); remaining = M - sum of
+//   floor sums, and the bin where the `remaining` largest keys end follows
+//   from the merged histogram; each shard writes floor + 1 above that bin and
+//   the floor below it, and sends the ids inside it (a few hundred for a
+//   whole row of spread remainders); the row's leader ranks them by key,
+//   ties to the lowest id, and places the bin's tickets.  Rows whose bin
+//   holds more ids than fit on chip (many equal remainders) finish the key's
+//   other digits over the row's flagged ids.  Two exchanges of small data
+//   per row instead of one histogram all-reduce per digit.
 // Sparse rows: each shard selects its local top-k (at most k candidates, by
 //   logit descending, id ascending); the row's workgroup merges the at most
 //   G k candidates into the exact global top-k and allocates the counts on
@@ -31,6 +35,8 @@ namespace dspark {
 constexpr int kTkBins = 2048;        // histogram bins of one digit
 constexpr int kTkLevels = 6;         // digits of a 64-bit remainder key
 constexpr int kSqMergeCap = 4096;    // candidates a row's merge may hold (G * k_max)
+constexpr int kSqCandCap = 1024;     // crossing-bin ids a row resolves on chip (and a shard stores)
+constexpr uint32_t kSqMark = 0x80000000u;  // count-row flag: in the crossing bin, not yet resolved
 
 __host__ __device__ constexpr int tk_shift(int l) { return l < 5 ? 53 - 11 * l : 0; }
 __host__ __device__ constexpr int tk_bins(int l) { return l < 5 ? 2048 : 512; }
@@ -39,16 +45,22 @@ struct TkShard {  // what one shard sends for its row
   uint64_t fsum;  // floor sum
   uint64_t npos;  // elements with a positive remainder
   uint64_t mass;  // count mass after the tickets
-  uint32_t take;  // tie members of the final key this shard takes
-  uint32_t ncand; // sparse rows: local top-k candidates
+  uint32_t ncand; // dense rows: ids in the crossing bin; sparse rows: local top-k candidates
+  uint32_t pad;
 };
 struct TkRow {  // a row's merged state
-  uint64_t prefix, pmask, need;
   float m;
   int32_t status;
   int32_t k;
-  int32_t mode;  // 0: tickets being placed, 1: no tickets (remaining 0)
+  int32_t pad;
 };
+struct TkCut {    // the tickets' first digit, from the all-reduced histogram
+  uint64_t need;  // tickets inside the crossing bin
+  int32_t bin;    // crossing bin of the first digit
+  int32_t mode;   // 0: tickets being placed, 1: none (remaining 0), 2: inconsistent
+};
+constexpr int32_t kSqNotMine = -1;  // a sparse row of a split fused step (the row kernel's)
+
 struct SqCand {
   int32_t id;
   uint32_t xbits;
@@ -72,26 +84,86 @@ struct ShardQArgs {
   Acc* sums;
   TkShard* tks;
   TkRow* tkr;
-  uint32_t* hist;  // [row][shard][kTkBins]
+  TkCut* cut;      // [row]
+  double* s64;     // [row] RN64 of the exact sum (dense rows)
+  uint32_t* hist;  // [row][kTkBins] the all-reduced first-digit histogram
+  uint32_t* cids;  // [row][shard][kSqCandCap] crossing-bin ids, in id order
   SqCand* cand;    // [row][shard][k_max]
-  int level;
+  // split rows of a fused step: only dense rows are this pipeline's (sparse
+  // rows are left to the row kernel, which then writes all their outputs);
+  // conf, when given, gets RN32(1 / S64) of the dense rows
+  int dense_only;
+  float* conf;
+  // target rows whose argmax and status come with this pipeline (Gt shards
+  // per row, heads after the draft rows'); n_target 0 for none
+  const void* target;
+  int64_t t_stride;
+  int n_target, Gt;
+  int32_t* t_argmax;
+  int32_t* t_status;
 };
+
+// (row, shard) workgroups: the shard heads of the draft rows, then (Gt
+// shards per row) of the target rows
+template <int DT>
+__global__ void __launch_bounds__(kShardBS) sq_max_kernel(ShardQArgs a) {
+  const int nd = a.n_rows * a.G;
+  const int b = blockIdx.x;
+  if (b < nd) shard_max_block<DT>(a.data, a.stride, b / a.G, a.V, a.G, b % a.G, a.heads + b);
+  else shard_max_block<DT>(a.target, a.t_stride, (b - nd) / a.Gt, a.V, a.Gt, (b - nd) % a.Gt, a.heads + b);
+}
 
 template <int DT>
 __device__ __forceinline__ float sq_value(const ShardQArgs& a, int r, int v) {
   return shard_value<DT>(a.data, a.stride, r, v);
 }
 
-// one thread per row: the merged heads (status, m, argmax), the row's kind
-// and the checks of its q storage and draw
-__global__ void sq_rows_kernel(ShardQArgs a) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= a.n_rows) return;
-  const ShardHead h = merge_heads(a.heads, r, a.G);
-  const float m = __uint_as_float(h.max_bits);
+// a wave per row: the merged heads (status, m, argmax; one lane per shard,
+// G <= 64), the row's kind, the checks of its q storage and draw; and a
+// zeroed first-digit histogram.  Waves past the draft rows merge the target
+// rows' heads into their argmax and status.
+__global__ void __launch_bounds__(64) sq_rows_kernel(ShardQArgs a) {
+  const int b = blockIdx.x, g = threadIdx.x;
+  const bool target = b >= a.n_rows;
+  const int r = target ? b - a.n_rows : b;
+  const int G = target ? a.Gt : a.G;
+  const ShardHead* hd = target ? a.heads + (size_t)a.n_rows * a.G + (size_t)r * a.Gt : a.heads + (size_t)r * a.G;
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff;
+  uint32_t fl = 0;
+  if (g < G) {
+    const ShardHead h = hd[g];
+    bv = __uint_as_float(h.max_bits);
+    bi = h.arg;
+    fl = h.flags;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {  // (value desc, id asc) is a total order: every lane ends equal
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (head_better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+    fl |= (uint32_t)__shfl_xor((int)fl, off);
+  }
+  if (target) {
+    if (g == 0) {
+      int st = DSPARK_ST_OK;
+      if (fl & 1u) st = DSPARK_ST_ROW_NAN;
+      else if (fl & 2u) st = DSPARK_ST_ROW_POSINF;
+      else if (bv == -__builtin_inff()) st = DSPARK_ST_ROW_ZERO_MASS;
+      a.t_argmax[r] = st == DSPARK_ST_OK ? bi : 0;
+      a.t_status[r] = st;
+    }
+    return;
+  }
+  for (int i = g; i < kTkBins; i += 64) a.hist[(size_t)r * kTkBins + i] = 0u;
+  if (g != 0) return;
+  const float m = bv;
   int st = DSPARK_ST_OK;
-  if (h.flags & 1u) st = DSPARK_ST_ROW_NAN;
-  else if (h.flags & 2u) st = DSPARK_ST_ROW_POSINF;
+  if (fl & 1u) st = DSPARK_ST_ROW_NAN;
+  else if (fl & 2u) st = DSPARK_ST_ROW_POSINF;
   else if (m == -__builtin_inff()) st = DSPARK_ST_ROW_ZERO_MASS;
   const int k = a.topk ? a.topk[r] : 0;
   const int kcap = a.k_max < a.V ? a.k_max : a.V;
@@ -99,56 +171,74 @@ __global__ void sq_rows_kernel(ShardQArgs a) {
     st = DSPARK_ST_BAD_TOPK;
   if (st == DSPARK_ST_OK && a.draws && a.draws[r] >= kMass) st = DSPARK_ST_DRAW_RANGE;
   TkRow t;
-  t.prefix = t.pmask = t.need = 0;
   t.m = m;
   t.status = st;
   t.k = k;
-  t.mode = 0;
+  t.pad = 0;
+  if (a.dense_only && k != 0) t.status = kSqNotMine;
   a.tkr[r] = t;
-  if (a.argmax) a.argmax[r] = st == DSPARK_ST_OK ? h.arg : 0;
+  if (a.argmax && t.status != kSqNotMine) a.argmax[r] = st == DSPARK_ST_OK ? bi : 0;
 }
 
-// RN64 of the row's exact sum, merged from the G shard sums
-__device__ __forceinline__ double sq_s64(const ShardQArgs& a, int r) {
-  Acc s;
-  acc_zero(s);
-  for (int g = 0; g < a.G; ++g) {
-    const Acc b = a.sums[(int64_t)r * a.G + g];
-    add128(s.mlo, s.mhi, b.mlo, b.mhi);
-    add128(s.tlo, s.thi, b.tlo, b.thi);
+// (row, shard) workgroups of a dense row: the exact integer sum of the
+// shard's weights RN32(exp(RN32(x - m))), and the weights themselves kept
+// in the row's count storage for the passes that follow
+template <int DT>
+__global__ void __launch_bounds__(kShardBS) sq_sum_kernel(ShardQArgs a) {
+  __shared__ Acc s_a[kShardNW];
+  const int r = blockIdx.x / a.G, g = blockIdx.x % a.G;
+  const TkRow t = a.tkr[r];
+  Acc acc;
+  acc_zero(acc);
+  if (t.status == DSPARK_ST_OK && t.k == 0) {
+    int lo, hi;
+    shard_range(a.V, a.G, g, &lo, &hi);
+    uint32_t* crow = a.dense + (size_t)r * a.V;
+    for (int i = lo + (int)threadIdx.x; i < hi; i += kShardBS) {
+      const uint32_t wb = __float_as_uint(cr_expf(sq_value<DT>(a, r, i) - t.m));
+      acc_add(acc, wb);
+      crow[i] = wb;
+    }
   }
-  return acc_rn64(s);
+  acc = block_acc_total(acc, s_a);
+  if (threadIdx.x == 0) a.sums[blockIdx.x] = acc;
 }
 
-struct SqShared {
-  BlockScratch bs;
-  uint32_t hist[kTkBins];
-  TkRow t;
+struct SqShared : SmemBase {
   double s64;
+  uint64_t u[2];
 };
 
-// (row, shard) workgroups of a dense row: weights into the count row, floor
-// sum, positive remainders and the first digit's histogram
-template <int DT>
+// (row, shard) workgroups of a dense row: S64 = RN64 of the all-reduced
+// exact sum (one lane per shard sum), then the shard's floor sum, its
+// positive remainders and their first-digit histogram, added into the
+// row's (the histogram all-reduce)
 __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
   __shared__ SqShared sh;
   const int r = blockIdx.x / a.G, g = blockIdx.x % a.G;
   const TkRow t = a.tkr[r];
   if (t.status != DSPARK_ST_OK || t.k != 0) return;  // (the same for every thread)
   for (int b = threadIdx.x; b < kTkBins; b += BS) sh.hist[b] = 0u;
-  if (threadIdx.x == 0) sh.s64 = sq_s64(a, r);
+  if (threadIdx.x < 64) {
+    Acc s;
+    acc_zero(s);
+    if ((int)threadIdx.x < a.G) s = a.sums[(size_t)r * a.G + threadIdx.x];
+    s = wave_acc_total(s);
+    if (threadIdx.x == 0) {
+      sh.s64 = acc_rn64(s);
+      if (g == 0) a.s64[r] = sh.s64;
+    }
+  }
   __syncthreads();
   const SumR S = sum_r(sh.s64);
   int lo, hi;
   shard_range(a.V, a.G, g, &lo, &hi);
-  uint32_t* crow = a.dense + (size_t)r * a.V;
+  const uint32_t* crow = a.dense + (size_t)r * a.V;
   uint64_t fsum = 0, npos = 0;
   for (int v = lo + (int)threadIdx.x; v < hi; v += BS) {
-    const float w = cr_expf(sq_value<DT>(a, r, v) - t.m);
-    crow[v] = __float_as_uint(w);
     uint32_t c;
     double rr;
-    floor_rem(w, S, c, rr);
+    floor_rem(__uint_as_float(crow[v]), S, c, rr);
     fsum += c;
     if (rr > 0.0) {
       ++npos;
@@ -157,99 +247,23 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
   }
   fsum = block_sum<uint64_t>(fsum, sh.bs);
   npos = block_sum<uint64_t>(npos, sh.bs);
-  const size_t rs = (size_t)blockIdx.x;
-  for (int b = threadIdx.x; b < kTkBins; b += BS) a.hist[rs * kTkBins + b] = sh.hist[b];
+  __syncthreads();
+  uint32_t* hrow = a.hist + (size_t)r * kTkBins;
+  for (int b = threadIdx.x; b < kTkBins; b += BS)
+    if (sh.hist[b]) atomicAdd(&hrow[b], sh.hist[b]);
   if (threadIdx.x == 0) {
-    a.tks[rs].fsum = fsum;
-    a.tks[rs].npos = npos;
+    a.tks[blockIdx.x].fsum = fsum;
+    a.tks[blockIdx.x].npos = npos;
   }
 }
 
-// one workgroup per dense row: level a.level of the threshold search.
-// Level 0 first checks remaining; the last level also gives each shard its
-// share of the final key's members.
-__global__ void __launch_bounds__(BS) sq_level_kernel(ShardQArgs a) {
-  __shared__ SmemBase sh;
-  const int r = blockIdx.x;
-  TkRow t = a.tkr[r];
-  if (t.status != DSPARK_ST_OK || t.k != 0 || t.mode != 0) return;  // (the same for every thread)
-  const int L = a.level;
-  if (L == 0) {
-    uint64_t fsum = 0, npos = 0;
-    for (int g = 0; g < a.G; ++g) {
-      fsum += a.tks[(size_t)r * a.G + g].fsum;
-      npos += a.tks[(size_t)r * a.G + g].npos;
-    }
-    const int64_t remaining = (int64_t)kMass - (int64_t)fsum;
-    if (remaining < 0 || remaining >= (int64_t)kMass || remaining > (int64_t)npos) {
-      if (threadIdx.x == 0) a.tkr[r].status = DSPARK_ST_ALLOC_INCONSISTENT;
-      return;
-    }
-    if (remaining == 0) {
-      if (threadIdx.x == 0) a.tkr[r].mode = 1;
-      return;
-    }
-    t.need = (uint64_t)remaining;
-  }
-  const int nb = tk_bins(L);
-  for (int b = threadIdx.x; b < nb; b += BS) {  // the all-reduce of the shards' histograms
-    uint32_t s = 0;
-    for (int g = 0; g < a.G; ++g) s += a.hist[((size_t)r * a.G + g) * kTkBins + b];
-    sh.hist[b] = s;
-  }
-  __syncthreads();
-  uint64_t before;
-  const int d = block_find_crossing(sh.hist, nb, t.need, false, sh, &before);
-  t.need -= before;
-  t.prefix |= (uint64_t)d << tk_shift(L);
-  t.pmask |= (uint64_t)(nb - 1) << tk_shift(L);
-  if (threadIdx.x == 0) {
-    a.tkr[r] = t;
-    if (L == kTkLevels - 1) {  // shard g's members of the final key: its histogram at d
-      uint64_t left = t.need;
-      for (int g = 0; g < a.G; ++g) {
-        const uint64_t n = a.hist[((size_t)r * a.G + g) * kTkBins + d];
-        const uint64_t take = n < left ? n : left;
-        a.tks[(size_t)r * a.G + g].take = (uint32_t)take;
-        left -= take;
-      }
-    }
-  }
-}
-
-// (row, shard) workgroups of a dense row: the histogram of digit a.level
-// among the keys that match the digits found so far
-__global__ void __launch_bounds__(BS) sq_hist_kernel(ShardQArgs a) {
-  __shared__ SqShared sh;
-  const int r = blockIdx.x / a.G, g = blockIdx.x % a.G;
-  const TkRow t = a.tkr[r];
-  if (t.status != DSPARK_ST_OK || t.k != 0 || t.mode != 0) return;  // (the same for every thread)
-  const int L = a.level, nb = tk_bins(L);
-  for (int b = threadIdx.x; b < nb; b += BS) sh.hist[b] = 0u;
-  if (threadIdx.x == 0) sh.s64 = sq_s64(a, r);
-  __syncthreads();
-  const SumR S = sum_r(sh.s64);
-  int lo, hi;
-  shard_range(a.V, a.G, g, &lo, &hi);
-  const uint32_t* crow = a.dense + (size_t)r * a.V;
-  for (int v = lo + (int)threadIdx.x; v < hi; v += BS) {
-    uint32_t c;
-    double rr;
-    floor_rem(__uint_as_float(crow[v]), S, c, rr);
-    if (rr > 0.0) {
-      const uint64_t key = rem_key(rr);
-      if ((key & t.pmask) == t.prefix) atomicAdd(&sh.hist[(key >> tk_shift(L)) & (uint64_t)(nb - 1)], 1u);
-    }
-  }
-  __syncthreads();
-  const size_t rs = (size_t)blockIdx.x;
-  for (int b = threadIdx.x; b < nb; b += BS) a.hist[rs * kTkBins + b] = sh.hist[b];
-}
-
-// (row, shard) workgroups of a dense row: the final counts of the shard (a
-// refused row's shard is zeroed) and the shard's count mass
-template <int DT>
-__global__ void __launch_bounds__(BS) sq_final_kernel(ShardQArgs a) {
+// (row, shard) workgroups of a dense row: every shard finds remaining (from
+// the shards' floor sums) and the crossing bin of the first digit (from the
+// all-reduced histogram) itself; then, in id order, writes floor + 1 above
+// the bin and the floor below it, flags the ids inside the bin (kSqMark) and
+// keeps the first kSqCandCap of them, and sends its count mass so far.  A
+// refused or inconsistent row's shard is zeroed.
+__global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
   __shared__ SqShared sh;
   const int r = blockIdx.x / a.G, g = blockIdx.x % a.G;
   const TkRow t = a.tkr[r];
@@ -257,40 +271,215 @@ __global__ void __launch_bounds__(BS) sq_final_kernel(ShardQArgs a) {
   int lo, hi;
   shard_range(a.V, a.G, g, &lo, &hi);
   uint32_t* crow = a.dense + (size_t)r * a.V;
-  const size_t rs = (size_t)blockIdx.x;
-  if (t.status != DSPARK_ST_OK) {
+  TkShard* ts = a.tks + blockIdx.x;
+  bool zero = t.status != DSPARK_ST_OK;
+  int64_t remaining = 0;
+  if (!zero) {
+    if (threadIdx.x < 64) {
+      uint64_t f = 0, n = 0;
+      if ((int)threadIdx.x < a.G) {
+        f = a.tks[(size_t)r * a.G + threadIdx.x].fsum;
+        n = a.tks[(size_t)r * a.G + threadIdx.x].npos;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        f += __shfl_xor(f, off);
+        n += __shfl_xor(n, off);
+      }
+      if (threadIdx.x == 0) {
+        sh.u[0] = f;
+        sh.u[1] = n;
+      }
+    }
+    __syncthreads();
+    remaining = (int64_t)kMass - (int64_t)sh.u[0];
+    if (remaining < 0 || remaining >= (int64_t)kMass || remaining > (int64_t)sh.u[1]) {
+      zero = true;
+      if (g == 0 && threadIdx.x == 0) a.cut[r] = TkCut{0ull, -1, 2};
+    }
+  }
+  if (zero) {
     for (int v = lo + (int)threadIdx.x; v < hi; v += BS) crow[v] = 0u;
+    if (threadIdx.x == 0) {
+      ts->mass = 0;
+      ts->ncand = 0;
+    }
     return;
   }
-  if (threadIdx.x == 0) sh.s64 = sq_s64(a, r);
-  __syncthreads();
-  const SumR S = sum_r(sh.s64);
-  const uint64_t T = t.prefix;
-  const bool tickets = t.mode == 0;
-  const uint32_t take = tickets ? a.tks[rs].take : 0u;
-  uint32_t before = 0;  // members of the final key met so far in this shard
+  const int mode = remaining == 0 ? 1 : 0;
+  int d = kTkBins;  // no bin: nothing above it, nothing inside it
+  uint64_t need = 0;
+  if (mode == 0) {
+    const uint32_t* hrow = a.hist + (size_t)r * kTkBins;
+    for (int b = threadIdx.x; b < kTkBins; b += BS) sh.hist[b] = hrow[b];
+    __syncthreads();
+    uint64_t before;
+    d = block_find_crossing(sh.hist, kTkBins, (uint64_t)remaining, false, sh, &before);
+    need = (uint64_t)remaining - before;
+  }
+  const SumR S = sum_r(a.s64[r]);
+  uint32_t* cbuf = a.cids + (size_t)blockIdx.x * kSqCandCap;
+  uint32_t base = 0;
   uint64_t mass = 0;
   for (int v0 = lo; v0 < hi; v0 += BS) {  // in id order, one id per thread
     const int v = v0 + (int)threadIdx.x;
     uint32_t c = 0;
-    uint64_t key = 0;
+    int bin = -1;
     if (v < hi) {
       double rr;
       floor_rem(__uint_as_float(crow[v]), S, c, rr);
-      key = rr > 0.0 ? rem_key(rr) : 0ull;
+      if (rr > 0.0) bin = (int)(rem_key(rr) >> tk_shift(0));
     }
-    const uint32_t member = (tickets && v < hi && key != 0ull && key == T) ? 1u : 0u;
+    const uint32_t in_bin = bin == d ? 1u : 0u;
     uint32_t tot;
-    const uint32_t rank = before + block_excl_scan<uint32_t>(member, sh.bs, &tot);
-    before += tot;
+    const uint32_t pos = base + block_excl_scan<uint32_t>(in_bin, sh.bs, &tot);
+    base += tot;
     if (v < hi) {
-      c += (tickets && key != 0ull && key > T) || (member && rank < take) ? 1u : 0u;
-      crow[v] = c;
+      c += bin > d ? 1u : 0u;
+      if (in_bin && pos < (uint32_t)kSqCandCap) cbuf[pos] = (uint32_t)v;
+      crow[v] = c | (in_bin ? kSqMark : 0u);
       mass += c;
     }
   }
   mass = block_sum<uint64_t>(mass, sh.bs);
-  if (threadIdx.x == 0) a.tks[rs].mass = mass;
+  if (threadIdx.x == 0) {
+    ts->mass = mass;
+    ts->ncand = base;
+    if (g == 0) a.cut[r] = TkCut{need, d, mode};
+  }
+}
+
+struct SqResShared : SmemBase {
+  uint64_t key[kSqCandCap];
+  uint32_t id[kSqCandCap];
+  uint32_t off[65];
+  uint32_t wins[64];
+};
+
+// the shard holding id v
+__device__ __forceinline__ int sq_shard_of(int v, int V, int G) {
+  int g = (int)((int64_t)v * G / V);
+  int lo, hi;
+  shard_range(V, G, g, &lo, &hi);
+  while (v >= hi) {
+    ++g;
+    shard_range(V, G, g, &lo, &hi);
+  }
+  while (v < lo) {
+    --g;
+    shard_range(V, G, g, &lo, &hi);
+  }
+  return g;
+}
+
+// one workgroup per dense row: the `need` tickets of the crossing bin go to
+// its largest remainder keys, ties to the lowest id.  Keys are recomputed
+// from the logits (the count row holds the counts by now).  Up to
+// kSqCandCap ids the bin is resolved on chip from the shards' stored ids;
+// beyond that the remaining five digits are found over the flagged ids of
+// the row and the tie cut follows id order.  The shards' masses get the
+// tickets they won.
+template <int DT>
+__global__ void __launch_bounds__(BS) sq_resolve_kernel(ShardQArgs a) {
+  __shared__ SqResShared sh;
+  const int r = blockIdx.x;
+  const TkRow t = a.tkr[r];
+  if (t.k != 0 || t.status != DSPARK_ST_OK || !a.dense) return;  // (the same for every thread)
+  const TkCut cut = a.cut[r];
+  if (cut.mode == 2) {
+    if (threadIdx.x == 0) a.tkr[r].status = DSPARK_ST_ALLOC_INCONSISTENT;
+    return;
+  }
+  if (cut.mode == 1) return;
+  const int G = a.G;
+  if (threadIdx.x < 64) {
+    const uint32_t n = (int)threadIdx.x < G ? a.tks[(size_t)r * G + threadIdx.x].ncand : 0u;
+    const uint32_t inc = wave_incl_scan(n);
+    sh.off[threadIdx.x + 1] = inc;
+    if (threadIdx.x == 0) sh.off[0] = 0u;
+    sh.wins[threadIdx.x] = 0u;
+  }
+  __syncthreads();
+  const uint32_t n = sh.off[G];
+  const uint64_t need0 = cut.need;
+  const SumR S = sum_r(a.s64[r]);
+  const float m = t.m;
+  uint32_t* crow = a.dense + (size_t)r * a.V;
+  auto key_of = [&](int v) {
+    uint32_t c;
+    double rr;
+    floor_rem(cr_expf(sq_value<DT>(a, r, v) - m), S, c, rr);
+    return rem_key(rr);
+  };
+  if (n <= (uint32_t)kSqCandCap) {
+    const bool all = need0 == (uint64_t)n;  // the whole bin wins
+    for (uint32_t j = threadIdx.x; j < n; j += BS) {
+      int g = 0, gh = G - 1;  // the shard holding position j: the last g with off[g] <= j (non-empty)
+      while (g < gh) {
+        const int mid = (g + gh + 1) >> 1;
+        if (sh.off[mid] <= j) g = mid;
+        else gh = mid - 1;
+      }
+      const uint32_t id = a.cids[((size_t)r * G + g) * kSqCandCap + (j - sh.off[g])];
+      sh.id[j] = id;
+      sh.key[j] = all ? 0ull : key_of((int)id);
+    }
+    __syncthreads();
+    for (uint32_t j = threadIdx.x; j < n; j += BS) {
+      bool win = true;
+      if (!all) {  // rank: larger keys, then equal keys at lower ids (the list is in id order)
+        const uint64_t kj = sh.key[j];
+        uint32_t rank = 0;
+        for (uint32_t i = 0; i < n; ++i) {
+          const uint64_t ki = sh.key[i];
+          rank += (ki > kj || (ki == kj && i < j)) ? 1u : 0u;
+        }
+        win = rank < need0;
+      }
+      const uint32_t id = sh.id[j];
+      crow[id] = (crow[id] & ~kSqMark) + (win ? 1u : 0u);
+      if (win) atomicAdd(&sh.wins[sq_shard_of((int)id, a.V, G)], 1u);
+    }
+  } else {
+    uint64_t prefix = (uint64_t)cut.bin << tk_shift(0), pmask = (uint64_t)(kTkBins - 1) << tk_shift(0);
+    uint64_t need = need0;
+    for (int L = 1; L < kTkLevels; ++L) {
+      const int nb = tk_bins(L), sft = tk_shift(L);
+      for (int b = threadIdx.x; b < nb; b += BS) sh.hist[b] = 0u;
+      __syncthreads();
+      for (int v = threadIdx.x; v < a.V; v += BS) {
+        if (crow[v] & kSqMark) {
+          const uint64_t k = key_of(v);
+          if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> sft) & (uint64_t)(nb - 1)], 1u);
+        }
+      }
+      __syncthreads();
+      uint64_t before;
+      const int dg = block_find_crossing(sh.hist, nb, need, false, sh, &before);
+      need -= before;
+      prefix |= (uint64_t)dg << sft;
+      pmask |= (uint64_t)(nb - 1) << sft;
+    }
+    const uint64_t T = prefix;  // the final key; its `need` lowest ids win
+    uint32_t run = 0;
+    for (int v0 = 0; v0 < a.V; v0 += BS) {
+      const int v = v0 + (int)threadIdx.x;
+      const uint32_t cw = v < a.V ? crow[v] : 0u;
+      const bool flagged = (cw & kSqMark) != 0u;
+      const uint64_t k = flagged ? key_of(v) : 0ull;
+      const uint32_t member = flagged && k == T ? 1u : 0u;
+      uint32_t tot;
+      const uint32_t rank = run + block_excl_scan<uint32_t>(member, sh.bs, &tot);
+      run += tot;
+      if (flagged) {
+        const bool win = k > T || (member && rank < need);
+        crow[v] = (cw & ~kSqMark) + (win ? 1u : 0u);
+        if (win) atomicAdd(&sh.wins[sq_shard_of(v, a.V, G)], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < G && sh.wins[threadIdx.x]) a.tks[(size_t)r * G + threadIdx.x].mass += sh.wins[threadIdx.x];
 }
 
 // (row, shard) workgroups of a sparse row: the shard's local top-k
@@ -388,22 +577,6 @@ __global__ void __launch_bounds__(BS) sq_merge_topk_kernel(ShardQArgs a) {
   }
 }
 
-// the shard holding id v
-__device__ __forceinline__ int sq_shard_of(int v, int V, int G) {
-  int g = (int)((int64_t)v * G / V);
-  int lo, hi;
-  shard_range(V, G, g, &lo, &hi);
-  while (v >= hi) {
-    ++g;
-    shard_range(V, G, g, &lo, &hi);
-  }
-  while (v < lo) {
-    --g;
-    shard_range(V, G, g, &lo, &hi);
-  }
-  return g;
-}
-
 struct SqSampleShared {
   BlockScratch bs;
   uint32_t mass[64];
@@ -483,11 +656,15 @@ __global__ void sq_out_kernel(ShardQArgs a) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= a.n_rows) return;
   const TkRow t = a.tkr[r];
+  if (t.status == kSqNotMine) return;
   a.row_status[r] = t.status;
   if (t.status != DSPARK_ST_OK) {
     if (a.argmax) a.argmax[r] = 0;
     if (a.sample) a.sample[r] = 0;
+    if (a.conf) a.conf[r] = 0.0f;
     if (t.k != 0 && a.sp_len) a.sp_len[r] = 0;
+  } else if (a.conf && t.k == 0) {
+    a.conf[r] = (float)(1.0 / a.s64[r]);
   }
 }
 
