@@ -402,3 +402,33 @@ def test_value_table_rows(V):
         for j in range(n5):
             ref = O.draft_row(raw[j], BF16, k, int(draws[j]))
             check_draft_row(f, j, ref, k, label=f"table fused V{V} k{k} {names[j]}")
+
+
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_split_all_dense_rows_verify_in_the_last_row(cfg):
+    """Every draft row dense and few rows: the split pipeline takes all rows,
+    and the last finishing row of each request verifies it.  Requests with
+    planted agreement (accept lengths 0..5), a refused draft row and an
+    invalid target row; all outputs equal the one-workgroup path and the
+    oracle's requests."""
+    R, V = 6, 40000
+    w = W.make(cfg, V=V, R=R)
+    sampled = w.mode == "sampled"
+    for r in range(R):  # target i agrees with draft token i for i < r (r = 5: all five)
+        for i in range(min(r, 5)):
+            ref = O.draft_row(w.draft[r * 5 + i], w.dtype, 0, int(w.draws[r * 5 + i]))
+            tok = ref["sample"] if sampled else ref["argmax"]
+            w.target[r * 6 + i, tok] = np.float32(w.target[r * 6 + i].max() + 30.0)
+    w.draft[1 * 5 + 3, 17] = np.nan      # request 1: a refused draft row
+    w.target[2 * 6 + 4, 99] = np.inf     # request 2: an invalid target row
+    d, t = to_dev(w.draft, w.dtype), to_dev(w.target, w.dtype)
+    mode = B.SAMPLED if sampled else B.GREEDY
+    draws = u32_dev(w.draws)
+    a = host(B.fused(d, t, mode, topk=np.zeros(5 * R, np.int32), draws=draws, split=True))
+    b = host(B.fused(d, t, mode, topk=np.zeros(5 * R, np.int32), draws=draws, split=False))
+    torch.cuda.synchronize()
+    for k in ("argmax", "status", "sample", "target_argmax", "target_status", "accept_len", "bonus", "req_status"):
+        assert np.array_equal(a[k], b[k]), k
+    assert np.array_equal(a["q"]["dense"], b["q"]["dense"])
+    check_workload(w, a, label="split, folded verification")
+    assert a["accept_len"].tolist() == [0, 1, 0, 3, 4, 5]

@@ -177,9 +177,13 @@ def _split_ws(x: torch.Tensor, op: int, split: bool = True):
 
 
 def _topk(topk, dev):
+    """Per-row k on the device, or None when every row is dense (k = 0 for
+    all rows is the same request as no top-k array)."""
     if topk is None:
         return None
     t = torch.as_tensor(topk, dtype=torch.int32)
+    if not bool(t.any()):
+        return None
     return t.to(dev).contiguous()
 
 

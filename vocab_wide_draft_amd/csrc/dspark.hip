@@ -55,6 +55,12 @@ struct RowsArgs {
   // target outputs
   int32_t* t_argmax;
   int32_t* t_status;
+  // greedy verification outputs (fused step), folded into the split
+  // pipeline when it takes every row
+  const int32_t* v_dtok;
+  int32_t* v_acc;
+  int32_t* v_bonus;
+  int32_t* v_rst;
 };
 
 template <int DT>
@@ -405,27 +411,7 @@ __global__ void verify_kernel(int R, int V, const int32_t* dtok, const int32_t* 
                               int32_t* bonus, int32_t* rst) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= R) return;
-  int status = DSPARK_ST_OK;
-  for (int i = 0; i < DSPARK_N_TARGET; ++i)
-    if (t_st[r * DSPARK_N_TARGET + i] != DSPARK_ST_OK) status = DSPARK_ST_TARGET_INVALID;
-  if (status == DSPARK_ST_OK) {
-    for (int i = 0; i < DSPARK_N_DRAFT; ++i) {
-      const bool valid = dst == nullptr || dst[r * DSPARK_N_DRAFT + i] == DSPARK_ST_OK;
-      const int d = dtok[r * DSPARK_N_DRAFT + i];
-      if (valid && (d < 0 || d >= V)) status = DSPARK_ST_DRAFT_INVALID;
-    }
-  }
-  int n = 0;
-  if (status == DSPARK_ST_OK) {
-    while (n < DSPARK_N_DRAFT) {
-      const bool valid = dst == nullptr || dst[r * DSPARK_N_DRAFT + n] == DSPARK_ST_OK;
-      if (!valid || dtok[r * DSPARK_N_DRAFT + n] != t_am[r * DSPARK_N_TARGET + n]) break;
-      ++n;
-    }
-  }
-  acc[r] = status == DSPARK_ST_OK ? n : 0;
-  bonus[r] = status == DSPARK_ST_OK ? t_am[r * DSPARK_N_TARGET + n] : 0;
-  rst[r] = status;
+  verify_request(r, V, dtok, dst, t_am, t_st, acc, bonus, rst);
 }
 
 // ---------------------------------------------------------------------------
@@ -839,7 +825,7 @@ namespace {
 // Workspace of the sharded q: the per-shard results the ranks would exchange
 // and the per-row merged state, each section 256-byte aligned.
 struct SqLayout {
-  size_t heads, sums, tks, tkr, cut, s64, hist, cids, cand, total;
+  size_t heads, sums, tks, tkr, cut, s64, req, hist, cids, ckeys, cflo, cand, total;
 };
 SqLayout sq_layout(int64_t n_rows, int32_t G, int32_t k_max) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -852,9 +838,12 @@ SqLayout sq_layout(int64_t n_rows, int32_t G, int32_t k_max) {
   L.tkr = up(L.tks + nb * sizeof(TkShard));
   L.cut = up(L.tkr + (size_t)n_rows * sizeof(TkRow));
   L.s64 = up(L.cut + (size_t)n_rows * sizeof(TkCut));
-  L.hist = up(L.s64 + (size_t)n_rows * sizeof(double));
+  L.req = up(L.s64 + (size_t)n_rows * sizeof(double));
+  L.hist = up(L.req + (size_t)n_rows * sizeof(uint32_t));
   L.cids = up(L.hist + (size_t)n_rows * kTkBins * sizeof(uint32_t));
-  L.cand = up(L.cids + nb * kSqCandCap * sizeof(uint32_t));
+  L.ckeys = up(L.cids + nb * kSqCandCap * sizeof(uint32_t));
+  L.cflo = up(L.ckeys + nb * kSqCandCap * sizeof(uint64_t));
+  L.cand = up(L.cflo + nb * kSqCandCap * sizeof(uint32_t));
   L.total = up(L.cand + nb * (size_t)(k_max > 0 ? k_max : 0) * sizeof(SqCand));
   return L;
 }
@@ -864,22 +853,18 @@ void launch_sharded_q(ShardQArgs a, bool sparse, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const unsigned nb = (unsigned)((int64_t)a.n_rows * a.G);
   const unsigned nr = (unsigned)a.n_rows;
-  const unsigned tr = (nr + 255) / 256;
   const unsigned nt = (unsigned)a.n_target;
   hipLaunchKernelGGL(sq_max_kernel<DT>, dim3(nb + nt * (unsigned)a.Gt), dim3(kShardBS), 0, s, a);
-  hipLaunchKernelGGL(sq_rows_kernel, dim3(nr + nt), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(sq_sum_kernel<DT>, dim3(nb + nt), dim3(kShardBS), 0, s, a);
   if (a.dense) {
-    hipLaunchKernelGGL(sq_sum_kernel<DT>, dim3(nb), dim3(kShardBS), 0, s, a);
     hipLaunchKernelGGL(sq_floor_kernel, dim3(nb), dim3(BS), 0, s, a);
     hipLaunchKernelGGL(sq_cand_kernel, dim3(nb), dim3(BS), 0, s, a);
-    hipLaunchKernelGGL(sq_resolve_kernel<DT>, dim3(nr), dim3(BS), 0, s, a);
   }
   if (sparse) {
     hipLaunchKernelGGL(sq_local_topk_kernel<DT>, dim3(nb), dim3(BS), 0, s, a);
     hipLaunchKernelGGL(sq_merge_topk_kernel, dim3(nr), dim3(BS), 0, s, a);
   }
-  if (a.draws) hipLaunchKernelGGL(sq_sample_kernel, dim3(nr), dim3(BS), 0, s, a);
-  hipLaunchKernelGGL(sq_out_kernel, dim3(tr), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(sq_finish_kernel<DT>, dim3(nr), dim3(BS), 0, s, a);
 }
 }  // namespace
 
@@ -956,22 +941,25 @@ int check_q(const dspark_q* q, int64_t n_rows) {
 // Shards per dense row when streamed rows are split across workgroups:
 // enough for about four waves of workgroups over the chip.
 int split_shards(int64_t n_draft, int64_t vocab) {
-  if (n_draft <= 0 || n_draft >= 128) return 1;  // 128 or more rows (and their target rows) fill the chip
-  int64_t g = (1024 + n_draft - 1) / n_draft;
+  // 512 or more rows (with their target rows, two rounds of the chip's
+  // 256 compute units) keep one workgroup per row
+  if (n_draft <= 0 || n_draft >= 512) return 1;
+  int64_t g = (2048 + n_draft - 1) / n_draft;  // about 2048 shard workgroups
   if (g > 64) g = 64;
   if (g > vocab) g = vocab;
   return g < 1 ? 1 : (int)g;
 }
 // Workspace that lets dspark_q_alloc / dspark_fused split dense streamed
-// rows (0 when splitting would not help: 128 rows or more already fill the
-// chip).
+// rows (0 when splitting does not apply: 512 rows or more).
 size_t split_workspace_bytes(int64_t n_draft, int64_t vocab) {
   const int G = split_shards(n_draft, vocab);
   return G >= 2 ? sq_layout(n_draft, G, 0).total : 0;
 }
 
 namespace {
-int launch_rows(RowsArgs a, int dtype, void* stream, void* ws = nullptr, size_t ws_bytes = 0) {
+int launch_rows(RowsArgs a, int dtype, void* stream, void* ws = nullptr, size_t ws_bytes = 0,
+                bool* verified = nullptr) {
+  if (verified) *verified = false;
   int nblk = a.n_draft + a.n_target;
   if (nblk == 0) return DSPARK_SUCCESS;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1024,12 +1012,27 @@ int launch_rows(RowsArgs a, int dtype, void* stream, void* ws = nullptr, size_t 
     q.s64 = reinterpret_cast<double*>(w + L.s64);
     q.hist = reinterpret_cast<uint32_t*>(w + L.hist);
     q.cids = reinterpret_cast<uint32_t*>(w + L.cids);
+    q.ckeys = reinterpret_cast<uint64_t*>(w + L.ckeys);
+    q.cflo = reinterpret_cast<uint32_t*>(w + L.cflo);
+    const bool all_rows = gt >= 1 && !a.topk;  // every row taken: all draft rows dense, targets too
+    if (all_rows && verified && a.v_dtok) {
+      q.vfy = 1;
+      q.v_dtok = a.v_dtok;
+      q.v_acc = a.v_acc;
+      q.v_bonus = a.v_bonus;
+      q.v_rst = a.v_rst;
+      q.req_cnt = reinterpret_cast<uint32_t*>(w + L.req);
+    }
     if (dtype == DSPARK_BF16) launch_sharded_q<DSPARK_BF16>(q, false, stream);
     else launch_sharded_q<DSPARK_F32>(q, false, stream);
     int rc = check_launch();
     if (rc) return rc;
     a.skip_dense = 1;
     if (gt >= 1) nblk = a.n_draft;  // the row kernel's blocks: draft rows only
+    if (all_rows) {
+      if (verified) *verified = q.vfy != 0;
+      return DSPARK_SUCCESS;
+    }
   }
   if (dtype == DSPARK_BF16)
     hipLaunchKernelGGL(rows_kernel<DSPARK_BF16>, dim3(nblk), dim3(BS), 0, s, a);
@@ -1298,8 +1301,14 @@ int dspark_fused(const dspark_rows* draft, const dspark_rows* target, int32_t mo
   a.n_target = (int)target->n_rows;
   a.t_argmax = target_argmax;
   a.t_status = target_status;
-  if ((rc = launch_rows(a, draft->dtype, stream, ws, ws_bytes))) return rc;
   const int32_t* dtok = mode == DSPARK_SAMPLED ? sample : argmax;
+  a.v_dtok = dtok;
+  a.v_acc = accept_len;
+  a.v_bonus = bonus;
+  a.v_rst = req_status;
+  bool verified = false;
+  if ((rc = launch_rows(a, draft->dtype, stream, ws, ws_bytes, &verified))) return rc;
+  if (verified) return DSPARK_SUCCESS;
   return launch_verify(R, (int)draft->vocab, dtok, row_status, target_argmax, target_status, accept_len, bonus,
                        req_status, stream);
 }
@@ -1465,6 +1474,8 @@ int dspark_sharded_q(const dspark_rows* rows, int32_t n_shards, const dspark_q* 
   a.s64 = reinterpret_cast<double*>(w + L.s64);
   a.hist = reinterpret_cast<uint32_t*>(w + L.hist);
   a.cids = reinterpret_cast<uint32_t*>(w + L.cids);
+  a.ckeys = reinterpret_cast<uint64_t*>(w + L.ckeys);
+  a.cflo = reinterpret_cast<uint32_t*>(w + L.cflo);
   a.cand = reinterpret_cast<SqCand*>(w + L.cand);
   if (rows->dtype == DSPARK_BF16) launch_sharded_q<DSPARK_BF16>(a, sparse, stream);
   else launch_sharded_q<DSPARK_F32>(a, sparse, stream);

@@ -25,6 +25,7 @@ namespace dspark {
 
 constexpr int kShardBS = 256;
 constexpr int kShardNW = kShardBS / 64;
+constexpr int kShardU = 8;  // elements per thread whose loads a shard pass issues together
 
 struct ShardHead {  // pass 1 result of one shard (16 bytes)
   uint32_t max_bits;
@@ -63,12 +64,21 @@ __device__ __forceinline__ void shard_max_block(const void* data, int64_t stride
   float bv = -__builtin_inff();
   int bi = 0x7fffffff;
   uint32_t fl = 0;
-  for (int i = lo + (int)threadIdx.x; i < hi; i += kShardBS) {
-    const float x = shard_value<DT>(data, stride, r, i);
-    fl |= (x != x ? 1u : 0u) | (x == __builtin_inff() ? 2u : 0u);
-    if (x > bv || (x == bv && x != -__builtin_inff() && i < bi)) {
-      bv = x;
-      bi = i;
+  for (int i0 = lo + (int)threadIdx.x; i0 < hi; i0 += kShardU * kShardBS) {
+    float x[kShardU];  // the loads of kShardU iterations in flight together
+#pragma unroll
+    for (int u = 0; u < kShardU; ++u) {
+      const int i = i0 + u * kShardBS;
+      x[u] = i < hi ? shard_value<DT>(data, stride, r, i) : -__builtin_inff();
+    }
+#pragma unroll
+    for (int u = 0; u < kShardU; ++u) {  // ids ascend with u: the first maximum stays
+      const int i = i0 + u * kShardBS;
+      fl |= (x[u] != x[u] ? 1u : 0u) | (x[u] == __builtin_inff() ? 2u : 0u);
+      if (x[u] > bv || (x[u] == bv && x[u] != -__builtin_inff() && i < bi)) {
+        bv = x[u];
+        bi = i;
+      }
     }
   }
   // a shard of -inf only has no maximum position (id INT32_MAX)

@@ -32,6 +32,37 @@
 
 namespace dspark {
 
+// Greedy verification of request r: a target row that is not OK makes the
+// request TARGET_INVALID; an OK draft row whose token is outside [0, V)
+// makes it DRAFT_INVALID; otherwise the accepted length is the number of
+// leading positions whose draft token is OK and equals the target argmax,
+// and the bonus token is the target argmax after them.
+__device__ __forceinline__ void verify_request(int r, int V, const int32_t* dtok, const int32_t* dst,
+                                               const int32_t* t_am, const int32_t* t_st, int32_t* acc,
+                                               int32_t* bonus, int32_t* rst) {
+  int status = DSPARK_ST_OK;
+  for (int i = 0; i < DSPARK_N_TARGET; ++i)
+    if (t_st[r * DSPARK_N_TARGET + i] != DSPARK_ST_OK) status = DSPARK_ST_TARGET_INVALID;
+  if (status == DSPARK_ST_OK) {
+    for (int i = 0; i < DSPARK_N_DRAFT; ++i) {
+      const bool valid = dst == nullptr || dst[r * DSPARK_N_DRAFT + i] == DSPARK_ST_OK;
+      const int d = dtok[r * DSPARK_N_DRAFT + i];
+      if (valid && (d < 0 || d >= V)) status = DSPARK_ST_DRAFT_INVALID;
+    }
+  }
+  int n = 0;
+  if (status == DSPARK_ST_OK) {
+    while (n < DSPARK_N_DRAFT) {
+      const bool valid = dst == nullptr || dst[r * DSPARK_N_DRAFT + n] == DSPARK_ST_OK;
+      if (!valid || dtok[r * DSPARK_N_DRAFT + n] != t_am[r * DSPARK_N_TARGET + n]) break;
+      ++n;
+    }
+  }
+  acc[r] = status == DSPARK_ST_OK ? n : 0;
+  bonus[r] = status == DSPARK_ST_OK ? t_am[r * DSPARK_N_TARGET + n] : 0;
+  rst[r] = status;
+}
+
 constexpr int kTkBins = 2048;        // histogram bins of one digit
 constexpr int kTkLevels = 6;         // digits of a 64-bit remainder key
 constexpr int kSqMergeCap = 4096;    // candidates a row's merge may hold (G * k_max)
@@ -88,6 +119,8 @@ struct ShardQArgs {
   double* s64;     // [row] RN64 of the exact sum (dense rows)
   uint32_t* hist;  // [row][kTkBins] the all-reduced first-digit histogram
   uint32_t* cids;  // [row][shard][kSqCandCap] crossing-bin ids, in id order
+  uint64_t* ckeys; // [row][shard][kSqCandCap] and their remainder keys
+  uint32_t* cflo;  // [row][shard][kSqCandCap] and their floor counts
   SqCand* cand;    // [row][shard][k_max]
   // split rows of a fused step: only dense rows are this pipeline's (sparse
   // rows are left to the row kernel, which then writes all their outputs);
@@ -101,6 +134,14 @@ struct ShardQArgs {
   int n_target, Gt;
   int32_t* t_argmax;
   int32_t* t_status;
+  // greedy verification folded in (every row of every request is this
+  // pipeline's): the last of a request's five finishing workgroups verifies it
+  int vfy;
+  const int32_t* v_dtok;  // draft tokens: the argmax or the sample outputs
+  int32_t* v_acc;
+  int32_t* v_bonus;
+  int32_t* v_rst;
+  uint32_t* req_cnt;  // [request] finished draft rows
 };
 
 // (row, shard) workgroups: the shard heads of the draft rows, then (Gt
@@ -118,16 +159,11 @@ __device__ __forceinline__ float sq_value(const ShardQArgs& a, int r, int v) {
   return shard_value<DT>(a.data, a.stride, r, v);
 }
 
-// a wave per row: the merged heads (status, m, argmax; one lane per shard,
-// G <= 64), the row's kind, the checks of its q storage and draw; and a
-// zeroed first-digit histogram.  Waves past the draft rows merge the target
-// rows' heads into their argmax and status.
-__global__ void __launch_bounds__(64) sq_rows_kernel(ShardQArgs a) {
-  const int b = blockIdx.x, g = threadIdx.x;
-  const bool target = b >= a.n_rows;
-  const int r = target ? b - a.n_rows : b;
-  const int G = target ? a.Gt : a.G;
-  const ShardHead* hd = target ? a.heads + (size_t)a.n_rows * a.G + (size_t)r * a.Gt : a.heads + (size_t)r * a.G;
+// The merged head of G <= 64 shard heads (one lane per shard), in every
+// lane of the calling wave: (value desc, id asc) is a total order, so the
+// butterfly leaves the same head everywhere.
+__device__ __forceinline__ void wave_merge_heads(const ShardHead* hd, int G, float* v, int* i, uint32_t* f) {
+  const int g = lane_id();
   float bv = -__builtin_inff();
   int bi = 0x7fffffff;
   uint32_t fl = 0;
@@ -138,7 +174,7 @@ __global__ void __launch_bounds__(64) sq_rows_kernel(ShardQArgs a) {
     fl = h.flags;
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {  // (value desc, id asc) is a total order: every lane ends equal
+  for (int off = 32; off >= 1; off >>= 1) {
     const float ov = __shfl_xor(bv, off);
     const int oi = __shfl_xor(bi, off);
     if (head_better(ov, oi, bv, bi)) {
@@ -147,24 +183,22 @@ __global__ void __launch_bounds__(64) sq_rows_kernel(ShardQArgs a) {
     }
     fl |= (uint32_t)__shfl_xor((int)fl, off);
   }
-  if (target) {
-    if (g == 0) {
-      int st = DSPARK_ST_OK;
-      if (fl & 1u) st = DSPARK_ST_ROW_NAN;
-      else if (fl & 2u) st = DSPARK_ST_ROW_POSINF;
-      else if (bv == -__builtin_inff()) st = DSPARK_ST_ROW_ZERO_MASS;
-      a.t_argmax[r] = st == DSPARK_ST_OK ? bi : 0;
-      a.t_status[r] = st;
-    }
-    return;
-  }
-  for (int i = g; i < kTkBins; i += 64) a.hist[(size_t)r * kTkBins + i] = 0u;
-  if (g != 0) return;
-  const float m = bv;
-  int st = DSPARK_ST_OK;
-  if (fl & 1u) st = DSPARK_ST_ROW_NAN;
-  else if (fl & 2u) st = DSPARK_ST_ROW_POSINF;
-  else if (m == -__builtin_inff()) st = DSPARK_ST_ROW_ZERO_MASS;
+  *v = bv;
+  *i = bi;
+  *f = fl;
+}
+
+__device__ __forceinline__ int head_status(float m, uint32_t fl) {
+  if (fl & 1u) return DSPARK_ST_ROW_NAN;
+  if (fl & 2u) return DSPARK_ST_ROW_POSINF;
+  if (m == -__builtin_inff()) return DSPARK_ST_ROW_ZERO_MASS;
+  return DSPARK_ST_OK;
+}
+
+// The row's state from its merged head: status, m, its kind and the checks
+// of its q storage and draw.
+__device__ __forceinline__ TkRow sq_row_state(const ShardQArgs& a, int r, float m, uint32_t fl) {
+  int st = head_status(m, fl);
   const int k = a.topk ? a.topk[r] : 0;
   const int kcap = a.k_max < a.V ? a.k_max : a.V;
   if (st == DSPARK_ST_OK && (k < 0 || k > kcap || (k == 0 && !a.dense) || (k > 0 && !a.sp_ids)))
@@ -172,36 +206,94 @@ __global__ void __launch_bounds__(64) sq_rows_kernel(ShardQArgs a) {
   if (st == DSPARK_ST_OK && a.draws && a.draws[r] >= kMass) st = DSPARK_ST_DRAW_RANGE;
   TkRow t;
   t.m = m;
-  t.status = st;
+  t.status = (a.dense_only && k != 0) ? kSqNotMine : st;
   t.k = k;
   t.pad = 0;
-  if (a.dense_only && k != 0) t.status = kSqNotMine;
-  a.tkr[r] = t;
-  if (a.argmax && t.status != kSqNotMine) a.argmax[r] = st == DSPARK_ST_OK ? bi : 0;
+  return t;
 }
 
-// (row, shard) workgroups of a dense row: the exact integer sum of the
-// shard's weights RN32(exp(RN32(x - m))), and the weights themselves kept
-// in the row's count storage for the passes that follow
+// (row, shard) workgroups: every shard merges its row's shard heads (m and
+// the row's state); shard 0 publishes the state and the argmax and zeroes
+// the row's first-digit histogram.  Dense rows: the exact integer sum of the
+// shard's weights RN32(exp(RN32(x - m))), and the weights themselves kept in
+// the row's count storage for the passes that follow.  Workgroups past the
+// draft rows' merge the target rows' heads into their argmax and status.
 template <int DT>
 __global__ void __launch_bounds__(kShardBS) sq_sum_kernel(ShardQArgs a) {
   __shared__ Acc s_a[kShardNW];
-  const int r = blockIdx.x / a.G, g = blockIdx.x % a.G;
-  const TkRow t = a.tkr[r];
+  __shared__ TkRow s_t;
+  const int nd = a.n_rows * a.G;
+  const int b = blockIdx.x;
+  if (b >= nd) {  // a target row (uniform)
+    const int r = b - nd;
+    if (threadIdx.x < 64) {
+      float m;
+      int am;
+      uint32_t fl;
+      wave_merge_heads(a.heads + (size_t)nd + (size_t)r * a.Gt, a.Gt, &m, &am, &fl);
+      if (threadIdx.x == 0) {
+        const int st = head_status(m, fl);
+        a.t_argmax[r] = st == DSPARK_ST_OK ? am : 0;
+        a.t_status[r] = st;
+      }
+    }
+    return;
+  }
+  const int r = b / a.G, g = b % a.G;
+  int lo, hi;
+  shard_range(a.V, a.G, g, &lo, &hi);
+  const int i00 = lo + (int)threadIdx.x;
+  float x[kShardU];  // the first loads: they need no m, so they fly during the merge
+#pragma unroll
+  for (int u = 0; u < kShardU; ++u) {
+    const int i = i00 + u * kShardBS;
+    x[u] = i < hi ? sq_value<DT>(a, r, i) : -__builtin_inff();
+  }
+  if (threadIdx.x < 64) {
+    float m;
+    int am;
+    uint32_t fl;
+    wave_merge_heads(a.heads + (size_t)r * a.G, a.G, &m, &am, &fl);
+    if (threadIdx.x == 0) {
+      const TkRow t = sq_row_state(a, r, m, fl);
+      s_t = t;
+      if (g == 0) {
+        a.tkr[r] = t;
+        if (a.argmax && t.status != kSqNotMine) a.argmax[r] = t.status == DSPARK_ST_OK ? am : 0;
+      }
+    }
+  }
+  if (g == 0) {
+    for (int i = threadIdx.x; i < kTkBins; i += kShardBS) a.hist[(size_t)r * kTkBins + i] = 0u;
+    if (a.vfy && r % DSPARK_N_DRAFT == 0 && threadIdx.x == 0) a.req_cnt[r / DSPARK_N_DRAFT] = 0u;
+  }
+  __syncthreads();
+  const TkRow t = s_t;
   Acc acc;
   acc_zero(acc);
   if (t.status == DSPARK_ST_OK && t.k == 0) {
-    int lo, hi;
-    shard_range(a.V, a.G, g, &lo, &hi);
     uint32_t* crow = a.dense + (size_t)r * a.V;
-    for (int i = lo + (int)threadIdx.x; i < hi; i += kShardBS) {
-      const uint32_t wb = __float_as_uint(cr_expf(sq_value<DT>(a, r, i) - t.m));
-      acc_add(acc, wb);
-      crow[i] = wb;
+    for (int i0 = i00; i0 < hi; i0 += kShardU * kShardBS) {
+      if (i0 != i00) {  // later batches (shards above kShardU * kShardBS ids)
+#pragma unroll
+        for (int u = 0; u < kShardU; ++u) {
+          const int i = i0 + u * kShardBS;
+          x[u] = i < hi ? sq_value<DT>(a, r, i) : -__builtin_inff();
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kShardU; ++u) {
+        const int i = i0 + u * kShardBS;
+        if (i < hi) {
+          const uint32_t wb = __float_as_uint(cr_expf(x[u] - t.m));
+          acc_add(acc, wb);
+          crow[i] = wb;
+        }
+      }
     }
   }
   acc = block_acc_total(acc, s_a);
-  if (threadIdx.x == 0) a.sums[blockIdx.x] = acc;
+  if (threadIdx.x == 0) a.sums[b] = acc;
 }
 
 struct SqShared : SmemBase {
@@ -218,6 +310,14 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
   const int r = blockIdx.x / a.G, g = blockIdx.x % a.G;
   const TkRow t = a.tkr[r];
   if (t.status != DSPARK_ST_OK || t.k != 0) return;  // (the same for every thread)
+  int lo, hi;
+  shard_range(a.V, a.G, g, &lo, &hi);
+  const uint32_t* crow = a.dense + (size_t)r * a.V;
+  constexpr int U = 4;  // loads in flight per thread
+  const int v00 = lo + (int)threadIdx.x;
+  uint32_t wb[U];  // the first weights: in flight while S64 is merged
+#pragma unroll
+  for (int u = 0; u < U; ++u) wb[u] = v00 + u * BS < hi ? crow[v00 + u * BS] : 0u;
   for (int b = threadIdx.x; b < kTkBins; b += BS) sh.hist[b] = 0u;
   if (threadIdx.x < 64) {
     Acc s;
@@ -231,18 +331,22 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
   }
   __syncthreads();
   const SumR S = sum_r(sh.s64);
-  int lo, hi;
-  shard_range(a.V, a.G, g, &lo, &hi);
-  const uint32_t* crow = a.dense + (size_t)r * a.V;
   uint64_t fsum = 0, npos = 0;
-  for (int v = lo + (int)threadIdx.x; v < hi; v += BS) {
-    uint32_t c;
-    double rr;
-    floor_rem(__uint_as_float(crow[v]), S, c, rr);
-    fsum += c;
-    if (rr > 0.0) {
-      ++npos;
-      atomicAdd(&sh.hist[rem_key(rr) >> tk_shift(0)], 1u);
+  for (int v0 = v00; v0 < hi; v0 += U * BS) {
+    if (v0 != v00) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) wb[u] = v0 + u * BS < hi ? crow[v0 + u * BS] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t c;
+      double rr;
+      floor_rem(__uint_as_float(wb[u]), S, c, rr);
+      fsum += c;
+      if (rr > 0.0) {
+        ++npos;
+        atomicAdd(&sh.hist[rem_key(rr) >> tk_shift(0)], 1u);
+      }
     }
   }
   fsum = block_sum<uint64_t>(fsum, sh.bs);
@@ -273,8 +377,19 @@ __global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
   uint32_t* crow = a.dense + (size_t)r * a.V;
   TkShard* ts = a.tks + blockIdx.x;
   bool zero = t.status != DSPARK_ST_OK;
+  constexpr int U = 4;  // consecutive ids per thread, loads in flight together
+  const int vt0 = lo + (int)threadIdx.x * U;
+  uint32_t wb[U];
+  double s64 = 0.0;
   int64_t remaining = 0;
   if (!zero) {
+    // everything this shard reads, issued together: its first weights, S64,
+    // the merged histogram and the shards' floor sums
+#pragma unroll
+    for (int u = 0; u < U; ++u) wb[u] = vt0 + u < hi ? crow[vt0 + u] : 0u;
+    s64 = a.s64[r];
+    const uint32_t* hrow = a.hist + (size_t)r * kTkBins;
+    for (int b = threadIdx.x; b < kTkBins; b += BS) sh.hist[b] = hrow[b];
     if (threadIdx.x < 64) {
       uint64_t f = 0, n = 0;
       if ((int)threadIdx.x < a.G) {
@@ -310,35 +425,52 @@ __global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
   int d = kTkBins;  // no bin: nothing above it, nothing inside it
   uint64_t need = 0;
   if (mode == 0) {
-    const uint32_t* hrow = a.hist + (size_t)r * kTkBins;
-    for (int b = threadIdx.x; b < kTkBins; b += BS) sh.hist[b] = hrow[b];
-    __syncthreads();
     uint64_t before;
     d = block_find_crossing(sh.hist, kTkBins, (uint64_t)remaining, false, sh, &before);
     need = (uint64_t)remaining - before;
   }
-  const SumR S = sum_r(a.s64[r]);
+  const SumR S = sum_r(s64);
   uint32_t* cbuf = a.cids + (size_t)blockIdx.x * kSqCandCap;
+  uint64_t* kbuf = a.ckeys + (size_t)blockIdx.x * kSqCandCap;
+  uint32_t* fbuf = a.cflo + (size_t)blockIdx.x * kSqCandCap;
   uint32_t base = 0;
   uint64_t mass = 0;
-  for (int v0 = lo; v0 < hi; v0 += BS) {  // in id order, one id per thread
-    const int v = v0 + (int)threadIdx.x;
-    uint32_t c = 0;
-    int bin = -1;
-    if (v < hi) {
-      double rr;
-      floor_rem(__uint_as_float(crow[v]), S, c, rr);
-      if (rr > 0.0) bin = (int)(rem_key(rr) >> tk_shift(0));
+  for (int v0 = lo; v0 < hi; v0 += U * BS) {  // in id order
+    const int vt = v0 + (int)threadIdx.x * U;
+    if (v0 != lo) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) wb[u] = vt + u < hi ? crow[vt + u] : 0u;
     }
-    const uint32_t in_bin = bin == d ? 1u : 0u;
+    uint32_t c[U], nin = 0;
+    uint64_t key[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      double rr = 0.0;
+      c[u] = 0;
+      if (vt + u < hi) floor_rem(__uint_as_float(wb[u]), S, c[u], rr);
+      key[u] = rr > 0.0 ? rem_key(rr) : 0ull;
+      const int bin = rr > 0.0 ? (int)(key[u] >> tk_shift(0)) : -1;
+      c[u] += bin > d ? 1u : 0u;
+      c[u] |= bin == d ? kSqMark : 0u;
+      nin += bin == d ? 1u : 0u;
+    }
     uint32_t tot;
-    const uint32_t pos = base + block_excl_scan<uint32_t>(in_bin, sh.bs, &tot);
+    uint32_t pos = base + block_excl_scan<uint32_t>(nin, sh.bs, &tot);
     base += tot;
-    if (v < hi) {
-      c += bin > d ? 1u : 0u;
-      if (in_bin && pos < (uint32_t)kSqCandCap) cbuf[pos] = (uint32_t)v;
-      crow[v] = c | (in_bin ? kSqMark : 0u);
-      mass += c;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (vt + u < hi) {
+        if (c[u] & kSqMark) {
+          if (pos < (uint32_t)kSqCandCap) {
+            cbuf[pos] = (uint32_t)(vt + u);
+            kbuf[pos] = key[u];
+            fbuf[pos] = c[u] & ~kSqMark;
+          }
+          ++pos;
+        }
+        crow[vt + u] = c[u];
+        mass += c[u] & ~kSqMark;
+      }
     }
   }
   mass = block_sum<uint64_t>(mass, sh.bs);
@@ -349,11 +481,16 @@ __global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
   }
 }
 
-struct SqResShared : SmemBase {
+struct SqFinShared : SmemBase {
   uint64_t key[kSqCandCap];
   uint32_t id[kSqCandCap];
+  uint32_t flo[kSqCandCap];
   uint32_t off[65];
   uint32_t wins[64];
+  uint32_t mass[64];
+  int gstar;
+  uint32_t rest;
+  int token;
 };
 
 // the shard holding id v
@@ -372,34 +509,20 @@ __device__ __forceinline__ int sq_shard_of(int v, int V, int G) {
   return g;
 }
 
-// one workgroup per dense row: the `need` tickets of the crossing bin go to
-// its largest remainder keys, ties to the lowest id.  Keys are recomputed
-// from the logits (the count row holds the counts by now).  Up to
-// kSqCandCap ids the bin is resolved on chip from the shards' stored ids;
-// beyond that the remaining five digits are found over the flagged ids of
-// the row and the tie cut follows id order.  The shards' masses get the
-// tickets they won.
+// A dense row's workgroup: the `need` tickets of the crossing bin go to its
+// largest remainder keys, ties to the lowest id.  Up to kSqCandCap ids the
+// bin is resolved on chip from the shards' stored ids and keys; beyond that
+// the remaining five digits are found over the flagged ids of the row (keys
+// recomputed from the logits: the count row holds the counts by now) and the
+// tie cut follows id order.  The shards' masses get the tickets they won.
+// Returns the row's status (the same in every thread).
+// Expects sh.off (the shards' candidate offsets) and sh.mass (their masses
+// before the tickets) filled and sh.wins zeroed.
 template <int DT>
-__global__ void __launch_bounds__(BS) sq_resolve_kernel(ShardQArgs a) {
-  __shared__ SqResShared sh;
-  const int r = blockIdx.x;
-  const TkRow t = a.tkr[r];
-  if (t.k != 0 || t.status != DSPARK_ST_OK || !a.dense) return;  // (the same for every thread)
-  const TkCut cut = a.cut[r];
-  if (cut.mode == 2) {
-    if (threadIdx.x == 0) a.tkr[r].status = DSPARK_ST_ALLOC_INCONSISTENT;
-    return;
-  }
-  if (cut.mode == 1) return;
+__device__ int sq_resolve_row(const ShardQArgs& a, int r, const TkRow& t, const TkCut& cut, SqFinShared& sh) {
+  if (cut.mode == 2) return DSPARK_ST_ALLOC_INCONSISTENT;
+  if (cut.mode == 1) return DSPARK_ST_OK;
   const int G = a.G;
-  if (threadIdx.x < 64) {
-    const uint32_t n = (int)threadIdx.x < G ? a.tks[(size_t)r * G + threadIdx.x].ncand : 0u;
-    const uint32_t inc = wave_incl_scan(n);
-    sh.off[threadIdx.x + 1] = inc;
-    if (threadIdx.x == 0) sh.off[0] = 0u;
-    sh.wins[threadIdx.x] = 0u;
-  }
-  __syncthreads();
   const uint32_t n = sh.off[G];
   const uint64_t need0 = cut.need;
   const SumR S = sum_r(a.s64[r]);
@@ -420,9 +543,10 @@ __global__ void __launch_bounds__(BS) sq_resolve_kernel(ShardQArgs a) {
         if (sh.off[mid] <= j) g = mid;
         else gh = mid - 1;
       }
-      const uint32_t id = a.cids[((size_t)r * G + g) * kSqCandCap + (j - sh.off[g])];
-      sh.id[j] = id;
-      sh.key[j] = all ? 0ull : key_of((int)id);
+      const size_t slot = ((size_t)r * G + g) * kSqCandCap + (j - sh.off[g]);
+      sh.id[j] = a.cids[slot];
+      sh.key[j] = a.ckeys[slot];
+      sh.flo[j] = a.cflo[slot];
     }
     __syncthreads();
     for (uint32_t j = threadIdx.x; j < n; j += BS) {
@@ -437,7 +561,7 @@ __global__ void __launch_bounds__(BS) sq_resolve_kernel(ShardQArgs a) {
         win = rank < need0;
       }
       const uint32_t id = sh.id[j];
-      crow[id] = (crow[id] & ~kSqMark) + (win ? 1u : 0u);
+      crow[id] = sh.flo[j] + (win ? 1u : 0u);
       if (win) atomicAdd(&sh.wins[sq_shard_of((int)id, a.V, G)], 1u);
     }
   } else {
@@ -479,7 +603,9 @@ __global__ void __launch_bounds__(BS) sq_resolve_kernel(ShardQArgs a) {
     }
   }
   __syncthreads();
-  if ((int)threadIdx.x < G && sh.wins[threadIdx.x]) a.tks[(size_t)r * G + threadIdx.x].mass += sh.wins[threadIdx.x];
+  if ((int)threadIdx.x < G) sh.mass[threadIdx.x] += sh.wins[threadIdx.x];
+  __syncthreads();
+  return DSPARK_ST_OK;
 }
 
 // (row, shard) workgroups of a sparse row: the shard's local top-k
@@ -577,46 +703,30 @@ __global__ void __launch_bounds__(BS) sq_merge_topk_kernel(ShardQArgs a) {
   }
 }
 
-struct SqSampleShared {
-  BlockScratch bs;
-  uint32_t mass[64];
-  int gstar;
-  uint32_t rest;
-  int token;
-};
-
-// one workgroup per row: the leader's draw picks the shard by count mass,
-// then the token inside it
-__global__ void __launch_bounds__(BS) sq_sample_kernel(ShardQArgs a) {
-  __shared__ SqSampleShared sh;
-  const int r = blockIdx.x;
-  const TkRow t = a.tkr[r];
-  if (t.status != DSPARK_ST_OK) return;  // (the same for every thread)
+// The row's workgroup: the leader's draw picks the shard by count mass, then
+// the token inside it.  Returns the row's status (the same in every thread).
+__device__ int sq_sample_row(const ShardQArgs& a, int r, const TkRow& t, SqFinShared& sh) {
   const uint32_t u = a.draws[r];
   const bool dense_row = t.k == 0;
   const int len = dense_row ? 0 : a.sp_len[r];
-  if (threadIdx.x < 64) sh.mass[threadIdx.x] = 0u;
-  __syncthreads();
-  if (dense_row) {
-    if (threadIdx.x < a.G) sh.mass[threadIdx.x] = (uint32_t)a.tks[(size_t)r * a.G + threadIdx.x].mass;
-  } else {
+  if (!dense_row) {  // (a dense row's shard masses are in sh.mass already)
+    if (threadIdx.x < 64) sh.mass[threadIdx.x] = 0u;
+    __syncthreads();
     for (int j = threadIdx.x; j < len; j += BS)
       atomicAdd(&sh.mass[sq_shard_of(a.sp_ids[(size_t)r * a.k_max + j], a.V, a.G)],
                 a.sp_cnt[(size_t)r * a.k_max + j]);
+    __syncthreads();
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t before = 0;
-    sh.gstar = -1;
-    sh.token = -1;
-    for (int g = 0; g < a.G; ++g) {
-      if (u < before + sh.mass[g]) {
-        sh.gstar = g;
-        sh.rest = u - before;
-        break;
-      }
-      before += sh.mass[g];
+  if (threadIdx.x < 64) {  // the first shard whose cumulative mass exceeds u (G <= 64 lanes)
+    const uint32_t mg = (int)threadIdx.x < a.G ? sh.mass[threadIdx.x] : 0u;
+    const uint32_t inc = wave_incl_scan(mg);
+    const uint64_t hit = __ballot((int)threadIdx.x < a.G && u < inc);
+    const int gs = hit ? __builtin_ctzll(hit) : -1;
+    if (threadIdx.x == 0) {
+      sh.gstar = gs;
+      sh.token = -1;
     }
+    if ((int)threadIdx.x == gs) sh.rest = u - (inc - mg);
   }
   __syncthreads();
   const int gs = sh.gstar;
@@ -645,26 +755,57 @@ __global__ void __launch_bounds__(BS) sq_sample_kernel(ShardQArgs a) {
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    if (sh.token < 0) a.tkr[r].status = DSPARK_ST_ALLOC_INCONSISTENT;
-    else a.sample[r] = sh.token;
-  }
+  if (sh.token < 0) return DSPARK_ST_ALLOC_INCONSISTENT;
+  if (threadIdx.x == 0) a.sample[r] = sh.token;
+  return DSPARK_ST_OK;
 }
 
-// one thread per row: final statuses, and zeros for refused rows
-__global__ void sq_out_kernel(ShardQArgs a) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= a.n_rows) return;
+// one workgroup per row: a dense row's tickets, the sample, the final status
+// and zeros for refused rows
+template <int DT>
+__global__ void __launch_bounds__(BS) sq_finish_kernel(ShardQArgs a) {
+  __shared__ SqFinShared sh;
+  const int r = blockIdx.x;
   const TkRow t = a.tkr[r];
-  if (t.status == kSqNotMine) return;
-  a.row_status[r] = t.status;
-  if (t.status != DSPARK_ST_OK) {
-    if (a.argmax) a.argmax[r] = 0;
-    if (a.sample) a.sample[r] = 0;
-    if (a.conf) a.conf[r] = 0.0f;
-    if (t.k != 0 && a.sp_len) a.sp_len[r] = 0;
-  } else if (a.conf && t.k == 0) {
-    a.conf[r] = (float)(1.0 / a.s64[r]);
+  if (t.status == kSqNotMine) return;  // (the same for every thread)
+  int st = t.status;
+  if (st == DSPARK_ST_OK && t.k == 0 && a.dense) {
+    const TkCut cut = a.cut[r];
+    if (threadIdx.x < 64) {  // the shards' candidate offsets and masses
+      const int g = threadIdx.x;
+      uint32_t n = 0, ms = 0;
+      if (g < a.G) {
+        const TkShard ts = a.tks[(size_t)r * a.G + g];
+        n = ts.ncand;
+        ms = (uint32_t)ts.mass;
+      }
+      sh.off[g + 1] = wave_incl_scan(n);
+      if (g == 0) sh.off[0] = 0u;
+      sh.mass[g] = ms;
+      sh.wins[g] = 0u;
+    }
+    __syncthreads();
+    st = sq_resolve_row<DT>(a, r, t, cut, sh);
+  }
+  if (st == DSPARK_ST_OK && a.draws) st = sq_sample_row(a, r, t, sh);
+  if (threadIdx.x == 0) {
+    a.row_status[r] = st;
+    if (st != DSPARK_ST_OK) {
+      if (a.argmax) a.argmax[r] = 0;
+      if (a.sample) a.sample[r] = 0;
+      if (a.conf) a.conf[r] = 0.0f;
+      if (t.k != 0 && a.sp_len) a.sp_len[r] = 0;
+    } else if (a.conf && t.k == 0) {
+      a.conf[r] = (float)(1.0 / a.s64[r]);
+    }
+    if (a.vfy) {  // the request's last finishing row verifies it (its rows' outputs published first)
+      const int q = r / DSPARK_N_DRAFT;
+      __threadfence();
+      if (atomicAdd(&a.req_cnt[q], 1u) == DSPARK_N_DRAFT - 1) {
+        __threadfence();
+        verify_request(q, a.V, a.v_dtok, a.row_status, a.t_argmax, a.t_status, a.v_acc, a.v_bonus, a.v_rst);
+      }
+    }
   }
 }
 
