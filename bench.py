@@ -422,6 +422,9 @@ def main():
                     help="also time the step captured as one HIP graph (default); the faster launch mode is "
                          "the reported step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads measured after the main one and reported under 'also' "
+                         "(default: 4 when --config is 5; an empty string for none)")
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
     ap.add_argument("--op", choices=["step", "wire", "stochastic", "ratio", "sharded"], default="step",
                     help="step: the fused propose/q/sample/verify step; wire: the receiver's check of the "
@@ -450,13 +453,33 @@ def main():
         sharded_bench(args)
         return
 
+    res, w = step_line(args.config, args)
+    also = [4] if args.also is None and args.config == 5 else [int(c) for c in (args.also or "").split(",") if c]
+    if also:
+        # the other configuration the bandwidth bar applies to, measured in the same run
+        res["also"] = {}
+        for c in also:
+            r, _ = step_line(c, args)
+            res["also"][r["config"]["workload"]] = {
+                "ms_per_step": r["ms_per_step"], "rows_per_s": r["value"], "launch": r["config"]["launch"],
+                "frac": r["roofline"]["frac"], "achieved": r["roofline"]["achieved"],
+                "algorithmic_bytes": r["roofline"]["algorithmic_bytes"], "kernel_ms": r["roofline"]["kernel_ms"],
+                "traffic": r["roofline"]["traffic"], "rows_failed": r["config"]["rows_failed"]}
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def step_line(cfg: int, args):
+    """The bench line of one workload's fused step (without the CPU baseline),
+    and the workload."""
     import numpy as np
     import torch
 
     from vocab_wide_draft_amd import binding as B
     from vocab_wide_draft_amd import workloads as W
 
-    w = W.make(args.config)
+    w = W.make(cfg)
     dev = torch.device("cuda:0")
 
     def up(a):
@@ -522,9 +545,9 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name),
                      "algorithmic_bytes": alg, "kernel_ms": round(mean_launch, 4)},
     }
-    if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+    return res, w
+
+
 
 
 if __name__ == "__main__":

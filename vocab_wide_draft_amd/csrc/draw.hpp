@@ -345,22 +345,65 @@ struct StreamSrc {
   static constexpr int E = Row<DT>::EPV;
   __device__ int vec(int ch) const { return (wave_id() * cpw + ch) * 64 + lane_id(); }
 };
-// One chunk of a lane: its E logits and, for residual sums over a dense q,
-// their E counts, all loaded before any is used (counts past V read 0).
+// One chunk of a lane: its E logits (bf16: the raw patterns, two per word;
+// past V: -inf) and, for residual sums over a dense q, their E counts, all
+// loaded before any is used (counts past V read 0).
 template <int DT>
 struct ChunkData {
-  float x[StreamSrc<DT>::E];
-  uint32_t cnt[StreamSrc<DT>::E];
+  static constexpr int E = StreamSrc<DT>::E;
+  static constexpr int NW_ = DT == DSPARK_BF16 ? E / 2 : E;
+  uint32_t w[NW_];
+  uint32_t cnt[E];
+  // weight-relevant bits of element e: the bf16 pattern, or the binary32 bits
+  __device__ __forceinline__ uint32_t bits(int e) const {
+    if constexpr (DT == DSPARK_BF16) return (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
+    else return w[e];
+  }
 };
+template <int DT>
+__device__ __forceinline__ void chunk_load_values(const Row<DT>& row, int q, ChunkData<DT>& d) {
+  constexpr int E = StreamSrc<DT>::E;
+  const int base = q * E;
+  const int nv = row.V - base < E ? row.V - base : E;
+  if (nv == E) {
+    const uint4 u = reinterpret_cast<const uint4*>(row.p)[q];
+    const uint32_t v[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < ChunkData<DT>::NW_; ++i) d.w[i] = v[i];
+  } else if constexpr (DT == DSPARK_BF16) {
+    const uint16_t* s = static_cast<const uint16_t*>(row.p);
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+      const uint32_t lo = 2 * i < nv ? (uint32_t)s[base + 2 * i] : 0xff80u;
+      const uint32_t hi = 2 * i + 1 < nv ? (uint32_t)s[base + 2 * i + 1] : 0xff80u;
+      d.w[i] = lo | (hi << 16);
+    }
+  } else {
+    const uint32_t* s = static_cast<const uint32_t*>(row.p);
+#pragma unroll
+    for (int i = 0; i < E; ++i) d.w[i] = i < nv ? s[base + i] : 0xff800000u;
+  }
+}
 template <int mode, int DT>
 __device__ __forceinline__ void stream_load(const StreamSrc<DT>& s, int ch, const DrawCtx& c,
-                                            __amdgpu_buffer_rsrc_t crs, ChunkData<DT>& d) {
+                                            __amdgpu_buffer_rsrc_t crs, bool c16, ChunkData<DT>& d) {
   constexpr int E = StreamSrc<DT>::E;
   const int q = s.vec(ch);
-  s.row.load(q, d.x);
+  chunk_load_values<DT>(s.row, q, d);
   if (mode != kDrawPlain && c.dense) {
+    if (c16) {  // a 16-byte aligned count row: E / 4 vector loads
 #pragma unroll
-    for (int e = 0; e < E; ++e) d.cnt[e] = __builtin_amdgcn_raw_buffer_load_b32(crs, (q * E + e) * 4, 0, 0);
+      for (int h = 0; h < E / 4; ++h) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(crs, (q * E + 4 * h) * 4, 0, 0);
+        d.cnt[4 * h] = v.x;
+        d.cnt[4 * h + 1] = v.y;
+        d.cnt[4 * h + 2] = v.z;
+        d.cnt[4 * h + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) d.cnt[e] = __builtin_amdgcn_raw_buffer_load_b32(crs, (q * E + e) * 4, 0, 0);
+    }
   }
 }
 // buffer over a dense q row (reads past V give 0)
@@ -369,8 +412,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t count_rsrc(const DrawCtx& c) {
                                            0x00020000);
 }
 template <int DT>
-__device__ __forceinline__ uint32_t chunk_weight_bits(float x, const DrawCtx& c, const DrawShared& sh) {
-  return DT == DSPARK_BF16 ? bf16_weight_bits(__float_as_uint(x) >> 16, c, sh) : __float_as_uint(cr_expf(x - c.m));
+__device__ __forceinline__ uint32_t chunk_weight_bits(uint32_t b, const DrawCtx& c, const DrawShared& sh) {
+  return DT == DSPARK_BF16 ? bf16_weight_bits(b, c, sh) : __float_as_uint(cr_expf(__uint_as_float(b) - c.m));
 }
 template <int mode, int DT>
 __device__ __forceinline__ void stream_add(const ChunkData<DT>& d, int q, const DrawCtx& c, const DrawShared& sh,
@@ -378,7 +421,7 @@ __device__ __forceinline__ void stream_add(const ChunkData<DT>& d, int q, const 
   constexpr int E = StreamSrc<DT>::E;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const uint32_t wb = chunk_weight_bits<DT>(d.x[e], c, sh);
+    const uint32_t wb = chunk_weight_bits<DT>(d.bits(e), c, sh);
     if (mode == kDrawPlain) {
       acc_add(s1, wb);
     } else if ((wb & 0x7fffffffu) != 0u) {
@@ -390,18 +433,26 @@ __device__ __forceinline__ void stream_add(const ChunkData<DT>& d, int q, const 
     }
   }
 }
-// this lane's sums over every chunk of its wave, the next chunk's loads in
-// flight while one is added
+// this lane's sums over every chunk of its wave, DrawPF<mode>::n chunks' loads in
+// flight together (fewer for residual sums, whose chunks carry counts)
+template <int mode>
+struct DrawPF {
+  static constexpr int n = mode == kDrawPlain ? 4 : 2;
+};
 template <int mode, int DT>
 __device__ __forceinline__ void stream_sums(const StreamSrc<DT>& s, const DrawCtx& c, const DrawShared& sh, Acc& s1,
                                             uint64_t& s2) {
   const __amdgpu_buffer_rsrc_t crs = count_rsrc(c);
-  ChunkData<DT> cur, nxt;
-  stream_load<mode, DT>(s, 0, c, crs, cur);
-  for (int ch = 0; ch < s.cpw; ++ch) {
-    if (ch + 1 < s.cpw) stream_load<mode, DT>(s, ch + 1, c, crs, nxt);
-    stream_add<mode, DT>(cur, s.vec(ch), c, sh, s1, s2);
-    cur = nxt;
+  const bool c16 = (reinterpret_cast<uintptr_t>(c.dense) & 15u) == 0u;
+  constexpr int PF = DrawPF<mode>::n;
+  for (int ch0 = 0; ch0 < s.cpw; ch0 += PF) {
+    ChunkData<DT> d[PF];
+#pragma unroll
+    for (int k = 0; k < PF; ++k)
+      if (ch0 + k < s.cpw) stream_load<mode, DT>(s, ch0 + k, c, crs, c16, d[k]);
+#pragma unroll
+    for (int k = 0; k < PF; ++k)
+      if (ch0 + k < s.cpw) stream_add<mode, DT>(d[k], s.vec(ch0 + k), c, sh, s1, s2);
   }
 }
 
@@ -479,32 +530,40 @@ __device__ __forceinline__ int stream_walk(const StreamSrc<DT>& s, const DrawCtx
   if (wave_id() == sh.wstar) {
     constexpr int E = StreamSrc<DT>::E;
     const __amdgpu_buffer_rsrc_t crs = count_rsrc(c);
+    const bool c16 = (reinterpret_cast<uintptr_t>(c.dense) & 15u) == 0u;
     U256 t = sh.rest;
     int ich = -1;
     Acc cs1;
     uint64_t cs2 = 0;
     acc_zero(cs1);
-    ChunkData<DT> cur, nxt, hit;
-    stream_load<mode, DT>(s, 0, c, crs, cur);
-    for (int ch = 0; ch < s.cpw && ich < 0; ++ch) {
-      if (ch + 1 < s.cpw) stream_load<mode, DT>(s, ch + 1, c, crs, nxt);
-      Acc a;
-      acc_zero(a);
-      uint64_t b = 0;
-      stream_add<mode, DT>(cur, s.vec(ch), c, sh, a, b);
-      Acc ta;
-      uint64_t tb;
-      wave_total(a, b, &ta, &tb);
-      const U256 wc = group_weight<mode>(ta, tb, c);
-      if (u256_lt(t, wc)) {
-        ich = ch;
-        cs1 = a;
-        cs2 = b;
-        hit = cur;
-      } else {
-        t = u256_sub(t, wc);
+    ChunkData<DT> hit;
+    constexpr int PF = DrawPF<mode>::n;
+    for (int ch0 = 0; ch0 < s.cpw && ich < 0; ch0 += PF) {  // PF chunks' loads in flight together
+      ChunkData<DT> d[PF];
+#pragma unroll
+      for (int k = 0; k < PF; ++k)
+        if (ch0 + k < s.cpw) stream_load<mode, DT>(s, ch0 + k, c, crs, c16, d[k]);
+#pragma unroll
+      for (int k = 0; k < PF; ++k) {
+        if (ch0 + k < s.cpw && ich < 0) {  // (wave-uniform)
+          Acc a;
+          acc_zero(a);
+          uint64_t b = 0;
+          stream_add<mode, DT>(d[k], s.vec(ch0 + k), c, sh, a, b);
+          Acc ta;
+          uint64_t tb;
+          wave_total(a, b, &ta, &tb);
+          const U256 wc = group_weight<mode>(ta, tb, c);
+          if (u256_lt(t, wc)) {
+            ich = ch0 + k;
+            cs1 = a;
+            cs2 = b;
+            hit = d[k];
+          } else {
+            t = u256_sub(t, wc);
+          }
+        }
       }
-      cur = nxt;
     }
     U256 lr;
     const int l = draw_find_lane<mode>(cs1, cs2, c, t, &lr);
@@ -515,7 +574,7 @@ __device__ __forceinline__ int stream_walk(const StreamSrc<DT>& s, const DrawCtx
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         if (tok < 0) {
-          const uint32_t wb = chunk_weight_bits<DT>(hit.x[e], c, sh);
+          const uint32_t wb = chunk_weight_bits<DT>(hit.bits(e), c, sh);
           // ids past V carry weight 0 and have no count
           uint32_t cnt = 0u;
           if (mode != kDrawPlain && (wb & 0x7fffffffu) != 0u)
