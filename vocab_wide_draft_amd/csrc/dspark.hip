@@ -825,7 +825,7 @@ namespace {
 // Workspace of the sharded q: the per-shard results the ranks would exchange
 // and the per-row merged state, each section 256-byte aligned.
 struct SqLayout {
-  size_t heads, sums, tks, tkr, cut, s64, req, hist, cids, ckeys, cflo, cand, total;
+  size_t heads, sums, tks, tkr, cut, s64, req, hist, cids, ckeys, cflo, cmass, cand, total;
 };
 SqLayout sq_layout(int64_t n_rows, int32_t G, int32_t k_max) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -843,7 +843,8 @@ SqLayout sq_layout(int64_t n_rows, int32_t G, int32_t k_max) {
   L.cids = up(L.hist + (size_t)n_rows * kTkBins * sizeof(uint32_t));
   L.ckeys = up(L.cids + nb * kSqCandCap * sizeof(uint32_t));
   L.cflo = up(L.ckeys + nb * kSqCandCap * sizeof(uint64_t));
-  L.cand = up(L.cflo + nb * kSqCandCap * sizeof(uint32_t));
+  L.cmass = up(L.cflo + nb * kSqCandCap * sizeof(uint32_t));
+  L.cand = up(L.cmass + nb * kSqMaxChunks * sizeof(uint32_t));
   L.total = up(L.cand + nb * (size_t)(k_max > 0 ? k_max : 0) * sizeof(SqCand));
   return L;
 }
@@ -1014,6 +1015,7 @@ int launch_rows(RowsArgs a, int dtype, void* stream, void* ws = nullptr, size_t 
     q.cids = reinterpret_cast<uint32_t*>(w + L.cids);
     q.ckeys = reinterpret_cast<uint64_t*>(w + L.ckeys);
     q.cflo = reinterpret_cast<uint32_t*>(w + L.cflo);
+    q.cmass = reinterpret_cast<uint32_t*>(w + L.cmass);
     const bool all_rows = gt >= 1 && !a.topk;  // every row taken: all draft rows dense, targets too
     if (all_rows && verified && a.v_dtok) {
       q.vfy = 1;
@@ -1476,6 +1478,7 @@ int dspark_sharded_q(const dspark_rows* rows, int32_t n_shards, const dspark_q* 
   a.cids = reinterpret_cast<uint32_t*>(w + L.cids);
   a.ckeys = reinterpret_cast<uint64_t*>(w + L.ckeys);
   a.cflo = reinterpret_cast<uint32_t*>(w + L.cflo);
+  a.cmass = reinterpret_cast<uint32_t*>(w + L.cmass);
   a.cand = reinterpret_cast<SqCand*>(w + L.cand);
   if (rows->dtype == DSPARK_BF16) launch_sharded_q<DSPARK_BF16>(a, sparse, stream);
   else launch_sharded_q<DSPARK_F32>(a, sparse, stream);

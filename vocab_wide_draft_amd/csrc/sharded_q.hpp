@@ -68,6 +68,8 @@ constexpr int kTkLevels = 6;         // digits of a 64-bit remainder key
 constexpr int kSqMergeCap = 4096;    // candidates a row's merge may hold (G * k_max)
 constexpr int kSqCandCap = 1024;     // crossing-bin ids a row resolves on chip (and a shard stores)
 constexpr uint32_t kSqMark = 0x80000000u;  // count-row flag: in the crossing bin, not yet resolved
+constexpr int kSqChunk = 4096;             // ids per chunk of the cand pass (4 per thread)
+constexpr int kSqMaxChunks = DSPARK_V_MAX / kSqChunk;  // chunks a shard can have
 
 __host__ __device__ constexpr int tk_shift(int l) { return l < 5 ? 53 - 11 * l : 0; }
 __host__ __device__ constexpr int tk_bins(int l) { return l < 5 ? 2048 : 512; }
@@ -121,6 +123,7 @@ struct ShardQArgs {
   uint32_t* cids;  // [row][shard][kSqCandCap] crossing-bin ids, in id order
   uint64_t* ckeys; // [row][shard][kSqCandCap] and their remainder keys
   uint32_t* cflo;  // [row][shard][kSqCandCap] and their floor counts
+  uint32_t* cmass; // [row][shard][kSqMaxChunks] count mass of each chunk before the tickets of the bin
   SqCand* cand;    // [row][shard][k_max]
   // split rows of a fused step: only dense rows are this pipeline's (sparse
   // rows are left to the row kernel, which then writes all their outputs);
@@ -454,9 +457,15 @@ __global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
       c[u] |= bin == d ? kSqMark : 0u;
       nin += bin == d ? 1u : 0u;
     }
-    uint32_t tot;
-    uint32_t pos = base + block_excl_scan<uint32_t>(nin, sh.bs, &tot);
-    base += tot;
+    uint32_t tmass = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) tmass += c[u] & ~kSqMark;
+    // one scan gives the candidates' positions (low word) and the chunk's mass (high word)
+    uint64_t tot;
+    uint32_t pos = base + (uint32_t)block_excl_scan<uint64_t>(((uint64_t)tmass << 32) | nin, sh.bs, &tot);
+    base += (uint32_t)tot;
+    mass += tot >> 32;
+    if (threadIdx.x == 0) a.cmass[(size_t)blockIdx.x * kSqMaxChunks + (v0 - lo) / kSqChunk] = (uint32_t)(tot >> 32);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (vt + u < hi) {
@@ -469,11 +478,9 @@ __global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
           ++pos;
         }
         crow[vt + u] = c[u];
-        mass += c[u] & ~kSqMark;
       }
     }
   }
-  mass = block_sum<uint64_t>(mass, sh.bs);
   if (threadIdx.x == 0) {
     ts->mass = mass;
     ts->ncand = base;
@@ -485,6 +492,11 @@ struct SqFinShared : SmemBase {
   uint64_t key[kSqCandCap];
   uint32_t id[kSqCandCap];
   uint32_t flo[kSqCandCap];
+  uint32_t won[kSqCandCap];           // the bin's ticket winners (on-chip resolution)
+  uint32_t cm[kSqMaxChunks];          // the sampled shard's chunk masses
+  int general;                        // the bin was resolved over the row's flagged ids
+  int cstar;
+  uint32_t crest;
   uint32_t off[65];
   uint32_t wins[64];
   uint32_t mass[64];
@@ -534,6 +546,7 @@ __device__ int sq_resolve_row(const ShardQArgs& a, int r, const TkRow& t, const 
     floor_rem(cr_expf(sq_value<DT>(a, r, v) - m), S, c, rr);
     return rem_key(rr);
   };
+  if (threadIdx.x == 0) sh.general = n > (uint32_t)kSqCandCap ? 1 : 0;  // (read after later barriers)
   if (n <= (uint32_t)kSqCandCap) {
     const bool all = need0 == (uint64_t)n;  // the whole bin wins
     for (uint32_t j = threadIdx.x; j < n; j += BS) {
@@ -562,6 +575,7 @@ __device__ int sq_resolve_row(const ShardQArgs& a, int r, const TkRow& t, const 
       }
       const uint32_t id = sh.id[j];
       crow[id] = sh.flo[j] + (win ? 1u : 0u);
+      sh.won[j] = win ? 1u : 0u;
       if (win) atomicAdd(&sh.wins[sq_shard_of((int)id, a.V, G)], 1u);
     }
   } else {
@@ -734,7 +748,48 @@ __device__ int sq_sample_row(const ShardQArgs& a, int r, const TkRow& t, SqFinSh
   if (gs >= 0) {
     int lo, hi;
     shard_range(a.V, a.G, gs, &lo, &hi);
-    if (dense_row) {
+    if (dense_row && !sh.general) {
+      // the shard's chunk masses (stored by the cand pass) plus the bin's
+      // winners in them give the chunk; only that chunk's counts are read
+      const uint32_t* crow = a.dense + (size_t)r * a.V;
+      const int nch = (hi - lo + kSqChunk - 1) / kSqChunk;
+      for (int ci = threadIdx.x; ci < nch; ci += BS) sh.cm[ci] = a.cmass[((size_t)r * a.G + gs) * kSqMaxChunks + ci];
+      if (threadIdx.x == 0) sh.cstar = -1;
+      __syncthreads();
+      const uint32_t o = sh.off[gs], ng = sh.off[gs + 1] - o;  // the bin's ids in this shard, resolved on chip
+      for (uint32_t j = threadIdx.x; j < ng; j += BS)
+        if (sh.won[o + j]) atomicAdd(&sh.cm[(int)(sh.id[o + j] - (uint32_t)lo) / kSqChunk], 1u);
+      __syncthreads();
+      const uint32_t mc = (int)threadIdx.x < nch ? sh.cm[threadIdx.x] : 0u;  // nch <= kSqMaxChunks < BS
+      uint32_t tot;
+      const uint32_t pre = block_excl_scan<uint32_t>(mc, sh.bs, &tot);
+      if (mc && pre <= rest && rest < pre + mc) {
+        sh.cstar = (int)threadIdx.x;
+        sh.crest = rest - pre;
+      }
+      __syncthreads();
+      const int cs = sh.cstar;
+      if (cs >= 0) {
+        const uint32_t cr = sh.crest;
+        const int vt = lo + cs * kSqChunk + 4 * (int)threadIdx.x;  // four consecutive ids per thread
+        uint32_t cc[4], ts = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          cc[u] = vt + u < hi ? crow[vt + u] : 0u;
+          ts += cc[u];
+        }
+        uint32_t run = block_excl_scan<uint32_t>(ts, sh.bs, &tot);
+        if (run <= cr && cr < run + ts) {
+          int tk = -1;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (tk < 0 && cr < run + cc[u]) tk = vt + u;
+            run += cc[u];
+          }
+          sh.token = tk;
+        }
+      }
+    } else if (dense_row) {  // (after a resolution over the row's flagged ids) the shard in id order
       const uint32_t* crow = a.dense + (size_t)r * a.V;
       uint32_t run = 0;
       for (int v0 = lo; v0 < hi; v0 += BS) {  // ids in order, one per thread
@@ -780,7 +835,10 @@ __global__ void __launch_bounds__(BS) sq_finish_kernel(ShardQArgs a) {
         ms = (uint32_t)ts.mass;
       }
       sh.off[g + 1] = wave_incl_scan(n);
-      if (g == 0) sh.off[0] = 0u;
+      if (g == 0) {
+        sh.off[0] = 0u;
+        sh.general = 0;
+      }
       sh.mass[g] = ms;
       sh.wins[g] = 0u;
     }
