@@ -260,14 +260,32 @@ __device__ __forceinline__ uint64_t rem_key(double r) {
 // ------------------------------------------- correctly rounded exp, binary32
 #include "exp_table.inc"
 
+// The binary32 rounding of a binary64 value tv > 0 known to within 2^-51 of
+// x (relatively), when that decides RN32(x): tv farther than 2^-48 tv from
+// the binary32 rounding midpoint on its side.  Returns false otherwise.
+__device__ __forceinline__ bool rn32_decided(double tv, float* out) {
+  const float f = (float)tv;
+  const double g = (double)f;
+  *out = f;
+  if (g == tv) return true;
+  const uint32_t fb = __float_as_uint(f);
+  const float nb = __uint_as_float(tv > g ? fb + 1u : (fb ? fb - 1u : 0u));
+  return __builtin_fabs(tv - 0.5 * (g + (double)nb)) > 0x1p-48 * tv;
+}
+
 // RN32(exp(d)) for binary32 d <= 0 (or -inf).  Tang's table method in
 // binary64: d = (64 e + j) ln2/64 + r with |r| <= ln2/128, exp(d) =
-// 2^e 2^(j/64) exp(r); 2^(j/64) is a double-double table entry, exp(r) - 1 a
-// degree-7 Taylor polynomial (truncation < 2^-74).  The product is kept as an
-// unevaluated pair H + L (relative error about 2^-70) and rounded to binary32
-// once; when the binary64 sum lands within 2^-48 of a binary32 rounding
-// midpoint, the side is decided from H and L exactly.  The function is checked
-// against an independent evaluation for every binary32 d in [-104, 0].
+// 2^e 2^(j/64) exp(r).  A first evaluation takes 2^(j/64) rounded to
+// binary64 and a degree-5 Taylor polynomial for exp(r) - 1 (truncation below
+// 2^-54.4): its relative error is below 2.4 * 2^-53 (the table entry and the
+// last fused multiply-add 2^-53 each, the reduced argument 2^-60.4), so its
+// binary32 rounding is the answer unless it lies within 2^-48 of a rounding
+// midpoint.  Those rare inputs take the accurate evaluation: a double-double
+// table entry, a degree-7 polynomial (truncation < 2^-74), and the product
+// kept as an unevaluated pair H + L (relative error about 2^-70), rounded to
+// binary32 once, with the side of a midpoint within 2^-48 decided from H and
+// L exactly.  The function is checked against an independent evaluation for
+// every binary32 d in [-104, 0].
 __device__ __forceinline__ float cr_expf(float d) {
   if (!(d > -104.0f)) return 0.0f;  // exp(-104) < 2^-150 rounds to 0; also -inf
   if (d == 0.0f) return 1.0f;
@@ -279,6 +297,15 @@ __device__ __forceinline__ float cr_expf(float d) {
   const double rhi = __builtin_fma(-kf, kExpCHi, dd);  // exact: k*C_HI is exact and close to d
   const double t = kf * kExpCLo;
   const double r1 = rhi - t;
+  {
+    double Q = __builtin_fma(r1, kExpP5, kExpP4);
+    Q = __builtin_fma(r1, Q, kExpP3);
+    Q = __builtin_fma(r1, Q, kExpP2);
+    const double q = __builtin_fma(r1 * r1, Q, r1);  // exp(r) - 1
+    const double T = kExpTabHi[j];
+    float f;
+    if (rn32_decided(__builtin_ldexp(__builtin_fma(T, q, T), e), &f)) return f;
+  }
   const double r2 = (rhi - r1) - t;  // r1 + r2 = rhi - t to ~2^-100
   double P = __builtin_fma(r1, kExpP7, kExpP6);
   P = __builtin_fma(r1, P, kExpP5);
