@@ -200,13 +200,13 @@ __device__ __forceinline__ int head_status(float m, uint32_t fl) {
 
 // The row's state from its merged head: status, m, its kind and the checks
 // of its q storage and draw.
-__device__ __forceinline__ TkRow sq_row_state(const ShardQArgs& a, int r, float m, uint32_t fl) {
+// k and u are the row's top-k and draw (read by the caller ahead of the merge).
+__device__ __forceinline__ TkRow sq_row_state(const ShardQArgs& a, float m, uint32_t fl, int k, uint32_t u) {
   int st = head_status(m, fl);
-  const int k = a.topk ? a.topk[r] : 0;
   const int kcap = a.k_max < a.V ? a.k_max : a.V;
   if (st == DSPARK_ST_OK && (k < 0 || k > kcap || (k == 0 && !a.dense) || (k > 0 && !a.sp_ids)))
     st = DSPARK_ST_BAD_TOPK;
-  if (st == DSPARK_ST_OK && a.draws && a.draws[r] >= kMass) st = DSPARK_ST_DRAW_RANGE;
+  if (st == DSPARK_ST_OK && a.draws && u >= kMass) st = DSPARK_ST_DRAW_RANGE;
   TkRow t;
   t.m = m;
   t.status = (a.dense_only && k != 0) ? kSqNotMine : st;
@@ -253,12 +253,14 @@ __global__ void __launch_bounds__(kShardBS) sq_sum_kernel(ShardQArgs a) {
     x[u] = i < hi ? sq_value<DT>(a, r, i) : -__builtin_inff();
   }
   if (threadIdx.x < 64) {
+    const int k = a.topk ? a.topk[r] : 0;  // (loads in flight with the heads')
+    const uint32_t u = a.draws ? a.draws[r] : 0u;
     float m;
     int am;
     uint32_t fl;
     wave_merge_heads(a.heads + (size_t)r * a.G, a.G, &m, &am, &fl);
     if (threadIdx.x == 0) {
-      const TkRow t = sq_row_state(a, r, m, fl);
+      const TkRow t = sq_row_state(a, m, fl, k, u);
       s_t = t;
       if (g == 0) {
         a.tkr[r] = t;
@@ -531,13 +533,14 @@ __device__ __forceinline__ int sq_shard_of(int v, int V, int G) {
 // Expects sh.off (the shards' candidate offsets) and sh.mass (their masses
 // before the tickets) filled and sh.wins zeroed.
 template <int DT>
-__device__ int sq_resolve_row(const ShardQArgs& a, int r, const TkRow& t, const TkCut& cut, SqFinShared& sh) {
+__device__ int sq_resolve_row(const ShardQArgs& a, int r, const TkRow& t, const TkCut& cut, double s64,
+                              SqFinShared& sh) {
   if (cut.mode == 2) return DSPARK_ST_ALLOC_INCONSISTENT;
   if (cut.mode == 1) return DSPARK_ST_OK;
   const int G = a.G;
   const uint32_t n = sh.off[G];
   const uint64_t need0 = cut.need;
-  const SumR S = sum_r(a.s64[r]);
+  const SumR S = sum_r(s64);
   const float m = t.m;
   uint32_t* crow = a.dense + (size_t)r * a.V;
   auto key_of = [&](int v) {
@@ -719,8 +722,7 @@ __global__ void __launch_bounds__(BS) sq_merge_topk_kernel(ShardQArgs a) {
 
 // The row's workgroup: the leader's draw picks the shard by count mass, then
 // the token inside it.  Returns the row's status (the same in every thread).
-__device__ int sq_sample_row(const ShardQArgs& a, int r, const TkRow& t, SqFinShared& sh) {
-  const uint32_t u = a.draws[r];
+__device__ int sq_sample_row(const ShardQArgs& a, int r, const TkRow& t, uint32_t u, SqFinShared& sh) {
   const bool dense_row = t.k == 0;
   const int len = dense_row ? 0 : a.sp_len[r];
   if (!dense_row) {  // (a dense row's shard masses are in sh.mass already)
@@ -823,6 +825,8 @@ __global__ void __launch_bounds__(BS) sq_finish_kernel(ShardQArgs a) {
   const int r = blockIdx.x;
   const TkRow t = a.tkr[r];
   if (t.status == kSqNotMine) return;  // (the same for every thread)
+  const uint32_t u = a.draws ? a.draws[r] : 0u;  // row-level reads issued together
+  const double s64 = t.k == 0 && a.dense ? a.s64[r] : 0.0;
   int st = t.status;
   if (st == DSPARK_ST_OK && t.k == 0 && a.dense) {
     const TkCut cut = a.cut[r];
@@ -843,9 +847,9 @@ __global__ void __launch_bounds__(BS) sq_finish_kernel(ShardQArgs a) {
       sh.wins[g] = 0u;
     }
     __syncthreads();
-    st = sq_resolve_row<DT>(a, r, t, cut, sh);
+    st = sq_resolve_row<DT>(a, r, t, cut, s64, sh);
   }
-  if (st == DSPARK_ST_OK && a.draws) st = sq_sample_row(a, r, t, sh);
+  if (st == DSPARK_ST_OK && a.draws) st = sq_sample_row(a, r, t, u, sh);
   if (threadIdx.x == 0) {
     a.row_status[r] = st;
     if (st != DSPARK_ST_OK) {
@@ -854,7 +858,7 @@ __global__ void __launch_bounds__(BS) sq_finish_kernel(ShardQArgs a) {
       if (a.conf) a.conf[r] = 0.0f;
       if (t.k != 0 && a.sp_len) a.sp_len[r] = 0;
     } else if (a.conf && t.k == 0) {
-      a.conf[r] = (float)(1.0 / a.s64[r]);
+      a.conf[r] = (float)(1.0 / s64);
     }
     if (a.vfy) {  // the request's last finishing row verifies it (its rows' outputs published first)
       const int q = r / DSPARK_N_DRAFT;
