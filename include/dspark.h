@@ -325,11 +325,12 @@ int dspark_sharded_propose_noalloc(const dspark_rows* rows, int32_t n_shards, in
  * exchange passed through ws:
  *   dense rows  - shard maxima and exact shard sums merged (every shard then
  *                 holds m and S64); each shard's floors and remainder keys;
- *                 remaining = M - the all-reduced floor sum; the threshold
- *                 key found digit by digit from all-reduced histograms of
- *                 the shards' keys; the tie at the threshold cut by lowest
- *                 global id across shards ("coordinate remaining tickets
- *                 globally");
+ *                 remaining = M - the all-reduced floor sum; the bin of the
+ *                 keys' top 11 bits where the `remaining` largest keys end,
+ *                 from an all-reduced histogram; the ids inside that bin
+ *                 gathered to the row's leader, which gives the bin's
+ *                 tickets to its largest keys, ties to the lowest global id
+ *                 across shards ("coordinate remaining tickets globally");
  *   sparse rows - each shard's local top-k (at most k candidates) merged by
  *                 (logit desc, global id asc) into the exact global top-k,
  *                 the counts allocated on that support;
@@ -341,7 +342,8 @@ int dspark_sharded_propose_noalloc(const dspark_rows* rows, int32_t n_shards, in
  * given).  Every output equals dspark_q_alloc's and the unsharded sample
  * for every n_shards in [1, min(64, V)].  Sparse rows need
  * n_shards * k_max <= 4096.  ws: at least dspark_sharded_q_workspace()
- * bytes, 256-byte aligned. */
+ * bytes (about 17 KB per row and shard and 8 KB per row, plus 8 B per
+ * candidate slot of a sparse row), 256-byte aligned. */
 size_t dspark_sharded_q_workspace(int64_t n_rows, int32_t n_shards, int32_t k_max);
 int dspark_sharded_q(const dspark_rows* rows, int32_t n_shards, const dspark_q* q, const uint32_t* draws,
                      int32_t* argmax, int32_t* sample, int32_t* row_status, void* ws, size_t ws_bytes,
