@@ -14,8 +14,9 @@
 // ascending id order, whose inclusive cumulative weight C_v satisfies
 // C_v > T = floor(u W / 2^64), W the total weight.  Residual weights are
 // max(2^24 A_v - c_v A, 0) for q counts c_v.  Everything is integer: the
-// per-element weights are summed exactly (the Acc accumulator), wave and
-// row totals are 256-bit integers.
+// per-element weights are summed exactly (a 64-bit word for weights of at
+// least 2^-24, the 128-bit accumulator below), wave and row totals are
+// 256-bit integers.
 //
 // Layout: wave w owns a contiguous id range, cut into chunks of 64 lanes x E
 // consecutive ids; lane l of chunk c holds ids base + c * 64E + l E + e.  A
@@ -123,6 +124,30 @@ __device__ __forceinline__ U256 u256_of_acc(const Acc& a) {
   U256 m = U256{{0ull, a.mlo << 15, (a.mlo >> 49) | (a.mhi << 15), a.mhi >> 49}};  // main << 79
   return u256_add(m, U256{{a.tlo, a.thi, 0ull, 0ull}});
 }
+// Exact sums of the draws' weights.  Weights of at least 2^-24 (binary32
+// exponent field E >= 103; nearly every weight of a row) are integers in
+// units of 2^-47 below 2^48, added in one 64-bit word: a lane adds at most
+// 2^10 of them and a wave 2^16 (V <= 2^20), so neither a lane's nor a wave's
+// word overflows.  Smaller weights go to the 128-bit accumulator.
+struct DAcc {
+  uint64_t q;
+  Acc a;
+};
+__device__ __forceinline__ void dacc_zero(DAcc& s) {
+  s.q = 0ull;
+  acc_zero(s.a);
+}
+__device__ __forceinline__ void dacc_add(DAcc& s, uint32_t wb) {
+  wb &= 0x7fffffffu;
+  const uint32_t E = wb >> 23;
+  if (E >= 103u) s.q += (uint64_t)((wb & 0x7fffffu) | 0x800000u) << (E - 103u);
+  else if (wb) acc_add(s.a, wb);
+}
+// the sum in units of 2^-149
+__device__ __forceinline__ U256 u256_of_dacc(const DAcc& s) {
+  const U256 q = U256{{0ull, s.q << 38, s.q >> 26, 0ull}};  // q * 2^102
+  return u256_add(q, u256_of_acc(s.a));
+}
 // a * 2^-149 to about 2^-60 relative (only used to pre-sort comparisons)
 __device__ __forceinline__ double u256_approx_scaled(const U256& a) {
   double r = 0.0;
@@ -155,17 +180,26 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
 __device__ __forceinline__ U256 u256_readlane(const U256& v, int l) {
   return U256{{readlane_u64(v.w[0], l), readlane_u64(v.w[1], l), readlane_u64(v.w[2], l), readlane_u64(v.w[3], l)}};
 }
-// wave totals of an exact accumulator and a 64-bit count, in every lane
-__device__ __forceinline__ void wave_total(const Acc& a, uint64_t s2, Acc* ta, uint64_t* ts2) {
-  Limbs4 mw = limbs_of(a.mlo, a.mhi);
-  add128_wave(mw);
-  Limbs4 tw = limbs_of(a.tlo, a.thi);
+// wave totals of an exact draw sum and a 64-bit count, in every lane (the
+// 128-bit words only when some lane holds a small weight)
+__device__ __forceinline__ void wave_total(const DAcc& s, uint64_t s2, DAcc* ts, uint64_t* ts2) {
+  ts->q = wave_sum<uint64_t>(s.q);
+  const Acc& a = s.a;
+  const bool main = __ballot((a.mlo | a.mhi) != 0ull) != 0ull;
   const bool tiny = __ballot((a.tlo | a.thi) != 0ull) != 0ull;
-  if (tiny) add128_wave(tw);
-  ta->mlo = readlane_u64(limbs_lo(mw), 63);
-  ta->mhi = readlane_u64(limbs_hi(mw), 63);
-  ta->tlo = tiny ? readlane_u64(limbs_lo(tw), 63) : 0ull;
-  ta->thi = tiny ? readlane_u64(limbs_hi(tw), 63) : 0ull;
+  acc_zero(ts->a);
+  if (main) {
+    Limbs4 mw = limbs_of(a.mlo, a.mhi);
+    add128_wave(mw);
+    ts->a.mlo = readlane_u64(limbs_lo(mw), 63);
+    ts->a.mhi = readlane_u64(limbs_hi(mw), 63);
+  }
+  if (tiny) {
+    Limbs4 tw = limbs_of(a.tlo, a.thi);
+    add128_wave(tw);
+    ts->a.tlo = readlane_u64(limbs_lo(tw), 63);
+    ts->a.thi = readlane_u64(limbs_hi(tw), 63);
+  }
   *ts2 = __ballot(s2 != 0ull) ? wave_sum<uint64_t>(s2) : 0ull;
 }
 
@@ -193,7 +227,7 @@ struct DrawShared : SmemBase {
   int32_t sid[DSPARK_K_MAX];          // sparse q ids (ascending) and counts
   uint32_t scnt[DSPARK_K_MAX];
   uint32_t gbits[DSPARK_V_MAX / 256];  // one bit per 8 ids: some sparse id in the group
-  Acc wsum[NW];
+  DAcc wsum[NW];
   uint64_t ws2[NW];
   U256 wtot[NW];
   U256 total;
@@ -257,23 +291,23 @@ __device__ __forceinline__ U256 elem_weight(uint32_t wb, uint32_t cnt, const Dra
 }
 // the exact total of a group from its accumulated weights and counts
 template <int mode>
-__device__ __forceinline__ U256 group_weight(const Acc& s1, uint64_t s2, const DrawCtx& c) {
-  const U256 a = u256_of_acc(s1);
+__device__ __forceinline__ U256 group_weight(const DAcc& s1, uint64_t s2, const DrawCtx& c) {
+  const U256 a = u256_of_dacc(s1);
   if (mode == kDrawPlain) return a;
   return u256_sub(u256_shl(a, 24), u256_mul64(c.A, s2));
 }
 // adds one element (weight bits wb, id v) to a lane's sums
 template <int mode>
-__device__ __forceinline__ void draw_add(uint32_t wb, int v, const DrawCtx& c, const DrawShared& sh, Acc& s1,
+__device__ __forceinline__ void draw_add(uint32_t wb, int v, const DrawCtx& c, const DrawShared& sh, DAcc& s1,
                                          uint64_t& s2) {
   if (mode == kDrawPlain) {
-    acc_add(s1, wb);
+    dacc_add(s1, wb);
     return;
   }
   if ((wb & 0x7fffffffu) == 0u) return;
   const uint32_t cnt = draw_count(c, sh, v);
   if (resid_positive(wb, cnt, c)) {
-    acc_add(s1, wb);
+    dacc_add(s1, wb);
     s2 += cnt;
   }
 }
@@ -332,9 +366,9 @@ __device__ __forceinline__ void wres_load(Res& R, const uint16_t* p, int V) {
 
 // this lane's plain sum over chunk v of a resident row, weights from the
 // value table
-__device__ __forceinline__ void wres_chunk(u32x4 v, const DrawCtx& c, const DrawShared& sh, Acc& s1) {
+__device__ __forceinline__ void wres_chunk(u32x4 v, const DrawCtx& c, const DrawShared& sh, DAcc& s1) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc_add(s1, bf16_weight_table(elem(v, e), c, sh));
+  for (int e = 0; e < 8; ++e) dacc_add(s1, bf16_weight_table(elem(v, e), c, sh));
 }
 
 // streamed rows: wave w holds chunks [cpw w, cpw (w + 1)) of 64 vectors
@@ -417,17 +451,17 @@ __device__ __forceinline__ uint32_t chunk_weight_bits(uint32_t b, const DrawCtx&
 }
 template <int mode, int DT>
 __device__ __forceinline__ void stream_add(const ChunkData<DT>& d, int q, const DrawCtx& c, const DrawShared& sh,
-                                           Acc& s1, uint64_t& s2) {
+                                           DAcc& s1, uint64_t& s2) {
   constexpr int E = StreamSrc<DT>::E;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t wb = chunk_weight_bits<DT>(d.bits(e), c, sh);
     if (mode == kDrawPlain) {
-      acc_add(s1, wb);
+      dacc_add(s1, wb);
     } else if ((wb & 0x7fffffffu) != 0u) {
       const uint32_t cnt = c.dense ? d.cnt[e] : draw_count(c, sh, q * E + e);
       if (resid_positive(wb, cnt, c)) {
-        acc_add(s1, wb);
+        dacc_add(s1, wb);
         s2 += cnt;
       }
     }
@@ -440,7 +474,7 @@ struct DrawPF {
   static constexpr int n = mode == kDrawPlain ? 4 : 2;
 };
 template <int mode, int DT>
-__device__ __forceinline__ void stream_sums(const StreamSrc<DT>& s, const DrawCtx& c, const DrawShared& sh, Acc& s1,
+__device__ __forceinline__ void stream_sums(const StreamSrc<DT>& s, const DrawCtx& c, const DrawShared& sh, DAcc& s1,
                                             uint64_t& s2) {
   const __amdgpu_buffer_rsrc_t crs = count_rsrc(c);
   const bool c16 = (reinterpret_cast<uintptr_t>(c.dense) & 15u) == 0u;
@@ -460,9 +494,9 @@ __device__ __forceinline__ void stream_sums(const StreamSrc<DT>& s, const DrawCt
 // Wave totals of the mode's weights from each lane's sums (all threads; ends
 // with a barrier): sh.wtot[w] and sh.total.
 template <int mode>
-__device__ __forceinline__ void draw_totals(const Acc& s1, uint64_t s2, const DrawCtx& c,
+__device__ __forceinline__ void draw_totals(const DAcc& s1, uint64_t s2, const DrawCtx& c,
                                             DrawShared& sh) {
-  Acc ta;
+  DAcc ta;
   uint64_t ts2;
   wave_total(s1, s2, &ta, &ts2);
   if (lane_id() == 0) {
@@ -508,7 +542,7 @@ __device__ __forceinline__ void draw_find_wave(uint64_t u, DrawShared& sh) {
 // left at the chunk's start): the lane holding the crossing and the
 // threshold left inside that lane.  Wave-uniform results.
 template <int mode>
-__device__ __forceinline__ int draw_find_lane(const Acc& s1, uint64_t s2, const DrawCtx& c,
+__device__ __forceinline__ int draw_find_lane(const DAcc& s1, uint64_t s2, const DrawCtx& c,
                                               const U256& t, U256* lane_rest) {
   const U256 wl = group_weight<mode>(s1, s2, c);
   const U256 inc = u256_wave_incl_scan(wl);
@@ -533,9 +567,9 @@ __device__ __forceinline__ int stream_walk(const StreamSrc<DT>& s, const DrawCtx
     const bool c16 = (reinterpret_cast<uintptr_t>(c.dense) & 15u) == 0u;
     U256 t = sh.rest;
     int ich = -1;
-    Acc cs1;
+    DAcc cs1;
     uint64_t cs2 = 0;
-    acc_zero(cs1);
+    dacc_zero(cs1);
     ChunkData<DT> hit;
     constexpr int PF = DrawPF<mode>::n;
     for (int ch0 = 0; ch0 < s.cpw && ich < 0; ch0 += PF) {  // PF chunks' loads in flight together
@@ -546,11 +580,11 @@ __device__ __forceinline__ int stream_walk(const StreamSrc<DT>& s, const DrawCtx
 #pragma unroll
       for (int k = 0; k < PF; ++k) {
         if (ch0 + k < s.cpw && ich < 0) {  // (wave-uniform)
-          Acc a;
-          acc_zero(a);
+          DAcc a;
+          dacc_zero(a);
           uint64_t b = 0;
           stream_add<mode, DT>(d[k], s.vec(ch0 + k), c, sh, a, b);
-          Acc ta;
+          DAcc ta;
           uint64_t tb;
           wave_total(a, b, &ta, &tb);
           const U256 wc = group_weight<mode>(ta, tb, c);
@@ -610,20 +644,20 @@ __device__ __forceinline__ int wres_walk(Res& R, const DrawCtx& c, uint64_t u, D
     int ich = -1;
     touch(R);
     for (int i = 0; i < NI && ich < 0; ++i) {
-      Acc a;
-      acc_zero(a);
+      DAcc a;
+      dacc_zero(a);
       wres_chunk(select_vec(R, i), c, sh, a);
-      Acc ta;
+      DAcc ta;
       uint64_t tb;
       wave_total(a, 0ull, &ta, &tb);
-      const U256 wc = u256_of_acc(ta);
+      const U256 wc = u256_of_dacc(ta);
       if (u256_lt(t, wc)) ich = i;
       else t = u256_sub(t, wc);
     }
     ich = ich < 0 ? 0 : ich;
     const u32x4 v = select_vec(R, ich);
-    Acc a;
-    acc_zero(a);
+    DAcc a;
+    dacc_zero(a);
     wres_chunk(v, c, sh, a);
     U256 lr;
     const int l = draw_find_lane<kDrawPlain>(a, 0ull, c, t, &lr);
@@ -651,8 +685,8 @@ __device__ __forceinline__ int wres_walk(Res& R, const DrawCtx& c, uint64_t u, D
 template <int mode, int DT>
 __device__ __forceinline__ int stream_draw(const StreamSrc<DT>& s, const DrawCtx& c, bool u_valid, uint64_t u,
                                            DrawShared& sh) {
-  Acc s1;
-  acc_zero(s1);
+  DAcc s1;
+  dacc_zero(s1);
   uint64_t s2 = 0;
   stream_sums<mode, DT>(s, c, sh, s1, s2);
   draw_totals<mode>(s1, s2, c, sh);
@@ -667,8 +701,8 @@ __device__ __forceinline__ int stream_draw(const StreamSrc<DT>& s, const DrawCtx
 // Resident bf16 row (loaded by wres_load) whose weights come from the value
 // table (c.table): plain sums and the draw from its registers.
 __device__ __forceinline__ int wres_draw(Res& R, const DrawCtx& c, bool u_valid, uint64_t u, DrawShared& sh) {
-  Acc s1;
-  acc_zero(s1);
+  DAcc s1;
+  dacc_zero(s1);
   touch(R);
 #pragma unroll
   for (int i = 0; i < NI; ++i) wres_chunk(fetch(R, i), c, sh, s1);
