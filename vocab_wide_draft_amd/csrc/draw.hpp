@@ -180,6 +180,14 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
 __device__ __forceinline__ U256 u256_readlane(const U256& v, int l) {
   return U256{{readlane_u64(v.w[0], l), readlane_u64(v.w[1], l), readlane_u64(v.w[2], l), readlane_u64(v.w[3], l)}};
 }
+// wave-uniform copy of a value every lane holds (scalar registers)
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v) |
+         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)) << 32);
+}
+__device__ __forceinline__ U256 uniform_u256(const U256& v) {
+  return U256{{uniform_u64(v.w[0]), uniform_u64(v.w[1]), uniform_u64(v.w[2]), uniform_u64(v.w[3])}};
+}
 // wave totals of an exact draw sum and a 64-bit count, in every lane (the
 // 128-bit words only when some lane holds a small weight)
 __device__ __forceinline__ void wave_total(const DAcc& s, uint64_t s2, DAcc* ts, uint64_t* ts2) {
@@ -227,13 +235,13 @@ struct DrawShared : SmemBase {
   int32_t sid[DSPARK_K_MAX];          // sparse q ids (ascending) and counts
   uint32_t scnt[DSPARK_K_MAX];
   uint32_t gbits[DSPARK_V_MAX / 256];  // one bit per 8 ids: some sparse id in the group
-  DAcc wsum[NW];
-  uint64_t ws2[NW];
   U256 wtot[NW];
   U256 total;
-  U256 rest;     // the draw's threshold, less everything before the crossing wave
+  U256 rest;     // the draw's threshold, less everything before the crossing wave (then chunk)
   int wstar;
   int token;
+  int ichunk;                            // the crossing chunk of a streamed row
+  U256 ctot[DSPARK_V_MAX / (64 * NW * 4)];  // chunk totals of the crossing wave's range (streamed rows)
 };
 
 // Builds the weight table of a bf16 row (all threads; ends with a barrier).
@@ -419,10 +427,9 @@ __device__ __forceinline__ void chunk_load_values(const Row<DT>& row, int q, Chu
   }
 }
 template <int mode, int DT>
-__device__ __forceinline__ void stream_load(const StreamSrc<DT>& s, int ch, const DrawCtx& c,
-                                            __amdgpu_buffer_rsrc_t crs, bool c16, ChunkData<DT>& d) {
+__device__ __forceinline__ void stream_load_vec(const StreamSrc<DT>& s, int q, const DrawCtx& c,
+                                                __amdgpu_buffer_rsrc_t crs, bool c16, ChunkData<DT>& d) {
   constexpr int E = StreamSrc<DT>::E;
-  const int q = s.vec(ch);
   chunk_load_values<DT>(s.row, q, d);
   if (mode != kDrawPlain && c.dense) {
     if (c16) {  // a 16-byte aligned count row: E / 4 vector loads
@@ -439,6 +446,11 @@ __device__ __forceinline__ void stream_load(const StreamSrc<DT>& s, int ch, cons
       for (int e = 0; e < E; ++e) d.cnt[e] = __builtin_amdgcn_raw_buffer_load_b32(crs, (q * E + e) * 4, 0, 0);
     }
   }
+}
+template <int mode, int DT>
+__device__ __forceinline__ void stream_load(const StreamSrc<DT>& s, int ch, const DrawCtx& c,
+                                            __amdgpu_buffer_rsrc_t crs, bool c16, ChunkData<DT>& d) {
+  stream_load_vec<mode, DT>(s, s.vec(ch), c, crs, c16, d);
 }
 // buffer over a dense q row (reads past V give 0)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t count_rsrc(const DrawCtx& c) {
@@ -492,47 +504,44 @@ __device__ __forceinline__ void stream_sums(const StreamSrc<DT>& s, const DrawCt
 
 // ----------------------------------------------------------------- passes
 // Wave totals of the mode's weights from each lane's sums (all threads; ends
-// with a barrier): sh.wtot[w] and sh.total.
+// with a barrier): sh.wtot[w] (each wave's own, from its lane 0) and
+// sh.total (a 256-bit scan of the NW wave totals by wave 0).
 template <int mode>
 __device__ __forceinline__ void draw_totals(const DAcc& s1, uint64_t s2, const DrawCtx& c,
                                             DrawShared& sh) {
   DAcc ta;
   uint64_t ts2;
   wave_total(s1, s2, &ta, &ts2);
-  if (lane_id() == 0) {
-    sh.wsum[wave_id()] = ta;
-    sh.ws2[wave_id()] = ts2;
-  }
+  if (lane_id() == 0) sh.wtot[wave_id()] = group_weight<mode>(ta, ts2, c);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    U256 t = u256_zero();
-    for (int w = 0; w < NW; ++w) {
-      const U256 ww = group_weight<mode>(sh.wsum[w], sh.ws2[w], c);
-      sh.wtot[w] = ww;
-      t = u256_add(t, ww);
-    }
-    sh.total = t;
+  if (wave_id() == 0) {
+    const U256 inc = u256_wave_incl_scan(lane_id() < NW ? sh.wtot[lane_id()] : u256_zero());
+    if (lane_id() == 63) sh.total = inc;
   }
   __syncthreads();
 }
 
-// Thread 0: the wave holding the draw's crossing and the threshold left
-// inside it (after draw_totals; ends with a barrier).  A zero total gives
-// wstar = -1.
+// Wave 0: the wave holding the draw's crossing and the threshold left
+// inside it, from one 256-bit scan of the wave totals (after draw_totals;
+// ends with a barrier).  A zero total gives wstar = -1.
 __device__ __forceinline__ void draw_find_wave(uint64_t u, DrawShared& sh) {
-  if (threadIdx.x == 0) {
-    sh.token = -1;
-    sh.wstar = -1;
-    if (!u256_is_zero(sh.total)) {
-      U256 t = u256_mulhi64(sh.total, u);  // < total
-      for (int w = 0; w < NW; ++w) {
-        if (u256_lt(t, sh.wtot[w])) {
-          sh.wstar = w;
-          break;
-        }
-        t = u256_sub(t, sh.wtot[w]);
-      }
-      sh.rest = t;
+  if (wave_id() == 0) {
+    const U256 total = uniform_u256(sh.total);
+    const int l = lane_id();
+    const U256 v = l < NW ? sh.wtot[l] : u256_zero();
+    const U256 inc = u256_wave_incl_scan(v);
+    int ws = -1;
+    U256 rest = u256_zero();
+    if (!u256_is_zero(total)) {
+      const U256 t = u256_mulhi64(total, u);  // < total
+      const uint64_t hit = __ballot(l < NW && u256_lt(t, inc));
+      ws = hit ? __builtin_ctzll(hit) : -1;
+      if (ws >= 0) rest = u256_sub(t, u256_readlane(u256_sub(inc, v), ws));
+    }
+    if (l == 0) {
+      sh.token = -1;
+      sh.wstar = ws;
+      sh.rest = rest;
     }
   }
   __syncthreads();
@@ -553,66 +562,78 @@ __device__ __forceinline__ int draw_find_lane(const DAcc& s1, uint64_t s2, const
   return l;
 }
 
-// The draw itself, from the totals of draw_totals: the crossing wave walks
-// its chunks in order (reloading them from memory, the next chunk's loads in
-// flight) to the crossing chunk, scans its lanes, and the crossing lane
+// The draw itself, from the totals of draw_totals: every wave totals its
+// share of the crossing wave's chunks (one load round each), wave 0 finds the
+// crossing chunk with 256-bit scans of the chunk totals, the wave that
+// totalled that chunk reloads it and scans its lanes, and the crossing lane
 // walks its elements.  Returns the token (-1 for a zero total).
 template <int mode, int DT>
 __device__ __forceinline__ int stream_walk(const StreamSrc<DT>& s, const DrawCtx& c, uint64_t u, DrawShared& sh) {
   draw_find_wave(u, sh);
-  if (sh.wstar < 0) return -1;
-  if (wave_id() == sh.wstar) {
-    constexpr int E = StreamSrc<DT>::E;
-    const __amdgpu_buffer_rsrc_t crs = count_rsrc(c);
-    const bool c16 = (reinterpret_cast<uintptr_t>(c.dense) & 15u) == 0u;
-    U256 t = sh.rest;
+  const int ws = sh.wstar;
+  if (ws < 0) return -1;
+  constexpr int E = StreamSrc<DT>::E;
+  const __amdgpu_buffer_rsrc_t crs = count_rsrc(c);
+  const bool c16 = (reinterpret_cast<uintptr_t>(c.dense) & 15u) == 0u;
+  StreamSrc<DT> sw = s;  // the crossing wave's chunks, addressed from any wave
+  auto vec_of = [&](int ch) { return (ws * s.cpw + ch) * 64 + lane_id(); };
+  for (int ch = wave_id(); ch < s.cpw; ch += NW) {
+    ChunkData<DT> d;
+    stream_load_vec<mode, DT>(sw, vec_of(ch), c, crs, c16, d);
+    DAcc a;
+    dacc_zero(a);
+    uint64_t b = 0;
+    stream_add<mode, DT>(d, vec_of(ch), c, sh, a, b);
+    DAcc ta;
+    uint64_t tb;
+    wave_total(a, b, &ta, &tb);
+    if (lane_id() == 0) sh.ctot[ch] = group_weight<mode>(ta, tb, c);
+  }
+  __syncthreads();
+  if (wave_id() == 0) {
+    U256 t = uniform_u256(sh.rest);
     int ich = -1;
-    DAcc cs1;
-    uint64_t cs2 = 0;
-    dacc_zero(cs1);
-    ChunkData<DT> hit;
-    constexpr int PF = DrawPF<mode>::n;
-    for (int ch0 = 0; ch0 < s.cpw && ich < 0; ch0 += PF) {  // PF chunks' loads in flight together
-      ChunkData<DT> d[PF];
-#pragma unroll
-      for (int k = 0; k < PF; ++k)
-        if (ch0 + k < s.cpw) stream_load<mode, DT>(s, ch0 + k, c, crs, c16, d[k]);
-#pragma unroll
-      for (int k = 0; k < PF; ++k) {
-        if (ch0 + k < s.cpw && ich < 0) {  // (wave-uniform)
-          DAcc a;
-          dacc_zero(a);
-          uint64_t b = 0;
-          stream_add<mode, DT>(d[k], s.vec(ch0 + k), c, sh, a, b);
-          DAcc ta;
-          uint64_t tb;
-          wave_total(a, b, &ta, &tb);
-          const U256 wc = group_weight<mode>(ta, tb, c);
-          if (u256_lt(t, wc)) {
-            ich = ch0 + k;
-            cs1 = a;
-            cs2 = b;
-            hit = d[k];
-          } else {
-            t = u256_sub(t, wc);
-          }
-        }
+    for (int base = 0; base < s.cpw && ich < 0; base += 64) {  // (wave-uniform)
+      const int ch = base + lane_id();
+      const U256 v = ch < s.cpw ? sh.ctot[ch] : u256_zero();
+      const U256 inc = u256_wave_incl_scan(v);
+      const uint64_t hit = __ballot(ch < s.cpw && u256_lt(t, inc));
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        ich = base + l;
+        t = u256_sub(t, u256_readlane(u256_sub(inc, v), l));
+      } else {
+        t = u256_sub(t, u256_readlane(inc, 63));
       }
     }
+    if (lane_id() == 0) {
+      sh.ichunk = ich;
+      sh.rest = t;
+    }
+  }
+  __syncthreads();
+  const int ich = sh.ichunk;
+  if (ich >= 0 && wave_id() == ich % NW) {
+    ChunkData<DT> d;
+    const int q = vec_of(ich);
+    stream_load_vec<mode, DT>(sw, q, c, crs, c16, d);
+    DAcc a;
+    dacc_zero(a);
+    uint64_t b = 0;
+    stream_add<mode, DT>(d, q, c, sh, a, b);
     U256 lr;
-    const int l = draw_find_lane<mode>(cs1, cs2, c, t, &lr);
-    if (lane_id() == l && ich >= 0) {
-      const int q = s.vec(ich);
+    const int l = draw_find_lane<mode>(a, b, c, uniform_u256(sh.rest), &lr);
+    if (lane_id() == l) {
       int tok = -1;
       U256 run = u256_zero();
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         if (tok < 0) {
-          const uint32_t wb = chunk_weight_bits<DT>(hit.bits(e), c, sh);
+          const uint32_t wb = chunk_weight_bits<DT>(d.bits(e), c, sh);
           // ids past V carry weight 0 and have no count
           uint32_t cnt = 0u;
           if (mode != kDrawPlain && (wb & 0x7fffffffu) != 0u)
-            cnt = c.dense ? hit.cnt[e] : draw_count(c, sh, q * E + e);
+            cnt = c.dense ? d.cnt[e] : draw_count(c, sh, q * E + e);
           run = u256_add(run, elem_weight<mode>(wb, cnt, c));
           if (u256_lt(lr, run)) tok = q * E + e;
         }
@@ -622,15 +643,6 @@ __device__ __forceinline__ int stream_walk(const StreamSrc<DT>& s, const DrawCtx
   }
   __syncthreads();
   return sh.token;
-}
-
-// wave-uniform copy of a value every lane holds (scalar registers)
-__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
-  return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v) |
-         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)) << 32);
-}
-__device__ __forceinline__ U256 uniform_u256(const U256& v) {
-  return U256{{uniform_u64(v.w[0]), uniform_u64(v.w[1]), uniform_u64(v.w[2]), uniform_u64(v.w[3])}};
 }
 
 // The same draw for a resident bf16 row whose weights come from the value
