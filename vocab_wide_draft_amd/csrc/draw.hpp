@@ -646,35 +646,57 @@ __device__ __forceinline__ int stream_walk(const StreamSrc<DT>& s, const DrawCtx
 }
 
 // The same draw for a resident bf16 row whose weights come from the value
-// table: the crossing wave's chunks are taken from its registers (a select
-// chain picks each one); the running threshold stays in scalar registers.
+// table: the crossing wave parks its 16 chunks in LDS (the histogram area,
+// unused by the draws), every wave totals one of them, wave 0 finds the
+// crossing chunk by a 256-bit scan, and one wave scans that chunk's lanes.
 __device__ __forceinline__ int wres_walk(Res& R, const DrawCtx& c, uint64_t u, DrawShared& sh) {
+  static_assert(sizeof(sh.hist) >= NI * 64 * sizeof(u32x4), "chunk area");
+  static_assert(NI == NW, "one chunk per wave");
   draw_find_wave(u, sh);
-  if (sh.wstar < 0) return -1;
-  if (wave_id() == sh.wstar) {
-    U256 t = uniform_u256(sh.rest);
-    int ich = -1;
+  const int ws = sh.wstar;
+  if (ws < 0) return -1;
+  u32x4* park = reinterpret_cast<u32x4*>(sh.hist);
+  if (wave_id() == ws) {
     touch(R);
-    for (int i = 0; i < NI && ich < 0; ++i) {
-      DAcc a;
-      dacc_zero(a);
-      wres_chunk(select_vec(R, i), c, sh, a);
-      DAcc ta;
-      uint64_t tb;
-      wave_total(a, 0ull, &ta, &tb);
-      const U256 wc = u256_of_dacc(ta);
-      if (u256_lt(t, wc)) ich = i;
-      else t = u256_sub(t, wc);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) park[i * 64 + lane_id()] = fetch(R, i);
+  }
+  __syncthreads();
+  {
+    const int i = wave_id();  // chunk i of the crossing wave
+    DAcc a;
+    dacc_zero(a);
+    wres_chunk(park[i * 64 + lane_id()], c, sh, a);
+    DAcc ta;
+    uint64_t tb;
+    wave_total(a, 0ull, &ta, &tb);
+    if (lane_id() == 0) sh.ctot[i] = u256_of_dacc(ta);
+  }
+  __syncthreads();
+  if (wave_id() == 0) {
+    const U256 t = uniform_u256(sh.rest);
+    const int l = lane_id();
+    const U256 v = l < NI ? sh.ctot[l] : u256_zero();
+    const U256 inc = u256_wave_incl_scan(v);
+    const uint64_t hit = __ballot(l < NI && u256_lt(t, inc));
+    const int ich = hit ? __builtin_ctzll(hit) : 0;
+    const U256 rest = u256_sub(t, u256_readlane(u256_sub(inc, v), ich));
+    if (l == 0) {
+      sh.ichunk = ich;
+      sh.rest = rest;
     }
-    ich = ich < 0 ? 0 : ich;
-    const u32x4 v = select_vec(R, ich);
+  }
+  __syncthreads();
+  const int ich = sh.ichunk;
+  if (wave_id() == ich) {
+    const u32x4 v = park[ich * 64 + lane_id()];
     DAcc a;
     dacc_zero(a);
     wres_chunk(v, c, sh, a);
     U256 lr;
-    const int l = draw_find_lane<kDrawPlain>(a, 0ull, c, t, &lr);
+    const int l = draw_find_lane<kDrawPlain>(a, 0ull, c, uniform_u256(sh.rest), &lr);
     if (lane_id() == l) {
-      const int base = wres_base(ich);
+      const int base = ws * 8192 + ich * 512 + lane_id() * 8;  // ids of the crossing wave's chunk ich
       int tok = -1;
       U256 run = u256_zero();
 #pragma unroll
