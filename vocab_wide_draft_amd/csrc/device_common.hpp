@@ -366,6 +366,17 @@ __device__ __forceinline__ void acc_add(Acc& a, uint32_t wb, uint32_t n = 1) {
     add128(a.tlo, a.thi, lo, hi);
   }
 }
+// A faster tier for many weights: weights of at least 2^-24 (exponent field
+// E >= 103) are integers in units of 2^-47 below 2^48, added in a 64-bit
+// word q (2^16 of them fit); smaller ones go to the accumulator.  acc_fold
+// adds q to the accumulator's main word (units 2^-70: q * 2^23).
+__device__ __forceinline__ void acc_add_q(Acc& a, uint64_t& q, uint32_t wb) {
+  wb &= 0x7fffffffu;
+  const uint32_t E = wb >> 23;
+  if (E >= 103u) q += (uint64_t)((wb & 0x7fffffu) | 0x800000u) << (E - 103u);
+  else if (wb) acc_add(a, wb);
+}
+__device__ __forceinline__ void acc_fold(Acc& a, uint64_t q) { add128(a.mlo, a.mhi, q << 23, q >> 41); }
 struct AccScratch {
   Acc w[NW];
   double s64;

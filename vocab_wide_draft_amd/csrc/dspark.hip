@@ -945,7 +945,7 @@ int split_shards(int64_t n_draft, int64_t vocab) {
   // 512 or more rows (with their target rows, two rounds of the chip's
   // 256 compute units) keep one workgroup per row
   if (n_draft <= 0 || n_draft >= 512) return 1;
-  int64_t g = (2048 + n_draft - 1) / n_draft;  // about 2048 shard workgroups
+  int64_t g = 2048 / n_draft;  // at most 2048 shard workgroups: one round of the sum pass (8 per CU)
   if (g > 64) g = 64;
   if (g > vocab) g = vocab;
   return g < 1 ? 1 : (int)g;

@@ -64,20 +64,42 @@ __device__ __forceinline__ void shard_max_block(const void* data, int64_t stride
   float bv = -__builtin_inff();
   int bi = 0x7fffffff;
   uint32_t fl = 0;
-  for (int i0 = lo + (int)threadIdx.x; i0 < hi; i0 += kShardU * kShardBS) {
-    float x[kShardU];  // the loads of kShardU iterations in flight together
+  auto take = [&](float x, int i) {
+    fl |= (x != x ? 1u : 0u) | (x == __builtin_inff() ? 2u : 0u);
+    if (x > bv || (x == bv && x != -__builtin_inff() && i < bi)) {
+      bv = x;
+      bi = i;
+    }
+  };
+  // the shard's 16-byte aligned middle as vectors (rows start 16-byte
+  // aligned), its unaligned head and tail element by element
+  constexpr int EPV = DT == DSPARK_BF16 ? 8 : 4;
+  const int a0 = (lo + EPV - 1) / EPV * EPV < hi ? (lo + EPV - 1) / EPV * EPV : hi;
+  const int a1 = hi / EPV * EPV > a0 ? hi / EPV * EPV : a0;
+  for (int i = lo + (int)threadIdx.x; i < a0; i += kShardBS) take(shard_value<DT>(data, stride, r, i), i);
+  for (int i = a1 + (int)threadIdx.x; i < hi; i += kShardBS) take(shard_value<DT>(data, stride, r, i), i);
+  const int es = DT == DSPARK_BF16 ? 2 : 4;
+  const uint4* vrow = reinterpret_cast<const uint4*>(static_cast<const char*>(data) + (size_t)r * (size_t)stride * es);
+  const int q1 = a1 / EPV;
+  constexpr int UV = 4;  // vectors per thread in flight together
+  for (int q0 = a0 / EPV + (int)threadIdx.x; q0 < q1; q0 += UV * kShardBS) {
+    uint4 v[UV];
 #pragma unroll
-    for (int u = 0; u < kShardU; ++u) {
-      const int i = i0 + u * kShardBS;
-      x[u] = i < hi ? shard_value<DT>(data, stride, r, i) : -__builtin_inff();
+    for (int u = 0; u < UV; ++u) {
+      const int q = q0 + u * kShardBS;
+      v[u] = q < q1 ? vrow[q] : uint4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
     }
 #pragma unroll
-    for (int u = 0; u < kShardU; ++u) {  // ids ascend with u: the first maximum stays
-      const int i = i0 + u * kShardBS;
-      fl |= (x[u] != x[u] ? 1u : 0u) | (x[u] == __builtin_inff() ? 2u : 0u);
-      if (x[u] > bv || (x[u] == bv && x[u] != -__builtin_inff() && i < bi)) {
-        bv = x[u];
-        bi = i;
+    for (int u = 0; u < UV; ++u) {
+      const int q = q0 + u * kShardBS;
+      if (q < q1) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float x = DT == DSPARK_BF16 ? __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16))
+                                            : __uint_as_float(w[e]);
+          take(x, q * EPV + e);
+        }
       }
     }
   }

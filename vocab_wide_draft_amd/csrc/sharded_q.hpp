@@ -68,7 +68,7 @@ constexpr int kTkLevels = 6;         // digits of a 64-bit remainder key
 constexpr int kSqMergeCap = 4096;    // candidates a row's merge may hold (G * k_max)
 constexpr int kSqCandCap = 1024;     // crossing-bin ids a row resolves on chip (and a shard stores)
 constexpr uint32_t kSqMark = 0x80000000u;  // count-row flag: in the crossing bin, not yet resolved
-constexpr int kSqChunk = 4096;             // ids per chunk of the cand pass (4 per thread)
+constexpr int kSqChunk = 4096;             // ids per count-mass chunk (two per cand pass; the sample reads one)
 constexpr int kSqMaxChunks = DSPARK_V_MAX / kSqChunk;  // chunks a shard can have
 
 __host__ __device__ constexpr int tk_shift(int l) { return l < 5 ? 53 - 11 * l : 0; }
@@ -245,13 +245,18 @@ __global__ void __launch_bounds__(kShardBS) sq_sum_kernel(ShardQArgs a) {
   const int r = b / a.G, g = b % a.G;
   int lo, hi;
   shard_range(a.V, a.G, g, &lo, &hi);
-  const int i00 = lo + (int)threadIdx.x;
-  float x[kShardU];  // the first loads: they need no m, so they fly during the merge
+  // the shard's 16-byte aligned middle [a0, a1) as vectors of EPV logits (rows
+  // start 16-byte aligned), its head and tail element by element
+  constexpr int EPV = DT == DSPARK_BF16 ? 8 : 4;
+  constexpr int UV = DT == DSPARK_BF16 ? 1 : 2;  // vectors per thread in flight (8 logits)
+  const int a0 = (lo + EPV - 1) / EPV * EPV < hi ? (lo + EPV - 1) / EPV * EPV : hi;
+  const int a1 = hi / EPV * EPV > a0 ? hi / EPV * EPV : a0;
+  const int es = DT == DSPARK_BF16 ? 2 : 4;
+  const uint4* vrow = reinterpret_cast<const uint4*>(static_cast<const char*>(a.data) + (size_t)r * (size_t)a.stride * es);
+  const int q1 = a1 / EPV, q00 = a0 / EPV + (int)threadIdx.x;
+  uint4 xv[UV];  // the first loads: they need no m, so they fly during the merge
 #pragma unroll
-  for (int u = 0; u < kShardU; ++u) {
-    const int i = i00 + u * kShardBS;
-    x[u] = i < hi ? sq_value<DT>(a, r, i) : -__builtin_inff();
-  }
+  for (int u = 0; u < UV; ++u) xv[u] = q00 + u * kShardBS < q1 ? vrow[q00 + u * kShardBS] : uint4{0u, 0u, 0u, 0u};
   if (threadIdx.x < 64) {
     const int k = a.topk ? a.topk[r] : 0;  // (loads in flight with the heads')
     const uint32_t u = a.draws ? a.draws[r] : 0u;
@@ -278,24 +283,49 @@ __global__ void __launch_bounds__(kShardBS) sq_sum_kernel(ShardQArgs a) {
   acc_zero(acc);
   if (t.status == DSPARK_ST_OK && t.k == 0) {
     uint32_t* crow = a.dense + (size_t)r * a.V;
-    for (int i0 = i00; i0 < hi; i0 += kShardU * kShardBS) {
-      if (i0 != i00) {  // later batches (shards above kShardU * kShardBS ids)
+    const bool cvec = (reinterpret_cast<uintptr_t>(crow) & 15u) == 0u;  // the count row 16-byte aligned
+    uint64_t q = 0;
+    for (int i = lo + (int)threadIdx.x; i < a0; i += kShardBS) {  // head and tail
+      const uint32_t wb = __float_as_uint(cr_expf(sq_value<DT>(a, r, i) - t.m));
+      acc_add_q(acc, q, wb);
+      crow[i] = wb;
+    }
+    for (int i = a1 + (int)threadIdx.x; i < hi; i += kShardBS) {
+      const uint32_t wb = __float_as_uint(cr_expf(sq_value<DT>(a, r, i) - t.m));
+      acc_add_q(acc, q, wb);
+      crow[i] = wb;
+    }
+    for (int q0 = q00; q0 < q1; q0 += UV * kShardBS) {
+      if (q0 != q00) {
 #pragma unroll
-        for (int u = 0; u < kShardU; ++u) {
-          const int i = i0 + u * kShardBS;
-          x[u] = i < hi ? sq_value<DT>(a, r, i) : -__builtin_inff();
-        }
+        for (int u = 0; u < UV; ++u) xv[u] = q0 + u * kShardBS < q1 ? vrow[q0 + u * kShardBS] : uint4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < kShardU; ++u) {
-        const int i = i0 + u * kShardBS;
-        if (i < hi) {
-          const uint32_t wb = __float_as_uint(cr_expf(x[u] - t.m));
-          acc_add(acc, wb);
-          crow[i] = wb;
+      for (int u = 0; u < UV; ++u) {
+        const int qv = q0 + u * kShardBS;
+        if (qv < q1) {
+          const uint32_t v[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+          uint32_t w[EPV];
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const float x = DT == DSPARK_BF16 ? __uint_as_float((e & 1) ? (v[e >> 1] & 0xffff0000u) : (v[e >> 1] << 16))
+                                              : __uint_as_float(v[e]);
+            w[e] = __float_as_uint(cr_expf(x - t.m));
+            acc_add_q(acc, q, w[e]);
+          }
+          uint32_t* dst = crow + (size_t)qv * EPV;
+          if (cvec) {
+#pragma unroll
+            for (int h = 0; h < EPV / 4; ++h)
+              reinterpret_cast<uint4*>(dst)[h] = uint4{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) dst[e] = w[e];
+          }
         }
       }
     }
+    acc_fold(acc, q);
   }
   acc = block_acc_total(acc, s_a);
   if (threadIdx.x == 0) a.sums[b] = acc;
@@ -318,11 +348,18 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
   int lo, hi;
   shard_range(a.V, a.G, g, &lo, &hi);
   const uint32_t* crow = a.dense + (size_t)r * a.V;
-  constexpr int U = 4;  // loads in flight per thread
-  const int v00 = lo + (int)threadIdx.x;
-  uint32_t wb[U];  // the first weights: in flight while S64 is merged
+  // a 16-byte aligned count row: its middle [a0, a1) as vectors of four
+  // weights (UV per thread in flight), head and tail element by element;
+  // otherwise every weight on its own
+  const bool cvec = (reinterpret_cast<uintptr_t>(crow) & 15u) == 0u;
+  const int a0 = cvec ? ((lo + 3) / 4 * 4 < hi ? (lo + 3) / 4 * 4 : hi) : hi;
+  const int a1 = cvec ? (hi / 4 * 4 > a0 ? hi / 4 * 4 : a0) : hi;
+  constexpr int UV = 2;
+  const uint4* vrow = reinterpret_cast<const uint4*>(crow);
+  const int q1 = a1 / 4, q00 = a0 / 4 + (int)threadIdx.x;
+  uint4 wv[UV];  // the first weights: in flight while S64 is merged
 #pragma unroll
-  for (int u = 0; u < U; ++u) wb[u] = v00 + u * BS < hi ? crow[v00 + u * BS] : 0u;
+  for (int u = 0; u < UV; ++u) wv[u] = q00 + u * BS < q1 ? vrow[q00 + u * BS] : uint4{0u, 0u, 0u, 0u};
   for (int b = threadIdx.x; b < kTkBins; b += BS) sh.hist[b] = 0u;
   if (threadIdx.x < 64) {
     Acc s;
@@ -337,20 +374,30 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
   __syncthreads();
   const SumR S = sum_r(sh.s64);
   uint64_t fsum = 0, npos = 0;
-  for (int v0 = v00; v0 < hi; v0 += U * BS) {
-    if (v0 != v00) {
+  auto take = [&](uint32_t wb) {
+    uint32_t c;
+    double rr;
+    floor_rem(__uint_as_float(wb), S, c, rr);
+    fsum += c;
+    if (rr > 0.0) {
+      ++npos;
+      atomicAdd(&sh.hist[rem_key(rr) >> tk_shift(0)], 1u);
+    }
+  };
+  for (int v = lo + (int)threadIdx.x; v < a0; v += BS) take(crow[v]);  // head (or the whole shard)
+  for (int v = a1 + (int)threadIdx.x; v < hi; v += BS) take(crow[v]);  // tail
+  for (int q0 = q00; q0 < q1; q0 += UV * BS) {
+    if (q0 != q00) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) wb[u] = v0 + u * BS < hi ? crow[v0 + u * BS] : 0u;
+      for (int u = 0; u < UV; ++u) wv[u] = q0 + u * BS < q1 ? vrow[q0 + u * BS] : uint4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint32_t c;
-      double rr;
-      floor_rem(__uint_as_float(wb[u]), S, c, rr);
-      fsum += c;
-      if (rr > 0.0) {
-        ++npos;
-        atomicAdd(&sh.hist[rem_key(rr) >> tk_shift(0)], 1u);
+    for (int u = 0; u < UV; ++u) {
+      if (q0 + u * BS < q1) {
+        take(wv[u].x);
+        take(wv[u].y);
+        take(wv[u].z);
+        take(wv[u].w);
       }
     }
   }
@@ -382,16 +429,31 @@ __global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
   uint32_t* crow = a.dense + (size_t)r * a.V;
   TkShard* ts = a.tks + blockIdx.x;
   bool zero = t.status != DSPARK_ST_OK;
-  constexpr int U = 4;  // consecutive ids per thread, loads in flight together
-  const int vt0 = lo + (int)threadIdx.x * U;
+  // ids in order on a grid from A = lo rounded down to a multiple of 4: U
+  // consecutive ids per thread (two 16-byte vectors when the count row is
+  // 16-byte aligned and all U are in the shard), kSqChunk * 2 per pass
+  constexpr int U = 8;
+  static_assert(U * BS == 2 * kSqChunk, "two chunks per pass");
+  const int A = lo & ~3;
+  const bool cvec = (reinterpret_cast<uintptr_t>(crow) & 15u) == 0u;
+  auto load8 = [&](int vt, uint32_t (&w)[U]) {
+    if (cvec && vt >= lo && vt + U <= hi) {
+      const uint4 x0 = reinterpret_cast<const uint4*>(crow + vt)[0], x1 = reinterpret_cast<const uint4*>(crow + vt)[1];
+      w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
+      w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) w[u] = vt + u >= lo && vt + u < hi ? crow[vt + u] : 0u;
+    }
+  };
+  const int vt0 = A + (int)threadIdx.x * U;
   uint32_t wb[U];
   double s64 = 0.0;
   int64_t remaining = 0;
   if (!zero) {
     // everything this shard reads, issued together: its first weights, S64,
     // the merged histogram and the shards' floor sums
-#pragma unroll
-    for (int u = 0; u < U; ++u) wb[u] = vt0 + u < hi ? crow[vt0 + u] : 0u;
+    load8(vt0, wb);
     s64 = a.s64[r];
     const uint32_t* hrow = a.hist + (size_t)r * kTkBins;
     for (int b = threadIdx.x; b < kTkBins; b += BS) sh.hist[b] = hrow[b];
@@ -440,46 +502,57 @@ __global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
   uint32_t* fbuf = a.cflo + (size_t)blockIdx.x * kSqCandCap;
   uint32_t base = 0;
   uint64_t mass = 0;
-  for (int v0 = lo; v0 < hi; v0 += U * BS) {  // in id order
+  for (int v0 = A; v0 < hi; v0 += U * BS) {  // in id order
     const int vt = v0 + (int)threadIdx.x * U;
-    if (v0 != lo) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) wb[u] = vt + u < hi ? crow[vt + u] : 0u;
-    }
-    uint32_t c[U], nin = 0;
-    uint64_t key[U];
+    if (v0 != A) load8(vt, wb);
+    uint32_t c[U], nin = 0, tmass = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       double rr = 0.0;
       c[u] = 0;
-      if (vt + u < hi) floor_rem(__uint_as_float(wb[u]), S, c[u], rr);
-      key[u] = rr > 0.0 ? rem_key(rr) : 0ull;
-      const int bin = rr > 0.0 ? (int)(key[u] >> tk_shift(0)) : -1;
+      if (vt + u >= lo && vt + u < hi) floor_rem(__uint_as_float(wb[u]), S, c[u], rr);
+      const int bin = rr > 0.0 ? (int)(rem_key(rr) >> tk_shift(0)) : -1;
       c[u] += bin > d ? 1u : 0u;
+      tmass += c[u];
       c[u] |= bin == d ? kSqMark : 0u;
       nin += bin == d ? 1u : 0u;
     }
-    uint32_t tmass = 0;
-#pragma unroll
-    for (int u = 0; u < U; ++u) tmass += c[u] & ~kSqMark;
-    // one scan gives the candidates' positions (low word) and the chunk's mass (high word)
+    // one scan gives the candidates' positions (low word) and the masses
+    // (high word): thread kSqChunk / U starts the pass's second chunk
     uint64_t tot;
-    uint32_t pos = base + (uint32_t)block_excl_scan<uint64_t>(((uint64_t)tmass << 32) | nin, sh.bs, &tot);
+    const uint64_t pre = block_excl_scan<uint64_t>(((uint64_t)tmass << 32) | nin, sh.bs, &tot);
+    uint32_t pos = base + (uint32_t)pre;
     base += (uint32_t)tot;
     mass += tot >> 32;
-    if (threadIdx.x == 0) a.cmass[(size_t)blockIdx.x * kSqMaxChunks + (v0 - lo) / kSqChunk] = (uint32_t)(tot >> 32);
+    if (threadIdx.x == kSqChunk / U) {
+      const uint32_t m0 = (uint32_t)(pre >> 32);
+      uint32_t* cm = a.cmass + (size_t)blockIdx.x * kSqMaxChunks + (v0 - A) / kSqChunk;
+      cm[0] = m0;
+      cm[1] = (uint32_t)(tot >> 32) - m0;
+    }
+    if (cvec && vt >= lo && vt + U <= hi) {
+      uint4* dst = reinterpret_cast<uint4*>(crow + vt);
+      dst[0] = uint4{c[0], c[1], c[2], c[3]};
+      dst[1] = uint4{c[4], c[5], c[6], c[7]};
+    } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (vt + u < hi) {
+      for (int u = 0; u < U; ++u)
+        if (vt + u >= lo && vt + u < hi) crow[vt + u] = c[u];
+    }
+    if (nin) {  // the bin's members (a few per shard): ids, keys and floors in id order
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
         if (c[u] & kSqMark) {
           if (pos < (uint32_t)kSqCandCap) {
+            uint32_t cf;
+            double rr;
+            floor_rem(__uint_as_float(wb[u]), S, cf, rr);
             cbuf[pos] = (uint32_t)(vt + u);
-            kbuf[pos] = key[u];
+            kbuf[pos] = rem_key(rr);
             fbuf[pos] = c[u] & ~kSqMark;
           }
           ++pos;
         }
-        crow[vt + u] = c[u];
       }
     }
   }
@@ -754,13 +827,14 @@ __device__ int sq_sample_row(const ShardQArgs& a, int r, const TkRow& t, uint32_
       // the shard's chunk masses (stored by the cand pass) plus the bin's
       // winners in them give the chunk; only that chunk's counts are read
       const uint32_t* crow = a.dense + (size_t)r * a.V;
-      const int nch = (hi - lo + kSqChunk - 1) / kSqChunk;
+      const int A = lo & ~3;  // the cand pass's chunk grid
+      const int nch = (hi - A + kSqChunk - 1) / kSqChunk;
       for (int ci = threadIdx.x; ci < nch; ci += BS) sh.cm[ci] = a.cmass[((size_t)r * a.G + gs) * kSqMaxChunks + ci];
       if (threadIdx.x == 0) sh.cstar = -1;
       __syncthreads();
       const uint32_t o = sh.off[gs], ng = sh.off[gs + 1] - o;  // the bin's ids in this shard, resolved on chip
       for (uint32_t j = threadIdx.x; j < ng; j += BS)
-        if (sh.won[o + j]) atomicAdd(&sh.cm[(int)(sh.id[o + j] - (uint32_t)lo) / kSqChunk], 1u);
+        if (sh.won[o + j]) atomicAdd(&sh.cm[(int)(sh.id[o + j] - (uint32_t)A) / kSqChunk], 1u);
       __syncthreads();
       const uint32_t mc = (int)threadIdx.x < nch ? sh.cm[threadIdx.x] : 0u;  // nch <= kSqMaxChunks < BS
       uint32_t tot;
@@ -773,11 +847,11 @@ __device__ int sq_sample_row(const ShardQArgs& a, int r, const TkRow& t, uint32_
       const int cs = sh.cstar;
       if (cs >= 0) {
         const uint32_t cr = sh.crest;
-        const int vt = lo + cs * kSqChunk + 4 * (int)threadIdx.x;  // four consecutive ids per thread
+        const int vt = A + cs * kSqChunk + 4 * (int)threadIdx.x;  // four consecutive ids per thread
         uint32_t cc[4], ts = 0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          cc[u] = vt + u < hi ? crow[vt + u] : 0u;
+          cc[u] = vt + u >= lo && vt + u < hi ? crow[vt + u] : 0u;
           ts += cc[u];
         }
         uint32_t run = block_excl_scan<uint32_t>(ts, sh.bs, &tot);
