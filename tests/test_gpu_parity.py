@@ -328,7 +328,9 @@ def test_cr_expf_sampled_and_hard_cases():
     d = np.concatenate([
         rng.uniform(-104.0, 0.0, 1 << 20).astype(np.float32),
         -np.abs(rng.standard_normal(1 << 18)).astype(np.float32) * np.float32(1e-3),
-        np.array([0.0, -0.0, -np.inf, -104.0, -103.972, -87.33654, -1e-45], np.float32),
+        np.array([0.0, -0.0, -np.inf, -104.0, -103.972, -87.33654, -1e-45, -104.00001, -105.0, -1000.0,
+                  -3.4e38], np.float32),
+        rng.uniform(-104.0, -86.0, 1 << 16).astype(np.float32),  # subnormal and near-subnormal results
     ])
     y = np.exp(d.astype(np.float64))
     f = y.astype(np.float32).astype(np.float64)

@@ -3,7 +3,8 @@
 For many weights w over one exact sum S, the kernel takes the binary64
 quotient RN64(w / S) as RN64(q0 + e y) with y = RN64(1 / S), q0 = RN64(w y)
 and the residual e = w - S q0 taken with one fused multiply-add (exact for a
-faithful q0).  For a correctly rounded reciprocal and no underflow this is the
+faithful q0); the floors use it scaled by 2^24 (S 2^-24 and its reciprocal in
+place of S and y), which gives RN64(w / S) 2^24 exactly.  For a correctly rounded reciprocal and no underflow this is the
 correctly rounded quotient (Markstein's theorem; "Handbook of Floating-Point
 Arithmetic", division by fused multiply-add).  The kernel's operands are a
 binary32 weight in (0, 1] (subnormals included) and a binary64 sum in
@@ -42,6 +43,14 @@ int main(void) {
     const double q = fma(e, y, q0);
     if (q != w / s) {
       if (bad < 5) printf("w=%a s=%a div=%a recip=%a\n", w, s, w / s, q);
+      ++bad;
+    }
+    /* the scaled form the floors use: sm = s 2^-24, ym = RN(1 / sm) */
+    const double sm = s * 0x1p-24, ym = 1.0 / sm;
+    const double p0 = w * ym;
+    const double qs = fma(fma(-p0, sm, w), ym, p0);
+    if (qs != (w / s) * 16777216.0) {
+      if (bad < 5) printf("scaled: w=%a s=%a div=%a recip=%a\n", w, s, (w / s) * 16777216.0, qs);
       ++bad;
     }
   }

@@ -260,33 +260,14 @@ __device__ __forceinline__ uint64_t rem_key(double r) {
 // ------------------------------------------- correctly rounded exp, binary32
 #include "exp_table.inc"
 
-// The binary32 rounding of a binary64 value tv > 0 known to within 2^-51 of
-// x (relatively), when that decides RN32(x): tv farther than 2^-48 tv from
-// the binary32 rounding midpoint on its side.  Returns false otherwise.
-__device__ __forceinline__ bool rn32_decided(double tv, float* out) {
-  const float f = (float)tv;
-  const double g = (double)f;
-  *out = f;
-  if (g == tv) return true;
-  const uint32_t fb = __float_as_uint(f);
-  const float nb = __uint_as_float(tv > g ? fb + 1u : (fb ? fb - 1u : 0u));
-  return __builtin_fabs(tv - 0.5 * (g + (double)nb)) > 0x1p-48 * tv;
-}
-
-// RN32(exp(d)) for binary32 d <= 0 (or -inf).  Tang's table method in
+// RN32(exp(d)) for binary32 d <= 0 (or -inf), Tang's table method in
 // binary64: d = (64 e + j) ln2/64 + r with |r| <= ln2/128, exp(d) =
-// 2^e 2^(j/64) exp(r).  A first evaluation takes 2^(j/64) rounded to
-// binary64 and a degree-5 Taylor polynomial for exp(r) - 1 (truncation below
-// 2^-54.4): its relative error is below 2.4 * 2^-53 (the table entry and the
-// last fused multiply-add 2^-53 each, the reduced argument 2^-60.4), so its
-// binary32 rounding is the answer unless it lies within 2^-48 of a rounding
-// midpoint.  Those rare inputs take the accurate evaluation: a double-double
+// 2^e 2^(j/64) exp(r).  This is the accurate evaluation: a double-double
 // table entry, a degree-7 polynomial (truncation < 2^-74), and the product
 // kept as an unevaluated pair H + L (relative error about 2^-70), rounded to
 // binary32 once, with the side of a midpoint within 2^-48 decided from H and
-// L exactly.  The function is checked against an independent evaluation for
-// every binary32 d in [-104, 0].
-__device__ __forceinline__ float cr_expf(float d) {
+// L exactly.
+__device__ __forceinline__ float cr_expf_accurate(float d) {
   if (!(d > -104.0f)) return 0.0f;  // exp(-104) < 2^-150 rounds to 0; also -inf
   if (d == 0.0f) return 1.0f;
   const double dd = (double)d;
@@ -297,15 +278,6 @@ __device__ __forceinline__ float cr_expf(float d) {
   const double rhi = __builtin_fma(-kf, kExpCHi, dd);  // exact: k*C_HI is exact and close to d
   const double t = kf * kExpCLo;
   const double r1 = rhi - t;
-  {
-    double Q = __builtin_fma(r1, kExpP5, kExpP4);
-    Q = __builtin_fma(r1, Q, kExpP3);
-    Q = __builtin_fma(r1, Q, kExpP2);
-    const double q = __builtin_fma(r1 * r1, Q, r1);  // exp(r) - 1
-    const double T = kExpTabHi[j];
-    float f;
-    if (rn32_decided(__builtin_ldexp(__builtin_fma(T, q, T), e), &f)) return f;
-  }
   const double r2 = (rhi - r1) - t;  // r1 + r2 = rhi - t to ~2^-100
   double P = __builtin_fma(r1, kExpP7, kExpP6);
   P = __builtin_fma(r1, P, kExpP5);
@@ -333,6 +305,52 @@ __device__ __forceinline__ float cr_expf(float d) {
   if (delta > 0.0) return up;
   if (delta < 0.0) return dn;
   return (__float_as_uint(up) & 1u) ? dn : up;  // exact tie: even significand
+}
+
+// Half-width, in units in the last place of a binary64 value, of the band
+// around a binary32 rounding midpoint in which cr_expf's first evaluation
+// does not decide the rounding (its error is below 400 such units).
+constexpr uint32_t kExpBandUlps = 4096u;
+
+// RN32(exp(d)) for binary32 d <= 0 (or -inf; never NaN).  A first
+// evaluation, branch-free: k = RN(d 64/ln2) from the low word of
+// d 64/ln2 + 1.5 2^52, the reduced argument r in two fused multiply-adds, a
+// degree-4 Taylor polynomial for exp(r) - 1 (truncation below 2^-44.5 for
+// |r| <= ln2/128), and tv = 2^e 2^(j/64) (1 + (exp(r) - 1)) with a binary64
+// table entry: relative error below 2^-44.4, under 400 units in the last
+// place of tv.  For a normal binary32 result (d >= -87) the 29 low bits of
+// tv's significand are those that binary32 rounding drops, and the rounding
+// midpoint sits at 2^28 of them; unless tv lies within kExpBandUlps of it,
+// the binary32 rounding of tv is that of exp(d).  The band (a few values in
+// a million) and the subnormal results take the accurate evaluation; a wave
+// with no such lane skips it.  Checked against an independent evaluation for
+// every binary32 d in [-104, 0].
+// tab: the 64 entries kExpTabHi, from global memory or from an LDS copy
+// (exp_table_to_lds): in LDS the per-lane lookup stays off the vector
+// memory counter, so a loop's streamed loads need not drain to serve it.
+__device__ __forceinline__ float cr_expf(float d, const double* tab = kExpTabHi) {
+  const float dc = __builtin_fmaxf(d, -104.0f);
+  const double dd = (double)dc;
+  const double kb = __builtin_fma(dd, kExpInvL, 0x1.8p52);  // 1.5 2^52 + k
+  const int k = (int)(uint32_t)__double_as_longlong(kb);
+  const double kf = kb - 0x1.8p52;
+  double r = __builtin_fma(-kf, kExpCHi, dd);
+  r = __builtin_fma(-kf, kExpCLo, r);
+  double Q = __builtin_fma(r, kExpP4, kExpP3);
+  Q = __builtin_fma(r, Q, kExpP2);
+  const double q = __builtin_fma(r * r, Q, r);  // exp(r) - 1
+  const double T = tab[k & 63];
+  const double tv = __builtin_ldexp(__builtin_fma(T, q, T), k >> 6);
+  float f = (float)tv;
+  const uint32_t low = (uint32_t)__double_as_longlong(tv) & 0x1fffffffu;
+  const bool band = low - (0x10000000u - kExpBandUlps) <= 2u * kExpBandUlps;
+  if (__builtin_expect(band || (dc < -87.0f && dc > -104.0f), 0)) f = cr_expf_accurate(d);
+  return dc > -104.0f ? f : 0.0f;
+}
+
+// copies cr_expf's table into s[64] (the caller's barrier publishes it)
+__device__ __forceinline__ void exp_table_to_lds(double* s) {
+  for (int i = (int)threadIdx.x; i < 64; i += (int)blockDim.x) s[i] = kExpTabHi[i];
 }
 
 // ------------------------------------------------- exact weight accumulator

@@ -459,7 +459,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t count_rsrc(const DrawCtx& c) {
 }
 template <int DT>
 __device__ __forceinline__ uint32_t chunk_weight_bits(uint32_t b, const DrawCtx& c, const DrawShared& sh) {
-  return DT == DSPARK_BF16 ? bf16_weight_bits(b, c, sh) : __float_as_uint(cr_expf(__uint_as_float(b) - c.m));
+  return DT == DSPARK_BF16 ? bf16_weight_bits(b, c, sh)
+                            : __float_as_uint(cr_expf(__uint_as_float(b) - c.m, sh.etab));
 }
 template <int mode, int DT>
 __device__ __forceinline__ void stream_add(const ChunkData<DT>& d, int q, const DrawCtx& c, const DrawShared& sh,

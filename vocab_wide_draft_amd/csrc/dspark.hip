@@ -68,6 +68,7 @@ __global__ void __launch_bounds__(BS) rows_kernel(RowsArgs a) {
   __shared__ RowShared sh;
   constexpr int ES = DT == DSPARK_BF16 ? 2 : 4;
   const int b = blockIdx.x;
+  exp_table_to_lds(sh.etab);  // (published by the barriers of the row statistics)
   const bool is_draft = b < a.n_draft;
   const int r = is_draft ? b : b - a.n_draft;
   if (is_draft && a.skip_dense && a.do_q && (a.topk ? a.topk[r] : 0) == 0) return;  // (uniform)
@@ -472,7 +473,7 @@ __device__ __forceinline__ int draw_streamed(const void* p, int V, const DrawCtx
 template <int SRC>
 __device__ __forceinline__ uint32_t draw_weight_at(const void* p, int x, const DrawCtx& c, const DrawShared& sh) {
   if constexpr (SRC == kSrcF32) {
-    return __float_as_uint(cr_expf(static_cast<const float*>(p)[x] - c.m));
+    return __float_as_uint(cr_expf(static_cast<const float*>(p)[x] - c.m, sh.etab));
   } else {
     return bf16_weight_bits((uint32_t)static_cast<const uint16_t*>(p)[x], c, sh);
   }
@@ -497,6 +498,7 @@ __global__ void __launch_bounds__(BS) target_draw_kernel(DrawArgs a) {
   __shared__ DrawShared sh;
   const int r = blockIdx.x;
   if (a.deferred_only && a.token[r] != kTokDeferred) return;  // (the same value for every thread)
+  exp_table_to_lds(sh.etab);  // (published by the barriers of the row's head)
   const int es = SRC == kSrcF32 ? 4 : 2;
   const void* p = static_cast<const char*>(a.rows) + (size_t)r * (size_t)a.stride * es;
   Res R;
@@ -587,6 +589,7 @@ template <int SRC>
 __global__ void __launch_bounds__(BS) ratio_step_kernel(RatioArgs a) {
   __shared__ DrawShared sh;
   const int r = blockIdx.x;
+  exp_table_to_lds(sh.etab);  // (published by the barriers before the first weight)
   if (a.pos == 0) {
     // every valid draft row carries a token in [0, V) with q(token) > 0
     if (threadIdx.x == 0) {
@@ -803,8 +806,11 @@ __global__ void __launch_bounds__(BS) weights_kernel(const float* w, int n, int6
 }
 
 __global__ void cr_exp_kernel(const float* d, float* w, int64_t n) {
+  __shared__ double s_exp[64];  // the table as the streaming kernels read it
+  exp_table_to_lds(s_exp);
+  __syncthreads();
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) w[i] = cr_expf(d[i]);
+  if (i < n) w[i] = cr_expf(d[i], s_exp);
 }
 
 }  // namespace dspark

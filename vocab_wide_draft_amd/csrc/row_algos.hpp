@@ -140,6 +140,7 @@ struct SmemBase {
   int bi[8];
   uint64_t bu[4];
   int amin;                          // argmax: lowest index of the maximum
+  double etab[64];                   // cr_expf's table (exp_table_to_lds at the kernel's start)
 };
 // The generic / sparse row kernels add the compaction and support arrays.
 struct RowShared : SmemBase {

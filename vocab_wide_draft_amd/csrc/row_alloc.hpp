@@ -108,20 +108,26 @@ __device__ __forceinline__ void floor_rem(float w, double s64, uint32_t& c, doub
   c = (uint32_t)f;
   r = y - f;
 }
-// The same for many weights over one sum: S64 and y = RN64(1 / S64).  The
-// quotient comes from the reciprocal: q0 = RN64(w y) is within one ulp of
-// w / S64, e = w - S64 q0 is exact (one FMA), and RN64(q0 + e y) is the
-// correctly rounded quotient RN64(w / S64) (Markstein's theorem for a
-// correctly rounded reciprocal; no underflow here: w >= 2^-149, S64 < 2^21).
+// The same for many weights over one sum: S64 and y = RN64(1 / S64), and
+// their scaled forms sm = S64 2^-24 (exact) and ym = RN64(1 / sm) = 2^24 y.
+// The quotient comes from the reciprocal: q0 = RN64(w ym) is within one ulp
+// of w / sm, e = w - sm q0 is exact (one FMA), and RN64(q0 + e ym) is the
+// correctly rounded quotient RN64(w / sm) (Markstein's theorem for a
+// correctly rounded reciprocal), which is RN64(w / S64) 2^24 exactly: a
+// power-of-two scaling commutes with rounding away from underflow (w >=
+// 2^-149, 1 <= S64 < 2^21).
 struct SumR {
-  double s, y;
+  double s, y, sm, ym;
 };
-__device__ __forceinline__ SumR sum_r(double s64) { return SumR{s64, 1.0 / s64}; }
+__device__ __forceinline__ SumR sum_r(double s64) {
+  const double sm = s64 * 0x1p-24;
+  return SumR{s64, 1.0 / s64, sm, 1.0 / sm};
+}
 __device__ __forceinline__ void floor_rem(float w, const SumR& S, uint32_t& c, double& r) {
   const double wd = (double)w;
-  const double q0 = wd * S.y;
-  const double e = __builtin_fma(-q0, S.s, wd);
-  const double y = __builtin_fma(e, S.y, q0) * 16777216.0;
+  const double q0 = wd * S.ym;
+  const double e = __builtin_fma(-q0, S.sm, wd);
+  const double y = __builtin_fma(e, S.ym, q0);
   const double f = __builtin_floor(y);
   c = (uint32_t)f;
   r = y - f;
@@ -342,7 +348,7 @@ __device__ QOut dense_q(const Row<DT>& row, float m, uint32_t* drow, bool want_s
     uint32_t wb[EPV];
 #pragma unroll
     for (int l = 0; l < EPV; ++l) {
-      const float w = cr_expf(x[l] - m);  // x = -inf (or past V) gives 0
+      const float w = cr_expf(x[l] - m, sh.etab);  // x = -inf (or past V) gives 0
       wb[l] = __float_as_uint(w);
       if (l < nv) acc_add(acc, wb[l]);
     }

@@ -52,7 +52,17 @@ __device__ __forceinline__ bool head_better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-// one workgroup of kShardBS threads: the head of shard g of row r
+// one workgroup of kShardBS threads: the head of shard g of row r.  A
+// thread's ids are its head element, its vectors of the shard's 16-byte
+// aligned middle and its tail element, in increasing order.  A vector enters
+// by the IEEE maximum of its values, which is NaN when one of them is and
+// +inf when one of them is and none is NaN: one class test per vector flags
+// the shard, a strict comparison keeps the thread's first winning vector,
+// kept in registers, and the position inside it is found once, at the end;
+// then the head element (loaded first, compared last) wins ties and the
+// tail element does not.  NaN and +inf are told apart by a rescan of the
+// shard, which only a refused row makes.  The vector loop's trip count is
+// the same for every thread, so the flags stay wave-wide bit masks.
 template <int DT>
 __device__ __forceinline__ void shard_max_block(const void* data, int64_t stride, int r, int V, int G, int g,
                                                 ShardHead* out) {
@@ -61,48 +71,80 @@ __device__ __forceinline__ void shard_max_block(const void* data, int64_t stride
   __shared__ uint32_t s_f[kShardNW];
   int lo, hi;
   shard_range(V, G, g, &lo, &hi);
-  float bv = -__builtin_inff();
-  int bi = 0x7fffffff;
-  uint32_t fl = 0;
-  auto take = [&](float x, int i) {
-    fl |= (x != x ? 1u : 0u) | (x == __builtin_inff() ? 2u : 0u);
-    if (x > bv || (x == bv && x != -__builtin_inff() && i < bi)) {
-      bv = x;
-      bi = i;
-    }
-  };
-  // the shard's 16-byte aligned middle as vectors (rows start 16-byte
-  // aligned), its unaligned head and tail element by element
   constexpr int EPV = DT == DSPARK_BF16 ? 8 : 4;
+  constexpr uint32_t kBad = 0x203u;  // class mask: signalling NaN, quiet NaN, +inf
+  constexpr uint32_t kNegInf = DT == DSPARK_BF16 ? 0xff80ff80u : 0xff800000u;  // -inf in every slot
   const int a0 = (lo + EPV - 1) / EPV * EPV < hi ? (lo + EPV - 1) / EPV * EPV : hi;
   const int a1 = hi / EPV * EPV > a0 ? hi / EPV * EPV : a0;
-  for (int i = lo + (int)threadIdx.x; i < a0; i += kShardBS) take(shard_value<DT>(data, stride, r, i), i);
-  for (int i = a1 + (int)threadIdx.x; i < hi; i += kShardBS) take(shard_value<DT>(data, stride, r, i), i);
+  // at most one head and one tail element per thread (a0 - lo < EPV, hi - a1 < EPV)
+  const int ih = lo + (int)threadIdx.x, it = a1 + (int)threadIdx.x;
+  const float xh = ih < a0 ? shard_value<DT>(data, stride, r, ih) : -__builtin_inff();
+  const float xt = it < hi ? shard_value<DT>(data, stride, r, it) : -__builtin_inff();
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff;
+  bool in_vec = false;  // bi is a vector index, the position inside wv still to find
+  uint4 wv = uint4{kNegInf, kNegInf, kNegInf, kNegInf};
+  auto unpack = [](const uint4& v, float (&x)[EPV]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < EPV; ++e)
+      x[e] = DT == DSPARK_BF16 ? __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16))
+                               : __uint_as_float(w[e]);
+  };
   const int es = DT == DSPARK_BF16 ? 2 : 4;
   const uint4* vrow = reinterpret_cast<const uint4*>(static_cast<const char*>(data) + (size_t)r * (size_t)stride * es);
   const int q1 = a1 / EPV;
-  constexpr int UV = 4;  // vectors per thread in flight together
-  for (int q0 = a0 / EPV + (int)threadIdx.x; q0 < q1; q0 += UV * kShardBS) {
+  constexpr int UV = 6;  // vectors per thread in flight together
+  uint64_t bad_w = 0;
+  for (int qb = a0 / EPV; qb < q1; qb += UV * kShardBS) {
     uint4 v[UV];
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
-      const int q = q0 + u * kShardBS;
-      v[u] = q < q1 ? vrow[q] : uint4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+      const int q = qb + (int)threadIdx.x + u * kShardBS;
+      v[u] = q < q1 ? vrow[q] : uint4{kNegInf, kNegInf, kNegInf, kNegInf};  // -inf past the middle
     }
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
-      const int q = q0 + u * kShardBS;
-      if (q < q1) {
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      float x[EPV];
+      unpack(v[u], x);
+      float vm = x[0];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const float x = DT == DSPARK_BF16 ? __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16))
-                                            : __uint_as_float(w[e]);
-          take(x, q * EPV + e);
-        }
+      for (int e = 1; e < EPV; ++e) vm = __builtin_elementwise_maximum(vm, x[e]);
+      bad_w |= __builtin_amdgcn_ballot_w64(__builtin_amdgcn_class(vm, kBad));
+      if (vm > bv) {
+        bv = vm;
+        bi = qb + (int)threadIdx.x + u * kShardBS;
+        in_vec = true;
+        wv = v[u];
       }
     }
   }
+  if (in_vec) {  // the lowest position of bv inside the winning vector
+    float x[EPV];
+    unpack(wv, x);
+    int e0 = EPV - 1;
+#pragma unroll
+    for (int e = EPV - 1; e >= 0; --e)
+      if (x[e] == bv) e0 = e;
+    bi = bi * EPV + e0;
+    bv = x[e0];  // the value there (of -0 and +0, the one at the lowest position)
+  }
+  uint32_t bad = 0;
+  if (ih < a0) {
+    bad |= __builtin_amdgcn_class(xh, kBad) ? 1u : 0u;
+    if (xh >= bv) {  // (NaN never compares)
+      bv = xh;
+      bi = ih;
+    }
+  }
+  if (it < hi) {
+    bad |= __builtin_amdgcn_class(xt, kBad) ? 1u : 0u;
+    if (xt > bv) {
+      bv = xt;
+      bi = it;
+    }
+  }
+  const uint64_t wave_bad = __builtin_amdgcn_ballot_w64(bad != 0u) | bad_w;
   // a shard of -inf only has no maximum position (id INT32_MAX)
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -112,29 +154,43 @@ __device__ __forceinline__ void shard_max_block(const void* data, int64_t stride
       bv = ov;
       bi = oi;
     }
-    fl |= (uint32_t)__shfl_xor((int)fl, off);
   }
   if (lane_id() == 0) {
     s_v[wave_id()] = bv;
     s_i[wave_id()] = bi;
-    s_f[wave_id()] = fl;
+    s_f[wave_id()] = wave_bad ? 1u : 0u;
   }
   __syncthreads();
+  uint32_t any_bad = 0;
+#pragma unroll
+  for (int w = 0; w < kShardNW; ++w) any_bad |= s_f[w];
+  uint32_t fl = 0;
+  if (any_bad) {  // a refused row: NaN or +inf, told apart element by element
+    for (int i = lo + (int)threadIdx.x; i < hi; i += kShardBS) {
+      const float x = shard_value<DT>(data, stride, r, i);
+      fl |= (x != x ? 1u : 0u) | (x == __builtin_inff() ? 2u : 0u);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) fl |= (uint32_t)__shfl_xor((int)fl, off);
+    __syncthreads();
+    if (lane_id() == 0) s_f[wave_id()] = fl;
+    __syncthreads();
+  }
   if (threadIdx.x == 0) {
     for (int w = 1; w < kShardNW; ++w) {
       if (head_better(s_v[w], s_i[w], bv, bi)) {
         bv = s_v[w];
         bi = s_i[w];
       }
-      fl |= s_f[w];
+      if (any_bad) fl |= s_f[w];
     }
     *out = ShardHead{__float_as_uint(bv), bv == -__builtin_inff() ? 0x7fffffff : bi, fl, 0u};
   }
 }
 
 template <int DT>
-__global__ void __launch_bounds__(kShardBS) shard_max_kernel(const void* data, int64_t stride, int V, int G,
-                                                             ShardHead* heads) {
+__global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(8, 8)))
+shard_max_kernel(const void* data, int64_t stride, int V, int G, ShardHead* heads) {
   shard_max_block<DT>(data, stride, (int)blockIdx.x / G, V, G, (int)blockIdx.x % G, heads + blockIdx.x);
 }
 
@@ -185,6 +241,9 @@ template <int DT>
 __global__ void __launch_bounds__(kShardBS) shard_sum_kernel(const void* data, int64_t stride, int V, int G,
                                                              const ShardHead* heads, Acc* sums) {
   __shared__ Acc s_a[kShardNW];
+  __shared__ double s_exp[64];
+  exp_table_to_lds(s_exp);
+  __syncthreads();
   const int r = blockIdx.x / G, g = blockIdx.x % G;
   const ShardHead h = merge_heads(heads, r, G);
   const float m = __uint_as_float(h.max_bits);
@@ -195,7 +254,7 @@ __global__ void __launch_bounds__(kShardBS) shard_sum_kernel(const void* data, i
     shard_range(V, G, g, &lo, &hi);
     for (int i = lo + (int)threadIdx.x; i < hi; i += kShardBS) {
       const float x = shard_value<DT>(data, stride, r, i);
-      acc_add(a, __float_as_uint(cr_expf(x - m)));
+      acc_add(a, __float_as_uint(cr_expf(x - m, s_exp)));
     }
   }
   a = block_acc_total(a, s_a);

@@ -72,6 +72,15 @@ constexpr int kSqChunk = 4096;             // ids per count-mass chunk (two per 
 constexpr int kSqMaxChunks = DSPARK_V_MAX / kSqChunk;  // chunks a shard can have
 
 __host__ __device__ constexpr int tk_shift(int l) { return l < 5 ? 53 - 11 * l : 0; }
+// The first digit rem_key(rr) >> tk_shift(0) of a positive remainder, -1 for
+// rr = 0: for rr >= 2^-11 the key is 2^63 + rr 2^63, whose top 11 bits are
+// 1024 + floor(rr 2^10) (rr 2^10 is exact); below, the key is rr's binary64
+// pattern, whose top 11 bits are the high word's.
+__device__ __forceinline__ int sq_first_digit(double rr) {
+  const int big = (int)(rr * 1024.0) | 1024;
+  const int small = (int)((uint32_t)((uint64_t)__double_as_longlong(rr) >> 32) >> 21);
+  return rr >= 0x1p-11 ? big : (rr > 0.0 ? small : -1);
+}
 __host__ __device__ constexpr int tk_bins(int l) { return l < 5 ? 2048 : 512; }
 
 struct TkShard {  // what one shard sends for its row
@@ -150,7 +159,7 @@ struct ShardQArgs {
 // (row, shard) workgroups: the shard heads of the draft rows, then (Gt
 // shards per row) of the target rows
 template <int DT>
-__global__ void __launch_bounds__(kShardBS) sq_max_kernel(ShardQArgs a) {
+__global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(8, 8))) sq_max_kernel(ShardQArgs a) {
   const int nd = a.n_rows * a.G;
   const int b = blockIdx.x;
   if (b < nd) shard_max_block<DT>(a.data, a.stride, b / a.G, a.V, a.G, b % a.G, a.heads + b);
@@ -222,9 +231,10 @@ __device__ __forceinline__ TkRow sq_row_state(const ShardQArgs& a, float m, uint
 // the row's count storage for the passes that follow.  Workgroups past the
 // draft rows' merge the target rows' heads into their argmax and status.
 template <int DT>
-__global__ void __launch_bounds__(kShardBS) sq_sum_kernel(ShardQArgs a) {
+__global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(8, 8))) sq_sum_kernel(ShardQArgs a) {
   __shared__ Acc s_a[kShardNW];
   __shared__ TkRow s_t;
+  __shared__ double s_exp[64];
   const int nd = a.n_rows * a.G;
   const int b = blockIdx.x;
   if (b >= nd) {  // a target row (uniform)
@@ -273,6 +283,7 @@ __global__ void __launch_bounds__(kShardBS) sq_sum_kernel(ShardQArgs a) {
       }
     }
   }
+  exp_table_to_lds(s_exp);
   if (g == 0) {
     for (int i = threadIdx.x; i < kTkBins; i += kShardBS) a.hist[(size_t)r * kTkBins + i] = 0u;
     if (a.vfy && r % DSPARK_N_DRAFT == 0 && threadIdx.x == 0) a.req_cnt[r / DSPARK_N_DRAFT] = 0u;
@@ -286,12 +297,12 @@ __global__ void __launch_bounds__(kShardBS) sq_sum_kernel(ShardQArgs a) {
     const bool cvec = (reinterpret_cast<uintptr_t>(crow) & 15u) == 0u;  // the count row 16-byte aligned
     uint64_t q = 0;
     for (int i = lo + (int)threadIdx.x; i < a0; i += kShardBS) {  // head and tail
-      const uint32_t wb = __float_as_uint(cr_expf(sq_value<DT>(a, r, i) - t.m));
+      const uint32_t wb = __float_as_uint(cr_expf(sq_value<DT>(a, r, i) - t.m, s_exp));
       acc_add_q(acc, q, wb);
       crow[i] = wb;
     }
     for (int i = a1 + (int)threadIdx.x; i < hi; i += kShardBS) {
-      const uint32_t wb = __float_as_uint(cr_expf(sq_value<DT>(a, r, i) - t.m));
+      const uint32_t wb = __float_as_uint(cr_expf(sq_value<DT>(a, r, i) - t.m, s_exp));
       acc_add_q(acc, q, wb);
       crow[i] = wb;
     }
@@ -310,7 +321,7 @@ __global__ void __launch_bounds__(kShardBS) sq_sum_kernel(ShardQArgs a) {
           for (int e = 0; e < EPV; ++e) {
             const float x = DT == DSPARK_BF16 ? __uint_as_float((e & 1) ? (v[e >> 1] & 0xffff0000u) : (v[e >> 1] << 16))
                                               : __uint_as_float(v[e]);
-            w[e] = __float_as_uint(cr_expf(x - t.m));
+            w[e] = __float_as_uint(cr_expf(x - t.m, s_exp));
             acc_add_q(acc, q, w[e]);
           }
           uint32_t* dst = crow + (size_t)qv * EPV;
@@ -379,9 +390,10 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
     double rr;
     floor_rem(__uint_as_float(wb), S, c, rr);
     fsum += c;
-    if (rr > 0.0) {
+    const int bin = sq_first_digit(rr);
+    if (bin >= 0) {
       ++npos;
-      atomicAdd(&sh.hist[rem_key(rr) >> tk_shift(0)], 1u);
+      atomicAdd(&sh.hist[bin], 1u);
     }
   };
   for (int v = lo + (int)threadIdx.x; v < a0; v += BS) take(crow[v]);  // head (or the whole shard)
@@ -456,7 +468,12 @@ __global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
     load8(vt0, wb);
     s64 = a.s64[r];
     const uint32_t* hrow = a.hist + (size_t)r * kTkBins;
-    for (int b = threadIdx.x; b < kTkBins; b += BS) sh.hist[b] = hrow[b];
+    static_assert(kTkBins % BS == 0, "whole histogram rows per thread");
+    uint32_t hv[kTkBins / BS];  // all loads in flight before the first LDS write
+#pragma unroll
+    for (int j = 0; j < kTkBins / BS; ++j) hv[j] = hrow[threadIdx.x + j * BS];
+#pragma unroll
+    for (int j = 0; j < kTkBins / BS; ++j) sh.hist[threadIdx.x + j * BS] = hv[j];
     if (threadIdx.x < 64) {
       uint64_t f = 0, n = 0;
       if ((int)threadIdx.x < a.G) {
@@ -511,7 +528,7 @@ __global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
       double rr = 0.0;
       c[u] = 0;
       if (vt + u >= lo && vt + u < hi) floor_rem(__uint_as_float(wb[u]), S, c[u], rr);
-      const int bin = rr > 0.0 ? (int)(rem_key(rr) >> tk_shift(0)) : -1;
+      const int bin = sq_first_digit(rr);
       c[u] += bin > d ? 1u : 0u;
       tmass += c[u];
       c[u] |= bin == d ? kSqMark : 0u;
@@ -619,7 +636,7 @@ __device__ int sq_resolve_row(const ShardQArgs& a, int r, const TkRow& t, const 
   auto key_of = [&](int v) {
     uint32_t c;
     double rr;
-    floor_rem(cr_expf(sq_value<DT>(a, r, v) - m), S, c, rr);
+    floor_rem(cr_expf(sq_value<DT>(a, r, v) - m, sh.etab), S, c, rr);
     return rem_key(rr);
   };
   if (threadIdx.x == 0) sh.general = n > (uint32_t)kSqCandCap ? 1 : 0;  // (read after later barriers)
@@ -899,6 +916,7 @@ __global__ void __launch_bounds__(BS) sq_finish_kernel(ShardQArgs a) {
   const int r = blockIdx.x;
   const TkRow t = a.tkr[r];
   if (t.status == kSqNotMine) return;  // (the same for every thread)
+  exp_table_to_lds(sh.etab);  // (published by the barriers before the resolution)
   const uint32_t u = a.draws ? a.draws[r] : 0u;  // row-level reads issued together
   const double s64 = t.k == 0 && a.dense ? a.s64[r] : 0.0;
   int st = t.status;
