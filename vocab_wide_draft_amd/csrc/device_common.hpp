@@ -238,6 +238,14 @@ __device__ __forceinline__ T block_excl_scan(T v, BlockScratch& s, T* total) {
   return r;
 }
 
+// a value that is the same in every lane, moved to scalar registers
+__device__ __forceinline__ double uniform_f64(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
 // ------------------------------------------------------------------- keys
 // Order-preserving map of a non-NaN binary32 to uint32; -0 and +0 map to the
 // same key (IEEE equality).  NaN never reaches it.
@@ -384,17 +392,31 @@ __device__ __forceinline__ void acc_add(Acc& a, uint32_t wb, uint32_t n = 1) {
     add128(a.tlo, a.thi, lo, hi);
   }
 }
-// A faster tier for many weights: weights of at least 2^-24 (exponent field
-// E >= 103) are integers in units of 2^-47 below 2^48, added in a 64-bit
-// word q (2^16 of them fit); smaller ones go to the accumulator.  acc_fold
-// adds q to the accumulator's main word (units 2^-70: q * 2^23).
-__device__ __forceinline__ void acc_add_q(Acc& a, uint64_t& q, uint32_t wb) {
+// A faster tier for many weights, without branches for the usual ones:
+// weights of at least 2^-24 (exponent field E >= 103) are integers in units
+// of 2^-47 below 2^48, added in the 64-bit word hi; weights in [2^-47,
+// 2^-24) (80 <= E < 103) are integers in units of 2^-70 below 2^47, added
+// in the 64-bit word lo.  Each word takes 2^16 additions.  Smaller weights
+// go to the accumulator.  acc_fold adds both words to the accumulator's
+// main word (units 2^-70: hi 2^23 + lo).
+struct AccQ {
+  uint64_t hi, lo;
+};
+__device__ __forceinline__ void accq_zero(AccQ& q) { q.hi = q.lo = 0; }
+__device__ __forceinline__ void acc_add_q(Acc& a, AccQ& q, uint32_t wb) {
   wb &= 0x7fffffffu;
   const uint32_t E = wb >> 23;
-  if (E >= 103u) q += (uint64_t)((wb & 0x7fffffu) | 0x800000u) << (E - 103u);
-  else if (wb) acc_add(a, wb);
+  const uint64_t mant = (wb & 0x7fffffu) | 0x800000u;
+  const bool big = E >= 103u;
+  const uint64_t v = mant << ((big ? E - 103u : E - 80u) & 63u);
+  q.hi += big ? v : 0ull;
+  q.lo += !big && E >= 80u ? v : 0ull;
+  if (E < 80u && wb) acc_add(a, wb);
 }
-__device__ __forceinline__ void acc_fold(Acc& a, uint64_t q) { add128(a.mlo, a.mhi, q << 23, q >> 41); }
+__device__ __forceinline__ void acc_fold(Acc& a, const AccQ& q) {
+  add128(a.mlo, a.mhi, q.hi << 23, q.hi >> 41);
+  add128(a.mlo, a.mhi, q.lo, 0ull);
+}
 struct AccScratch {
   Acc w[NW];
   double s64;

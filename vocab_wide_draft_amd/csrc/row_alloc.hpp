@@ -128,9 +128,8 @@ __device__ __forceinline__ void floor_rem(float w, const SumR& S, uint32_t& c, d
   const double q0 = wd * S.ym;
   const double e = __builtin_fma(-q0, S.sm, wd);
   const double y = __builtin_fma(e, S.ym, q0);
-  const double f = __builtin_floor(y);
-  c = (uint32_t)f;
-  r = y - f;
+  c = (uint32_t)y;                 // y >= 0: truncation is the floor
+  r = __builtin_amdgcn_fract(y);  // y - floor(y), exact
 }
 
 // Finishes a threshold inside one bucket of the remainder keys when the

@@ -72,14 +72,29 @@ constexpr int kSqChunk = 4096;             // ids per count-mass chunk (two per 
 constexpr int kSqMaxChunks = DSPARK_V_MAX / kSqChunk;  // chunks a shard can have
 
 __host__ __device__ constexpr int tk_shift(int l) { return l < 5 ? 53 - 11 * l : 0; }
-// The first digit rem_key(rr) >> tk_shift(0) of a positive remainder, -1 for
-// rr = 0: for rr >= 2^-11 the key is 2^63 + rr 2^63, whose top 11 bits are
-// 1024 + floor(rr 2^10) (rr 2^10 is exact); below, the key is rr's binary64
-// pattern, whose top 11 bits are the high word's.
+// The first digit rem_key(rr) >> tk_shift(0) of a remainder rr in (0, 1),
+// from the bits alone (no branch): for rr >= 2^-11 (exponent field e >=
+// 1012) the key is 2^63 + rr 2^63, whose top 11 bits are 1024 + floor(rr
+// 2^10), the 21-bit high part of the significand shifted right by 1033 - e
+// (11 to 21); below, the key is rr's binary64 pattern, whose top 11 bits are
+// the high word's (at most 505).
 __device__ __forceinline__ int sq_first_digit(double rr) {
-  const int big = (int)(rr * 1024.0) | 1024;
-  const int small = (int)((uint32_t)((uint64_t)__double_as_longlong(rr) >> 32) >> 21);
-  return rr >= 0x1p-11 ? big : (rr > 0.0 ? small : -1);
+  const uint32_t hi = (uint32_t)((uint64_t)__double_as_longlong(rr) >> 32);
+  const uint32_t e = hi >> 20;
+  const uint32_t big = (((hi & 0xfffffu) | 0x100000u) >> ((1033u - e) & 31u)) | 1024u;
+  return (int)(e >= 1012u ? big : hi >> 21);
+}
+// The remainders whose first digit is d form [lo, hi): the inverse of
+// sq_first_digit (digits 506 to 1023 are never taken).  No digit (d outside
+// [0, kTkBins)) gives the empty range at +inf.
+struct DigitRange {
+  double lo, hi;
+};
+__device__ __forceinline__ DigitRange sq_digit_range(int d) {
+  if (d < 0 || d >= kTkBins) return DigitRange{__builtin_inf(), __builtin_inf()};
+  if (d >= 1024) return DigitRange{d == 1024 ? 0x1p-11 : (double)(d - 1024) / 1024.0, (double)(d - 1023) / 1024.0};
+  return DigitRange{d == 0 ? 0x1p-1074 : __longlong_as_double((long long)((uint64_t)d << 53)),
+                    __longlong_as_double((long long)((uint64_t)(d + 1) << 53))};
 }
 __host__ __device__ constexpr int tk_bins(int l) { return l < 5 ? 2048 : 512; }
 
@@ -231,7 +246,8 @@ __device__ __forceinline__ TkRow sq_row_state(const ShardQArgs& a, float m, uint
 // the row's count storage for the passes that follow.  Workgroups past the
 // draft rows' merge the target rows' heads into their argmax and status.
 template <int DT>
-__global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(8, 8))) sq_sum_kernel(ShardQArgs a) {
+__global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(DT == DSPARK_BF16 ? 6 : 8, 8)))
+sq_sum_kernel(ShardQArgs a) {
   __shared__ Acc s_a[kShardNW];
   __shared__ TkRow s_t;
   __shared__ double s_exp[64];
@@ -258,7 +274,7 @@ __global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(8
   // the shard's 16-byte aligned middle [a0, a1) as vectors of EPV logits (rows
   // start 16-byte aligned), its head and tail element by element
   constexpr int EPV = DT == DSPARK_BF16 ? 8 : 4;
-  constexpr int UV = DT == DSPARK_BF16 ? 1 : 2;  // vectors per thread in flight (8 logits)
+  constexpr int UV = 1;  // vectors per thread in flight (4 or 8 logits)
   const int a0 = (lo + EPV - 1) / EPV * EPV < hi ? (lo + EPV - 1) / EPV * EPV : hi;
   const int a1 = hi / EPV * EPV > a0 ? hi / EPV * EPV : a0;
   const int es = DT == DSPARK_BF16 ? 2 : 4;
@@ -295,7 +311,8 @@ __global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(8
   if (t.status == DSPARK_ST_OK && t.k == 0) {
     uint32_t* crow = a.dense + (size_t)r * a.V;
     const bool cvec = (reinterpret_cast<uintptr_t>(crow) & 15u) == 0u;  // the count row 16-byte aligned
-    uint64_t q = 0;
+    AccQ q;
+    accq_zero(q);
     for (int i = lo + (int)threadIdx.x; i < a0; i += kShardBS) {  // head and tail
       const uint32_t wb = __float_as_uint(cr_expf(sq_value<DT>(a, r, i) - t.m, s_exp));
       acc_add_q(acc, q, wb);
@@ -306,6 +323,7 @@ __global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(8
       acc_add_q(acc, q, wb);
       crow[i] = wb;
     }
+    // the next UV vectors are loaded before the current ones are taken
     for (int q0 = q00; q0 < q1; q0 += UV * kShardBS) {
       if (q0 != q00) {
 #pragma unroll
@@ -384,20 +402,21 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
   }
   __syncthreads();
   const SumR S = sum_r(sh.s64);
-  uint64_t fsum = 0, npos = 0;
+  uint32_t fsum = 0, npos = 0;  // (a row's floors add up to at most about 2^24)
   auto take = [&](uint32_t wb) {
     uint32_t c;
     double rr;
     floor_rem(__uint_as_float(wb), S, c, rr);
     fsum += c;
-    const int bin = sq_first_digit(rr);
-    if (bin >= 0) {
+    if (rr > 0.0) {
       ++npos;
-      atomicAdd(&sh.hist[bin], 1u);
+      atomicAdd(&sh.hist[sq_first_digit(rr)], 1u);
     }
   };
   for (int v = lo + (int)threadIdx.x; v < a0; v += BS) take(crow[v]);  // head (or the whole shard)
   for (int v = a1 + (int)threadIdx.x; v < hi; v += BS) take(crow[v]);  // tail
+  // the middle: the next UV vectors are loaded before the current ones are
+  // taken; a vector past the middle reads as zeros, which add nothing
   for (int q0 = q00; q0 < q1; q0 += UV * BS) {
     if (q0 != q00) {
 #pragma unroll
@@ -413,15 +432,15 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
       }
     }
   }
-  fsum = block_sum<uint64_t>(fsum, sh.bs);
-  npos = block_sum<uint64_t>(npos, sh.bs);
+  const uint64_t fsum_b = block_sum<uint64_t>(fsum, sh.bs);
+  const uint64_t npos_b = block_sum<uint64_t>(npos, sh.bs);
   __syncthreads();
   uint32_t* hrow = a.hist + (size_t)r * kTkBins;
   for (int b = threadIdx.x; b < kTkBins; b += BS)
     if (sh.hist[b]) atomicAdd(&hrow[b], sh.hist[b]);
   if (threadIdx.x == 0) {
-    a.tks[blockIdx.x].fsum = fsum;
-    a.tks[blockIdx.x].npos = npos;
+    a.tks[blockIdx.x].fsum = fsum_b;
+    a.tks[blockIdx.x].npos = npos_b;
   }
 }
 
@@ -431,7 +450,7 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
 // the bin and the floor below it, flags the ids inside the bin (kSqMark) and
 // keeps the first kSqCandCap of them, and sends its count mass so far.  A
 // refused or inconsistent row's shard is zeroed.
-__global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
+__global__ void __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(8, 8))) sq_cand_kernel(ShardQArgs a) {
   __shared__ SqShared sh;
   const int r = blockIdx.x / a.G, g = blockIdx.x % a.G;
   const TkRow t = a.tkr[r];
@@ -513,7 +532,13 @@ __global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
     d = block_find_crossing(sh.hist, kTkBins, (uint64_t)remaining, false, sh, &before);
     need = (uint64_t)remaining - before;
   }
-  const SumR S = sum_r(s64);
+  // the row's constants of the loop, held in scalar registers (the same in every thread)
+  SumR S = sum_r(s64);
+  S.sm = uniform_f64(S.sm);
+  S.ym = uniform_f64(S.ym);
+  DigitRange dr = sq_digit_range(d);  // (no bin: nothing above it, nothing inside it)
+  dr.lo = uniform_f64(dr.lo);
+  dr.hi = uniform_f64(dr.hi);
   uint32_t* cbuf = a.cids + (size_t)blockIdx.x * kSqCandCap;
   uint64_t* kbuf = a.ckeys + (size_t)blockIdx.x * kSqCandCap;
   uint32_t* fbuf = a.cflo + (size_t)blockIdx.x * kSqCandCap;
@@ -524,15 +549,14 @@ __global__ void __launch_bounds__(BS) sq_cand_kernel(ShardQArgs a) {
     if (v0 != A) load8(vt, wb);
     uint32_t c[U], nin = 0, tmass = 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      double rr = 0.0;
-      c[u] = 0;
-      if (vt + u >= lo && vt + u < hi) floor_rem(__uint_as_float(wb[u]), S, c[u], rr);
-      const int bin = sq_first_digit(rr);
-      c[u] += bin > d ? 1u : 0u;
+    for (int u = 0; u < U; ++u) {  // (ids outside the shard read weight 0: count 0, remainder 0)
+      double rr;
+      floor_rem(__uint_as_float(wb[u]), S, c[u], rr);
+      const bool above = rr >= dr.hi, inside = rr >= dr.lo && !above;  // first digit > d, == d
+      c[u] += above ? 1u : 0u;
       tmass += c[u];
-      c[u] |= bin == d ? kSqMark : 0u;
-      nin += bin == d ? 1u : 0u;
+      c[u] |= inside ? kSqMark : 0u;
+      nin += inside ? 1u : 0u;
     }
     // one scan gives the candidates' positions (low word) and the masses
     // (high word): thread kSqChunk / U starts the pass's second chunk
