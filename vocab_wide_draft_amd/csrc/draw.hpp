@@ -408,7 +408,7 @@ __device__ __forceinline__ void chunk_load_values(const Row<DT>& row, int q, Chu
   const int base = q * E;
   const int nv = row.V - base < E ? row.V - base : E;
   if (nv == E) {
-    const uint4 u = reinterpret_cast<const uint4*>(row.p)[q];
+    const uint4 u = ld_nt(reinterpret_cast<const uint4*>(row.p) + q);
     const uint32_t v[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < ChunkData<DT>::NW_; ++i) d.w[i] = v[i];

@@ -101,7 +101,7 @@ __device__ __forceinline__ void shard_max_block(const void* data, int64_t stride
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
       const int q = qb + (int)threadIdx.x + u * kShardBS;
-      v[u] = q < q1 ? vrow[q] : uint4{kNegInf, kNegInf, kNegInf, kNegInf};  // -inf past the middle
+      v[u] = q < q1 ? ld_nt(vrow + q) : uint4{kNegInf, kNegInf, kNegInf, kNegInf};  // -inf past the middle
     }
 #pragma unroll
     for (int u = 0; u < UV; ++u) {

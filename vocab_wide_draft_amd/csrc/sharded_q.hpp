@@ -282,7 +282,7 @@ sq_sum_kernel(ShardQArgs a) {
   const int q1 = a1 / EPV, q00 = a0 / EPV + (int)threadIdx.x;
   uint4 xv[UV];  // the first loads: they need no m, so they fly during the merge
 #pragma unroll
-  for (int u = 0; u < UV; ++u) xv[u] = q00 + u * kShardBS < q1 ? vrow[q00 + u * kShardBS] : uint4{0u, 0u, 0u, 0u};
+  for (int u = 0; u < UV; ++u) xv[u] = q00 + u * kShardBS < q1 ? ld_nt(vrow + q00 + u * kShardBS) : uint4{0u, 0u, 0u, 0u};
   if (threadIdx.x < 64) {
     const int k = a.topk ? a.topk[r] : 0;  // (loads in flight with the heads')
     const uint32_t u = a.draws ? a.draws[r] : 0u;
@@ -327,7 +327,7 @@ sq_sum_kernel(ShardQArgs a) {
     for (int q0 = q00; q0 < q1; q0 += UV * kShardBS) {
       if (q0 != q00) {
 #pragma unroll
-        for (int u = 0; u < UV; ++u) xv[u] = q0 + u * kShardBS < q1 ? vrow[q0 + u * kShardBS] : uint4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < UV; ++u) xv[u] = q0 + u * kShardBS < q1 ? ld_nt(vrow + q0 + u * kShardBS) : uint4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < UV; ++u) {
