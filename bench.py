@@ -539,8 +539,8 @@ def step_line(cfg: int, args):
                    "requests_per_s": round(w.R / (ms_per_step * 1e-3), 1),
                    "rows_failed": int((st != 0).sum()), "launch": launch,
                    "ms_per_step_by_launch": {k: round(v[1], 4) for k, v in times.items()},
-                   "parallelism": "single GPU, one workgroup per row (fewer than 512 streamed draft rows: "
-                                  "vocabulary shards per dense row)"},
+                   "parallelism": "single GPU; bf16 rows: one workgroup per row; streamed dense rows: "
+                                  "vocabulary shards per row, a workgroup per shard and pass"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name),
                      "algorithmic_bytes": alg, "kernel_ms": round(mean_launch, 4)},

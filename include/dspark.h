@@ -367,12 +367,13 @@ int dspark_cr_expf(const float* d, float* w, int64_t n, void* stream);
  * sample, 3 verify, 4 fused, 5 q_alloc_weights; n_rows = draft rows).  No
  * entry point needs one (ws may be NULL with ws_bytes 0).  dspark_q_alloc
  * and dspark_fused use a workspace of at least this size, 256-byte aligned,
- * to split each dense-q draft row that is streamed from memory (float32
- * rows, bf16 rows above 131072 ids) over several workgroups -- the rows'
- * vocabulary shards, merged as dspark_sharded_q merges them -- which fills
- * the chip when there are few rows; the results are the same either way.
- * It returns 0 where splitting does not apply (other ops, or 512 or more
- * draft rows). */
+ * to run each dense-q draft row that is streamed from memory (float32
+ * rows, bf16 rows above 131072 ids) through the split pipeline: the row's
+ * vocabulary shards (min(64, 2048 / rows) of them, at least one), each a
+ * workgroup per pass, merged as dspark_sharded_q merges them -- which fills
+ * the chip when there are few rows and is faster than one workgroup per row
+ * at every batch size; the results are the same either way.  It returns 0
+ * where splitting does not apply (other ops, no draft rows). */
 size_t dspark_workspace_bytes(int32_t op, int64_t n_rows, int64_t vocab, int32_t k_max);
 
 const char* dspark_q_semantic_id(void); /* "dyadic24-standard-v1" [Q] */

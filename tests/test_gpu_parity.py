@@ -406,6 +406,39 @@ def test_value_table_rows(V):
             check_draft_row(f, j, ref, k, label=f"table fused V{V} k{k} {names[j]}")
 
 
+@pytest.mark.parametrize("R", [120, 210])  # 600 draft rows (3 shards per row), 1,050 (one shard per row)
+def test_split_many_rows_equal_one_workgroup_rows(R):
+    """Batches past a round of the chip still take the split pipeline (one
+    shard per row from 1,024 draft rows on; the target rows' heads with it):
+    every output equals the one-workgroup path's (the confidence within the
+    tolerance), and sampled rows, the edge rows among them, equal the
+    oracle's."""
+    V = 3000
+    rng = np.random.default_rng(R)
+    dr = (rng.standard_normal((5 * R, V)) * 3).astype(np.float32)
+    dr[7, 11] = np.nan
+    dr[300, :V // 2] = -np.inf
+    dr[401] = -2.5
+    dr[5 * R - 1, [0, V - 1]] = dr[5 * R - 1].max() + 2
+    tg = (rng.standard_normal((6 * R, V)) * 3).astype(np.float32)
+    tg[5, 7] = np.inf
+    tg[6 * R - 1, [1, V - 2]] = tg[6 * R - 1].max() + 2
+    topk = np.zeros(5 * R, np.int32)
+    draws = rng.integers(0, 1 << 24, 5 * R, dtype=np.uint32)
+    d, t = to_dev(dr, F32), to_dev(tg, F32)
+    a = host(B.fused(d, t, B.SAMPLED, topk=topk, draws=u32_dev(draws), split=True))
+    b = host(B.fused(d, t, B.SAMPLED, topk=topk, draws=u32_dev(draws), split=False))
+    torch.cuda.synchronize()
+    for k in ("argmax", "status", "sample", "target_argmax", "target_status", "accept_len", "bonus", "req_status"):
+        assert np.array_equal(a[k], b[k]), k
+    assert np.array_equal(a["q"]["dense"], b["q"]["dense"])
+    assert np.allclose(a["conf"], b["conf"], rtol=1e-6, atol=0)
+    assert a["target_argmax"][6 * R - 1] == 1 and a["target_status"][5] != 0
+    for j in sorted({0, 7, 300, 401, 5 * R - 1, *rng.integers(0, 5 * R, 6).tolist()}):
+        ref = O.draft_row(dr[j], F32, 0, int(draws[j]))
+        check_draft_row(a, j, ref, 0, "split, many rows")
+
+
 @pytest.mark.parametrize("cfg", [1, 3])
 def test_split_all_dense_rows_verify_in_the_last_row(cfg):
     """Every draft row dense and few rows: the split pipeline takes all rows,
