@@ -36,7 +36,13 @@ def test_host_queries():
     for code, name in B.STATUS_NAMES.items():
         assert B.status_name(code) == name
     assert B.status_name(99) == "UNKNOWN"
-    assert B.workspace_bytes(4, 5120, 129280, 1024) == 0
+    # the split pipeline's workspace: for the fused step and q_alloc at every batch size, for nothing else
+    for n in (1, 320, 5120):
+        assert B.workspace_bytes(4, n, 129280, 1024) == B.workspace_bytes(1, n, 129280, 0) > 0
+    assert B.workspace_bytes(4, 5120, 129280, 0) > B.workspace_bytes(4, 320, 129280, 0)
+    for op in (0, 2, 3, 5):
+        assert B.workspace_bytes(op, 320, 129280, 0) == 0
+    assert B.workspace_bytes(4, 0, 129280, 0) == 0
 
 
 def test_argument_errors_enqueue_nothing():
