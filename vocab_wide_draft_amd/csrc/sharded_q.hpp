@@ -73,16 +73,14 @@ constexpr int kSqMaxChunks = DSPARK_V_MAX / kSqChunk;  // chunks a shard can hav
 
 __host__ __device__ constexpr int tk_shift(int l) { return l < 5 ? 53 - 11 * l : 0; }
 // The first digit rem_key(rr) >> tk_shift(0) of a remainder rr in (0, 1),
-// from the bits alone (no branch): for rr >= 2^-11 (exponent field e >=
-// 1012) the key is 2^63 + rr 2^63, whose top 11 bits are 1024 + floor(rr
-// 2^10), the 21-bit high part of the significand shifted right by 1033 - e
-// (11 to 21); below, the key is rr's binary64 pattern, whose top 11 bits are
+// without branches: for rr >= 2^-11 the key is 2^63 + rr 2^63, whose top 11
+// bits are 1024 + floor(rr 2^10) (rr 2^10 is exact, the conversion
+// truncates); below, the key is rr's binary64 pattern, whose top 11 bits are
 // the high word's (at most 505).
 __device__ __forceinline__ int sq_first_digit(double rr) {
-  const uint32_t hi = (uint32_t)((uint64_t)__double_as_longlong(rr) >> 32);
-  const uint32_t e = hi >> 20;
-  const uint32_t big = (((hi & 0xfffffu) | 0x100000u) >> ((1033u - e) & 31u)) | 1024u;
-  return (int)(e >= 1012u ? big : hi >> 21);
+  const int big = (int)(rr * 1024.0) | 1024;
+  const int small = (int)((uint32_t)((uint64_t)__double_as_longlong(rr) >> 32) >> 21);
+  return rr >= 0x1p-11 ? big : small;
 }
 // The remainders whose first digit is d form [lo, hi): the inverse of
 // sq_first_digit (digits 506 to 1023 are never taken).  No digit (d outside
@@ -679,17 +677,26 @@ __device__ int sq_resolve_row(const ShardQArgs& a, int r, const TkRow& t, const 
       sh.flo[j] = a.cflo[slot];
     }
     __syncthreads();
-    for (uint32_t j = threadIdx.x; j < n; j += BS) {
-      bool win = true;
-      if (!all) {  // rank: larger keys, then equal keys at lower ids (the list is in id order)
-        const uint64_t kj = sh.key[j];
-        uint32_t rank = 0;
-        for (uint32_t i = 0; i < n; ++i) {
-          const uint64_t ki = sh.key[i];
-          rank += (ki > kj || (ki == kj && i < j)) ? 1u : 0u;
-        }
-        win = rank < need0;
+    // rank of id j: the ids before it in (key desc, id asc) order (the list
+    // is in id order, so id order is list order).  P lanes of one wave share
+    // an id, each comparing every P-th key, so that few ids spread over all
+    // threads and each lane's reads are few and independent
+    static_assert(kSqCandCap <= BS, "one id per thread at least");
+    int P = 64;
+    while (P > 1 && (uint32_t)(BS / P) < n) P >>= 1;
+    const uint32_t j = threadIdx.x / P, p = threadIdx.x % P;
+    uint32_t rank = 0;
+    if (!all && j < n) {
+      const uint64_t kj = sh.key[j];
+#pragma unroll 4
+      for (uint32_t i = p; i < n; i += P) {
+        const uint64_t ki = sh.key[i];
+        rank += (ki > kj || (ki == kj && i < j)) ? 1u : 0u;
       }
+    }
+    for (int off = 1; off < P; off <<= 1) rank += (uint32_t)__shfl_xor((int)rank, off);  // (P divides 64)
+    if (j < n && p == 0) {
+      const bool win = all || rank < need0;
       const uint32_t id = sh.id[j];
       crow[id] = sh.flo[j] + (win ? 1u : 0u);
       sh.won[j] = win ? 1u : 0u;
