@@ -617,6 +617,11 @@ __global__ void __launch_bounds__(BS) ratio_step_kernel(RatioArgs a) {
   const int es = SRC == kSrcF32 ? 4 : 2;
   const int trow = r * DSPARK_N_TARGET + a.pos;
   const void* p = static_cast<const char*>(a.target) + (size_t)trow * (size_t)a.t_stride * es;
+  // SRC kSrcRes (bf16 rows of up to 131,072 ids): the row is read once into
+  // registers for its head and, when its value table applies, its plain pass;
+  // the residual pass streams it (its per-element counts do not fit beside the
+  // row's registers).  Otherwise every pass streams the row.
+  constexpr int STR = SRC == kSrcRes ? kSrcBf16 : SRC;  // how the streamed passes read the row
   Res R;
   DrawCtx c;
   const int status = draw_head<SRC>(R, p, a.V, c, sh);
@@ -635,12 +640,17 @@ __global__ void __launch_bounds__(BS) ratio_step_kernel(RatioArgs a) {
   int acc_len = a.pos;
   // one plain pass: the draw from p at the end of the request, or the total A
   // (sh.total) for the ratio test
-  int tok = draw_streamed<SRC, kDrawPlain>(p, a.V, c, final_p, uf, sh);
+  int tok;
+  if constexpr (SRC == kSrcRes) {
+    tok = c.table ? wres_draw(R, c, final_p, uf, sh) : draw_streamed<STR, kDrawPlain>(p, a.V, c, final_p, uf, sh);
+  } else {
+    tok = draw_streamed<SRC, kDrawPlain>(p, a.V, c, final_p, uf, sh);
+  }
   if (!final_p) {
     if (threadIdx.x == 0) {
       const int x = a.dtok[j];
       const uint32_t cx = ratio_q_count(a, j, x);
-      const U256 ax = u256_of_weight(draw_weight_at<SRC>(p, x, c, sh));
+      const U256 ax = u256_of_weight(draw_weight_at<STR>(p, x, c, sh));
       sh.bi[1] = ratio_accepts(a.acc_draws[(size_t)r * DSPARK_N_DRAFT + a.pos], cx, ax, sh.total) ? 1 : 0;
     }
     __syncthreads();
@@ -661,7 +671,7 @@ __global__ void __launch_bounds__(BS) ratio_step_kernel(RatioArgs a) {
       c.sp_len = a.sp_len[j];
       draw_sparse_q(a.sp_ids + (size_t)j * a.k_max, a.sp_cnt + (size_t)j * a.k_max, c.sp_len, sh);
     }
-    tok = draw_streamed<SRC, kDrawResidual>(p, a.V, c, true, uf, sh);
+    tok = draw_streamed<STR, kDrawResidual>(p, a.V, c, true, uf, sh);
     if (tok < 0) st = DSPARK_ST_ALLOC_INCONSISTENT;  // zero residual: q's counts do not sum to 2^24
   }
   if (threadIdx.x == 0) {
@@ -1264,12 +1274,15 @@ int dspark_verify_ratio(const dspark_rows* target, const int32_t* draft_tokens, 
   a.req_status = req_status;
   const dim3 grid((unsigned)n_requests);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // the rows are streamed: a request reads at most one row whose residual
-  // is drawn, and its q row beside it
+  // a request reads at most one row whose residual is drawn, and its q row
+  // beside it; bf16 rows that fit in registers are read into them once for
+  // the head and the plain pass
   const bool f32 = target->dtype == DSPARK_F32;
+  const bool res = !f32 && target->vocab <= NI * BS * 8;
   for (int pos = 0; pos <= DSPARK_N_DRAFT; ++pos) {
     a.pos = pos;
     if (f32) hipLaunchKernelGGL(ratio_step_kernel<kSrcF32>, grid, dim3(BS), 0, s, a);
+    else if (res) hipLaunchKernelGGL(ratio_step_kernel<kSrcRes>, grid, dim3(BS), 0, s, a);
     else hipLaunchKernelGGL(ratio_step_kernel<kSrcBf16>, grid, dim3(BS), 0, s, a);
     if ((rc = check_launch())) return rc;
   }
