@@ -431,6 +431,35 @@ __device__ __forceinline__ void acc_add_q(Acc& a, AccQ& q, uint32_t wb) {
   q.lo += !big && E >= 80u ? v : 0ull;
   if (E < 80u && wb) acc_add(a, wb);
 }
+// The cheapest tier, for streams of weights: binary64 words that stay exact
+// for a bounded number of additions.  Weights of at least 2^-24 are
+// multiples of 2^-47: their sum is exact in binary64 below 2^6, so for up to
+// 63 weights (each at most 1).  Weights in [2^-47, 2^-24) are multiples of
+// 2^-70: exact below 2^-17, so for up to 127 of them.  Each weight goes to
+// its word by a fused multiply-add with 1 or 0 (no branch); accd_flush moves
+// both words, as integers in units of 2^-47 and 2^-70, into the AccQ words,
+// and must follow every kAccDRun additions.  Smaller weights go to the
+// accumulator.
+constexpr int kAccDRun = 32;
+struct AccD {
+  double big, mid;
+};
+__device__ __forceinline__ void accd_zero(AccD& d) { d.big = d.mid = 0.0; }
+__device__ __forceinline__ void accd_add(Acc& a, AccD& d, uint32_t wb) {  // wb: the bits of a weight in [0, 1]
+  if (wb - 1u < (80u << 23) - 1u) {  // 0 < w < 2^-47: rare
+    acc_add(a, wb);
+    return;
+  }
+  const double w = (double)__uint_as_float(wb);
+  const bool big = wb >= (103u << 23);
+  d.big = __builtin_fma(w, big ? 1.0 : 0.0, d.big);
+  d.mid = __builtin_fma(w, big ? 0.0 : 1.0, d.mid);
+}
+__device__ __forceinline__ void accd_flush(AccQ& q, AccD& d) {
+  q.hi += (uint64_t)(d.big * 0x1p47);  // integers below 2^53
+  q.lo += (uint64_t)(d.mid * 0x1p70);
+  accd_zero(d);
+}
 __device__ __forceinline__ void acc_fold(Acc& a, const AccQ& q) {
   add128(a.mlo, a.mhi, q.hi << 23, q.hi >> 41);
   add128(a.mlo, a.mhi, q.lo, 0ull);

@@ -311,7 +311,10 @@ sq_sum_kernel(ShardQArgs a) {
     const bool cvec = (reinterpret_cast<uintptr_t>(crow) & 15u) == 0u;  // the count row 16-byte aligned
     AccQ q;
     accq_zero(q);
-    for (int i = lo + (int)threadIdx.x; i < a0; i += kShardBS) {  // head and tail
+    AccD dd;
+    accd_zero(dd);
+    int run = 0;  // weights in dd since its last flush
+    for (int i = lo + (int)threadIdx.x; i < a0; i += kShardBS) {  // head and tail (at most one each per thread)
       const uint32_t wb = __float_as_uint(cr_expf(sq_value<DT>(a, r, i) - t.m, s_exp));
       acc_add_q(acc, q, wb);
       crow[i] = wb;
@@ -321,12 +324,17 @@ sq_sum_kernel(ShardQArgs a) {
       acc_add_q(acc, q, wb);
       crow[i] = wb;
     }
-    // the next UV vectors are loaded before the current ones are taken
+    static_assert(EPV * UV <= kAccDRun, "a step's weights fit one run");
     for (int q0 = q00; q0 < q1; q0 += UV * kShardBS) {
       if (q0 != q00) {
 #pragma unroll
         for (int u = 0; u < UV; ++u) xv[u] = q0 + u * kShardBS < q1 ? ld_nt(vrow + q0 + u * kShardBS) : uint4{0u, 0u, 0u, 0u};
       }
+      if (run + EPV * UV > kAccDRun) {
+        accd_flush(q, dd);
+        run = 0;
+      }
+      run += EPV * UV;
 #pragma unroll
       for (int u = 0; u < UV; ++u) {
         const int qv = q0 + u * kShardBS;
@@ -338,7 +346,7 @@ sq_sum_kernel(ShardQArgs a) {
             const float x = DT == DSPARK_BF16 ? __uint_as_float((e & 1) ? (v[e >> 1] & 0xffff0000u) : (v[e >> 1] << 16))
                                               : __uint_as_float(v[e]);
             w[e] = __float_as_uint(cr_expf(x - t.m, s_exp));
-            acc_add_q(acc, q, w[e]);
+            accd_add(acc, dd, w[e]);
           }
           uint32_t* dst = crow + (size_t)qv * EPV;
           if (cvec) {
@@ -352,6 +360,7 @@ sq_sum_kernel(ShardQArgs a) {
         }
       }
     }
+    accd_flush(q, dd);
     acc_fold(acc, q);
   }
   acc = block_acc_total(acc, s_a);
