@@ -237,25 +237,61 @@ __device__ __forceinline__ Acc block_acc_total(Acc a, Acc* s_a) {
   return a;
 }
 
+// The shard's exact weight sum: the 16-byte aligned middle of the shard as
+// vectors of logits (non-temporal loads, UV per thread in flight), head and
+// tail element by element; the weights summed in binary64 runs of
+// kAccDRun moved into 64-bit integer words (device_common.hpp), the rare tiny
+// weights into the 128-bit accumulator.
 template <int DT>
-__global__ void __launch_bounds__(kShardBS) shard_sum_kernel(const void* data, int64_t stride, int V, int G,
-                                                             const ShardHead* heads, Acc* sums) {
+__global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(8, 8)))
+shard_sum_kernel(const void* data, int64_t stride, int V, int G, const ShardHead* heads, Acc* sums) {
   __shared__ Acc s_a[kShardNW];
   __shared__ double s_exp[64];
+  const int r = blockIdx.x / G, g = blockIdx.x % G;
+  int lo, hi;
+  shard_range(V, G, g, &lo, &hi);
+  constexpr int EPV = DT == DSPARK_BF16 ? 8 : 4;
+  constexpr int UV = 1;  // vectors per thread per step
+  const int a0 = (lo + EPV - 1) / EPV * EPV < hi ? (lo + EPV - 1) / EPV * EPV : hi;
+  const int a1 = hi / EPV * EPV > a0 ? hi / EPV * EPV : a0;
+  const int es = DT == DSPARK_BF16 ? 2 : 4;
+  const uint4* vrow = reinterpret_cast<const uint4*>(static_cast<const char*>(data) + (size_t)r * (size_t)stride * es);
+  const int q1 = a1 / EPV, q00 = a0 / EPV + (int)threadIdx.x;
+  uint4 xv = q00 < q1 ? ld_nt(vrow + q00) : uint4{0u, 0u, 0u, 0u};  // in flight during the merge
   exp_table_to_lds(s_exp);
   __syncthreads();
-  const int r = blockIdx.x / G, g = blockIdx.x % G;
   const ShardHead h = merge_heads(heads, r, G);
   const float m = __uint_as_float(h.max_bits);
   Acc a;
   acc_zero(a);
   if (h.flags == 0u && m != -__builtin_inff()) {  // a refused row has no sum
-    int lo, hi;
-    shard_range(V, G, g, &lo, &hi);
-    for (int i = lo + (int)threadIdx.x; i < hi; i += kShardBS) {
-      const float x = shard_value<DT>(data, stride, r, i);
-      acc_add(a, __float_as_uint(cr_expf(x - m, s_exp)));
+    AccQ q;
+    accq_zero(q);
+    for (int i = lo + (int)threadIdx.x; i < a0; i += kShardBS)
+      acc_add_q(a, q, __float_as_uint(cr_expf(shard_value<DT>(data, stride, r, i) - m, s_exp)));
+    for (int i = a1 + (int)threadIdx.x; i < hi; i += kShardBS)
+      acc_add_q(a, q, __float_as_uint(cr_expf(shard_value<DT>(data, stride, r, i) - m, s_exp)));
+    AccD dd;
+    accd_zero(dd);
+    int run = 0;  // weights in dd since its last flush
+    static_assert(EPV * UV <= kAccDRun, "a step's weights fit one run");
+    for (int q0 = q00; q0 < q1; q0 += kShardBS) {
+      if (q0 != q00) xv = ld_nt(vrow + q0);
+      if (run + EPV > kAccDRun) {
+        accd_flush(q, dd);
+        run = 0;
+      }
+      run += EPV;
+      const uint32_t v[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const float x = DT == DSPARK_BF16 ? __uint_as_float((e & 1) ? (v[e >> 1] & 0xffff0000u) : (v[e >> 1] << 16))
+                                          : __uint_as_float(v[e]);
+        accd_add(a, dd, __float_as_uint(cr_expf(x - m, s_exp)));
+      }
     }
+    accd_flush(q, dd);
+    acc_fold(a, q);
   }
   a = block_acc_total(a, s_a);
   if (threadIdx.x == 0) sums[blockIdx.x] = a;
