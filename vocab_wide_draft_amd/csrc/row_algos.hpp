@@ -51,7 +51,9 @@ struct Row {
 };
 
 // A row, or a vocabulary shard of one, that starts at any element offset:
-// element-wise loads, so no alignment is assumed.  Same interface as Row.
+// no alignment is assumed.  A start aligned for whole vectors (8 bytes for
+// bf16, 16 bytes for fp32) loads them whole; any other start loads element by
+// element.  Same interface as Row.
 template <int DT>
 struct ScalarRow {
   static constexpr int EPV = 4;
@@ -61,6 +63,20 @@ struct ScalarRow {
   __device__ __forceinline__ int load(int q, float (&x)[EPV]) const {
     const int base = q * EPV;
     const int nv = V - base < EPV ? V - base : EPV;
+    constexpr uintptr_t kAlign = DT == DSPARK_BF16 ? 7u : 15u;
+    if (nv == EPV && (reinterpret_cast<uintptr_t>(p) & kAlign) == 0u) {
+      if constexpr (DT == DSPARK_BF16) {
+        const uint2 u = reinterpret_cast<const uint2*>(p)[q];
+        x[0] = __uint_as_float(u.x << 16);
+        x[1] = __uint_as_float(u.x & 0xffff0000u);
+        x[2] = __uint_as_float(u.y << 16);
+        x[3] = __uint_as_float(u.y & 0xffff0000u);
+      } else {
+        const float4 u = reinterpret_cast<const float4*>(p)[q];
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+      }
+      return nv;
+    }
 #pragma unroll
     for (int l = 0; l < EPV; ++l) {
       if (l < nv) {
