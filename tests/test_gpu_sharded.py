@@ -25,6 +25,8 @@ def _rows(V, rng):
     rows.append(np.full(V, 1.25, np.float32))                                # constant
     r = base.copy(); r[:V // 2] = -np.inf; rows.append(r)                    # masked first half
     r = (base - 60.0).astype(np.float32); r[3 % V] = 10.0; rows.append(r)    # tiny weights
+    rows.append((base * 40.0).astype(np.float32))                            # wide: many zero weights
+    rows.append((base - 30.0).astype(np.float32))                            # negative maximum
     r = base.copy(); r[V // 3] = np.nan; rows.append(r)
     r = base.copy(); r[V - 1] = np.inf; rows.append(r)
     rows.append(np.full(V, -np.inf, np.float32))
@@ -59,6 +61,8 @@ def _q_rows(V, rng):
     r = np.full(V, -np.inf, np.float32); r[rng.integers(0, V, 9)] = 1.5; rows.append(r)  # few finite logits
     r = base.copy(); r[rng.random(V) < 0.4] = -np.inf; rows.append(r)
     r = (base - 70.0).astype(np.float32); r[V // 2] = 0.0; rows.append(r)    # tiny weights
+    rows.append((base * 40.0).astype(np.float32))                            # wide: many zero weights
+    rows.append((base - 30.0).astype(np.float32))                            # negative maximum
     r = base.copy(); r[V - 1] = np.nan; rows.append(r)                      # refused
     return np.stack(rows)
 
@@ -75,7 +79,7 @@ def test_sharded_q(dtype, V):
     n = raw.shape[0]
     d = to_dev(raw, dtype)
     draws = rng.integers(0, 1 << 24, n, dtype=np.uint32)
-    for ks in ((0,) * n, (7, 0, 64, 0, 33, 1, 5)[:n]):
+    for ks in ((0,) * n, (7, 0, 64, 0, 33, 1, 5, 0, 12)[:n]):
         topk = np.array(ks, np.int32)
         refs = [O.draft_row(raw[j], dtype, int(topk[j]), int(draws[j])) for j in range(n)]
         for G in (1, 2, 3, 8, 64):

@@ -20,6 +20,7 @@
 #include <stdint.h>
 
 #include "device_common.hpp"
+#include "fast_q.hpp"
 
 namespace dspark {
 
@@ -237,13 +238,38 @@ __device__ __forceinline__ Acc block_acc_total(Acc a, Acc* s_a) {
   return a;
 }
 
+// bf16 weights from a per-workgroup table: the weight of every bf16 value in
+// the window [m - 105, m], laid out as the row kernel's value table
+// (fast_q.hpp), so that an element's weight is a table read.  Rows whose table
+// would exceed kNBF entries (a maximum below about 0.04) take the exponential
+// per element.
+struct ShardWTab {
+  FMap f;
+  bool on;
+};
+// all threads; the caller's barrier publishes the table
+__device__ __forceinline__ ShardWTab shard_wtab_build(float m, float* tab, const double* etab) {
+  ShardWTab w;
+  w.f = fmap_make(__float_as_uint(m) >> 16);  // (m is a bf16 value)
+  w.on = w.f.NB <= kNBF;
+  if (w.on)
+    for (int b = (int)threadIdx.x; b < w.f.NB; b += (int)blockDim.x)
+      tab[b] = cr_expf(bf16_to_f32(fmap_raw(b, w.f)) - m, etab);
+  return w;
+}
+__device__ __forceinline__ uint32_t shard_wtab_weight(uint32_t raw, const ShardWTab& w, const float* tab) {
+  const int bin = fmap_bin(raw, w.f);
+  return bin >= 0 && bin < w.f.NB ? __float_as_uint(tab[bin]) : 0u;  // (below the window: 0)
+}
+
 // The shard's exact weight sum: the 16-byte aligned middle of the shard as
 // vectors of logits (non-temporal loads, UV per thread in flight), head and
-// tail element by element; the weights summed in binary64 runs of
-// kAccDRun moved into 64-bit integer words (device_common.hpp), the rare tiny
-// weights into the 128-bit accumulator.
+// tail element by element; bf16 weights from the value table when it applies;
+// the weights summed in binary64 runs of kAccDRun moved into 64-bit integer
+// words (device_common.hpp), the rare tiny weights into the 128-bit
+// accumulator.
 template <int DT>
-__global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(8, 8)))
+__global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(DT == DSPARK_BF16 ? 4 : 8, 8)))
 shard_sum_kernel(const void* data, int64_t stride, int V, int G, const ShardHead* heads, Acc* sums) {
   __shared__ Acc s_a[kShardNW];
   __shared__ double s_exp[64];
@@ -251,43 +277,65 @@ shard_sum_kernel(const void* data, int64_t stride, int V, int G, const ShardHead
   int lo, hi;
   shard_range(V, G, g, &lo, &hi);
   constexpr int EPV = DT == DSPARK_BF16 ? 8 : 4;
-  constexpr int UV = 1;  // vectors per thread per step
+  // vectors per thread per step: the bf16 value table leaves room for four
+  // workgroups per CU, and these keep more loads in flight
+  constexpr int UV = DT == DSPARK_BF16 ? 4 : 1;
   const int a0 = (lo + EPV - 1) / EPV * EPV < hi ? (lo + EPV - 1) / EPV * EPV : hi;
   const int a1 = hi / EPV * EPV > a0 ? hi / EPV * EPV : a0;
   const int es = DT == DSPARK_BF16 ? 2 : 4;
   const uint4* vrow = reinterpret_cast<const uint4*>(static_cast<const char*>(data) + (size_t)r * (size_t)stride * es);
   const int q1 = a1 / EPV, q00 = a0 / EPV + (int)threadIdx.x;
-  uint4 xv = q00 < q1 ? ld_nt(vrow + q00) : uint4{0u, 0u, 0u, 0u};  // in flight during the merge
+  uint4 xv[UV];  // the first loads: they need no m, so they fly during the merge
+#pragma unroll
+  for (int u = 0; u < UV; ++u) xv[u] = q00 + u * kShardBS < q1 ? ld_nt(vrow + q00 + u * kShardBS) : uint4{0u, 0u, 0u, 0u};
   exp_table_to_lds(s_exp);
   __syncthreads();
   const ShardHead h = merge_heads(heads, r, G);
   const float m = __uint_as_float(h.max_bits);
+  const bool ok = h.flags == 0u && m != -__builtin_inff();  // a refused row has no sum (the same for every thread)
+  __shared__ float s_wtab[DT == DSPARK_BF16 ? kNBFD : 1];
+  ShardWTab wt{};
+  if constexpr (DT == DSPARK_BF16) {
+    if (ok) wt = shard_wtab_build(m, s_wtab, s_exp);
+    __syncthreads();
+  }
+  auto weight = [&](float x) -> uint32_t {
+    if constexpr (DT == DSPARK_BF16)
+      if (wt.on) return shard_wtab_weight(__float_as_uint(x) >> 16, wt, s_wtab);
+    return __float_as_uint(cr_expf(x - m, s_exp));
+  };
   Acc a;
   acc_zero(a);
-  if (h.flags == 0u && m != -__builtin_inff()) {  // a refused row has no sum
+  if (ok) {
     AccQ q;
     accq_zero(q);
-    for (int i = lo + (int)threadIdx.x; i < a0; i += kShardBS)
-      acc_add_q(a, q, __float_as_uint(cr_expf(shard_value<DT>(data, stride, r, i) - m, s_exp)));
-    for (int i = a1 + (int)threadIdx.x; i < hi; i += kShardBS)
-      acc_add_q(a, q, __float_as_uint(cr_expf(shard_value<DT>(data, stride, r, i) - m, s_exp)));
+    for (int i = lo + (int)threadIdx.x; i < a0; i += kShardBS) acc_add_q(a, q, weight(shard_value<DT>(data, stride, r, i)));
+    for (int i = a1 + (int)threadIdx.x; i < hi; i += kShardBS) acc_add_q(a, q, weight(shard_value<DT>(data, stride, r, i)));
     AccD dd;
     accd_zero(dd);
     int run = 0;  // weights in dd since its last flush
     static_assert(EPV * UV <= kAccDRun, "a step's weights fit one run");
-    for (int q0 = q00; q0 < q1; q0 += kShardBS) {
-      if (q0 != q00) xv = ld_nt(vrow + q0);
-      if (run + EPV > kAccDRun) {
+    for (int q0 = q00; q0 < q1; q0 += UV * kShardBS) {
+      if (q0 != q00) {
+#pragma unroll
+        for (int u = 0; u < UV; ++u) xv[u] = q0 + u * kShardBS < q1 ? ld_nt(vrow + q0 + u * kShardBS) : uint4{0u, 0u, 0u, 0u};
+      }
+      if (run + EPV * UV > kAccDRun) {
         accd_flush(q, dd);
         run = 0;
       }
-      run += EPV;
-      const uint32_t v[4] = {xv.x, xv.y, xv.z, xv.w};
+      run += EPV * UV;
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const float x = DT == DSPARK_BF16 ? __uint_as_float((e & 1) ? (v[e >> 1] & 0xffff0000u) : (v[e >> 1] << 16))
-                                          : __uint_as_float(v[e]);
-        accd_add(a, dd, __float_as_uint(cr_expf(x - m, s_exp)));
+      for (int u = 0; u < UV; ++u) {
+        if (q0 + u * kShardBS < q1) {
+          const uint32_t v[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const float x = DT == DSPARK_BF16 ? __uint_as_float((e & 1) ? (v[e >> 1] & 0xffff0000u) : (v[e >> 1] << 16))
+                                              : __uint_as_float(v[e]);
+            accd_add(a, dd, weight(x));
+          }
+        }
       }
     }
     accd_flush(q, dd);

@@ -244,7 +244,7 @@ __device__ __forceinline__ TkRow sq_row_state(const ShardQArgs& a, float m, uint
 // the row's count storage for the passes that follow.  Workgroups past the
 // draft rows' merge the target rows' heads into their argmax and status.
 template <int DT>
-__global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(DT == DSPARK_BF16 ? 6 : 8, 8)))
+__global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(DT == DSPARK_BF16 ? 4 : 8, 8)))
 sq_sum_kernel(ShardQArgs a) {
   __shared__ Acc s_a[kShardNW];
   __shared__ TkRow s_t;
@@ -272,7 +272,9 @@ sq_sum_kernel(ShardQArgs a) {
   // the shard's 16-byte aligned middle [a0, a1) as vectors of EPV logits (rows
   // start 16-byte aligned), its head and tail element by element
   constexpr int EPV = DT == DSPARK_BF16 ? 8 : 4;
-  constexpr int UV = 1;  // vectors per thread in flight (4 or 8 logits)
+  // vectors per thread in flight (4 or 8 logits each): the bf16 value table
+  // leaves room for four workgroups per CU, and these keep more loads in flight
+  constexpr int UV = DT == DSPARK_BF16 ? 4 : 1;
   const int a0 = (lo + EPV - 1) / EPV * EPV < hi ? (lo + EPV - 1) / EPV * EPV : hi;
   const int a1 = hi / EPV * EPV > a0 ? hi / EPV * EPV : a0;
   const int es = DT == DSPARK_BF16 ? 2 : 4;
@@ -304,9 +306,21 @@ sq_sum_kernel(ShardQArgs a) {
   }
   __syncthreads();
   const TkRow t = s_t;
+  const bool dense = t.status == DSPARK_ST_OK && t.k == 0;  // (the same for every thread)
+  __shared__ float s_wtab[DT == DSPARK_BF16 ? kNBFD : 1];
+  ShardWTab wt{};
+  if constexpr (DT == DSPARK_BF16) {
+    if (dense) wt = shard_wtab_build(t.m, s_wtab, s_exp);
+    __syncthreads();
+  }
+  auto weight = [&](float x) -> uint32_t {
+    if constexpr (DT == DSPARK_BF16)
+      if (wt.on) return shard_wtab_weight(__float_as_uint(x) >> 16, wt, s_wtab);
+    return __float_as_uint(cr_expf(x - t.m, s_exp));
+  };
   Acc acc;
   acc_zero(acc);
-  if (t.status == DSPARK_ST_OK && t.k == 0) {
+  if (dense) {
     uint32_t* crow = a.dense + (size_t)r * a.V;
     const bool cvec = (reinterpret_cast<uintptr_t>(crow) & 15u) == 0u;  // the count row 16-byte aligned
     AccQ q;
@@ -315,12 +329,12 @@ sq_sum_kernel(ShardQArgs a) {
     accd_zero(dd);
     int run = 0;  // weights in dd since its last flush
     for (int i = lo + (int)threadIdx.x; i < a0; i += kShardBS) {  // head and tail (at most one each per thread)
-      const uint32_t wb = __float_as_uint(cr_expf(sq_value<DT>(a, r, i) - t.m, s_exp));
+      const uint32_t wb = weight(sq_value<DT>(a, r, i));
       acc_add_q(acc, q, wb);
       crow[i] = wb;
     }
     for (int i = a1 + (int)threadIdx.x; i < hi; i += kShardBS) {
-      const uint32_t wb = __float_as_uint(cr_expf(sq_value<DT>(a, r, i) - t.m, s_exp));
+      const uint32_t wb = weight(sq_value<DT>(a, r, i));
       acc_add_q(acc, q, wb);
       crow[i] = wb;
     }
@@ -345,7 +359,7 @@ sq_sum_kernel(ShardQArgs a) {
           for (int e = 0; e < EPV; ++e) {
             const float x = DT == DSPARK_BF16 ? __uint_as_float((e & 1) ? (v[e >> 1] & 0xffff0000u) : (v[e >> 1] << 16))
                                               : __uint_as_float(v[e]);
-            w[e] = __float_as_uint(cr_expf(x - t.m, s_exp));
+            w[e] = weight(x);
             accd_add(acc, dd, w[e]);
           }
           uint32_t* dst = crow + (size_t)qv * EPV;
