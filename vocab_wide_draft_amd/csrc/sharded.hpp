@@ -264,10 +264,11 @@ __device__ __forceinline__ uint32_t shard_wtab_weight(uint32_t raw, const ShardW
 
 // The shard's exact weight sum: the 16-byte aligned middle of the shard as
 // vectors of logits (non-temporal loads, UV per thread in flight), head and
-// tail element by element; bf16 weights from the value table when it applies;
-// the weights summed in binary64 runs of kAccDRun moved into 64-bit integer
-// words (device_common.hpp), the rare tiny weights into the 128-bit
-// accumulator.
+// tail element by element.  bf16 shards whose row has a value table
+// (fast_q.hpp) count their values per table entry in LDS and add count x
+// weight once per occupied entry.  Otherwise the weights are summed in
+// binary64 runs of kAccDRun moved into 64-bit integer words
+// (device_common.hpp), the rare tiny weights into the 128-bit accumulator.
 template <int DT>
 __global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(DT == DSPARK_BF16 ? 4 : 8, 8)))
 shard_sum_kernel(const void* data, int64_t stride, int V, int G, const ShardHead* heads, Acc* sums) {
@@ -289,23 +290,57 @@ shard_sum_kernel(const void* data, int64_t stride, int V, int G, const ShardHead
 #pragma unroll
   for (int u = 0; u < UV; ++u) xv[u] = q00 + u * kShardBS < q1 ? ld_nt(vrow + q00 + u * kShardBS) : uint4{0u, 0u, 0u, 0u};
   exp_table_to_lds(s_exp);
+  __shared__ uint32_t s_nb[DT == DSPARK_BF16 ? kNBFD : 1];  // counts per table entry (and overflow slots)
+  if constexpr (DT == DSPARK_BF16)
+    for (int b = (int)threadIdx.x; b < kNBFD; b += kShardBS) s_nb[b] = 0u;
   __syncthreads();
   const ShardHead h = merge_heads(heads, r, G);
   const float m = __uint_as_float(h.max_bits);
   const bool ok = h.flags == 0u && m != -__builtin_inff();  // a refused row has no sum (the same for every thread)
-  __shared__ float s_wtab[DT == DSPARK_BF16 ? kNBFD : 1];
-  ShardWTab wt{};
-  if constexpr (DT == DSPARK_BF16) {
-    if (ok) wt = shard_wtab_build(m, s_wtab, s_exp);
-    __syncthreads();
-  }
-  auto weight = [&](float x) -> uint32_t {
-    if constexpr (DT == DSPARK_BF16)
-      if (wt.on) return shard_wtab_weight(__float_as_uint(x) >> 16, wt, s_wtab);
-    return __float_as_uint(cr_expf(x - m, s_exp));
-  };
   Acc a;
   acc_zero(a);
+  if constexpr (DT == DSPARK_BF16) {
+    const FMap f = fmap_make(ok ? h.max_bits >> 16 : 0u);  // (m is a bf16 value)
+    if (ok && f.NB <= kNBF) {
+      const uint32_t D2 = fmap_dummy2();
+      char* base = reinterpret_cast<char*>(s_nb);
+      for (int i = lo + (int)threadIdx.x; i < a0; i += kShardBS) {
+        const int b = fmap_bin(__float_as_uint(shard_value<DT>(data, stride, r, i)) >> 16, f);
+        if (b < f.NB) atomicAdd(&s_nb[b], 1u);  // (below the window: weight 0)
+      }
+      for (int i = a1 + (int)threadIdx.x; i < hi; i += kShardBS) {
+        const int b = fmap_bin(__float_as_uint(shard_value<DT>(data, stride, r, i)) >> 16, f);
+        if (b < f.NB) atomicAdd(&s_nb[b], 1u);
+      }
+      for (int q0 = q00; q0 < q1; q0 += UV * kShardBS) {
+        if (q0 != q00) {
+#pragma unroll
+          for (int u = 0; u < UV; ++u) xv[u] = q0 + u * kShardBS < q1 ? ld_nt(vrow + q0 + u * kShardBS) : uint4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+          if (q0 + u * kShardBS < q1) {
+            const uint32_t w[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t o = fmap_off2(w[c], f, D2);
+              atomicAdd(reinterpret_cast<uint32_t*>(base + (o & 0xffffu)), 1u);
+              atomicAdd(reinterpret_cast<uint32_t*>(base + (o >> 16)), 1u);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      for (int b = (int)threadIdx.x; b < f.NB; b += kShardBS) {
+        const uint32_t n = s_nb[b];
+        if (n) acc_add(a, __float_as_uint(cr_expf(bf16_to_f32(fmap_raw(b, f)) - m, s_exp)), n);
+      }
+      a = block_acc_total(a, s_a);
+      if (threadIdx.x == 0) sums[blockIdx.x] = a;
+      return;
+    }
+  }
+  auto weight = [&](float x) -> uint32_t { return __float_as_uint(cr_expf(x - m, s_exp)); };
   if (ok) {
     AccQ q;
     accq_zero(q);
