@@ -63,6 +63,13 @@ def _q_rows(V, rng):
     r = (base - 70.0).astype(np.float32); r[V // 2] = 0.0; rows.append(r)    # tiny weights
     rows.append((base * 40.0).astype(np.float32))                            # wide: many zero weights
     rows.append((base - 30.0).astype(np.float32))                            # negative maximum
+    tiny = np.array([1e-7, -1e-7, 0.0, -0.0, 3e-8], np.float32)             # values of one collapsed table entry
+    r = np.full(V, -np.inf, np.float32); t = rng.random(V) < 0.3; r[t] = tiny[rng.integers(0, 5, int(t.sum()))]
+    r[V // 3] = 100.0; rows.append(r)                                        # top-k cut inside the collapsed entry
+    r = (rng.standard_normal(V) * 3 - 20).astype(np.float32); r[rng.random(V) < 0.4] = -np.inf
+    t = rng.random(V) < 0.02; r[t] = tiny[rng.integers(0, 5, int(t.sum()))]
+    r[V // 5] = 10.0; rows.append(r)                                         # collapsed entry above the cut
+    rows.append((0.75 + rng.standard_normal(V) * 1e-6).astype(np.float32))  # fp32: one first digit, many keys
     r = base.copy(); r[V - 1] = np.nan; rows.append(r)                      # refused
     return np.stack(rows)
 
@@ -79,7 +86,7 @@ def test_sharded_q(dtype, V):
     n = raw.shape[0]
     d = to_dev(raw, dtype)
     draws = rng.integers(0, 1 << 24, n, dtype=np.uint32)
-    for ks in ((0,) * n, (7, 0, 64, 0, 33, 1, 5, 0, 12)[:n]):
+    for ks in ((0,) * n, (7, 0, 64, 0, 33, 1, 5, 0, 12, 6, 33, 0)[:n]):
         topk = np.array(ks, np.int32)
         refs = [O.draft_row(raw[j], dtype, int(topk[j]), int(draws[j])) for j in range(n)]
         for G in (1, 2, 3, 8, 64):

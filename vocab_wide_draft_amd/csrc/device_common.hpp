@@ -150,6 +150,8 @@ __device__ __forceinline__ float lowest_of(float) { return -__builtin_inff(); }
 __device__ __forceinline__ int highest_of(int) { return 2147483647; }
 __device__ __forceinline__ uint32_t highest_of(uint32_t) { return 0xffffffffu; }
 __device__ __forceinline__ float highest_of(float) { return __builtin_inff(); }
+__device__ __forceinline__ uint64_t lowest_of(uint64_t) { return 0ull; }
+__device__ __forceinline__ uint64_t highest_of(uint64_t) { return ~0ull; }
 // inclusive prefix sum over the 64 lanes: row shifts by 1, 2, 4, 8 (scan
 // inside each row of 16), then the row broadcasts of lanes 15 and 31
 template <class T>

@@ -504,6 +504,20 @@ __device__ __forceinline__ QOut support_alloc(float m, int n, int32_t* ids_out, 
   return res;
 }
 
+// Adds 1 at hist[b] for every active lane with b >= 0.  When all active
+// lanes of the wave hold the same b (a run of equal keys, such as the -inf
+// of a masked row), the first of them adds their count at once: equal
+// addresses would otherwise serialise the LDS atomics lane by lane.
+__device__ __forceinline__ void hist_add_wave(uint32_t* hist, int b) {
+  const int b0 = __builtin_amdgcn_readfirstlane(b);
+  const uint64_t act = __ballot(1), same = __ballot(b == b0);
+  if (same == act) {
+    if (b0 >= 0 && lane_id() == __builtin_ctzll(act)) atomicAdd(&hist[b0], (uint32_t)__builtin_popcountll(act));
+  } else if (b >= 0) {
+    atomicAdd(&hist[b], 1u);
+  }
+}
+
 // The top-k support of a streamed row by (logit desc, id asc), 1 <= k <=
 // the row's length, into (sh.cid, sh.sx) in ascending id order (ids
 // relative to the row's start); m = the row maximum, tkey = key32 of this
@@ -533,7 +547,7 @@ __device__ int stream_topk_support(const ROW& row, float m, uint32_t tkey, int k
 #pragma unroll
       for (int l = 0; l < EPV; ++l) {
         const uint32_t K = key32(x[l]);
-        if (l < nv && K >= lo && K <= hi) atomicAdd(&sh.hist[(hi - K) >> shift], 1u);
+        hist_add_wave(sh.hist, l < nv && K >= lo && K <= hi ? (int)((hi - K) >> shift) : -1);
       }
     }
     __syncthreads();

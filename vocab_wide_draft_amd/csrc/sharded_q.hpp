@@ -661,9 +661,12 @@ __device__ __forceinline__ int sq_shard_of(int v, int V, int G) {
 // A dense row's workgroup: the `need` tickets of the crossing bin go to its
 // largest remainder keys, ties to the lowest id.  Up to kSqCandCap ids the
 // bin is resolved on chip from the shards' stored ids and keys; beyond that
-// the remaining five digits are found over the flagged ids of the row (keys
-// recomputed from the logits: the count row holds the counts by now) and the
-// tie cut follows id order.  The shards' masses get the tickets they won.
+// over the flagged ids of the row (keys recomputed from the logits: the count
+// row holds the counts by now): when the bin holds one key (ids of one
+// repeated value) the tickets go to its lowest ids, otherwise the remaining
+// five digits are found first.  The final pass gives each wave a contiguous
+// run of ids, so that id order costs ballots and one block scan.  The
+// shards' masses get the tickets they won.
 // Returns the row's status (the same in every thread).
 // Expects sh.off (the shards' candidate offsets) and sh.mass (their masses
 // before the tickets) filled and sh.wins zeroed.
@@ -678,10 +681,10 @@ __device__ int sq_resolve_row(const ShardQArgs& a, int r, const TkRow& t, const 
   const SumR S = sum_r(s64);
   const float m = t.m;
   uint32_t* crow = a.dense + (size_t)r * a.V;
-  auto key_of = [&](int v) {
+  auto key_x = [&](float x) {  // remainder key of a logit
     uint32_t c;
     double rr;
-    floor_rem(cr_expf(sq_value<DT>(a, r, v) - m, sh.etab), S, c, rr);
+    floor_rem(cr_expf(x - m, sh.etab), S, c, rr);
     return rem_key(rr);
   };
   if (threadIdx.x == 0) sh.general = n > (uint32_t)kSqCandCap ? 1 : 0;  // (read after later barriers)
@@ -726,40 +729,117 @@ __device__ int sq_resolve_row(const ShardQArgs& a, int r, const TkRow& t, const 
       if (win) atomicAdd(&sh.wins[sq_shard_of((int)id, a.V, G)], 1u);
     }
   } else {
-    uint64_t prefix = (uint64_t)cut.bin << tk_shift(0), pmask = (uint64_t)(kTkBins - 1) << tk_shift(0);
-    uint64_t need = need0;
-    for (int L = 1; L < kTkLevels; ++L) {
-      const int nb = tk_bins(L), sft = tk_shift(L);
-      for (int b = threadIdx.x; b < nb; b += BS) sh.hist[b] = 0u;
-      __syncthreads();
-      for (int v = threadIdx.x; v < a.V; v += BS) {
-        if (crow[v] & kSqMark) {
-          const uint64_t k = key_of(v);
-          if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> sft) & (uint64_t)(nb - 1)], 1u);
+    // Every pass below loads UB words (and logits) per thread before it
+    // uses any: the row's count words come from memory, and a loop that
+    // waited for each one would take a memory latency per id step.
+    constexpr int UB = 6;
+    auto load_ids = [&](int v0, int step, int lim, bool with_x, uint32_t (&cw)[UB], float (&x)[UB]) {
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int v = v0 + u * step;
+        cw[u] = v < lim ? crow[v] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int v = v0 + u * step;
+        x[u] = with_x && v < lim ? sq_value<DT>(a, r, v) : 0.0f;
+      }
+    };
+    uint64_t kmin = ~0ull, kmax = 0ull;  // over the flagged ids
+    for (int v0 = (int)threadIdx.x; v0 < a.V; v0 += UB * BS) {
+      uint32_t cw[UB];
+      float x[UB];
+      load_ids(v0, BS, a.V, true, cw, x);
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        if (cw[u] & kSqMark) {
+          const uint64_t k = key_x(x[u]);
+          kmin = k < kmin ? k : kmin;
+          kmax = k > kmax ? k : kmax;
         }
       }
-      __syncthreads();
-      uint64_t before;
-      const int dg = block_find_crossing(sh.hist, nb, need, false, sh, &before);
-      need -= before;
-      prefix |= (uint64_t)dg << sft;
-      pmask |= (uint64_t)(nb - 1) << sft;
+    }
+    kmin = block_min<uint64_t>(kmin, sh.bs);
+    kmax = block_max<uint64_t>(kmax, sh.bs);
+    const bool one_key = kmin == kmax;  // (the same for every thread)
+    uint64_t prefix = (uint64_t)cut.bin << tk_shift(0), pmask = (uint64_t)(kTkBins - 1) << tk_shift(0);
+    uint64_t need = need0;
+    if (one_key) {
+      prefix = kmin;
+    } else {
+      for (int L = 1; L < kTkLevels; ++L) {
+        const int nb = tk_bins(L), sft = tk_shift(L);
+        for (int b = threadIdx.x; b < nb; b += BS) sh.hist[b] = 0u;
+        __syncthreads();
+        for (int v0 = (int)threadIdx.x; v0 < a.V; v0 += UB * BS) {
+          uint32_t cw[UB];
+          float x[UB];
+          load_ids(v0, BS, a.V, true, cw, x);
+#pragma unroll
+          for (int u = 0; u < UB; ++u) {
+            if (cw[u] & kSqMark) {
+              const uint64_t k = key_x(x[u]);
+              if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> sft) & (uint64_t)(nb - 1)], 1u);
+            }
+          }
+        }
+        __syncthreads();
+        uint64_t before;
+        const int dg = block_find_crossing(sh.hist, nb, need, false, sh, &before);
+        need -= before;
+        prefix |= (uint64_t)dg << sft;
+        pmask |= (uint64_t)(nb - 1) << sft;
+      }
     }
     const uint64_t T = prefix;  // the final key; its `need` lowest ids win
-    uint32_t run = 0;
-    for (int v0 = 0; v0 < a.V; v0 += BS) {
-      const int v = v0 + (int)threadIdx.x;
-      const uint32_t cw = v < a.V ? crow[v] : 0u;
-      const bool flagged = (cw & kSqMark) != 0u;
-      const uint64_t k = flagged ? key_of(v) : 0ull;
-      const uint32_t member = flagged && k == T ? 1u : 0u;
-      uint32_t tot;
-      const uint32_t rank = run + block_excl_scan<uint32_t>(member, sh.bs, &tot);
-      run += tot;
-      if (flagged) {
-        const bool win = k > T || (member && rank < need);
-        crow[v] = (cw & ~kSqMark) + (win ? 1u : 0u);
-        if (win) atomicAdd(&sh.wins[sq_shard_of(v, a.V, G)], 1u);
+    // wave w takes the ids [w span, (w + 1) span), 64 consecutive ids a
+    // step: ranks inside a wave from ballots, the waves' offsets from one
+    // scan of their member counts
+    const int span = ((a.V + NW - 1) / NW + 63) & ~63;
+    const int w0 = wave_id() * span, w1 = w0 + span < a.V ? w0 + span : a.V;
+    uint32_t nm = 0;
+    for (int vb0 = w0; vb0 < w1; vb0 += 64 * UB) {  // (the same in every lane of the wave)
+      uint32_t cw[UB];
+      float x[UB];
+      load_ids(vb0 + lane_id(), 64, w1, !one_key, cw, x);
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const bool member = (cw[u] & kSqMark) && (one_key || key_x(x[u]) == T);
+        nm += (uint32_t)__builtin_popcountll(__ballot(member));
+      }
+    }
+    uint32_t tot;
+    uint32_t base = block_excl_scan<uint32_t>(lane_id() == 0 ? nm : 0u, sh.bs, &tot);
+    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);  // lane 0's: the waves before this one
+    int g = 0, glo, ghi;
+    shard_range(a.V, G, 0, &glo, &ghi);
+    for (int vb0 = w0; vb0 < w1; vb0 += 64 * UB) {
+      uint32_t cw[UB];
+      float x[UB];
+      load_ids(vb0 + lane_id(), 64, w1, !one_key, cw, x);
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int vb = vb0 + u * 64;
+        if (vb >= w1) break;  // (the same in every lane)
+        while (vb >= ghi) shard_range(a.V, G, ++g, &glo, &ghi);  // (vb < V: g stays below G)
+        const int v = vb + lane_id();
+        const bool flagged = (cw[u] & kSqMark) != 0u;
+        const uint64_t k = flagged ? (one_key ? T : key_x(x[u])) : 0ull;
+        const bool member = flagged && k == T;
+        const uint64_t bm = __ballot(member);
+        const uint32_t rank = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+        base += (uint32_t)__builtin_popcountll(bm);
+        const bool win = flagged && (k > T || (member && rank < need));
+        if (flagged) crow[v] = (cw[u] & ~kSqMark) + (win ? 1u : 0u);
+        const uint64_t wm = __ballot(win);
+        if (wm) {
+          const int vl = vb + 63 < w1 - 1 ? vb + 63 : w1 - 1;
+          if (vl < ghi) {  // the step's ids all in shard g
+            if (lane_id() == 0) atomicAdd(&sh.wins[g], (uint32_t)__builtin_popcountll(wm));
+          } else if (win) {
+            atomicAdd(&sh.wins[sq_shard_of(v, a.V, G)], 1u);
+          }
+        }
       }
     }
   }
@@ -769,11 +849,152 @@ __device__ int sq_resolve_row(const ShardQArgs& a, int r, const TkRow& t, const 
   return DSPARK_ST_OK;
 }
 
+// LDS of a bf16 shard's top-k from the row's value table
+constexpr int kSqTopkIters = 128;  // vector iterations of a shard the table path takes (4 * BS * 128 ids)
+struct SqTopkFastShared : SmemBase {
+  uint32_t nb[kNBFD];                 // counts per table entry (and overflow slots)
+  uint32_t cab[kSqTopkIters * NW];    // per (iteration, wave): elements above the threshold entry
+  uint32_t ctie[kSqTopkIters * NW];   // per (iteration, wave): elements of the threshold entry
+};
+union SqTopkShared {
+  RowShared rs;
+  SqTopkFastShared ft;
+};
+
+// The top-kl of a bf16 shard by (logit desc, id asc), in ascending id order,
+// from the row's value table (fast_q.hpp: entries ordered by value, largest
+// first; m = the row maximum): the shard's values counted per entry, the
+// threshold entry where the running count reaches kl, then every element
+// above it and the need lowest ids of it, placed by one count pass and one
+// write pass.  Returns the count (kl), or -1 where the table does not decide
+// (no table for this m, fewer than kl values in the weight window, or a
+// partly taken collapsed entry, which holds several values); the same in
+// every thread.
+template <int DT>
+__device__ int sq_topk_table(const ScalarRow<DT>& row, int lo, float m, int kl, SqCand* out, SqTopkFastShared& sh) {
+  constexpr int EPV = ScalarRow<DT>::EPV;
+  const int nvec = row.nvec();
+  const int n_iter = (nvec + BS - 1) / BS;
+  if (kl < 1 || n_iter > kSqTopkIters) return -1;
+  const FMap f = fmap_make(__float_as_uint(m) >> 16);  // (m is a bf16 value)
+  if (f.NB > kNBF) return -1;
+  auto bin_of = [&](float x) { return fmap_bin(__float_as_uint(x) >> 16, f); };
+  for (int b = threadIdx.x; b < kNBFD; b += BS) sh.nb[b] = 0u;
+  __syncthreads();
+  for_vecs<kPF, float, EPV>(nvec, [&](int q, float (&x)[EPV]) { return row.load(q, x); },
+                            [&](int q, const float (&x)[EPV], int nv) {
+#pragma unroll
+    for (int l = 0; l < EPV; ++l) {
+      const int b = bin_of(x[l]);
+      if (l < nv && b < f.NB) atomicAdd(&sh.nb[b], 1u);  // (below the window: not counted)
+    }
+  });
+  __syncthreads();
+  uint32_t s = 0;
+  for (int b = threadIdx.x; b < f.NB; b += BS) s += sh.nb[b];
+  if (block_sum<uint32_t>(s, sh.bs) < (uint32_t)kl) return -1;
+  uint64_t before;
+  const int bt = block_find_crossing(sh.nb, f.NB, (uint64_t)kl, true, sh, &before);
+  const uint32_t need = (uint32_t)kl - (uint32_t)before;
+  if (bt == f.B0 && need < sh.nb[bt]) return -1;
+  // elements above the threshold entry and in it, per (iteration, wave)
+  for (int i0 = 0; i0 < n_iter; i0 += kPF) {
+    float x[kPF][EPV];
+    int nv[kPF];
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      const int q = (i0 + k) * BS + (int)threadIdx.x;
+      nv[k] = i0 + k < n_iter && q < nvec ? row.load(q, x[k]) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      if (i0 + k < n_iter) {  // (uniform)
+        uint32_t ca = 0, ct = 0;
+#pragma unroll
+        for (int l = 0; l < EPV; ++l) {
+          const int b = bin_of(x[k][l]);
+          ca += l < nv[k] && b < bt ? 1u : 0u;
+          ct += l < nv[k] && b == bt ? 1u : 0u;
+        }
+        ca = wave_sum(ca);
+        ct = wave_sum(ct);
+        if (lane_id() == 0) {
+          sh.cab[(i0 + k) * NW + wave_id()] = ca;
+          sh.ctie[(i0 + k) * NW + wave_id()] = ct;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  {  // exclusive prefix of both tables in (iteration, wave) order: id order
+    constexpr int PER = kSqTopkIters * NW / BS;
+    const int nt = n_iter * NW;
+    uint64_t v[PER], sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = (int)threadIdx.x * PER + j;
+      v[j] = e < nt ? ((uint64_t)sh.ctie[e] << 32) | sh.cab[e] : 0ull;
+      sum += v[j];
+    }
+    uint64_t tot;
+    uint64_t pre = block_excl_scan<uint64_t>(sum, sh.bs, &tot);
+    __syncthreads();  // (every table entry read before any is overwritten)
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = (int)threadIdx.x * PER + j;
+      if (e < nt) {
+        sh.cab[e] = (uint32_t)pre;
+        sh.ctie[e] = (uint32_t)(pre >> 32);
+      }
+      pre += v[j];
+    }
+  }
+  __syncthreads();
+  for (int i0 = 0; i0 < n_iter; i0 += kPF) {
+    float x[kPF][EPV];
+    int nv[kPF];
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      const int q = (i0 + k) * BS + (int)threadIdx.x;
+      nv[k] = i0 + k < n_iter && q < nvec ? row.load(q, x[k]) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      if (i0 + k < n_iter) {  // (uniform)
+        uint32_t ma = 0, mt = 0;
+#pragma unroll
+        for (int l = 0; l < EPV; ++l) {
+          const int b = bin_of(x[k][l]);
+          ma |= l < nv[k] && b < bt ? 1u << l : 0u;
+          mt |= l < nv[k] && b == bt ? 1u << l : 0u;
+        }
+        const uint32_t ca = (uint32_t)__builtin_popcount(ma), ct = (uint32_t)__builtin_popcount(mt);
+        uint32_t ab = sh.cab[(i0 + k) * NW + wave_id()] + wave_incl_scan(ca) - ca;  // above before this lane
+        uint32_t tb = sh.ctie[(i0 + k) * NW + wave_id()] + wave_incl_scan(ct) - ct;  // threshold ones before it
+        const int q = (i0 + k) * BS + (int)threadIdx.x;
+#pragma unroll
+        for (int l = 0; l < EPV; ++l) {
+          const SqCand c{lo + q * EPV + l, __float_as_uint(x[k][l])};
+          if ((ma >> l) & 1u) {
+            out[ab + (tb < need ? tb : need)] = c;
+            ++ab;
+          } else if ((mt >> l) & 1u) {
+            if (tb < need) out[ab + tb] = c;
+            ++tb;
+          }
+        }
+      }
+    }
+  }
+  return kl;
+}
+
 // (row, shard) workgroups of a sparse row: the shard's local top-k
-// candidates (global ids and logits)
+// candidates (global ids and logits), from the row's value table where it
+// decides (bf16), else by narrowing key histograms over the shard
 template <int DT>
 __global__ void __launch_bounds__(BS) sq_local_topk_kernel(ShardQArgs a) {
-  __shared__ RowShared sh;
+  __shared__ SqTopkShared sh;
   const int r = blockIdx.x / a.G, g = blockIdx.x % a.G;
   const TkRow t = a.tkr[r];
   if (t.status != DSPARK_ST_OK || t.k == 0) return;  // (the same for every thread)
@@ -782,12 +1003,17 @@ __global__ void __launch_bounds__(BS) sq_local_topk_kernel(ShardQArgs a) {
   const int es = DT == DSPARK_BF16 ? 2 : 4;
   const ScalarRow<DT> row{static_cast<const char*>(a.data) + ((size_t)r * (size_t)a.stride + (size_t)lo) * es,
                           hi - lo};
-  const Stats st = row_stats(row, sh.bs);
   const int kl = t.k < hi - lo ? t.k : hi - lo;
-  const int n = stream_topk_support(row, st.m, st.tkey, kl, sh);
   const size_t rs = (size_t)blockIdx.x;
-  for (int j = threadIdx.x; j < n; j += BS)
-    a.cand[rs * a.k_max + j] = SqCand{lo + (int)sh.cid[j], __float_as_uint(sh.sx[j])};
+  int n = -1;
+  if constexpr (DT == DSPARK_BF16) n = sq_topk_table(row, lo, t.m, kl, a.cand + rs * a.k_max, sh.ft);
+  if (n < 0) {
+    __syncthreads();  // (the table path's LDS is the same memory)
+    const Stats st = row_stats(row, sh.rs.bs);
+    n = stream_topk_support(row, st.m, st.tkey, kl, sh.rs);
+    for (int j = threadIdx.x; j < n; j += BS)
+      a.cand[rs * a.k_max + j] = SqCand{lo + (int)sh.rs.cid[j], __float_as_uint(sh.rs.sx[j])};
+  }
   if (threadIdx.x == 0) a.tks[rs].ncand = (uint32_t)n;
 }
 
@@ -936,16 +1162,52 @@ __device__ int sq_sample_row(const ShardQArgs& a, int r, const TkRow& t, uint32_
           sh.token = tk;
         }
       }
-    } else if (dense_row) {  // (after a resolution over the row's flagged ids) the shard in id order
+    } else if (dense_row) {
+      // (after a resolution over the row's flagged ids) the shard in id
+      // order: every wave sums a contiguous run of ids, one scan finds the
+      // run that holds the ticket, and its wave walks it 64 ids a step
       const uint32_t* crow = a.dense + (size_t)r * a.V;
-      uint32_t run = 0;
-      for (int v0 = lo; v0 < hi; v0 += BS) {  // ids in order, one per thread
-        const int v = v0 + (int)threadIdx.x;
-        const uint32_t c = v < hi ? crow[v] : 0u;
-        uint32_t tot;
-        const uint32_t pre = run + block_excl_scan<uint32_t>(c, sh.bs, &tot);
-        if (c && pre <= rest && rest < pre + c) sh.token = v;
-        run += tot;
+      const int span = ((hi - lo + NW - 1) / NW + 63) & ~63;
+      const int w0 = lo + wave_id() * span, w1 = w0 + span < hi ? w0 + span : hi;
+      constexpr int UB = 8;  // windows whose loads go out together
+      uint32_t sm = 0;
+      for (int vb0 = w0; vb0 < w1; vb0 += 64 * UB) {
+        uint32_t c[UB];
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+          const int v = vb0 + u * 64 + lane_id();
+          c[u] = v < w1 ? crow[v] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < UB; ++u) sm += c[u];
+      }
+      sm = wave_sum(sm);
+      uint32_t tot;
+      uint32_t pre = block_excl_scan<uint32_t>(lane_id() == 0 ? sm : 0u, sh.bs, &tot);
+      pre = (uint32_t)__builtin_amdgcn_readfirstlane((int)pre);  // lane 0's: the waves before this one
+      if (pre <= rest && rest < pre + sm) {  // (one wave, all its lanes)
+        uint32_t run = pre;
+        bool found = false;
+        for (int vb0 = w0; vb0 < w1 && !found; vb0 += 64 * UB) {
+          uint32_t c[UB];
+#pragma unroll
+          for (int u = 0; u < UB; ++u) {
+            const int v = vb0 + u * 64 + lane_id();
+            c[u] = v < w1 ? crow[v] : 0u;
+          }
+#pragma unroll
+          for (int u = 0; u < UB; ++u) {
+            if (!found) {  // (the same in every lane)
+              const uint32_t inc = wave_incl_scan(c[u]);
+              const uint32_t step = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+              if (rest < run + step) {
+                if (c[u] && run + inc - c[u] <= rest && rest < run + inc) sh.token = vb0 + u * 64 + lane_id();
+                found = true;
+              }
+              run += step;
+            }
+          }
+        }
       }
     } else {
       const int j = threadIdx.x;  // entries in id order, one per thread (len <= 1024)
@@ -965,7 +1227,7 @@ __device__ int sq_sample_row(const ShardQArgs& a, int r, const TkRow& t, uint32_
 // one workgroup per row: a dense row's tickets, the sample, the final status
 // and zeros for refused rows
 template <int DT>
-__global__ void __launch_bounds__(BS) sq_finish_kernel(ShardQArgs a) {
+__global__ void __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(8, 8))) sq_finish_kernel(ShardQArgs a) {
   __shared__ SqFinShared sh;
   const int r = blockIdx.x;
   const TkRow t = a.tkr[r];
