@@ -1017,19 +1017,22 @@ __global__ void __launch_bounds__(BS) sq_local_topk_kernel(ShardQArgs a) {
   if (threadIdx.x == 0) a.tks[rs].ncand = (uint32_t)n;
 }
 
-struct SqMergeShared {
-  RowShared rs;
-  uint64_t comp[kSqMergeCap];  // key32 << 32 | ~id: larger means logit larger, then id lower
-  float x[kSqMergeCap];
-};
-
 // one workgroup per sparse row: the exact global top-k from the shards'
 // candidates, then the allocation on that support.  The k-th largest
 // (logit, -id) pair is found by bisection over its 64-bit code (every code
 // is distinct); the candidates are stored shard after shard, each shard's in
 // ascending id order, so the selected ones come out in ascending id order.
+// The candidates' codes and logits live in LDS that the allocation uses
+// only later (the key list and compaction table, the histogram), so that
+// two workgroups fit a CU.
 __global__ void __launch_bounds__(BS) sq_merge_topk_kernel(ShardQArgs a) {
-  __shared__ SqMergeShared sh;
+  __shared__ RowShared sh;
+  static_assert(kSqMergeCap - kCandCap <= (int)(sizeof(sh.ctab) / sizeof(uint64_t)), "codes fit the key list and table");
+  static_assert(kSqMergeCap <= kHistBins, "logits fit the histogram");
+  uint64_t* const comp_lo = sh.ckey;
+  uint64_t* const comp_hi = reinterpret_cast<uint64_t*>(sh.ctab);
+  auto comp = [&](int j) -> uint64_t& { return j < kCandCap ? comp_lo[j] : comp_hi[j - kCandCap]; };  // key32 << 32 | ~id
+  float* const xs = reinterpret_cast<float*>(sh.hist);
   const int r = blockIdx.x;
   const TkRow t = a.tkr[r];
   if (t.k == 0 || !a.sp_len) return;  // (the same for every thread)
@@ -1044,46 +1047,52 @@ __global__ void __launch_bounds__(BS) sq_merge_topk_kernel(ShardQArgs a) {
     for (int j = threadIdx.x; j < n; j += BS) {
       const SqCand c = a.cand[rs * a.k_max + j];
       const float x = __uint_as_float(c.xbits);
-      sh.comp[nc + j] = ((uint64_t)key32(x) << 32) | (0xffffffffu - (uint32_t)c.id);
-      sh.x[nc + j] = x;
+      comp(nc + j) = ((uint64_t)key32(x) << 32) | (0xffffffffu - (uint32_t)c.id);
+      xs[nc + j] = x;
     }
     nc += n;
   }
   __syncthreads();
   const int k = t.k < nc ? t.k : nc;
   constexpr int PER = kSqMergeCap / BS;  // candidates per thread, in order
-  uint64_t lo = 0, hi = ~0ull;           // the largest T with #{comp >= T} >= k
+  uint64_t cv[PER];  // this thread's codes (0 past the end: below every code, never counted)
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = (int)threadIdx.x * PER + i;
+    cv[i] = j < nc ? comp(j) : 0ull;
+  }
+  uint64_t lo = 0, hi = ~0ull;  // the largest T with #{comp >= T} >= k
   while (lo < hi) {
     const uint64_t mid = lo + (hi - lo) / 2 + 1;
     uint32_t cnt = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int j = (int)threadIdx.x * PER + i;
-      cnt += (j < nc && sh.comp[j] >= mid) ? 1u : 0u;
-    }
-    if (block_sum<uint32_t>(cnt, sh.rs.bs) >= (uint32_t)k) lo = mid;
+    for (int i = 0; i < PER; ++i) cnt += cv[i] >= mid ? 1u : 0u;
+    if (block_sum<uint32_t>(cnt, sh.bs) >= (uint32_t)k) lo = mid;
     else hi = mid - 1;
   }
   uint32_t mine = 0;
+  float xv[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int j = (int)threadIdx.x * PER + i;
-    mine += (j < nc && sh.comp[j] >= lo) ? 1u : 0u;
+    mine += cv[i] >= lo && j < nc ? 1u : 0u;
+    xv[i] = j < nc ? xs[j] : 0.0f;
   }
   uint32_t tot;
-  uint32_t pos = block_excl_scan<uint32_t>(mine, sh.rs.bs, &tot);
+  uint32_t pos = block_excl_scan<uint32_t>(mine, sh.bs, &tot);
+  __syncthreads();  // (codes and logits read: their LDS is the allocation's from here on)
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int j = (int)threadIdx.x * PER + i;
-    if (j < nc && sh.comp[j] >= lo) {
-      sh.rs.cid[pos] = 0xffffffffu - (uint32_t)sh.comp[j];
-      sh.rs.sx[pos] = sh.x[j];
+    if (j < nc && cv[i] >= lo) {
+      sh.cid[pos] = 0xffffffffu - (uint32_t)cv[i];
+      sh.sx[pos] = xv[i];
       ++pos;
     }
   }
   __syncthreads();
   const QOut qo = support_alloc(t.m, k, a.sp_ids + (size_t)r * a.k_max, a.sp_cnt + (size_t)r * a.k_max,
-                                a.sp_len + r, false, 0u, sh.rs);
+                                a.sp_len + r, false, 0u, sh);
   if (qo.status != DSPARK_ST_OK && threadIdx.x == 0) {
     a.tkr[r].status = qo.status;
     a.sp_len[r] = 0;
