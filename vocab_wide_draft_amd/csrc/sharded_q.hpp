@@ -861,34 +861,80 @@ union SqTopkShared {
   SqTopkFastShared ft;
 };
 
+// A bf16 shard [lo, hi) of a row as vectors of eight values on the grid of
+// ids A + 8 q (A = lo rounded down to a multiple of 8, so the vectors are
+// 16-byte aligned): whole vectors inside the shard in one load, the first
+// and last element by element; ids outside the shard are masked off.
+struct Bf16ShardVecs {
+  const uint16_t* row;  // the row's first logit
+  int lo, hi, A;
+  __device__ int nvec() const { return (hi - A + 7) / 8; }
+  // the vector's four words (two values each, the lower id in the low half)
+  // and the mask of its ids inside the shard
+  __device__ __forceinline__ uint32_t load(int q, uint32_t (&w)[4]) const {
+    const int b = A + 8 * q;
+    if (b >= lo && b + 8 <= hi) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + b);
+      w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+      return 0xffu;
+    }
+    uint32_t msk = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i0 = b + 2 * c, i1 = i0 + 1;
+      const uint32_t v0 = i0 >= lo && i0 < hi ? row[i0] : 0u, v1 = i1 >= lo && i1 < hi ? row[i1] : 0u;
+      w[c] = v0 | (v1 << 16);
+      msk |= (i0 >= lo && i0 < hi ? 1u : 0u) << (2 * c);
+      msk |= (i1 >= lo && i1 < hi ? 1u : 0u) << (2 * c + 1);
+    }
+    return msk;
+  }
+};
+
 // The top-kl of a bf16 shard by (logit desc, id asc), in ascending id order,
 // from the row's value table (fast_q.hpp: entries ordered by value, largest
 // first; m = the row maximum): the shard's values counted per entry, the
 // threshold entry where the running count reaches kl, then every element
 // above it and the need lowest ids of it, placed by one count pass and one
-// write pass.  Returns the count (kl), or -1 where the table does not decide
+// write pass.  Table entries of two values at once come from packed 16-bit
+// arithmetic.  Returns the count (kl), or -1 where the table does not decide
 // (no table for this m, fewer than kl values in the weight window, or a
 // partly taken collapsed entry, which holds several values); the same in
 // every thread.
-template <int DT>
-__device__ int sq_topk_table(const ScalarRow<DT>& row, int lo, float m, int kl, SqCand* out, SqTopkFastShared& sh) {
-  constexpr int EPV = ScalarRow<DT>::EPV;
-  const int nvec = row.nvec();
+__device__ int sq_topk_table(const Bf16ShardVecs& sv, float m, int kl, SqCand* out, SqTopkFastShared& sh) {
+  const int nvec = sv.nvec();
   const int n_iter = (nvec + BS - 1) / BS;
   if (kl < 1 || n_iter > kSqTopkIters) return -1;
   const FMap f = fmap_make(__float_as_uint(m) >> 16);  // (m is a bf16 value)
   if (f.NB > kNBF) return -1;
-  auto bin_of = [&](float x) { return fmap_bin(__float_as_uint(x) >> 16, f); };
+  const uint32_t D2 = fmap_dummy2();
+  // entries (times 4, as byte offsets) of the eight values; ids outside the
+  // shard get an overflow slot, which no threshold reaches
+  auto offsets = [&](const uint32_t (&w)[4], uint32_t msk, uint32_t (&o)[8]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t t = fmap_off2(w[c], f, D2);
+      o[2 * c] = (msk >> (2 * c)) & 1u ? (t & 0xffffu) : (D2 & 0xffffu) << 2;
+      o[2 * c + 1] = (msk >> (2 * c + 1)) & 1u ? (t >> 16) : (D2 & 0xffffu) << 2;
+    }
+  };
   for (int b = threadIdx.x; b < kNBFD; b += BS) sh.nb[b] = 0u;
   __syncthreads();
-  for_vecs<kPF, float, EPV>(nvec, [&](int q, float (&x)[EPV]) { return row.load(q, x); },
-                            [&](int q, const float (&x)[EPV], int nv) {
+  char* const nbase = reinterpret_cast<char*>(sh.nb);
+  for (int q0 = threadIdx.x; q0 < nvec; q0 += kPF * BS) {
+    uint32_t w[kPF][4], msk[kPF];
 #pragma unroll
-    for (int l = 0; l < EPV; ++l) {
-      const int b = bin_of(x[l]);
-      if (l < nv && b < f.NB) atomicAdd(&sh.nb[b], 1u);  // (below the window: not counted)
+    for (int k = 0; k < kPF; ++k) msk[k] = q0 + k * BS < nvec ? sv.load(q0 + k * BS, w[k]) : 0u;
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      if (msk[k]) {
+        uint32_t o[8];
+        offsets(w[k], msk[k], o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) atomicAdd(reinterpret_cast<uint32_t*>(nbase + o[e]), 1u);
+      }
     }
-  });
+  }
   __syncthreads();
   uint32_t s = 0;
   for (int b = threadIdx.x; b < f.NB; b += BS) s += sh.nb[b];
@@ -897,27 +943,32 @@ __device__ int sq_topk_table(const ScalarRow<DT>& row, int lo, float m, int kl, 
   const int bt = block_find_crossing(sh.nb, f.NB, (uint64_t)kl, true, sh, &before);
   const uint32_t need = (uint32_t)kl - (uint32_t)before;
   if (bt == f.B0 && need < sh.nb[bt]) return -1;
+  const uint32_t ot = 4u * (uint32_t)bt;  // the threshold entry's offset
+  auto classify = [&](const uint32_t (&w)[4], uint32_t msk, uint32_t& ma, uint32_t& mt) {
+    uint32_t o[8];
+    offsets(w, msk, o);
+    ma = mt = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ma |= o[e] < ot ? 1u << e : 0u;
+      mt |= o[e] == ot ? 1u << e : 0u;
+    }
+  };
   // elements above the threshold entry and in it, per (iteration, wave)
   for (int i0 = 0; i0 < n_iter; i0 += kPF) {
-    float x[kPF][EPV];
-    int nv[kPF];
+    uint32_t w[kPF][4], msk[kPF];
 #pragma unroll
     for (int k = 0; k < kPF; ++k) {
       const int q = (i0 + k) * BS + (int)threadIdx.x;
-      nv[k] = i0 + k < n_iter && q < nvec ? row.load(q, x[k]) : 0;
+      msk[k] = i0 + k < n_iter && q < nvec ? sv.load(q, w[k]) : 0u;
     }
 #pragma unroll
     for (int k = 0; k < kPF; ++k) {
       if (i0 + k < n_iter) {  // (uniform)
-        uint32_t ca = 0, ct = 0;
-#pragma unroll
-        for (int l = 0; l < EPV; ++l) {
-          const int b = bin_of(x[k][l]);
-          ca += l < nv[k] && b < bt ? 1u : 0u;
-          ct += l < nv[k] && b == bt ? 1u : 0u;
-        }
-        ca = wave_sum(ca);
-        ct = wave_sum(ct);
+        uint32_t ma = 0, mt = 0;
+        if (msk[k]) classify(w[k], msk[k], ma, mt);
+        const uint32_t ca = wave_sum((uint32_t)__builtin_popcount(ma));
+        const uint32_t ct = wave_sum((uint32_t)__builtin_popcount(mt));
         if (lane_id() == 0) {
           sh.cab[(i0 + k) * NW + wave_id()] = ca;
           sh.ctie[(i0 + k) * NW + wave_id()] = ct;
@@ -951,36 +1002,33 @@ __device__ int sq_topk_table(const ScalarRow<DT>& row, int lo, float m, int kl, 
   }
   __syncthreads();
   for (int i0 = 0; i0 < n_iter; i0 += kPF) {
-    float x[kPF][EPV];
-    int nv[kPF];
+    uint32_t w[kPF][4], msk[kPF];
 #pragma unroll
     for (int k = 0; k < kPF; ++k) {
       const int q = (i0 + k) * BS + (int)threadIdx.x;
-      nv[k] = i0 + k < n_iter && q < nvec ? row.load(q, x[k]) : 0;
+      msk[k] = i0 + k < n_iter && q < nvec ? sv.load(q, w[k]) : 0u;
     }
 #pragma unroll
     for (int k = 0; k < kPF; ++k) {
       if (i0 + k < n_iter) {  // (uniform)
         uint32_t ma = 0, mt = 0;
-#pragma unroll
-        for (int l = 0; l < EPV; ++l) {
-          const int b = bin_of(x[k][l]);
-          ma |= l < nv[k] && b < bt ? 1u << l : 0u;
-          mt |= l < nv[k] && b == bt ? 1u << l : 0u;
-        }
+        if (msk[k]) classify(w[k], msk[k], ma, mt);
         const uint32_t ca = (uint32_t)__builtin_popcount(ma), ct = (uint32_t)__builtin_popcount(mt);
         uint32_t ab = sh.cab[(i0 + k) * NW + wave_id()] + wave_incl_scan(ca) - ca;  // above before this lane
         uint32_t tb = sh.ctie[(i0 + k) * NW + wave_id()] + wave_incl_scan(ct) - ct;  // threshold ones before it
-        const int q = (i0 + k) * BS + (int)threadIdx.x;
+        if (ma | mt) {
+          const int id0 = sv.A + 8 * ((i0 + k) * BS + (int)threadIdx.x);
 #pragma unroll
-        for (int l = 0; l < EPV; ++l) {
-          const SqCand c{lo + q * EPV + l, __float_as_uint(x[k][l])};
-          if ((ma >> l) & 1u) {
-            out[ab + (tb < need ? tb : need)] = c;
-            ++ab;
-          } else if ((mt >> l) & 1u) {
-            if (tb < need) out[ab + tb] = c;
-            ++tb;
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t word = w[k][e >> 1];
+            const SqCand c{id0 + e, (e & 1) ? (word & 0xffff0000u) : (word << 16)};
+            if ((ma >> e) & 1u) {
+              out[ab + (tb < need ? tb : need)] = c;
+              ++ab;
+            } else if ((mt >> e) & 1u) {
+              if (tb < need) out[ab + tb] = c;
+              ++tb;
+            }
           }
         }
       }
@@ -1006,7 +1054,9 @@ __global__ void __launch_bounds__(BS) sq_local_topk_kernel(ShardQArgs a) {
   const int kl = t.k < hi - lo ? t.k : hi - lo;
   const size_t rs = (size_t)blockIdx.x;
   int n = -1;
-  if constexpr (DT == DSPARK_BF16) n = sq_topk_table(row, lo, t.m, kl, a.cand + rs * a.k_max, sh.ft);
+  if constexpr (DT == DSPARK_BF16)
+    n = sq_topk_table(Bf16ShardVecs{static_cast<const uint16_t*>(a.data) + (size_t)r * (size_t)a.stride, lo, hi, lo & ~7},
+                      t.m, kl, a.cand + rs * a.k_max, sh.ft);
   if (n < 0) {
     __syncthreads();  // (the table path's LDS is the same memory)
     const Stats st = row_stats(row, sh.rs.bs);
