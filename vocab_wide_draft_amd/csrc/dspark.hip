@@ -876,8 +876,8 @@ void launch_sharded_q(ShardQArgs a, bool sparse, void* stream) {
   hipLaunchKernelGGL(sq_max_kernel<DT>, dim3(nb + nt * (unsigned)a.Gt), dim3(kShardBS), 0, s, a);
   hipLaunchKernelGGL(sq_sum_kernel<DT>, dim3(nb + nt), dim3(kShardBS), 0, s, a);
   if (a.dense) {
-    hipLaunchKernelGGL(sq_floor_kernel, dim3(nb), dim3(BS), 0, s, a);
-    hipLaunchKernelGGL(sq_cand_kernel, dim3(nb), dim3(BS), 0, s, a);
+    hipLaunchKernelGGL(sq_floor_kernel<DT>, dim3(nb), dim3(BS), 0, s, a);
+    hipLaunchKernelGGL(sq_cand_kernel<DT>, dim3(nb), dim3(BS), 0, s, a);
   }
   if (sparse) {
     hipLaunchKernelGGL(sq_local_topk_kernel<DT>, dim3(nb), dim3(BS), 0, s, a);

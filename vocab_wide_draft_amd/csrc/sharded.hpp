@@ -238,28 +238,45 @@ __device__ __forceinline__ Acc block_acc_total(Acc a, Acc* s_a) {
   return a;
 }
 
-// bf16 weights from a per-workgroup table: the weight of every bf16 value in
-// the window [m - 105, m], laid out as the row kernel's value table
-// (fast_q.hpp), so that an element's weight is a table read.  Rows whose table
-// would exceed kNBF entries (a maximum below about 0.04) take the exponential
-// per element.
-struct ShardWTab {
-  FMap f;
-  bool on;
-};
-// all threads; the caller's barrier publishes the table
-__device__ __forceinline__ ShardWTab shard_wtab_build(float m, float* tab, const double* etab) {
-  ShardWTab w;
-  w.f = fmap_make(__float_as_uint(m) >> 16);  // (m is a bf16 value)
-  w.on = w.f.NB <= kNBF;
-  if (w.on)
-    for (int b = (int)threadIdx.x; b < w.f.NB; b += (int)blockDim.x)
-      tab[b] = cr_expf(bf16_to_f32(fmap_raw(b, w.f)) - m, etab);
-  return w;
-}
-__device__ __forceinline__ uint32_t shard_wtab_weight(uint32_t raw, const ShardWTab& w, const float* tab) {
-  const int bin = fmap_bin(raw, w.f);
-  return bin >= 0 && bin < w.f.NB ? __float_as_uint(tab[bin]) : 0u;  // (below the window: 0)
+// Counts the values of the bf16 shard [lo, hi) of a row (16-byte aligned
+// row start) per entry of the row's value table (fast_q.hpp) into nb, which
+// the caller cleared before an earlier barrier: the 16-byte aligned middle
+// as vectors of eight values, UV per thread in flight, their entries two at
+// a time; head and tail element by element.  Values below the weight window
+// and -inf land in the overflow slots [NB, kNBFD).  NT threads.
+template <int NT, int UV>
+__device__ __forceinline__ void bf16_count_entries(const uint16_t* row, int lo, int hi, const FMap& f, uint32_t* nb) {
+  const int a0 = (lo + 7) / 8 * 8 < hi ? (lo + 7) / 8 * 8 : hi;
+  const int a1 = hi / 8 * 8 > a0 ? hi / 8 * 8 : a0;
+  for (int i = lo + (int)threadIdx.x; i < a0; i += NT) {
+    const int b = fmap_bin(row[i], f);
+    if (b < f.NB) atomicAdd(&nb[b], 1u);
+  }
+  for (int i = a1 + (int)threadIdx.x; i < hi; i += NT) {
+    const int b = fmap_bin(row[i], f);
+    if (b < f.NB) atomicAdd(&nb[b], 1u);
+  }
+  const uint4* vrow = reinterpret_cast<const uint4*>(row);
+  const uint32_t D2 = fmap_dummy2();
+  char* const base = reinterpret_cast<char*>(nb);
+  const int q1 = a1 / 8;
+  for (int q0 = a0 / 8 + (int)threadIdx.x; q0 < q1; q0 += UV * NT) {
+    uint4 xv[UV];
+#pragma unroll
+    for (int u = 0; u < UV; ++u) xv[u] = q0 + u * NT < q1 ? ld_nt(vrow + q0 + u * NT) : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+      if (q0 + u * NT < q1) {
+        const uint32_t w[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t o = fmap_off2(w[c], f, D2);
+          atomicAdd(reinterpret_cast<uint32_t*>(base + (o & 0xffffu)), 1u);
+          atomicAdd(reinterpret_cast<uint32_t*>(base + (o >> 16)), 1u);
+        }
+      }
+    }
+  }
 }
 
 // The shard's exact weight sum: the 16-byte aligned middle of the shard as

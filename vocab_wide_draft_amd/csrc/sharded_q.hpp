@@ -184,6 +184,11 @@ __device__ __forceinline__ float sq_value(const ShardQArgs& a, int r, int v) {
   return shard_value<DT>(a.data, a.stride, r, v);
 }
 
+template <bool B>
+struct BoolC {  // a compile-time flag passed as an argument
+  static constexpr bool value = B;
+};
+
 // The merged head of G <= 64 shard heads (one lane per shard), in every
 // lane of the calling wave: (value desc, id asc) is a total order, so the
 // butterfly leaves the same head everywhere.
@@ -240,8 +245,9 @@ __device__ __forceinline__ TkRow sq_row_state(const ShardQArgs& a, float m, uint
 // (row, shard) workgroups: every shard merges its row's shard heads (m and
 // the row's state); shard 0 publishes the state and the argmax and zeroes
 // the row's first-digit histogram.  Dense rows: the exact integer sum of the
-// shard's weights RN32(exp(RN32(x - m))), and the weights themselves kept in
-// the row's count storage for the passes that follow.  Workgroups past the
+// shard's weights RN32(exp(RN32(x - m))), and (rows without a value table)
+// the weights themselves kept in the row's count storage for the passes
+// that follow.  Workgroups past the
 // draft rows' merge the target rows' heads into their argmax and status.
 template <int DT>
 __global__ void __launch_bounds__(kShardBS) __attribute__((amdgpu_waves_per_eu(DT == DSPARK_BF16 ? 4 : 8, 8)))
@@ -307,19 +313,30 @@ sq_sum_kernel(ShardQArgs a) {
   __syncthreads();
   const TkRow t = s_t;
   const bool dense = t.status == DSPARK_ST_OK && t.k == 0;  // (the same for every thread)
-  __shared__ float s_wtab[DT == DSPARK_BF16 ? kNBFD : 1];
-  ShardWTab wt{};
-  if constexpr (DT == DSPARK_BF16) {
-    if (dense) wt = shard_wtab_build(t.m, s_wtab, s_exp);
-    __syncthreads();
-  }
-  auto weight = [&](float x) -> uint32_t {
-    if constexpr (DT == DSPARK_BF16)
-      if (wt.on) return shard_wtab_weight(__float_as_uint(x) >> 16, wt, s_wtab);
-    return __float_as_uint(cr_expf(x - t.m, s_exp));
-  };
   Acc acc;
   acc_zero(acc);
+  if constexpr (DT == DSPARK_BF16) {
+    // a row with a value table (fast_q.hpp): its values counted per entry,
+    // count x weight added once per occupied entry; no weights stored (the
+    // floor and cand passes take them from the table too)
+    __shared__ uint32_t s_nb[kNBFD];
+    const FMap f = fmap_make(dense ? __float_as_uint(t.m) >> 16 : 0u);  // (m is a bf16 value)
+    if (dense && f.NB <= kNBF) {
+      for (int j = (int)threadIdx.x; j < kNBFD; j += kShardBS) s_nb[j] = 0u;
+      __syncthreads();
+      bf16_count_entries<kShardBS, 4>(static_cast<const uint16_t*>(a.data) + (size_t)r * (size_t)a.stride, lo, hi, f,
+                                      s_nb);
+      __syncthreads();
+      for (int j = (int)threadIdx.x; j < f.NB; j += kShardBS) {
+        const uint32_t n = s_nb[j];
+        if (n) acc_add(acc, __float_as_uint(cr_expf(bf16_to_f32(fmap_raw(j, f)) - t.m, s_exp)), n);
+      }
+      acc = block_acc_total(acc, s_a);
+      if (threadIdx.x == 0) a.sums[b] = acc;
+      return;
+    }
+  }
+  auto weight = [&](float x) -> uint32_t { return __float_as_uint(cr_expf(x - t.m, s_exp)); };
   if (dense) {
     uint32_t* crow = a.dense + (size_t)r * a.V;
     const bool cvec = (reinterpret_cast<uintptr_t>(crow) & 15u) == 0u;  // the count row 16-byte aligned
@@ -389,14 +406,71 @@ struct SqShared : SmemBase {
 // (row, shard) workgroups of a dense row: S64 = RN64 of the all-reduced
 // exact sum (one lane per shard sum), then the shard's floor sum, its
 // positive remainders and their first-digit histogram, added into the
-// row's (the histogram all-reduce)
+// row's (the histogram all-reduce).  bf16 rows with a value table count
+// their values per entry and take floor and remainder once per occupied
+// entry; the others read their stored weights.
+template <int DT>
 __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
   __shared__ SqShared sh;
+  __shared__ uint32_t s_nb[DT == DSPARK_BF16 ? kNBFD : 1];
   const int r = blockIdx.x / a.G, g = blockIdx.x % a.G;
   const TkRow t = a.tkr[r];
   if (t.status != DSPARK_ST_OK || t.k != 0) return;  // (the same for every thread)
   int lo, hi;
   shard_range(a.V, a.G, g, &lo, &hi);
+  auto merge_s64 = [&]() {
+    if (threadIdx.x < 64) {
+      Acc s;
+      acc_zero(s);
+      if ((int)threadIdx.x < a.G) s = a.sums[(size_t)r * a.G + threadIdx.x];
+      s = wave_acc_total(s);
+      if (threadIdx.x == 0) {
+        sh.s64 = acc_rn64(s);
+        if (g == 0) a.s64[r] = sh.s64;
+      }
+    }
+  };
+  auto finish = [&](uint32_t fsum, uint32_t npos) {
+    const uint64_t fsum_b = block_sum<uint64_t>(fsum, sh.bs);
+    const uint64_t npos_b = block_sum<uint64_t>(npos, sh.bs);
+    __syncthreads();
+    uint32_t* hrow = a.hist + (size_t)r * kTkBins;
+    for (int b = threadIdx.x; b < kTkBins; b += BS)
+      if (sh.hist[b]) atomicAdd(&hrow[b], sh.hist[b]);
+    if (threadIdx.x == 0) {
+      a.tks[blockIdx.x].fsum = fsum_b;
+      a.tks[blockIdx.x].npos = npos_b;
+    }
+  };
+  if constexpr (DT == DSPARK_BF16) {
+    const FMap f = fmap_make(__float_as_uint(t.m) >> 16);  // (m is a bf16 value)
+    if (f.NB <= kNBF) {  // (the same for every thread)
+      for (int j = threadIdx.x; j < kNBFD; j += BS) s_nb[j] = 0u;
+      for (int b = threadIdx.x; b < kTkBins; b += BS) sh.hist[b] = 0u;
+      exp_table_to_lds(sh.etab);
+      merge_s64();
+      __syncthreads();
+      bf16_count_entries<BS, 2>(static_cast<const uint16_t*>(a.data) + (size_t)r * (size_t)a.stride, lo, hi, f, s_nb);
+      __syncthreads();
+      const SumR S = sum_r(sh.s64);
+      uint32_t fsum = 0, npos = 0;  // (a row's floors add up to at most about 2^24)
+      for (int j = threadIdx.x; j < f.NB; j += BS) {
+        const uint32_t n = s_nb[j];
+        if (n) {
+          uint32_t c;
+          double rr;
+          floor_rem(cr_expf(bf16_to_f32(fmap_raw(j, f)) - t.m, sh.etab), S, c, rr);
+          fsum += n * c;
+          if (rr > 0.0) {
+            npos += n;
+            atomicAdd(&sh.hist[sq_first_digit(rr)], n);
+          }
+        }
+      }
+      finish(fsum, npos);
+      return;
+    }
+  }
   const uint32_t* crow = a.dense + (size_t)r * a.V;
   // a 16-byte aligned count row: its middle [a0, a1) as vectors of four
   // weights (UV per thread in flight), head and tail element by element;
@@ -411,16 +485,7 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
 #pragma unroll
   for (int u = 0; u < UV; ++u) wv[u] = q00 + u * BS < q1 ? vrow[q00 + u * BS] : uint4{0u, 0u, 0u, 0u};
   for (int b = threadIdx.x; b < kTkBins; b += BS) sh.hist[b] = 0u;
-  if (threadIdx.x < 64) {
-    Acc s;
-    acc_zero(s);
-    if ((int)threadIdx.x < a.G) s = a.sums[(size_t)r * a.G + threadIdx.x];
-    s = wave_acc_total(s);
-    if (threadIdx.x == 0) {
-      sh.s64 = acc_rn64(s);
-      if (g == 0) a.s64[r] = sh.s64;
-    }
-  }
+  merge_s64();
   __syncthreads();
   const SumR S = sum_r(sh.s64);
   uint32_t fsum = 0, npos = 0;  // (a row's floors add up to at most about 2^24)
@@ -453,16 +518,7 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
       }
     }
   }
-  const uint64_t fsum_b = block_sum<uint64_t>(fsum, sh.bs);
-  const uint64_t npos_b = block_sum<uint64_t>(npos, sh.bs);
-  __syncthreads();
-  uint32_t* hrow = a.hist + (size_t)r * kTkBins;
-  for (int b = threadIdx.x; b < kTkBins; b += BS)
-    if (sh.hist[b]) atomicAdd(&hrow[b], sh.hist[b]);
-  if (threadIdx.x == 0) {
-    a.tks[blockIdx.x].fsum = fsum_b;
-    a.tks[blockIdx.x].npos = npos_b;
-  }
+  finish(fsum, npos);
 }
 
 // (row, shard) workgroups of a dense row: every shard finds remaining (from
@@ -470,9 +526,15 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
 // all-reduced histogram) itself; then, in id order, writes floor + 1 above
 // the bin and the floor below it, flags the ids inside the bin (kSqMark) and
 // keeps the first kSqCandCap of them, and sends its count mass so far.  A
-// refused or inconsistent row's shard is zeroed.
+// refused or inconsistent row's shard is zeroed.  bf16 rows with a value
+// table read their logits and take each id's count word (count and flag)
+// from a table of the entries' words; the others read their stored weights.
+template <int DT>
 __global__ void __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(8, 8))) sq_cand_kernel(ShardQArgs a) {
   __shared__ SqShared sh;
+  __shared__ uint32_t s_cwt[DT == DSPARK_BF16 ? kNBFD : 1];  // count word per table entry
+  __shared__ uint32_t s_cid[DT == DSPARK_BF16 ? kSqCandCap : 1];  // (table rows) the bin's members: ids
+  __shared__ uint32_t s_cfl[DT == DSPARK_BF16 ? kSqCandCap : 1];  // and floors; keys after the pass
   const int r = blockIdx.x / a.G, g = blockIdx.x % a.G;
   const TkRow t = a.tkr[r];
   if (t.k != 0 || !a.dense) return;  // (the same for every thread)
@@ -481,6 +543,15 @@ __global__ void __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(8, 8)))
   uint32_t* crow = a.dense + (size_t)r * a.V;
   TkShard* ts = a.tks + blockIdx.x;
   bool zero = t.status != DSPARK_ST_OK;
+  FMap f{};
+  bool tab = false;  // (the same for every thread)
+  if constexpr (DT == DSPARK_BF16) {
+    if (!zero) {
+      f = fmap_make(__float_as_uint(t.m) >> 16);  // (m is a bf16 value)
+      tab = f.NB <= kNBF;
+    }
+  }
+  const uint16_t* lrow = static_cast<const uint16_t*>(a.data) + (size_t)r * (size_t)a.stride;  // (bf16 rows)
   // ids in order on a grid from A = lo rounded down to a multiple of 4: U
   // consecutive ids per thread (two 16-byte vectors when the count row is
   // 16-byte aligned and all U are in the shard), kSqChunk * 2 per pass
@@ -488,7 +559,22 @@ __global__ void __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(8, 8)))
   static_assert(U * BS == 2 * kSqChunk, "two chunks per pass");
   const int A = lo & ~3;
   const bool cvec = (reinterpret_cast<uintptr_t>(crow) & 15u) == 0u;
-  auto load8 = [&](int vt, uint32_t (&w)[U]) {
+  auto load8 = [&](auto tab_c, int vt, uint32_t (&w)[U]) {
+    if constexpr (decltype(tab_c)::value) {  // the logits, two to a word (ids outside the shard read as -inf: count word 0)
+      if (vt >= lo && vt + U <= hi) {
+        const uint2 x0 = *reinterpret_cast<const uint2*>(lrow + vt), x1 = *reinterpret_cast<const uint2*>(lrow + vt + 4);
+        w[0] = x0.x; w[1] = x0.y; w[2] = x1.x; w[3] = x1.y;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int i0 = vt + 2 * c, i1 = i0 + 1;
+          const uint32_t v0 = i0 >= lo && i0 < hi ? lrow[i0] : 0xff80u, v1 = i1 >= lo && i1 < hi ? lrow[i1] : 0xff80u;
+          w[c] = v0 | (v1 << 16);
+        }
+      }
+      w[4] = w[5] = w[6] = w[7] = 0u;
+      return;
+    }
     if (cvec && vt >= lo && vt + U <= hi) {
       const uint4 x0 = reinterpret_cast<const uint4*>(crow + vt)[0], x1 = reinterpret_cast<const uint4*>(crow + vt)[1];
       w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
@@ -502,10 +588,12 @@ __global__ void __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(8, 8)))
   uint32_t wb[U];
   double s64 = 0.0;
   int64_t remaining = 0;
+  if constexpr (DT == DSPARK_BF16) exp_table_to_lds(sh.etab);
   if (!zero) {
     // everything this shard reads, issued together: its first weights, S64,
     // the merged histogram and the shards' floor sums
-    load8(vt0, wb);
+    if (tab) load8(BoolC<true>{}, vt0, wb);
+    else load8(BoolC<false>{}, vt0, wb);
     s64 = a.s64[r];
     const uint32_t* hrow = a.hist + (size_t)r * kTkBins;
     static_assert(kTkBins % BS == 0, "whole histogram rows per thread");
@@ -560,24 +648,56 @@ __global__ void __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(8, 8)))
   DigitRange dr = sq_digit_range(d);  // (no bin: nothing above it, nothing inside it)
   dr.lo = uniform_f64(dr.lo);
   dr.hi = uniform_f64(dr.hi);
+  if (tab) {
+    for (int j = threadIdx.x; j < kNBFD; j += BS) {
+      uint32_t cw = 0u;
+      if (j < f.NB) {
+        uint32_t c;
+        double rr;
+        floor_rem(cr_expf(bf16_to_f32(fmap_raw(j, f)) - t.m, sh.etab), S, c, rr);
+        const bool above = rr >= dr.hi, inside = rr >= dr.lo && !above;
+        cw = (c + (above ? 1u : 0u)) | (inside ? kSqMark : 0u);
+      }
+      s_cwt[j] = cw;
+    }
+    __syncthreads();
+  }
   uint32_t* cbuf = a.cids + (size_t)blockIdx.x * kSqCandCap;
   uint64_t* kbuf = a.ckeys + (size_t)blockIdx.x * kSqCandCap;
   uint32_t* fbuf = a.cflo + (size_t)blockIdx.x * kSqCandCap;
+  // the pass, compiled once for table rows and once for stored weights
+  auto pass = [&](auto tab_c) {
+  constexpr bool TAB = decltype(tab_c)::value;
+  const uint32_t D2 = fmap_dummy2();
   uint32_t base = 0;
   uint64_t mass = 0;
   for (int v0 = A; v0 < hi; v0 += U * BS) {  // in id order
     const int vt = v0 + (int)threadIdx.x * U;
-    if (v0 != A) load8(vt, wb);
+    if (v0 != A) load8(tab_c, vt, wb);
     uint32_t c[U], nin = 0, tmass = 0;
+    if constexpr (TAB) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {  // (ids outside the shard read weight 0: count 0, remainder 0)
-      double rr;
-      floor_rem(__uint_as_float(wb[u]), S, c[u], rr);
-      const bool above = rr >= dr.hi, inside = rr >= dr.lo && !above;  // first digit > d, == d
-      c[u] += above ? 1u : 0u;
-      tmass += c[u];
-      c[u] |= inside ? kSqMark : 0u;
-      nin += inside ? 1u : 0u;
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t o = fmap_off2(wb[k], f, D2);
+        c[2 * k] = s_cwt[(o & 0xffffu) >> 2];
+        c[2 * k + 1] = s_cwt[o >> 18];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        tmass += c[u] & ~kSqMark;
+        nin += (c[u] & kSqMark) ? 1u : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {  // (ids outside the shard read weight 0: count 0, remainder 0)
+        double rr;
+        floor_rem(__uint_as_float(wb[u]), S, c[u], rr);
+        const bool above = rr >= dr.hi, inside = rr >= dr.lo && !above;  // first digit > d, == d
+        c[u] += above ? 1u : 0u;
+        tmass += c[u];
+        c[u] |= inside ? kSqMark : 0u;
+        nin += inside ? 1u : 0u;
+      }
     }
     // one scan gives the candidates' positions (low word) and the masses
     // (high word): thread kSqChunk / U starts the pass's second chunk
@@ -606,16 +726,34 @@ __global__ void __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(8, 8)))
       for (int u = 0; u < U; ++u) {
         if (c[u] & kSqMark) {
           if (pos < (uint32_t)kSqCandCap) {
-            uint32_t cf;
-            double rr;
-            floor_rem(__uint_as_float(wb[u]), S, cf, rr);
-            cbuf[pos] = (uint32_t)(vt + u);
-            kbuf[pos] = rem_key(rr);
-            fbuf[pos] = c[u] & ~kSqMark;
+            if constexpr (TAB) {
+              s_cid[pos] = (uint32_t)(vt + u);
+              s_cfl[pos] = c[u] & ~kSqMark;
+            } else {
+              uint32_t cf;
+              double rr;
+              floor_rem(__uint_as_float(wb[u]), S, cf, rr);
+              cbuf[pos] = (uint32_t)(vt + u);
+              kbuf[pos] = rem_key(rr);
+              fbuf[pos] = c[u] & ~kSqMark;
+            }
           }
           ++pos;
         }
       }
+    }
+  }
+  if constexpr (TAB) {  // the members' keys, from their logits
+    __syncthreads();
+    const int nk = base < (uint32_t)kSqCandCap ? (int)base : kSqCandCap;
+    for (int j = threadIdx.x; j < nk; j += BS) {
+      const uint32_t id = s_cid[j];
+      uint32_t cf;
+      double rr;
+      floor_rem(cr_expf(bf16_to_f32(lrow[id]) - t.m, sh.etab), S, cf, rr);
+      cbuf[j] = id;
+      kbuf[j] = rem_key(rr);
+      fbuf[j] = s_cfl[j];
     }
   }
   if (threadIdx.x == 0) {
@@ -623,6 +761,14 @@ __global__ void __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(8, 8)))
     ts->ncand = base;
     if (g == 0) a.cut[r] = TkCut{need, d, mode};
   }
+  };
+  if constexpr (DT == DSPARK_BF16) {
+    if (tab) {
+      pass(BoolC<true>{});
+      return;
+    }
+  }
+  pass(BoolC<false>{});
 }
 
 struct SqFinShared : SmemBase {
