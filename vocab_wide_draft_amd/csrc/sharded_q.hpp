@@ -1090,6 +1090,19 @@ __device__ int sq_topk_table(const Bf16ShardVecs& sv, float m, int kl, SqCand* o
   const uint32_t need = (uint32_t)kl - (uint32_t)before;
   if (bt == f.B0 && need < sh.nb[bt]) return -1;
   const uint32_t ot = 4u * (uint32_t)bt;  // the threshold entry's offset
+  // Above the collapsed entry the threshold entry is one positive value T,
+  // and raw bf16 patterns order like signed 16-bit integers against it
+  // (negative values have the sign bit set): a vector none of whose values
+  // reaches T holds nothing above the threshold and nothing of it.
+  const bool quick = bt < f.B0;
+  const short traw = (short)fmap_raw(bt, f);
+  auto may_hold = [&](const uint32_t (&w)[4]) {
+    if (!quick) return true;
+    const s16x2 m = __builtin_elementwise_max(
+        __builtin_elementwise_max(__builtin_bit_cast(s16x2, w[0]), __builtin_bit_cast(s16x2, w[1])),
+        __builtin_elementwise_max(__builtin_bit_cast(s16x2, w[2]), __builtin_bit_cast(s16x2, w[3])));
+    return (m.x > m.y ? m.x : m.y) >= traw;
+  };
   auto classify = [&](const uint32_t (&w)[4], uint32_t msk, uint32_t& ma, uint32_t& mt) {
     uint32_t o[8];
     offsets(w, msk, o);
@@ -1112,7 +1125,7 @@ __device__ int sq_topk_table(const Bf16ShardVecs& sv, float m, int kl, SqCand* o
     for (int k = 0; k < kPF; ++k) {
       if (i0 + k < n_iter) {  // (uniform)
         uint32_t ma = 0, mt = 0;
-        if (msk[k]) classify(w[k], msk[k], ma, mt);
+        if (msk[k] && may_hold(w[k])) classify(w[k], msk[k], ma, mt);
         const uint32_t ca = wave_sum((uint32_t)__builtin_popcount(ma));
         const uint32_t ct = wave_sum((uint32_t)__builtin_popcount(mt));
         if (lane_id() == 0) {
@@ -1158,7 +1171,7 @@ __device__ int sq_topk_table(const Bf16ShardVecs& sv, float m, int kl, SqCand* o
     for (int k = 0; k < kPF; ++k) {
       if (i0 + k < n_iter) {  // (uniform)
         uint32_t ma = 0, mt = 0;
-        if (msk[k]) classify(w[k], msk[k], ma, mt);
+        if (msk[k] && may_hold(w[k])) classify(w[k], msk[k], ma, mt);
         const uint32_t ca = (uint32_t)__builtin_popcount(ma), ct = (uint32_t)__builtin_popcount(mt);
         uint32_t ab = sh.cab[(i0 + k) * NW + wave_id()] + wave_incl_scan(ca) - ca;  // above before this lane
         uint32_t tb = sh.ctie[(i0 + k) * NW + wave_id()] + wave_incl_scan(ct) - ct;  // threshold ones before it
