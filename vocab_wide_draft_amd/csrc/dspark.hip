@@ -881,7 +881,7 @@ void launch_sharded_q(ShardQArgs a, bool sparse, void* stream) {
   }
   if (sparse) {
     hipLaunchKernelGGL(sq_local_topk_kernel<DT>, dim3(nb), dim3(BS), 0, s, a);
-    hipLaunchKernelGGL(sq_merge_topk_kernel, dim3(nr), dim3(BS), 0, s, a);
+    hipLaunchKernelGGL(sq_merge_topk_kernel<DT>, dim3(nr), dim3(BS), 0, s, a);
   }
   hipLaunchKernelGGL(sq_finish_kernel<DT>, dim3(nr), dim3(BS), 0, s, a);
 }

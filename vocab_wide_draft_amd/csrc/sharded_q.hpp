@@ -1228,19 +1228,25 @@ __global__ void __launch_bounds__(BS) sq_local_topk_kernel(ShardQArgs a) {
 
 // one workgroup per sparse row: the exact global top-k from the shards'
 // candidates, then the allocation on that support.  The k-th largest
-// (logit, -id) pair is found by bisection over its 64-bit code (every code
-// is distinct); the candidates are stored shard after shard, each shard's in
+// (logit, -id) pair is found by bisection over its code, the logit's order
+// key above 20 bits of inverted id (ids are below 2^20; bf16 logits need
+// only the top 16 bits of the key), between the smallest and the largest
+// code present: every code is distinct, and the narrower codes take fewer
+// steps.  The candidates are stored shard after shard, each shard's in
 // ascending id order, so the selected ones come out in ascending id order.
 // The candidates' codes and logits live in LDS that the allocation uses
 // only later (the key list and compaction table, the histogram), so that
 // two workgroups fit a CU.
+template <int DT>
 __global__ void __launch_bounds__(BS) sq_merge_topk_kernel(ShardQArgs a) {
   __shared__ RowShared sh;
   static_assert(kSqMergeCap - kCandCap <= (int)(sizeof(sh.ctab) / sizeof(uint64_t)), "codes fit the key list and table");
   static_assert(kSqMergeCap <= kHistBins, "logits fit the histogram");
   uint64_t* const comp_lo = sh.ckey;
   uint64_t* const comp_hi = reinterpret_cast<uint64_t*>(sh.ctab);
-  auto comp = [&](int j) -> uint64_t& { return j < kCandCap ? comp_lo[j] : comp_hi[j - kCandCap]; };  // key32 << 32 | ~id
+  auto comp = [&](int j) -> uint64_t& { return j < kCandCap ? comp_lo[j] : comp_hi[j - kCandCap]; };
+  static_assert(DSPARK_V_MAX <= (1 << 20), "ids fit 20 bits");
+  constexpr int KS = DT == DSPARK_BF16 ? 16 : 0;  // low key bits that bf16 logits leave constant
   float* const xs = reinterpret_cast<float*>(sh.hist);
   const int r = blockIdx.x;
   const TkRow t = a.tkr[r];
@@ -1256,7 +1262,7 @@ __global__ void __launch_bounds__(BS) sq_merge_topk_kernel(ShardQArgs a) {
     for (int j = threadIdx.x; j < n; j += BS) {
       const SqCand c = a.cand[rs * a.k_max + j];
       const float x = __uint_as_float(c.xbits);
-      comp(nc + j) = ((uint64_t)key32(x) << 32) | (0xffffffffu - (uint32_t)c.id);
+      comp(nc + j) = ((uint64_t)(key32(x) >> KS) << 20) | (0xfffffu - (uint32_t)c.id);  // (never 0: see below)
       xs[nc + j] = x;
     }
     nc += n;
@@ -1264,13 +1270,19 @@ __global__ void __launch_bounds__(BS) sq_merge_topk_kernel(ShardQArgs a) {
   __syncthreads();
   const int k = t.k < nc ? t.k : nc;
   constexpr int PER = kSqMergeCap / BS;  // candidates per thread, in order
-  uint64_t cv[PER];  // this thread's codes (0 past the end: below every code, never counted)
+  // this thread's codes; 0 past the end, below every code (a logit's key
+  // is at least key32(-inf) = 0x7fffff, so its shifted key is not 0)
+  uint64_t cv[PER], cmin = ~0ull, cmax = 0ull;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int j = (int)threadIdx.x * PER + i;
     cv[i] = j < nc ? comp(j) : 0ull;
+    cmin = j < nc && cv[i] < cmin ? cv[i] : cmin;
+    cmax = cv[i] > cmax ? cv[i] : cmax;
   }
-  uint64_t lo = 0, hi = ~0ull;  // the largest T with #{comp >= T} >= k
+  // the largest T with #{comp >= T} >= k, which lies between the smallest
+  // and the largest code (with no candidate: none selected)
+  uint64_t lo = block_min<uint64_t>(cmin, sh.bs), hi = block_max<uint64_t>(cmax, sh.bs);
   while (lo < hi) {
     const uint64_t mid = lo + (hi - lo) / 2 + 1;
     uint32_t cnt = 0;
@@ -1294,7 +1306,7 @@ __global__ void __launch_bounds__(BS) sq_merge_topk_kernel(ShardQArgs a) {
   for (int i = 0; i < PER; ++i) {
     const int j = (int)threadIdx.x * PER + i;
     if (j < nc && cv[i] >= lo) {
-      sh.cid[pos] = 0xffffffffu - (uint32_t)cv[i];
+      sh.cid[pos] = 0xfffffu - (uint32_t)(cv[i] & 0xfffffu);
       sh.sx[pos] = xv[i];
       ++pos;
     }
