@@ -70,6 +70,8 @@ def _q_rows(V, rng):
     t = rng.random(V) < 0.02; r[t] = tiny[rng.integers(0, 5, int(t.sum()))]
     r[V // 5] = 10.0; rows.append(r)                                         # collapsed entry above the cut
     rows.append((0.75 + rng.standard_normal(V) * 1e-6).astype(np.float32))  # fp32: one first digit, many keys
+    r = np.full(V, -np.inf, np.float32); r[(2 * V) // 3] = 2.5; rows.append(r)   # one-hot: top-k reaches into -inf
+    r = np.full(V, -np.inf, np.float32); r[rng.integers(0, V, 5)] = -3.0; r[V - 2] = -1.0; rows.append(r)  # negative maximum, few finite
     r = base.copy(); r[V - 1] = np.nan; rows.append(r)                      # refused
     return np.stack(rows)
 
@@ -86,7 +88,7 @@ def test_sharded_q(dtype, V):
     n = raw.shape[0]
     d = to_dev(raw, dtype)
     draws = rng.integers(0, 1 << 24, n, dtype=np.uint32)
-    for ks in ((0,) * n, (7, 0, 64, 0, 33, 1, 5, 0, 12, 6, 33, 0)[:n]):
+    for ks in ((0,) * n, (7, 0, 64, 0, 33, 1, 5, 0, 12, 6, 33, 0, 64, 9)[:n]):
         topk = np.array(ks, np.int32)
         refs = [O.draft_row(raw[j], dtype, int(topk[j]), int(draws[j])) for j in range(n)]
         for G in (1, 2, 3, 8, 64):

@@ -1037,6 +1037,98 @@ struct Bf16ShardVecs {
   }
 };
 
+// The second half of a bf16 shard's top-k: every element that
+// classify(w, msk, ma, mt) marks in ma ("above"), and the need lowest ids of
+// those it marks in mt ("tied"), written to out in ascending id order by one
+// count pass (per (iteration, wave)), one scan and one write pass.  The
+// caller's marks must total need plus the number of ids written before.
+template <class CL>
+__device__ __forceinline__ void sq_topk_place(const Bf16ShardVecs& sv, CL classify, uint32_t need, SqCand* out,
+                                              SqTopkFastShared& sh) {
+  const int nvec = sv.nvec();
+  const int n_iter = (nvec + BS - 1) / BS;
+  // elements above the threshold entry and in it, per (iteration, wave)
+  for (int i0 = 0; i0 < n_iter; i0 += kPF) {
+    uint32_t w[kPF][4], msk[kPF];
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      const int q = (i0 + k) * BS + (int)threadIdx.x;
+      msk[k] = i0 + k < n_iter && q < nvec ? sv.load(q, w[k]) : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      if (i0 + k < n_iter) {  // (uniform)
+        uint32_t ma = 0, mt = 0;
+        if (msk[k]) classify(w[k], msk[k], ma, mt);
+        const uint32_t ca = wave_sum((uint32_t)__builtin_popcount(ma));
+        const uint32_t ct = wave_sum((uint32_t)__builtin_popcount(mt));
+        if (lane_id() == 0) {
+          sh.cab[(i0 + k) * NW + wave_id()] = ca;
+          sh.ctie[(i0 + k) * NW + wave_id()] = ct;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  {  // exclusive prefix of both tables in (iteration, wave) order: id order
+    constexpr int PER = kSqTopkIters * NW / BS;
+    const int nt = n_iter * NW;
+    uint64_t v[PER], sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = (int)threadIdx.x * PER + j;
+      v[j] = e < nt ? ((uint64_t)sh.ctie[e] << 32) | sh.cab[e] : 0ull;
+      sum += v[j];
+    }
+    uint64_t tot;
+    uint64_t pre = block_excl_scan<uint64_t>(sum, sh.bs, &tot);
+    __syncthreads();  // (every table entry read before any is overwritten)
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = (int)threadIdx.x * PER + j;
+      if (e < nt) {
+        sh.cab[e] = (uint32_t)pre;
+        sh.ctie[e] = (uint32_t)(pre >> 32);
+      }
+      pre += v[j];
+    }
+  }
+  __syncthreads();
+  for (int i0 = 0; i0 < n_iter; i0 += kPF) {
+    uint32_t w[kPF][4], msk[kPF];
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      const int q = (i0 + k) * BS + (int)threadIdx.x;
+      msk[k] = i0 + k < n_iter && q < nvec ? sv.load(q, w[k]) : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      if (i0 + k < n_iter) {  // (uniform)
+        uint32_t ma = 0, mt = 0;
+        if (msk[k]) classify(w[k], msk[k], ma, mt);
+        const uint32_t ca = (uint32_t)__builtin_popcount(ma), ct = (uint32_t)__builtin_popcount(mt);
+        uint32_t ab = sh.cab[(i0 + k) * NW + wave_id()] + wave_incl_scan(ca) - ca;  // above before this lane
+        uint32_t tb = sh.ctie[(i0 + k) * NW + wave_id()] + wave_incl_scan(ct) - ct;  // threshold ones before it
+        if (ma | mt) {
+          const int id0 = sv.A + 8 * ((i0 + k) * BS + (int)threadIdx.x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t word = w[k][e >> 1];
+            const SqCand c{id0 + e, (e & 1) ? (word & 0xffff0000u) : (word << 16)};
+            if ((ma >> e) & 1u) {
+              out[ab + (tb < need ? tb : need)] = c;
+              ++ab;
+            } else if ((mt >> e) & 1u) {
+              if (tb < need) out[ab + tb] = c;
+              ++tb;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 // The top-kl of a bf16 shard by (logit desc, id asc), in ascending id order,
 // from the row's value table (fast_q.hpp: entries ordered by value, largest
 // first; m = the row maximum): the shard's values counted per entry, the
@@ -1113,94 +1205,59 @@ __device__ int sq_topk_table(const Bf16ShardVecs& sv, float m, int kl, SqCand* o
       mt |= o[e] == ot ? 1u << e : 0u;
     }
   };
-  // elements above the threshold entry and in it, per (iteration, wave)
-  for (int i0 = 0; i0 < n_iter; i0 += kPF) {
+  auto classify_q = [&](const uint32_t (&w)[4], uint32_t msk, uint32_t& ma, uint32_t& mt) {
+    ma = mt = 0u;
+    if (may_hold(w)) classify(w, msk, ma, mt);
+  };
+  sq_topk_place(sv, classify_q, need, out, sh);
+  return kl;
+}
+
+
+// The top-kl of a bf16 shard with at most kl finite values (one-hot and
+// masked rows, whose top-k reaches into -inf): every finite value, then the
+// lowest ids of -inf.  Returns kl, or -1 when the shard holds more finite
+// values (the same in every thread).  A row of status OK holds no NaN and no
+// +inf.
+__device__ __forceinline__ int sq_topk_fewfinite(const Bf16ShardVecs& sv, int kl, SqCand* out,
+                                                 SqTopkFastShared& sh) {
+  const int nvec = sv.nvec();
+  const int n_iter = (nvec + BS - 1) / BS;
+  if (kl < 1 || n_iter > kSqTopkIters) return -1;
+  auto inf_mask = [](const uint32_t (&w)[4], uint32_t msk) {  // the -inf values among the shard's ones
+    uint32_t mi = 0u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      mi |= (w[c] & 0xffffu) == 0xff80u ? 1u << (2 * c) : 0u;
+      mi |= (w[c] >> 16) == 0xff80u ? 1u << (2 * c + 1) : 0u;
+    }
+    return mi & msk;
+  };
+  uint32_t nfin = 0u;
+  for (int q0 = threadIdx.x; q0 < nvec; q0 += kPF * BS) {
     uint32_t w[kPF][4], msk[kPF];
 #pragma unroll
-    for (int k = 0; k < kPF; ++k) {
-      const int q = (i0 + k) * BS + (int)threadIdx.x;
-      msk[k] = i0 + k < n_iter && q < nvec ? sv.load(q, w[k]) : 0u;
-    }
+    for (int k = 0; k < kPF; ++k) msk[k] = q0 + k * BS < nvec ? sv.load(q0 + k * BS, w[k]) : 0u;
 #pragma unroll
-    for (int k = 0; k < kPF; ++k) {
-      if (i0 + k < n_iter) {  // (uniform)
-        uint32_t ma = 0, mt = 0;
-        if (msk[k] && may_hold(w[k])) classify(w[k], msk[k], ma, mt);
-        const uint32_t ca = wave_sum((uint32_t)__builtin_popcount(ma));
-        const uint32_t ct = wave_sum((uint32_t)__builtin_popcount(mt));
-        if (lane_id() == 0) {
-          sh.cab[(i0 + k) * NW + wave_id()] = ca;
-          sh.ctie[(i0 + k) * NW + wave_id()] = ct;
-        }
-      }
-    }
+    for (int k = 0; k < kPF; ++k) nfin += (uint32_t)__builtin_popcount(msk[k] & ~inf_mask(w[k], msk[k]));
   }
-  __syncthreads();
-  {  // exclusive prefix of both tables in (iteration, wave) order: id order
-    constexpr int PER = kSqTopkIters * NW / BS;
-    const int nt = n_iter * NW;
-    uint64_t v[PER], sum = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = (int)threadIdx.x * PER + j;
-      v[j] = e < nt ? ((uint64_t)sh.ctie[e] << 32) | sh.cab[e] : 0ull;
-      sum += v[j];
-    }
-    uint64_t tot;
-    uint64_t pre = block_excl_scan<uint64_t>(sum, sh.bs, &tot);
-    __syncthreads();  // (every table entry read before any is overwritten)
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = (int)threadIdx.x * PER + j;
-      if (e < nt) {
-        sh.cab[e] = (uint32_t)pre;
-        sh.ctie[e] = (uint32_t)(pre >> 32);
-      }
-      pre += v[j];
-    }
-  }
-  __syncthreads();
-  for (int i0 = 0; i0 < n_iter; i0 += kPF) {
-    uint32_t w[kPF][4], msk[kPF];
-#pragma unroll
-    for (int k = 0; k < kPF; ++k) {
-      const int q = (i0 + k) * BS + (int)threadIdx.x;
-      msk[k] = i0 + k < n_iter && q < nvec ? sv.load(q, w[k]) : 0u;
-    }
-#pragma unroll
-    for (int k = 0; k < kPF; ++k) {
-      if (i0 + k < n_iter) {  // (uniform)
-        uint32_t ma = 0, mt = 0;
-        if (msk[k] && may_hold(w[k])) classify(w[k], msk[k], ma, mt);
-        const uint32_t ca = (uint32_t)__builtin_popcount(ma), ct = (uint32_t)__builtin_popcount(mt);
-        uint32_t ab = sh.cab[(i0 + k) * NW + wave_id()] + wave_incl_scan(ca) - ca;  // above before this lane
-        uint32_t tb = sh.ctie[(i0 + k) * NW + wave_id()] + wave_incl_scan(ct) - ct;  // threshold ones before it
-        if (ma | mt) {
-          const int id0 = sv.A + 8 * ((i0 + k) * BS + (int)threadIdx.x);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t word = w[k][e >> 1];
-            const SqCand c{id0 + e, (e & 1) ? (word & 0xffff0000u) : (word << 16)};
-            if ((ma >> e) & 1u) {
-              out[ab + (tb < need ? tb : need)] = c;
-              ++ab;
-            } else if ((mt >> e) & 1u) {
-              if (tb < need) out[ab + tb] = c;
-              ++tb;
-            }
-          }
-        }
-      }
-    }
-  }
+  nfin = block_sum<uint32_t>(nfin, sh.bs);
+  if (nfin > (uint32_t)kl) return -1;
+  auto classify = [&](const uint32_t (&w)[4], uint32_t msk, uint32_t& ma, uint32_t& mt) {
+    mt = inf_mask(w, msk);
+    ma = msk & ~mt;
+  };
+  sq_topk_place(sv, classify, (uint32_t)kl - nfin, out, sh);
   return kl;
 }
 
 // (row, shard) workgroups of a sparse row: the shard's local top-k
 // candidates (global ids and logits), from the row's value table where it
-// decides (bf16), else by narrowing key histograms over the shard
+// decides (bf16), else, for a bf16 shard with at most k finite values, its
+// finite values and the lowest ids of -inf, else by narrowing key histograms
+// over the shard
 template <int DT>
-__global__ void __launch_bounds__(BS) sq_local_topk_kernel(ShardQArgs a) {
+__global__ void __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(8, 8))) sq_local_topk_kernel(ShardQArgs a) {
   __shared__ SqTopkShared sh;
   const int r = blockIdx.x / a.G, g = blockIdx.x % a.G;
   const TkRow t = a.tkr[r];
@@ -1213,9 +1270,14 @@ __global__ void __launch_bounds__(BS) sq_local_topk_kernel(ShardQArgs a) {
   const int kl = t.k < hi - lo ? t.k : hi - lo;
   const size_t rs = (size_t)blockIdx.x;
   int n = -1;
-  if constexpr (DT == DSPARK_BF16)
-    n = sq_topk_table(Bf16ShardVecs{static_cast<const uint16_t*>(a.data) + (size_t)r * (size_t)a.stride, lo, hi, lo & ~7},
-                      t.m, kl, a.cand + rs * a.k_max, sh.ft);
+  if constexpr (DT == DSPARK_BF16) {
+    const Bf16ShardVecs sv{static_cast<const uint16_t*>(a.data) + (size_t)r * (size_t)a.stride, lo, hi, lo & ~7};
+    n = sq_topk_table(sv, t.m, kl, a.cand + rs * a.k_max, sh.ft);
+    if (n < 0) {
+      __syncthreads();  // (the table path's LDS reads done)
+      n = sq_topk_fewfinite(sv, kl, a.cand + rs * a.k_max, sh.ft);
+    }
+  }
   if (n < 0) {
     __syncthreads();  // (the table path's LDS is the same memory)
     const Stats st = row_stats(row, sh.rs.bs);
