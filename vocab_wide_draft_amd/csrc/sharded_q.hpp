@@ -318,7 +318,10 @@ sq_sum_kernel(ShardQArgs a) {
   if constexpr (DT == DSPARK_BF16) {
     // a row with a value table (fast_q.hpp): its values counted per entry,
     // count x weight added once per occupied entry; no weights stored (the
-    // floor and cand passes take them from the table too)
+    // floor and cand passes take them from the table too).  A shard of at
+    // least kNBF ids keeps its entry counts at the start of its own part of
+    // the count row, which nothing reads or writes until the cand pass, so
+    // that the floor pass need not count again.
     __shared__ uint32_t s_nb[kNBFD];
     const FMap f = fmap_make(dense ? __float_as_uint(t.m) >> 16 : 0u);  // (m is a bf16 value)
     if (dense && f.NB <= kNBF) {
@@ -327,8 +330,10 @@ sq_sum_kernel(ShardQArgs a) {
       bf16_count_entries<kShardBS, 4>(static_cast<const uint16_t*>(a.data) + (size_t)r * (size_t)a.stride, lo, hi, f,
                                       s_nb);
       __syncthreads();
+      uint32_t* const keep = hi - lo >= kNBF ? a.dense + (size_t)r * a.V + lo : nullptr;
       for (int j = (int)threadIdx.x; j < f.NB; j += kShardBS) {
         const uint32_t n = s_nb[j];
+        if (keep) keep[j] = n;
         if (n) acc_add(acc, __float_as_uint(cr_expf(bf16_to_f32(fmap_raw(j, f)) - t.m, s_exp)), n);
       }
       acc = block_acc_total(acc, s_a);
@@ -445,17 +450,22 @@ __global__ void __launch_bounds__(BS) sq_floor_kernel(ShardQArgs a) {
   if constexpr (DT == DSPARK_BF16) {
     const FMap f = fmap_make(__float_as_uint(t.m) >> 16);  // (m is a bf16 value)
     if (f.NB <= kNBF) {  // (the same for every thread)
-      for (int j = threadIdx.x; j < kNBFD; j += BS) s_nb[j] = 0u;
+      // the entry counts the sum pass kept (shards of at least kNBF ids), else counted again
+      const uint32_t* const kept = hi - lo >= kNBF ? a.dense + (size_t)r * a.V + lo : nullptr;
+      if (!kept)
+        for (int j = threadIdx.x; j < kNBFD; j += BS) s_nb[j] = 0u;
       for (int b = threadIdx.x; b < kTkBins; b += BS) sh.hist[b] = 0u;
       exp_table_to_lds(sh.etab);
       merge_s64();
       __syncthreads();
-      bf16_count_entries<BS, 2>(static_cast<const uint16_t*>(a.data) + (size_t)r * (size_t)a.stride, lo, hi, f, s_nb);
-      __syncthreads();
+      if (!kept) {
+        bf16_count_entries<BS, 2>(static_cast<const uint16_t*>(a.data) + (size_t)r * (size_t)a.stride, lo, hi, f, s_nb);
+        __syncthreads();
+      }
       const SumR S = sum_r(sh.s64);
       uint32_t fsum = 0, npos = 0;  // (a row's floors add up to at most about 2^24)
       for (int j = threadIdx.x; j < f.NB; j += BS) {
-        const uint32_t n = s_nb[j];
+        const uint32_t n = kept ? kept[j] : s_nb[j];
         if (n) {
           uint32_t c;
           double rr;
